@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer forward on one MI355X.
+
+One step = one pass of the whole layer over one batch of synthetic tokens:
+route -> dispatch -> grouped GEMM up -> grouped GEMM down (-> shared expert)
+-> combine, each stage a call of the C ABI on the current stream, inputs and
+weights resident in HBM.  HIP events between the stage calls time every stage
+inside the timed region; the whole-step throughput comes from the wall clock
+around K steps bracketed by device synchronisation.
+
+Prints one JSON line (see the keys below).  Default workload: the
+Mixtral-8x7B-shaped layer (T=4096, d=4096, d_ff=14336, 8 experts, top-2,
+SwiGLU, bf16).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0                        # MI355X HBM3E
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+METRIC = "MoE layer tokens/s + grouped-GEMM % MFMA peak, Mixtral-shaped layer, 1 GPU"
+
+
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def workload_desc(cfg):
+    s = (f"{cfg.name}: T={cfg.T} d_model={cfg.d} d_ff={cfg.F} experts={cfg.E} top_k={cfg.k} "
+         f"{cfg.act} {cfg.gate} {cfg.act_dtype}")
+    if cfg.capacity_factor > 0:
+        s += f" capacity_factor={cfg.capacity_factor}"
+    if cfg.n_shared:
+        s += f" shared_expert d_ff={cfg.F_shared}"
+    return s
+
+
+def cpu_baseline(cfg, dinp, target_s):
+    """The oracle as it stands, on the host cores, on the first Ts tokens of
+    the same workload (whole layer, every weight); Ts is sized so the run
+    takes about target_s seconds."""
+    import oracle
+    host = {k: v.cpu() for k, v in dinp.items()}
+    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+
+    def run(ts):
+        sub = dict(host)
+        sub["x"] = host["x"][:ts].contiguous()
+        if "noise" in sub:
+            sub["noise"] = host["noise"][:ts].contiguous()
+        c = cfg.replace(T=ts)
+        t0 = time.perf_counter()
+        oracle.forward(c, sub, noise="philox")
+        return time.perf_counter() - t0
+
+    ts = min(8, cfg.T)
+    t_small = run(ts)
+    if t_small < target_s / 4 and ts < cfg.T:
+        ts = int(min(cfg.T, max(ts, ts * target_s / max(t_small, 1e-3))))
+        t = run(ts)
+    else:
+        t = t_small
+    return {"value": ts / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {ts} of the {cfg.T} tokens, whole layer (route, dispatch, experts, combine) "
+                      f"with all weights, {t:.1f} s of oracle time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=None,
+                    help="measured HBM bytes per launch of the dominant kernel (from rocprofv3 counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs the layer on one GPU only; multi-GPU runs are not part of it "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import sparse_mixture_experts_39_amd as moe
+
+    cfg = workloads.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: drawing {workload_desc(cfg)} on {torch.cuda.get_device_name(0)}")
+    dinp = workloads.make_inputs(cfg, device=dev, with_noise=False)
+    c = moe.config(T=cfg.T, d_model=cfg.d, d_ff=cfg.F, n_experts=cfg.E, top_k=cfg.k, act_dtype=cfg.act_dtype,
+                   act=cfg.act, gate=cfg.gate, capacity_factor=cfg.capacity_factor, residual=cfg.residual,
+                   n_shared=cfg.n_shared, d_ff_shared=cfg.F_shared, seed=cfg.seed)
+    w = moe.weights_from(c, dinp)
+    ws = moe.workspace(c)
+    st = moe.alloc_stats(c)
+    T, E, k, d, F = c.T, c.n_experts, c.top_k, c.d_model, c.d_ff
+    R = moe.max_rows(c)
+    dt = dinp["x"].dtype
+    i32 = dict(dtype=torch.int32, device=dev)
+    idx = torch.empty((T, k), **i32)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    x_perm = torch.empty((R, d), dtype=dt, device=dev)
+    H = torch.empty((R, F), dtype=dt, device=dev)
+    y_perm = torch.empty((R, d), dtype=dt, device=dev)
+    offsets = torch.empty((E + 1,), **i32)
+    perm_src = torch.empty((R,), **i32)
+    slot_pos = torch.empty((T, k), **i32)
+    shared = torch.empty((T, d), dtype=dt, device=dev) if cfg.n_shared else None
+    out = torch.empty((T, d), dtype=dt, device=dev)
+    x = dinp["x"]
+    stages = ["route", "dispatch", "expert_up", "expert_down"] + (["shared_expert"] if shared is not None else []) + ["combine"]
+
+    def step(ev):
+        ev[0].record()
+        moe.moe_route(c, x, w, idx, gates, None, st, ws)
+        ev[1].record()
+        moe.moe_dispatch(c, x, idx, x_perm, offsets, perm_src, slot_pos, st, ws)
+        ev[2].record()
+        moe.moe_expert_up(c, x_perm, offsets, w, H, ws)
+        ev[3].record()
+        moe.moe_expert_down(c, H, offsets, w, y_perm, ws)
+        ev[4].record()
+        i = 5
+        if shared is not None:
+            moe.moe_shared_expert(c, x, w, shared, ws)
+            ev[i].record()
+            i += 1
+        moe.moe_combine(c, y_perm, slot_pos, gates, x if cfg.residual else None, shared, out)
+        ev[i].record()
+
+    nev = len(stages) + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps + args.warmup)]
+    for i in range(args.warmup):
+        step(events[i])
+    torch.cuda.synchronize()
+    log(f"bench: {args.warmup} warmup steps done, timing {args.steps}")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[args.warmup + i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stage_ms = {s: 0.0 for s in stages}
+    for i in range(args.steps):
+        ev = events[args.warmup + i]
+        for j, s in enumerate(stages):
+            stage_ms[s] += ev[j].elapsed_time(ev[j + 1]) / args.steps
+
+    kept = int(st["kept"].sum().item())
+    es = 2 if cfg.act_dtype == "bf16" else 4
+    gemm_mult = 2 if cfg.act == "swiglu" else 1
+    flops_up = 2.0 * kept * d * F * gemm_mult
+    flops_down = 2.0 * kept * F * d
+    counts = st["kept"].cpu()
+    active = int((counts > 0).sum().item())
+    w_up_bytes = active * gemm_mult * F * d * es
+    w_down_bytes = active * d * F * es
+    up_bytes = w_up_bytes + kept * d * es + kept * F * es          # weights + x_perm rows + h rows
+    down_bytes = w_down_bytes + kept * F * es + kept * d * es
+    if shared is not None:
+        fs = cfg.F_shared
+        flops_sh = 2.0 * T * d * fs * 3
+        sh_bytes = 3 * d * fs * es + 2 * T * d * es + 2 * T * fs * es
+    peak_f = PEAK_MFMA_TFLOPS[cfg.act_dtype]
+
+    def roof(name, flops, nbytes):
+        t = stage_ms[name] * 1e-3
+        mfma_t, hbm_t = flops / (peak_f * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)
+        if mfma_t >= hbm_t:
+            a = flops / t / 1e12
+            return {"bound": "mfma", "achieved": a, "peak": peak_f, "unit": "TFLOP/s", "frac": a / peak_f}
+        a = nbytes / t / 1e9
+        return {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": a / PEAK_HBM_GBS}
+
+    r_up = roof("expert_up", flops_up, up_bytes)
+    r_down = roof("expert_down", flops_down, down_bytes)
+    dominant = "expert_up" if stage_ms["expert_up"] >= stage_ms["expert_down"] else "expert_down"
+    roofline = dict(r_up if dominant == "expert_up" else r_down)
+    roofline["kernel"] = "k_grouped_gemm (" + ("SwiGLU up" if dominant == "expert_up" and cfg.act == "swiglu"
+                                              else "ReLU up" if dominant == "expert_up" else "down") + ")"
+    roofline["per_launch"] = {"flops": flops_up if dominant == "expert_up" else flops_down,
+                              "bytes": up_bytes if dominant == "expert_up" else down_bytes,
+                              "avg_ms": stage_ms[dominant]}
+    roofline["traffic"] = None
+    if args.traffic_json and os.path.exists(args.traffic_json):
+        tr = json.load(open(args.traffic_json))
+        if tr.get("workload") == cfg.name and tr.get("stage") == dominant:
+            roofline["traffic"] = tr.get("hbm_bytes_per_launch")
+
+    gemm_ms = stage_ms["expert_up"] + stage_ms["expert_down"]
+    disp_bytes = T * d * es + kept * d * es                            # read x once, write k copies
+    comb_bytes = kept * d * es + T * d * es + (T * d * es if cfg.residual else 0) + (T * d * es if shared is not None else 0)
+    value = T * args.steps / wall
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.act_dtype,
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+        "config": {"workload": workload_desc(cfg), "T": T, "d_model": d, "d_ff": F, "n_experts": E, "top_k": k,
+                   "parallelism": "single GPU, all experts resident"},
+        "grouped_gemm_pct_mfma_peak": 100.0 * (flops_up + flops_down) / (gemm_ms * 1e-3) / (peak_f * 1e12),
+        "dispatch_pct_hbm_peak": 100.0 * disp_bytes / (stage_ms["dispatch"] * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "combine_pct_hbm_peak": 100.0 * comb_bytes / (stage_ms["combine"] * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "stages_ms": stage_ms,
+        "expert_up_roofline": r_up,
+        "expert_down_roofline": r_down,
+        "roofline": roofline,
+        "rows_kept": kept,
+        "experts_with_rows": active,
+    }
+    if shared is not None:
+        res["shared_expert_roofline"] = roof("shared_expert", flops_sh, sh_bytes)
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(cfg, dinp, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,243 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse token-choice MoE FFN layer.
+ *
+ * One call of the layer, on one GPU that holds every expert, computes
+ *   route -> dispatch -> expert FFNs -> combine
+ * in the order the pages state the layer (CS25 "Lecture29" notes, section
+ * "Top-two routing", minimal pseudocode: router logits, top-k, gates from the
+ * selected logits, dispatch by expert, run the selected experts, combine and
+ * restore the token order; awesome-ai-roadmap ch. 19, section 19.3.2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every tensor argument is a DEVICE pointer to memory the caller
+ * owns (e.g. a PyTorch allocation).  The library never allocates, frees or
+ * synchronizes: all work is enqueued on `stream` (a hipStream_t; NULL means
+ * the null stream) and completes asynchronously.  No entry point copies
+ * device data to the host, so a sequence of calls can be captured in a HIP
+ * graph.  The library keeps no state between calls and is re-entrant; calls
+ * that share a workspace must not overlap in time.
+ *
+ * Layouts.  Row-major, densely packed.  Activations x, x_perm, y_perm and out
+ * are [rows][d_model] in the activation dtype (fp32, or bf16 stored as
+ * uint16).  Expert weights use the [out][in] layout so the reduction
+ * dimension is contiguous: w_gate / w_up are [E][d_ff][d_model], w_down is
+ * [E][d_model][d_ff].  Router-side tensors are always fp32.  Index tensors are
+ * int32.  An assignment is the pair (token t, slot j) with flat id
+ * a = t * top_k + j; slots are ordered by selection score, best first.
+ *
+ * Errors.  Every argument check runs on the host before anything is
+ * enqueued; a failed check returns MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED
+ * or MOE_ERR_WORKSPACE and enqueues nothing.  A failed kernel launch returns
+ * MOE_ERR_HIP; the HIP error code is kept per thread and read with
+ * moe_last_hip_error().  Conditions found on the device (a non-finite
+ * selection score) are reported through stats.device_status.  The library
+ * never aborts and never throws across this ABI.
+ *
+ * Limits.  1 <= top_k <= min(n_experts, 16); n_experts <= 1024;
+ * d_model and d_ff (and d_ff_shared) multiples of 64; T >= 0 and
+ * T * top_k < 2^31.  n_shared is 0 or 1.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,  /* a null required pointer, a size out of range, an unknown enum */
+    MOE_ERR_UNSUPPORTED = 2,  /* a valid layer this library does not implement (alignment, limits) */
+    MOE_ERR_WORKSPACE = 3,    /* workspace null or smaller than moe_workspace_size() */
+    MOE_ERR_HIP = 4           /* a HIP launch failed; see moe_last_hip_error() */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Gate families (how the selection is turned into mixing weights). */
+typedef enum {
+    /* g = softmax over the k selected logits (Lecture29, eq. for g_i). */
+    MOE_GATE_SOFTMAX_TOPK = 0,
+    /* g = full softmax over all E logits, read at the selected experts, no
+     * renormalisation (CS336 lecture 4 notes, section 5 listing; Switch
+     * lesson: the chosen expert's output times the router probability). */
+    MOE_GATE_SOFTMAX_FULL = 1,
+    /* Shazeer noisy top-k: H = z + n * softplus(x W_noise), n ~ N(0,1);
+     * g = softmax over the k selected H (Outrageously Large Neural Networks
+     * reading notes, section 2.2). */
+    MOE_GATE_NOISY_TOPK = 2,
+    /* DeepSeek-V3: s = sigmoid(z); select the top-k of s + b; g = s of the
+     * selected experts renormalised to sum to 1; the bias never enters g
+     * (awesome-ai-roadmap 19.3.4; CS336 notes, section 12). */
+    MOE_GATE_SIGMOID_BIAS = 3
+} moe_gate;
+
+/* Expert MLP: y = W2 relu(W1 a) (Shazeer notes 2.2), or
+ * y = W2 (SiLU(W1 a) * W3 a) with W1 = gate, W3 = up, W2 = down (Lecture29,
+ * "Dense baseline", SwiGLU MLP). */
+typedef enum { MOE_ACT_RELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
+
+enum {
+    MOE_F_ADD_RESIDUAL = 1u, /* out += x (CS336 notes section 5 listing: h = sum g FFN(u) + u) */
+    MOE_F_NOISE_INPUT = 2u   /* NOISY_TOPK: read n from the caller's noise tensor
+                                instead of the built-in Philox4x32-10 stream */
+};
+
+enum { MOE_DEV_NONFINITE = 1 }; /* device_status bit: a selection score was NaN or infinite */
+
+typedef struct {
+    int32_t T;              /* tokens in this call */
+    int32_t d_model;
+    int32_t d_ff;           /* routed expert hidden width */
+    int32_t n_experts;      /* E */
+    int32_t top_k;          /* k */
+    int32_t n_shared;       /* 0 or 1 always-on shared expert (SwiGLU), weight 1 */
+    int32_t d_ff_shared;
+    int32_t act_dtype;      /* moe_dtype of x, out, expert weights and intermediates */
+    int32_t act;            /* moe_act */
+    int32_t gate;           /* moe_gate */
+    float capacity_factor;  /* > 0: C = ceil(cf * T * k / E); <= 0: dropless */
+    uint32_t flags;         /* MOE_F_* */
+    uint64_t seed;          /* Philox key of the noisy gate */
+    uint64_t noise_offset;  /* Philox counter offset (words 2,3) of the noisy gate */
+} moe_config;
+
+/* Weights of one layer (device pointers). */
+typedef struct {
+    const float* w_router;   /* [E][d] fp32 router matrix W_r */
+    const float* logit_bias; /* [E] fp32 added to the logits, or NULL */
+    const float* sel_bias;   /* [E] fp32 selection-only bias (SIGMOID_BIAS), or NULL */
+    const float* w_noise;    /* [E][d] fp32 noise-scale matrix (NOISY_TOPK) */
+    const float* noise;      /* [T][E] fp32 standard-normal draws when MOE_F_NOISE_INPUT */
+    const void* w_gate;      /* [E][d_ff][d] W1 (gate for SwiGLU, the hidden layer for ReLU) */
+    const void* w_up;        /* [E][d_ff][d] W3 (SwiGLU only; NULL for ReLU) */
+    const void* w_down;      /* [E][d][d_ff] W2 */
+    const void* ws_gate;     /* shared expert [d_ff_shared][d] (n_shared = 1) */
+    const void* ws_up;       /* shared expert [d_ff_shared][d] */
+    const void* ws_down;     /* shared expert [d][d_ff_shared] */
+} moe_weights;
+
+/* Load statistics (device pointers; any member may be NULL to skip it).
+ * f_i is the fraction of the T*k assignments routed to expert i before
+ * capacity drops (so sum f = 1), and P_i the batch mean of the router
+ * probability of expert i (awesome-ai-roadmap 19.3.3; CS336 notes section
+ * 9); the router probability vector is softmax(z) for the softmax gates,
+ * softmax(H) for the noisy gate and s / sum(s) for the sigmoid gate.
+ * imbalance = max_i n_i / (T k / E) (Lecture29, "Myth 3");
+ * aux = E * sum_i f_i P_i (the Switch balance term without its coefficient). */
+typedef struct {
+    int32_t* counts;        /* [E] assignments per expert before drops */
+    int32_t* kept;          /* [E] assignments kept after the capacity cut */
+    float* f;               /* [E] */
+    float* P;               /* [E] */
+    int32_t* n_dropped;     /* [1] */
+    float* imbalance;       /* [1] */
+    float* aux;             /* [1] */
+    int32_t* device_status; /* [1] MOE_DEV_* bits, written by moe_route */
+} moe_stats;
+
+/* ---- pure host helpers (no device work, usable without a GPU) ---------- */
+
+/* Check a configuration.  MOE_OK, MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED. */
+moe_status moe_validate_config(const moe_config* cfg);
+
+/* Bytes of workspace moe_layer_forward needs (the stage calls need no more). */
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Rows of x_perm / y_perm the caller must allocate: T*k when dropless, else
+ * min(T*k, E*C).  -1 for an invalid configuration. */
+int64_t moe_max_rows(const moe_config* cfg);
+
+/* Expert capacity C = ceil(capacity_factor * T * k / E) computed in fp64
+ * (Lecture29, "Inference load balance"), or -1 when dropless or invalid. */
+int64_t moe_capacity(const moe_config* cfg);
+
+/* HIP error code of the last MOE_ERR_HIP on this thread (0 if none). */
+int32_t moe_last_hip_error(void);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status s);
+
+/* ---- stages ------------------------------------------------------------- */
+
+/* Route.  For every token: fp32 logits z = W_r x (+ logit_bias) with the
+ * fixed sequential-fma order, the selection score, the k best experts
+ * (score descending, ties to the lower index), the gates, and the router
+ * probabilities, whose batch mean is written to stats->P.
+ *   x        [T][d] act dtype          w_router [E][d] fp32
+ *   topk_idx [T][k] int32 (out)        topk_gate [T][k] fp32 (out)
+ *   scores   [T][E] fp32 selection scores (out, optional, may be NULL)
+ * Sets stats->device_status.  Needs ws (>= moe_workspace_size bytes). */
+moe_status moe_route(const moe_config* cfg, const void* x, const moe_weights* w,
+                     int32_t* topk_idx, float* topk_gate, float* scores,
+                     const moe_stats* stats, void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch.  Per-expert histogram of the assignments, a prefix scan into
+ * expert_offsets, the capacity cut, and a permutation of token rows into
+ * expert-contiguous order, stable in assignment order (Lecture29, "Top-k
+ * routing semantics"); with a capacity the first C assignments of each
+ * expert are kept and the rest dropped (CS336 notes section 10; Switch
+ * lesson token-drop answer).
+ *   x [T][d] act dtype; topk_idx [T][k]
+ *   x_perm [max_rows][d] act dtype (out): row r holds x[perm_src[r] / k]
+ *   expert_offsets [E+1] (out): expert e owns rows [off[e], off[e+1])
+ *   perm_src [max_rows] (out): assignment id of each kept row
+ *   slot_pos [T][k] (out): row of each assignment, -1 if dropped
+ * Writes stats counts, kept, n_dropped, f, imbalance and aux (the last two
+ * read stats->P written by moe_route; pass the same stats). */
+moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                        void* x_perm, int32_t* expert_offsets, int32_t* perm_src,
+                        int32_t* slot_pos, const moe_stats* stats,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFNs as two grouped GEMMs over ragged per-expert row ranges:
+ * rows [off[e], off[e+1]) of x_perm go through expert e, the hidden tensor
+ * is stored in the act dtype inside ws, and y_perm receives the expert
+ * outputs in the same row order (fp32 accumulation).
+ *   x_perm, y_perm [max_rows][d]; expert_offsets [E+1] from moe_dispatch. */
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                          const moe_weights* w, void* y_perm,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* The two grouped GEMMs of moe_expert_ffn as separate calls.
+ * moe_expert_up:   h[r] = SiLU(x_perm[r] W1_e^T) * (x_perm[r] W3_e^T)   (SwiGLU)
+ *                  h[r] = relu(x_perm[r] W1_e^T)                        (ReLU)
+ *                  for every row r of expert e; h is [max_rows][d_ff] in the act dtype.
+ * moe_expert_down: y_perm[r] = h[r] W2_e^T.
+ * Same layouts and ownership as moe_expert_ffn; h is caller-owned here. */
+moe_status moe_expert_up(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                         const moe_weights* w, void* h, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
+                           const moe_weights* w, void* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* The always-on shared expert on every token (awesome-ai-roadmap 19.5):
+ * shared_out[T][d] = SwiGLU_shared(x).  Requires n_shared = 1. */
+moe_status moe_shared_expert(const moe_config* cfg, const void* x, const moe_weights* w,
+                             void* shared_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Combine.  out[t] = (residual ? x[t] : 0) + (shared_out ? shared_out[t] : 0)
+ *                    + sum_j topk_gate[t][j] * y_perm[slot_pos[t][j]],
+ * accumulated in fp32 in slot order, a dropped slot contributing nothing
+ * (Lecture29, eq. y = sum_i g_i Expert_i; CS336 notes section 10: a dropped
+ * token's MLP output is zero and the residual passes through).  One writer
+ * per output element, no atomics: bitwise deterministic.
+ *   residual: x [T][d] or NULL; shared_out [T][d] or NULL; out [T][d]. */
+moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_pos,
+                       const float* topk_gate, const void* residual, const void* shared_out,
+                       void* out, void* stream);
+
+/* The whole layer: route, dispatch, experts (+ shared expert), combine, with
+ * every intermediate carved from ws.  x [T][d], out [T][d].  The residual is
+ * added when cfg->flags has MOE_F_ADD_RESIDUAL. */
+moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x, void* out,
+                             const moe_stats* stats, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,211 @@
+// Dispatch stage for gfx950: per-expert histogram, prefix scan with the
+// capacity cut, stable scatter of assignments into expert order, and the row
+// permutation of the token activations.
+//
+// The layer re-arranges tokens by expert, runs every expert on its batch and
+// restores the token order afterwards (CS25 "Lecture29" notes, "Top-k routing
+// semantics").  The order inside an expert is the assignment order
+// a = t*k + j, so the permutation is the stable counting sort of the
+// assignments by expert; with a capacity C (Lecture29, "Inference load
+// balance": C = ceil(alpha T k / E)) the first C assignments of an expert are
+// kept and later ones dropped (CS336 lecture 4 notes, section 10).  Ranks come
+// from positions, never from the arrival order of atomics, so every output is
+// bitwise reproducible.
+//
+// Kernels
+//   k_histogram   256 assignments per block; lanes holding the same expert
+//                 are found with one ballot per expert-id bit; per-wave counts
+//                 in LDS; per-block histogram hist[b][e]
+//   k_scan        one block: column scan over blocks (rank base of each block
+//                 inside each expert), capacity cut, exclusive scan over
+//                 experts -> offsets, and the load statistics
+//   k_scatter     same ranking as k_histogram, plus the wave prefix inside the
+//                 block -> slot_pos / perm_src
+//   k_permute     x_perm[row] = x[perm_src[row] / k], 16-byte vector copies
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// Lanes of the wave whose (valid) expert id equals this lane's.
+__device__ __forceinline__ uint64_t match_lanes(int e, bool valid, int ebits) {
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < ebits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bm = __ballot(bit);
+        m &= bit ? bm : ~bm;
+    }
+    return m;
+}
+
+static int id_bits(int E) { int b = 0; while ((1 << b) < E) ++b; return b; }
+
+__global__ __launch_bounds__(256) void k_histogram(const int32_t* __restrict__ topk_idx, int64_t n_assign, int E,
+                                                   int ebits, int32_t* __restrict__ hist) {
+    extern __shared__ int32_t cnt[];  // [4][E]
+    for (int i = threadIdx.x; i < 4 * E; i += 256) cnt[i] = 0;
+    __syncthreads();
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int64_t a = (int64_t)blockIdx.x * kAssignBlock + threadIdx.x;
+    const int ev = a < n_assign ? topk_idx[a] : -1;
+    const bool valid = ev >= 0 && ev < E;   // an id outside [0, E) is ignored (never indexes memory)
+    const int e = valid ? ev : 0;
+    const uint64_t m = match_lanes(e, valid, ebits);
+    if (valid && lane == __ffsll((unsigned long long)m) - 1) cnt[wave * E + e] = __popcll(m);
+    __syncthreads();
+    for (int i = threadIdx.x; i < E; i += 256)
+        hist[(int64_t)blockIdx.x * E + i] = ((cnt[i] + cnt[E + i]) + cnt[2 * E + i]) + cnt[3 * E + i];
+}
+
+__global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ hist, int nblocks, int E, int64_t n_assign,
+                                               int64_t capacity, int32_t* __restrict__ blockbase,
+                                               int32_t* __restrict__ offsets, const float* __restrict__ P,
+                                               int32_t* counts_out, int32_t* kept_out, float* f_out,
+                                               int32_t* dropped_out, float* imbalance_out, float* aux_out) {
+    __shared__ int32_t scan[1024];
+    __shared__ int64_t kept_red[1024];
+    __shared__ int32_t max_red[1024];
+    __shared__ double aux_red[1024];
+    const int e = threadIdx.x;
+    int32_t c = 0, kp = 0;
+    double fe = 0.0;
+    if (e < E) {
+        int32_t run = 0;
+        for (int b = 0; b < nblocks; ++b) {
+            blockbase[(int64_t)b * E + e] = run;
+            run += hist[(int64_t)b * E + e];
+        }
+        c = run;
+        kp = (capacity >= 0 && (int64_t)c > capacity) ? (int32_t)capacity : c;
+        fe = n_assign > 0 ? (double)c / (double)n_assign : 0.0;
+    }
+    // inclusive scan of kept over experts (Hillis-Steele, integers)
+    scan[e] = kp;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int32_t v = e >= off ? scan[e - off] : 0;
+        __syncthreads();
+        scan[e] += v;
+        __syncthreads();
+    }
+    if (e < E) {
+        offsets[e] = scan[e] - kp;
+        if (e == E - 1) offsets[E] = scan[e];
+        if (counts_out) counts_out[e] = c;
+        if (kept_out) kept_out[e] = kp;
+        if (f_out) f_out[e] = (float)fe;
+    }
+    // fixed-tree reductions for the scalar statistics
+    kept_red[e] = kp;
+    max_red[e] = c;
+    aux_red[e] = (e < E && P) ? fe * (double)P[e] : 0.0;
+    __syncthreads();
+    for (int half = 512; half >= 1; half >>= 1) {
+        if (e < half) {
+            kept_red[e] += kept_red[e + half];
+            max_red[e] = max(max_red[e], max_red[e + half]);
+            aux_red[e] += aux_red[e + half];
+        }
+        __syncthreads();
+    }
+    if (e == 0) {
+        if (dropped_out) dropped_out[0] = (int32_t)(n_assign - kept_red[0]);
+        if (imbalance_out) imbalance_out[0] = n_assign > 0 ? (float)((double)max_red[0] * (double)E / (double)n_assign) : 0.0f;
+        if (aux_out && P) aux_out[0] = (float)((double)E * aux_red[0]);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ topk_idx, int64_t n_assign, int E,
+                                                 int ebits, const int32_t* __restrict__ blockbase,
+                                                 const int32_t* __restrict__ offsets, int64_t capacity,
+                                                 int32_t* __restrict__ perm_src, int32_t* __restrict__ slot_pos) {
+    extern __shared__ int32_t cnt[];  // [4][E]
+    for (int i = threadIdx.x; i < 4 * E; i += 256) cnt[i] = 0;
+    __syncthreads();
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int64_t a = (int64_t)blockIdx.x * kAssignBlock + threadIdx.x;
+    const int ev = a < n_assign ? topk_idx[a] : -1;
+    const bool valid = ev >= 0 && ev < E;   // an id outside [0, E) is ignored (never indexes memory)
+    const int e = valid ? ev : 0;
+    const uint64_t m = match_lanes(e, valid, ebits);
+    if (valid && lane == __ffsll((unsigned long long)m) - 1) cnt[wave * E + e] = __popcll(m);
+    __syncthreads();
+    if (!valid) {
+        if (a < n_assign) slot_pos[a] = -1;
+        return;
+    }
+    int32_t r = blockbase[(int64_t)blockIdx.x * E + e];
+    for (int w = 0; w < wave; ++w) r += cnt[w * E + e];
+    r += __popcll(m & ((1ull << lane) - 1ull));
+    if (capacity < 0 || (int64_t)r < capacity) {
+        const int32_t row = offsets[e] + r;
+        slot_pos[a] = row;
+        perm_src[row] = (int32_t)a;
+    } else {
+        slot_pos[a] = -1;
+    }
+}
+
+// Grid-stride over (row, 16-byte chunk); rows >= offsets[E] are not copied.
+__global__ __launch_bounds__(256) void k_permute(const uint4* __restrict__ x, int k, int cpr,
+                                                 const int32_t* __restrict__ perm_src,
+                                                 const int32_t* __restrict__ offsets, int E, int64_t max_rows,
+                                                 uint4* __restrict__ x_perm) {
+    const int64_t R = offsets[E];
+    const int64_t total = (R < max_rows ? R : max_rows) * cpr;
+    const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+    for (int64_t base = (int64_t)blockIdx.x * 256 * 4 + threadIdx.x; base < total; base += stride) {
+        uint4 v[4];
+        int64_t dst[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = base + (int64_t)u * 256;
+            dst[u] = -1;
+            if (i < total) {
+                const int64_t row = i / cpr;
+                const int c = (int)(i - row * cpr);
+                const int64_t t = perm_src[row] / k;
+                v[u] = x[t * cpr + c];
+                dst[u] = i;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (dst[u] >= 0) x_perm[dst[u]] = v[u];
+    }
+}
+
+void launch_histogram(const int32_t* topk_idx, int64_t n_assign, int E, int32_t* hist, hipStream_t s) {
+    const int nb = (int)((n_assign + kAssignBlock - 1) / kAssignBlock);
+    if (nb == 0) return;
+    hipLaunchKernelGGL(k_histogram, dim3(nb), dim3(256), 4 * E * sizeof(int32_t), s, topk_idx, n_assign, E,
+                       id_bits(E), hist);
+}
+
+void launch_scan(const int32_t* hist, int nblocks, int E, int64_t n_assign, int64_t capacity, int32_t* blockbase,
+                 int32_t* offsets, const float* P, const moe_stats* st, hipStream_t s) {
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, nblocks, E, n_assign, capacity, blockbase, offsets, P,
+                       st ? st->counts : nullptr, st ? st->kept : nullptr, st ? st->f : nullptr,
+                       st ? st->n_dropped : nullptr, st ? st->imbalance : nullptr, st ? st->aux : nullptr);
+}
+
+void launch_scatter(const int32_t* topk_idx, int64_t n_assign, int E, const int32_t* blockbase,
+                    const int32_t* offsets, int64_t capacity, int32_t* perm_src, int32_t* slot_pos, hipStream_t s) {
+    const int nb = (int)((n_assign + kAssignBlock - 1) / kAssignBlock);
+    if (nb == 0) return;
+    hipLaunchKernelGGL(k_scatter, dim3(nb), dim3(256), 4 * E * sizeof(int32_t), s, topk_idx, n_assign, E, id_bits(E),
+                       blockbase, offsets, capacity, perm_src, slot_pos);
+}
+
+void launch_permute_rows(const void* x, int k, int d, int elem_bytes, const int32_t* perm_src, const int32_t* offsets,
+                         int E, int64_t max_rows, void* x_perm, hipStream_t s) {
+    const int cpr = d * elem_bytes / 16;
+    const int64_t total = max_rows * cpr;
+    if (total == 0) return;
+    int64_t nb = (total + 1023) / 1024;
+    if (nb > 16384) nb = 16384;
+    hipLaunchKernelGGL(k_permute, dim3((unsigned)nb), dim3(256), 0, s, (const uint4*)x, k, cpr, perm_src, offsets, E,
+                       max_rows, (uint4*)x_perm);
+}
+
+}  // namespace moe

@@ -1,0 +1,55 @@
+// Internal launchers of the gfx950 kernels (host side).  Every launcher only
+// enqueues work on the given stream; argument validation happens in
+// moe_api.cpp before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// route.hip
+void launch_router_dots(bool bf16, const void* x, const float* w0, const float* w1, int T, int d, int E, int NC,
+                        float* dots, hipStream_t s);
+int select_blocks(int T, int E);
+void launch_select(const float* dots, int NC, const float* logit_bias, const float* sel_bias, const float* noise,
+                   int gate, int T, int E, int k, uint64_t seed, uint64_t noise_offset, int32_t* topk_idx,
+                   float* topk_gate, float* scores, float* P_part, int32_t* status, hipStream_t s);
+void launch_reduce_P(const float* P_part, int nblocks, int E, int T, float* P_ws, float* P_out,
+                     const int32_t* status_ws, int32_t* status_out, hipStream_t s);
+void launch_zero_i32(int32_t* p, int n, hipStream_t s);
+
+// dispatch.hip
+constexpr int kAssignBlock = 256;  // assignments per histogram / scatter block
+void launch_histogram(const int32_t* topk_idx, int64_t n_assign, int E, int32_t* hist, hipStream_t s);
+void launch_scan(const int32_t* hist, int nblocks, int E, int64_t n_assign, int64_t capacity,
+                 int32_t* blockbase, int32_t* offsets, const float* P, const moe_stats* st, hipStream_t s);
+void launch_scatter(const int32_t* topk_idx, int64_t n_assign, int E, const int32_t* blockbase,
+                    const int32_t* offsets, int64_t capacity, int32_t* perm_src, int32_t* slot_pos, hipStream_t s);
+void launch_permute_rows(const void* x, int k, int d, int elem_bytes, const int32_t* perm_src, const int32_t* offsets,
+                         int E, int64_t max_rows, void* x_perm, hipStream_t s);
+
+// combine.hip
+void launch_combine(const void* y_perm, const int32_t* slot_pos, const float* gates, const void* residual,
+                    const void* shared, void* out, int T, int d, int k, bool bf16, hipStream_t s);
+
+// ffn.hip
+struct GemmShape {
+    int BM, BN;
+};
+// Tile plan: prefix sums of ceil(M_e / BM) over experts, built on the device.
+void launch_tile_plan(const int32_t* offsets, int E, int uniform_rows, int BM, int32_t* tile_prefix,
+                      int32_t* offsets_copy, hipStream_t s);
+size_t ffn_tile_plan_ints(int E);
+// Grouped GEMM C[rows][N] = act(A[rows][K] . B_e[N][K]^T) per expert group.
+// epi: 0 store, 1 relu, 2 swiglu (B0 = gate, B1 = up, N = d_ff, output width N).
+hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B0, const void* B1,
+                               int64_t b_expert_stride, void* C, int64_t ldc, int N, int K, int E,
+                               int64_t max_rows, const int32_t* offsets, const int32_t* tile_prefix,
+                               int BM, int BN, hipStream_t s);
+GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N);
+
+}  // namespace moe

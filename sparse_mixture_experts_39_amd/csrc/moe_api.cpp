@@ -1,0 +1,340 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace layout and the order of kernel launches for each stage.
+// Nothing here allocates, frees or synchronizes; every check runs before the
+// first launch of a call.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <string.h>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(const moe_config* c) { return c->act_dtype == MOE_BF16 ? 2 : 4; }
+bool is_bf16(const moe_config* c) { return c->act_dtype == MOE_BF16; }
+int64_t n_assign(const moe_config* c) { return (int64_t)c->T * c->top_k; }
+
+int64_t capacity_of(const moe_config* c) {
+    if (!(c->capacity_factor > 0.0f)) return -1;
+    const double v = ceil((double)c->capacity_factor * (double)c->T * (double)c->top_k / (double)c->n_experts);
+    return (int64_t)v;
+}
+
+int64_t max_rows_of(const moe_config* c) {
+    const int64_t tk = n_assign(c);
+    const int64_t cap = capacity_of(c);
+    if (cap < 0) return tk;
+    const int64_t ec = cap * (int64_t)c->n_experts;
+    return ec < tk ? ec : tk;
+}
+
+// Workspace regions (byte offsets from the workspace base).
+struct Layout {
+    size_t dots, P_part, P_ws, status;                    // route
+    size_t hist, blockbase;                               // dispatch
+    size_t H, plan_up, plan_down, plan_copy;              // experts
+    size_t Hs, plan_s_up, plan_s_down, plan_s_copy;       // shared expert
+    size_t idx, gates, slot_pos, perm_src, offsets;       // whole-layer intermediates
+    size_t x_perm, y_perm, shared_out;
+    size_t total;
+};
+
+Layout compute_layout(const moe_config* c) {
+    Layout L;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
+    const int E = c->n_experts, T = c->T;
+    const int NC = c->gate == MOE_GATE_NOISY_TOPK ? 2 * E : E;
+    const int es = elem_bytes(c);
+    const int64_t R = max_rows_of(c);
+    const int64_t nasg_blocks = (n_assign(c) + moe::kAssignBlock - 1) / moe::kAssignBlock;
+    const size_t plan = moe::ffn_tile_plan_ints(E) * sizeof(int32_t);
+    L.dots = take((size_t)T * NC * sizeof(float));
+    L.P_part = take((size_t)moe::select_blocks(T, E) * E * sizeof(float));
+    L.P_ws = take((size_t)E * sizeof(float));
+    L.status = take(sizeof(int32_t));
+    L.hist = take((size_t)nasg_blocks * E * sizeof(int32_t));
+    L.blockbase = take((size_t)nasg_blocks * E * sizeof(int32_t));
+    L.H = take((size_t)R * c->d_ff * es);
+    L.plan_up = take(plan);
+    L.plan_down = take(plan);
+    L.plan_copy = take(2 * sizeof(int32_t));
+    const bool sh = c->n_shared > 0;
+    L.Hs = take(sh ? (size_t)T * c->d_ff_shared * es : 0);
+    L.plan_s_up = take(plan);
+    L.plan_s_down = take(plan);
+    L.plan_s_copy = take(2 * sizeof(int32_t));
+    L.idx = take((size_t)n_assign(c) * sizeof(int32_t));
+    L.gates = take((size_t)n_assign(c) * sizeof(float));
+    L.slot_pos = take((size_t)n_assign(c) * sizeof(int32_t));
+    L.perm_src = take((size_t)R * sizeof(int32_t));
+    L.offsets = take((size_t)(E + 1) * sizeof(int32_t));
+    L.x_perm = take((size_t)R * c->d_model * es);
+    L.y_perm = take((size_t)R * c->d_model * es);
+    L.shared_out = take(sh ? (size_t)T * c->d_model * es : 0);
+    L.total = o;
+    return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return (T*)((char*)ws + off); }
+
+moe_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return MOE_OK;
+    g_last_hip_error = (int32_t)e;
+    return MOE_ERR_HIP;
+}
+
+moe_status after_launch() { return hip_status(hipGetLastError()); }
+
+moe_status check_ws(const moe_config* c, void* ws, size_t ws_bytes) {
+    if (!ws) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < compute_layout(c).total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_validate_config(const moe_config* c) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (c->T < 0 || c->d_model <= 0 || c->d_ff <= 0 || c->n_experts <= 0 || c->top_k <= 0) return MOE_ERR_INVALID_ARG;
+    if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
+    if (c->gate < MOE_GATE_SOFTMAX_TOPK || c->gate > MOE_GATE_SIGMOID_BIAS) return MOE_ERR_INVALID_ARG;
+    if (c->top_k > c->n_experts) return MOE_ERR_INVALID_ARG;
+    if (c->n_shared < 0 || c->n_shared > 1) return MOE_ERR_INVALID_ARG;
+    if (c->n_shared == 1 && c->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
+    if (c->capacity_factor != c->capacity_factor) return MOE_ERR_INVALID_ARG;
+    if (c->flags & ~(uint32_t)(MOE_F_ADD_RESIDUAL | MOE_F_NOISE_INPUT)) return MOE_ERR_INVALID_ARG;
+    if (c->top_k > 16 || c->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
+    if (c->d_model % 64 || c->d_ff % 64) return MOE_ERR_UNSUPPORTED;
+    if (c->n_shared == 1 && (c->d_ff_shared % 64 || c->act != MOE_ACT_SWIGLU)) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)c->T * c->top_k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int64_t moe_max_rows(const moe_config* c) {
+    if (moe_validate_config(c) != MOE_OK) return -1;
+    return max_rows_of(c);
+}
+
+int64_t moe_capacity(const moe_config* c) {
+    if (moe_validate_config(c) != MOE_OK) return -1;
+    return capacity_of(c);
+}
+
+moe_status moe_workspace_size(const moe_config* c, size_t* bytes) {
+    const moe_status st = moe_validate_config(c);
+    if (st != MOE_OK) return st;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    *bytes = compute_layout(c).total;
+    return MOE_OK;
+}
+
+int32_t moe_last_hip_error(void) { return g_last_hip_error; }
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+moe_status moe_route(const moe_config* c, const void* x, const moe_weights* w, int32_t* topk_idx, float* topk_gate,
+                     float* scores, const moe_stats* st, void* ws, size_t ws_bytes, void* stream) {
+    moe_status s = moe_validate_config(c);
+    if (s != MOE_OK) return s;
+    if (!w || !w->w_router) return MOE_ERR_INVALID_ARG;
+    if (c->T > 0 && (!x || !topk_idx || !topk_gate)) return MOE_ERR_INVALID_ARG;
+    if (c->gate == MOE_GATE_NOISY_TOPK) {
+        if (!w->w_noise) return MOE_ERR_INVALID_ARG;
+        if ((c->flags & MOE_F_NOISE_INPUT) && !w->noise) return MOE_ERR_INVALID_ARG;
+    }
+    if ((s = check_ws(c, ws, ws_bytes)) != MOE_OK) return s;
+    hipStream_t h = (hipStream_t)stream;
+    const Layout L = compute_layout(c);
+    const int E = c->n_experts, T = c->T;
+    const bool noisy = c->gate == MOE_GATE_NOISY_TOPK;
+    const int NC = noisy ? 2 * E : E;
+    float* dots = at<float>(ws, L.dots);
+    int32_t* status = at<int32_t>(ws, L.status);
+    moe::launch_zero_i32(status, 1, h);
+    moe::launch_router_dots(is_bf16(c), x, w->w_router, noisy ? w->w_noise : nullptr, T, c->d_model, E, NC, dots, h);
+    const float* noise = (noisy && (c->flags & MOE_F_NOISE_INPUT)) ? w->noise : nullptr;
+    moe::launch_select(dots, NC, w->logit_bias, c->gate == MOE_GATE_SIGMOID_BIAS ? w->sel_bias : nullptr, noise,
+                       c->gate, T, E, c->top_k, c->seed, c->noise_offset, topk_idx, topk_gate, scores,
+                       at<float>(ws, L.P_part), status, h);
+    moe::launch_reduce_P(at<float>(ws, L.P_part), T > 0 ? moe::select_blocks(T, E) : 0, E, T, at<float>(ws, L.P_ws),
+                         st ? st->P : nullptr, status, st ? st->device_status : nullptr, h);
+    return after_launch();
+}
+
+moe_status moe_dispatch(const moe_config* c, const void* x, const int32_t* topk_idx, void* x_perm,
+                        int32_t* expert_offsets, int32_t* perm_src, int32_t* slot_pos, const moe_stats* st, void* ws,
+                        size_t ws_bytes, void* stream) {
+    moe_status s = moe_validate_config(c);
+    if (s != MOE_OK) return s;
+    if (!expert_offsets) return MOE_ERR_INVALID_ARG;
+    if (c->T > 0 && (!x || !topk_idx || !x_perm || !perm_src || !slot_pos)) return MOE_ERR_INVALID_ARG;
+    if ((s = check_ws(c, ws, ws_bytes)) != MOE_OK) return s;
+    hipStream_t h = (hipStream_t)stream;
+    const Layout L = compute_layout(c);
+    const int E = c->n_experts;
+    const int64_t na = n_assign(c);
+    const int nb = (int)((na + moe::kAssignBlock - 1) / moe::kAssignBlock);
+    const int64_t cap = capacity_of(c);
+    int32_t* hist = at<int32_t>(ws, L.hist);
+    int32_t* bbase = at<int32_t>(ws, L.blockbase);
+    const float* P = (st && st->P) ? st->P : at<float>(ws, L.P_ws);
+    moe::launch_histogram(topk_idx, na, E, hist, h);
+    moe::launch_scan(hist, nb, E, na, cap, bbase, expert_offsets, P, st, h);
+    moe::launch_scatter(topk_idx, na, E, bbase, expert_offsets, cap, perm_src, slot_pos, h);
+    moe::launch_permute_rows(x, c->top_k, c->d_model, elem_bytes(c), perm_src, expert_offsets, E, max_rows_of(c),
+                             x_perm, h);
+    return after_launch();
+}
+
+// One grouped GEMM of an expert stack: builds the tile plan for the chosen
+// row tile, then launches.  up = true: a -> H (ReLU / SwiGLU epilogue);
+// up = false: H -> y.  With offsets == NULL the call covers one group of
+// `rows` rows (the shared expert) and the plan writes its offsets to plan_copy.
+static moe_status run_gemm(const moe_config* c, bool up, const void* a, int64_t rows, int E, const int32_t* offsets,
+                           const void* w1, const void* w3, const void* w2, int F, void* dst, int32_t* plan,
+                           int32_t* plan_copy, hipStream_t h) {
+    const bool bf = is_bf16(c);
+    const int d = c->d_model;
+    const int epi = up ? (c->act == MOE_ACT_SWIGLU ? 2 : 1) : 0;
+    const int N = up ? F : d;
+    const moe::GemmShape g = moe::pick_gemm_shape(bf, epi, rows, E, N);
+    moe::launch_tile_plan(offsets, E, (int)rows, g.BM, plan, plan_copy, h);
+    const int32_t* offs = offsets ? offsets : plan_copy;
+    const hipError_t e = up ? moe::launch_grouped_gemm(bf, epi, a, d, w1, w3, (int64_t)F * d, dst, F, F, d, E, rows,
+                                                       offs, plan, g.BM, g.BN, h)
+                            : moe::launch_grouped_gemm(bf, 0, a, F, w2, nullptr, (int64_t)d * F, dst, d, d, F, E,
+                                                       rows, offs, plan, g.BM, g.BN, h);
+    if (e != hipSuccess) return hip_status(e);
+    return after_launch();
+}
+
+static moe_status check_ffn_args(const moe_config* c, const void* a, const int32_t* offsets, const moe_weights* w,
+                                 const void* dst, bool need_up, bool need_down) {
+    if (!w || !offsets) return MOE_ERR_INVALID_ARG;
+    if (c->T > 0 && (!a || !dst)) return MOE_ERR_INVALID_ARG;
+    if (c->T > 0 && need_up && (!w->w_gate || (c->act == MOE_ACT_SWIGLU && !w->w_up))) return MOE_ERR_INVALID_ARG;
+    if (c->T > 0 && need_down && !w->w_down) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+moe_status moe_expert_up(const moe_config* c, const void* x_perm, const int32_t* expert_offsets, const moe_weights* w,
+                         void* hbuf, void* ws, size_t ws_bytes, void* stream) {
+    moe_status s = moe_validate_config(c);
+    if (s != MOE_OK) return s;
+    if ((s = check_ffn_args(c, x_perm, expert_offsets, w, hbuf, true, false)) != MOE_OK) return s;
+    if ((s = check_ws(c, ws, ws_bytes)) != MOE_OK) return s;
+    const int64_t R = max_rows_of(c);
+    if (R == 0) return MOE_OK;
+    const Layout L = compute_layout(c);
+    return run_gemm(c, true, x_perm, R, c->n_experts, expert_offsets, w->w_gate, w->w_up, nullptr, c->d_ff, hbuf,
+                    at<int32_t>(ws, L.plan_up), at<int32_t>(ws, L.plan_copy), (hipStream_t)stream);
+}
+
+moe_status moe_expert_down(const moe_config* c, const void* hbuf, const int32_t* expert_offsets, const moe_weights* w,
+                           void* y_perm, void* ws, size_t ws_bytes, void* stream) {
+    moe_status s = moe_validate_config(c);
+    if (s != MOE_OK) return s;
+    if ((s = check_ffn_args(c, hbuf, expert_offsets, w, y_perm, false, true)) != MOE_OK) return s;
+    if ((s = check_ws(c, ws, ws_bytes)) != MOE_OK) return s;
+    const int64_t R = max_rows_of(c);
+    if (R == 0) return MOE_OK;
+    const Layout L = compute_layout(c);
+    return run_gemm(c, false, hbuf, R, c->n_experts, expert_offsets, nullptr, nullptr, w->w_down, c->d_ff, y_perm,
+                    at<int32_t>(ws, L.plan_down), at<int32_t>(ws, L.plan_copy), (hipStream_t)stream);
+}
+
+moe_status moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* expert_offsets,
+                          const moe_weights* w, void* y_perm, void* ws, size_t ws_bytes, void* stream) {
+    moe_status s = moe_validate_config(c);
+    if (s != MOE_OK) return s;
+    if ((s = check_ffn_args(c, x_perm, expert_offsets, w, y_perm, true, true)) != MOE_OK) return s;
+    if ((s = check_ws(c, ws, ws_bytes)) != MOE_OK) return s;
+    const int64_t R = max_rows_of(c);
+    if (R == 0) return MOE_OK;
+    const Layout L = compute_layout(c);
+    void* H = at<void>(ws, L.H);
+    if ((s = moe_expert_up(c, x_perm, expert_offsets, w, H, ws, ws_bytes, stream)) != MOE_OK) return s;
+    return moe_expert_down(c, H, expert_offsets, w, y_perm, ws, ws_bytes, stream);
+}
+
+moe_status moe_shared_expert(const moe_config* c, const void* x, const moe_weights* w, void* shared_out, void* ws,
+                             size_t ws_bytes, void* stream) {
+    moe_status s = moe_validate_config(c);
+    if (s != MOE_OK) return s;
+    if (c->n_shared != 1) return MOE_ERR_INVALID_ARG;
+    if (!w) return MOE_ERR_INVALID_ARG;
+    if (c->T > 0 && (!x || !shared_out || !w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_INVALID_ARG;
+    if ((s = check_ws(c, ws, ws_bytes)) != MOE_OK) return s;
+    if (c->T == 0) return MOE_OK;
+    const Layout L = compute_layout(c);
+    hipStream_t h = (hipStream_t)stream;
+    void* Hs = at<void>(ws, L.Hs);
+    if ((s = run_gemm(c, true, x, c->T, 1, nullptr, w->ws_gate, w->ws_up, nullptr, c->d_ff_shared, Hs,
+                      at<int32_t>(ws, L.plan_s_up), at<int32_t>(ws, L.plan_s_copy), h)) != MOE_OK)
+        return s;
+    return run_gemm(c, false, Hs, c->T, 1, nullptr, nullptr, nullptr, w->ws_down, c->d_ff_shared, shared_out,
+                    at<int32_t>(ws, L.plan_s_down), at<int32_t>(ws, L.plan_s_copy), h);
+}
+
+moe_status moe_combine(const moe_config* c, const void* y_perm, const int32_t* slot_pos, const float* topk_gate,
+                       const void* residual, const void* shared_out, void* out, void* stream) {
+    moe_status s = moe_validate_config(c);
+    if (s != MOE_OK) return s;
+    if (c->T > 0 && (!slot_pos || !topk_gate || !out)) return MOE_ERR_INVALID_ARG;
+    if (c->T > 0 && max_rows_of(c) > 0 && !y_perm) return MOE_ERR_INVALID_ARG;
+    moe::launch_combine(y_perm, slot_pos, topk_gate, residual, shared_out, out, c->T, c->d_model, c->top_k,
+                        is_bf16(c), (hipStream_t)stream);
+    return after_launch();
+}
+
+moe_status moe_layer_forward(const moe_config* c, const moe_weights* w, const void* x, void* out,
+                             const moe_stats* st, void* ws, size_t ws_bytes, void* stream) {
+    moe_status s = moe_validate_config(c);
+    if (s != MOE_OK) return s;
+    if (!w || !w->w_router) return MOE_ERR_INVALID_ARG;
+    if (c->T > 0 && (!x || !out)) return MOE_ERR_INVALID_ARG;
+    if (c->T > 0 && (!w->w_gate || !w->w_down || (c->act == MOE_ACT_SWIGLU && !w->w_up))) return MOE_ERR_INVALID_ARG;
+    if (c->n_shared == 1 && c->T > 0 && (!w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_INVALID_ARG;
+    if (c->gate == MOE_GATE_NOISY_TOPK &&
+        (!w->w_noise || ((c->flags & MOE_F_NOISE_INPUT) && !w->noise)))
+        return MOE_ERR_INVALID_ARG;
+    if ((s = check_ws(c, ws, ws_bytes)) != MOE_OK) return s;
+    const Layout L = compute_layout(c);
+    int32_t* idx = at<int32_t>(ws, L.idx);
+    float* gates = at<float>(ws, L.gates);
+    int32_t* slot_pos = at<int32_t>(ws, L.slot_pos);
+    int32_t* perm_src = at<int32_t>(ws, L.perm_src);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    void* x_perm = at<void>(ws, L.x_perm);
+    void* y_perm = at<void>(ws, L.y_perm);
+    void* shared_out = c->n_shared ? at<void>(ws, L.shared_out) : nullptr;
+    if ((s = moe_route(c, x, w, idx, gates, nullptr, st, ws, ws_bytes, stream)) != MOE_OK) return s;
+    if ((s = moe_dispatch(c, x, idx, x_perm, offsets, perm_src, slot_pos, st, ws, ws_bytes, stream)) != MOE_OK)
+        return s;
+    if ((s = moe_expert_ffn(c, x_perm, offsets, w, y_perm, ws, ws_bytes, stream)) != MOE_OK) return s;
+    if (shared_out && (s = moe_shared_expert(c, x, w, shared_out, ws, ws_bytes, stream)) != MOE_OK) return s;
+    const void* resid = (c->flags & MOE_F_ADD_RESIDUAL) ? x : nullptr;
+    return moe_combine(c, y_perm, slot_pos, gates, resid, shared_out, out, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,371 @@
+// Route stage for gfx950: router logits, selection scores, top-k, gates and
+// router probabilities.
+//
+// The router is an inner product per (token, expert) in fp32 (CS25
+// "Lecture29" notes, section "Top-two routing": z = W_r x; CS336 lecture 4
+// notes, section 5: the router is a single inner product, and section 11:
+// computed in float32).  Because the selection is an integer decision taken on
+// these fp32 values, every dot product walks its reduction index in order with
+// one fma per step from +0 (no split-K, no MFMA whose internal summation order
+// is unspecified), and the score transforms use the canonical functions of
+// canon_math.h.  This file is compiled with -ffp-contract=off.
+//
+// Kernels
+//   k_router_dots   SIMT register-blocked tile GEMM  x[T][d] . W[NC][d]^T -> dots[T][NC]
+//                   (NC = E, or 2E for the noisy gate whose second half is x W_noise)
+//   k_select        G lanes per token: scores, k passes of a segmented arg-max,
+//                   gates, router probabilities, per-block P partial sums
+//   k_reduce_P      fixed-order sum of the per-block partials -> P[E]
+#include "device_common.h"
+#include "canon_math.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// router dot products
+// ---------------------------------------------------------------------------
+
+// Tile: BT tokens x BE columns, K staged through LDS in chunks of KC.  Thread
+// (tg, cg) owns tokens tg + (BT/TT)*a and columns cg + (BE/EE)*b.  The LDS
+// rows are padded to 36 floats so the 16-byte reads of eight different rows
+// fall in distinct banks.
+template <int TT, int EE, int BE, int NT, bool BF16>
+__global__ __launch_bounds__(NT) void k_router_dots(const void* __restrict__ x, const float* __restrict__ w0,
+                                                    const float* __restrict__ w1, int T, int d, int E, int NC,
+                                                    float* __restrict__ dots) {
+    constexpr int KC = 32, LD = KC + 4;
+    constexpr int NCG = BE / EE;          // column groups
+    constexpr int NTG = NT / NCG;         // token groups
+    constexpr int BT = NTG * TT;
+    __shared__ __align__(16) float xs[BT * LD];
+    __shared__ __align__(16) float wsh[BE * LD];
+
+    const int tid = threadIdx.x;
+    const int cg = tid % NCG, tg = tid / NCG;
+    const int t0 = blockIdx.x * BT;
+    const int c0 = blockIdx.y * BE;
+
+    float acc[TT][EE];
+#pragma unroll
+    for (int a = 0; a < TT; ++a)
+#pragma unroll
+        for (int b = 0; b < EE; ++b) acc[a][b] = 0.0f;
+
+    for (int k0 = 0; k0 < d; k0 += KC) {
+        __syncthreads();
+        for (int q = tid; q < BT * KC; q += NT) {
+            const int r = q / KC, i = q % KC;
+            const int t = min(t0 + r, T - 1);
+            xs[r * LD + i] = load_act<BF16>(x, (int64_t)t * d + k0 + i);
+        }
+        for (int q = tid; q < BE * KC; q += NT) {
+            const int r = q / KC, i = q % KC;
+            const int c = min(c0 + r, NC - 1);
+            const float* wr = c < E ? w0 + (int64_t)c * d : w1 + (int64_t)(c - E) * d;
+            wsh[r * LD + i] = wr[k0 + i];
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int i = 0; i < KC; i += 4) {
+            float4 xv[TT], wv[EE];
+#pragma unroll
+            for (int a = 0; a < TT; ++a) xv[a] = *(const float4*)&xs[(tg + NTG * a) * LD + i];
+#pragma unroll
+            for (int b = 0; b < EE; ++b) wv[b] = *(const float4*)&wsh[(cg + NCG * b) * LD + i];
+#pragma unroll
+            for (int a = 0; a < TT; ++a)
+#pragma unroll
+                for (int b = 0; b < EE; ++b) {
+                    float s = acc[a][b];
+                    s = __builtin_fmaf(xv[a].x, wv[b].x, s);
+                    s = __builtin_fmaf(xv[a].y, wv[b].y, s);
+                    s = __builtin_fmaf(xv[a].z, wv[b].z, s);
+                    s = __builtin_fmaf(xv[a].w, wv[b].w, s);
+                    acc[a][b] = s;
+                }
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < TT; ++a) {
+        const int t = t0 + tg + NTG * a;
+        if (t >= T) continue;
+#pragma unroll
+        for (int b = 0; b < EE; ++b) {
+            const int c = c0 + cg + NCG * b;
+            if (c < NC) dots[(int64_t)t * NC + c] = acc[a][b];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// selection, gates, probabilities
+// ---------------------------------------------------------------------------
+
+// Pack (score order key, expert) so that a plain unsigned max picks the
+// larger score and, on equal scores, the lower expert index.  0 is below
+// every real candidate (a NaN score still packs above 0).
+__device__ __forceinline__ uint64_t pack_cand(float key, int e) {
+    const uint32_t ok = (uint32_t)canon::order_key(key) ^ 0x80000000u;
+    return ((uint64_t)ok << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+}
+
+template <int G>
+__device__ __forceinline__ uint64_t seg_max_u64(uint64_t v) {
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) {
+        const uint64_t o = __shfl_xor(v, off, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+template <int G>
+__device__ __forceinline__ float seg_max_f(float v) {
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+template <int G>
+__device__ __forceinline__ float seg_sum_f(float v) {
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) v = v + __shfl_xor(v, off, 64);
+    return v;
+}
+
+// One pass of 256 threads handles 4 * (64 / G) tokens: lane = seg * G + g
+// covers token seg of its wave and experts g, g + G, ..., g + G (V-1).
+template <int G, int V>
+__global__ __launch_bounds__(256) void k_select(const float* __restrict__ dots, int NC, const float* __restrict__ logit_bias,
+                                                const float* __restrict__ sel_bias, const float* __restrict__ noise,
+                                                int gate, int T, int E, int k, uint64_t seed, uint64_t noise_offset,
+                                                int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+                                                float* __restrict__ scores, float* __restrict__ P_part,
+                                                int32_t* __restrict__ status) {
+    constexpr int SEGS = 64 / G;
+    constexpr int TB = 4 * SEGS;
+    __shared__ float red[4][V * G];
+
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int seg = lane / G, g = lane % G;
+    const int t = blockIdx.x * TB + wave * SEGS + seg;
+    const bool tok_ok = t < T;
+
+    float key[V], src[V], sig[V];
+    bool valid[V];
+    uint32_t taken = 0;
+    int bad = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int e = g + G * v;
+        valid[v] = tok_ok && e < E;
+        key[v] = 0.0f; src[v] = 0.0f; sig[v] = 0.0f;
+        if (!valid[v]) continue;
+        float z = dots[(int64_t)t * NC + e];
+        if (logit_bias) z = z + logit_bias[e];
+        float kv = z, sv = z;
+        if (gate == MOE_GATE_NOISY_TOPK) {
+            const float zn = dots[(int64_t)t * NC + E + e];
+            const uint64_t flat = (uint64_t)t * (uint64_t)E + (uint64_t)e;
+            const float n = noise ? noise[flat] : canon::normalc(seed, noise_offset, flat);
+            kv = __builtin_fmaf(n, canon::softplusc(zn), z);
+            sv = kv;
+        } else if (gate == MOE_GATE_SIGMOID_BIAS) {
+            const float s = canon::sigmoidc(z);
+            sig[v] = s;
+            kv = sel_bias ? s + sel_bias[e] : s;
+        }
+        key[v] = kv;
+        src[v] = sv;
+        if (!__builtin_isfinite(kv)) bad = 1;
+        if (scores) scores[(int64_t)t * E + e] = kv;
+    }
+
+    // top-k: k passes of a segmented arg-max over the experts not yet taken
+    // (loops run to the compile-time bound 16 so every array index is static)
+    float src_sel[16], sig_sel[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        src_sel[j] = 0.0f; sig_sel[j] = 0.0f;
+        if (j >= k) continue;
+        uint64_t best = 0;
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            if (valid[v] && !((taken >> v) & 1u)) {
+                const uint64_t c = pack_cand(key[v], g + G * v);
+                best = c > best ? c : best;
+            }
+        best = seg_max_u64<G>(best);
+        const int ew = (int)(0xffffffffu - (uint32_t)best);
+        const int owner_g = ew % G, vw = ew / G;
+        float s_own = 0.0f, sg_own = 0.0f;
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            if (v == vw && g == owner_g) { s_own = src[v]; sg_own = sig[v]; taken |= 1u << v; }
+        src_sel[j] = __shfl(s_own, seg * G + owner_g, 64);
+        sig_sel[j] = __shfl(sg_own, seg * G + owner_g, 64);
+        if (tok_ok && g == 0) topk_idx[(int64_t)t * k + j] = ew;
+    }
+
+    // softmax statistics over every expert (probabilities, full-softmax gate)
+    float m_all = -__builtin_inff(), s_all = 0.0f;
+    if (gate == MOE_GATE_SIGMOID_BIAS) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) if (valid[v]) s_all = s_all + sig[v];
+        s_all = seg_sum_f<G>(s_all);
+    } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v) if (valid[v]) m_all = fmaxf(m_all, src[v]);
+        m_all = seg_max_f<G>(m_all);
+#pragma unroll
+        for (int v = 0; v < V; ++v) if (valid[v]) s_all = s_all + canon::expc(src[v] - m_all);
+        s_all = seg_sum_f<G>(s_all);
+    }
+
+    // gates
+    if (tok_ok && g == 0) {
+        float gv[16];
+        if (gate == MOE_GATE_SOFTMAX_FULL) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) gv[j] = canon::expc(src_sel[j] - m_all) / s_all;
+        } else if (gate == MOE_GATE_SIGMOID_BIAS) {
+            float s = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) if (j < k) s = s + sig_sel[j];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) gv[j] = sig_sel[j] / s;
+        } else {
+            const float m = src_sel[0];
+            float s = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                gv[j] = canon::expc(src_sel[j] - m);
+                if (j < k) s = s + gv[j];
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) gv[j] = gv[j] / s;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (j < k) topk_gate[(int64_t)t * k + j] = gv[j];
+    }
+
+    // router probabilities -> per-block partial sums of P, in a fixed order
+    float pacc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        float p = 0.0f;
+        if (valid[v]) p = gate == MOE_GATE_SIGMOID_BIAS ? sig[v] / s_all : canon::expc(src[v] - m_all) / s_all;
+        pacc[v] = p;
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int off = G; off < 64; off <<= 1) pacc[v] = pacc[v] + __shfl_xor(pacc[v], off, 64);
+    if (seg == 0) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) red[wave][g + G * v] = pacc[v];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) {
+        const float s = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+        P_part[(int64_t)blockIdx.x * E + e] = s;
+    }
+    if (bad) status[0] = MOE_DEV_NONFINITE;  // benign race: every writer stores the same value
+}
+
+__global__ void k_reduce_P(const float* __restrict__ P_part, int nblocks, int E, int T, float* __restrict__ P_ws,
+                           float* __restrict__ P_out, const int32_t* __restrict__ status_ws,
+                           int32_t* __restrict__ status_out) {
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e == 0 && status_out) status_out[0] = status_ws[0];
+    if (e >= E) return;
+    float s = 0.0f;
+    for (int b = 0; b < nblocks; ++b) s = s + P_part[(int64_t)b * E + e];
+    const float p = T > 0 ? s / (float)T : 0.0f;
+    P_ws[e] = p;
+    if (P_out) P_out[e] = p;
+}
+
+__global__ void k_zero_i32(int32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+
+static int pow2_at_least(int v) { int p = 1; while (p < v) p <<= 1; return p; }
+
+template <bool BF16>
+static void launch_dots_t(const void* x, const float* w0, const float* w1, int T, int d, int E, int NC, float* dots,
+                          hipStream_t s) {
+    if (NC >= 64) {
+        dim3 grid((T + 63) / 64, (NC + 63) / 64);
+        hipLaunchKernelGGL((k_router_dots<4, 4, 64, 256, BF16>), grid, dim3(256), 0, s, x, w0, w1, T, d, E, NC, dots);
+        return;
+    }
+    const int BE = pow2_at_least(NC);
+    const int BT = 64 / BE;
+    dim3 grid((T + BT - 1) / BT, 1);
+    switch (BE) {
+#define MOE_DOTS_CASE(B) \
+    case B: hipLaunchKernelGGL((k_router_dots<1, 1, B, 64, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, NC, dots); break;
+        MOE_DOTS_CASE(1) MOE_DOTS_CASE(2) MOE_DOTS_CASE(4) MOE_DOTS_CASE(8) MOE_DOTS_CASE(16) MOE_DOTS_CASE(32)
+#undef MOE_DOTS_CASE
+    }
+}
+
+void launch_router_dots(bool bf16, const void* x, const float* w0, const float* w1, int T, int d, int E, int NC,
+                        float* dots, hipStream_t s) {
+    if (T <= 0) return;
+    if (bf16) launch_dots_t<true>(x, w0, w1, T, d, E, NC, dots, s);
+    else launch_dots_t<false>(x, w0, w1, T, d, E, NC, dots, s);
+}
+
+int select_blocks(int T, int E) {
+    const int G = E >= 64 ? 64 : pow2_at_least(E);
+    const int TB = 4 * (64 / G);
+    return (T + TB - 1) / TB;
+}
+
+void launch_select(const float* dots, int NC, const float* logit_bias, const float* sel_bias, const float* noise,
+                   int gate, int T, int E, int k, uint64_t seed, uint64_t noise_offset, int32_t* topk_idx,
+                   float* topk_gate, float* scores, float* P_part, int32_t* status, hipStream_t s) {
+    if (T <= 0) return;
+    const int G = E >= 64 ? 64 : pow2_at_least(E);
+    const int V = (E + G - 1) / G;
+    const int nb = select_blocks(T, E);
+#define MOE_SEL_ARGS dots, NC, logit_bias, sel_bias, noise, gate, T, E, k, seed, noise_offset, topk_idx, topk_gate, scores, P_part, status
+#define MOE_SEL(GG, VV) hipLaunchKernelGGL((k_select<GG, VV>), dim3(nb), dim3(256), 0, s, MOE_SEL_ARGS)
+    if (G < 64) {
+        switch (G) {
+            case 1: MOE_SEL(1, 1); break;
+            case 2: MOE_SEL(2, 1); break;
+            case 4: MOE_SEL(4, 1); break;
+            case 8: MOE_SEL(8, 1); break;
+            case 16: MOE_SEL(16, 1); break;
+            default: MOE_SEL(32, 1); break;
+        }
+    } else if (V <= 1) MOE_SEL(64, 1);
+    else if (V <= 2) MOE_SEL(64, 2);
+    else if (V <= 4) MOE_SEL(64, 4);
+    else if (V <= 8) MOE_SEL(64, 8);
+    else MOE_SEL(64, 16);
+#undef MOE_SEL
+#undef MOE_SEL_ARGS
+}
+
+void launch_reduce_P(const float* P_part, int nblocks, int E, int T, float* P_ws, float* P_out,
+                     const int32_t* status_ws, int32_t* status_out, hipStream_t s) {
+    hipLaunchKernelGGL(k_reduce_P, dim3((E + 255) / 256), dim3(256), 0, s, P_part, nblocks, E, T, P_ws, P_out,
+                       status_ws, status_out);
+}
+
+void launch_zero_i32(int32_t* p, int n, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_zero_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+}
+
+}  // namespace moe

@@ -1,0 +1,230 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small and mid-size layers are compared element by element on every stage;
+the full-size Mixtral-, DeepSeek-V3- and Shazeer-shaped layers are compared
+bit-exactly on routing and dispatch over all tokens and on sampled expert rows
+and output tokens, which the oracle computes one by one.  Tolerances are the
+ones stated in tests/gpu_helpers.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import Config
+import tests.gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+MID = {
+    # several tiles in every dimension and ragged tails everywhere
+    "rag_bf16_swiglu": Config("rag_bf16_swiglu", T=1000, d=256, F=512, E=16, k=3, act_dtype="bf16",
+                              act="swiglu", gate="softmax_topk", seed=11),
+    "rag_bf16_relu_cap": Config("rag_bf16_relu_cap", T=777, d=192, F=320, E=6, k=2, act_dtype="bf16",
+                                act="relu", gate="softmax_full", capacity_factor=1.0, residual=True, seed=12),
+    "sigmoid_shared": Config("sigmoid_shared", T=300, d=128, F=128, E=64, k=8, act_dtype="bf16", act="swiglu",
+                             gate="sigmoid_bias", n_shared=1, F_shared=192, sel_bias=True, seed=13),
+    "noisy_small": Config("noisy_small", T=500, d=64, F=128, E=40, k=4, act_dtype="bf16", act="relu",
+                          gate="noisy_topk", seed=14),
+    "f32_swiglu_mid": Config("f32_swiglu_mid", T=600, d=320, F=448, E=12, k=2, act_dtype="f32", act="swiglu",
+                             gate="softmax_topk", seed=15),
+    "many_experts": Config("many_experts", T=2000, d=64, F=64, E=1024, k=16, act_dtype="bf16", act="relu",
+                           gate="softmax_topk", seed=16),
+}
+
+
+def full_oracle(cfg, inp, noise="input", noise_offset=0):
+    return oracle.forward(cfg, inp, noise=noise, noise_offset=noise_offset)
+
+
+def check_all(cfg, g, o):
+    T = cfg.T
+    H.compare_route(cfg, g, o, T)
+    H.compare_dispatch(cfg, g, o)
+    R = o["R"]
+    np.testing.assert_array_equal(H.bytes_of(g["x_perm"][:R]), o["x_perm"].view(np.int16 if cfg.act_dtype == "bf16" else np.int32),
+                                  err_msg="x_perm bytes")
+    if R:
+        H.assert_close_rel(H.as_f64(g["y_perm"][:R]), o["y"], cfg.act_dtype, "y_perm")
+    if cfg.n_shared:
+        H.assert_close_rel(H.as_f64(g["shared"]), o["shared"], cfg.act_dtype, "shared expert")
+    return H.assert_close_rel(H.as_f64(g["out"]), o["out"], cfg.act_dtype, "out")
+
+
+@pytest.mark.parametrize("name", ["tiny", "switch"])
+def test_small_configs_every_stage(name):
+    cfg = workloads.get(name)
+    H.log(f"[parity] {name} T={cfg.T}")
+    inp = workloads.make_inputs(cfg)
+    g = H.run_stages(cfg, H.to_device(inp))
+    o = full_oracle(cfg, inp)
+    err = check_all(cfg, g, o)
+    H.log(f"[parity] {name} out rel err {err:.2e}")
+
+
+@pytest.mark.parametrize("name", list(MID))
+def test_mid_configs_every_stage(name):
+    cfg = MID[name]
+    H.log(f"[parity] {name}")
+    inp = workloads.make_inputs(cfg)
+    g = H.run_stages(cfg, H.to_device(inp))
+    o = full_oracle(cfg, inp)
+    err = check_all(cfg, g, o)
+    H.log(f"[parity] {name} out rel err {err:.2e}")
+
+
+def test_noisy_builtin_philox_stream_matches_oracle():
+    """In-kernel Philox4x32-10 + Box-Muller + canonical softplus: scores equal
+    the oracle's bit for bit, hence the same selection."""
+    cfg = MID["noisy_small"]
+    inp = workloads.make_inputs(cfg)
+    g = H.run_stages(cfg, H.to_device(inp), noise_input=False, noise_offset=7)
+    o = full_oracle(cfg, inp, noise="philox", noise_offset=7)
+    check_all(cfg, g, o)
+
+
+def test_layer_forward_equals_stages_and_is_deterministic():
+    cfg = MID["sigmoid_shared"]
+    inp = workloads.make_inputs(cfg)
+    d = H.to_device(inp)
+    g = H.run_stages(cfg, d)
+    out1, st1 = H.run_layer(cfg, d)
+    out2, st2 = H.run_layer(cfg, d)
+    np.testing.assert_array_equal(H.bytes_of(out1), H.bytes_of(g["out"]))
+    np.testing.assert_array_equal(H.bytes_of(out1), H.bytes_of(out2))
+    for k in st1:
+        np.testing.assert_array_equal(st1[k].numpy(), st2[k].numpy())
+
+
+# ---------------------------------------------------------------- edge cases
+
+EDGE = {
+    "one_token": dict(T=1),
+    "all_ties": dict(zero_router=True),
+    "single_expert": dict(E=1, k=1),
+    "k_equals_E": dict(E=4, k=4),
+    "capacity_one": dict(capacity_factor=0.01, residual=True),
+    "d64": dict(d=64, F=64),
+    "ragged_T": dict(T=257),
+}
+
+
+@pytest.mark.parametrize("case", list(EDGE))
+def test_edge_cases(case):
+    kw = dict(EDGE[case])
+    zero_router = kw.pop("zero_router", False)
+    cfg = Config("edge", T=130, d=128, F=192, E=8, k=2, act_dtype="bf16", act="swiglu", gate="softmax_topk",
+                 seed=21).replace(**kw)
+    H.log(f"[edge] {case}")
+    inp = workloads.make_inputs(cfg)
+    if zero_router:
+        inp["w_router"] = torch.zeros_like(inp["w_router"])     # every token on experts 0..k-1
+    g = H.run_stages(cfg, H.to_device(inp))
+    o = full_oracle(cfg, inp)
+    check_all(cfg, g, o)
+    if zero_router:
+        assert (g["stats"]["counts"].numpy()[cfg.k:] == 0).all()
+
+
+def test_empty_batch():
+    cfg = Config("empty", T=0, d=128, F=128, E=8, k=2, act_dtype="bf16", act="swiglu", gate="softmax_topk", seed=1)
+    inp = workloads.make_inputs(cfg.replace(T=1))
+    d = H.to_device(inp)
+    d["x"] = d["x"][:0]
+    g = H.run_stages(cfg, d)
+    assert g["out"].shape == (0, 128)
+    assert (g["offsets"].numpy() == 0).all()
+    assert (g["stats"]["counts"].numpy() == 0).all()
+    assert int(g["stats"]["n_dropped"][0]) == 0
+
+
+def test_nonfinite_input_sets_device_status():
+    cfg = Config("nan", T=64, d=64, F=64, E=8, k=2, act_dtype="f32", act="relu", gate="softmax_topk", seed=2)
+    inp = workloads.make_inputs(cfg)
+    inp["x"][5, 3] = float("nan")
+    g = H.run_stages(cfg, H.to_device(inp))
+    assert int(g["stats"]["device_status"][0]) == 1
+    o = oracle.route(cfg, inp["x"], inp["w_router"])
+    assert o["status"] == 1
+    np.testing.assert_array_equal(g["idx"].numpy(), o["idx"])
+
+
+# ---------------------------------------------------------------- full sizes, sampled
+
+def _sampled_full_size(name, n_tokens=12, rows_per_expert=2, max_experts=24, noise_input=True):
+    cfg = workloads.get(name)
+    H.log(f"[full] {name}: drawing inputs on the GPU")
+    dinp = workloads.make_inputs(cfg, device="cuda")
+    g = H.run_stages(cfg, dinp, noise_input=noise_input)
+    H.log(f"[full] {name}: GPU path done, oracle route/dispatch over all {cfg.T} tokens")
+    x = dinp["x"].cpu()
+    o = oracle.route(cfg, x, dinp["w_router"].cpu(),
+                     logit_bias=dinp["logit_bias"].cpu() if "logit_bias" in dinp else None,
+                     sel_bias=dinp["sel_bias"].cpu() if "sel_bias" in dinp else None,
+                     w_noise=dinp["w_noise"].cpu() if "w_noise" in dinp else None,
+                     noise=dinp["noise"].cpu() if (noise_input and "noise" in dinp) else None)
+    o.update(oracle.dispatch(cfg, o["idx"]))
+    o.update(oracle.stats(cfg, o["counts"], o["kept"], o["P"], cfg.T))
+    o["status"] = 0
+    H.compare_route(cfg, g, o, cfg.T)
+    H.compare_dispatch(cfg, g, o)
+    R = o["R"]
+    xp = oracle.gather_rows(cfg, x, o["perm_src"])
+    np.testing.assert_array_equal(H.bytes_of(g["x_perm"][:R]), xp.view(np.int16))
+    H.log(f"[full] {name}: routing and dispatch bit-exact; sampling expert rows")
+    rng = np.random.default_rng(0)
+    off = o["offsets"]
+    experts = [e for e in range(cfg.E) if off[e + 1] > off[e]]
+    experts = sorted(rng.choice(experts, size=min(max_experts, len(experts)), replace=False).tolist())
+
+    def weights(e):
+        return oracle.expert_weights(cfg, {k: v for k, v in dinp.items() if k.startswith("w")}, e)
+
+    y_ref, y_got = [], []
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows = sorted(set([lo, hi - 1] + rng.integers(lo, hi, size=rows_per_expert).tolist()))
+        y_ref.append(oracle.expert_ffn(cfg, xp[rows], *weights(e)))
+        y_got.append(H.as_f64(g["y_perm"][rows]))
+    err_y = H.assert_close_rel(np.concatenate(y_got), np.concatenate(y_ref), cfg.act_dtype, "sampled y_perm")
+    H.log(f"[full] {name}: sampled y rel err {err_y:.2e}; sampling output tokens")
+    tokens = np.sort(rng.choice(cfg.T, size=n_tokens, replace=False)).astype(np.int32)
+    sp = o["slot_pos"][tokens]
+    need = sorted(set(int(r) for r in sp.reshape(-1) if r >= 0))
+    compact = {r: i for i, r in enumerate(need)}
+    y_c = np.zeros((len(need), cfg.d))
+    ends = off[1:]
+    for r in need:
+        e = int(np.searchsorted(ends, r, side="right"))
+        y_c[compact[r]] = oracle.expert_ffn(cfg, xp[[r]], *weights(e))[0]
+    sp_c = np.where(sp >= 0, np.vectorize(lambda r: compact.get(int(r), -1))(sp), -1).astype(np.int32)
+    shared = None
+    if cfg.n_shared:
+        shared = oracle.expert_ffn(cfg, x[torch.from_numpy(tokens).long()], *oracle.shared_weights(dinp),
+                                   F=cfg.F_shared)
+        H.assert_close_rel(H.as_f64(g["shared"][torch.from_numpy(tokens).long()]), shared, cfg.act_dtype,
+                           "sampled shared expert")
+    out_ref = oracle.combine(cfg, sp_c, o["gates"][tokens], y_c, x[torch.from_numpy(tokens).long()],
+                             shared=shared)
+    err = H.assert_close_rel(H.as_f64(g["out"][torch.from_numpy(tokens).long()]), out_ref, cfg.act_dtype,
+                             "sampled out")
+    H.log(f"[full] {name}: sampled out rel err {err:.2e}")
+
+
+def test_full_size_mixtral_sampled():
+    _sampled_full_size("mixtral", max_experts=8, rows_per_expert=3)
+
+
+def test_full_size_dsv3_sampled():
+    _sampled_full_size("dsv3", n_tokens=6, max_experts=16, rows_per_expert=1)
+
+
+def test_full_size_noisy_sampled():
+    _sampled_full_size("noisy", n_tokens=24, max_experts=32, rows_per_expert=2)
+
+
+def test_full_size_noisy_philox_routing():
+    _sampled_full_size("noisy", n_tokens=8, max_experts=8, rows_per_expert=1, noise_input=False)
