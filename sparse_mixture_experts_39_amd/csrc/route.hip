@@ -26,25 +26,81 @@ namespace moe {
 // router dot products
 // ---------------------------------------------------------------------------
 
-// Tile: BT tokens x BE columns, K staged through LDS in chunks of KC.  Thread
-// (tg, cg) owns tokens tg + (BT/TT)*a and columns cg + (BE/EE)*b.  The LDS
-// rows are padded to 36 floats so the 16-byte reads of eight different rows
-// fall in distinct banks.
-template <int TT, int EE, int BE, int NT, bool BF16>
+// Tile: BT tokens x BE columns, K staged through LDS in chunks of KC
+// (double buffered; the next chunk's global loads are in flight while the
+// current chunk is consumed).  Thread (tg, cg) owns tokens tg + NTG*a and
+// columns cg + NCG*b; for every output it walks i = 0..d-1 in order with one
+// fma per step.  LDS rows are padded by 4 floats so the 16-byte reads of
+// eight different rows fall in distinct banks.
+template <int TT, int EE, int BE, int NT, int KC, bool BF16>
 __global__ __launch_bounds__(NT) void k_router_dots(const void* __restrict__ x, const float* __restrict__ w0,
                                                     const float* __restrict__ w1, int T, int d, int E, int NC,
                                                     float* __restrict__ dots) {
-    constexpr int KC = 32, LD = KC + 4;
+    constexpr int LD = KC + 4;
     constexpr int NCG = BE / EE;          // column groups
     constexpr int NTG = NT / NCG;         // token groups
     constexpr int BT = NTG * TT;
-    __shared__ __align__(16) float xs[BT * LD];
-    __shared__ __align__(16) float wsh[BE * LD];
+    constexpr int XV = BF16 ? 8 : 4;      // x elements per 16-byte load
+    constexpr int XCH = BT * KC / XV;     // 16-byte x chunks per K chunk
+    constexpr int WCH = BE * KC / 4;      // 16-byte w chunks per K chunk
+    constexpr int XPT = (XCH + NT - 1) / NT, WPT = (WCH + NT - 1) / NT;
+    __shared__ __align__(16) float xs[2][BT * LD];
+    __shared__ __align__(16) float wsh[2][BE * LD];
 
     const int tid = threadIdx.x;
     const int cg = tid % NCG, tg = tid / NCG;
     const int t0 = blockIdx.x * BT;
     const int c0 = blockIdx.y * BE;
+
+    u32x4_t rx[XPT], rw[WPT];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int q = 0; q < XPT; ++q) {
+            const int ch = tid + q * NT;
+            if (ch < XCH) {
+                const int r = ch / (KC / XV), i = (ch % (KC / XV)) * XV;
+                const int t = min(t0 + r, T - 1);
+                rx[q] = *(const u32x4_t*)((const uint8_t*)x + ((int64_t)t * d + k0 + i) * (BF16 ? 2 : 4));
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < WPT; ++q) {
+            const int ch = tid + q * NT;
+            if (ch < WCH) {
+                const int r = ch / (KC / 4), i = (ch % (KC / 4)) * 4;
+                const int c = min(c0 + r, NC - 1);
+                const float* wr = c < E ? w0 + (int64_t)c * d : w1 + (int64_t)(c - E) * d;
+                rw[q] = *(const u32x4_t*)(wr + k0 + i);
+            }
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < XPT; ++q) {
+            const int ch = tid + q * NT;
+            if (ch < XCH) {
+                const int r = ch / (KC / XV), i = (ch % (KC / XV)) * XV;
+                float* dst = &xs[buf][r * LD + i];
+                if constexpr (BF16) {
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        dst[2 * h] = bf16_bits_to_f32(rx[q][h] & 0xffffu);
+                        dst[2 * h + 1] = bf16_bits_to_f32(rx[q][h] >> 16);
+                    }
+                } else {
+                    *(u32x4_t*)dst = rx[q];
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < WPT; ++q) {
+            const int ch = tid + q * NT;
+            if (ch < WCH) {
+                const int r = ch / (KC / 4), i = (ch % (KC / 4)) * 4;
+                *(u32x4_t*)&wsh[buf][r * LD + i] = rw[q];
+            }
+        }
+    };
 
     float acc[TT][EE];
 #pragma unroll
@@ -52,39 +108,34 @@ __global__ __launch_bounds__(NT) void k_router_dots(const void* __restrict__ x, 
 #pragma unroll
         for (int b = 0; b < EE; ++b) acc[a][b] = 0.0f;
 
-    for (int k0 = 0; k0 < d; k0 += KC) {
-        __syncthreads();
-        for (int q = tid; q < BT * KC; q += NT) {
-            const int r = q / KC, i = q % KC;
-            const int t = min(t0 + r, T - 1);
-            xs[r * LD + i] = load_act<BF16>(x, (int64_t)t * d + k0 + i);
-        }
-        for (int q = tid; q < BE * KC; q += NT) {
-            const int r = q / KC, i = q % KC;
-            const int c = min(c0 + r, NC - 1);
-            const float* wr = c < E ? w0 + (int64_t)c * d : w1 + (int64_t)(c - E) * d;
-            wsh[r * LD + i] = wr[k0 + i];
-        }
-        __syncthreads();
-#pragma unroll 2
+    const int nch = d / KC;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < nch) load((c + 1) * KC);
+#pragma unroll 4
         for (int i = 0; i < KC; i += 4) {
             float4 xv[TT], wv[EE];
 #pragma unroll
-            for (int a = 0; a < TT; ++a) xv[a] = *(const float4*)&xs[(tg + NTG * a) * LD + i];
+            for (int a = 0; a < TT; ++a) xv[a] = *(const float4*)&xs[buf][(tg + NTG * a) * LD + i];
 #pragma unroll
-            for (int b = 0; b < EE; ++b) wv[b] = *(const float4*)&wsh[(cg + NCG * b) * LD + i];
+            for (int b = 0; b < EE; ++b) wv[b] = *(const float4*)&wsh[buf][(cg + NCG * b) * LD + i];
 #pragma unroll
             for (int a = 0; a < TT; ++a)
 #pragma unroll
                 for (int b = 0; b < EE; ++b) {
-                    float s = acc[a][b];
-                    s = __builtin_fmaf(xv[a].x, wv[b].x, s);
-                    s = __builtin_fmaf(xv[a].y, wv[b].y, s);
-                    s = __builtin_fmaf(xv[a].z, wv[b].z, s);
-                    s = __builtin_fmaf(xv[a].w, wv[b].w, s);
-                    acc[a][b] = s;
+                    float sacc = acc[a][b];
+                    sacc = __builtin_fmaf(xv[a].x, wv[b].x, sacc);
+                    sacc = __builtin_fmaf(xv[a].y, wv[b].y, sacc);
+                    sacc = __builtin_fmaf(xv[a].z, wv[b].z, sacc);
+                    sacc = __builtin_fmaf(xv[a].w, wv[b].w, sacc);
+                    acc[a][b] = sacc;
                 }
         }
+        if (c + 1 < nch) store(buf ^ 1);
+        __syncthreads();
     }
 #pragma unroll
     for (int a = 0; a < TT; ++a) {
@@ -304,15 +355,25 @@ static void launch_dots_t(const void* x, const float* w0, const float* w1, int T
                           hipStream_t s) {
     if (NC >= 64) {
         dim3 grid((T + 63) / 64, (NC + 63) / 64);
-        hipLaunchKernelGGL((k_router_dots<4, 4, 64, 256, BF16>), grid, dim3(256), 0, s, x, w0, w1, T, d, E, NC, dots);
+        hipLaunchKernelGGL((k_router_dots<4, 4, 64, 256, 64, BF16>), grid, dim3(256), 0, s, x, w0, w1, T, d, E, NC,
+                           dots);
         return;
     }
     const int BE = pow2_at_least(NC);
     const int BT = 64 / BE;
     dim3 grid((T + BT - 1) / BT, 1);
+    // K chunks of 128 when d allows it, else 64 (d is a multiple of 64)
+    const bool k128 = d % 128 == 0;
     switch (BE) {
-#define MOE_DOTS_CASE(B) \
-    case B: hipLaunchKernelGGL((k_router_dots<1, 1, B, 64, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, NC, dots); break;
+#define MOE_DOTS_CASE(B)                                                                                        \
+    case B:                                                                                                     \
+        if (k128)                                                                                               \
+            hipLaunchKernelGGL((k_router_dots<1, 1, B, 64, 128, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, \
+                               NC, dots);                                                                       \
+        else                                                                                                    \
+            hipLaunchKernelGGL((k_router_dots<1, 1, B, 64, 64, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E,  \
+                               NC, dots);                                                                       \
+        break;
         MOE_DOTS_CASE(1) MOE_DOTS_CASE(2) MOE_DOTS_CASE(4) MOE_DOTS_CASE(8) MOE_DOTS_CASE(16) MOE_DOTS_CASE(32)
 #undef MOE_DOTS_CASE
     }
