@@ -109,8 +109,8 @@ def cpu_baseline(cfg, dinp, target_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -12,21 +12,22 @@
 //
 // Kernel design (one kernel template, k_grouped_gemm):
 //   * 256 threads = 4 waves in a 2x2 grid; a block computes a BM x BN tile,
-//     each wave a (BM/2) x (BN/2) tile of 16x16 MFMA blocks.
+//     each wave a (BM/2) x (BN/2) tile of MFMA blocks.
 //   * MFMA operand order: the weights are source 0 and the activations
 //     source 1, so the accumulator lanes hold 4 consecutive output columns of
 //     one row and the epilogue stores 8 (bf16) or 16 (fp32) bytes per lane.
-//   * bf16 uses v_mfma_f32_16x16x32_bf16 (one 16-byte fragment per lane = 8 k
+//   * bf16 uses v_mfma_f32_32x32x16_bf16 (one 16-byte fragment per lane = 8 k
 //     values); fp32 uses four v_mfma_f32_16x16x4_f32 per 16-byte fragment.
 //     The k positions inside a fragment are the same for both operands, so
 //     the product is exact whatever order the unit visits them in.
-//   * K is staged through LDS in 128-byte rows (64 bf16 / 32 fp32 values),
-//     double buffered, one barrier per K step.  The tiles move with gfx950's
-//     direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds), so no VGPRs
-//     hold staged data; the loads for step k+1 are in flight during the
-//     MFMAs of step k.
-//     16-byte chunks are XOR swizzled by (r ^ (r >> 3)) & 7 so fragment
-//     reads of 8 or 16 consecutive rows hit distinct banks.
+//   * K is staged through LDS in slices of 128-byte rows (64 bf16 / 32 fp32
+//     values): one direct-to-LDS buffer load (buffer_load_dwordx4 ... lds)
+//     of a wave moves 8 rows x 128 bytes, i.e. whole 128-byte lines, with no
+//     VGPR staging.  A and B slices live in two rings of NA and NB slots that
+//     fill the 160 KB of LDS; one barrier per slice; the loads of later
+//     slices are in flight while the MFMAs consume the current one.
+//     16-byte chunks are XOR swizzled by (r >> 1) & 7 so the fragment reads of
+//     16 consecutive rows at one logical chunk hit distinct banks.
 //   * Ragged M: the tile plan holds prefix sums of ceil(M_e / BM); a block
 //     finds its expert by binary search, so no host synchronisation is
 //     needed.  Rows past the expert's end are loaded from its last row and
@@ -60,13 +61,68 @@ struct GemmParams {
     int K;
     int E;
     int NT;                 // N tiles
+    int nk;                 // K slices of 128-byte rows
     const int32_t* offsets; // [E+1]
-    const int32_t* tile_prefix;  // [E+1]
+    const int32_t* plan;    // [E+1] tile prefix over experts, then full, split, tail
+    float* partial;         // split-K partial accumulators
 };
 
-// XOR swizzle of the four 16-byte chunks of a 64-byte LDS row: fragment reads
-// of 8 or 16 consecutive rows at one logical chunk land in distinct banks.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Work decomposition.  The plan lists ceil(M_e / BM) row tiles per expert,
+// each with NT column tiles, T tiles in all.  When the last round of tiles
+// would leave the chip mostly idle (T mod kSplitUnits <= kSplitUnits / 2) and
+// that round is a large share of the launch (T < 4 kSplitUnits), those `tail`
+// tiles are cut into `split` K ranges each, one block per range:
+// every block writes its fp32 partial accumulators, and k_split_fixup adds
+// the ranges of a tile in a fixed order and applies the epilogue, so results
+// do not depend on timing.  kSplitUnits is the CU count of the target chip.
+constexpr int kSplitUnits = 256;
+constexpr int kMaxSplit = 16;
+
+// Tile L of the natural order: experts in order; inside an expert, groups of
+// NG column tiles, row tiles fastest inside a group.
+__device__ __forceinline__ void decode_tile(const GemmParams& p, int L, int& e, int& mt, int& nt) {
+    const int NT = p.NT;
+    int lo = 0, hi = p.E;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.plan[mid] * NT <= L) lo = mid; else hi = mid;
+    }
+    e = lo;
+    const int tiles_e = p.plan[e + 1] - p.plan[e];
+    const int local = L - p.plan[e] * NT;
+    constexpr int NG = 8;
+    const int grp = local / (tiles_e * NG);
+    const int inside = local - grp * tiles_e * NG;
+    mt = inside % tiles_e;
+    nt = grp * NG + inside / tiles_e;
+}
+
+// XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row.  LDS serves
+// 16 lanes of a 16-byte read per pass: rows r .. r+15 at one logical chunk
+// then cover every (row parity, physical chunk) pair, i.e. 16 distinct
+// 16-byte bank groups.  Depends on r mod 16 only.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+// Ring depths of the A and B slices.  Batch j (issued after the barrier of
+// slice j) loads A slice j + NA and B slice j + NB, in that order; before that
+// barrier a wave waits until slice j + 1 has landed, which leaves `wait`
+// of its own loads in flight (`wait0` before the first slice).  NB is NA or
+// NA + 1; the depths maximise `wait` within 160 KB of LDS.
+struct RingDepth {
+    int na, nb, wait, wait0, bytes;
+};
+constexpr RingDepth ring_depth(int BM, int BN) {
+    const int SA = BM * 128, SB = BN * 128, ga = BM / 32, gb = BN / 32;
+    RingDepth best{2, 2, 0, ga + gb, 2 * (SA + SB)};
+    for (int na = 2; na <= 16; ++na)
+        for (int nb = na; nb <= na + 1; ++nb) {
+            const int bytes = na * SA + nb * SB;
+            if (bytes > 160 * 1024) continue;
+            const int w = (nb == na ? 0 : gb) + (na - 2) * (ga + gb);
+            if (w > best.wait || (w == best.wait && bytes < best.bytes)) best = {na, nb, w, w + ga + gb, bytes};
+        }
+    return best;
+}
 
 // s_waitcnt vmcnt(n) for a compile-time n (other counters left alone).
 template <int N>
@@ -84,43 +140,163 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Epilogue of one wave's accumulators (shared by the GEMM and the split-K
+// fixup).
 template <bool BF16, int BM, int BN, int EPI>
+struct GemmEpilogue {
+    static constexpr int WM = BM / 2, WN = BN / 2;
+    static constexpr int MB = BF16 ? 32 : 16;
+    static constexpr int FM = WM / MB, FN = WN / MB;
+    static constexpr int RA = BF16 ? 16 : 4;   // accumulator registers per MFMA block
+    typedef typename std::conditional<BF16, floatx16_t, floatx4_t>::type acc_t;
+
+    // float4 index of partial element (i, j, 4*r4 .. 4*r4+3) of wave w, unit u
+    __device__ static int64_t partial_index(int u, int w, int i, int j, int r4, int lane) {
+        return (((((int64_t)u * 4 + w) * FN + i) * FM + j) * (RA / 4) + r4) * 64 + lane;
+    }
+
+    __device__ static void store_partial(const GemmParams& p, const acc_t (&acc)[FN][FM], int u, int w, int lane) {
+        float4* dst = (float4*)p.partial;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int r4 = 0; r4 < RA / 4; ++r4)
+                    dst[partial_index(u, w, i, j, r4, lane)] =
+                        make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
+    }
+
+    __device__ static void store(const GemmParams& p, const acc_t (&acc)[FN][FM], int row0, int rows, int nt, int wm,
+                                 int wn, int lane) {
+            // Output tile.  bf16 blocks (32x32): lane l, element r = 4q + t holds
+        // D[n = 8q + 4(l/32) + t][m = l % 32].  fp32 blocks (16x16): element t
+        // holds D[n = 4(l/16) + t][m = l % 16].  Either way a lane owns 4
+        // consecutive output columns of one row per (q) and stores them at once.
+        auto store4 = [&](int m, int64_t col, const float* v) {
+            const int64_t o = (int64_t)(row0 + m) * p.ldc + col;
+            if constexpr (BF16) {
+                uint2 w;
+                w.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+                w.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                *(uint2*)((uint16_t*)p.C + o) = w;
+            } else {
+                *(float4*)((float*)p.C + o) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        };
+        auto silu_mul = [](float gt, float up) { return gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up; };
+        if constexpr (BF16) {
+            const int h = lane >> 5;
+    #pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                const int m = wm * WM + j * 32 + (lane & 31);
+                if (m >= rows) continue;
+    #pragma unroll
+                for (int i = 0; i < FN; ++i) {
+                    const int blk = wn * (WN / 32) + i;              // 32-row block of the B tile
+                    if constexpr (EPI == EPI_SWIGLU) {
+                        // rows 0-15 of the block are gate units, rows 16-31 the
+                        // up units of the same 16 hidden units: q and q+2 pair up
+    #pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            float v[4];
+    #pragma unroll
+                            for (int t = 0; t < 4; ++t) v[t] = silu_mul(acc[i][j][4 * q + t], acc[i][j][4 * (q + 2) + t]);
+                            store4(m, (int64_t)nt * (BN / 2) + blk * 16 + 8 * q + 4 * h, v);
+                        }
+                    } else {
+    #pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            float v[4];
+    #pragma unroll
+                            for (int t = 0; t < 4; ++t) {
+                                float x = acc[i][j][4 * q + t];
+                                if constexpr (EPI == EPI_RELU) x = fmaxf(x, 0.0f);
+                                v[t] = x;
+                            }
+                            store4(m, (int64_t)nt * BN + blk * 32 + 8 * q + 4 * h, v);
+                        }
+                    }
+                }
+            }
+        } else {
+            const int lg = lane >> 4;
+    #pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                const int m = wm * WM + j * 16 + (lane & 15);
+                if (m >= rows) continue;
+                if constexpr (EPI == EPI_SWIGLU) {
+    #pragma unroll
+                    for (int pi = 0; pi < FN / 2; ++pi) {
+                        const int fblock = (wn * FN + 2 * pi) >> 1;    // 16-row blocks alternate gate / up
+                        float v[4];
+    #pragma unroll
+                        for (int t = 0; t < 4; ++t) v[t] = silu_mul(acc[2 * pi][j][t], acc[2 * pi + 1][j][t]);
+                        store4(m, (int64_t)nt * (BN / 2) + fblock * 16 + 4 * lg, v);
+                    }
+                } else {
+    #pragma unroll
+                    for (int i = 0; i < FN; ++i) {
+                        float v[4];
+    #pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            float x = acc[i][j][t];
+                            if constexpr (EPI == EPI_RELU) x = fmaxf(x, 0.0f);
+                            v[t] = x;
+                        }
+                        store4(m, (int64_t)nt * BN + wn * WN + i * 16 + 4 * lg, v);
+                    }
+                }
+            }
+        }
+    }
+};
+
+template <bool BF16, int BM, int BN, int EPI, bool SPLIT>
 __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int MB = BF16 ? 32 : 16;        // MFMA block edge (32x32x16 bf16, 16x16x4 fp32)
     constexpr int FM = WM / MB, FN = WN / MB;
     constexpr int ES = BF16 ? 2 : 4;
-    constexpr int KT = 64 / ES;               // K elements per stage (64-byte rows)
-    constexpr int NS = 4;                     // pipeline stages
-    constexpr int STAGE = (BM + BN) * 64;     // bytes per stage
-    constexpr int KS = BF16 ? 2 : 1;          // MFMA k-steps per stage
-    typedef typename std::conditional<BF16, floatx16_t, floatx4_t>::type acc_t;
+    constexpr int KS = BF16 ? 2 : 1;          // fragments per 32-row block per half slice
+    constexpr int SA = BM * 128, SB = BN * 128;
+    constexpr RingDepth RD = ring_depth(BM, BN);
+    constexpr int NA = RD.na, NB = RD.nb;
+    constexpr int GA = BM / 8, GB = BN / 8;   // 1 KB load groups: 8 rows x 128 bytes
+    constexpr int ga = GA / 4, gb = GB / 4;   // groups per wave
+    typedef GemmEpilogue<BF16, BM, BN, EPI> Epi;
+    typedef typename Epi::acc_t acc_t;
     static_assert(FM >= 1 && FN >= 1, "tile smaller than one MFMA block");
     static_assert(BF16 || EPI != EPI_SWIGLU || (FN % 2) == 0, "SwiGLU pairs 16-row blocks");
-    __shared__ __align__(16) uint8_t lds[NS * STAGE];
+    static_assert(RD.wait0 < 64 && RD.bytes <= 160 * 1024, "ring exceeds vmcnt or LDS");
+    __shared__ __align__(16) uint8_t lds[RD.bytes];
 
-    // ---- tile decode (device-side ragged plan, XCD-contiguous ranges)
-    const int NT = p.NT;
-    const int total = p.tile_prefix[p.E] * NT;
-    const int per_xcd = (total + 7) / 8;
-    const int slot = blockIdx.x / 8;
-    if (slot >= per_xcd) return;
-    const int L = (blockIdx.x % 8) * per_xcd + slot;
-    if (L >= total) return;
-    int lo = 0, hi = p.E;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.tile_prefix[mid] * NT <= L) lo = mid; else hi = mid;
+    // ---- work unit.  Whole tiles (SPLIT = false): block ids are dealt
+    // round-robin to the 8 XCDs, so tiles are remapped to give each XCD a
+    // contiguous range (its blocks share weight and activation panels in its
+    // L2).  Split units (SPLIT = true, a launch of its own): block u is unit
+    // u, range u % split of tail tile u / split.
+    const int total = p.plan[p.E] * p.NT;
+    const int full = p.plan[p.E + 1], split = p.plan[p.E + 2], tail = p.plan[p.E + 3];
+    int L, k0 = 0, k1 = p.nk, unit = -1;
+    if constexpr (!SPLIT) {
+        const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+        const int per_xcd = split > 1 ? full / 8 : (total + 7) / 8;
+        if (slot >= per_xcd) return;
+        L = xcd * per_xcd + slot;
+        if (L >= total) return;
+    } else {
+        if (split <= 1) return;
+        unit = blockIdx.x;
+        if (unit >= tail * split) return;
+        L = full + unit / split;
+        const int c = unit % split;
+        k0 = c * p.nk / split;
+        k1 = (c + 1) * p.nk / split;
     }
-    const int e = lo;
-    const int tiles_e = p.tile_prefix[e + 1] - p.tile_prefix[e];
-    const int local = L - p.tile_prefix[e] * NT;
-    constexpr int NG = 8;
-    const int grp = local / (tiles_e * NG);
-    const int inside = local - grp * tiles_e * NG;
-    const int mt = inside % tiles_e;
-    const int nt = grp * NG + inside / tiles_e;
+    int e, mt, nt;
+    decode_tile(p, L, e, mt, nt);
     const int row0 = p.offsets[e] + mt * BM;
     const int rows = min(BM, p.offsets[e + 1] - row0);
 
@@ -128,16 +304,14 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
     const int wm = wave >> 1, wn = wave & 1;
 
-    // ---- direct-to-LDS loads.  A stage holds the A rows then the B rows of
-    // one K slice, 64 bytes per row, filled in 1 KB groups of 16 rows; one
-    // buffer_load_dwordx4 ... lds of a wave fills one group, lane l landing
-    // at byte 16*l, i.e. row 16*g + l/4, physical chunk l%4.  The lane
-    // fetches logical chunk (l%4) ^ swz(row): the swizzle is applied on the
-    // global side.  Addresses are buffer descriptors (SGPRs) holding the
-    // tile's base and extent, a 32-bit lane offset, and the K offset in an
-    // SGPR; a read past the extent returns zeros instead of touching memory.
-    constexpr int GA = BM / 16, GB = BN / 16, GPW = (GA + GB) / 4;  // groups per wave
-    static_assert((GA + GB) % 4 == 0, "groups split evenly over 4 waves");
+    // ---- direct-to-LDS loads.  Slot layout: NA A slots of BM rows, then NB B
+    // slots of BN rows, 128 bytes per row.  One buffer_load_dwordx4 ... lds of
+    // a wave fills a 1 KB group: lane l lands at byte 16*l, i.e. row
+    // 8*g + l/8, physical chunk l%8, and fetches logical chunk (l%8) ^ swz(row)
+    // (the swizzle is applied on the global side).  Each wave loads ga A
+    // groups and gb B groups of every slice.  Addresses are buffer descriptors
+    // (SGPRs) holding the tile's base and extent, a 32-bit lane offset, and
+    // the K offset in an SGPR.
     constexpr int kRsrcWord3 = 0x00020000;
     const int64_t brow_base = EPI == EPI_SWIGLU ? (int64_t)nt * (BN / 2) : (int64_t)nt * BN;
     const int b_rows = EPI == EPI_SWIGLU ? BN / 2 : BN;
@@ -150,44 +324,41 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     const __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const uint8_t*)(EPI == EPI_SWIGLU ? p.B1 : p.B0) + boff), (short)0,
         (int)((int64_t)b_rows * p.K * ES), kRsrcWord3);
-    uint32_t voff[GPW];
-    int src_of[GPW];  // 0: A, 1: B0, 2: B1 (wave-uniform)
+    uint32_t voffA[ga], voffB[gb];
 #pragma unroll
-    for (int q = 0; q < GPW; ++q) {
-        const int g = wave * GPW + q;
-        if (g < GA) {
-            const int r = 16 * g + (lane >> 2);
-            const int lc = (lane & 3) ^ swz(r);
-            src_of[q] = 0;
-            voff[q] = (uint32_t)(min(r, rows - 1) * (int)p.lda * ES + lc * 16);
-        } else {
-            const int j = g - GA;                          // 16-row block of B
-            const int r = 16 * j + (lane >> 2);
-            const int lc = (lane & 3) ^ swz(r);
-            int rr;
-            if constexpr (EPI == EPI_SWIGLU) {
-                src_of[q] = (j & 1) ? 2 : 1;               // gate / up blocks alternate
-                rr = (j >> 1) * 16 + (lane >> 2);
-            } else {
-                src_of[q] = 1;
-                rr = r;
-            }
-            voff[q] = (uint32_t)(rr * p.K * ES + lc * 16);
-        }
+    for (int q = 0; q < ga; ++q) {
+        const int r = 8 * (wave * ga + q) + (lane >> 3);
+        voffA[q] = (uint32_t)(min(r, rows - 1) * (int)p.lda * ES + (((lane & 7) ^ swz(r)) << 4));
+    }
+#pragma unroll
+    for (int q = 0; q < gb; ++q) {
+        const int g = wave * gb + q;
+        const int r = 8 * g + (lane >> 3);
+        // SwiGLU: 16-row block j of the tile is rows (j/2)*16 .. +15 of W1 (j
+        // even) or W3 (j odd)
+        const int rr = EPI == EPI_SWIGLU ? ((g >> 2) * 16 + (r & 15)) : r;
+        voffB[q] = (uint32_t)(rr * p.K * ES + (((lane & 7) ^ swz(r)) << 4));
     }
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
-    auto issue = [&](int kt, int stage) {
-        const int koff = kt * 64;
+    const int nk = k1 - k0;
+    // virtual slice v goes to slot v % N; slices past the end reload the last
+    // one into a free slot (nobody reads it), which keeps the per-wave load
+    // count of every batch the same
+    auto issueA = [&](int v) {
+        uint8_t* dst = &lds[(v % NA) * SA + wave * ga * 1024];
+        const int koff = (k0 + min(v, nk - 1)) * 128;
 #pragma unroll
-        for (int q = 0; q < GPW; ++q) {
-            const int g = wave * GPW + q;
-            lds_ptr_t dst = (lds_ptr_t)(&lds[stage * STAGE + g * 1024]);
-            if (src_of[q] == 0)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, dst, 16, voff[q], koff, 0, 0);
-            else if (src_of[q] == 1)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB0, dst, 16, voff[q], koff, 0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB1, dst, 16, voff[q], koff, 0, 0);
+        for (int q = 0; q < ga; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)(dst + q * 1024), 16, voffA[q], koff, 0, 0);
+    };
+    auto issueB = [&](int v) {
+        uint8_t* dst = &lds[NA * SA + (v % NB) * SB + wave * gb * 1024];
+        const int koff = (k0 + min(v, nk - 1)) * 128;
+#pragma unroll
+        for (int q = 0; q < gb; ++q) {
+            const bool up = EPI == EPI_SWIGLU && (((wave * gb + q) >> 1) & 1);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? rsB1 : rsB0, (lds_ptr_t)(dst + q * 1024), 16, voffB[q],
+                                                     koff, 0, 0);
         }
     };
 
@@ -199,31 +370,36 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
 #pragma unroll
             for (int r = 0; r < (BF16 ? 16 : 4); ++r) acc[i][j][r] = 0.0f;
 
-    // Fragment reads.  bf16 (32x32x16): lane l takes row l % 32 of a 32-row
-    // block at chunk 2*s + l/32 for k-step s (8 k values per lane).  fp32
-    // (16x16x4): lane l takes row l % 16 at chunk l/16 (4 k values, four
-    // MFMAs).  Weights are MFMA source 0 (rows = output columns n),
-    // activations source 1 (columns = token rows m).
-    constexpr int NF = KS * (FM + FN);       // fragments per stage
-    int f_off[NF];
+    // Fragment reads, per half slice h (64 bytes of K).  bf16 (32x32x16):
+    // lane l takes row l % 32 of a 32-row block at logical chunk
+    // 4h + 2s + l/32 for k-step s (8 k values per lane).  fp32 (16x16x4):
+    // lane l takes row l % 16 at chunk 4h + l/16 (4 k values, four MFMAs).
+    // Weights are MFMA source 0 (rows = output columns n), activations
+    // source 1 (columns = token rows m).  The swizzle depends on the row mod
+    // 16 only, so blocks i of one operand differ by the constant i*MB*128.
+    constexpr int NF = KS * (FM + FN);       // fragments per half slice
+    int fo[2][KS][2];
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) {
-        const int ch = BF16 ? (2 * s2 + (lane >> 5)) : (lane >> 4);
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int r = wm * WM + i * MB + (lane & (MB - 1));
-            f_off[s2 * (FM + FN) + i] = r * 64 + ((ch ^ swz(r)) << 4);
+        for (int s2 = 0; s2 < KS; ++s2) {
+            const int lr = lane & (MB - 1);
+            const int ch = BF16 ? (4 * h + 2 * s2 + (lane >> 5)) : (4 * h + (lane >> 4));
+            fo[h][s2][0] = (wm * WM + lr) * 128 + ((ch ^ swz(lr)) << 4);
+            fo[h][s2][1] = NA * SA + (wn * WN + lr) * 128 + ((ch ^ swz(lr)) << 4);
         }
+    auto read_frags = [&](int ks, int h, u32x4_t* f) {
+        const uint8_t* La = &lds[(ks % NA) * SA];
+        const uint8_t* Lb = &lds[(ks % NB) * SB];
 #pragma unroll
-        for (int i = 0; i < FN; ++i) {
-            const int r = wn * WN + i * MB + (lane & (MB - 1));
-            f_off[s2 * (FM + FN) + FM + i] = (BM + r) * 64 + ((ch ^ swz(r)) << 4);
+        for (int s2 = 0; s2 < KS; ++s2) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                f[s2 * (FM + FN) + i] = *(const u32x4_t*)(La + fo[h][s2][0] + i * MB * 128);
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+                f[s2 * (FM + FN) + FM + i] = *(const u32x4_t*)(Lb + fo[h][s2][1] + i * MB * 128);
         }
-    }
-    auto read_frags = [&](int stage, u32x4_t* f) {
-        const uint8_t* Lb = &lds[stage * STAGE];
-#pragma unroll
-        for (int i = 0; i < NF; ++i) f[i] = *(const u32x4_t*)(Lb + f_off[i]);
     };
     auto mma = [&](const u32x4_t* f) {
 #pragma unroll
@@ -246,134 +422,126 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
                     }
                 }
     };
+    // Scheduling hints: spread the LDS reads (and the batch's loads) between
+    // the MFMAs of a half slice instead of issuing them in one burst.
+    constexpr int NMMA = KS * FM * FN * (BF16 ? 1 : 4);
+    auto interleave_reads = [&]() {
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NMMA / NF > 0 ? NMMA / NF : 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto interleave_loads = [&]() {
+#pragma unroll
+        for (int i = 0; i < ga + gb; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NMMA / (ga + gb) > 0 ? NMMA / (ga + gb) : 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, NF / (ga + gb) > 0 ? NF / (ga + gb) : 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
-    // Pipeline over K stages kt = 0 .. nk-1, stage kt in buffer kt % NS.
-    // Loads run NS stages ahead of the MFMAs.  Iteration kt holds stage kt's
-    // fragments in registers and
-    //   1. waits until this wave's loads of stage kt+1 have landed,
-    //   2. barrier: every wave's stage kt+1 is visible, and every wave has
-    //      its stage-kt fragments in registers, so buffer kt % NS is free,
-    //   3. refills buffer kt % NS with stage kt+NS,
-    //   4. reads stage kt+1's fragments  while  5. MFMAs consume stage kt's.
-    const int nk = p.K / KT;
+    // Pipeline over slices ks = 0 .. nk-1, two half slices each.  Entering
+    // slice ks, f0 holds its first half's fragments.
+    //   half 0: read the second half's fragments into f1; MFMAs on f0.
+    //   half 1: wait until this wave's loads of slice ks+1 have landed;
+    //           barrier (slice ks+1 is visible, and every wave has slice ks in
+    //           registers, so its A and B slots are free); issue batch ks
+    //           into those slots; read slice ks+1's first half into f0;
+    //           MFMAs on f1.
+    // The prologue issues the batches j = -NB .. -1 (parts with a negative
+    // slice index are skipped) in the same order, so the wait counts hold
+    // from the first slice on.
     u32x4_t f0[NF], f1[NF];
-    auto wait_pending = [&](int pending) {      // leave `pending` stages in flight
-        if (pending >= 3) wait_vmcnt<3 * GPW>();
-        else if (pending == 2) wait_vmcnt<2 * GPW>();
-        else if (pending == 1) wait_vmcnt<GPW>();
-        else wait_vmcnt<0>();
-    };
-    const int pre = nk < NS ? nk : NS;
-    for (int s = 0; s < pre; ++s) issue(s, s);
-    wait_pending(pre - 1);
+#pragma unroll
+    for (int j = -NB; j < 0; ++j) {
+        if (j + NA >= 0) issueA(j + NA);
+        issueB(j + NB);
+    }
+    wait_vmcnt<RD.wait0>();
     lds_barrier();
-    read_frags(0, f0);
-    int kt = 0;
-    auto step = [&](u32x4_t* f, u32x4_t* f_n) {
-        const int issued_last = min(kt + NS - 1, nk - 1);   // loads issued: stages 0 .. issued_last
-        if (kt + 1 < nk) wait_pending(issued_last - (kt + 1));
+    read_frags(0, 0, f0);
+    int ks = 0;
+    for (; ks + 2 < nk; ++ks) {
+        read_frags(ks, 1, f1);
+        mma(f0);
+        interleave_reads();
+        wait_vmcnt<RD.wait>();
         lds_barrier();
-        if (kt + NS < nk) issue(kt + NS, kt % NS);
-        if (kt + 1 < nk) read_frags((kt + 1) % NS, f_n);
-        __builtin_amdgcn_sched_barrier(0);
-        mma(f);
-        __builtin_amdgcn_sched_barrier(0);
-        ++kt;
-    };
-    while (kt + 1 < nk) {
-        step(f0, f1);
-        step(f1, f0);
+        issueA(ks + NA);
+        issueB(ks + NB);
+        read_frags(ks + 1, 0, f0);
+        mma(f1);
+        interleave_loads();
     }
-    if (kt < nk) step(f0, f1);
+    for (; ks < nk; ++ks) {
+        read_frags(ks, 1, f1);
+        mma(f0);
+        interleave_reads();
+        if (ks + 1 < nk) {
+            wait_vmcnt<RD.wait>();
+            lds_barrier();
+            read_frags(ks + 1, 0, f0);
+        }
+        mma(f1);
+        interleave_reads();
+    }
+    wait_vmcnt<0>();   // reloads of the last slice may still be landing
 
-    // ---- epilogue.  bf16 blocks (32x32): lane l, element r = 4q + t holds
-    // D[n = 8q + 4(l/32) + t][m = l % 32].  fp32 blocks (16x16): element t
-    // holds D[n = 4(l/16) + t][m = l % 16].  Either way a lane owns 4
-    // consecutive output columns of one row per (q) and stores them at once.
-    auto store4 = [&](int m, int64_t col, const float* v) {
-        const int64_t o = (int64_t)(row0 + m) * p.ldc + col;
-        if constexpr (BF16) {
-            uint2 w;
-            w.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-            w.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-            *(uint2*)((uint16_t*)p.C + o) = w;
-        } else {
-            *(float4*)((float*)p.C + o) = make_float4(v[0], v[1], v[2], v[3]);
-        }
-    };
-    auto silu_mul = [](float gt, float up) { return gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up; };
-    if constexpr (BF16) {
-        const int h = lane >> 5;
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-            const int m = wm * WM + j * 32 + (lane & 31);
-            if (m >= rows) continue;
-#pragma unroll
-            for (int i = 0; i < FN; ++i) {
-                const int blk = wn * (WN / 32) + i;              // 32-row block of the B tile
-                if constexpr (EPI == EPI_SWIGLU) {
-                    // rows 0-15 of the block are gate units, rows 16-31 the
-                    // up units of the same 16 hidden units: q and q+2 pair up
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        float v[4];
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) v[t] = silu_mul(acc[i][j][4 * q + t], acc[i][j][4 * (q + 2) + t]);
-                        store4(m, (int64_t)nt * (BN / 2) + blk * 16 + 8 * q + 4 * h, v);
-                    }
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float v[4];
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            float x = acc[i][j][4 * q + t];
-                            if constexpr (EPI == EPI_RELU) x = fmaxf(x, 0.0f);
-                            v[t] = x;
-                        }
-                        store4(m, (int64_t)nt * BN + blk * 32 + 8 * q + 4 * h, v);
-                    }
-                }
-            }
-        }
-    } else {
-        const int lg = lane >> 4;
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-            const int m = wm * WM + j * 16 + (lane & 15);
-            if (m >= rows) continue;
-            if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-                for (int pi = 0; pi < FN / 2; ++pi) {
-                    const int fblock = (wn * FN + 2 * pi) >> 1;    // 16-row blocks alternate gate / up
-                    float v[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = silu_mul(acc[2 * pi][j][t], acc[2 * pi + 1][j][t]);
-                    store4(m, (int64_t)nt * (BN / 2) + fblock * 16 + 4 * lg, v);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < FN; ++i) {
-                    float v[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        float x = acc[i][j][t];
-                        if constexpr (EPI == EPI_RELU) x = fmaxf(x, 0.0f);
-                        v[t] = x;
-                    }
-                    store4(m, (int64_t)nt * BN + wn * WN + i * 16 + 4 * lg, v);
-                }
-            }
-        }
-    }
+    if constexpr (SPLIT) Epi::store_partial(p, acc, unit, wave, lane);
+    else Epi::store(p, acc, row0, rows, nt, wm, wn, lane);
 #endif
 }
 
-// Tile plan: prefix[e+1] = sum_{e' <= e} ceil(M_e' / BM).  With offsets == NULL
-// the plan describes one group of uniform_rows rows and offsets_copy receives
+// Split-K fixup: block (t, w) adds the `split` partial accumulators of wave
+// w of tail tile t in range order and applies the epilogue.
+template <bool BF16, int BM, int BN, int EPI>
+__global__ __launch_bounds__(64) void k_split_fixup(GemmParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef GemmEpilogue<BF16, BM, BN, EPI> Epi;
+    constexpr int FM = Epi::FM, FN = Epi::FN, RA = Epi::RA;
+    const int full = p.plan[p.E + 1], split = p.plan[p.E + 2], tail = p.plan[p.E + 3];
+    const int t = blockIdx.x >> 2, w = blockIdx.x & 3, lane = threadIdx.x;
+    if (split <= 1 || t >= tail) return;
+    typename Epi::acc_t acc[FN][FM];
+    const float4* src = (const float4*)p.partial;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int r = 0; r < RA; ++r) acc[i][j][r] = 0.0f;
+    for (int c = 0; c < split; ++c) {
+        const int u = t * split + c;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int r4 = 0; r4 < RA / 4; ++r4) {
+                    const float4 v = src[Epi::partial_index(u, w, i, j, r4, lane)];
+                    acc[i][j][4 * r4] += v.x;
+                    acc[i][j][4 * r4 + 1] += v.y;
+                    acc[i][j][4 * r4 + 2] += v.z;
+                    acc[i][j][4 * r4 + 3] += v.w;
+                }
+    }
+    int e, mt, nt;
+    decode_tile(p, full + t, e, mt, nt);
+    const int row0 = p.offsets[e] + mt * BM;
+    const int rows = min(BM, p.offsets[e + 1] - row0);
+    Epi::store(p, acc, row0, rows, nt, w >> 1, w & 1, lane);
+#endif
+}
+
+// Tile plan: prefix[e+1] = sum_{e' <= e} ceil(M_e' / BM), then the split-K
+// decision {full, split, tail} (see kSplitUnits).  With offsets == NULL the
+// plan describes one group of uniform_rows rows and offsets_copy receives
 // {0, uniform_rows}.  One block of 1024 threads (E <= 1024).
 __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ offsets, int E, int uniform_rows,
-                                                    int BM, int32_t* __restrict__ prefix,
+                                                    int BM, int NT, int nk, int32_t* __restrict__ prefix,
                                                     int32_t* __restrict__ offsets_copy) {
     __shared__ int32_t scan[1024];
     const int e = threadIdx.x;
@@ -399,21 +567,36 @@ __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ 
     }
     if (e == 0) prefix[0] = 0;
     if (e < E) prefix[e + 1] = scan[e];
+    if (e == 0) {
+        const int total = scan[E - 1] * NT;
+        const int rem = total % kSplitUnits;
+        int split = 1, tail = 0;
+        if (rem > 0 && rem <= kSplitUnits / 2 && total < 4 * kSplitUnits) {
+            int sp = kSplitUnits / rem;
+            sp = min(sp, kMaxSplit);
+            sp = min(sp, nk / 4);                  // at least 4 slices per range
+            if (sp >= 2) {
+                split = sp;
+                tail = rem;
+            }
+        }
+        prefix[E + 1] = total - tail;
+        prefix[E + 2] = split;
+        prefix[E + 3] = tail;
+    }
 }
 
-size_t ffn_tile_plan_ints(int E) { return (size_t)(E + 1) + 2; }
+size_t ffn_tile_plan_ints(int E) { return (size_t)(E + 1) + 3; }
 
-void launch_tile_plan(const int32_t* offsets, int E, int uniform_rows, int BM, int32_t* tile_prefix,
-                      int32_t* offsets_copy, hipStream_t s) {
-    hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, offsets, E, uniform_rows, BM, tile_prefix,
-                       offsets_copy);
-}
+size_t gemm_partial_bytes(int BM, int BN) { return (size_t)kSplitUnits * BM * BN * sizeof(float); }
 
 GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N) {
-    (void)bf16;
     const int64_t avg = E > 0 ? rows / E : rows;
     GemmShape g;
     g.BM = avg >= 384 ? 256 : (avg >= 96 ? 128 : 64);
+    // fp32 tiles stop at 128 rows: 256 x 256 fp32 accumulators leave no
+    // registers for the epilogue
+    if (!bf16 && g.BM > 128) g.BM = 128;
     // output columns per tile for BN = 256 / 128 / 64 (SwiGLU tiles hold gate
     // and up rows, so they produce half as many columns)
     const int div = epi == EPI_SWIGLU ? 2 : 1;
@@ -421,53 +604,66 @@ GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N) {
     return g;
 }
 
+// Whole tiles, split units (exit at once when the plan has no split), fixup.
+template <bool BF16, int BM, int BN, int EPI>
+static void launch_pair(const GemmParams& p, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, false>), dim3(grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, true>), dim3(kSplitUnits), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_split_fixup<BF16, BM, BN, EPI>), dim3(kSplitUnits / 2 * 4), dim3(64), 0, s, p);
+}
+
 template <bool BF16, int BM, int BN>
-static hipError_t launch_bmbn(int epi, const GemmParams& p, int grid, hipStream_t s) {
+static void launch_bmbn(int epi, const GemmParams& p, int grid, hipStream_t s) {
     switch (epi) {
-        case EPI_STORE:
-            hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI_STORE>), dim3(grid), dim3(256), 0, s, p);
-            break;
-        case EPI_RELU:
-            hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI_RELU>), dim3(grid), dim3(256), 0, s, p);
-            break;
-        default:
-            hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI_SWIGLU>), dim3(grid), dim3(256), 0, s, p);
-            break;
+        case EPI_STORE: launch_pair<BF16, BM, BN, EPI_STORE>(p, grid, s); break;
+        case EPI_RELU: launch_pair<BF16, BM, BN, EPI_RELU>(p, grid, s); break;
+        default: launch_pair<BF16, BM, BN, EPI_SWIGLU>(p, grid, s); break;
     }
-    return hipGetLastError();
 }
 
 template <bool BF16>
-static hipError_t launch_t(int epi, const GemmParams& p, int BM, int BN, int grid, hipStream_t s) {
+static void launch_t(int epi, const GemmParams& p, int BM, int BN, int grid, hipStream_t s) {
+    if constexpr (BF16) {
+        if (BM == 256) {
+            if (BN == 256) return launch_bmbn<BF16, 256, 256>(epi, p, grid, s);
+            if (BN == 128) return launch_bmbn<BF16, 256, 128>(epi, p, grid, s);
+            return launch_bmbn<BF16, 256, 64>(epi, p, grid, s);
+        }
+    }
     if (BN == 256) {
-        if (BM == 256) return launch_bmbn<BF16, 256, 256>(epi, p, grid, s);
         if (BM == 128) return launch_bmbn<BF16, 128, 256>(epi, p, grid, s);
         return launch_bmbn<BF16, 64, 256>(epi, p, grid, s);
     }
     if (BN == 128) {
-        if (BM == 256) return launch_bmbn<BF16, 256, 128>(epi, p, grid, s);
         if (BM == 128) return launch_bmbn<BF16, 128, 128>(epi, p, grid, s);
         return launch_bmbn<BF16, 64, 128>(epi, p, grid, s);
     }
-    if (BM == 256) return launch_bmbn<BF16, 256, 64>(epi, p, grid, s);
     if (BM == 128) return launch_bmbn<BF16, 128, 64>(epi, p, grid, s);
     return launch_bmbn<BF16, 64, 64>(epi, p, grid, s);
 }
 
 hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B0, const void* B1,
                                int64_t b_expert_stride, void* C, int64_t ldc, int N, int K, int E, int64_t max_rows,
-                               const int32_t* offsets, const int32_t* tile_prefix, int BM, int BN, hipStream_t s) {
+                               const int32_t* offsets, int32_t* plan, int32_t* plan_copy, float* partial, int BM,
+                               int BN, hipStream_t s) {
     if (max_rows <= 0) return hipSuccess;
     GemmParams p;
     p.A = A; p.lda = lda; p.B0 = B0; p.B1 = B1; p.bstride = b_expert_stride;
-    p.C = C; p.ldc = ldc; p.N = N; p.K = K; p.E = E;
+    p.C = C; p.ldc = ldc; p.N = N; p.K = K; p.E = offsets ? E : 1;
     p.NT = epi == EPI_SWIGLU ? N / (BN / 2) : N / BN;
-    p.offsets = offsets; p.tile_prefix = tile_prefix;
-    const int64_t m_tiles_ub = (max_rows + BM - 1) / BM + (E > 1 ? E : 0);
-    int64_t grid = m_tiles_ub * p.NT;
-    grid = (grid + 7) / 8 * 8;
+    p.nk = K * (bf16 ? 2 : 4) / 128;
+    p.offsets = offsets ? offsets : plan_copy;
+    p.plan = plan;
+    p.partial = partial;
+    hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, offsets, E, (int)max_rows, BM, p.NT, p.nk, plan,
+                       plan_copy);
+    const int64_t m_tiles_ub = (max_rows + BM - 1) / BM + (p.E > 1 ? p.E : 0);
+    int64_t grid = (m_tiles_ub * p.NT + 7) / 8 * 8;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    return bf16 ? launch_t<true>(epi, p, BM, BN, (int)grid, s) : launch_t<false>(epi, p, BM, BN, (int)grid, s);
+    if (!bf16 && BM > 128) return hipErrorInvalidValue;
+    if (bf16) launch_t<true>(epi, p, BM, BN, (int)grid, s);
+    else launch_t<false>(epi, p, BM, BN, (int)grid, s);
+    return hipGetLastError();
 }
 
 }  // namespace moe

@@ -40,16 +40,18 @@ void launch_combine(const void* y_perm, const int32_t* slot_pos, const float* ga
 struct GemmShape {
     int BM, BN;
 };
-// Tile plan: prefix sums of ceil(M_e / BM) over experts, built on the device.
-void launch_tile_plan(const int32_t* offsets, int E, int uniform_rows, int BM, int32_t* tile_prefix,
-                      int32_t* offsets_copy, hipStream_t s);
 size_t ffn_tile_plan_ints(int E);
+// Split-K partial accumulator workspace needed by a BM x BN launch.
+size_t gemm_partial_bytes(int BM, int BN);
 // Grouped GEMM C[rows][N] = act(A[rows][K] . B_e[N][K]^T) per expert group.
 // epi: 0 store, 1 relu, 2 swiglu (B0 = gate, B1 = up, N = d_ff, output width N).
+// Builds the tile plan on the device (offsets == NULL: one group of max_rows
+// rows, whose offsets go to plan_copy), then runs the GEMM and its split-K
+// fixup.
 hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B0, const void* B1,
                                int64_t b_expert_stride, void* C, int64_t ldc, int N, int K, int E,
-                               int64_t max_rows, const int32_t* offsets, const int32_t* tile_prefix,
-                               int BM, int BN, hipStream_t s);
+                               int64_t max_rows, const int32_t* offsets, int32_t* plan, int32_t* plan_copy,
+                               float* partial, int BM, int BN, hipStream_t s);
 GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N);
 
 }  // namespace moe

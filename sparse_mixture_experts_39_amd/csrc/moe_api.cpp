@@ -42,8 +42,31 @@ struct Layout {
     size_t Hs, plan_s_up, plan_s_down, plan_s_copy;       // shared expert
     size_t idx, gates, slot_pos, perm_src, offsets;       // whole-layer intermediates
     size_t x_perm, y_perm, shared_out;
+    size_t partial;                                       // split-K accumulators
     size_t total;
 };
+
+// Split-K workspace: the largest need over the grouped GEMMs the layer runs.
+size_t partial_bytes_of(const moe_config* c) {
+    const bool bf = c->act_dtype == MOE_BF16;
+    const int epi_up = c->act == MOE_ACT_SWIGLU ? 2 : 1;
+    size_t b = 0;
+    auto need = [&](int epi, int64_t rows, int E, int N) {
+        const moe::GemmShape g = moe::pick_gemm_shape(bf, epi, rows, E, N);
+        const size_t n = moe::gemm_partial_bytes(g.BM, g.BN);
+        if (n > b) b = n;
+    };
+    const int64_t R = max_rows_of(c);
+    if (R > 0) {
+        need(epi_up, R, c->n_experts, c->d_ff);
+        need(0, R, c->n_experts, c->d_model);
+    }
+    if (c->n_shared > 0 && c->T > 0) {
+        need(2, c->T, 1, c->d_ff_shared);
+        need(0, c->T, 1, c->d_model);
+    }
+    return b;
+}
 
 Layout compute_layout(const moe_config* c) {
     Layout L;
@@ -78,6 +101,7 @@ Layout compute_layout(const moe_config* c) {
     L.x_perm = take((size_t)R * c->d_model * es);
     L.y_perm = take((size_t)R * c->d_model * es);
     L.shared_out = take(sh ? (size_t)T * c->d_model * es : 0);
+    L.partial = take(partial_bytes_of(c));
     L.total = o;
     return L;
 }
@@ -206,24 +230,22 @@ moe_status moe_dispatch(const moe_config* c, const void* x, const int32_t* topk_
     return after_launch();
 }
 
-// One grouped GEMM of an expert stack: builds the tile plan for the chosen
-// row tile, then launches.  up = true: a -> H (ReLU / SwiGLU epilogue);
-// up = false: H -> y.  With offsets == NULL the call covers one group of
-// `rows` rows (the shared expert) and the plan writes its offsets to plan_copy.
+// One grouped GEMM of an expert stack (tile plan, GEMM and split-K fixup, all
+// on the device).  up = true: a -> H (ReLU / SwiGLU epilogue); up = false:
+// H -> y.  With offsets == NULL the call covers one group of `rows` rows (the
+// shared expert) and the plan writes its offsets to plan_copy.
 static moe_status run_gemm(const moe_config* c, bool up, const void* a, int64_t rows, int E, const int32_t* offsets,
                            const void* w1, const void* w3, const void* w2, int F, void* dst, int32_t* plan,
-                           int32_t* plan_copy, hipStream_t h) {
+                           int32_t* plan_copy, float* partial, hipStream_t h) {
     const bool bf = is_bf16(c);
     const int d = c->d_model;
     const int epi = up ? (c->act == MOE_ACT_SWIGLU ? 2 : 1) : 0;
     const int N = up ? F : d;
     const moe::GemmShape g = moe::pick_gemm_shape(bf, epi, rows, E, N);
-    moe::launch_tile_plan(offsets, E, (int)rows, g.BM, plan, plan_copy, h);
-    const int32_t* offs = offsets ? offsets : plan_copy;
     const hipError_t e = up ? moe::launch_grouped_gemm(bf, epi, a, d, w1, w3, (int64_t)F * d, dst, F, F, d, E, rows,
-                                                       offs, plan, g.BM, g.BN, h)
+                                                       offsets, plan, plan_copy, partial, g.BM, g.BN, h)
                             : moe::launch_grouped_gemm(bf, 0, a, F, w2, nullptr, (int64_t)d * F, dst, d, d, F, E,
-                                                       rows, offs, plan, g.BM, g.BN, h);
+                                                       rows, offsets, plan, plan_copy, partial, g.BM, g.BN, h);
     if (e != hipSuccess) return hip_status(e);
     return after_launch();
 }
@@ -247,7 +269,8 @@ moe_status moe_expert_up(const moe_config* c, const void* x_perm, const int32_t*
     if (R == 0) return MOE_OK;
     const Layout L = compute_layout(c);
     return run_gemm(c, true, x_perm, R, c->n_experts, expert_offsets, w->w_gate, w->w_up, nullptr, c->d_ff, hbuf,
-                    at<int32_t>(ws, L.plan_up), at<int32_t>(ws, L.plan_copy), (hipStream_t)stream);
+                    at<int32_t>(ws, L.plan_up), at<int32_t>(ws, L.plan_copy), at<float>(ws, L.partial),
+                    (hipStream_t)stream);
 }
 
 moe_status moe_expert_down(const moe_config* c, const void* hbuf, const int32_t* expert_offsets, const moe_weights* w,
@@ -260,7 +283,8 @@ moe_status moe_expert_down(const moe_config* c, const void* hbuf, const int32_t*
     if (R == 0) return MOE_OK;
     const Layout L = compute_layout(c);
     return run_gemm(c, false, hbuf, R, c->n_experts, expert_offsets, nullptr, nullptr, w->w_down, c->d_ff, y_perm,
-                    at<int32_t>(ws, L.plan_down), at<int32_t>(ws, L.plan_copy), (hipStream_t)stream);
+                    at<int32_t>(ws, L.plan_down), at<int32_t>(ws, L.plan_copy), at<float>(ws, L.partial),
+                    (hipStream_t)stream);
 }
 
 moe_status moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* expert_offsets,
@@ -290,10 +314,11 @@ moe_status moe_shared_expert(const moe_config* c, const void* x, const moe_weigh
     hipStream_t h = (hipStream_t)stream;
     void* Hs = at<void>(ws, L.Hs);
     if ((s = run_gemm(c, true, x, c->T, 1, nullptr, w->ws_gate, w->ws_up, nullptr, c->d_ff_shared, Hs,
-                      at<int32_t>(ws, L.plan_s_up), at<int32_t>(ws, L.plan_s_copy), h)) != MOE_OK)
+                      at<int32_t>(ws, L.plan_s_up), at<int32_t>(ws, L.plan_s_copy), at<float>(ws, L.partial), h)) !=
+        MOE_OK)
         return s;
     return run_gemm(c, false, Hs, c->T, 1, nullptr, nullptr, nullptr, w->ws_down, c->d_ff_shared, shared_out,
-                    at<int32_t>(ws, L.plan_s_down), at<int32_t>(ws, L.plan_s_copy), h);
+                    at<int32_t>(ws, L.plan_s_down), at<int32_t>(ws, L.plan_s_copy), at<float>(ws, L.partial), h);
 }
 
 moe_status moe_combine(const moe_config* c, const void* y_perm, const int32_t* slot_pos, const float* topk_gate,

@@ -33,6 +33,18 @@ MID = {
                              gate="softmax_topk", seed=15),
     "many_experts": Config("many_experts", T=2000, d=64, F=64, E=1024, k=16, act_dtype="bf16", act="relu",
                            gate="softmax_topk", seed=16),
+    # fewer than half a round of tiles on 256 CUs and K long enough: both
+    # GEMMs cut every tile into K ranges and add them in the fixup kernel
+    "split_k_bf16": Config("split_k_bf16", T=1024, d=1024, F=1024, E=4, k=2, act_dtype="bf16", act="swiglu",
+                           gate="softmax_topk", seed=17),
+    "split_k_f32": Config("split_k_f32", T=512, d=512, F=512, E=4, k=2, act_dtype="f32", act="swiglu",
+                          gate="softmax_topk", seed=18),
+    "split_k_relu_cap": Config("split_k_relu_cap", T=900, d=768, F=640, E=5, k=2, act_dtype="bf16", act="relu",
+                               gate="softmax_full", capacity_factor=1.0, seed=19),
+    # 256 x 256 tiles without split: every accumulator goes through the
+    # LDS-staged epilogue
+    "tiles_256_bf16": Config("tiles_256_bf16", T=2048, d=256, F=256, E=2, k=1, act_dtype="bf16", act="swiglu",
+                             gate="softmax_topk", seed=23),
 }
 
 
