@@ -60,10 +60,10 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y_perm
         }
         uint4 o;
         if constexpr (BF16) {
-            o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
-            o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
-            o.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
-            o.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
+            o.x = pack_bf16x2(acc[0], acc[1]);
+            o.y = pack_bf16x2(acc[2], acc[3]);
+            o.z = pack_bf16x2(acc[4], acc[5]);
+            o.w = pack_bf16x2(acc[6], acc[7]);
         } else {
             o.x = __float_as_uint(acc[0]); o.y = __float_as_uint(acc[1]);
             o.z = __float_as_uint(acc[2]); o.w = __float_as_uint(acc[3]);

@@ -16,12 +16,15 @@ constexpr int kWave = 64;
 // bf16 is carried as its 16 raw bits.
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> one packed bf16 pair (a in the low half), round to
+// nearest even (the default rounding mode; denormals kept), with one
+// v_cvt_pk_bf16_f32; a NaN stays a NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const floatx2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Element i of an activation vector as fp32 (exact for both dtypes).

@@ -177,8 +177,8 @@ struct GemmEpilogue {
             const int64_t o = (int64_t)(row0 + m) * p.ldc + col;
             if constexpr (BF16) {
                 uint2 w;
-                w.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                w.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                w.x = pack_bf16x2(v[0], v[1]);
+                w.y = pack_bf16x2(v[2], v[3]);
                 *(uint2*)((uint16_t*)p.C + o) = w;
             } else {
                 *(float4*)((float*)p.C + o) = make_float4(v[0], v[1], v[2], v[3]);
