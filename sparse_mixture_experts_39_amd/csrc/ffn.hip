@@ -40,6 +40,8 @@
 //   * SwiGLU is fused: a BN-row weight tile interleaves 16-row blocks of W1
 //     and W3 for the same BN/2 hidden units, so a wave holds the gate and up
 //     accumulators of the same (row, unit) in one lane and writes h directly.
+//   * Split-K tail: a mostly empty last round of tiles is cut into K ranges
+//     (second launch, fp32 partials) and reduced in order by k_split_fixup.
 #include <type_traits>
 
 #include "device_common.h"
@@ -167,12 +169,18 @@ struct GemmEpilogue {
                         make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
     }
 
-    __device__ static void store(const GemmParams& p, const acc_t (&acc)[FN][FM], int row0, int rows, int nt, int wm,
-                                 int wn, int lane) {
-            // Output tile.  bf16 blocks (32x32): lane l, element r = 4q + t holds
-        // D[n = 8q + 4(l/32) + t][m = l % 32].  fp32 blocks (16x16): element t
-        // holds D[n = 4(l/16) + t][m = l % 16].  Either way a lane owns 4
-        // consecutive output columns of one row per (q) and stores them at once.
+    // Column groups of the epilogue: the 32- (bf16) or 16-row (fp32) blocks i
+    // of the wave's B tile are independent, except that fp32 SwiGLU pairs
+    // block 2p (gate) with block 2p+1 (up).
+    static constexpr int IG = (!BF16 && EPI == EPI_SWIGLU) ? 2 : 1;
+
+    // Output of blocks i0 .. i0+IG-1 (acc[0 .. IG-1]).  bf16 blocks (32x32):
+    // lane l, element r = 4q + t holds D[n = 8q + 4(l/32) + t][m = l % 32].
+    // fp32 blocks (16x16): element t holds D[n = 4(l/16) + t][m = l % 16].
+    // Either way a lane owns 4 consecutive output columns of one row per q
+    // and stores them at once.
+    __device__ static void store_cols(const GemmParams& p, const acc_t (*acc)[FM], int i0, int row0, int rows, int nt,
+                                      int wm, int wn, int lane) {
         auto store4 = [&](int m, int64_t col, const float* v) {
             const int64_t o = (int64_t)(row0 + m) * p.ldc + col;
             if constexpr (BF16) {
@@ -187,68 +195,65 @@ struct GemmEpilogue {
         auto silu_mul = [](float gt, float up) { return gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up; };
         if constexpr (BF16) {
             const int h = lane >> 5;
-    #pragma unroll
+            const int blk = wn * (WN / 32) + i0;                 // 32-row block of the B tile
+#pragma unroll
             for (int j = 0; j < FM; ++j) {
                 const int m = wm * WM + j * 32 + (lane & 31);
                 if (m >= rows) continue;
-    #pragma unroll
-                for (int i = 0; i < FN; ++i) {
-                    const int blk = wn * (WN / 32) + i;              // 32-row block of the B tile
-                    if constexpr (EPI == EPI_SWIGLU) {
-                        // rows 0-15 of the block are gate units, rows 16-31 the
-                        // up units of the same 16 hidden units: q and q+2 pair up
-    #pragma unroll
-                        for (int q = 0; q < 2; ++q) {
-                            float v[4];
-    #pragma unroll
-                            for (int t = 0; t < 4; ++t) v[t] = silu_mul(acc[i][j][4 * q + t], acc[i][j][4 * (q + 2) + t]);
-                            store4(m, (int64_t)nt * (BN / 2) + blk * 16 + 8 * q + 4 * h, v);
+                if constexpr (EPI == EPI_SWIGLU) {
+                    // rows 0-15 of the block are gate units, rows 16-31 the
+                    // up units of the same 16 hidden units: q and q+2 pair up
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        float v[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) v[t] = silu_mul(acc[0][j][4 * q + t], acc[0][j][4 * (q + 2) + t]);
+                        store4(m, (int64_t)nt * (BN / 2) + blk * 16 + 8 * q + 4 * h, v);
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float v[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            float x = acc[0][j][4 * q + t];
+                            if constexpr (EPI == EPI_RELU) x = fmaxf(x, 0.0f);
+                            v[t] = x;
                         }
-                    } else {
-    #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            float v[4];
-    #pragma unroll
-                            for (int t = 0; t < 4; ++t) {
-                                float x = acc[i][j][4 * q + t];
-                                if constexpr (EPI == EPI_RELU) x = fmaxf(x, 0.0f);
-                                v[t] = x;
-                            }
-                            store4(m, (int64_t)nt * BN + blk * 32 + 8 * q + 4 * h, v);
-                        }
+                        store4(m, (int64_t)nt * BN + blk * 32 + 8 * q + 4 * h, v);
                     }
                 }
             }
         } else {
             const int lg = lane >> 4;
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < FM; ++j) {
                 const int m = wm * WM + j * 16 + (lane & 15);
                 if (m >= rows) continue;
                 if constexpr (EPI == EPI_SWIGLU) {
-    #pragma unroll
-                    for (int pi = 0; pi < FN / 2; ++pi) {
-                        const int fblock = (wn * FN + 2 * pi) >> 1;    // 16-row blocks alternate gate / up
-                        float v[4];
-    #pragma unroll
-                        for (int t = 0; t < 4; ++t) v[t] = silu_mul(acc[2 * pi][j][t], acc[2 * pi + 1][j][t]);
-                        store4(m, (int64_t)nt * (BN / 2) + fblock * 16 + 4 * lg, v);
-                    }
+                    const int fblock = (wn * FN + i0) >> 1;        // 16-row blocks alternate gate / up
+                    float v[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) v[t] = silu_mul(acc[0][j][t], acc[1][j][t]);
+                    store4(m, (int64_t)nt * (BN / 2) + fblock * 16 + 4 * lg, v);
                 } else {
-    #pragma unroll
-                    for (int i = 0; i < FN; ++i) {
-                        float v[4];
-    #pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            float x = acc[i][j][t];
-                            if constexpr (EPI == EPI_RELU) x = fmaxf(x, 0.0f);
-                            v[t] = x;
-                        }
-                        store4(m, (int64_t)nt * BN + wn * WN + i * 16 + 4 * lg, v);
+                    float v[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        float x = acc[0][j][t];
+                        if constexpr (EPI == EPI_RELU) x = fmaxf(x, 0.0f);
+                        v[t] = x;
                     }
+                    store4(m, (int64_t)nt * BN + wn * WN + i0 * 16 + 4 * lg, v);
                 }
             }
         }
+    }
+
+    __device__ static void store(const GemmParams& p, const acc_t (&acc)[FN][FM], int row0, int rows, int nt, int wm,
+                                 int wn, int lane) {
+#pragma unroll
+        for (int i0 = 0; i0 < FN; i0 += IG) store_cols(p, acc + i0, i0, row0, rows, nt, wm, wn, lane);
     }
 };
 
@@ -422,38 +427,20 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
                     }
                 }
     };
-    // Scheduling hints: spread the LDS reads (and the batch's loads) between
-    // the MFMAs of a half slice instead of issuing them in one burst.
-    constexpr int NMMA = KS * FM * FN * (BF16 ? 1 : 4);
-    auto interleave_reads = [&]() {
-#pragma unroll
-        for (int i = 0; i < NF; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, NMMA / NF > 0 ? NMMA / NF : 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    auto interleave_loads = [&]() {
-#pragma unroll
-        for (int i = 0; i < ga + gb; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, NMMA / (ga + gb) > 0 ? NMMA / (ga + gb) : 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, NF / (ga + gb) > 0 ? NF / (ga + gb) : 1, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // Pipeline over slices ks = 0 .. nk-1, two half slices each.  Entering
-    // slice ks, f0 holds its first half's fragments.
-    //   half 0: read the second half's fragments into f1; MFMAs on f0.
-    //   half 1: wait until this wave's loads of slice ks+1 have landed;
-    //           barrier (slice ks+1 is visible, and every wave has slice ks in
-    //           registers, so its A and B slots are free); issue batch ks
-    //           into those slots; read slice ks+1's first half into f0;
-    //           MFMAs on f1.
+    // Pipeline over slices ks = 0 .. nk-1 (two half slices each).  Between
+    // two barriers runs one region: the second half of slice ks (fragments
+    // in f1) and the first half of slice ks+1 (f0).  Region ks:
+    //   wait until this wave's loads of slice ks+1 have landed; barrier
+    //   (slice ks+1 is visible to all waves, and every wave has read both
+    //   halves of slice ks, so its A and B slots are free); issue batch ks
+    //   into those slots; read slice ks+1's first half into f0; MFMAs on f1;
+    //   read slice ks+1's second half into f1; MFMAs on f0.
     // The prologue issues the batches j = -NB .. -1 (parts with a negative
     // slice index are skipped) in the same order, so the wait counts hold
-    // from the first slice on.
+    // from the first slice on.  Scheduling hints spread the region's loads
+    // and LDS reads between its MFMAs instead of issuing them in bursts.
+    constexpr int NMMA = KS * FM * FN * (BF16 ? 1 : 4);   // MFMAs per half slice
+    constexpr int NV = ga + gb;                             // loads per batch
     u32x4_t f0[NF], f1[NF];
 #pragma unroll
     for (int j = -NB; j < 0; ++j) {
@@ -463,31 +450,38 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     wait_vmcnt<RD.wait0>();
     lds_barrier();
     read_frags(0, 0, f0);
+    read_frags(0, 1, f1);
+    mma(f0);
+    __builtin_amdgcn_sched_barrier(0);
     int ks = 0;
     for (; ks + 2 < nk; ++ks) {
-        read_frags(ks, 1, f1);
-        mma(f0);
-        interleave_reads();
         wait_vmcnt<RD.wait>();
         lds_barrier();
         issueA(ks + NA);
         issueB(ks + NB);
         read_frags(ks + 1, 0, f0);
         mma(f1);
-        interleave_loads();
-    }
-    for (; ks < nk; ++ks) {
-        read_frags(ks, 1, f1);
+        read_frags(ks + 1, 1, f1);
         mma(f0);
-        interleave_reads();
-        if (ks + 1 < nk) {
-            wait_vmcnt<RD.wait>();
-            lds_barrier();
-            read_frags(ks + 1, 0, f0);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * NMMA / NV > 0 ? 2 * NMMA / NV : 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * NF / NV > 0 ? 2 * NF / NV : 1, 0);       // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                        // load
         }
-        mma(f1);
-        interleave_reads();
+        __builtin_amdgcn_sched_barrier(0);
     }
+    for (; ks + 1 < nk; ++ks) {      // last region with a next slice: no batch left to issue
+        wait_vmcnt<RD.wait>();
+        lds_barrier();
+        read_frags(ks + 1, 0, f0);
+        mma(f1);
+        read_frags(ks + 1, 1, f1);
+        mma(f0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    mma(f1);
+    __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();   // reloads of the last slice may still be landing
 
     if constexpr (SPLIT) Epi::store_partial(p, acc, unit, wave, lane);
@@ -495,20 +489,22 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
 #endif
 }
 
-// Split-K fixup: block (t, w) adds the `split` partial accumulators of wave
-// w of tail tile t in range order and applies the epilogue.
+// Split-K fixup: block (t, w, g) adds, in range order, the `split` partial
+// accumulators of column group g of wave w of tail tile t, and applies the
+// epilogue to them.
 template <bool BF16, int BM, int BN, int EPI>
 __global__ __launch_bounds__(64) void k_split_fixup(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     typedef GemmEpilogue<BF16, BM, BN, EPI> Epi;
-    constexpr int FM = Epi::FM, FN = Epi::FN, RA = Epi::RA;
+    constexpr int FM = Epi::FM, FN = Epi::FN, RA = Epi::RA, IG = Epi::IG, NGRP = FN / IG;
     const int full = p.plan[p.E + 1], split = p.plan[p.E + 2], tail = p.plan[p.E + 3];
-    const int t = blockIdx.x >> 2, w = blockIdx.x & 3, lane = threadIdx.x;
+    const int t = blockIdx.x / (4 * NGRP), w = (blockIdx.x / NGRP) % 4, i0 = (blockIdx.x % NGRP) * IG;
+    const int lane = threadIdx.x;
     if (split <= 1 || t >= tail) return;
-    typename Epi::acc_t acc[FN][FM];
+    typename Epi::acc_t acc[IG][FM];
     const float4* src = (const float4*)p.partial;
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
+    for (int i = 0; i < IG; ++i)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
 #pragma unroll
@@ -516,12 +512,12 @@ __global__ __launch_bounds__(64) void k_split_fixup(GemmParams p) {
     for (int c = 0; c < split; ++c) {
         const int u = t * split + c;
 #pragma unroll
-        for (int i = 0; i < FN; ++i)
+        for (int i = 0; i < IG; ++i)
 #pragma unroll
             for (int j = 0; j < FM; ++j)
 #pragma unroll
                 for (int r4 = 0; r4 < RA / 4; ++r4) {
-                    const float4 v = src[Epi::partial_index(u, w, i, j, r4, lane)];
+                    const float4 v = src[Epi::partial_index(u, w, i0 + i, j, r4, lane)];
                     acc[i][j][4 * r4] += v.x;
                     acc[i][j][4 * r4 + 1] += v.y;
                     acc[i][j][4 * r4 + 2] += v.z;
@@ -532,7 +528,7 @@ __global__ __launch_bounds__(64) void k_split_fixup(GemmParams p) {
     decode_tile(p, full + t, e, mt, nt);
     const int row0 = p.offsets[e] + mt * BM;
     const int rows = min(BM, p.offsets[e + 1] - row0);
-    Epi::store(p, acc, row0, rows, nt, w >> 1, w & 1, lane);
+    Epi::store_cols(p, acc, i0, row0, rows, nt, w >> 1, w & 1, lane);
 #endif
 }
 
@@ -609,7 +605,8 @@ template <bool BF16, int BM, int BN, int EPI>
 static void launch_pair(const GemmParams& p, int grid, hipStream_t s) {
     hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, false>), dim3(grid), dim3(256), 0, s, p);
     hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, true>), dim3(kSplitUnits), dim3(256), 0, s, p);
-    hipLaunchKernelGGL((k_split_fixup<BF16, BM, BN, EPI>), dim3(kSplitUnits / 2 * 4), dim3(64), 0, s, p);
+    constexpr int groups = GemmEpilogue<BF16, BM, BN, EPI>::FN / GemmEpilogue<BF16, BM, BN, EPI>::IG;
+    hipLaunchKernelGGL((k_split_fixup<BF16, BM, BN, EPI>), dim3(kSplitUnits / 2 * 4 * groups), dim3(64), 0, s, p);
 }
 
 template <bool BF16, int BM, int BN>
