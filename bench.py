@@ -94,13 +94,18 @@ def cpu_baseline(cfg, dinp, target_s):
         oracle.forward(c, sub, noise="philox")
         return time.perf_counter() - t0
 
-    ts = min(8, cfg.T)
-    t_small = run(ts)
-    if t_small < target_s / 4 and ts < cfg.T:
-        ts = int(min(cfg.T, max(ts, ts * target_s / max(t_small, 1e-3))))
-        t = run(ts)
+    # two probes give the per-token slope and the fixed per-call cost (the
+    # oracle converts every weight to fp64 on each call), then one run sized
+    # for target_s
+    t1 = run(min(8, cfg.T))
+    if cfg.T <= 8 or t1 >= target_s:
+        ts, t = min(8, cfg.T), t1
     else:
-        t = t_small
+        t2 = run(min(32, cfg.T))
+        slope = max((t2 - t1) / (min(32, cfg.T) - 8), 1e-6)
+        fixed = max(t1 - 8 * slope, 0.0)
+        ts = int(min(cfg.T, max(32, (target_s - fixed) / slope)))
+        t = run(ts) if ts > 32 else t2
     return {"value": ts / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {ts} of the {cfg.T} tokens, whole layer (route, dispatch, experts, combine) "
                       f"with all weights, {t:.1f} s of oracle time"}
