@@ -70,8 +70,20 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ hist,
     int32_t c = 0, kp = 0;
     double fe = 0.0;
     if (e < E) {
+        // column scan over the blocks, 16 loads in flight at a time
         int32_t run = 0;
-        for (int b = 0; b < nblocks; ++b) {
+        int b = 0;
+        for (; b + 16 <= nblocks; b += 16) {
+            int32_t h[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) h[u] = hist[(int64_t)(b + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                blockbase[(int64_t)(b + u) * E + e] = run;
+                run += h[u];
+            }
+        }
+        for (; b < nblocks; ++b) {
             blockbase[(int64_t)b * E + e] = run;
             run += hist[(int64_t)b * E + e];
         }

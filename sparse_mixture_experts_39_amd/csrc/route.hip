@@ -15,7 +15,7 @@
 //                   (NC = E, or 2E for the noisy gate whose second half is x W_noise)
 //   k_select        G lanes per token: scores, k passes of a segmented arg-max,
 //                   gates, router probabilities, per-block P partial sums
-//   k_reduce_P      fixed-order sum of the per-block partials -> P[E]
+//   k_reduce_P      fixed-order two-level sum of the per-block partials -> P[E]
 #include "device_common.h"
 #include "canon_math.h"
 #include "kernels.h"
@@ -326,17 +326,46 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ dots, 
     if (bad) status[0] = MOE_DEV_NONFINITE;  // benign race: every writer stores the same value
 }
 
-__global__ void k_reduce_P(const float* __restrict__ P_part, int nblocks, int E, int T, float* __restrict__ P_ws,
-                           float* __restrict__ P_out, const int32_t* __restrict__ status_ws,
-                           int32_t* __restrict__ status_out) {
-    const int e = blockIdx.x * blockDim.x + threadIdx.x;
-    if (e == 0 && status_out) status_out[0] = status_ws[0];
-    if (e >= E) return;
-    float s = 0.0f;
-    for (int b = 0; b < nblocks; ++b) s = s + P_part[(int64_t)b * E + e];
-    const float p = T > 0 ? s / (float)T : 0.0f;
-    P_ws[e] = p;
-    if (P_out) P_out[e] = p;
+// P[e] = (sum of the per-block partials) / T.  A block covers 64 experts
+// with 16 waves; wave w sums its contiguous range of partial blocks with 8
+// interleaved accumulators (so 8 loads are in flight), then the 8 and the 16
+// wave sums are added in a fixed order: the result does not depend on timing.
+__global__ __launch_bounds__(1024) void k_reduce_P(const float* __restrict__ P_part, int nblocks, int E, int T,
+                                                   float* __restrict__ P_ws, float* __restrict__ P_out,
+                                                   const int32_t* __restrict__ status_ws,
+                                                   int32_t* __restrict__ status_out) {
+    __shared__ float part[16][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int e = blockIdx.x * 64 + lane;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && status_out) status_out[0] = status_ws[0];
+    const int chunk = (nblocks + 15) / 16;
+    const int b0 = min(nblocks, w * chunk), b1 = min(nblocks, b0 + chunk);
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f, a4 = 0.0f, a5 = 0.0f, a6 = 0.0f, a7 = 0.0f, r = 0.0f;
+    if (e < E) {
+        const float* src = P_part + e;
+        int b = b0;
+        for (; b + 8 <= b1; b += 8) {
+            a0 = a0 + src[(int64_t)(b + 0) * E];
+            a1 = a1 + src[(int64_t)(b + 1) * E];
+            a2 = a2 + src[(int64_t)(b + 2) * E];
+            a3 = a3 + src[(int64_t)(b + 3) * E];
+            a4 = a4 + src[(int64_t)(b + 4) * E];
+            a5 = a5 + src[(int64_t)(b + 5) * E];
+            a6 = a6 + src[(int64_t)(b + 6) * E];
+            a7 = a7 + src[(int64_t)(b + 7) * E];
+        }
+        for (; b < b1; ++b) r = r + src[(int64_t)b * E];
+    }
+    part[w][lane] = (((a0 + a1) + (a2 + a3)) + ((a4 + a5) + (a6 + a7))) + r;
+    __syncthreads();
+    if (w == 0 && e < E) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s = s + part[i][lane];
+        const float p = T > 0 ? s / (float)T : 0.0f;
+        P_ws[e] = p;
+        if (P_out) P_out[e] = p;
+    }
 }
 
 __global__ void k_zero_i32(int32_t* p, int n) {
@@ -421,7 +450,7 @@ void launch_select(const float* dots, int NC, const float* logit_bias, const flo
 
 void launch_reduce_P(const float* P_part, int nblocks, int E, int T, float* P_ws, float* P_out,
                      const int32_t* status_ws, int32_t* status_out, hipStream_t s) {
-    hipLaunchKernelGGL(k_reduce_P, dim3((E + 255) / 256), dim3(256), 0, s, P_part, nblocks, E, T, P_ws, P_out,
+    hipLaunchKernelGGL(k_reduce_P, dim3((E + 63) / 64), dim3(1024), 0, s, P_part, nblocks, E, T, P_ws, P_out,
                        status_ws, status_out);
 }
 
