@@ -71,7 +71,7 @@ def lib():
         L.oc_normal_batch.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64, P]
         L.oc_philox4x32_10.argtypes = [P, P, P]
         L.oc_route.restype = ctypes.c_int
-        L.oc_route.argtypes = [ctypes.POINTER(_Cfg)] + [P] * 13
+        L.oc_route.argtypes = [ctypes.POINTER(_Cfg)] + [P] * 14
         L.oc_capacity.restype = ctypes.c_int64
         L.oc_capacity.argtypes = [ctypes.POINTER(_Cfg)]
         L.oc_dispatch.restype = ctypes.c_int64
@@ -80,6 +80,9 @@ def lib():
         L.oc_expert_ffn.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int32, P, ctypes.c_int64, P, P, P, P]
         L.oc_combine.argtypes = [ctypes.POINTER(_Cfg), P, ctypes.c_int64, P, P, P, P, P, P]
         L.oc_stats.argtypes = [ctypes.POINTER(_Cfg), P, P, P, P, P, P, P]
+        L.oc_balance.restype = ctypes.c_int
+        L.oc_balance.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int32] + [P] * 12
+        L.oc_update_bias.argtypes = [ctypes.c_int32, P, ctypes.c_float, P]
         _lib = L
     return _lib
 
@@ -193,13 +196,17 @@ def route(cfg, x, w_router, *, logit_bias=None, sel_bias=None, w_noise=None, noi
     probs = np.empty((T, E), dtype=np.float64) if want_probs else None
     P = np.empty(E, dtype=np.float64)
     status = np.zeros(1, dtype=np.int32)
+    nscale = np.empty((T, E), dtype=np.float32) if cfg.gate == "noisy_topk" else None
     rc = lib().oc_route(ctypes.byref(c), _ptr(xa), _ptr(wr), _ptr(lb), _ptr(sb), _ptr(wn), _ptr(nz),
-                        _ptr(idx), _ptr(gates), _ptr(keys), _ptr(logits), _ptr(probs), _ptr(P), _ptr(status))
+                        _ptr(idx), _ptr(gates), _ptr(keys), _ptr(logits), _ptr(probs), _ptr(P), _ptr(status),
+                        _ptr(nscale))
     if rc != 0:
         raise ValueError("oracle route rejected the configuration")
     out = dict(idx=idx, gates=gates, keys=keys, logits=logits, P=P, status=int(status[0]))
     if want_probs:
         out["probs"] = probs
+    if nscale is not None:
+        out["noise_scale"] = nscale
     return out
 
 
@@ -275,6 +282,38 @@ def stats(cfg, counts, kept, P, T: int) -> Dict[str, object]:
     aux = np.zeros(1, np.float64)
     lib().oc_stats(ctypes.byref(c), _ptr(counts), _ptr(kept), _ptr(P), _ptr(f), _ptr(nd), _ptr(imb), _ptr(aux))
     return dict(f=f, n_dropped=int(nd[0]), imbalance=float(imb[0]), aux=float(aux[0]))
+
+
+def balance(cfg, r, seq_len: int = 0) -> Dict[str, object]:
+    """Router z-loss, importance and load (with their CV^2) and the
+    sequence-wise balance term from the outputs of route(..., want_probs=True)."""
+    T = r["idx"].shape[0]
+    c = make_cfg(cfg, T=T)
+    E = cfg.E
+    imp = np.empty(E, np.float64)
+    load = np.full(E, np.nan, np.float64)
+    z = np.zeros(1, np.float64)
+    icv = np.zeros(1, np.float64)
+    lcv = np.full(1, np.nan, np.float64)
+    sa = np.zeros(1, np.float64)
+    ns = r.get("noise_scale")
+    rc = lib().oc_balance(ctypes.byref(c), int(seq_len), _ptr(_np(r["logits"], np.float32)),
+                          _ptr(_np(r["keys"], np.float32)), _ptr(None if ns is None else _np(ns, np.float32)),
+                          _ptr(_np(r["probs"], np.float64)), _ptr(_np(r["idx"], np.int32)),
+                          _ptr(_np(r["gates"], np.float64)), _ptr(z), _ptr(imp), _ptr(icv), _ptr(load),
+                          _ptr(lcv), _ptr(sa))
+    if rc != 0:
+        raise ValueError("seq_len must divide T")
+    return dict(z_loss=float(z[0]), importance=imp, importance_cv2=float(icv[0]), load=load,
+                load_cv2=float(lcv[0]), seq_aux=float(sa[0]))
+
+
+def update_bias(counts, bias, gamma: float) -> np.ndarray:
+    """The auxiliary-loss-free bias step b += gamma * sign(mean count - count)."""
+    counts = _np(counts, np.int32)
+    b = np.array(_np(bias, np.float32), dtype=np.float32, copy=True)
+    lib().oc_update_bias(int(counts.shape[0]), _ptr(counts), ctypes.c_float(gamma), _ptr(b))
+    return b
 
 
 # --------------------------------------------------------------------------

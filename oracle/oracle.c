@@ -330,13 +330,15 @@ static inline int32_t order_key(float f) {
  * softmax gates, softmax(H) for the noisy gate, s / sum(s) for the sigmoid.
  *
  * Outputs: idx [T][k], gates [T][k], optional keys [T][E] (fp32), optional
- * logits [T][E] (fp32), optional probs [T][E], P [E].  *status gets bit 0 if
- * any key was not finite.
+ * logits [T][E] (fp32), optional probs [T][E], P [E], and for the noisy gate
+ * the optional noise scale softplus(x W_noise) [T][E] (fp32).  *status gets
+ * bit 0 if any key was not finite.
  */
 OC_EXPORT int oc_route(const oc_config* cfg, const void* x, const float* w_router,
                        const float* logit_bias, const float* sel_bias, const float* w_noise,
                        const float* noise, int32_t* idx, double* gates, float* keys_out,
-                       float* logits_out, double* probs_out, double* P, int32_t* status) {
+                       float* logits_out, double* probs_out, double* P, int32_t* status,
+                       float* noise_scale_out) {
     const int T = cfg->T, d = cfg->d, E = cfg->E, k = cfg->k;
     if (k < 1 || k > E) return -1;
     if (cfg->gate == OC_NOISY_TOPK && !w_noise) return -1;
@@ -363,7 +365,9 @@ OC_EXPORT int oc_route(const oc_config* cfg, const void* x, const float* w_route
                     float zn = dot_c(xr, cfg->act_bf16, w_noise + (size_t)e * d, d);
                     float n = noise ? noise[(size_t)t * E + e]
                                     : oc_normal(cfg->seed, cfg->noise_offset, (uint64_t)t * (uint64_t)E + (uint64_t)e);
-                    ke = fmaf(n, oc_softplus(zn), ze);
+                    const float sc = oc_softplus(zn);
+                    if (noise_scale_out) noise_scale_out[(size_t)t * E + e] = sc;
+                    ke = fmaf(n, sc, ze);
                 } else if (cfg->gate == OC_SIGMOID_BIAS) {
                     float s = oc_sigmoid(ze);
                     ke = sel_bias ? s + sel_bias[e] : s;
@@ -596,4 +600,134 @@ OC_EXPORT void oc_stats(const oc_config* cfg, const int32_t* counts, const int32
     *n_dropped = (int64_t)tk - kept_sum;
     *imbalance = (double)nmax / (tk / (double)E);
     *aux = (double)E * a;
+}
+
+/* ------------------------------------------------------------------------ */
+/* balance and stability statistics                                         */
+/* ------------------------------------------------------------------------ */
+
+/* Standard normal CDF, Phi(x) = erfc(-x / sqrt(2)) / 2 (fp64 libm). */
+static double oc_phi(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
+
+/*
+ * Statistics the pages attach to the router, computed from the route's
+ * per-token outputs (logits z [T][E], selection keys [T][E], the noisy
+ * gate's noise scale softplus(x W_noise) [T][E] or NULL, probabilities
+ * p [T][E], idx and gates [T][k]).  All fp64.
+ *
+ *   z_loss = mean_t (log sum_e exp z_t,e)^2: the router z-loss, the squared
+ *     log of the softmax normaliser (CS336 notes section 11; awesome-ai-
+ *     roadmap 19.6.2 table: the squared logsumexp of the logits).  Taken
+ *     over the clean logits z for every gate.
+ *   importance_e = sum_t G(x_t)_e, the gate values an expert receives
+ *     (Shazeer notes: Importance, balanced through CV^2); importance_cv2 =
+ *     Var/mean^2 over the experts (CV = std / mean, population std).
+ *   load_e = sum_t P(x_t, e) for the noisy gate, with
+ *     P(x, e) = Phi((z_e - kth_excluding(H(x), k, e)) / softplus((x W_noise)_e))
+ *     (Shazeer notes, Load(X) and Phi, eq. 9): kth_excluding is the k-th
+ *     largest noisy score other than e's own, i.e. the (k+1)-th largest of H
+ *     when e is among the top k and the k-th largest otherwise; with k = E
+ *     every expert is always chosen and P = 1.  load_cv2 as above.  Left
+ *     untouched when noise_scale is NULL.
+ *   seq_aux = mean over sequences of E * sum_e f_e^s P_e^s, the balance term
+ *     counted per sequence (CS336 notes section 9: V3 keeps a complementary
+ *     sequence-level auxiliary loss; awesome-ai-roadmap 19.3.4), with
+ *     f_e^s = n_e^s / (L k) from the selections of the sequence's L tokens
+ *     and P_e^s their mean probability; seq_len <= 0 means one sequence of
+ *     all T tokens (then seq_aux equals the batch aux).
+ * Returns -1 when seq_len does not divide T.
+ */
+OC_EXPORT int oc_balance(const oc_config* cfg, int32_t seq_len, const float* logits, const float* keys,
+                         const float* noise_scale, const double* probs, const int32_t* idx, const double* gates,
+                         double* z_loss, double* importance, double* importance_cv2, double* load, double* load_cv2,
+                         double* seq_aux) {
+    const int T = cfg->T, E = cfg->E, k = cfg->k;
+    const int L = seq_len > 0 ? seq_len : T;
+    if (T > 0 && (L <= 0 || T % L != 0)) return -1;
+    double zsum = 0.0;
+    for (int e = 0; e < E; ++e) { importance[e] = 0.0; if (noise_scale) load[e] = 0.0; }
+    unsigned char* sel = (unsigned char*)malloc((size_t)(E > 0 ? E : 1));
+    for (int t = 0; t < T; ++t) {
+        const float* z = logits + (size_t)t * E;
+        double m = -INFINITY;
+        for (int e = 0; e < E; ++e) if ((double)z[e] > m) m = (double)z[e];
+        double s = 0.0;
+        for (int e = 0; e < E; ++e) s += exp((double)z[e] - m);
+        const double lse = m + log(s);
+        zsum += lse * lse;
+        for (int j = 0; j < k; ++j) importance[idx[(size_t)t * k + j]] += gates[(size_t)t * k + j];
+        if (noise_scale) {
+            const float* h = keys + (size_t)t * E;
+            memset(sel, 0, (size_t)E);
+            for (int j = 0; j < k; ++j) sel[idx[(size_t)t * k + j]] = 1;
+            /* k-th largest key = the smallest selected one; (k+1)-th = the
+               largest unselected one */
+            double kth = INFINITY, next = -INFINITY;
+            for (int e = 0; e < E; ++e) {
+                if (sel[e]) { if ((double)h[e] < kth) kth = (double)h[e]; }
+                else if ((double)h[e] > next) next = (double)h[e];
+            }
+            for (int e = 0; e < E; ++e) {
+                double pe;
+                if (k >= E) pe = 1.0;
+                else {
+                    const double thr = sel[e] ? next : kth;
+                    pe = oc_phi(((double)z[e] - thr) / (double)noise_scale[(size_t)t * E + e]);
+                }
+                load[e] += pe;
+            }
+        }
+    }
+    free(sel);
+    *z_loss = T > 0 ? zsum / (double)T : 0.0;
+    /* CV^2 = population variance / mean^2 */
+    for (int pass = 0; pass < 2; ++pass) {
+        const double* v = pass == 0 ? importance : load;
+        double* out = pass == 0 ? importance_cv2 : load_cv2;
+        if (pass == 1 && !noise_scale) break;
+        double mean = 0.0;
+        for (int e = 0; e < E; ++e) mean += v[e];
+        mean /= (double)E;
+        double var = 0.0;
+        for (int e = 0; e < E; ++e) var += (v[e] - mean) * (v[e] - mean);
+        var /= (double)E;
+        *out = mean != 0.0 ? var / (mean * mean) : 0.0;
+    }
+    /* sequence-wise balance term */
+    double acc = 0.0;
+    const int nseq = T > 0 ? T / L : 0;
+    double* Ps = (double*)malloc(sizeof(double) * (size_t)(E > 0 ? E : 1));
+    int64_t* ns = (int64_t*)malloc(sizeof(int64_t) * (size_t)(E > 0 ? E : 1));
+    for (int sq = 0; sq < nseq; ++sq) {
+        for (int e = 0; e < E; ++e) { Ps[e] = 0.0; ns[e] = 0; }
+        for (int t = sq * L; t < (sq + 1) * L; ++t) {
+            for (int e = 0; e < E; ++e) Ps[e] += probs[(size_t)t * E + e];
+            for (int j = 0; j < k; ++j) ns[idx[(size_t)t * k + j]] += 1;
+        }
+        double a = 0.0;
+        for (int e = 0; e < E; ++e) a += ((double)ns[e] / ((double)L * k)) * (Ps[e] / (double)L);
+        acc += (double)E * a;
+    }
+    free(Ps); free(ns);
+    *seq_aux = nseq > 0 ? acc / (double)nseq : 0.0;
+    return 0;
+}
+
+/*
+ * Auxiliary-loss-free balancing (CS336 notes section 9; awesome-ai-roadmap
+ * 19.3.4): after a batch, every expert's selection bias moves by gamma
+ * towards balance, up when the expert received fewer assignments than the
+ * mean, down when more, unchanged when equal:
+ *   b_e += gamma * sign(mean - n_e),  mean = sum_e n_e / E.
+ * The comparison n_e * E <=> sum n is exact in integers.  The bias only
+ * enters the selection keys, never the gates.
+ */
+OC_EXPORT void oc_update_bias(int32_t E, const int32_t* counts, float gamma, float* bias) {
+    int64_t total = 0;
+    for (int e = 0; e < E; ++e) total += counts[e];
+    for (int e = 0; e < E; ++e) {
+        const int64_t c = (int64_t)counts[e] * E;
+        if (c < total) bias[e] = bias[e] + gamma;
+        else if (c > total) bias[e] = bias[e] - gamma;
+    }
 }
