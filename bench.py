@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--balance-stats", action="store_true",
+                    help="also request the balance statistics (z-loss, importance, load, seq_aux) from the route stage")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "mixtral_expert_up_hbm_traffic.md"),
                     help="rocprofv3 counter summary giving the dominant kernel's HBM bytes per launch")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -155,7 +157,7 @@ def main():
                    n_shared=cfg.n_shared, d_ff_shared=cfg.F_shared, seed=cfg.seed)
     w = moe.weights_from(c, dinp)
     ws = moe.workspace(c)
-    st = moe.alloc_stats(c)
+    st = moe.alloc_stats(c, balance=args.balance_stats)
     T, E, k, d, F = c.T, c.n_experts, c.top_k, c.d_model, c.d_ff
     R = moe.max_rows(c)
     dt = dinp["x"].dtype

@@ -104,6 +104,9 @@ typedef struct {
     uint32_t flags;         /* MOE_F_* */
     uint64_t seed;          /* Philox key of the noisy gate */
     uint64_t noise_offset;  /* Philox counter offset (words 2,3) of the noisy gate */
+    int32_t seq_len;        /* tokens per sequence for stats.seq_aux: 0 = the whole call is one
+                               sequence, else a multiple of 256 that divides T */
+    int32_t reserved;       /* must be 0 */
 } moe_config;
 
 /* Weights of one layer (device pointers). */
@@ -138,6 +141,27 @@ typedef struct {
     float* imbalance;       /* [1] */
     float* aux;             /* [1] */
     int32_t* device_status; /* [1] MOE_DEV_* bits, written by moe_route */
+    /* Balance and stability statistics, written by moe_route when any of
+     * them is requested (all fp32, fixed summation orders):
+     * z_loss = mean over tokens of (log sum_e exp z_t,e)^2 over the clean
+     *   router logits, the router z-loss (CS336 notes section 11;
+     *   awesome-ai-roadmap 19.6.2 table);
+     * importance_e = sum over tokens of the gate expert e receives, and its
+     *   CV^2 = Var / mean^2 over the experts (population variance)
+     *   (Shazeer notes, Importance and CV);
+     * load_e = sum_t Phi((z_t,e - kth_excluding(H_t, k, e)) / softplus((x W_noise)_t,e)),
+     *   the smooth load estimate of the noisy gate, and its CV^2 (Shazeer
+     *   notes, Load(X) and eq. 9); NOISY_TOPK only, untouched otherwise;
+     * seq_aux = mean over sequences of seq_len tokens of E sum_e f_e P_e
+     *   counted within the sequence (CS336 notes section 9: V3's
+     *   complementary sequence-level balance term; awesome-ai-roadmap
+     *   19.3.4). */
+    float* z_loss;          /* [1] */
+    float* importance;      /* [E] */
+    float* importance_cv2;  /* [1] */
+    float* load;            /* [E] */
+    float* load_cv2;        /* [1] */
+    float* seq_aux;         /* [1] */
 } moe_stats;
 
 /* ---- pure host helpers (no device work, usable without a GPU) ---------- */
@@ -229,6 +253,17 @@ moe_status moe_shared_expert(const moe_config* cfg, const void* x, const moe_wei
 moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_pos,
                        const float* topk_gate, const void* residual, const void* shared_out,
                        void* out, void* stream);
+
+/* Auxiliary-loss-free balancing step (CS336 notes section 9: after each
+ * batch an underloaded expert's bias goes up by gamma and an overloaded one's
+ * down; awesome-ai-roadmap 19.3.4: the bias corrects only the scores used for
+ * selection).  For every expert e:
+ *   sel_bias[e] += gamma * sign(mean - counts[e]),  mean = sum_e counts[e] / E,
+ * with the comparison done exactly in integers (counts[e] * E vs the sum).
+ * counts: [E] int32 device (e.g. stats.counts of the last call); sel_bias:
+ * [E] fp32 device, updated in place.  Returns MOE_ERR_INVALID_ARG for NULL
+ * pointers or a non-finite gamma. */
+moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float gamma, float* sel_bias, void* stream);
 
 /* The whole layer: route, dispatch, experts (+ shared expert), combine, with
  * every intermediate carved from ws.  x [T][d], out [T][d].  The residual is

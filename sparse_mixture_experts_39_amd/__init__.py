@@ -34,7 +34,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "wo
 EXPORTED_SYMBOLS = (
     "moe_validate_config", "moe_workspace_size", "moe_max_rows", "moe_capacity", "moe_last_hip_error",
     "moe_status_string", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
-    "moe_shared_expert", "moe_combine", "moe_layer_forward",
+    "moe_shared_expert", "moe_combine", "moe_layer_forward", "moe_update_bias",
 )
 
 
@@ -54,6 +54,7 @@ class MoeConfig(ctypes.Structure):
         ("d_ff_shared", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("act", ctypes.c_int32),
         ("gate", ctypes.c_int32), ("capacity_factor", ctypes.c_float), ("flags", ctypes.c_uint32),
         ("seed", ctypes.c_uint64), ("noise_offset", ctypes.c_uint64),
+        ("seq_len", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -65,7 +66,8 @@ class MoeWeights(ctypes.Structure):
 
 class MoeStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "counts", "kept", "f", "P", "n_dropped", "imbalance", "aux", "device_status")]
+        "counts", "kept", "f", "P", "n_dropped", "imbalance", "aux", "device_status",
+        "z_loss", "importance", "importance_cv2", "load", "load_cv2", "seq_aux")]
 
 
 _lib = None
@@ -109,6 +111,8 @@ def lib():
         L.moe_combine.argtypes = [C, P, P, P, P, P, P, P]
         L.moe_layer_forward.restype = ctypes.c_int
         L.moe_layer_forward.argtypes = [C, W, P, P, S, P, sz, P]
+        L.moe_update_bias.restype = ctypes.c_int
+        L.moe_update_bias.argtypes = [C, P, ctypes.c_float, P, P]
         _lib = L
     return _lib
 
@@ -118,7 +122,7 @@ def lib():
 def config(*, T: int, d_model: int, d_ff: int, n_experts: int, top_k: int, act_dtype: str = "bf16",
            act: str = "swiglu", gate: str = "softmax_topk", capacity_factor: float = 0.0,
            residual: bool = False, n_shared: int = 0, d_ff_shared: int = 0, noise_input: bool = False,
-           seed: int = 0, noise_offset: int = 0) -> MoeConfig:
+           seed: int = 0, noise_offset: int = 0, seq_len: int = 0) -> MoeConfig:
     c = MoeConfig()
     c.T, c.d_model, c.d_ff, c.n_experts, c.top_k = T, d_model, d_ff, n_experts, top_k
     c.n_shared, c.d_ff_shared = n_shared, d_ff_shared
@@ -128,6 +132,7 @@ def config(*, T: int, d_model: int, d_ff: int, n_experts: int, top_k: int, act_d
     c.capacity_factor = capacity_factor
     c.flags = (MOE_F_ADD_RESIDUAL if residual else 0) | (MOE_F_NOISE_INPUT if noise_input else 0)
     c.seed, c.noise_offset = seed, noise_offset
+    c.seq_len = seq_len
     return c
 
 
@@ -182,12 +187,20 @@ def weights_from(c: MoeConfig, t: Dict[str, torch.Tensor]) -> MoeWeights:
     return w
 
 
-def alloc_stats(c: MoeConfig, device="cuda") -> Dict[str, torch.Tensor]:
+def alloc_stats(c: MoeConfig, device="cuda", balance: bool = False) -> Dict[str, torch.Tensor]:
+    """Device buffers for moe_stats; balance=True adds the balance and
+    stability statistics (z_loss, importance, load, their CV^2, seq_aux),
+    which makes moe_route run their kernels."""
     E = c.n_experts
     i32, f32 = dict(dtype=torch.int32, device=device), dict(dtype=torch.float32, device=device)
-    return dict(counts=torch.zeros(E, **i32), kept=torch.zeros(E, **i32), f=torch.zeros(E, **f32),
-                P=torch.zeros(E, **f32), n_dropped=torch.zeros(1, **i32), imbalance=torch.zeros(1, **f32),
-                aux=torch.zeros(1, **f32), device_status=torch.zeros(1, **i32))
+    st = dict(counts=torch.zeros(E, **i32), kept=torch.zeros(E, **i32), f=torch.zeros(E, **f32),
+              P=torch.zeros(E, **f32), n_dropped=torch.zeros(1, **i32), imbalance=torch.zeros(1, **f32),
+              aux=torch.zeros(1, **f32), device_status=torch.zeros(1, **i32))
+    if balance:
+        st.update(z_loss=torch.zeros(1, **f32), importance=torch.zeros(E, **f32),
+                  importance_cv2=torch.zeros(1, **f32), load=torch.full((E,), float("nan"), **f32),
+                  load_cv2=torch.full((1,), float("nan"), **f32), seq_aux=torch.zeros(1, **f32))
+    return st
 
 
 def _stats_struct(st: Optional[Dict[str, torch.Tensor]]) -> Optional[MoeStats]:
@@ -311,3 +324,11 @@ def moe_layer_forward(c: MoeConfig, w: MoeWeights, x, out, stats=None, ws=None, 
                                  _ptr(ws, torch.uint8, name="ws"), ws.numel() if ws is not None else 0,
                                  _stream(stream))
     _check("moe_layer_forward", rc)
+
+
+def moe_update_bias(c: MoeConfig, counts, gamma: float, sel_bias, stream=None):
+    """sel_bias += gamma * sign(mean(counts) - counts), in place on the device."""
+    E = c.n_experts
+    rc = lib().moe_update_bias(ctypes.byref(c), _ptr(counts, torch.int32, (E,), "counts"), ctypes.c_float(gamma),
+                               _ptr(sel_bias, torch.float32, (E,), "sel_bias"), _stream(stream))
+    _check("moe_update_bias", rc)

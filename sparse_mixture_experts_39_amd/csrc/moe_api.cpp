@@ -43,6 +43,7 @@ struct Layout {
     size_t idx, gates, slot_pos, perm_src, offsets;       // whole-layer intermediates
     size_t x_perm, y_perm, shared_out;
     size_t partial;                                       // split-K accumulators
+    size_t imp_part, load_part, z_part, imp_ws, load_ws, z_ws, seq_part;   // balance statistics
     size_t total;
 };
 
@@ -102,6 +103,14 @@ Layout compute_layout(const moe_config* c) {
     L.y_perm = take((size_t)R * c->d_model * es);
     L.shared_out = take(sh ? (size_t)T * c->d_model * es : 0);
     L.partial = take(partial_bytes_of(c));
+    const size_t sb = T > 0 ? (size_t)moe::select_blocks(T, E) : 0;
+    L.imp_part = take(sb * E * sizeof(float));
+    L.load_part = take(sb * E * sizeof(float));
+    L.z_part = take(sb * sizeof(float));
+    L.imp_ws = take((size_t)E * sizeof(float));
+    L.load_ws = take((size_t)E * sizeof(float));
+    L.z_ws = take(sizeof(float));
+    L.seq_part = take((size_t)(T / 256 + 1) * sizeof(float));
     L.total = o;
     return L;
 }
@@ -142,6 +151,8 @@ moe_status moe_validate_config(const moe_config* c) {
     if (c->d_model % 64 || c->d_ff % 64) return MOE_ERR_UNSUPPORTED;
     if (c->n_shared == 1 && (c->d_ff_shared % 64 || c->act != MOE_ACT_SWIGLU)) return MOE_ERR_UNSUPPORTED;
     if ((int64_t)c->T * c->top_k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    if (c->reserved != 0 || c->seq_len < 0) return MOE_ERR_INVALID_ARG;
+    if (c->seq_len > 0 && (c->seq_len % 256 != 0 || c->T % c->seq_len != 0)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -202,6 +213,21 @@ moe_status moe_route(const moe_config* c, const void* x, const moe_weights* w, i
                        at<float>(ws, L.P_part), status, h);
     moe::launch_reduce_P(at<float>(ws, L.P_part), T > 0 ? moe::select_blocks(T, E) : 0, E, T, at<float>(ws, L.P_ws),
                          st ? st->P : nullptr, status, st ? st->device_status : nullptr, h);
+    const bool balance = st && (st->z_loss || st->importance || st->importance_cv2 || st->load || st->load_cv2 ||
+                                st->seq_aux);
+    if (balance)
+        moe::launch_balance(dots, NC, w->logit_bias, noise, c->gate, T, E, c->top_k, c->seed, c->noise_offset,
+                            topk_idx, topk_gate, at<float>(ws, L.P_part), c->seq_len, at<float>(ws, L.imp_part),
+                            at<float>(ws, L.load_part), at<float>(ws, L.z_part), at<float>(ws, L.imp_ws),
+                            at<float>(ws, L.load_ws), at<float>(ws, L.z_ws), at<float>(ws, L.seq_part), st, h);
+    return after_launch();
+}
+
+moe_status moe_update_bias(const moe_config* c, const int32_t* counts, float gamma, float* sel_bias, void* stream) {
+    moe_status s = moe_validate_config(c);
+    if (s != MOE_OK) return s;
+    if (!counts || !sel_bias || !(gamma == gamma) || gamma - gamma != 0.0f) return MOE_ERR_INVALID_ARG;
+    moe::launch_update_bias(counts, c->n_experts, gamma, sel_bias, (hipStream_t)stream);
     return after_launch();
 }
 

@@ -16,6 +16,9 @@
 //   k_select        G lanes per token: scores, k passes of a segmented arg-max,
 //                   gates, router probabilities, per-block P partial sums
 //   k_reduce_P      fixed-order two-level sum of the per-block partials -> P[E]
+//   k_balance       (when requested) z-loss, importance and load partials;
+//                   k_column_sums, k_seq_aux, k_balance_final reduce them
+//   k_update_bias   the auxiliary-loss-free bias step
 #include "device_common.h"
 #include "canon_math.h"
 #include "kernels.h"
@@ -326,23 +329,20 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ dots, 
     if (bad) status[0] = MOE_DEV_NONFINITE;  // benign race: every writer stores the same value
 }
 
-// P[e] = (sum of the per-block partials) / T.  A block covers 64 experts
-// with 16 waves; wave w sums its contiguous range of partial blocks with 8
-// interleaved accumulators (so 8 loads are in flight), then the 8 and the 16
-// wave sums are added in a fixed order: the result does not depend on timing.
-__global__ __launch_bounds__(1024) void k_reduce_P(const float* __restrict__ P_part, int nblocks, int E, int T,
-                                                   float* __restrict__ P_ws, float* __restrict__ P_out,
-                                                   const int32_t* __restrict__ status_ws,
-                                                   int32_t* __restrict__ status_out) {
-    __shared__ float part[16][64];
+// out[e] = scale * (sum over b of part[b][e]) for the 64 experts of this
+// block, with 16 waves: wave w sums its contiguous range of b with 8
+// interleaved accumulators (8 loads in flight), then the 8 and the 16 wave
+// sums are added in a fixed order, so the result does not depend on timing.
+__device__ __forceinline__ void column_sums(const float* __restrict__ part, int nblocks, int E, float scale,
+                                            float* __restrict__ out_ws, float* __restrict__ out_user) {
+    __shared__ float sums[16][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int e = blockIdx.x * 64 + lane;
-    if (blockIdx.x == 0 && threadIdx.x == 0 && status_out) status_out[0] = status_ws[0];
     const int chunk = (nblocks + 15) / 16;
     const int b0 = min(nblocks, w * chunk), b1 = min(nblocks, b0 + chunk);
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f, a4 = 0.0f, a5 = 0.0f, a6 = 0.0f, a7 = 0.0f, r = 0.0f;
     if (e < E) {
-        const float* src = P_part + e;
+        const float* src = part + e;
         int b = b0;
         for (; b + 8 <= b1; b += 8) {
             a0 = a0 + src[(int64_t)(b + 0) * E];
@@ -356,15 +356,238 @@ __global__ __launch_bounds__(1024) void k_reduce_P(const float* __restrict__ P_p
         }
         for (; b < b1; ++b) r = r + src[(int64_t)b * E];
     }
-    part[w][lane] = (((a0 + a1) + (a2 + a3)) + ((a4 + a5) + (a6 + a7))) + r;
+    sums[w][lane] = (((a0 + a1) + (a2 + a3)) + ((a4 + a5) + (a6 + a7))) + r;
     __syncthreads();
     if (w == 0 && e < E) {
-        float s = 0.0f;
+        float t = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s = s + part[i][lane];
-        const float p = T > 0 ? s / (float)T : 0.0f;
-        P_ws[e] = p;
-        if (P_out) P_out[e] = p;
+        for (int i = 0; i < 16; ++i) t = t + sums[i][lane];
+        t = t * scale;
+        if (out_ws) out_ws[e] = t;
+        if (out_user) out_user[e] = t;
+    }
+}
+
+// P[e] = (sum of the per-block partials) / T, and the device status copy.
+__global__ __launch_bounds__(1024) void k_reduce_P(const float* __restrict__ P_part, int nblocks, int E, int T,
+                                                   float* __restrict__ P_ws, float* __restrict__ P_out,
+                                                   const int32_t* __restrict__ status_ws,
+                                                   int32_t* __restrict__ status_out) {
+    if (blockIdx.x == 0 && threadIdx.x == 0 && status_out) status_out[0] = status_ws[0];
+    column_sums(P_part, nblocks, E, T > 0 ? 1.0f / (float)T : 0.0f, P_ws, P_out);
+}
+
+// Plain column sums (importance, load, z-loss partials).
+__global__ __launch_bounds__(1024) void k_column_sums(const float* __restrict__ part, int nblocks, int E, float scale,
+                                                      float* __restrict__ out_ws, float* __restrict__ out_user) {
+    column_sums(part, nblocks, E, scale, out_ws, out_user);
+}
+
+// ---------------------------------------------------------------------------
+// balance and stability statistics (after k_select, when requested)
+// ---------------------------------------------------------------------------
+
+// Standard normal CDF, Phi(x) = erfc(-x / sqrt 2) / 2.
+__device__ __forceinline__ float phi_f(float x) { return 0.5f * erfcf(-x * 0.70710678118654752f); }
+
+// Same lane mapping as k_select.  Per token: the squared log-sum-exp of the
+// clean logits; every expert's received gate (importance) and, for the noisy
+// gate, Phi((z_e - kth_excluding(H, k, e)) / softplus(zn_e)) (load).  The
+// noisy scores H are recomputed with the same canonical functions and noise
+// as in k_select, so they are bit-identical to the ones the selection used.
+// kth_excluding is the (k+1)-th largest H for a selected expert and the k-th
+// largest (the smallest selected one) otherwise.  Per-block partial sums in a
+// fixed order.
+template <int G, int V>
+__global__ __launch_bounds__(256) void k_balance(const float* __restrict__ dots, int NC,
+                                                 const float* __restrict__ logit_bias, const float* __restrict__ noise,
+                                                 int gate, int T, int E, int k, uint64_t seed, uint64_t noise_offset,
+                                                 const int32_t* __restrict__ topk_idx,
+                                                 const float* __restrict__ topk_gate, float* __restrict__ imp_part,
+                                                 float* __restrict__ load_part, float* __restrict__ z_part) {
+    constexpr int SEGS = 64 / G;
+    __shared__ float red_i[4][V * G];
+    __shared__ float red_l[4][V * G];
+    __shared__ float red_z[4];
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int seg = lane / G, g = lane % G;
+    const int t = blockIdx.x * (4 * SEGS) + wave * SEGS + seg;
+    const bool tok_ok = t < T;
+    const bool noisy = gate == MOE_GATE_NOISY_TOPK;
+
+    float z[V], key[V], sc[V], imp[V];
+    bool valid[V], sel[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int e = g + G * v;
+        valid[v] = tok_ok && e < E;
+        z[v] = 0.0f; key[v] = 0.0f; sc[v] = 1.0f; imp[v] = 0.0f; sel[v] = false;
+        if (!valid[v]) continue;
+        float zz = dots[(int64_t)t * NC + e];
+        if (logit_bias) zz = zz + logit_bias[e];
+        z[v] = zz;
+        key[v] = zz;
+        if (noisy) {
+            const float zn = dots[(int64_t)t * NC + E + e];
+            const uint64_t flat = (uint64_t)t * (uint64_t)E + (uint64_t)e;
+            const float n = noise ? noise[flat] : canon::normalc(seed, noise_offset, flat);
+            sc[v] = canon::softplusc(zn);
+            key[v] = __builtin_fmaf(n, sc[v], zz);
+        }
+    }
+    // selected experts and their gates
+    if (tok_ok) {
+        for (int j = 0; j < k; ++j) {
+            const int ej = topk_idx[(int64_t)t * k + j];
+            const float gj = topk_gate[(int64_t)t * k + j];
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                if (valid[v] && ej == g + G * v) { sel[v] = true; imp[v] = gj; }
+        }
+    }
+    // log-sum-exp of the clean logits
+    float m = -__builtin_inff(), sm = 0.0f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) if (valid[v]) m = fmaxf(m, z[v]);
+    m = seg_max_f<G>(m);
+#pragma unroll
+    for (int v = 0; v < V; ++v) if (valid[v]) sm = sm + canon::expc(z[v] - m);
+    sm = seg_sum_f<G>(sm);
+    const float lse = m + canon::logc(sm);
+    float zterm = (tok_ok && g == 0) ? lse * lse : 0.0f;
+    // smooth load (noisy gate)
+    float ld[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) ld[v] = 0.0f;
+    if (noisy) {
+        float kth = __builtin_inff(), nxt = -__builtin_inff();
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            if (valid[v]) {
+                if (sel[v]) kth = fminf(kth, key[v]);
+                else nxt = fmaxf(nxt, key[v]);
+            }
+        kth = -seg_max_f<G>(-kth);
+        nxt = seg_max_f<G>(nxt);
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            if (valid[v]) ld[v] = k >= E ? 1.0f : phi_f((z[v] - (sel[v] ? nxt : kth)) / sc[v]);
+    }
+    // per-block partials, fixed order: across the segments of a wave, then the 4 waves
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int off = G; off < 64; off <<= 1) {
+            imp[v] = imp[v] + __shfl_xor(imp[v], off, 64);
+            ld[v] = ld[v] + __shfl_xor(ld[v], off, 64);
+        }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) zterm = zterm + __shfl_xor(zterm, off, 64);
+    if (seg == 0) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            red_i[wave][g + G * v] = imp[v];
+            red_l[wave][g + G * v] = ld[v];
+        }
+    }
+    if (lane == 0) red_z[wave] = zterm;
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) {
+        imp_part[(int64_t)blockIdx.x * E + e] = ((red_i[0][e] + red_i[1][e]) + red_i[2][e]) + red_i[3][e];
+        if (noisy) load_part[(int64_t)blockIdx.x * E + e] = ((red_l[0][e] + red_l[1][e]) + red_l[2][e]) + red_l[3][e];
+    }
+    if (threadIdx.x == 0) z_part[blockIdx.x] = ((red_z[0] + red_z[1]) + red_z[2]) + red_z[3];
+}
+
+// Fixed-tree sum of one value per thread over a block of 256 threads.
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+    red[threadIdx.x] = v;
+    __syncthreads();
+    for (int half = 128; half >= 1; half >>= 1) {
+        if ((int)threadIdx.x < half) red[threadIdx.x] = red[threadIdx.x] + red[threadIdx.x + half];
+        __syncthreads();
+    }
+    const float r = red[0];
+    __syncthreads();
+    return r;
+}
+
+// Sequence s (tokens [s L, (s+1) L)): E * sum_e f_e P_e with f_e = n_e / (L k)
+// from the sequence's selections and P_e the mean router probability, summed
+// from k_select's per-block P partials: a sequence covers the blocks
+// [s nb, (s+1) nb) (the last block of a single whole-call sequence may be
+// partly empty; its missing tokens added nothing).
+__global__ __launch_bounds__(256) void k_seq_aux(const int32_t* __restrict__ topk_idx, const float* __restrict__ P_part,
+                                                 int L, int k, int E, int nb, float* __restrict__ seq_part) {
+    __shared__ int32_t hist[1024];
+    __shared__ float red[256];
+    const int s = blockIdx.x;
+    for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+    __syncthreads();
+    const int64_t a0 = (int64_t)s * L * k;
+    for (int a = threadIdx.x; a < L * k; a += 256) {
+        const int e = topk_idx[a0 + a];
+        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);   // integer counts: order-free
+    }
+    __syncthreads();
+    const int b0 = s * nb;
+    float acc = 0.0f;
+    for (int e = threadIdx.x; e < E; e += 256) {
+        float p = 0.0f;
+        for (int b = b0; b < b0 + nb; ++b) p = p + P_part[(int64_t)b * E + e];
+        acc = acc + ((float)hist[e] / (float)(L * k)) * (p / (float)L);
+    }
+    const float tot = block_sum_256(acc, red);
+    if (threadIdx.x == 0) seq_part[s] = (float)E * tot;
+}
+
+// Scalars: CV^2 of importance and load (population variance / mean^2), the
+// z-loss and the mean of the per-sequence balance terms.
+__global__ __launch_bounds__(256) void k_balance_final(const float* __restrict__ imp, const float* __restrict__ load,
+                                                       const float* __restrict__ z_total, const float* __restrict__ seq_part,
+                                                       int nseq, int E, float* __restrict__ imp_cv2,
+                                                       float* __restrict__ load_cv2, float* __restrict__ z_loss,
+                                                       float* __restrict__ seq_aux) {
+    __shared__ float red[256];
+    for (int pass = 0; pass < 2; ++pass) {
+        const float* v = pass == 0 ? imp : load;
+        float* out = pass == 0 ? imp_cv2 : load_cv2;
+        if (!v) continue;
+        float s = 0.0f;
+        for (int e = threadIdx.x; e < E; e += 256) s = s + v[e];
+        const float mean = block_sum_256(s, red) / (float)E;
+        float q = 0.0f;
+        for (int e = threadIdx.x; e < E; e += 256) q = q + (v[e] - mean) * (v[e] - mean);
+        const float var = block_sum_256(q, red) / (float)E;
+        if (threadIdx.x == 0 && out) out[0] = mean != 0.0f ? var / (mean * mean) : 0.0f;
+    }
+    float a = 0.0f;
+    for (int i = threadIdx.x; i < nseq; i += 256) a = a + seq_part[i];
+    const float tot = block_sum_256(a, red);
+    if (threadIdx.x == 0) {
+        if (z_loss) z_loss[0] = z_total[0];
+        if (seq_aux) seq_aux[0] = nseq > 0 ? tot / (float)nseq : 0.0f;
+    }
+}
+
+// b_e += gamma * sign(mean - n_e), the comparison n_e * E <=> sum n exact in
+// integers.
+__global__ __launch_bounds__(1024) void k_update_bias(const int32_t* __restrict__ counts, int E, float gamma,
+                                                      float* __restrict__ bias) {
+    __shared__ int64_t red[1024];
+    int64_t s = 0;
+    for (int e = threadIdx.x; e < E; e += 1024) s += counts[e];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int half = 512; half >= 1; half >>= 1) {
+        if ((int)threadIdx.x < half) red[threadIdx.x] += red[threadIdx.x + half];
+        __syncthreads();
+    }
+    const int64_t total = red[0];
+    for (int e = threadIdx.x; e < E; e += 1024) {
+        const int64_t c = (int64_t)counts[e] * E;
+        if (c < total) bias[e] = bias[e] + gamma;
+        else if (c > total) bias[e] = bias[e] - gamma;
     }
 }
 
@@ -452,6 +675,58 @@ void launch_reduce_P(const float* P_part, int nblocks, int E, int T, float* P_ws
                      const int32_t* status_ws, int32_t* status_out, hipStream_t s) {
     hipLaunchKernelGGL(k_reduce_P, dim3((E + 63) / 64), dim3(1024), 0, s, P_part, nblocks, E, T, P_ws, P_out,
                        status_ws, status_out);
+}
+
+int select_tokens_per_block(int E) {
+    const int G = E >= 64 ? 64 : pow2_at_least(E);
+    return 4 * (64 / G);
+}
+
+void launch_balance(const float* dots, int NC, const float* logit_bias, const float* noise, int gate, int T, int E,
+                    int k, uint64_t seed, uint64_t noise_offset, const int32_t* topk_idx, const float* topk_gate,
+                    const float* P_part, int seq_len, float* imp_part, float* load_part, float* z_part, float* imp_ws,
+                    float* load_ws, float* z_ws, float* seq_part, const moe_stats* st, hipStream_t s) {
+    if (T <= 0) return;
+    const int G = E >= 64 ? 64 : pow2_at_least(E);
+    const int V = (E + G - 1) / G;
+    const int nb = select_blocks(T, E);
+    const bool noisy = gate == MOE_GATE_NOISY_TOPK;
+#define MOE_BAL_ARGS dots, NC, logit_bias, noise, gate, T, E, k, seed, noise_offset, topk_idx, topk_gate, imp_part, load_part, z_part
+#define MOE_BAL(GG, VV) hipLaunchKernelGGL((k_balance<GG, VV>), dim3(nb), dim3(256), 0, s, MOE_BAL_ARGS)
+    if (G < 64) {
+        switch (G) {
+            case 1: MOE_BAL(1, 1); break;
+            case 2: MOE_BAL(2, 1); break;
+            case 4: MOE_BAL(4, 1); break;
+            case 8: MOE_BAL(8, 1); break;
+            case 16: MOE_BAL(16, 1); break;
+            default: MOE_BAL(32, 1); break;
+        }
+    } else if (V <= 1) MOE_BAL(64, 1);
+    else if (V <= 2) MOE_BAL(64, 2);
+    else if (V <= 4) MOE_BAL(64, 4);
+    else if (V <= 8) MOE_BAL(64, 8);
+    else MOE_BAL(64, 16);
+#undef MOE_BAL
+#undef MOE_BAL_ARGS
+    const dim3 cs((E + 63) / 64);
+    hipLaunchKernelGGL(k_column_sums, cs, dim3(1024), 0, s, imp_part, nb, E, 1.0f, imp_ws, st->importance);
+    if (noisy) hipLaunchKernelGGL(k_column_sums, cs, dim3(1024), 0, s, load_part, nb, E, 1.0f, load_ws, st->load);
+    hipLaunchKernelGGL(k_column_sums, dim3(1), dim3(1024), 0, s, z_part, nb, 1, 1.0f / (float)T, z_ws, (float*)nullptr);
+    // sequences of seq_len tokens cover whole select blocks (seq_len is a
+    // multiple of 256, every block size divides 256); seq_len = 0: one
+    // sequence over all blocks
+    const int L = seq_len > 0 ? seq_len : T;
+    const int nseq = T / L;
+    const int bps = seq_len > 0 ? seq_len / select_tokens_per_block(E) : nb;
+    hipLaunchKernelGGL(k_seq_aux, dim3(nseq), dim3(256), 0, s, topk_idx, P_part, L, k, E, bps, seq_part);
+    hipLaunchKernelGGL(k_balance_final, dim3(1), dim3(256), 0, s, imp_ws, noisy ? load_ws : (const float*)nullptr,
+                       z_ws, seq_part, nseq, E, st->importance_cv2, noisy ? st->load_cv2 : (float*)nullptr,
+                       st->z_loss, st->seq_aux);
+}
+
+void launch_update_bias(const int32_t* counts, int E, float gamma, float* bias, hipStream_t s) {
+    hipLaunchKernelGGL(k_update_bias, dim3(1), dim3(1024), 0, s, counts, E, gamma, bias);
 }
 
 void launch_zero_i32(int32_t* p, int n, hipStream_t s) {

@@ -1,0 +1,119 @@
+"""GPU parity of the balance and stability statistics that moe_route writes
+when they are requested (router z-loss, importance and load with their CV^2,
+the sequence-wise balance term) and of moe_update_bias, against the oracle
+(fp64) on the oracle's own routing of the same inputs.  Tolerances: these
+are fp32 sums of fp32 values whose inputs match the oracle bit for bit
+(logits, noisy scores, selections) or within 2e-6 (gates), so 1e-5 relative
+on every vector and scalar (CV^2 also within 1e-7 absolute)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import Config
+import tests.gpu_helpers as H
+import sparse_mixture_experts_39_amd as moe
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "noisy": (Config("bal_noisy", T=512, d=64, F=64, E=40, k=4, act_dtype="bf16", act="relu", gate="noisy_topk",
+                     seed=41), 0),
+    "noisy_seq": (Config("bal_noisy_seq", T=1024, d=128, F=64, E=64, k=2, act_dtype="bf16", act="relu",
+                         gate="noisy_topk", seed=42), 256),
+    "sigmoid": (Config("bal_sigmoid", T=512, d=128, F=64, E=64, k=8, act_dtype="bf16", act="swiglu",
+                       gate="sigmoid_bias", sel_bias=True, seed=43), 256),
+    "softmax_topk": (Config("bal_topk", T=768, d=256, F=64, E=16, k=3, act_dtype="bf16", act="swiglu",
+                            gate="softmax_topk", seed=44), 256),
+    "softmax_full_f32": (Config("bal_full", T=512, d=64, F=64, E=8, k=1, act_dtype="f32", act="relu",
+                                gate="softmax_full", logit_bias="zipf", seed=45), 512),
+    "noisy_k_equals_E": (Config("bal_kE", T=256, d=64, F=64, E=4, k=4, act_dtype="bf16", act="relu",
+                                gate="noisy_topk", seed=46), 0),
+}
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.abs(b).max()
+    return float(np.abs(a - b).max() / (den if den > 0 else 1.0))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_balance_statistics_match_oracle(name):
+    cfg, seq_len = CASES[name]
+    H.log(f"[balance] {name}")
+    inp = workloads.make_inputs(cfg)
+    d = H.to_device(inp)
+    c = H.bind_config(cfg, T=cfg.T)
+    c.seq_len = seq_len
+    w = moe.weights_from(c, d)
+    ws = moe.workspace(c)
+    st = moe.alloc_stats(c, balance=True)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    moe.moe_route(c, d["x"], w, idx, gates, None, st, ws)
+    torch.cuda.synchronize()
+    nz = inp.get("noise") if cfg.gate == "noisy_topk" else None
+    r = oracle.route(cfg, inp["x"], inp["w_router"], logit_bias=inp.get("logit_bias"), sel_bias=inp.get("sel_bias"),
+                     w_noise=inp.get("w_noise"), noise=nz, want_probs=True)
+    np.testing.assert_array_equal(idx.cpu().numpy(), r["idx"], err_msg="selection")
+    o = oracle.balance(cfg, r, seq_len=seq_len)
+    g = {k2: v.cpu().numpy().astype(np.float64) for k2, v in st.items()}
+    assert rel(g["z_loss"], o["z_loss"]) <= 1e-5, (g["z_loss"], o["z_loss"])
+    assert rel(g["importance"], o["importance"]) <= 1e-5
+    assert abs(g["importance_cv2"][0] - o["importance_cv2"]) <= 1e-5 * abs(o["importance_cv2"]) + 1e-7
+    assert rel(g["seq_aux"], o["seq_aux"]) <= 1e-5, (g["seq_aux"], o["seq_aux"])
+    if cfg.gate == "noisy_topk":
+        assert rel(g["load"], o["load"]) <= 1e-5
+        assert abs(g["load_cv2"][0] - o["load_cv2"]) <= 1e-5 * abs(o["load_cv2"]) + 1e-7
+    else:
+        assert np.isnan(g["load"]).all() and np.isnan(g["load_cv2"]).all(), "load written for a non-noisy gate"
+    H.log(f"[balance] {name} z_loss {g['z_loss'][0]:.6g} imp_cv2 {g['importance_cv2'][0]:.4g} "
+          f"seq_aux {g['seq_aux'][0]:.4g}")
+
+
+def test_balance_statistics_leave_layer_outputs_unchanged():
+    cfg, seq_len = CASES["sigmoid"]
+    inp = workloads.make_inputs(cfg)
+    d = H.to_device(inp)
+    c = H.bind_config(cfg, T=cfg.T)
+    w = moe.weights_from(c, d)
+    outs = []
+    for balance in (False, True):
+        ws = moe.workspace(c)
+        st = moe.alloc_stats(c, balance=balance)
+        out = torch.empty_like(d["x"])
+        moe.moe_layer_forward(c, w, d["x"], out, st, ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu())
+    np.testing.assert_array_equal(H.bytes_of(outs[0]), H.bytes_of(outs[1]))
+
+
+def test_update_bias_matches_oracle_over_steps():
+    """Three auxiliary-loss-free steps on the device, each fed the counts of a
+    routing with the current bias, against the oracle's steps on the same
+    counts (bit for bit: one fp32 add per step)."""
+    cfg = Config("bias_steps", T=512, d=128, F=64, E=32, k=4, act_dtype="bf16", act="swiglu", gate="sigmoid_bias",
+                 sel_bias=True, seed=47)
+    inp = workloads.make_inputs(cfg)
+    d = H.to_device(inp)
+    c = H.bind_config(cfg, T=cfg.T)
+    bias_dev = d["sel_bias"].clone()
+    bias_ref = inp["sel_bias"].numpy().astype(np.float32).copy()
+    for step in range(3):
+        d2 = dict(d)
+        d2["sel_bias"] = bias_dev
+        w = moe.weights_from(c, d2)
+        ws = moe.workspace(c)
+        st = moe.alloc_stats(c)
+        out = torch.empty_like(d["x"])
+        moe.moe_layer_forward(c, w, d["x"], out, st, ws)
+        counts = st["counts"].clone()
+        moe.moe_update_bias(c, counts, 0.01, bias_dev)
+        torch.cuda.synchronize()
+        bias_ref = oracle.update_bias(counts.cpu().numpy(), bias_ref, 0.01)
+        np.testing.assert_array_equal(bias_dev.cpu().numpy(), bias_ref, err_msg=f"step {step}")
