@@ -24,8 +24,9 @@ void launch_zero_i32(int32_t* p, int n, hipStream_t s);
 int select_tokens_per_block(int E);
 void launch_balance(const float* dots, int NC, const float* logit_bias, const float* noise, int gate, int T, int E,
                     int k, uint64_t seed, uint64_t noise_offset, const int32_t* topk_idx, const float* topk_gate,
-                    const float* P_part, int seq_len, float* imp_part, float* load_part, float* z_part, float* imp_ws,
-                    float* load_ws, float* z_ws, float* seq_part, const moe_stats* st, hipStream_t s);
+                    const float* P_part, const float* P_mean, int seq_len, float* imp_part, float* load_part,
+                    float* cnt_part, float* z_part, float* imp_ws, float* load_ws, float* cnt_ws, float* z_ws,
+                    float* seq_part, const moe_stats* st, hipStream_t s);
 void launch_update_bias(const int32_t* counts, int E, float gamma, float* bias, hipStream_t s);
 
 // dispatch.hip

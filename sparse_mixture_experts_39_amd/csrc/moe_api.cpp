@@ -43,7 +43,7 @@ struct Layout {
     size_t idx, gates, slot_pos, perm_src, offsets;       // whole-layer intermediates
     size_t x_perm, y_perm, shared_out;
     size_t partial;                                       // split-K accumulators
-    size_t imp_part, load_part, z_part, imp_ws, load_ws, z_ws, seq_part;   // balance statistics
+    size_t imp_part, load_part, cnt_part, z_part, imp_ws, load_ws, cnt_ws, z_ws, seq_part;   // balance statistics
     size_t total;
 };
 
@@ -106,9 +106,11 @@ Layout compute_layout(const moe_config* c) {
     const size_t sb = T > 0 ? (size_t)moe::select_blocks(T, E) : 0;
     L.imp_part = take(sb * E * sizeof(float));
     L.load_part = take(sb * E * sizeof(float));
+    L.cnt_part = take(sb * E * sizeof(float));
     L.z_part = take(sb * sizeof(float));
     L.imp_ws = take((size_t)E * sizeof(float));
     L.load_ws = take((size_t)E * sizeof(float));
+    L.cnt_ws = take((size_t)E * sizeof(float));
     L.z_ws = take(sizeof(float));
     L.seq_part = take((size_t)(T / 256 + 1) * sizeof(float));
     L.total = o;
@@ -217,9 +219,10 @@ moe_status moe_route(const moe_config* c, const void* x, const moe_weights* w, i
                                 st->seq_aux);
     if (balance)
         moe::launch_balance(dots, NC, w->logit_bias, noise, c->gate, T, E, c->top_k, c->seed, c->noise_offset,
-                            topk_idx, topk_gate, at<float>(ws, L.P_part), c->seq_len, at<float>(ws, L.imp_part),
-                            at<float>(ws, L.load_part), at<float>(ws, L.z_part), at<float>(ws, L.imp_ws),
-                            at<float>(ws, L.load_ws), at<float>(ws, L.z_ws), at<float>(ws, L.seq_part), st, h);
+                            topk_idx, topk_gate, at<float>(ws, L.P_part), at<float>(ws, L.P_ws), c->seq_len,
+                            at<float>(ws, L.imp_part), at<float>(ws, L.load_part), at<float>(ws, L.cnt_part),
+                            at<float>(ws, L.z_part), at<float>(ws, L.imp_ws), at<float>(ws, L.load_ws),
+                            at<float>(ws, L.cnt_ws), at<float>(ws, L.z_ws), at<float>(ws, L.seq_part), st, h);
     return after_launch();
 }
 

@@ -404,10 +404,12 @@ __global__ __launch_bounds__(256) void k_balance(const float* __restrict__ dots,
                                                  int gate, int T, int E, int k, uint64_t seed, uint64_t noise_offset,
                                                  const int32_t* __restrict__ topk_idx,
                                                  const float* __restrict__ topk_gate, float* __restrict__ imp_part,
-                                                 float* __restrict__ load_part, float* __restrict__ z_part) {
+                                                 float* __restrict__ load_part, float* __restrict__ cnt_part,
+                                                 float* __restrict__ z_part) {
     constexpr int SEGS = 64 / G;
     __shared__ float red_i[4][V * G];
     __shared__ float red_l[4][V * G];
+    __shared__ float red_c[4][V * G];
     __shared__ float red_z[4];
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int seg = lane / G, g = lane % G;
@@ -473,13 +475,18 @@ __global__ __launch_bounds__(256) void k_balance(const float* __restrict__ dots,
         for (int v = 0; v < V; ++v)
             if (valid[v]) ld[v] = k >= E ? 1.0f : phi_f((z[v] - (sel[v] ? nxt : kth)) / sc[v]);
     }
-    // per-block partials, fixed order: across the segments of a wave, then the 4 waves
+    // per-block partials, fixed order: across the segments of a wave, then the
+    // 4 waves (selection counts are small integers, exact in fp32)
+    float cn[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) cn[v] = sel[v] ? 1.0f : 0.0f;
 #pragma unroll
     for (int v = 0; v < V; ++v)
 #pragma unroll
         for (int off = G; off < 64; off <<= 1) {
             imp[v] = imp[v] + __shfl_xor(imp[v], off, 64);
             ld[v] = ld[v] + __shfl_xor(ld[v], off, 64);
+            cn[v] = cn[v] + __shfl_xor(cn[v], off, 64);
         }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) zterm = zterm + __shfl_xor(zterm, off, 64);
@@ -488,6 +495,7 @@ __global__ __launch_bounds__(256) void k_balance(const float* __restrict__ dots,
         for (int v = 0; v < V; ++v) {
             red_i[wave][g + G * v] = imp[v];
             red_l[wave][g + G * v] = ld[v];
+            red_c[wave][g + G * v] = cn[v];
         }
     }
     if (lane == 0) red_z[wave] = zterm;
@@ -495,6 +503,7 @@ __global__ __launch_bounds__(256) void k_balance(const float* __restrict__ dots,
     for (int e = threadIdx.x; e < E; e += 256) {
         imp_part[(int64_t)blockIdx.x * E + e] = ((red_i[0][e] + red_i[1][e]) + red_i[2][e]) + red_i[3][e];
         if (noisy) load_part[(int64_t)blockIdx.x * E + e] = ((red_l[0][e] + red_l[1][e]) + red_l[2][e]) + red_l[3][e];
+        cnt_part[(int64_t)blockIdx.x * E + e] = ((red_c[0][e] + red_c[1][e]) + red_c[2][e]) + red_c[3][e];
     }
     if (threadIdx.x == 0) z_part[blockIdx.x] = ((red_z[0] + red_z[1]) + red_z[2]) + red_z[3];
 }
@@ -512,30 +521,40 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
     return r;
 }
 
-// Sequence s (tokens [s L, (s+1) L)): E * sum_e f_e P_e with f_e = n_e / (L k)
-// from the sequence's selections and P_e the mean router probability, summed
-// from k_select's per-block P partials: a sequence covers the blocks
-// [s nb, (s+1) nb) (the last block of a single whole-call sequence may be
-// partly empty; its missing tokens added nothing).
-__global__ __launch_bounds__(256) void k_seq_aux(const int32_t* __restrict__ topk_idx, const float* __restrict__ P_part,
+// Sequence s (tokens [s L, (s+1) L), blocks [s nb, (s+1) nb) of k_select /
+// k_balance): E * sum_e f_e P_e with f_e = n_e / (L k) and P_e the mean
+// router probability, both summed from the per-block partials with 8
+// interleaved accumulators in a fixed order.  With whole_call the sequence
+// is the whole call and the already reduced counts and mean P are used.
+__device__ __forceinline__ float sum_blocks(const float* __restrict__ part, int b0, int b1, int E, int e) {
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f, a4 = 0.0f, a5 = 0.0f, a6 = 0.0f, a7 = 0.0f, r = 0.0f;
+    const float* src = part + e;
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+        a0 = a0 + src[(int64_t)(b + 0) * E];
+        a1 = a1 + src[(int64_t)(b + 1) * E];
+        a2 = a2 + src[(int64_t)(b + 2) * E];
+        a3 = a3 + src[(int64_t)(b + 3) * E];
+        a4 = a4 + src[(int64_t)(b + 4) * E];
+        a5 = a5 + src[(int64_t)(b + 5) * E];
+        a6 = a6 + src[(int64_t)(b + 6) * E];
+        a7 = a7 + src[(int64_t)(b + 7) * E];
+    }
+    for (; b < b1; ++b) r = r + src[(int64_t)b * E];
+    return (((a0 + a1) + (a2 + a3)) + ((a4 + a5) + (a6 + a7))) + r;
+}
+
+__global__ __launch_bounds__(256) void k_seq_aux(const float* __restrict__ cnt_part, const float* __restrict__ P_part,
+                                                 const float* __restrict__ cnt_all, const float* __restrict__ P_mean,
                                                  int L, int k, int E, int nb, float* __restrict__ seq_part) {
-    __shared__ int32_t hist[1024];
     __shared__ float red[256];
     const int s = blockIdx.x;
-    for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
-    __syncthreads();
-    const int64_t a0 = (int64_t)s * L * k;
-    for (int a = threadIdx.x; a < L * k; a += 256) {
-        const int e = topk_idx[a0 + a];
-        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);   // integer counts: order-free
-    }
-    __syncthreads();
-    const int b0 = s * nb;
+    const int b0 = s * nb, b1 = b0 + nb;
     float acc = 0.0f;
     for (int e = threadIdx.x; e < E; e += 256) {
-        float p = 0.0f;
-        for (int b = b0; b < b0 + nb; ++b) p = p + P_part[(int64_t)b * E + e];
-        acc = acc + ((float)hist[e] / (float)(L * k)) * (p / (float)L);
+        const float n = cnt_all ? cnt_all[e] : sum_blocks(cnt_part, b0, b1, E, e);
+        const float pm = P_mean ? P_mean[e] : sum_blocks(P_part, b0, b1, E, e) / (float)L;
+        acc = acc + (n / (float)(L * k)) * pm;
     }
     const float tot = block_sum_256(acc, red);
     if (threadIdx.x == 0) seq_part[s] = (float)E * tot;
@@ -684,14 +703,15 @@ int select_tokens_per_block(int E) {
 
 void launch_balance(const float* dots, int NC, const float* logit_bias, const float* noise, int gate, int T, int E,
                     int k, uint64_t seed, uint64_t noise_offset, const int32_t* topk_idx, const float* topk_gate,
-                    const float* P_part, int seq_len, float* imp_part, float* load_part, float* z_part, float* imp_ws,
-                    float* load_ws, float* z_ws, float* seq_part, const moe_stats* st, hipStream_t s) {
+                    const float* P_part, const float* P_mean, int seq_len, float* imp_part, float* load_part,
+                    float* cnt_part, float* z_part, float* imp_ws, float* load_ws, float* cnt_ws, float* z_ws,
+                    float* seq_part, const moe_stats* st, hipStream_t s) {
     if (T <= 0) return;
     const int G = E >= 64 ? 64 : pow2_at_least(E);
     const int V = (E + G - 1) / G;
     const int nb = select_blocks(T, E);
     const bool noisy = gate == MOE_GATE_NOISY_TOPK;
-#define MOE_BAL_ARGS dots, NC, logit_bias, noise, gate, T, E, k, seed, noise_offset, topk_idx, topk_gate, imp_part, load_part, z_part
+#define MOE_BAL_ARGS dots, NC, logit_bias, noise, gate, T, E, k, seed, noise_offset, topk_idx, topk_gate, imp_part, load_part, cnt_part, z_part
 #define MOE_BAL(GG, VV) hipLaunchKernelGGL((k_balance<GG, VV>), dim3(nb), dim3(256), 0, s, MOE_BAL_ARGS)
     if (G < 64) {
         switch (G) {
@@ -719,7 +739,11 @@ void launch_balance(const float* dots, int NC, const float* logit_bias, const fl
     const int L = seq_len > 0 ? seq_len : T;
     const int nseq = T / L;
     const int bps = seq_len > 0 ? seq_len / select_tokens_per_block(E) : nb;
-    hipLaunchKernelGGL(k_seq_aux, dim3(nseq), dim3(256), 0, s, topk_idx, P_part, L, k, E, bps, seq_part);
+    if (seq_len == 0)
+        hipLaunchKernelGGL(k_column_sums, cs, dim3(1024), 0, s, cnt_part, nb, E, 1.0f, cnt_ws, (float*)nullptr);
+    hipLaunchKernelGGL(k_seq_aux, dim3(nseq), dim3(256), 0, s, cnt_part, P_part,
+                       seq_len > 0 ? (const float*)nullptr : (const float*)cnt_ws,
+                       seq_len > 0 ? (const float*)nullptr : P_mean, L, k, E, bps, seq_part);
     hipLaunchKernelGGL(k_balance_final, dim3(1), dim3(256), 0, s, imp_ws, noisy ? load_ws : (const float*)nullptr,
                        z_ws, seq_part, nseq, E, st->importance_cv2, noisy ? st->load_cv2 : (float*)nullptr,
                        st->z_loss, st->seq_aux);
