@@ -25,7 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-GATES = {"softmax_topk": 0, "softmax_full": 1, "noisy_topk": 2, "sigmoid_bias": 3}
+GATES = {"softmax_topk": 0, "softmax_full": 1, "noisy_topk": 2, "sigmoid_bias": 3, "expert_choice": 4}
 ACTS = {"relu": 0, "swiglu": 1}
 MAP_FN = {"exp": 0, "log": 1, "log1p": 2, "softplus": 3, "sigmoid": 4, "sin": 5, "cos": 6}
 
@@ -83,6 +83,10 @@ def lib():
         L.oc_balance.restype = ctypes.c_int
         L.oc_balance.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int32] + [P] * 12
         L.oc_update_bias.argtypes = [ctypes.c_int32, P, ctypes.c_float, P]
+        L.oc_ec_capacity.restype = ctypes.c_int64
+        L.oc_ec_capacity.argtypes = [ctypes.POINTER(_Cfg)]
+        L.oc_route_ec.restype = ctypes.c_int
+        L.oc_route_ec.argtypes = [ctypes.POINTER(_Cfg), P, P, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -179,9 +183,26 @@ def philox4x32_10(ctr: Sequence[int], key: Sequence[int]) -> np.ndarray:
 def route(cfg, x, w_router, *, logit_bias=None, sel_bias=None, w_noise=None, noise=None,
           seed: Optional[int] = None, noise_offset: int = 0, want_probs: bool = False) -> Dict[str, np.ndarray]:
     """Router logits, scores, top-k indices, gates and P for all tokens.
-    ``noise`` [T][E] fp32, or None to draw it from the Philox stream."""
+    ``noise`` [T][E] fp32, or None to draw it from the Philox stream.
+    Expert choice returns E slots per token (idx -1 where the expert did not
+    take the token) and its scores S as ``keys``."""
     xa = _np(x)
     T = xa.shape[0]
+    if cfg.gate == "expert_choice":
+        c = make_cfg(cfg, T=T)
+        E = cfg.E
+        idx = np.empty((T, E), dtype=np.int32)
+        gates = np.empty((T, E), dtype=np.float64)
+        S = np.empty((T, E), dtype=np.float32)
+        P = np.empty(E, dtype=np.float64)
+        rc = lib().oc_route_ec(ctypes.byref(c), _ptr(xa), _ptr(_np(w_router, np.float32)),
+                               _ptr(_np(logit_bias, np.float32)), _ptr(idx), _ptr(gates), _ptr(S), _ptr(P))
+        if rc != 0:
+            raise ValueError("oracle route rejected the configuration")
+        out = dict(idx=idx, gates=gates, keys=S, P=P, status=0)
+        if want_probs:
+            out["probs"] = S.astype(np.float64)
+        return out
     c = make_cfg(cfg, seed=seed, noise_offset=noise_offset, T=T)
     wr = _np(w_router, np.float32)
     lb = _np(logit_bias, np.float32)
@@ -212,12 +233,29 @@ def route(cfg, x, w_router, *, logit_bias=None, sel_bias=None, w_noise=None, noi
 
 def capacity(cfg, T: Optional[int] = None) -> int:
     c = make_cfg(cfg, T=T)
+    if cfg.gate == "expert_choice":
+        return int(lib().oc_ec_capacity(ctypes.byref(c)))
     return int(lib().oc_capacity(ctypes.byref(c)))
+
+
+def slots(cfg) -> int:
+    """Selection slots per token: k for token choice, E for expert choice."""
+    return cfg.E if cfg.gate == "expert_choice" else cfg.k
+
+
+def _slot_cfg(cfg):
+    # dispatch / combine see one slot per (token, expert) under expert
+    # choice, and no capacity cut (the selection already took C per expert)
+    if cfg.gate == "expert_choice":
+        return cfg.replace(k=cfg.E, capacity_factor=0.0)
+    return cfg
 
 
 def dispatch(cfg, idx, T: Optional[int] = None) -> Dict[str, np.ndarray]:
     idx = _np(idx, np.int32)
     T = idx.shape[0] if T is None else T
+    C = capacity(cfg, T)
+    cfg = _slot_cfg(cfg)
     c = make_cfg(cfg, T=T)
     E, k = cfg.E, cfg.k
     counts = np.empty(E, np.int32)
@@ -228,7 +266,7 @@ def dispatch(cfg, idx, T: Optional[int] = None) -> Dict[str, np.ndarray]:
     R = lib().oc_dispatch(ctypes.byref(c), _ptr(idx), _ptr(counts), _ptr(kept), _ptr(offsets),
                           _ptr(perm_src), _ptr(slot_pos))
     return dict(counts=counts, kept=kept, offsets=offsets, perm_src=perm_src[:R].copy(),
-                slot_pos=slot_pos.reshape(T, k), R=int(R), C=capacity(cfg, T))
+                slot_pos=slot_pos.reshape(T, k), R=int(R), C=C)
 
 
 def gather_rows(cfg, x, perm_src) -> np.ndarray:
@@ -236,7 +274,7 @@ def gather_rows(cfg, x, perm_src) -> np.ndarray:
     ps = _np(perm_src, np.int32)
     R = ps.shape[0]
     out = np.empty((R, cfg.d), dtype=xa.dtype)
-    c = make_cfg(cfg, T=xa.shape[0])
+    c = make_cfg(_slot_cfg(cfg), T=xa.shape[0])
     lib().oc_gather_rows(ctypes.byref(c), _ptr(xa), _ptr(ps), R, _ptr(out))
     return out
 
@@ -265,7 +303,7 @@ def combine(cfg, slot_pos, gates, y, x, shared=None, tokens=None,
     sh = _np(shared, np.float64)
     tok = _np(tokens, np.int32)
     ntok = T if tok is None else tok.shape[0]
-    c = make_cfg(cfg, round_intermediates=round_intermediates, T=T)
+    c = make_cfg(_slot_cfg(cfg), round_intermediates=round_intermediates, T=T)
     out = np.empty((ntok, cfg.d), dtype=np.float64)
     lib().oc_combine(ctypes.byref(c), _ptr(tok), ntok, _ptr(sp), _ptr(g), _ptr(ya), _ptr(xa), _ptr(sh), _ptr(out))
     return out

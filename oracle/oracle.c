@@ -45,7 +45,7 @@
 /* ------------------------------------------------------------------------ */
 
 enum { OC_RELU = 0, OC_SWIGLU = 1 };
-enum { OC_SOFTMAX_TOPK = 0, OC_SOFTMAX_FULL = 1, OC_NOISY_TOPK = 2, OC_SIGMOID_BIAS = 3 };
+enum { OC_SOFTMAX_TOPK = 0, OC_SOFTMAX_FULL = 1, OC_NOISY_TOPK = 2, OC_SIGMOID_BIAS = 3, OC_EXPERT_CHOICE = 4 };
 
 typedef struct {
     int32_t T, d, F, E, k;
@@ -465,7 +465,8 @@ OC_EXPORT int64_t oc_dispatch(const oc_config* cfg, const int32_t* idx, int32_t*
     if (E <= 0 || k <= 0 || T < 0) return -1;
     int64_t C = oc_capacity(cfg);
     for (int e = 0; e < E; ++e) counts[e] = 0;
-    for (int64_t a = 0; a < (int64_t)T * k; ++a) counts[idx[a]] += 1;
+    for (int64_t a = 0; a < (int64_t)T * k; ++a)
+        if (idx[a] >= 0 && idx[a] < E) counts[idx[a]] += 1;   /* other ids: no assignment */
     offsets[0] = 0;
     for (int e = 0; e < E; ++e) {
         kept[e] = (C >= 0 && counts[e] > C) ? (int32_t)C : counts[e];
@@ -474,6 +475,7 @@ OC_EXPORT int64_t oc_dispatch(const oc_config* cfg, const int32_t* idx, int32_t*
     int32_t* rank = (int32_t*)calloc((size_t)E, sizeof(int32_t));
     for (int64_t a = 0; a < (int64_t)T * k; ++a) {
         int e = idx[a];
+        if (e < 0 || e >= E) { slot_pos[a] = -1; continue; }
         int32_t r = rank[e]++;
         if (C >= 0 && r >= C) { slot_pos[a] = -1; continue; }
         int32_t row = offsets[e] + r;
@@ -579,15 +581,18 @@ OC_EXPORT void oc_combine(const oc_config* cfg, const int32_t* tokens, int64_t n
 }
 
 /*
- * Load statistics.  f_i = fraction of the T*k assignments routed to expert i
- * before capacity drops, so sum f = 1 (awesome-ai-roadmap 19.3.3; CS336 notes
- * section 9); aux = E * sum_i f_i P_i, the Switch balance term without its
- * coefficient; imbalance I = max_i n_i / (T k / E) (Lecture29, "Myth 3").
+ * Load statistics.  f_i = fraction of the assignments (T*k for token choice)
+ * routed to expert i before capacity drops, so sum f = 1 (awesome-ai-roadmap
+ * 19.3.3; CS336 notes section 9); aux = E * sum_i f_i P_i, the Switch balance
+ * term without its coefficient; imbalance I = max_i n_i / (mean n)
+ * (Lecture29, "Myth 3").
  */
 OC_EXPORT void oc_stats(const oc_config* cfg, const int32_t* counts, const int32_t* kept, const double* P,
                         double* f, int64_t* n_dropped, double* imbalance, double* aux) {
     const int E = cfg->E;
-    const double tk = (double)cfg->T * (double)cfg->k;
+    /* the assignments that exist: T k for token choice, E C for expert choice */
+    double tk = 0.0;
+    for (int e = 0; e < E; ++e) tk += (double)counts[e];
     int64_t kept_sum = 0;
     int32_t nmax = 0;
     double a = 0.0;
@@ -730,4 +735,98 @@ OC_EXPORT void oc_update_bias(int32_t E, const int32_t* counts, float gamma, flo
         if (c < total) bias[e] = bias[e] + gamma;
         else if (c > total) bias[e] = bias[e] - gamma;
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* expert choice                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Tokens per expert under expert choice: C = ceil(cf * T * k / E) with the
+ * capacity factor cf (1 when not set) and k the mean number of experts per
+ * token, at most T. */
+OC_EXPORT int64_t oc_ec_capacity(const oc_config* cfg) {
+    const double cf = cfg->capacity_factor > 0.0 ? cfg->capacity_factor : 1.0;
+    int64_t C = (int64_t)ceil(cf * (double)cfg->T * (double)cfg->k / (double)cfg->E);
+    return C < cfg->T ? C : cfg->T;
+}
+
+/*
+ * Expert-choice routing (CS336 notes section 4: every expert scores all
+ * tokens and takes its top K, "top-K along the rows", so every expert gets
+ * exactly the same number of tokens; awesome-ai-roadmap 19.6.1: experts each
+ * take a fixed number of tokens and a token may be processed by a varying
+ * number of experts).  Reading: the score of token t for expert e is its
+ * router probability S = softmax over the experts of the logits z (fp32:
+ * m = max_e z, s = sum over e = 0..E-1 in order of exp(z_e - m) with the
+ * canonical exp, S_e = exp(z_e - m) / s correctly rounded); expert e takes the
+ * C tokens with the largest S[., e], ties to the lower token index; the gate
+ * of a chosen (t, e) is S[t, e].
+ * Outputs, with E slots per token: idx[t][e] = e if e took t, else -1;
+ * gates[t][e] = S[t][e] or 0; scores [T][E] = S (fp32, optional); P_e =
+ * mean_t S[t][e].
+ */
+OC_EXPORT int oc_route_ec(const oc_config* cfg, const void* x, const float* w_router, const float* logit_bias,
+                          int32_t* idx, double* gates, float* scores_out, double* P) {
+    const int T = cfg->T, d = cfg->d, E = cfg->E;
+    if (E < 1 || cfg->k < 1 || cfg->k > E) return -1;
+    const int64_t C = oc_ec_capacity(cfg);
+    float* S = (float*)malloc(sizeof(float) * (size_t)T * (size_t)E + 1);
+    #pragma omp parallel
+    {
+        float* z = (float*)malloc(sizeof(float) * (size_t)E);
+        #pragma omp for schedule(static)
+        for (int t = 0; t < T; ++t) {
+            const void* xr = cfg->act_bf16 ? (const void*)((const uint16_t*)x + (size_t)t * d)
+                                           : (const void*)((const float*)x + (size_t)t * d);
+            float m = -INFINITY;
+            for (int e = 0; e < E; ++e) {
+                float ze = dot_c(xr, cfg->act_bf16, w_router + (size_t)e * d, d);
+                if (logit_bias) ze = ze + logit_bias[e];
+                z[e] = ze;
+                if (ze > m) m = ze;
+            }
+            float s = 0.0f;
+            for (int e = 0; e < E; ++e) s = s + oc_exp(z[e] - m);
+            for (int e = 0; e < E; ++e) S[(size_t)t * E + e] = oc_exp(z[e] - m) / s;
+        }
+        free(z);
+    }
+    for (size_t i = 0; i < (size_t)T * E; ++i) { idx[i] = -1; gates[i] = 0.0; }
+    int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+    for (int e = 0; e < E; ++e) {
+        /* the C first tokens in the order (S descending, index ascending) */
+        double psum = 0.0;
+        for (int t = 0; t < T; ++t) psum += (double)S[(size_t)t * E + e];
+        P[e] = T > 0 ? psum / (double)T : 0.0;
+        for (int t = 0; t < T; ++t) order[t] = t;
+        /* plain bottom-up merge sort of the token indices */
+        for (int width = 1; width < T; width *= 2) {
+            for (int lo = 0; lo < T; lo += 2 * width) {
+                int mid = lo + width < T ? lo + width : T, hi = lo + 2 * width < T ? lo + 2 * width : T;
+                int i = lo, j = mid, n = 0;
+                int32_t* tmp = (int32_t*)malloc(sizeof(int32_t) * (size_t)(hi - lo + 1));
+                while (i < mid || j < hi) {
+                    int take_left;
+                    if (i >= mid) take_left = 0;
+                    else if (j >= hi) take_left = 1;
+                    else {
+                        const float a = S[(size_t)order[i] * E + e], b = S[(size_t)order[j] * E + e];
+                        take_left = order_key(a) > order_key(b) || (order_key(a) == order_key(b) && order[i] < order[j]);
+                    }
+                    tmp[n++] = take_left ? order[i++] : order[j++];
+                }
+                memcpy(order + lo, tmp, sizeof(int32_t) * (size_t)(hi - lo));
+                free(tmp);
+            }
+        }
+        for (int64_t r = 0; r < C; ++r) {
+            const int t = order[r];
+            idx[(size_t)t * E + e] = e;
+            gates[(size_t)t * E + e] = (double)S[(size_t)t * E + e];
+        }
+    }
+    if (scores_out) memcpy(scores_out, S, sizeof(float) * (size_t)T * E);
+    free(order);
+    free(S);
+    return 0;
 }

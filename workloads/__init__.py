@@ -55,7 +55,7 @@ class Config:
     k: int                      # top-k
     act_dtype: str              # "f32" | "bf16": activations and expert weights
     act: str                    # "relu" | "swiglu"
-    gate: str                   # "softmax_topk" | "softmax_full" | "noisy_topk" | "sigmoid_bias"
+    gate: str                   # "softmax_topk" | "softmax_full" | "noisy_topk" | "sigmoid_bias" | "expert_choice"
     capacity_factor: float = 0.0  # <= 0: dropless
     residual: bool = False
     n_shared: int = 0
