@@ -158,7 +158,7 @@ def main():
     w = moe.weights_from(c, dinp)
     ws = moe.workspace(c)
     st = moe.alloc_stats(c, balance=args.balance_stats)
-    T, E, k, d, F = c.T, c.n_experts, c.top_k, c.d_model, c.d_ff
+    T, E, k, d, F = c.T, c.n_experts, moe.route_slots(c), c.d_model, c.d_ff
     R = moe.max_rows(c)
     dt = dinp["x"].dtype
     i32 = dict(dtype=torch.int32, device=dev)
@@ -265,7 +265,7 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.act_dtype,
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
-        "config": {"workload": workload_desc(cfg), "T": T, "d_model": d, "d_ff": F, "n_experts": E, "top_k": k,
+        "config": {"workload": workload_desc(cfg), "T": T, "d_model": d, "d_ff": F, "n_experts": E, "top_k": c.top_k,
                    "parallelism": "single GPU, all experts resident"},
         "grouped_gemm_pct_mfma_peak": 100.0 * (flops_up + flops_down) / (gemm_ms * 1e-3) / (peak_f * 1e12),
         "dispatch_pct_hbm_peak": 100.0 * disp_bytes / (stage_ms["dispatch"] * 1e-3) / (PEAK_HBM_GBS * 1e9),

@@ -73,7 +73,16 @@ typedef enum {
     /* DeepSeek-V3: s = sigmoid(z); select the top-k of s + b; g = s of the
      * selected experts renormalised to sum to 1; the bias never enters g
      * (awesome-ai-roadmap 19.3.4; CS336 notes, section 12). */
-    MOE_GATE_SIGMOID_BIAS = 3
+    MOE_GATE_SIGMOID_BIAS = 3,
+    /* Expert choice: every expert takes the C tokens with the largest router
+     * probability S = softmax over the experts of z (ties to the lower token
+     * index), C = ceil(cf * T * k / E) (cf <= 0 means 1; at most T), so all
+     * experts get exactly C tokens and a token is taken by 0..E experts; the
+     * gate of a taken (t, e) is S[t, e] (CS336 notes, section 4: top-K along
+     * the rows; awesome-ai-roadmap 19.6.1).  top_k is the mean number of
+     * experts per token.  The routing outputs then have E slots per token
+     * (moe_route_slots): topk_idx[t][e] = e or -1, topk_gate[t][e] = S or 0. */
+    MOE_GATE_EXPERT_CHOICE = 4
 } moe_gate;
 
 /* Expert MLP: y = W2 relu(W1 a) (Shazeer notes 2.2), or
@@ -173,12 +182,17 @@ moe_status moe_validate_config(const moe_config* cfg);
 moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
 
 /* Rows of x_perm / y_perm the caller must allocate: T*k when dropless, else
- * min(T*k, E*C).  -1 for an invalid configuration. */
+ * min(T*k, E*C); E*C under expert choice.  -1 for an invalid configuration. */
 int64_t moe_max_rows(const moe_config* cfg);
 
 /* Expert capacity C = ceil(capacity_factor * T * k / E) computed in fp64
- * (Lecture29, "Inference load balance"), or -1 when dropless or invalid. */
+ * (Lecture29, "Inference load balance"), or -1 when dropless or invalid;
+ * under expert choice the tokens each expert takes. */
 int64_t moe_capacity(const moe_config* cfg);
+
+/* Selection slots per token in topk_idx / topk_gate / slot_pos: top_k, or
+ * n_experts under expert choice.  -1 for an invalid configuration. */
+int32_t moe_route_slots(const moe_config* cfg);
 
 /* HIP error code of the last MOE_ERR_HIP on this thread (0 if none). */
 int32_t moe_last_hip_error(void);

@@ -86,7 +86,7 @@ def lib():
         L.oc_ec_capacity.restype = ctypes.c_int64
         L.oc_ec_capacity.argtypes = [ctypes.POINTER(_Cfg)]
         L.oc_route_ec.restype = ctypes.c_int
-        L.oc_route_ec.argtypes = [ctypes.POINTER(_Cfg), P, P, P, P, P, P, P]
+        L.oc_route_ec.argtypes = [ctypes.POINTER(_Cfg), P, P, P, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -194,12 +194,14 @@ def route(cfg, x, w_router, *, logit_bias=None, sel_bias=None, w_noise=None, noi
         idx = np.empty((T, E), dtype=np.int32)
         gates = np.empty((T, E), dtype=np.float64)
         S = np.empty((T, E), dtype=np.float32)
+        z = np.empty((T, E), dtype=np.float32)
         P = np.empty(E, dtype=np.float64)
         rc = lib().oc_route_ec(ctypes.byref(c), _ptr(xa), _ptr(_np(w_router, np.float32)),
-                               _ptr(_np(logit_bias, np.float32)), _ptr(idx), _ptr(gates), _ptr(S), _ptr(P))
+                               _ptr(_np(logit_bias, np.float32)), _ptr(idx), _ptr(gates), _ptr(S), _ptr(z),
+                               _ptr(P))
         if rc != 0:
             raise ValueError("oracle route rejected the configuration")
-        out = dict(idx=idx, gates=gates, keys=S, P=P, status=0)
+        out = dict(idx=idx, gates=gates, keys=S, logits=z, P=P, status=0)
         if want_probs:
             out["probs"] = S.astype(np.float64)
         return out

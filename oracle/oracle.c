@@ -618,7 +618,8 @@ static double oc_phi(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
  * Statistics the pages attach to the router, computed from the route's
  * per-token outputs (logits z [T][E], selection keys [T][E], the noisy
  * gate's noise scale softplus(x W_noise) [T][E] or NULL, probabilities
- * p [T][E], idx and gates [T][k]).  All fp64.
+ * p [T][E], idx and gates [T][slots]: slots = k for token choice, E for
+ * expert choice, whose untaken slots hold id -1 and are skipped).  All fp64.
  *
  *   z_loss = mean_t (log sum_e exp z_t,e)^2: the router z-loss, the squared
  *     log of the softmax normaliser (CS336 notes section 11; awesome-ai-
@@ -638,6 +639,7 @@ static double oc_phi(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
  *     counted per sequence (CS336 notes section 9: V3 keeps a complementary
  *     sequence-level auxiliary loss; awesome-ai-roadmap 19.3.4), with
  *     f_e^s = n_e^s / (L k) from the selections of the sequence's L tokens
+ *     (k = top_k, the mean experts per token, also under expert choice)
  *     and P_e^s their mean probability; seq_len <= 0 means one sequence of
  *     all T tokens (then seq_aux equals the batch aux).
  * Returns -1 when seq_len does not divide T.
@@ -647,6 +649,7 @@ OC_EXPORT int oc_balance(const oc_config* cfg, int32_t seq_len, const float* log
                          double* z_loss, double* importance, double* importance_cv2, double* load, double* load_cv2,
                          double* seq_aux) {
     const int T = cfg->T, E = cfg->E, k = cfg->k;
+    const int slots = cfg->gate == OC_EXPERT_CHOICE ? E : k;
     const int L = seq_len > 0 ? seq_len : T;
     if (T > 0 && (L <= 0 || T % L != 0)) return -1;
     double zsum = 0.0;
@@ -660,7 +663,10 @@ OC_EXPORT int oc_balance(const oc_config* cfg, int32_t seq_len, const float* log
         for (int e = 0; e < E; ++e) s += exp((double)z[e] - m);
         const double lse = m + log(s);
         zsum += lse * lse;
-        for (int j = 0; j < k; ++j) importance[idx[(size_t)t * k + j]] += gates[(size_t)t * k + j];
+        for (int j = 0; j < slots; ++j) {
+            const int32_t e = idx[(size_t)t * slots + j];
+            if (e >= 0 && e < E) importance[e] += gates[(size_t)t * slots + j];
+        }
         if (noise_scale) {
             const float* h = keys + (size_t)t * E;
             memset(sel, 0, (size_t)E);
@@ -707,7 +713,10 @@ OC_EXPORT int oc_balance(const oc_config* cfg, int32_t seq_len, const float* log
         for (int e = 0; e < E; ++e) { Ps[e] = 0.0; ns[e] = 0; }
         for (int t = sq * L; t < (sq + 1) * L; ++t) {
             for (int e = 0; e < E; ++e) Ps[e] += probs[(size_t)t * E + e];
-            for (int j = 0; j < k; ++j) ns[idx[(size_t)t * k + j]] += 1;
+            for (int j = 0; j < slots; ++j) {
+                const int32_t e = idx[(size_t)t * slots + j];
+                if (e >= 0 && e < E) ns[e] += 1;
+            }
         }
         double a = 0.0;
         for (int e = 0; e < E; ++e) a += ((double)ns[e] / ((double)L * k)) * (Ps[e] / (double)L);
@@ -762,11 +771,11 @@ OC_EXPORT int64_t oc_ec_capacity(const oc_config* cfg) {
  * C tokens with the largest S[., e], ties to the lower token index; the gate
  * of a chosen (t, e) is S[t, e].
  * Outputs, with E slots per token: idx[t][e] = e if e took t, else -1;
- * gates[t][e] = S[t][e] or 0; scores [T][E] = S (fp32, optional); P_e =
- * mean_t S[t][e].
+ * gates[t][e] = S[t][e] or 0; scores [T][E] = S (fp32, optional); logits
+ * [T][E] = z (fp32, optional); P_e = mean_t S[t][e].
  */
 OC_EXPORT int oc_route_ec(const oc_config* cfg, const void* x, const float* w_router, const float* logit_bias,
-                          int32_t* idx, double* gates, float* scores_out, double* P) {
+                          int32_t* idx, double* gates, float* scores_out, float* logits_out, double* P) {
     const int T = cfg->T, d = cfg->d, E = cfg->E;
     if (E < 1 || cfg->k < 1 || cfg->k > E) return -1;
     const int64_t C = oc_ec_capacity(cfg);
@@ -783,6 +792,7 @@ OC_EXPORT int oc_route_ec(const oc_config* cfg, const void* x, const float* w_ro
                 float ze = dot_c(xr, cfg->act_bf16, w_router + (size_t)e * d, d);
                 if (logit_bias) ze = ze + logit_bias[e];
                 z[e] = ze;
+                if (logits_out) logits_out[(size_t)t * E + e] = ze;
                 if (ze > m) m = ze;
             }
             float s = 0.0f;

@@ -26,13 +26,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 ACTS = {"relu": 0, "swiglu": 1}
-GATES = {"softmax_topk": 0, "softmax_full": 1, "noisy_topk": 2, "sigmoid_bias": 3}
+GATES = {"softmax_topk": 0, "softmax_full": 1, "noisy_topk": 2, "sigmoid_bias": 3, "expert_choice": 4}
 MOE_F_ADD_RESIDUAL, MOE_F_NOISE_INPUT = 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace missing or too small",
           4: "HIP launch failed"}
 
 EXPORTED_SYMBOLS = (
-    "moe_validate_config", "moe_workspace_size", "moe_max_rows", "moe_capacity", "moe_last_hip_error",
+    "moe_validate_config", "moe_workspace_size", "moe_max_rows", "moe_capacity", "moe_route_slots",
+    "moe_last_hip_error",
     "moe_status_string", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
     "moe_shared_expert", "moe_combine", "moe_layer_forward", "moe_update_bias",
 )
@@ -89,6 +90,8 @@ def lib():
         L.moe_max_rows.argtypes = [C]
         L.moe_capacity.restype = ctypes.c_int64
         L.moe_capacity.argtypes = [C]
+        L.moe_route_slots.restype = ctypes.c_int32
+        L.moe_route_slots.argtypes = [C]
         L.moe_last_hip_error.restype = ctypes.c_int32
         L.moe_last_hip_error.argtypes = []
         L.moe_status_string.restype = ctypes.c_char_p
@@ -235,6 +238,11 @@ def capacity(c: MoeConfig) -> int:
     return int(lib().moe_capacity(ctypes.byref(c)))
 
 
+def route_slots(c: MoeConfig) -> int:
+    """Selection slots per token: top_k, or n_experts under expert choice."""
+    return int(lib().moe_route_slots(ctypes.byref(c)))
+
+
 def workspace(c: MoeConfig, device="cuda") -> torch.Tensor:
     return torch.empty(max(workspace_size(c), 1), dtype=torch.uint8, device=device)
 
@@ -242,7 +250,7 @@ def workspace(c: MoeConfig, device="cuda") -> torch.Tensor:
 # ---------------------------------------------------------------- stages
 
 def moe_route(c: MoeConfig, x, w: MoeWeights, topk_idx, topk_gate, scores=None, stats=None, ws=None, stream=None):
-    T, E, k, d = c.T, c.n_experts, c.top_k, c.d_model
+    T, E, k, d = c.T, c.n_experts, route_slots(c), c.d_model
     st = _stats_struct(stats)
     rc = lib().moe_route(ctypes.byref(c), _ptr(x, _dt(c), (T, d), "x"), ctypes.byref(w),
                          _ptr(topk_idx, torch.int32, (T, k), "topk_idx"),
@@ -254,7 +262,7 @@ def moe_route(c: MoeConfig, x, w: MoeWeights, topk_idx, topk_gate, scores=None, 
 
 def moe_dispatch(c: MoeConfig, x, topk_idx, x_perm, expert_offsets, perm_src, slot_pos, stats=None, ws=None,
                  stream=None):
-    T, E, k, d = c.T, c.n_experts, c.top_k, c.d_model
+    T, E, k, d = c.T, c.n_experts, route_slots(c), c.d_model
     R = max_rows(c)
     st = _stats_struct(stats)
     rc = lib().moe_dispatch(ctypes.byref(c), _ptr(x, _dt(c), (T, d), "x"),
@@ -305,7 +313,7 @@ def moe_shared_expert(c: MoeConfig, x, w: MoeWeights, shared_out, ws=None, strea
 
 
 def moe_combine(c: MoeConfig, y_perm, slot_pos, topk_gate, residual, shared_out, out, stream=None):
-    T, d, k = c.T, c.d_model, c.top_k
+    T, d, k = c.T, c.d_model, route_slots(c)
     R = max_rows(c)
     rc = lib().moe_combine(ctypes.byref(c), _ptr(y_perm, _dt(c), (R, d), "y_perm"),
                            _ptr(slot_pos, torch.int32, (T, k), "slot_pos"),

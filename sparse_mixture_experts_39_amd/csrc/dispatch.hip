@@ -57,18 +57,18 @@ __global__ __launch_bounds__(256) void k_histogram(const int32_t* __restrict__ t
         hist[(int64_t)blockIdx.x * E + i] = ((cnt[i] + cnt[E + i]) + cnt[2 * E + i]) + cnt[3 * E + i];
 }
 
-__global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ hist, int nblocks, int E, int64_t n_assign,
+__global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ hist, int nblocks, int E,
                                                int64_t capacity, int32_t* __restrict__ blockbase,
                                                int32_t* __restrict__ offsets, const float* __restrict__ P,
                                                int32_t* counts_out, int32_t* kept_out, float* f_out,
                                                int32_t* dropped_out, float* imbalance_out, float* aux_out) {
     __shared__ int32_t scan[1024];
     __shared__ int64_t kept_red[1024];
+    __shared__ int64_t cnt_red[1024];
     __shared__ int32_t max_red[1024];
     __shared__ double aux_red[1024];
     const int e = threadIdx.x;
     int32_t c = 0, kp = 0;
-    double fe = 0.0;
     if (e < E) {
         // column scan over the blocks, 16 loads in flight at a time
         int32_t run = 0;
@@ -89,7 +89,6 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ hist,
         }
         c = run;
         kp = (capacity >= 0 && (int64_t)c > capacity) ? (int32_t)capacity : c;
-        fe = n_assign > 0 ? (double)c / (double)n_assign : 0.0;
     }
     // inclusive scan of kept over experts (Hillis-Steele, integers)
     scan[e] = kp;
@@ -105,24 +104,34 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ hist,
         if (e == E - 1) offsets[E] = scan[e];
         if (counts_out) counts_out[e] = c;
         if (kept_out) kept_out[e] = kp;
-        if (f_out) f_out[e] = (float)fe;
     }
-    // fixed-tree reductions for the scalar statistics
+    // integer totals: the assignments made (T k for token choice, E C for
+    // expert choice), the kept ones, and the largest expert count
     kept_red[e] = kp;
+    cnt_red[e] = c;
     max_red[e] = c;
-    aux_red[e] = (e < E && P) ? fe * (double)P[e] : 0.0;
     __syncthreads();
     for (int half = 512; half >= 1; half >>= 1) {
         if (e < half) {
             kept_red[e] += kept_red[e + half];
+            cnt_red[e] += cnt_red[e + half];
             max_red[e] = max(max_red[e], max_red[e + half]);
-            aux_red[e] += aux_red[e + half];
         }
         __syncthreads();
     }
+    const int64_t total = cnt_red[0];
+    const double fe = (e < E && total > 0) ? (double)c / (double)total : 0.0;
+    if (e < E && f_out) f_out[e] = (float)fe;
+    // aux = E sum_e f_e P_e, fixed tree
+    aux_red[e] = (e < E && P) ? fe * (double)P[e] : 0.0;
+    __syncthreads();
+    for (int half = 512; half >= 1; half >>= 1) {
+        if (e < half) aux_red[e] += aux_red[e + half];
+        __syncthreads();
+    }
     if (e == 0) {
-        if (dropped_out) dropped_out[0] = (int32_t)(n_assign - kept_red[0]);
-        if (imbalance_out) imbalance_out[0] = n_assign > 0 ? (float)((double)max_red[0] * (double)E / (double)n_assign) : 0.0f;
+        if (dropped_out) dropped_out[0] = (int32_t)(total - kept_red[0]);
+        if (imbalance_out) imbalance_out[0] = total > 0 ? (float)((double)max_red[0] * (double)E / (double)total) : 0.0f;
         if (aux_out && P) aux_out[0] = (float)((double)E * aux_red[0]);
     }
 }
@@ -194,9 +203,9 @@ void launch_histogram(const int32_t* topk_idx, int64_t n_assign, int E, int32_t*
                        id_bits(E), hist);
 }
 
-void launch_scan(const int32_t* hist, int nblocks, int E, int64_t n_assign, int64_t capacity, int32_t* blockbase,
+void launch_scan(const int32_t* hist, int nblocks, int E, int64_t capacity, int32_t* blockbase,
                  int32_t* offsets, const float* P, const moe_stats* st, hipStream_t s) {
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, nblocks, E, n_assign, capacity, blockbase, offsets, P,
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, nblocks, E, capacity, blockbase, offsets, P,
                        st ? st->counts : nullptr, st ? st->kept : nullptr, st ? st->f : nullptr,
                        st ? st->n_dropped : nullptr, st ? st->imbalance : nullptr, st ? st->aux : nullptr);
 }

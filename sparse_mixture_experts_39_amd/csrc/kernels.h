@@ -26,13 +26,16 @@ void launch_balance(const float* dots, int NC, const float* logit_bias, const fl
                     int k, uint64_t seed, uint64_t noise_offset, const int32_t* topk_idx, const float* topk_gate,
                     const float* P_part, const float* P_mean, int seq_len, float* imp_part, float* load_part,
                     float* cnt_part, float* z_part, float* imp_ws, float* load_ws, float* cnt_ws, float* z_ws,
-                    float* seq_part, const moe_stats* st, hipStream_t s);
+                    float* seq_part, const moe_stats* st, int k_mean, int p_row_tokens, hipStream_t s);
 void launch_update_bias(const int32_t* counts, int E, float gamma, float* bias, hipStream_t s);
+void launch_ec_route(const float* dots, const float* logit_bias, int T, int E, int C, float* S, float* P_ws,
+                     float* P_out, int32_t* status, int32_t* status_out, int32_t* topk_idx, float* topk_gate,
+                     hipStream_t s);
 
 // dispatch.hip
 constexpr int kAssignBlock = 256;  // assignments per histogram / scatter block
 void launch_histogram(const int32_t* topk_idx, int64_t n_assign, int E, int32_t* hist, hipStream_t s);
-void launch_scan(const int32_t* hist, int nblocks, int E, int64_t n_assign, int64_t capacity,
+void launch_scan(const int32_t* hist, int nblocks, int E, int64_t capacity,
                  int32_t* blockbase, int32_t* offsets, const float* P, const moe_stats* st, hipStream_t s);
 void launch_scatter(const int32_t* topk_idx, int64_t n_assign, int E, const int32_t* blockbase,
                     const int32_t* offsets, int64_t capacity, int32_t* perm_src, int32_t* slot_pos, hipStream_t s);

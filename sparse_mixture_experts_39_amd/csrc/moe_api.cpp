@@ -18,15 +18,28 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int elem_bytes(const moe_config* c) { return c->act_dtype == MOE_BF16 ? 2 : 4; }
 bool is_bf16(const moe_config* c) { return c->act_dtype == MOE_BF16; }
-int64_t n_assign(const moe_config* c) { return (int64_t)c->T * c->top_k; }
+bool expert_choice(const moe_config* c) { return c->gate == MOE_GATE_EXPERT_CHOICE; }
+// selection slots per token: k, or E under expert choice
+int slots_of(const moe_config* c) { return expert_choice(c) ? c->n_experts : c->top_k; }
+int64_t n_assign(const moe_config* c) { return (int64_t)c->T * slots_of(c); }
 
+// tokens each expert takes under expert choice
+int64_t ec_capacity_of(const moe_config* c) {
+    const double cf = c->capacity_factor > 0.0f ? (double)c->capacity_factor : 1.0;
+    const int64_t v = (int64_t)ceil(cf * (double)c->T * (double)c->top_k / (double)c->n_experts);
+    return v < c->T ? v : c->T;
+}
+
+// capacity cut applied by the dispatch stage (-1: none)
 int64_t capacity_of(const moe_config* c) {
+    if (expert_choice(c)) return -1;
     if (!(c->capacity_factor > 0.0f)) return -1;
     const double v = ceil((double)c->capacity_factor * (double)c->T * (double)c->top_k / (double)c->n_experts);
     return (int64_t)v;
 }
 
 int64_t max_rows_of(const moe_config* c) {
+    if (expert_choice(c)) return ec_capacity_of(c) * (int64_t)c->n_experts;
     const int64_t tk = n_assign(c);
     const int64_t cap = capacity_of(c);
     if (cap < 0) return tk;
@@ -44,6 +57,7 @@ struct Layout {
     size_t x_perm, y_perm, shared_out;
     size_t partial;                                       // split-K accumulators
     size_t imp_part, load_part, cnt_part, z_part, imp_ws, load_ws, cnt_ws, z_ws, seq_part;   // balance statistics
+    size_t ec_scores;                                     // expert choice: S [T][E]
     size_t total;
 };
 
@@ -113,6 +127,7 @@ Layout compute_layout(const moe_config* c) {
     L.cnt_ws = take((size_t)E * sizeof(float));
     L.z_ws = take(sizeof(float));
     L.seq_part = take((size_t)(T / 256 + 1) * sizeof(float));
+    L.ec_scores = take(expert_choice(c) ? (size_t)T * E * sizeof(float) : 0);
     L.total = o;
     return L;
 }
@@ -143,7 +158,7 @@ moe_status moe_validate_config(const moe_config* c) {
     if (c->T < 0 || c->d_model <= 0 || c->d_ff <= 0 || c->n_experts <= 0 || c->top_k <= 0) return MOE_ERR_INVALID_ARG;
     if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
     if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
-    if (c->gate < MOE_GATE_SOFTMAX_TOPK || c->gate > MOE_GATE_SIGMOID_BIAS) return MOE_ERR_INVALID_ARG;
+    if (c->gate < MOE_GATE_SOFTMAX_TOPK || c->gate > MOE_GATE_EXPERT_CHOICE) return MOE_ERR_INVALID_ARG;
     if (c->top_k > c->n_experts) return MOE_ERR_INVALID_ARG;
     if (c->n_shared < 0 || c->n_shared > 1) return MOE_ERR_INVALID_ARG;
     if (c->n_shared == 1 && c->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
@@ -153,6 +168,7 @@ moe_status moe_validate_config(const moe_config* c) {
     if (c->d_model % 64 || c->d_ff % 64) return MOE_ERR_UNSUPPORTED;
     if (c->n_shared == 1 && (c->d_ff_shared % 64 || c->act != MOE_ACT_SWIGLU)) return MOE_ERR_UNSUPPORTED;
     if ((int64_t)c->T * c->top_k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)c->T * slots_of(c) >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     if (c->reserved != 0 || c->seq_len < 0) return MOE_ERR_INVALID_ARG;
     if (c->seq_len > 0 && (c->seq_len % 256 != 0 || c->T % c->seq_len != 0)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
@@ -165,7 +181,12 @@ int64_t moe_max_rows(const moe_config* c) {
 
 int64_t moe_capacity(const moe_config* c) {
     if (moe_validate_config(c) != MOE_OK) return -1;
-    return capacity_of(c);
+    return expert_choice(c) ? ec_capacity_of(c) : capacity_of(c);
+}
+
+int32_t moe_route_slots(const moe_config* c) {
+    if (moe_validate_config(c) != MOE_OK) return -1;
+    return slots_of(c);
 }
 
 moe_status moe_workspace_size(const moe_config* c, size_t* bytes) {
@@ -209,20 +230,33 @@ moe_status moe_route(const moe_config* c, const void* x, const moe_weights* w, i
     int32_t* status = at<int32_t>(ws, L.status);
     moe::launch_zero_i32(status, 1, h);
     moe::launch_router_dots(is_bf16(c), x, w->w_router, noisy ? w->w_noise : nullptr, T, c->d_model, E, NC, dots, h);
+    const bool balance = st && (st->z_loss || st->importance || st->importance_cv2 || st->load || st->load_cv2 ||
+                                st->seq_aux);
+    if (expert_choice(c)) {
+        float* S = scores ? scores : at<float>(ws, L.ec_scores);
+        moe::launch_ec_route(dots, w->logit_bias, T, E, (int)ec_capacity_of(c), S, at<float>(ws, L.P_ws),
+                             st ? st->P : nullptr, status, st ? st->device_status : nullptr, topk_idx, topk_gate, h);
+        if (balance)
+            moe::launch_balance(dots, NC, w->logit_bias, nullptr, c->gate, T, E, slots_of(c), c->seed, c->noise_offset,
+                                topk_idx, topk_gate, S, at<float>(ws, L.P_ws), c->seq_len, at<float>(ws, L.imp_part),
+                                at<float>(ws, L.load_part), at<float>(ws, L.cnt_part), at<float>(ws, L.z_part),
+                                at<float>(ws, L.imp_ws), at<float>(ws, L.load_ws), at<float>(ws, L.cnt_ws),
+                                at<float>(ws, L.z_ws), at<float>(ws, L.seq_part), st, c->top_k, 1, h);
+        return after_launch();
+    }
     const float* noise = (noisy && (c->flags & MOE_F_NOISE_INPUT)) ? w->noise : nullptr;
     moe::launch_select(dots, NC, w->logit_bias, c->gate == MOE_GATE_SIGMOID_BIAS ? w->sel_bias : nullptr, noise,
                        c->gate, T, E, c->top_k, c->seed, c->noise_offset, topk_idx, topk_gate, scores,
                        at<float>(ws, L.P_part), status, h);
     moe::launch_reduce_P(at<float>(ws, L.P_part), T > 0 ? moe::select_blocks(T, E) : 0, E, T, at<float>(ws, L.P_ws),
                          st ? st->P : nullptr, status, st ? st->device_status : nullptr, h);
-    const bool balance = st && (st->z_loss || st->importance || st->importance_cv2 || st->load || st->load_cv2 ||
-                                st->seq_aux);
     if (balance)
         moe::launch_balance(dots, NC, w->logit_bias, noise, c->gate, T, E, c->top_k, c->seed, c->noise_offset,
                             topk_idx, topk_gate, at<float>(ws, L.P_part), at<float>(ws, L.P_ws), c->seq_len,
                             at<float>(ws, L.imp_part), at<float>(ws, L.load_part), at<float>(ws, L.cnt_part),
                             at<float>(ws, L.z_part), at<float>(ws, L.imp_ws), at<float>(ws, L.load_ws),
-                            at<float>(ws, L.cnt_ws), at<float>(ws, L.z_ws), at<float>(ws, L.seq_part), st, h);
+                            at<float>(ws, L.cnt_ws), at<float>(ws, L.z_ws), at<float>(ws, L.seq_part), st,
+                            c->top_k, moe::select_tokens_per_block(E), h);
     return after_launch();
 }
 
@@ -252,9 +286,9 @@ moe_status moe_dispatch(const moe_config* c, const void* x, const int32_t* topk_
     int32_t* bbase = at<int32_t>(ws, L.blockbase);
     const float* P = (st && st->P) ? st->P : at<float>(ws, L.P_ws);
     moe::launch_histogram(topk_idx, na, E, hist, h);
-    moe::launch_scan(hist, nb, E, na, cap, bbase, expert_offsets, P, st, h);
+    moe::launch_scan(hist, nb, E, cap, bbase, expert_offsets, P, st, h);
     moe::launch_scatter(topk_idx, na, E, bbase, expert_offsets, cap, perm_src, slot_pos, h);
-    moe::launch_permute_rows(x, c->top_k, c->d_model, elem_bytes(c), perm_src, expert_offsets, E, max_rows_of(c),
+    moe::launch_permute_rows(x, slots_of(c), c->d_model, elem_bytes(c), perm_src, expert_offsets, E, max_rows_of(c),
                              x_perm, h);
     return after_launch();
 }
@@ -356,7 +390,7 @@ moe_status moe_combine(const moe_config* c, const void* y_perm, const int32_t* s
     if (s != MOE_OK) return s;
     if (c->T > 0 && (!slot_pos || !topk_gate || !out)) return MOE_ERR_INVALID_ARG;
     if (c->T > 0 && max_rows_of(c) > 0 && !y_perm) return MOE_ERR_INVALID_ARG;
-    moe::launch_combine(y_perm, slot_pos, topk_gate, residual, shared_out, out, c->T, c->d_model, c->top_k,
+    moe::launch_combine(y_perm, slot_pos, topk_gate, residual, shared_out, out, c->T, c->d_model, slots_of(c),
                         is_bf16(c), (hipStream_t)stream);
     return after_launch();
 }

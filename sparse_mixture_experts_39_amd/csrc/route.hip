@@ -19,6 +19,8 @@
 //   k_balance       (when requested) z-loss, importance and load partials;
 //                   k_column_sums, k_seq_aux, k_balance_final reduce them
 //   k_update_bias   the auxiliary-loss-free bias step
+//   k_ec_scores, k_ec_select   expert choice: router probabilities, and each
+//                   expert's top-C tokens by radix select
 #include "device_common.h"
 #include "canon_math.h"
 #include "kernels.h"
@@ -546,14 +548,14 @@ __device__ __forceinline__ float sum_blocks(const float* __restrict__ part, int 
 
 __global__ __launch_bounds__(256) void k_seq_aux(const float* __restrict__ cnt_part, const float* __restrict__ P_part,
                                                  const float* __restrict__ cnt_all, const float* __restrict__ P_mean,
-                                                 int L, int k, int E, int nb, float* __restrict__ seq_part) {
+                                                 int L, int k, int E, int nb_cnt, int nb_p,
+                                                 float* __restrict__ seq_part) {
     __shared__ float red[256];
     const int s = blockIdx.x;
-    const int b0 = s * nb, b1 = b0 + nb;
     float acc = 0.0f;
     for (int e = threadIdx.x; e < E; e += 256) {
-        const float n = cnt_all ? cnt_all[e] : sum_blocks(cnt_part, b0, b1, E, e);
-        const float pm = P_mean ? P_mean[e] : sum_blocks(P_part, b0, b1, E, e) / (float)L;
+        const float n = cnt_all ? cnt_all[e] : sum_blocks(cnt_part, s * nb_cnt, (s + 1) * nb_cnt, E, e);
+        const float pm = P_mean ? P_mean[e] : sum_blocks(P_part, s * nb_p, (s + 1) * nb_p, E, e) / (float)L;
         acc = acc + (n / (float)(L * k)) * pm;
     }
     const float tot = block_sum_256(acc, red);
@@ -610,9 +612,107 @@ __global__ __launch_bounds__(1024) void k_update_bias(const int32_t* __restrict_
     }
 }
 
+__global__ void k_copy_status(const int32_t* __restrict__ status_ws, int32_t* __restrict__ status_out) {
+    if (threadIdx.x == 0 && status_out) status_out[0] = status_ws[0];
+}
+
 __global__ void k_zero_i32(int32_t* p, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// expert choice
+// ---------------------------------------------------------------------------
+
+// S[t][e] = softmax over the experts of z[t] (+ logit bias): one thread per
+// token, m = max, s = sum over e = 0..E-1 in order of exp(z_e - m) with the
+// canonical exp, S_e = exp(z_e - m) / s (correctly rounded fp32 division), so
+// the scores, and hence the selection, are reproducible bit for bit.
+__global__ __launch_bounds__(256) void k_ec_scores(const float* __restrict__ dots, const float* __restrict__ logit_bias,
+                                                   int T, int E, float* __restrict__ S,
+                                                   int32_t* __restrict__ status) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= T) return;
+    const float* z = dots + (int64_t)t * E;
+    float m = -__builtin_inff();
+    for (int e = 0; e < E; ++e) m = fmaxf(m, logit_bias ? z[e] + logit_bias[e] : z[e]);
+    float s = 0.0f;
+    for (int e = 0; e < E; ++e) s = s + canon::expc((logit_bias ? z[e] + logit_bias[e] : z[e]) - m);
+    int bad = 0;
+    for (int e = 0; e < E; ++e) {
+        const float v = canon::expc((logit_bias ? z[e] + logit_bias[e] : z[e]) - m) / s;
+        if (!__builtin_isfinite(v)) bad = 1;
+        S[(int64_t)t * E + e] = v;
+    }
+    if (bad) status[0] = MOE_DEV_NONFINITE;   // benign race: every writer stores the same value
+}
+
+// Expert e (one block of 1024 threads) takes the C tokens with the largest
+// S[., e], ties to the lower token index.  S >= 0, so its bit pattern orders
+// like the value: a 4-pass radix select (8 bits per pass, most significant
+// first) finds the C-th largest key K; every token above K is taken, and the
+// first `need` tokens equal to K in index order (an exclusive scan over the
+// tokens in chunks of 1024).  Integer histograms: the result does not depend
+// on timing.
+__global__ __launch_bounds__(1024) void k_ec_select(const float* __restrict__ S, int T, int E, int C,
+                                                    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
+    __shared__ int32_t hist[256];
+    __shared__ int32_t sel_digit, sel_above;
+    __shared__ int32_t scan[1024];
+    const int e = blockIdx.x, tid = threadIdx.x;
+    uint32_t prefix = 0, mask = 0;
+    int need = C;                                  // tokens still to take at or below the prefix
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += 1024) hist[i] = 0;
+        __syncthreads();
+        for (int t = tid; t < T; t += 1024) {
+            const uint32_t u = __float_as_uint(S[(int64_t)t * E + e]);
+            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int above = 0, d = 255;
+            for (; d > 0; --d) {
+                if (above + hist[d] >= need) break;
+                above += hist[d];
+            }
+            sel_digit = d;
+            sel_above = above;
+        }
+        __syncthreads();
+        prefix |= (uint32_t)sel_digit << shift;
+        mask |= 255u << shift;
+        need -= sel_above;
+        __syncthreads();
+    }
+    // prefix is now the C-th largest key; take everything above it and the
+    // first `need` tokens equal to it
+    int carry = 0;
+    for (int t0 = 0; t0 < T; t0 += 1024) {
+        const int t = t0 + tid;
+        uint32_t u = 0;
+        float v = 0.0f;
+        if (t < T) { v = S[(int64_t)t * E + e]; u = __float_as_uint(v); }
+        const int eq = (t < T && u == prefix) ? 1 : 0;
+        scan[tid] = eq;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int add = tid >= off ? scan[tid - off] : 0;
+            __syncthreads();
+            scan[tid] += add;
+            __syncthreads();
+        }
+        const int rank_eq = carry + scan[tid] - eq;   // equal tokens before t
+        const int total_eq = scan[1023];
+        if (t < T) {
+            const bool take = u > prefix || (eq && rank_eq < need);
+            topk_idx[(int64_t)t * E + e] = take ? e : -1;
+            topk_gate[(int64_t)t * E + e] = take ? v : 0.0f;
+        }
+        carry += total_eq;
+        __syncthreads();
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -705,7 +805,7 @@ void launch_balance(const float* dots, int NC, const float* logit_bias, const fl
                     int k, uint64_t seed, uint64_t noise_offset, const int32_t* topk_idx, const float* topk_gate,
                     const float* P_part, const float* P_mean, int seq_len, float* imp_part, float* load_part,
                     float* cnt_part, float* z_part, float* imp_ws, float* load_ws, float* cnt_ws, float* z_ws,
-                    float* seq_part, const moe_stats* st, hipStream_t s) {
+                    float* seq_part, const moe_stats* st, int k_mean, int p_row_tokens, hipStream_t s) {
     if (T <= 0) return;
     const int G = E >= 64 ? 64 : pow2_at_least(E);
     const int V = (E + G - 1) / G;
@@ -739,14 +839,27 @@ void launch_balance(const float* dots, int NC, const float* logit_bias, const fl
     const int L = seq_len > 0 ? seq_len : T;
     const int nseq = T / L;
     const int bps = seq_len > 0 ? seq_len / select_tokens_per_block(E) : nb;
+    const int pps = seq_len > 0 ? seq_len / p_row_tokens : 0;    // rows of P_part per sequence
     if (seq_len == 0)
         hipLaunchKernelGGL(k_column_sums, cs, dim3(1024), 0, s, cnt_part, nb, E, 1.0f, cnt_ws, (float*)nullptr);
     hipLaunchKernelGGL(k_seq_aux, dim3(nseq), dim3(256), 0, s, cnt_part, P_part,
                        seq_len > 0 ? (const float*)nullptr : (const float*)cnt_ws,
-                       seq_len > 0 ? (const float*)nullptr : P_mean, L, k, E, bps, seq_part);
+                       seq_len > 0 ? (const float*)nullptr : P_mean, L, k_mean, E, bps, pps, seq_part);
     hipLaunchKernelGGL(k_balance_final, dim3(1), dim3(256), 0, s, imp_ws, noisy ? load_ws : (const float*)nullptr,
                        z_ws, seq_part, nseq, E, st->importance_cv2, noisy ? st->load_cv2 : (float*)nullptr,
                        st->z_loss, st->seq_aux);
+}
+
+void launch_ec_route(const float* dots, const float* logit_bias, int T, int E, int C, float* S, float* P_ws,
+                     float* P_out, int32_t* status, int32_t* status_out, int32_t* topk_idx, float* topk_gate,
+                     hipStream_t s) {
+    if (T > 0) {
+        hipLaunchKernelGGL(k_ec_scores, dim3((T + 255) / 256), dim3(256), 0, s, dots, logit_bias, T, E, S, status);
+        hipLaunchKernelGGL(k_column_sums, dim3((E + 63) / 64), dim3(1024), 0, s, S, T, E, 1.0f / (float)T, P_ws,
+                           P_out);
+        hipLaunchKernelGGL(k_ec_select, dim3(E), dim3(1024), 0, s, S, T, E, C, topk_idx, topk_gate);
+    }
+    hipLaunchKernelGGL(k_copy_status, dim3(1), dim3(64), 0, s, status, status_out);
 }
 
 void launch_update_bias(const int32_t* counts, int E, float gamma, float* bias, hipStream_t s) {

@@ -49,7 +49,7 @@ def run_stages(cfg, dinp: Dict[str, torch.Tensor], *, noise_input=True, noise_of
     """Run route -> dispatch -> experts (-> shared) -> combine on the GPU.
     Returns host copies of every stage output."""
     c = bind_config(cfg, T=dinp["x"].shape[0], noise_input=noise_input, noise_offset=noise_offset)
-    T, E, k, d = c.T, c.n_experts, c.top_k, c.d_model
+    T, E, k, d = c.T, c.n_experts, moe.route_slots(c), c.d_model
     dt = dinp["x"].dtype
     R = moe.max_rows(c)
     w = moe.weights_from(c, dinp)

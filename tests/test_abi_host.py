@@ -157,3 +157,18 @@ def test_update_bias_rejects_bad_arguments_on_the_host():
     dummy = ctypes.c_void_p(16)   # never dereferenced: the argument checks fail first
     assert L.moe_update_bias(ctypes.byref(c), dummy, ctypes.c_float(float("nan")), dummy, None) == 1
     assert L.moe_update_bias(ctypes.byref(c), dummy, ctypes.c_float(float("inf")), dummy, None) == 1
+
+
+def test_expert_choice_slots_capacity_and_rows():
+    """Expert choice: E selection slots per token, C = ceil(cf T k / E)
+    tokens per expert (cf <= 0 reads as 1, at most T), E C permuted rows."""
+    for T, E, k, cf in [(4096, 8, 2, 1.0), (100, 6, 2, 0.0), (10, 8, 4, 4.0), (0, 8, 2, 1.0)]:
+        c = moe.config(T=T, d_model=128, d_ff=128, n_experts=E, top_k=k, gate="expert_choice",
+                       capacity_factor=cf)
+        assert moe.validate_config(c) == OK
+        C = min(T, math.ceil((cf if cf > 0 else 1.0) * T * k / E))
+        assert moe.route_slots(c) == E
+        assert moe.capacity(c) == C
+        assert moe.max_rows(c) == E * C
+    c = moe.config(T=64, d_model=128, d_ff=128, n_experts=8, top_k=3)
+    assert moe.route_slots(c) == 3

@@ -32,6 +32,10 @@ CASES = {
                                 gate="softmax_full", logit_bias="zipf", seed=45), 512),
     "noisy_k_equals_E": (Config("bal_kE", T=256, d=64, F=64, E=4, k=4, act_dtype="bf16", act="relu",
                                 gate="noisy_topk", seed=46), 0),
+    "expert_choice": (Config("bal_ec", T=768, d=128, F=64, E=16, k=2, act_dtype="bf16", act="relu",
+                             gate="expert_choice", capacity_factor=1.0, seed=47), 0),
+    "expert_choice_seq": (Config("bal_ec_seq", T=1024, d=64, F=64, E=64, k=4, act_dtype="f32", act="relu",
+                                 gate="expert_choice", capacity_factor=1.25, logit_bias="zipf", seed=48), 256),
 }
 
 
@@ -53,8 +57,9 @@ def test_balance_statistics_match_oracle(name):
     w = moe.weights_from(c, d)
     ws = moe.workspace(c)
     st = moe.alloc_stats(c, balance=True)
-    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
-    gates = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    k = moe.route_slots(c)
+    idx = torch.empty((cfg.T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((cfg.T, k), dtype=torch.float32, device="cuda")
     moe.moe_route(c, d["x"], w, idx, gates, None, st, ws)
     torch.cuda.synchronize()
     nz = inp.get("noise") if cfg.gate == "noisy_topk" else None

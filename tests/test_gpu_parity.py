@@ -45,6 +45,13 @@ MID = {
     # LDS-staged epilogue
     "tiles_256_bf16": Config("tiles_256_bf16", T=2048, d=256, F=256, E=2, k=1, act_dtype="bf16", act="swiglu",
                              gate="softmax_topk", seed=23),
+    # expert choice: every expert takes its C top tokens, E slots per token
+    "ec_bf16_swiglu": Config("ec_bf16_swiglu", T=1000, d=256, F=512, E=16, k=2, act_dtype="bf16", act="swiglu",
+                             gate="expert_choice", capacity_factor=1.0, residual=True, seed=24),
+    "ec_f32_relu": Config("ec_f32_relu", T=333, d=128, F=192, E=12, k=3, act_dtype="f32", act="relu",
+                          gate="expert_choice", capacity_factor=1.5, logit_bias="zipf", seed=25),
+    "ec_many_experts_shared": Config("ec_many_experts_shared", T=700, d=64, F=64, E=256, k=8, act_dtype="bf16",
+                                     act="swiglu", gate="expert_choice", n_shared=1, F_shared=128, seed=26),
 }
 
 
@@ -122,6 +129,35 @@ EDGE = {
     "d64": dict(d=64, F=64),
     "ragged_T": dict(T=257),
 }
+
+
+EC_EDGE = {
+    "ec_one_token": dict(T=1),
+    "ec_all_ties": dict(zero_router=True),
+    "ec_every_token": dict(capacity_factor=100.0),       # C = T: every expert takes every token
+    "ec_single_expert": dict(E=1, k=1),
+    "ec_ragged_T": dict(T=1031, E=5, k=2),
+}
+
+
+@pytest.mark.parametrize("case", list(EC_EDGE))
+def test_expert_choice_edge_cases(case):
+    kw = dict(EC_EDGE[case])
+    zero_router = kw.pop("zero_router", False)
+    cfg = Config("ec_edge", T=130, d=128, F=192, E=8, k=2, act_dtype="bf16", act="swiglu", gate="expert_choice",
+                 capacity_factor=1.0, residual=True, seed=27).replace(**kw)
+    H.log(f"[edge] {case}")
+    inp = workloads.make_inputs(cfg)
+    if zero_router:
+        inp["w_router"] = torch.zeros_like(inp["w_router"])     # every expert takes tokens 0..C-1
+    g = H.run_stages(cfg, H.to_device(inp))
+    o = full_oracle(cfg, inp)
+    check_all(cfg, g, o)
+    C = oracle.capacity(cfg)
+    np.testing.assert_array_equal(g["stats"]["counts"].numpy(), np.full(cfg.E, C))
+    if zero_router:
+        taken = g["idx"].numpy() >= 0
+        assert taken[:C].all() and not taken[C:].any()
 
 
 @pytest.mark.parametrize("case", list(EDGE))
@@ -236,6 +272,10 @@ def test_full_size_dsv3_sampled():
 
 def test_full_size_noisy_sampled():
     _sampled_full_size("noisy", n_tokens=24, max_experts=32, rows_per_expert=2)
+
+
+def test_full_size_mixtral_expert_choice_sampled():
+    _sampled_full_size("mixtral_ec", max_experts=8, rows_per_expert=3)
 
 
 def test_full_size_noisy_philox_routing():

@@ -83,3 +83,21 @@ def test_untaken_tokens_pass_through_and_stats_are_balanced():
     assert o["imbalance"] == pytest.approx(1.0)
     assert o["aux"] == pytest.approx(o["P"].sum(), rel=1e-12)
     assert o["P"].sum() == pytest.approx(1.0, rel=1e-6)
+
+
+def test_balance_statistics_under_expert_choice():
+    """Importance of expert e is the sum of its C largest probabilities (a
+    column sort of the scores); over one sequence of all T tokens every
+    expert's f is C / (T k) and the probabilities of a token sum to 1, so the
+    balance term is E C / (T k) in closed form (1 when C = T k / E)."""
+    for T, E, k, cf in [(96, 6, 2, 0.0), (64, 8, 1, 1.5), (40, 4, 3, 1.0)]:
+        cfg = _cfg(T=T, E=E, k=k, capacity_factor=cf)
+        inp = workloads.make_inputs(cfg)
+        r = oracle.route(cfg, inp["x"], inp["w_router"], want_probs=True)
+        C = oracle.capacity(cfg)
+        b = oracle.balance(cfg, r)
+        S = r["keys"].astype(np.float64)
+        imp = np.array([np.sort(S[:, e])[::-1][:C].sum() for e in range(E)])
+        np.testing.assert_allclose(b["importance"], imp, rtol=1e-12)
+        assert b["seq_aux"] == pytest.approx(E * C / (T * k), rel=1e-6)
+        assert np.isnan(b["load"]).all()

@@ -1,6 +1,6 @@
 """Seeded synthetic workloads for the sparse token-choice MoE FFN layer.
 
-This module holds the five layer shapes and a deterministic input generator.
+This module holds the six layer shapes and a deterministic input generator.
 It contains none of the layer's arithmetic: it only draws tensors.  Both the
 HIP path and the CPU oracle take their inputs from here, and nothing here
 imports either of them.
@@ -22,6 +22,10 @@ Shapes and distributions follow the layer configurations studied on the pages:
                d_ff 2048 plus one shared expert, sigmoid affinity with a
                selection-only bias, top-8 ("awesome-ai-roadmap" ch. 19,
                sections 19.3.4 and 19.5; CS336 lecture 4 notes, section 12).
+* ``mixtral_ec`` the Mixtral-shaped layer routed by expert choice: each of
+               the 8 experts takes the T k / E = 1024 tokens of highest router
+               probability (CS336 lecture 4 notes, section 4; "awesome-ai-
+               roadmap" 19.6.1), so every expert GEMM has the same M.
 
 Distributions: x ~ N(0,1); every weight ~ N(0, 1/fan_in); the DeepSeek-style
 selection bias ~ N(0, 0.1) read as a variance; the Switch logit bias is
@@ -85,6 +89,8 @@ CONFIGS: Dict[str, Config] = {
     "dsv3": Config("dsv3", T=4096, d=7168, F=2048, E=256, k=8, act_dtype="bf16",
                    act="swiglu", gate="sigmoid_bias", n_shared=1, F_shared=2048,
                    sel_bias=True, seed=1005),
+    "mixtral_ec": Config("mixtral_ec", T=4096, d=4096, F=14336, E=8, k=2, act_dtype="bf16",
+                         act="swiglu", gate="expert_choice", capacity_factor=1.0, seed=1006),
 }
 
 
