@@ -349,22 +349,25 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     // virtual slice v goes to slot v % N; slices past the end reload the last
     // one into a free slot (nobody reads it), which keeps the per-wave load
     // count of every batch the same
-    auto issueA = [&](int v) {
+    auto issueA1 = [&](int v, int q) {      // group q of this wave's part of A slice v
         uint8_t* dst = &lds[(v % NA) * SA + wave * ga * 1024];
         const int koff = (k0 + min(v, nk - 1)) * 128;
-#pragma unroll
-        for (int q = 0; q < ga; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)(dst + q * 1024), 16, voffA[q], koff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)(dst + q * 1024), 16, voffA[q], koff, 0, 0);
     };
-    auto issueB = [&](int v) {
+    auto issueB1 = [&](int v, int q) {
         uint8_t* dst = &lds[NA * SA + (v % NB) * SB + wave * gb * 1024];
         const int koff = (k0 + min(v, nk - 1)) * 128;
+        const bool up = EPI == EPI_SWIGLU && (((wave * gb + q) >> 1) & 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? rsB1 : rsB0, (lds_ptr_t)(dst + q * 1024), 16, voffB[q], koff,
+                                                 0, 0);
+    };
+    auto issueA = [&](int v) {
 #pragma unroll
-        for (int q = 0; q < gb; ++q) {
-            const bool up = EPI == EPI_SWIGLU && (((wave * gb + q) >> 1) & 1);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? rsB1 : rsB0, (lds_ptr_t)(dst + q * 1024), 16, voffB[q],
-                                                     koff, 0, 0);
-        }
+        for (int q = 0; q < ga; ++q) issueA1(v, q);
+    };
+    auto issueB = [&](int v) {
+#pragma unroll
+        for (int q = 0; q < gb; ++q) issueB1(v, q);
     };
 
     acc_t acc[FN][FM];
@@ -393,18 +396,16 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
             fo[h][s2][0] = (wm * WM + lr) * 128 + ((ch ^ swz(lr)) << 4);
             fo[h][s2][1] = NA * SA + (wn * WN + lr) * 128 + ((ch ^ swz(lr)) << 4);
         }
+    // fragment r of half slice h: k-step r / (FM + FN), then FM A blocks and
+    // FN B blocks
+    auto read1 = [&](int ks, int h, u32x4_t* f, int r) {
+        const int s2 = r / (FM + FN), q = r % (FM + FN);
+        if (q < FM) f[r] = *(const u32x4_t*)(&lds[(ks % NA) * SA] + fo[h][s2][0] + q * MB * 128);
+        else f[r] = *(const u32x4_t*)(&lds[(ks % NB) * SB] + fo[h][s2][1] + (q - FM) * MB * 128);
+    };
     auto read_frags = [&](int ks, int h, u32x4_t* f) {
-        const uint8_t* La = &lds[(ks % NA) * SA];
-        const uint8_t* Lb = &lds[(ks % NB) * SB];
 #pragma unroll
-        for (int s2 = 0; s2 < KS; ++s2) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                f[s2 * (FM + FN) + i] = *(const u32x4_t*)(La + fo[h][s2][0] + i * MB * 128);
-#pragma unroll
-            for (int i = 0; i < FN; ++i)
-                f[s2 * (FM + FN) + FM + i] = *(const u32x4_t*)(Lb + fo[h][s2][1] + i * MB * 128);
-        }
+        for (int r = 0; r < NF; ++r) read1(ks, h, f, r);
     };
     auto mma = [&](const u32x4_t* f) {
 #pragma unroll
@@ -427,6 +428,16 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
                     }
                 }
     };
+    // MFMA m of a bf16 half slice: k-step m / (FN FM), B block (m / FM) % FN,
+    // A block m % FM
+    auto mma1 = [&](const u32x4_t* f, int m) {
+        if constexpr (BF16) {
+            const int s2 = m / (FN * FM), i = (m / FM) % FN, j = m % FM;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f[s2 * (FM + FN) + FM + i]),
+                                                                __builtin_bit_cast(bf16x8_t, f[s2 * (FM + FN) + j]),
+                                                                acc[i][j], 0, 0, 0);
+        }
+    };
     // Pipeline over slices ks = 0 .. nk-1 (two half slices each).  Between
     // two barriers runs one region: the second half of slice ks (fragments
     // in f1) and the first half of slice ks+1 (f0).  Region ks:
@@ -437,8 +448,15 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     //   read slice ks+1's second half into f1; MFMAs on f0.
     // The prologue issues the batches j = -NB .. -1 (parts with a negative
     // slice index are skipped) in the same order, so the wait counts hold
-    // from the first slice on.  Scheduling hints spread the region's loads
-    // and LDS reads between its MFMAs instead of issuing them in bursts.
+    // from the first slice on.
+    // bf16 schedule, pinned with scheduling fences: each half of a region is
+    // CH chunks of MFMAs on one fragment set; the half's slice loads (A in
+    // the first half, B in the second) are dealt one per chunk or so, and the
+    // fragment reads of the other set go into the first CH/2 chunks, so they
+    // land well before use and before the next barrier drains them.  A wave
+    // then never queues a burst of loads behind the address unit while its
+    // MFMAs wait (bursts stalled the matrix unit measurably).  fp32 keeps
+    // scheduling hints only.
     constexpr int NMMA = KS * FM * FN * (BF16 ? 1 : 4);   // MFMAs per half slice
     constexpr int NV = ga + gb;                             // loads per batch
     u32x4_t f0[NF], f1[NF];
@@ -454,31 +472,68 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     mma(f0);
     __builtin_amdgcn_sched_barrier(0);
     int ks = 0;
-    for (; ks + 2 < nk; ++ks) {
-        wait_vmcnt<RD.wait>();
-        lds_barrier();
-        issueA(ks + NA);
-        issueB(ks + NB);
-        read_frags(ks + 1, 0, f0);
-        mma(f1);
-        read_frags(ks + 1, 1, f1);
-        mma(f0);
+    if constexpr (BF16) {
+        constexpr int CH = NMMA < 8 ? NMMA : 8;            // chunks per half region
+        auto half = [&](bool loads, bool is_a, int v, int rks, int h, u32x4_t* fr, const u32x4_t* fm) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * NMMA / NV > 0 ? 2 * NMMA / NV : 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * NF / NV > 0 ? 2 * NF / NV : 1, 0);       // LDS read
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                        // load
+            for (int c = 0; c < CH; ++c) {
+                if (loads) {
+                    const int nv = is_a ? ga : gb;
+#pragma unroll
+                    for (int q = 0; q < (ga > gb ? ga : gb); ++q)
+                        if (q < nv && q * CH / nv == c) {
+                            if (is_a) issueA1(v, q);
+                            else issueB1(v, q);
+                        }
+                }
+#pragma unroll
+                for (int r = 0; r < NF; ++r)
+                    if (r * (CH / 2 > 0 ? CH / 2 : 1) / NF == c) read1(rks, h, fr, r);
+#pragma unroll
+                for (int m = c * (NMMA / CH); m < (c + 1) * (NMMA / CH); ++m) mma1(fm, m);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        static_assert(NMMA % CH == 0, "chunks of whole MFMAs");
+        for (; ks + 2 < nk; ++ks) {
+            wait_vmcnt<RD.wait>();
+            lds_barrier();
+            half(true, true, ks + NA, ks + 1, 0, f0, f1);
+            half(true, false, ks + NB, ks + 1, 1, f1, f0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    for (; ks + 1 < nk; ++ks) {      // last region with a next slice: no batch left to issue
-        wait_vmcnt<RD.wait>();
-        lds_barrier();
-        read_frags(ks + 1, 0, f0);
-        mma(f1);
-        read_frags(ks + 1, 1, f1);
-        mma(f0);
-        __builtin_amdgcn_sched_barrier(0);
+        for (; ks + 1 < nk; ++ks) {      // last region with a next slice: no batch left to issue
+            wait_vmcnt<RD.wait>();
+            lds_barrier();
+            half(false, true, 0, ks + 1, 0, f0, f1);
+            half(false, false, 0, ks + 1, 1, f1, f0);
+        }
+    } else {
+        for (; ks + 2 < nk; ++ks) {
+            wait_vmcnt<RD.wait>();
+            lds_barrier();
+            issueA(ks + NA);
+            issueB(ks + NB);
+            read_frags(ks + 1, 0, f0);
+            mma(f1);
+            read_frags(ks + 1, 1, f1);
+            mma(f0);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * NMMA / NV > 0 ? 2 * NMMA / NV : 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * NF / NV > 0 ? 2 * NF / NV : 1, 0);       // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                        // load
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (; ks + 1 < nk; ++ks) {      // last region with a next slice: no batch left to issue
+            wait_vmcnt<RD.wait>();
+            lds_barrier();
+            read_frags(ks + 1, 0, f0);
+            mma(f1);
+            read_frags(ks + 1, 1, f1);
+            mma(f0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     mma(f1);
     __builtin_amdgcn_sched_barrier(0);
