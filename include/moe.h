@@ -134,12 +134,14 @@ typedef struct {
 } moe_weights;
 
 /* Load statistics (device pointers; any member may be NULL to skip it).
- * f_i is the fraction of the T*k assignments routed to expert i before
- * capacity drops (so sum f = 1), and P_i the batch mean of the router
+ * f_i is the fraction of the assignments (T*k; E*C under expert choice)
+ * routed to expert i before capacity drops (so sum f = 1), and P_i the
+ * batch mean of the router
  * probability of expert i (awesome-ai-roadmap 19.3.3; CS336 notes section
  * 9); the router probability vector is softmax(z) for the softmax gates,
- * softmax(H) for the noisy gate and s / sum(s) for the sigmoid gate.
- * imbalance = max_i n_i / (T k / E) (Lecture29, "Myth 3");
+ * softmax(H) for the noisy gate, s / sum(s) for the sigmoid gate and the
+ * scores S for expert choice.
+ * imbalance = max_i n_i / (sum_i n_i / E) (Lecture29, "Myth 3");
  * aux = E * sum_i f_i P_i (the Switch balance term without its coefficient). */
 typedef struct {
     int32_t* counts;        /* [E] assignments per expert before drops */

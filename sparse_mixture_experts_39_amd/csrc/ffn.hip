@@ -71,9 +71,8 @@ struct GemmParams {
 
 // Work decomposition.  The plan lists ceil(M_e / BM) row tiles per expert,
 // each with NT column tiles, T tiles in all.  When the last round of tiles
-// would leave the chip mostly idle (T mod kSplitUnits <= kSplitUnits / 2) and
-// that round is a large share of the launch (T < 4 kSplitUnits), those `tail`
-// tiles are cut into `split` K ranges each, one block per range:
+// would leave the chip mostly idle (T mod kSplitUnits <= kSplitUnits / 2),
+// those `tail` tiles are cut into `split` K ranges each, one block per range:
 // every block writes its fp32 partial accumulators, and k_split_fixup adds
 // the ranges of a tile in a fixed order and applies the epilogue, so results
 // do not depend on timing.  kSplitUnits is the CU count of the target chip.
@@ -622,7 +621,7 @@ __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ 
         const int total = scan[E - 1] * NT;
         const int rem = total % kSplitUnits;
         int split = 1, tail = 0;
-        if (rem > 0 && rem <= kSplitUnits / 2 && total < 4 * kSplitUnits) {
+        if (rem > 0 && rem <= kSplitUnits / 2) {
             int sp = kSplitUnits / rem;
             sp = min(sp, kMaxSplit);
             sp = min(sp, nk / 4);                  // at least 4 slices per range
