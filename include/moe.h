@@ -82,7 +82,19 @@ typedef enum {
      * the rows; awesome-ai-roadmap 19.6.1).  top_k is the mean number of
      * experts per token.  The routing outputs then have E slots per token
      * (moe_route_slots): topk_idx[t][e] = e or -1, topk_gate[t][e] = S or 0. */
-    MOE_GATE_EXPERT_CHOICE = 4
+    MOE_GATE_EXPERT_CHOICE = 4,
+    /* Hash routing: no learned score decides; a token goes to experts fixed
+     * by a hash of its id, so equal tokens always meet the same experts
+     * (CS336 notes, section 4, hash routing).  The key of expert e for a
+     * token with id u is the top 24 bits of element i = u*E + e of the
+     * Philox4x32-10 stream (counter (i>>2, noise_offset), key seed, word
+     * i & 3), read as an integer; the k experts with the largest keys are
+     * taken (ties to the lower index) and each gets gate 1: their outputs are
+     * added (CS336 notes, section 4: some implementations add the expert
+     * outputs directly).  Reads moe_weights.token_ids, not the router; P is
+     * the selection frequency 1/k per taken expert, scores are the keys.
+     * The balance statistics are not defined for it (no logits). */
+    MOE_GATE_HASH = 5
 } moe_gate;
 
 /* Expert MLP: y = W2 relu(W1 a) (Shazeer notes 2.2), or
@@ -131,6 +143,7 @@ typedef struct {
     const void* ws_gate;     /* shared expert [d_ff_shared][d] (n_shared = 1) */
     const void* ws_up;       /* shared expert [d_ff_shared][d] */
     const void* ws_down;     /* shared expert [d][d_ff_shared] */
+    const int32_t* token_ids; /* [T] token ids (HASH only), else NULL */
 } moe_weights;
 
 /* Load statistics (device pointers; any member may be NULL to skip it).

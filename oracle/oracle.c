@@ -45,7 +45,8 @@
 /* ------------------------------------------------------------------------ */
 
 enum { OC_RELU = 0, OC_SWIGLU = 1 };
-enum { OC_SOFTMAX_TOPK = 0, OC_SOFTMAX_FULL = 1, OC_NOISY_TOPK = 2, OC_SIGMOID_BIAS = 3, OC_EXPERT_CHOICE = 4 };
+enum { OC_SOFTMAX_TOPK = 0, OC_SOFTMAX_FULL = 1, OC_NOISY_TOPK = 2, OC_SIGMOID_BIAS = 3, OC_EXPERT_CHOICE = 4,
+       OC_HASH = 5 };
 
 typedef struct {
     int32_t T, d, F, E, k;
@@ -255,6 +256,21 @@ OC_EXPORT float oc_normal(uint64_t seed, uint64_t offset, uint64_t i) {
     return j < 2 ? box_muller(w[0], w[1], j & 1) : box_muller(w[2], w[3], j & 1);
 }
 
+/* Hash-routing key (CS336 notes section 4, hash routing: a fixed hash of the
+ * token, not a learned score, picks its experts).  For token id u and expert
+ * e the element is i = u*E + e of the same counter layout as the noise
+ * stream: Philox block (i>>2 low, i>>2 high, offset low, offset high) under
+ * key (seed low, seed high), word i & 3; the key is that word's top 24 bits,
+ * an integer, exact in fp32. */
+OC_EXPORT float oc_hash_key(uint64_t seed, uint64_t offset, uint64_t i) {
+    uint64_t g = i >> 2;
+    uint32_t ctr[4] = {(uint32_t)g, (uint32_t)(g >> 32), (uint32_t)offset, (uint32_t)(offset >> 32)};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t w[4];
+    oc_philox4x32_10(ctr, key, w);
+    return (float)(w[i & 3u] >> 8);
+}
+
 /* ------------------------------------------------------------------------ */
 /* batch wrappers used by the tests of the scalar functions                 */
 /* ------------------------------------------------------------------------ */
@@ -314,6 +330,8 @@ static inline int32_t order_key(float f) {
  *   SIGMOID_BIAS: s = sigmoid(z), key = s + b (awesome-ai-roadmap 19.3.4:
  *     the bias corrects only the score used for top-k selection; CS336 notes
  *     section 12: V3 uses sigmoid affinities).
+ *   HASH: key = oc_hash_key(seed, noise_offset, id_t * E + e) from the token
+ *     ids; x and the router are not read and the logits are 0.
  * S = the k largest keys, ordered by key descending, ties to the lower
  * expert index.  Gates (fp64):
  *   SOFTMAX_TOPK: softmax over the selected logits (Lecture29, eq. g_i).
@@ -325,9 +343,12 @@ static inline int32_t order_key(float f) {
  *   SIGMOID_BIAS: raw affinities s of the selected experts renormalised to
  *     sum to 1 (awesome-ai-roadmap 19.3.4: mixing weights come from the
  *     original affinity, not the bias).
+ *   HASH: 1 for every selected expert: the outputs are summed (CS336 notes
+ *     section 4: some implementations add the expert outputs directly).
  * Router probabilities p_t (fp64), whose batch mean is P_i
  * (awesome-ai-roadmap 19.3.3; CS336 notes section 9): softmax(z) for the two
- * softmax gates, softmax(H) for the noisy gate, s / sum(s) for the sigmoid.
+ * softmax gates, softmax(H) for the noisy gate, s / sum(s) for the sigmoid,
+ * and for HASH the selection itself, 1/k on each selected expert.
  *
  * Outputs: idx [T][k], gates [T][k], optional keys [T][E] (fp32), optional
  * logits [T][E] (fp32), optional probs [T][E], P [E], and for the noisy gate
@@ -338,10 +359,12 @@ OC_EXPORT int oc_route(const oc_config* cfg, const void* x, const float* w_route
                        const float* logit_bias, const float* sel_bias, const float* w_noise,
                        const float* noise, int32_t* idx, double* gates, float* keys_out,
                        float* logits_out, double* probs_out, double* P, int32_t* status,
-                       float* noise_scale_out) {
+                       float* noise_scale_out, const int32_t* token_ids) {
     const int T = cfg->T, d = cfg->d, E = cfg->E, k = cfg->k;
+    const int hashed = cfg->gate == OC_HASH;
     if (k < 1 || k > E) return -1;
     if (cfg->gate == OC_NOISY_TOPK && !w_noise) return -1;
+    if (hashed && T > 0 && !token_ids) return -1;
     double* Psum = (double*)calloc((size_t)E, sizeof(double));
     int32_t bad = 0;
     #pragma omp parallel
@@ -357,6 +380,14 @@ OC_EXPORT int oc_route(const oc_config* cfg, const void* x, const float* w_route
             const void* xr = cfg->act_bf16 ? (const void*)((const uint16_t*)x + (size_t)t * d)
                                            : (const void*)((const float*)x + (size_t)t * d);
             for (int e = 0; e < E; ++e) {
+                if (hashed) {
+                    z[e] = 0.0f;
+                    key[e] = oc_hash_key(cfg->seed, cfg->noise_offset,
+                                         (uint64_t)(uint32_t)token_ids[t] * (uint64_t)E + (uint64_t)e);
+                    if (keys_out) keys_out[(size_t)t * E + e] = key[e];
+                    if (logits_out) logits_out[(size_t)t * E + e] = 0.0f;
+                    continue;
+                }
                 float ze = dot_c(xr, cfg->act_bf16, w_router + (size_t)e * d, d);
                 if (logit_bias) ze = ze + logit_bias[e];
                 z[e] = ze;
@@ -389,7 +420,9 @@ OC_EXPORT int oc_route(const oc_config* cfg, const void* x, const float* w_route
                 idx[(size_t)t * k + j] = best;
             }
             /* router probabilities over all experts, fp64 */
-            if (cfg->gate == OC_SIGMOID_BIAS) {
+            if (hashed) {
+                for (int e = 0; e < E; ++e) prob[e] = taken[e] ? 1.0 / (double)k : 0.0;
+            } else if (cfg->gate == OC_SIGMOID_BIAS) {
                 double ssum = 0.0;
                 for (int e = 0; e < E; ++e) { prob[e] = 1.0 / (1.0 + exp(-(double)z[e])); ssum += prob[e]; }
                 for (int e = 0; e < E; ++e) prob[e] /= ssum;
@@ -406,7 +439,9 @@ OC_EXPORT int oc_route(const oc_config* cfg, const void* x, const float* w_route
             /* gates, fp64 */
             const int32_t* sel = idx + (size_t)t * k;
             double* g = gates + (size_t)t * k;
-            if (cfg->gate == OC_SOFTMAX_FULL) {
+            if (hashed) {
+                for (int j = 0; j < k; ++j) g[j] = 1.0;
+            } else if (cfg->gate == OC_SOFTMAX_FULL) {
                 for (int j = 0; j < k; ++j) g[j] = prob[sel[j]];
             } else if (cfg->gate == OC_SIGMOID_BIAS) {
                 double sum = 0.0;

@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 ACTS = {"relu": 0, "swiglu": 1}
-GATES = {"softmax_topk": 0, "softmax_full": 1, "noisy_topk": 2, "sigmoid_bias": 3, "expert_choice": 4}
+GATES = {"softmax_topk": 0, "softmax_full": 1, "noisy_topk": 2, "sigmoid_bias": 3, "expert_choice": 4, "hash": 5}
 MOE_F_ADD_RESIDUAL, MOE_F_NOISE_INPUT = 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace missing or too small",
           4: "HIP launch failed"}
@@ -62,7 +62,7 @@ class MoeConfig(ctypes.Structure):
 class MoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_router", "logit_bias", "sel_bias", "w_noise", "noise", "w_gate", "w_up", "w_down",
-        "ws_gate", "ws_up", "ws_down")]
+        "ws_gate", "ws_up", "ws_down", "token_ids")]
 
 
 class MoeStats(ctypes.Structure):
@@ -174,7 +174,7 @@ def weights_from(c: MoeConfig, t: Dict[str, torch.Tensor]) -> MoeWeights:
     (ReLU experts may use ``w1``/``w2`` for ``w_gate``/``w_down``)."""
     dt, E, d, F = _dt(c), c.n_experts, c.d_model, c.d_ff
     w = MoeWeights()
-    w.w_router = _ptr(t["w_router"], torch.float32, (E, d), "w_router")
+    w.w_router = _ptr(t.get("w_router"), torch.float32, (E, d), "w_router")
     w.logit_bias = _ptr(t.get("logit_bias"), torch.float32, (E,), "logit_bias")
     w.sel_bias = _ptr(t.get("sel_bias"), torch.float32, (E,), "sel_bias")
     w.w_noise = _ptr(t.get("w_noise"), torch.float32, (E, d), "w_noise")
@@ -182,6 +182,7 @@ def weights_from(c: MoeConfig, t: Dict[str, torch.Tensor]) -> MoeWeights:
     w.w_gate = _ptr(t.get("w_gate", t.get("w1")), dt, (E, F, d), "w_gate")
     w.w_up = _ptr(t.get("w_up"), dt, (E, F, d), "w_up")
     w.w_down = _ptr(t.get("w_down", t.get("w2")), dt, (E, d, F), "w_down")
+    w.token_ids = _ptr(t.get("token_ids"), torch.int32, (c.T,), "token_ids")
     if c.n_shared:
         Fs = c.d_ff_shared
         w.ws_gate = _ptr(t["ws_gate"].reshape(Fs, d) if "ws_gate" in t else None, dt, (Fs, d), "ws_gate")

@@ -146,6 +146,18 @@ __device__ __forceinline__ float normalc(uint64_t seed, uint64_t offset, uint64_
     return (j & 1) ? rad * s : rad * co;
 }
 
+// Hash-routing key of flat element i = u*E + e (token id u, expert e): the
+// top 24 bits of Philox word i & 3 of block (i>>2, offset) under key seed,
+// as an exact fp32 integer in [0, 2^24).
+__device__ __forceinline__ float hash_keyc(uint64_t seed, uint64_t offset, uint64_t i) {
+    const uint64_t g = i >> 2;
+    uint32_t c[4] = {(uint32_t)g, (uint32_t)(g >> 32), (uint32_t)offset, (uint32_t)(offset >> 32)};
+    philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+    const int j = (int)(i & 3u);
+    const uint32_t w = j == 0 ? c[0] : (j == 1 ? c[1] : (j == 2 ? c[2] : c[3]));
+    return (float)(w >> 8);
+}
+
 // Total order on fp32 scores: larger first, -0 == +0, NaN below -inf.
 __device__ __forceinline__ int32_t order_key(float f) {
     if (f != f) return (int32_t)0x80000000;

@@ -16,8 +16,9 @@ void launch_router_dots(bool bf16, const void* x, const float* w0, const float* 
                         float* dots, hipStream_t s);
 int select_blocks(int T, int E);
 void launch_select(const float* dots, int NC, const float* logit_bias, const float* sel_bias, const float* noise,
-                   int gate, int T, int E, int k, uint64_t seed, uint64_t noise_offset, int32_t* topk_idx,
-                   float* topk_gate, float* scores, float* P_part, int32_t* status, hipStream_t s);
+                   const int32_t* token_ids, int gate, int T, int E, int k, uint64_t seed, uint64_t noise_offset,
+                   int32_t* topk_idx, float* topk_gate, float* scores, float* P_part, int32_t* status,
+                   hipStream_t s);
 void launch_reduce_P(const float* P_part, int nblocks, int E, int T, float* P_ws, float* P_out,
                      const int32_t* status_ws, int32_t* status_out, hipStream_t s);
 void launch_zero_i32(int32_t* p, int n, hipStream_t s);

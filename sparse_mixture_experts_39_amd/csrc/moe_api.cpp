@@ -158,7 +158,7 @@ moe_status moe_validate_config(const moe_config* c) {
     if (c->T < 0 || c->d_model <= 0 || c->d_ff <= 0 || c->n_experts <= 0 || c->top_k <= 0) return MOE_ERR_INVALID_ARG;
     if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
     if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
-    if (c->gate < MOE_GATE_SOFTMAX_TOPK || c->gate > MOE_GATE_EXPERT_CHOICE) return MOE_ERR_INVALID_ARG;
+    if (c->gate < MOE_GATE_SOFTMAX_TOPK || c->gate > MOE_GATE_HASH) return MOE_ERR_INVALID_ARG;
     if (c->top_k > c->n_experts) return MOE_ERR_INVALID_ARG;
     if (c->n_shared < 0 || c->n_shared > 1) return MOE_ERR_INVALID_ARG;
     if (c->n_shared == 1 && c->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
@@ -214,8 +214,10 @@ moe_status moe_route(const moe_config* c, const void* x, const moe_weights* w, i
                      float* scores, const moe_stats* st, void* ws, size_t ws_bytes, void* stream) {
     moe_status s = moe_validate_config(c);
     if (s != MOE_OK) return s;
-    if (!w || !w->w_router) return MOE_ERR_INVALID_ARG;
-    if (c->T > 0 && (!x || !topk_idx || !topk_gate)) return MOE_ERR_INVALID_ARG;
+    const bool hashed = c->gate == MOE_GATE_HASH;
+    if (!w || (!hashed && !w->w_router)) return MOE_ERR_INVALID_ARG;
+    if (c->T > 0 && ((!hashed && !x) || !topk_idx || !topk_gate)) return MOE_ERR_INVALID_ARG;
+    if (hashed && c->T > 0 && !w->token_ids) return MOE_ERR_INVALID_ARG;
     if (c->gate == MOE_GATE_NOISY_TOPK) {
         if (!w->w_noise) return MOE_ERR_INVALID_ARG;
         if ((c->flags & MOE_F_NOISE_INPUT) && !w->noise) return MOE_ERR_INVALID_ARG;
@@ -228,10 +230,13 @@ moe_status moe_route(const moe_config* c, const void* x, const moe_weights* w, i
     const int NC = noisy ? 2 * E : E;
     float* dots = at<float>(ws, L.dots);
     int32_t* status = at<int32_t>(ws, L.status);
-    moe::launch_zero_i32(status, 1, h);
-    moe::launch_router_dots(is_bf16(c), x, w->w_router, noisy ? w->w_noise : nullptr, T, c->d_model, E, NC, dots, h);
     const bool balance = st && (st->z_loss || st->importance || st->importance_cv2 || st->load || st->load_cv2 ||
                                 st->seq_aux);
+    if (hashed && balance) return MOE_ERR_UNSUPPORTED;
+    moe::launch_zero_i32(status, 1, h);
+    if (!hashed)
+        moe::launch_router_dots(is_bf16(c), x, w->w_router, noisy ? w->w_noise : nullptr, T, c->d_model, E, NC, dots,
+                                h);
     if (expert_choice(c)) {
         float* S = scores ? scores : at<float>(ws, L.ec_scores);
         moe::launch_ec_route(dots, w->logit_bias, T, E, (int)ec_capacity_of(c), S, at<float>(ws, L.P_ws),
@@ -246,7 +251,8 @@ moe_status moe_route(const moe_config* c, const void* x, const moe_weights* w, i
     }
     const float* noise = (noisy && (c->flags & MOE_F_NOISE_INPUT)) ? w->noise : nullptr;
     moe::launch_select(dots, NC, w->logit_bias, c->gate == MOE_GATE_SIGMOID_BIAS ? w->sel_bias : nullptr, noise,
-                       c->gate, T, E, c->top_k, c->seed, c->noise_offset, topk_idx, topk_gate, scores,
+                       hashed ? w->token_ids : nullptr, c->gate, T, E, c->top_k, c->seed, c->noise_offset, topk_idx,
+                       topk_gate, scores,
                        at<float>(ws, L.P_part), status, h);
     moe::launch_reduce_P(at<float>(ws, L.P_part), T > 0 ? moe::select_blocks(T, E) : 0, E, T, at<float>(ws, L.P_ws),
                          st ? st->P : nullptr, status, st ? st->device_status : nullptr, h);
@@ -399,7 +405,7 @@ moe_status moe_layer_forward(const moe_config* c, const moe_weights* w, const vo
                              const moe_stats* st, void* ws, size_t ws_bytes, void* stream) {
     moe_status s = moe_validate_config(c);
     if (s != MOE_OK) return s;
-    if (!w || !w->w_router) return MOE_ERR_INVALID_ARG;
+    if (!w || (c->gate != MOE_GATE_HASH && !w->w_router)) return MOE_ERR_INVALID_ARG;
     if (c->T > 0 && (!x || !out)) return MOE_ERR_INVALID_ARG;
     if (c->T > 0 && (!w->w_gate || !w->w_down || (c->act == MOE_ACT_SWIGLU && !w->w_up))) return MOE_ERR_INVALID_ARG;
     if (c->n_shared == 1 && c->T > 0 && (!w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_INVALID_ARG;

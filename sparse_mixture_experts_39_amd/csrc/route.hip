@@ -13,7 +13,7 @@
 // Kernels
 //   k_router_dots   SIMT register-blocked tile GEMM  x[T][d] . W[NC][d]^T -> dots[T][NC]
 //                   (NC = E, or 2E for the noisy gate whose second half is x W_noise)
-//   k_select        G lanes per token: scores, k passes of a segmented arg-max,
+//   k_select        G lanes per token: scores (or hashed keys), k passes of a segmented arg-max,
 //                   gates, router probabilities, per-block P partial sums
 //   k_reduce_P      fixed-order two-level sum of the per-block partials -> P[E]
 //   k_balance       (when requested) z-loss, importance and load partials;
@@ -195,10 +195,10 @@ __device__ __forceinline__ float seg_sum_f(float v) {
 template <int G, int V>
 __global__ __launch_bounds__(256) void k_select(const float* __restrict__ dots, int NC, const float* __restrict__ logit_bias,
                                                 const float* __restrict__ sel_bias, const float* __restrict__ noise,
-                                                int gate, int T, int E, int k, uint64_t seed, uint64_t noise_offset,
-                                                int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
-                                                float* __restrict__ scores, float* __restrict__ P_part,
-                                                int32_t* __restrict__ status) {
+                                                const int32_t* __restrict__ token_ids, int gate, int T, int E, int k,
+                                                uint64_t seed, uint64_t noise_offset, int32_t* __restrict__ topk_idx,
+                                                float* __restrict__ topk_gate, float* __restrict__ scores,
+                                                float* __restrict__ P_part, int32_t* __restrict__ status) {
     constexpr int SEGS = 64 / G;
     constexpr int TB = 4 * SEGS;
     __shared__ float red[4][V * G];
@@ -207,6 +207,8 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ dots, 
     const int seg = lane / G, g = lane % G;
     const int t = blockIdx.x * TB + wave * SEGS + seg;
     const bool tok_ok = t < T;
+    const bool hashed = gate == MOE_GATE_HASH;
+    const uint32_t uid = (hashed && tok_ok) ? (uint32_t)token_ids[t] : 0u;
 
     float key[V], src[V], sig[V];
     bool valid[V];
@@ -218,6 +220,11 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ dots, 
         valid[v] = tok_ok && e < E;
         key[v] = 0.0f; src[v] = 0.0f; sig[v] = 0.0f;
         if (!valid[v]) continue;
+        if (hashed) {          // no router: the key is a hash of (token id, expert)
+            key[v] = canon::hash_keyc(seed, noise_offset, (uint64_t)uid * (uint64_t)E + (uint64_t)e);
+            if (scores) scores[(int64_t)t * E + e] = key[v];
+            continue;
+        }
         float z = dots[(int64_t)t * NC + e];
         if (logit_bias) z = z + logit_bias[e];
         float kv = z, sv = z;
@@ -282,7 +289,10 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ dots, 
     // gates
     if (tok_ok && g == 0) {
         float gv[16];
-        if (gate == MOE_GATE_SOFTMAX_FULL) {
+        if (hashed) {          // the selected experts' outputs are added
+#pragma unroll
+            for (int j = 0; j < 16; ++j) gv[j] = 1.0f;
+        } else if (gate == MOE_GATE_SOFTMAX_FULL) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) gv[j] = canon::expc(src_sel[j] - m_all) / s_all;
         } else if (gate == MOE_GATE_SIGMOID_BIAS) {
@@ -312,7 +322,10 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ dots, 
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         float p = 0.0f;
-        if (valid[v]) p = gate == MOE_GATE_SIGMOID_BIAS ? sig[v] / s_all : canon::expc(src[v] - m_all) / s_all;
+        if (valid[v]) {
+            if (hashed) p = ((taken >> v) & 1u) ? 1.0f / (float)k : 0.0f;
+            else p = gate == MOE_GATE_SIGMOID_BIAS ? sig[v] / s_all : canon::expc(src[v] - m_all) / s_all;
+        }
         pacc[v] = p;
     }
 #pragma unroll
@@ -764,13 +777,14 @@ int select_blocks(int T, int E) {
 }
 
 void launch_select(const float* dots, int NC, const float* logit_bias, const float* sel_bias, const float* noise,
-                   int gate, int T, int E, int k, uint64_t seed, uint64_t noise_offset, int32_t* topk_idx,
-                   float* topk_gate, float* scores, float* P_part, int32_t* status, hipStream_t s) {
+                   const int32_t* token_ids, int gate, int T, int E, int k, uint64_t seed, uint64_t noise_offset,
+                   int32_t* topk_idx, float* topk_gate, float* scores, float* P_part, int32_t* status,
+                   hipStream_t s) {
     if (T <= 0) return;
     const int G = E >= 64 ? 64 : pow2_at_least(E);
     const int V = (E + G - 1) / G;
     const int nb = select_blocks(T, E);
-#define MOE_SEL_ARGS dots, NC, logit_bias, sel_bias, noise, gate, T, E, k, seed, noise_offset, topk_idx, topk_gate, scores, P_part, status
+#define MOE_SEL_ARGS dots, NC, logit_bias, sel_bias, noise, token_ids, gate, T, E, k, seed, noise_offset, topk_idx, topk_gate, scores, P_part, status
 #define MOE_SEL(GG, VV) hipLaunchKernelGGL((k_select<GG, VV>), dim3(nb), dim3(256), 0, s, MOE_SEL_ARGS)
     if (G < 64) {
         switch (G) {

@@ -172,3 +172,20 @@ def test_expert_choice_slots_capacity_and_rows():
         assert moe.max_rows(c) == E * C
     c = moe.config(T=64, d_model=128, d_ff=128, n_experts=8, top_k=3)
     assert moe.route_slots(c) == 3
+
+
+def test_hash_gate_checks_token_ids_and_refuses_balance_statistics():
+    """Hash routing reads token ids instead of the router, and has no logits
+    for the balance statistics: both are caught before any launch."""
+    L = moe.lib()
+    c = _cfg(gate="hash")
+    w = moe.MoeWeights()          # no router: allowed for the hash gate
+    fake = ctypes.c_void_p(0x1000)
+    big = 1 << 40
+    assert L.moe_route(ctypes.byref(c), fake, ctypes.byref(w), fake, fake, None, None, fake, big, None) == INVALID
+    w.token_ids = fake
+    st = moe.MoeStats()
+    st.z_loss = fake
+    assert L.moe_route(ctypes.byref(c), fake, ctypes.byref(w), fake, fake, None, ctypes.byref(st), fake, big,
+                       None) == UNSUPPORTED
+    assert moe.route_slots(c) == c.top_k

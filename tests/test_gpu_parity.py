@@ -52,6 +52,13 @@ MID = {
                           gate="expert_choice", capacity_factor=1.5, logit_bias="zipf", seed=25),
     "ec_many_experts_shared": Config("ec_many_experts_shared", T=700, d=64, F=64, E=256, k=8, act_dtype="bf16",
                                      act="swiglu", gate="expert_choice", n_shared=1, F_shared=128, seed=26),
+    # hash routing: experts from a hash of Zipf token ids, outputs summed
+    "hash_bf16_swiglu": Config("hash_bf16_swiglu", T=1000, d=256, F=512, E=16, k=2, act_dtype="bf16", act="swiglu",
+                               gate="hash", residual=True, seed=28),
+    "hash_f32_top1_cap": Config("hash_f32_top1_cap", T=333, d=128, F=192, E=12, k=1, act_dtype="f32", act="relu",
+                                gate="hash", capacity_factor=1.25, residual=True, seed=29),
+    "hash_k_equals_E": Config("hash_k_equals_E", T=130, d=128, F=128, E=4, k=4, act_dtype="bf16", act="swiglu",
+                              gate="hash", seed=30),
 }
 
 
@@ -213,7 +220,8 @@ def _sampled_full_size(name, n_tokens=12, rows_per_expert=2, max_experts=24, noi
                      logit_bias=dinp["logit_bias"].cpu() if "logit_bias" in dinp else None,
                      sel_bias=dinp["sel_bias"].cpu() if "sel_bias" in dinp else None,
                      w_noise=dinp["w_noise"].cpu() if "w_noise" in dinp else None,
-                     noise=dinp["noise"].cpu() if (noise_input and "noise" in dinp) else None)
+                     noise=dinp["noise"].cpu() if (noise_input and "noise" in dinp) else None,
+                     token_ids=dinp["token_ids"].cpu() if "token_ids" in dinp else None)
     o.update(oracle.dispatch(cfg, o["idx"]))
     o.update(oracle.stats(cfg, o["counts"], o["kept"], o["P"], cfg.T))
     o["status"] = 0
@@ -276,6 +284,10 @@ def test_full_size_noisy_sampled():
 
 def test_full_size_mixtral_expert_choice_sampled():
     _sampled_full_size("mixtral_ec", max_experts=8, rows_per_expert=3)
+
+
+def test_full_size_mixtral_hash_sampled():
+    _sampled_full_size("mixtral_hash", max_experts=8, rows_per_expert=3)
 
 
 def test_full_size_noisy_philox_routing():

@@ -1,6 +1,6 @@
 """Seeded synthetic workloads for the sparse token-choice MoE FFN layer.
 
-This module holds the six layer shapes and a deterministic input generator.
+This module holds the seven layer shapes and a deterministic input generator.
 It contains none of the layer's arithmetic: it only draws tensors.  Both the
 HIP path and the CPU oracle take their inputs from here, and nothing here
 imports either of them.
@@ -26,6 +26,9 @@ Shapes and distributions follow the layer configurations studied on the pages:
                the 8 experts takes the T k / E = 1024 tokens of highest router
                probability (CS336 lecture 4 notes, section 4; "awesome-ai-
                roadmap" 19.6.1), so every expert GEMM has the same M.
+* ``mixtral_hash`` the Mixtral-shaped layer routed by a hash of Zipf(1.1)
+               token ids, top-2 with the outputs summed (CS336 lecture 4
+               notes, section 4, hash routing).
 
 Distributions: x ~ N(0,1); every weight ~ N(0, 1/fan_in); the DeepSeek-style
 selection bias ~ N(0, 0.1) read as a variance; the Switch logit bias is
@@ -59,7 +62,7 @@ class Config:
     k: int                      # top-k
     act_dtype: str              # "f32" | "bf16": activations and expert weights
     act: str                    # "relu" | "swiglu"
-    gate: str                   # "softmax_topk" | "softmax_full" | "noisy_topk" | "sigmoid_bias" | "expert_choice"
+    gate: str                   # "softmax_topk" | "softmax_full" | "noisy_topk" | "sigmoid_bias" | "expert_choice" | "hash"
     capacity_factor: float = 0.0  # <= 0: dropless
     residual: bool = False
     n_shared: int = 0
@@ -91,6 +94,8 @@ CONFIGS: Dict[str, Config] = {
                    sel_bias=True, seed=1005),
     "mixtral_ec": Config("mixtral_ec", T=4096, d=4096, F=14336, E=8, k=2, act_dtype="bf16",
                          act="swiglu", gate="expert_choice", capacity_factor=1.0, seed=1006),
+    "mixtral_hash": Config("mixtral_hash", T=4096, d=4096, F=14336, E=8, k=2, act_dtype="bf16",
+                           act="swiglu", gate="hash", seed=1007),
 }
 
 
@@ -130,7 +135,8 @@ def make_inputs(cfg: Config, device="cpu", with_noise: Optional[bool] = None) ->
     in), ``logit_bias`` [E], ``sel_bias`` [E], the expert stacks
     (``w_gate``/``w_up`` [E][F][d] and ``w_down`` [E][d][F] for SwiGLU,
     ``w1`` [E][F][d] and ``w2`` [E][d][F] for ReLU) and the shared expert
-    (``ws_gate``/``ws_up`` [S][Fs][d], ``ws_down`` [S][d][Fs]).
+    (``ws_gate``/``ws_up`` [S][Fs][d], ``ws_down`` [S][d][Fs]); for the hash
+    gate ``token_ids`` [T] int32.
     Weight layouts are [out][in] (the reduction dimension is contiguous).
     """
     device = torch.device(device)
@@ -164,4 +170,11 @@ def make_inputs(cfg: Config, device="cpu", with_noise: Optional[bool] = None) ->
         with_noise = cfg.gate == "noisy_topk"
     if with_noise:
         inp["noise"] = _normal((T, E), 1.0, gen, device, torch.float32)
+    if cfg.gate == "hash":
+        # token ids with a Zipf(1.1) law over a 32000-id vocabulary, so that
+        # frequent ids repeat (CS336 notes section 4: under a Zipf law a word
+        # like "the" can dominate one expert)
+        ranks = torch.arange(1, 32001, dtype=torch.float64, device=device)
+        w = ranks.pow(-1.1)
+        inp["token_ids"] = torch.multinomial(w / w.sum(), T, replacement=True, generator=gen).to(torch.int32)
     return inp
