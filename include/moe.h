@@ -94,7 +94,20 @@ typedef enum {
      * outputs directly).  Reads moe_weights.token_ids, not the router; P is
      * the selection frequency 1/k per taken expert, scores are the keys.
      * The balance statistics are not defined for it (no logits). */
-    MOE_GATE_HASH = 5
+    MOE_GATE_HASH = 5,
+    /* Hierarchical (two-level) gating (Shazeer notes, appendix B: a primary
+     * gate picks groups, a secondary gate picks experts inside each picked
+     * group, which cuts the branching factor from n to about sqrt(n)): the
+     * E experts form n_groups groups of b = E / n_groups consecutive experts;
+     * the primary logits zp = W_group x pick the group_top_k largest groups,
+     * the secondary logits z = W_r x (+ logit bias) of each picked group pick
+     * its ks = top_k / group_top_k largest experts (ties to the lower index);
+     * each gate is a softmax over the picked logits, and expert (i, j) gets
+     * gp_i * gs_ij.  Slots are ordered by group rank, then expert rank.  The
+     * router probability of expert (i, j) is softmax(zp)_i times the softmax
+     * of group i's b logits at j.  n_groups <= 64, b <= 64; balance
+     * statistics are not offered for it. */
+    MOE_GATE_HIERARCHICAL = 6
 } moe_gate;
 
 /* Expert MLP: y = W2 relu(W1 a) (Shazeer notes 2.2), or
@@ -128,6 +141,8 @@ typedef struct {
     int32_t seq_len;        /* tokens per sequence for stats.seq_aux: 0 = the whole call is one
                                sequence, else a multiple of 256 that divides T */
     int32_t reserved;       /* must be 0 */
+    int32_t n_groups;       /* HIERARCHICAL: groups of the primary gate; else 0 */
+    int32_t group_top_k;    /* HIERARCHICAL: groups picked per token (divides top_k); else 0 */
 } moe_config;
 
 /* Weights of one layer (device pointers). */
@@ -144,6 +159,7 @@ typedef struct {
     const void* ws_up;       /* shared expert [d_ff_shared][d] */
     const void* ws_down;     /* shared expert [d][d_ff_shared] */
     const int32_t* token_ids; /* [T] token ids (HASH only), else NULL */
+    const float* w_group_router; /* [n_groups][d] fp32 primary router (HIERARCHICAL only) */
 } moe_weights;
 
 /* Load statistics (device pointers; any member may be NULL to skip it).

@@ -25,7 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-GATES = {"softmax_topk": 0, "softmax_full": 1, "noisy_topk": 2, "sigmoid_bias": 3, "expert_choice": 4, "hash": 5}
+GATES = {"softmax_topk": 0, "softmax_full": 1, "noisy_topk": 2, "sigmoid_bias": 3, "expert_choice": 4, "hash": 5, "hierarchical": 6}
 ACTS = {"relu": 0, "swiglu": 1}
 MAP_FN = {"exp": 0, "log": 1, "log1p": 2, "softplus": 3, "sigmoid": 4, "sin": 5, "cos": 6}
 
@@ -39,6 +39,7 @@ class _Cfg(ctypes.Structure):
         ("n_shared", ctypes.c_int32), ("F_shared", ctypes.c_int32),
         ("round_intermediates", ctypes.c_int32), ("pad_", ctypes.c_int32),
         ("seed", ctypes.c_uint64), ("noise_offset", ctypes.c_uint64),
+        ("n_groups", ctypes.c_int32), ("group_k", ctypes.c_int32),
     ]
 
 
@@ -73,7 +74,7 @@ def lib():
         L.oc_normal_batch.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64, P]
         L.oc_philox4x32_10.argtypes = [P, P, P]
         L.oc_route.restype = ctypes.c_int
-        L.oc_route.argtypes = [ctypes.POINTER(_Cfg)] + [P] * 15
+        L.oc_route.argtypes = [ctypes.POINTER(_Cfg)] + [P] * 16
         L.oc_capacity.restype = ctypes.c_int64
         L.oc_capacity.argtypes = [ctypes.POINTER(_Cfg)]
         L.oc_dispatch.restype = ctypes.c_int64
@@ -142,6 +143,8 @@ def make_cfg(cfg, *, round_intermediates: bool = True, seed: Optional[int] = Non
     c.round_intermediates = 1 if round_intermediates else 0
     c.seed = cfg.seed if seed is None else seed
     c.noise_offset = noise_offset
+    c.n_groups = getattr(cfg, "n_groups", 0)
+    c.group_k = getattr(cfg, "group_top_k", 0)
     return c
 
 
@@ -189,7 +192,7 @@ def hash_key(seed: int, offset: int, i: int) -> float:
 
 def route(cfg, x, w_router, *, logit_bias=None, sel_bias=None, w_noise=None, noise=None,
           seed: Optional[int] = None, noise_offset: int = 0, want_probs: bool = False,
-          token_ids=None) -> Dict[str, np.ndarray]:
+          token_ids=None, w_group_router=None) -> Dict[str, np.ndarray]:
     """Router logits, scores, top-k indices, gates and P for all tokens.
     ``noise`` [T][E] fp32, or None to draw it from the Philox stream.
     Expert choice returns E slots per token (idx -1 where the expert did not
@@ -230,7 +233,7 @@ def route(cfg, x, w_router, *, logit_bias=None, sel_bias=None, w_noise=None, noi
     nscale = np.empty((T, E), dtype=np.float32) if cfg.gate == "noisy_topk" else None
     rc = lib().oc_route(ctypes.byref(c), _ptr(xa), _ptr(wr), _ptr(lb), _ptr(sb), _ptr(wn), _ptr(nz),
                         _ptr(idx), _ptr(gates), _ptr(keys), _ptr(logits), _ptr(probs), _ptr(P), _ptr(status),
-                        _ptr(nscale), _ptr(_np(token_ids, np.int32)))
+                        _ptr(nscale), _ptr(_np(token_ids, np.int32)), _ptr(_np(w_group_router, np.float32)))
     if rc != 0:
         raise ValueError("oracle route rejected the configuration")
     out = dict(idx=idx, gates=gates, keys=keys, logits=logits, P=P, status=int(status[0]))
@@ -388,7 +391,8 @@ def forward(cfg, inputs, *, round_intermediates: bool = True, noise: str = "inpu
     nz = inputs.get("noise") if (cfg.gate == "noisy_topk" and noise == "input") else None
     r = route(cfg, x, inputs["w_router"], logit_bias=inputs.get("logit_bias"),
               sel_bias=inputs.get("sel_bias"), w_noise=inputs.get("w_noise"), noise=nz,
-              noise_offset=noise_offset, want_probs=True, token_ids=inputs.get("token_ids"))
+              noise_offset=noise_offset, want_probs=True, token_ids=inputs.get("token_ids"),
+              w_group_router=inputs.get("w_group_router"))
     dp = dispatch(cfg, r["idx"], T=T)
     x_perm = gather_rows(cfg, x, dp["perm_src"])
     R = dp["R"]

@@ -46,7 +46,7 @@
 
 enum { OC_RELU = 0, OC_SWIGLU = 1 };
 enum { OC_SOFTMAX_TOPK = 0, OC_SOFTMAX_FULL = 1, OC_NOISY_TOPK = 2, OC_SIGMOID_BIAS = 3, OC_EXPERT_CHOICE = 4,
-       OC_HASH = 5 };
+       OC_HASH = 5, OC_HIERARCHICAL = 6 };
 
 typedef struct {
     int32_t T, d, F, E, k;
@@ -59,6 +59,7 @@ typedef struct {
     int32_t round_intermediates; /* 1: round h, y, shared, out to the activation dtype */
     int32_t pad_;
     uint64_t seed, noise_offset; /* Philox key and counter offset for the noisy gate */
+    int32_t n_groups, group_k;   /* hierarchical gate: groups, and groups picked per token */
 } oc_config;
 
 /* ------------------------------------------------------------------------ */
@@ -332,6 +333,12 @@ static inline int32_t order_key(float f) {
  *     section 12: V3 uses sigmoid affinities).
  *   HASH: key = oc_hash_key(seed, noise_offset, id_t * E + e) from the token
  *     ids; x and the router are not read and the logits are 0.
+ *   HIERARCHICAL (Shazeer notes, appendix B: a primary gate picks groups, a
+ *     secondary gate inside each picked group picks experts): the E experts
+ *     form A = n_groups groups of B = E / A consecutive experts; the primary
+ *     logits zp = W_group x (no bias) pick the group_k largest groups, then
+ *     in each picked group the keys z of its B experts pick ks = k / group_k
+ *     experts; slot order is group rank, then expert rank.
  * S = the k largest keys, ordered by key descending, ties to the lower
  * expert index.  Gates (fp64):
  *   SOFTMAX_TOPK: softmax over the selected logits (Lecture29, eq. g_i).
@@ -345,10 +352,14 @@ static inline int32_t order_key(float f) {
  *     original affinity, not the bias).
  *   HASH: 1 for every selected expert: the outputs are summed (CS336 notes
  *     section 4: some implementations add the expert outputs directly).
+ *   HIERARCHICAL: softmax over the picked primary logits times softmax over
+ *     the picked logits of the expert's group (appendix B: the output is the
+ *     sum over groups and experts of the product of the two gates).
  * Router probabilities p_t (fp64), whose batch mean is P_i
  * (awesome-ai-roadmap 19.3.3; CS336 notes section 9): softmax(z) for the two
  * softmax gates, softmax(H) for the noisy gate, s / sum(s) for the sigmoid,
- * and for HASH the selection itself, 1/k on each selected expert.
+ * for HASH the selection itself, 1/k on each selected expert, and for
+ * HIERARCHICAL softmax(zp)_g times the softmax of group g's logits.
  *
  * Outputs: idx [T][k], gates [T][k], optional keys [T][E] (fp32), optional
  * logits [T][E] (fp32), optional probs [T][E], P [E], and for the noisy gate
@@ -359,9 +370,15 @@ OC_EXPORT int oc_route(const oc_config* cfg, const void* x, const float* w_route
                        const float* logit_bias, const float* sel_bias, const float* w_noise,
                        const float* noise, int32_t* idx, double* gates, float* keys_out,
                        float* logits_out, double* probs_out, double* P, int32_t* status,
-                       float* noise_scale_out, const int32_t* token_ids) {
+                       float* noise_scale_out, const int32_t* token_ids, const float* w_group) {
     const int T = cfg->T, d = cfg->d, E = cfg->E, k = cfg->k;
     const int hashed = cfg->gate == OC_HASH;
+    const int hier = cfg->gate == OC_HIERARCHICAL;
+    const int A = hier ? cfg->n_groups : 1, KP = hier ? cfg->group_k : 1;
+    if (hier && (A < 1 || A > 64 || KP < 1 || KP > A || E % A != 0 || k % KP != 0 || k / KP > E / A || k > 16 ||
+                 !w_group))
+        return -1;
+    const int B = E / A, KS = k / KP;
     if (k < 1 || k > E) return -1;
     if (cfg->gate == OC_NOISY_TOPK && !w_noise) return -1;
     if (hashed && T > 0 && !token_ids) return -1;
@@ -410,17 +427,67 @@ OC_EXPORT int oc_route(const oc_config* cfg, const void* x, const float* w_route
             }
             /* top-k: k passes of a strict arg-max over the experts not yet taken */
             memset(taken, 0, (size_t)E);
-            for (int j = 0; j < k; ++j) {
-                int best = -1;
-                for (int e = 0; e < E; ++e) {
-                    if (taken[e]) continue;
-                    if (best < 0 || order_key(key[e]) > order_key(key[best])) best = e;
+            double hg[16];               /* hierarchical gates of the k slots */
+            if (hier) {
+                /* primary logits, picked groups, then experts inside each group */
+                double zp[64], pp[64];
+                int gtaken[64] = {0};
+                for (int g = 0; g < A; ++g) zp[g] = (double)dot_c(xr, cfg->act_bf16, w_group + (size_t)g * d, d);
+                for (int g = 0; g < A; ++g) if (!isfinite(zp[g])) badloc = 1;
+                int gsel[16];
+                for (int j = 0; j < KP; ++j) {
+                    int best = -1;
+                    for (int g = 0; g < A; ++g) {
+                        if (gtaken[g]) continue;
+                        if (best < 0 || order_key((float)zp[g]) > order_key((float)zp[best])) best = g;
+                    }
+                    gtaken[best] = 1;
+                    gsel[j] = best;
                 }
-                taken[best] = 1;
-                idx[(size_t)t * k + j] = best;
+                double mpk = zp[gsel[0]], spk = 0.0, gpk[16];
+                for (int j = 0; j < KP; ++j) { gpk[j] = exp(zp[gsel[j]] - mpk); spk += gpk[j]; }
+                for (int j = 0; j < KP; ++j) {
+                    const int g = gsel[j];
+                    int esel[16];
+                    for (int q = 0; q < KS; ++q) {
+                        int best = -1;
+                        for (int e = g * B; e < (g + 1) * B; ++e) {
+                            if (taken[e]) continue;
+                            if (best < 0 || order_key(key[e]) > order_key(key[best])) best = e;
+                        }
+                        taken[best] = 1;
+                        esel[q] = best;
+                        idx[(size_t)t * k + j * KS + q] = best;
+                    }
+                    double ms = (double)key[esel[0]], ss = 0.0, gs[16];
+                    for (int q = 0; q < KS; ++q) { gs[q] = exp((double)key[esel[q]] - ms); ss += gs[q]; }
+                    for (int q = 0; q < KS; ++q) hg[j * KS + q] = (gpk[j] / spk) * (gs[q] / ss);
+                }
+                /* probabilities: softmax(zp)_g times the softmax of group g's logits */
+                double mpa = -INFINITY, spa = 0.0;
+                for (int g = 0; g < A; ++g) if (zp[g] > mpa) mpa = zp[g];
+                for (int g = 0; g < A; ++g) { pp[g] = exp(zp[g] - mpa); spa += pp[g]; }
+                for (int g = 0; g < A; ++g) {
+                    double mg = -INFINITY, sg = 0.0;
+                    for (int e = g * B; e < (g + 1) * B; ++e) if ((double)z[e] > mg) mg = (double)z[e];
+                    for (int e = g * B; e < (g + 1) * B; ++e) sg += exp((double)z[e] - mg);
+                    for (int e = g * B; e < (g + 1) * B; ++e) prob[e] = (pp[g] / spa) * (exp((double)z[e] - mg) / sg);
+                }
+            } else {
+                for (int j = 0; j < k; ++j) {
+                    int best = -1;
+                    for (int e = 0; e < E; ++e) {
+                        if (taken[e]) continue;
+                        if (best < 0 || order_key(key[e]) > order_key(key[best])) best = e;
+                    }
+                    taken[best] = 1;
+                    idx[(size_t)t * k + j] = best;
+                }
             }
             /* router probabilities over all experts, fp64 */
-            if (hashed) {
+            if (hier) {
+                /* computed with the selection above */
+            } else if (hashed) {
                 for (int e = 0; e < E; ++e) prob[e] = taken[e] ? 1.0 / (double)k : 0.0;
             } else if (cfg->gate == OC_SIGMOID_BIAS) {
                 double ssum = 0.0;
@@ -441,6 +508,8 @@ OC_EXPORT int oc_route(const oc_config* cfg, const void* x, const float* w_route
             double* g = gates + (size_t)t * k;
             if (hashed) {
                 for (int j = 0; j < k; ++j) g[j] = 1.0;
+            } else if (hier) {
+                for (int j = 0; j < k; ++j) g[j] = hg[j];
             } else if (cfg->gate == OC_SOFTMAX_FULL) {
                 for (int j = 0; j < k; ++j) g[j] = prob[sel[j]];
             } else if (cfg->gate == OC_SIGMOID_BIAS) {

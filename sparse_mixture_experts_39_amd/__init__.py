@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 ACTS = {"relu": 0, "swiglu": 1}
-GATES = {"softmax_topk": 0, "softmax_full": 1, "noisy_topk": 2, "sigmoid_bias": 3, "expert_choice": 4, "hash": 5}
+GATES = {"softmax_topk": 0, "softmax_full": 1, "noisy_topk": 2, "sigmoid_bias": 3, "expert_choice": 4, "hash": 5, "hierarchical": 6}
 MOE_F_ADD_RESIDUAL, MOE_F_NOISE_INPUT = 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace missing or too small",
           4: "HIP launch failed"}
@@ -56,13 +56,14 @@ class MoeConfig(ctypes.Structure):
         ("gate", ctypes.c_int32), ("capacity_factor", ctypes.c_float), ("flags", ctypes.c_uint32),
         ("seed", ctypes.c_uint64), ("noise_offset", ctypes.c_uint64),
         ("seq_len", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("n_groups", ctypes.c_int32), ("group_top_k", ctypes.c_int32),
     ]
 
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_router", "logit_bias", "sel_bias", "w_noise", "noise", "w_gate", "w_up", "w_down",
-        "ws_gate", "ws_up", "ws_down", "token_ids")]
+        "ws_gate", "ws_up", "ws_down", "token_ids", "w_group_router")]
 
 
 class MoeStats(ctypes.Structure):
@@ -125,7 +126,8 @@ def lib():
 def config(*, T: int, d_model: int, d_ff: int, n_experts: int, top_k: int, act_dtype: str = "bf16",
            act: str = "swiglu", gate: str = "softmax_topk", capacity_factor: float = 0.0,
            residual: bool = False, n_shared: int = 0, d_ff_shared: int = 0, noise_input: bool = False,
-           seed: int = 0, noise_offset: int = 0, seq_len: int = 0) -> MoeConfig:
+           seed: int = 0, noise_offset: int = 0, seq_len: int = 0, n_groups: int = 0,
+           group_top_k: int = 0) -> MoeConfig:
     c = MoeConfig()
     c.T, c.d_model, c.d_ff, c.n_experts, c.top_k = T, d_model, d_ff, n_experts, top_k
     c.n_shared, c.d_ff_shared = n_shared, d_ff_shared
@@ -136,6 +138,7 @@ def config(*, T: int, d_model: int, d_ff: int, n_experts: int, top_k: int, act_d
     c.flags = (MOE_F_ADD_RESIDUAL if residual else 0) | (MOE_F_NOISE_INPUT if noise_input else 0)
     c.seed, c.noise_offset = seed, noise_offset
     c.seq_len = seq_len
+    c.n_groups, c.group_top_k = n_groups, group_top_k
     return c
 
 
@@ -183,6 +186,7 @@ def weights_from(c: MoeConfig, t: Dict[str, torch.Tensor]) -> MoeWeights:
     w.w_up = _ptr(t.get("w_up"), dt, (E, F, d), "w_up")
     w.w_down = _ptr(t.get("w_down", t.get("w2")), dt, (E, d, F), "w_down")
     w.token_ids = _ptr(t.get("token_ids"), torch.int32, (c.T,), "token_ids")
+    w.w_group_router = _ptr(t.get("w_group_router"), torch.float32, (c.n_groups, d), "w_group_router")
     if c.n_shared:
         Fs = c.d_ff_shared
         w.ws_gate = _ptr(t["ws_gate"].reshape(Fs, d) if "ws_gate" in t else None, dt, (Fs, d), "ws_gate")

@@ -15,6 +15,12 @@ namespace moe {
 void launch_router_dots(bool bf16, const void* x, const float* w0, const float* w1, int T, int d, int E, int NC,
                         float* dots, hipStream_t s);
 int select_blocks(int T, int E);
+// Hierarchical gate: A groups of E / A experts, KP groups then KS experts per
+// group per token; P partials of hier_select_blocks(T) blocks.
+int hier_select_blocks(int T);
+void launch_select_hier(const float* dots, int NC, const float* logit_bias, int T, int E, int A, int KP, int KS,
+                        int32_t* topk_idx, float* topk_gate, float* scores, float* P_part, int32_t* status,
+                        hipStream_t s);
 void launch_select(const float* dots, int NC, const float* logit_bias, const float* sel_bias, const float* noise,
                    const int32_t* token_ids, int gate, int T, int E, int k, uint64_t seed, uint64_t noise_offset,
                    int32_t* topk_idx, float* topk_gate, float* scores, float* P_part, int32_t* status,

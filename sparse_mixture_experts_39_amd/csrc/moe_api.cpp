@@ -19,6 +19,18 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int elem_bytes(const moe_config* c) { return c->act_dtype == MOE_BF16 ? 2 : 4; }
 bool is_bf16(const moe_config* c) { return c->act_dtype == MOE_BF16; }
 bool expert_choice(const moe_config* c) { return c->gate == MOE_GATE_EXPERT_CHOICE; }
+bool hierarchical(const moe_config* c) { return c->gate == MOE_GATE_HIERARCHICAL; }
+// router product columns: E logits, then E noise-scale logits (noisy gate) or
+// the n_groups primary logits (hierarchical gate)
+int router_cols(const moe_config* c) {
+    return c->gate == MOE_GATE_NOISY_TOPK ? 2 * c->n_experts
+                                          : c->n_experts + (hierarchical(c) ? c->n_groups : 0);
+}
+// blocks of the selection kernel (rows of the P partials)
+int route_blocks(const moe_config* c) {
+    if (c->T <= 0) return 0;
+    return hierarchical(c) ? moe::hier_select_blocks(c->T) : moe::select_blocks(c->T, c->n_experts);
+}
 // selection slots per token: k, or E under expert choice
 int slots_of(const moe_config* c) { return expert_choice(c) ? c->n_experts : c->top_k; }
 int64_t n_assign(const moe_config* c) { return (int64_t)c->T * slots_of(c); }
@@ -88,13 +100,13 @@ Layout compute_layout(const moe_config* c) {
     size_t o = 0;
     auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
     const int E = c->n_experts, T = c->T;
-    const int NC = c->gate == MOE_GATE_NOISY_TOPK ? 2 * E : E;
+    const int NC = router_cols(c);
     const int es = elem_bytes(c);
     const int64_t R = max_rows_of(c);
     const int64_t nasg_blocks = (n_assign(c) + moe::kAssignBlock - 1) / moe::kAssignBlock;
     const size_t plan = moe::ffn_tile_plan_ints(E) * sizeof(int32_t);
     L.dots = take((size_t)T * NC * sizeof(float));
-    L.P_part = take((size_t)moe::select_blocks(T, E) * E * sizeof(float));
+    L.P_part = take((size_t)route_blocks(c) * E * sizeof(float));
     L.P_ws = take((size_t)E * sizeof(float));
     L.status = take(sizeof(int32_t));
     L.hist = take((size_t)nasg_blocks * E * sizeof(int32_t));
@@ -158,7 +170,7 @@ moe_status moe_validate_config(const moe_config* c) {
     if (c->T < 0 || c->d_model <= 0 || c->d_ff <= 0 || c->n_experts <= 0 || c->top_k <= 0) return MOE_ERR_INVALID_ARG;
     if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
     if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
-    if (c->gate < MOE_GATE_SOFTMAX_TOPK || c->gate > MOE_GATE_HASH) return MOE_ERR_INVALID_ARG;
+    if (c->gate < MOE_GATE_SOFTMAX_TOPK || c->gate > MOE_GATE_HIERARCHICAL) return MOE_ERR_INVALID_ARG;
     if (c->top_k > c->n_experts) return MOE_ERR_INVALID_ARG;
     if (c->n_shared < 0 || c->n_shared > 1) return MOE_ERR_INVALID_ARG;
     if (c->n_shared == 1 && c->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
@@ -170,6 +182,15 @@ moe_status moe_validate_config(const moe_config* c) {
     if ((int64_t)c->T * c->top_k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     if ((int64_t)c->T * slots_of(c) >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     if (c->reserved != 0 || c->seq_len < 0) return MOE_ERR_INVALID_ARG;
+    if (c->gate == MOE_GATE_HIERARCHICAL) {
+        if (c->n_groups < 1 || c->group_top_k < 1 || c->group_top_k > c->n_groups ||
+            c->n_experts % c->n_groups != 0 || c->top_k % c->group_top_k != 0 ||
+            c->top_k / c->group_top_k > c->n_experts / c->n_groups)
+            return MOE_ERR_INVALID_ARG;
+        if (c->n_groups > 64 || c->n_experts / c->n_groups > 64) return MOE_ERR_UNSUPPORTED;
+    } else if (c->n_groups != 0 || c->group_top_k != 0) {
+        return MOE_ERR_INVALID_ARG;
+    }
     if (c->seq_len > 0 && (c->seq_len % 256 != 0 || c->T % c->seq_len != 0)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -218,6 +239,7 @@ moe_status moe_route(const moe_config* c, const void* x, const moe_weights* w, i
     if (!w || (!hashed && !w->w_router)) return MOE_ERR_INVALID_ARG;
     if (c->T > 0 && ((!hashed && !x) || !topk_idx || !topk_gate)) return MOE_ERR_INVALID_ARG;
     if (hashed && c->T > 0 && !w->token_ids) return MOE_ERR_INVALID_ARG;
+    if (hierarchical(c) && !w->w_group_router) return MOE_ERR_INVALID_ARG;
     if (c->gate == MOE_GATE_NOISY_TOPK) {
         if (!w->w_noise) return MOE_ERR_INVALID_ARG;
         if ((c->flags & MOE_F_NOISE_INPUT) && !w->noise) return MOE_ERR_INVALID_ARG;
@@ -227,16 +249,25 @@ moe_status moe_route(const moe_config* c, const void* x, const moe_weights* w, i
     const Layout L = compute_layout(c);
     const int E = c->n_experts, T = c->T;
     const bool noisy = c->gate == MOE_GATE_NOISY_TOPK;
-    const int NC = noisy ? 2 * E : E;
+    const int NC = router_cols(c);
     float* dots = at<float>(ws, L.dots);
     int32_t* status = at<int32_t>(ws, L.status);
     const bool balance = st && (st->z_loss || st->importance || st->importance_cv2 || st->load || st->load_cv2 ||
                                 st->seq_aux);
-    if (hashed && balance) return MOE_ERR_UNSUPPORTED;
+    if ((hashed || hierarchical(c)) && balance) return MOE_ERR_UNSUPPORTED;
     moe::launch_zero_i32(status, 1, h);
     if (!hashed)
-        moe::launch_router_dots(is_bf16(c), x, w->w_router, noisy ? w->w_noise : nullptr, T, c->d_model, E, NC, dots,
-                                h);
+        moe::launch_router_dots(is_bf16(c), x, w->w_router,
+                                noisy ? w->w_noise : (hierarchical(c) ? w->w_group_router : nullptr), T, c->d_model,
+                                E, NC, dots, h);
+    if (hierarchical(c)) {
+        moe::launch_select_hier(dots, NC, w->logit_bias, T, E, c->n_groups, c->group_top_k,
+                                c->top_k / c->group_top_k, topk_idx, topk_gate, scores, at<float>(ws, L.P_part),
+                                status, h);
+        moe::launch_reduce_P(at<float>(ws, L.P_part), route_blocks(c), E, T, at<float>(ws, L.P_ws),
+                             st ? st->P : nullptr, status, st ? st->device_status : nullptr, h);
+        return after_launch();
+    }
     if (expert_choice(c)) {
         float* S = scores ? scores : at<float>(ws, L.ec_scores);
         moe::launch_ec_route(dots, w->logit_bias, T, E, (int)ec_capacity_of(c), S, at<float>(ws, L.P_ws),
@@ -406,6 +437,7 @@ moe_status moe_layer_forward(const moe_config* c, const moe_weights* w, const vo
     moe_status s = moe_validate_config(c);
     if (s != MOE_OK) return s;
     if (!w || (c->gate != MOE_GATE_HASH && !w->w_router)) return MOE_ERR_INVALID_ARG;
+    if (hierarchical(c) && !w->w_group_router) return MOE_ERR_INVALID_ARG;
     if (c->T > 0 && (!x || !out)) return MOE_ERR_INVALID_ARG;
     if (c->T > 0 && (!w->w_gate || !w->w_down || (c->act == MOE_ACT_SWIGLU && !w->w_up))) return MOE_ERR_INVALID_ARG;
     if (c->n_shared == 1 && c->T > 0 && (!w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_INVALID_ARG;

@@ -19,6 +19,7 @@
 //   k_balance       (when requested) z-loss, importance and load partials;
 //                   k_column_sums, k_seq_aux, k_balance_final reduce them
 //   k_update_bias   the auxiliary-loss-free bias step
+//   k_select_hier   hierarchical gate: groups, then experts inside each group
 //   k_ec_scores, k_ec_select   expert choice: router probabilities, and each
 //                   expert's top-C tokens by radix select
 #include "device_common.h"
@@ -396,6 +397,124 @@ __global__ __launch_bounds__(1024) void k_reduce_P(const float* __restrict__ P_p
 __global__ __launch_bounds__(1024) void k_column_sums(const float* __restrict__ part, int nblocks, int E, float scale,
                                                       float* __restrict__ out_ws, float* __restrict__ out_user) {
     column_sums(part, nblocks, E, scale, out_ws, out_user);
+}
+
+// Hierarchical gate (two levels): one wave per token, 4 tokens per block.
+// Lanes hold the primary logits of the n_groups groups (columns E .. E+A-1
+// of the router product); KP passes of a wave arg-max pick the groups (ties
+// to the lower index), then for each picked group its B secondary logits
+// (columns g B .. g B + B-1, plus the logit bias) give KS more passes.  Gates:
+// softmax over the picked primary logits times softmax over the picked
+// secondary logits of the group, in fp32 with the canonical exp.  Router
+// probabilities softmax(zp)_g * softmax(z of group g)_j for every expert, summed
+// per block in wave order.
+__global__ __launch_bounds__(256) void k_select_hier(const float* __restrict__ dots, int NC,
+                                                     const float* __restrict__ logit_bias, int T, int E, int A, int KP,
+                                                     int KS, int32_t* __restrict__ topk_idx,
+                                                     float* __restrict__ topk_gate, float* __restrict__ scores,
+                                                     float* __restrict__ P_part, int32_t* __restrict__ status) {
+    __shared__ float pw[4][1024];      // router probabilities per wave (token)
+    __shared__ float gstat[4][64][2];  // per group: max and sum of exp of its secondary logits
+    __shared__ float pprob[4][64];     // primary probabilities softmax(zp)
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    const int B = E / A, k = KP * KS;
+    const float ninf = -__builtin_inff();
+    int bad = 0;
+    if (t < T) {
+        const float* zr = dots + (int64_t)t * NC;
+        auto zsec = [&](int e) { return logit_bias ? zr[e] + logit_bias[e] : zr[e]; };
+        for (int e = lane; e < E; e += 64) {
+            const float z = zsec(e);
+            if (!__builtin_isfinite(z)) bad = 1;
+            if (scores) scores[(int64_t)t * E + e] = z;
+        }
+        const float zp = lane < A ? zr[E + lane] : ninf;
+        if (lane < A && !__builtin_isfinite(zp)) bad = 1;
+        // primary softmax over all groups (probabilities)
+        const float mp = seg_max_f<64>(zp);
+        const float sp = seg_sum_f<64>(lane < A ? canon::expc(zp - mp) : 0.0f);
+        if (lane < A) pprob[wave][lane] = canon::expc(zp - mp) / sp;
+        // per-group softmax statistics of the secondary logits
+        for (int g = 0; g < A; ++g) {
+            const float z = lane < B ? zsec(g * B + lane) : ninf;
+            const float m = seg_max_f<64>(z);
+            const float sm = seg_sum_f<64>(lane < B ? canon::expc(z - m) : 0.0f);
+            if (lane == 0) { gstat[wave][g][0] = m; gstat[wave][g][1] = sm; }
+        }
+        // pick the groups
+        bool taken = false;
+        int grp[16];
+        float zps[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            grp[j] = 0; zps[j] = 0.0f;
+            if (j >= KP) continue;
+            const uint64_t best = seg_max_u64<64>((lane < A && !taken) ? pack_cand(zp, lane) : 0ull);
+            const int g = (int)(0xffffffffu - (uint32_t)best);
+            grp[j] = g;
+            zps[j] = __shfl(zp, g, 64);
+            if (lane == g) taken = true;
+        }
+        float gp[16], sgp = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            gp[j] = canon::expc(zps[j] - zps[0]);
+            if (j < KP) sgp = sgp + gp[j];
+        }
+        // pick the experts inside each picked group
+        for (int j = 0; j < KP; ++j) {
+            const int g = grp[j];
+            const float z = lane < B ? zsec(g * B + lane) : ninf;
+            bool tk = false;
+            int ex[16];
+            float zs[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                ex[q] = 0; zs[q] = 0.0f;
+                if (q >= KS) continue;
+                const uint64_t best = seg_max_u64<64>((lane < B && !tk) ? pack_cand(z, lane) : 0ull);
+                const int jj = (int)(0xffffffffu - (uint32_t)best);
+                ex[q] = g * B + jj;
+                zs[q] = __shfl(z, jj, 64);
+                if (lane == jj) tk = true;
+            }
+            float gs[16], sgs = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                gs[q] = canon::expc(zs[q] - zs[0]);
+                if (q < KS) sgs = sgs + gs[q];
+            }
+            if (lane == 0) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    if (q < KS) {
+                        topk_idx[(int64_t)t * k + j * KS + q] = ex[q];
+                        topk_gate[(int64_t)t * k + j * KS + q] = (gp[j] / sgp) * (gs[q] / sgs);
+                    }
+            }
+        }
+        for (int e = lane; e < E; e += 64) {
+            const int g = e / B;
+            pw[wave][e] = pprob[wave][g] * (canon::expc(zsec(e) - gstat[wave][g][0]) / gstat[wave][g][1]);
+        }
+    } else {
+        for (int e = lane; e < E; e += 64) pw[wave][e] = 0.0f;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256)
+        P_part[(int64_t)blockIdx.x * E + e] = ((pw[0][e] + pw[1][e]) + pw[2][e]) + pw[3][e];
+    if (bad) status[0] = MOE_DEV_NONFINITE;   // benign race: every writer stores the same value
+}
+
+int hier_select_blocks(int T) { return (T + 3) / 4; }
+
+void launch_select_hier(const float* dots, int NC, const float* logit_bias, int T, int E, int A, int KP, int KS,
+                        int32_t* topk_idx, float* topk_gate, float* scores, float* P_part, int32_t* status,
+                        hipStream_t s) {
+    if (T <= 0) return;
+    hipLaunchKernelGGL(k_select_hier, dim3(hier_select_blocks(T)), dim3(256), 0, s, dots, NC, logit_bias, T, E, A, KP,
+                       KS, topk_idx, topk_gate, scores, P_part, status);
 }
 
 // ---------------------------------------------------------------------------

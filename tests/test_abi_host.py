@@ -79,7 +79,7 @@ def test_capacity_and_rows_match_the_oracle(name):
     cfg = workloads.get(name)
     c = moe.config(T=cfg.T, d_model=cfg.d, d_ff=cfg.F, n_experts=cfg.E, top_k=cfg.k, act_dtype=cfg.act_dtype,
                    act=cfg.act, gate=cfg.gate, capacity_factor=cfg.capacity_factor, n_shared=cfg.n_shared,
-                   d_ff_shared=cfg.F_shared)
+                   d_ff_shared=cfg.F_shared, n_groups=cfg.n_groups, group_top_k=cfg.group_top_k)
     assert moe.validate_config(c) == OK
     C = oracle.capacity(cfg)
     assert moe.capacity(c) == C

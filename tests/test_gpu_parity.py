@@ -59,6 +59,14 @@ MID = {
                                 gate="hash", capacity_factor=1.25, residual=True, seed=29),
     "hash_k_equals_E": Config("hash_k_equals_E", T=130, d=128, F=128, E=4, k=4, act_dtype="bf16", act="swiglu",
                               gate="hash", seed=30),
+    # two-level gate: groups first, then experts inside each picked group
+    "hier_bf16_relu": Config("hier_bf16_relu", T=1000, d=256, F=256, E=64, k=4, act_dtype="bf16", act="relu",
+                             gate="hierarchical", n_groups=8, group_top_k=2, seed=31),
+    "hier_f32_swiglu_bias": Config("hier_f32_swiglu_bias", T=333, d=128, F=192, E=24, k=3, act_dtype="f32",
+                                   act="swiglu", gate="hierarchical", n_groups=3, group_top_k=3,
+                                   logit_bias="zipf", capacity_factor=1.5, residual=True, seed=32),
+    "hier_wide": Config("hier_wide", T=300, d=64, F=64, E=1024, k=16, act_dtype="bf16", act="relu",
+                        gate="hierarchical", n_groups=32, group_top_k=4, seed=33),
 }
 
 
@@ -221,7 +229,8 @@ def _sampled_full_size(name, n_tokens=12, rows_per_expert=2, max_experts=24, noi
                      sel_bias=dinp["sel_bias"].cpu() if "sel_bias" in dinp else None,
                      w_noise=dinp["w_noise"].cpu() if "w_noise" in dinp else None,
                      noise=dinp["noise"].cpu() if (noise_input and "noise" in dinp) else None,
-                     token_ids=dinp["token_ids"].cpu() if "token_ids" in dinp else None)
+                     token_ids=dinp["token_ids"].cpu() if "token_ids" in dinp else None,
+                     w_group_router=dinp["w_group_router"].cpu() if "w_group_router" in dinp else None)
     o.update(oracle.dispatch(cfg, o["idx"]))
     o.update(oracle.stats(cfg, o["counts"], o["kept"], o["P"], cfg.T))
     o["status"] = 0
@@ -288,6 +297,10 @@ def test_full_size_mixtral_expert_choice_sampled():
 
 def test_full_size_mixtral_hash_sampled():
     _sampled_full_size("mixtral_hash", max_experts=8, rows_per_expert=3)
+
+
+def test_full_size_hierarchical_sampled():
+    _sampled_full_size("hier", n_tokens=24, max_experts=32, rows_per_expert=2)
 
 
 def test_full_size_noisy_philox_routing():

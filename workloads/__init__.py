@@ -1,6 +1,6 @@
 """Seeded synthetic workloads for the sparse token-choice MoE FFN layer.
 
-This module holds the seven layer shapes and a deterministic input generator.
+This module holds the eight layer shapes and a deterministic input generator.
 It contains none of the layer's arithmetic: it only draws tensors.  Both the
 HIP path and the CPU oracle take their inputs from here, and nothing here
 imports either of them.
@@ -29,6 +29,11 @@ Shapes and distributions follow the layer configurations studied on the pages:
 * ``mixtral_hash`` the Mixtral-shaped layer routed by a hash of Zipf(1.1)
                token ids, top-2 with the outputs summed (CS336 lecture 4
                notes, section 4, hash routing).
+* ``hier``     the Shazeer-shaped layer (256 ReLU experts 512->1024->512,
+               bf16) under a two-level gate: 16 groups of 16 experts, 2
+               groups then 2 experts each, k = 4 ("Outrageously Large Neural
+               Networks" reading notes, appendix B hierarchical MoE and the
+               2 x 2 remark).
 
 Distributions: x ~ N(0,1); every weight ~ N(0, 1/fan_in); the DeepSeek-style
 selection bias ~ N(0, 0.1) read as a variance; the Switch logit bias is
@@ -62,7 +67,8 @@ class Config:
     k: int                      # top-k
     act_dtype: str              # "f32" | "bf16": activations and expert weights
     act: str                    # "relu" | "swiglu"
-    gate: str                   # "softmax_topk" | "softmax_full" | "noisy_topk" | "sigmoid_bias" | "expert_choice" | "hash"
+    gate: str                   # "softmax_topk" | "softmax_full" | "noisy_topk" | "sigmoid_bias" | "expert_choice"
+                                #  | "hash" | "hierarchical"
     capacity_factor: float = 0.0  # <= 0: dropless
     residual: bool = False
     n_shared: int = 0
@@ -70,6 +76,8 @@ class Config:
     logit_bias: str = "none"    # "none" | "zipf"
     sel_bias: bool = False
     seed: int = 0
+    n_groups: int = 0           # hierarchical gate: groups of E / n_groups experts
+    group_top_k: int = 0        # hierarchical gate: groups picked per token
 
     def replace(self, **kw) -> "Config":
         return dataclasses.replace(self, **kw)
@@ -96,6 +104,8 @@ CONFIGS: Dict[str, Config] = {
                          act="swiglu", gate="expert_choice", capacity_factor=1.0, seed=1006),
     "mixtral_hash": Config("mixtral_hash", T=4096, d=4096, F=14336, E=8, k=2, act_dtype="bf16",
                            act="swiglu", gate="hash", seed=1007),
+    "hier": Config("hier", T=8192, d=512, F=1024, E=256, k=4, act_dtype="bf16", act="relu",
+                   gate="hierarchical", n_groups=16, group_top_k=2, seed=1008),
 }
 
 
@@ -136,7 +146,8 @@ def make_inputs(cfg: Config, device="cpu", with_noise: Optional[bool] = None) ->
     (``w_gate``/``w_up`` [E][F][d] and ``w_down`` [E][d][F] for SwiGLU,
     ``w1`` [E][F][d] and ``w2`` [E][d][F] for ReLU) and the shared expert
     (``ws_gate``/``ws_up`` [S][Fs][d], ``ws_down`` [S][d][Fs]); for the hash
-    gate ``token_ids`` [T] int32.
+    gate ``token_ids`` [T] int32, for the hierarchical gate ``w_group_router``
+    [n_groups][d] fp32.
     Weight layouts are [out][in] (the reduction dimension is contiguous).
     """
     device = torch.device(device)
@@ -170,6 +181,8 @@ def make_inputs(cfg: Config, device="cpu", with_noise: Optional[bool] = None) ->
         with_noise = cfg.gate == "noisy_topk"
     if with_noise:
         inp["noise"] = _normal((T, E), 1.0, gen, device, torch.float32)
+    if cfg.gate == "hierarchical":
+        inp["w_group_router"] = _normal((cfg.n_groups, d), 1.0 / math.sqrt(d), gen, device, torch.float32)
     if cfg.gate == "hash":
         # token ids with a Zipf(1.1) law over a 32000-id vocabulary, so that
         # frequent ids repeat (CS336 notes section 4: under a Zipf law a word
