@@ -155,7 +155,7 @@ def main():
     c = moe.config(T=cfg.T, d_model=cfg.d, d_ff=cfg.F, n_experts=cfg.E, top_k=cfg.k, act_dtype=cfg.act_dtype,
                    act=cfg.act, gate=cfg.gate, capacity_factor=cfg.capacity_factor, residual=cfg.residual,
                    n_shared=cfg.n_shared, d_ff_shared=cfg.F_shared, seed=cfg.seed, n_groups=cfg.n_groups,
-                   group_top_k=cfg.group_top_k)
+                   group_top_k=cfg.group_top_k, reroute=cfg.reroute)
     w = moe.weights_from(c, dinp)
     ws = moe.workspace(c)
     st = moe.alloc_stats(c, balance=args.balance_stats)

@@ -117,8 +117,18 @@ typedef enum { MOE_ACT_RELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
 
 enum {
     MOE_F_ADD_RESIDUAL = 1u, /* out += x (CS336 notes section 5 listing: h = sum g FFN(u) + u) */
-    MOE_F_NOISE_INPUT = 2u   /* NOISY_TOPK: read n from the caller's noise tensor
+    MOE_F_NOISE_INPUT = 2u,  /* NOISY_TOPK: read n from the caller's noise tensor
                                 instead of the built-in Philox4x32-10 stream */
+    /* Capacity reroute instead of drop (Lecture29, "Inference load balance":
+     * an expert over capacity may drop, reroute or delay the extra tokens).
+     * moe_route rewrites topk_idx: the assignments are taken in (t, j) order,
+     * the first C of an expert stay, and every later one, in that order,
+     * moves to its token's best other expert (largest selection key, ties to
+     * the lower index) that the token does not hold yet and that still has
+     * room; with none it stays and moe_dispatch drops it.  The slot keeps its
+     * gate.  Needs a capacity factor > 0; not for EXPERT_CHOICE (no overflow)
+     * nor HIERARCHICAL (a move would leave the picked groups). */
+    MOE_F_REROUTE = 4u
 };
 
 enum { MOE_DEV_NONFINITE = 1 }; /* device_status bit: a selection score was NaN or infinite */

@@ -77,6 +77,8 @@ def lib():
         L.oc_route.argtypes = [ctypes.POINTER(_Cfg)] + [P] * 16
         L.oc_capacity.restype = ctypes.c_int64
         L.oc_capacity.argtypes = [ctypes.POINTER(_Cfg)]
+        L.oc_reroute.restype = ctypes.c_int64
+        L.oc_reroute.argtypes = [ctypes.POINTER(_Cfg), P, P]
         L.oc_dispatch.restype = ctypes.c_int64
         L.oc_dispatch.argtypes = [ctypes.POINTER(_Cfg)] + [P] * 6
         L.oc_gather_rows.argtypes = [ctypes.POINTER(_Cfg), P, P, ctypes.c_int64, P]
@@ -264,6 +266,17 @@ def _slot_cfg(cfg):
     return cfg
 
 
+def reroute(cfg, keys, idx) -> np.ndarray:
+    """Capacity reroute of the route's selection (a new idx array): the
+    assignments past an expert's capacity move, in (t, j) order, to their
+    token's best other expert with room."""
+    idx = np.array(_np(idx, np.int32), dtype=np.int32, copy=True)
+    keys = _np(keys, np.float32)
+    c = make_cfg(cfg, T=idx.shape[0])
+    lib().oc_reroute(ctypes.byref(c), _ptr(keys), _ptr(idx))
+    return idx
+
+
 def dispatch(cfg, idx, T: Optional[int] = None) -> Dict[str, np.ndarray]:
     idx = _np(idx, np.int32)
     T = idx.shape[0] if T is None else T
@@ -393,6 +406,8 @@ def forward(cfg, inputs, *, round_intermediates: bool = True, noise: str = "inpu
               sel_bias=inputs.get("sel_bias"), w_noise=inputs.get("w_noise"), noise=nz,
               noise_offset=noise_offset, want_probs=True, token_ids=inputs.get("token_ids"),
               w_group_router=inputs.get("w_group_router"))
+    if getattr(cfg, "reroute", False):
+        r["idx"] = reroute(cfg, r["keys"], r["idx"])
     dp = dispatch(cfg, r["idx"], T=T)
     x_perm = gather_rows(cfg, x, dp["perm_src"])
     R = dp["R"]

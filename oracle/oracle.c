@@ -551,6 +551,53 @@ OC_EXPORT int64_t oc_capacity(const oc_config* cfg) {
 }
 
 /*
+ * Capacity reroute (Lecture29, "Inference load balance": an expert that
+ * receives more than C tokens may drop, reroute or delay the extra ones).
+ * Reading: the assignments are taken in (t, j) order; the first C of an
+ * expert stay; every later one, in that same order, moves to the best other
+ * expert of its token (largest selection key, ties to the lower index) that
+ * is not already among the token's current experts and still has room; with
+ * none it stays and dispatch drops it.  The slot keeps its gate.  idx [T][k]
+ * is rewritten in place; keys [T][E] are the selection keys of the route.
+ * Returns the number of moved assignments (0 when dropless).
+ */
+OC_EXPORT int64_t oc_reroute(const oc_config* cfg, const float* keys, int32_t* idx) {
+    const int T = cfg->T, E = cfg->E, k = cfg->k;
+    const int64_t C = oc_capacity(cfg);
+    if (C < 0 || T <= 0) return 0;
+    int64_t* n = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    unsigned char* over = (unsigned char*)calloc((size_t)T * k, 1);
+    for (int64_t a = 0; a < (int64_t)T * k; ++a) {
+        const int e = idx[a];
+        if (e < 0 || e >= E) continue;
+        if (n[e] < C) n[e] += 1;
+        else over[a] = 1;
+    }
+    int64_t moved = 0;
+    for (int64_t a = 0; a < (int64_t)T * k; ++a) {
+        if (!over[a]) continue;
+        const int64_t t = a / k;
+        const int32_t* cur = idx + t * k;
+        int best = -1;
+        for (int e = 0; e < E; ++e) {
+            if (n[e] >= C) continue;
+            int mine = 0;
+            for (int j = 0; j < k; ++j) if (cur[j] == e) mine = 1;
+            if (mine) continue;
+            if (best < 0 || order_key(keys[t * E + e]) > order_key(keys[t * E + best])) best = e;
+        }
+        if (best >= 0) {
+            idx[a] = best;
+            n[best] += 1;
+            moved += 1;
+        }
+    }
+    free(n);
+    free(over);
+    return moved;
+}
+
+/*
  * Counting sort of the T*k assignments (t, j) by expert, stable in (t, j)
  * order (Lecture29, "Top-k routing semantics": tokens are re-arranged by
  * expert, run in batches, and inverse-permuted).  Assignment a = t*k + j.

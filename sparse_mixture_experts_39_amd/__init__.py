@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 MOE_F32, MOE_BF16 = 0, 1
 ACTS = {"relu": 0, "swiglu": 1}
 GATES = {"softmax_topk": 0, "softmax_full": 1, "noisy_topk": 2, "sigmoid_bias": 3, "expert_choice": 4, "hash": 5, "hierarchical": 6}
-MOE_F_ADD_RESIDUAL, MOE_F_NOISE_INPUT = 1, 2
+MOE_F_ADD_RESIDUAL, MOE_F_NOISE_INPUT, MOE_F_REROUTE = 1, 2, 4
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace missing or too small",
           4: "HIP launch failed"}
 
@@ -127,7 +127,7 @@ def config(*, T: int, d_model: int, d_ff: int, n_experts: int, top_k: int, act_d
            act: str = "swiglu", gate: str = "softmax_topk", capacity_factor: float = 0.0,
            residual: bool = False, n_shared: int = 0, d_ff_shared: int = 0, noise_input: bool = False,
            seed: int = 0, noise_offset: int = 0, seq_len: int = 0, n_groups: int = 0,
-           group_top_k: int = 0) -> MoeConfig:
+           group_top_k: int = 0, reroute: bool = False) -> MoeConfig:
     c = MoeConfig()
     c.T, c.d_model, c.d_ff, c.n_experts, c.top_k = T, d_model, d_ff, n_experts, top_k
     c.n_shared, c.d_ff_shared = n_shared, d_ff_shared
@@ -135,7 +135,8 @@ def config(*, T: int, d_model: int, d_ff: int, n_experts: int, top_k: int, act_d
     c.act = ACTS[act]
     c.gate = GATES[gate]
     c.capacity_factor = capacity_factor
-    c.flags = (MOE_F_ADD_RESIDUAL if residual else 0) | (MOE_F_NOISE_INPUT if noise_input else 0)
+    c.flags = ((MOE_F_ADD_RESIDUAL if residual else 0) | (MOE_F_NOISE_INPUT if noise_input else 0) |
+               (MOE_F_REROUTE if reroute else 0))
     c.seed, c.noise_offset = seed, noise_offset
     c.seq_len = seq_len
     c.n_groups, c.group_top_k = n_groups, group_top_k

@@ -18,6 +18,11 @@ int select_blocks(int T, int E);
 // Hierarchical gate: A groups of E / A experts, KP groups then KS experts per
 // group per token; P partials of hier_select_blocks(T) blocks.
 int hier_select_blocks(int T);
+// Capacity reroute: assignments with slot_pos < 0 move, in order, to their
+// token's best other expert with room (offsets: the capacity cut's kept
+// prefix).  Rewrites idx in place.
+void launch_reroute(int32_t* idx, const float* keys, const int32_t* slot_pos, const int32_t* offsets, int T, int E,
+                    int k, int64_t C, hipStream_t s);
 void launch_select_hier(const float* dots, int NC, const float* logit_bias, int T, int E, int A, int KP, int KS,
                         int32_t* topk_idx, float* topk_gate, float* scores, float* P_part, int32_t* status,
                         hipStream_t s);

@@ -70,6 +70,7 @@ struct Layout {
     size_t partial;                                       // split-K accumulators
     size_t imp_part, load_part, cnt_part, z_part, imp_ws, load_ws, cnt_ws, z_ws, seq_part;   // balance statistics
     size_t ec_scores;                                     // expert choice: S [T][E]
+    size_t keys;                                          // capacity reroute: selection keys [T][E]
     size_t total;
 };
 
@@ -140,6 +141,7 @@ Layout compute_layout(const moe_config* c) {
     L.z_ws = take(sizeof(float));
     L.seq_part = take((size_t)(T / 256 + 1) * sizeof(float));
     L.ec_scores = take(expert_choice(c) ? (size_t)T * E * sizeof(float) : 0);
+    L.keys = take((c->flags & MOE_F_REROUTE) ? (size_t)T * E * sizeof(float) : 0);
     L.total = o;
     return L;
 }
@@ -175,7 +177,11 @@ moe_status moe_validate_config(const moe_config* c) {
     if (c->n_shared < 0 || c->n_shared > 1) return MOE_ERR_INVALID_ARG;
     if (c->n_shared == 1 && c->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
     if (c->capacity_factor != c->capacity_factor) return MOE_ERR_INVALID_ARG;
-    if (c->flags & ~(uint32_t)(MOE_F_ADD_RESIDUAL | MOE_F_NOISE_INPUT)) return MOE_ERR_INVALID_ARG;
+    if (c->flags & ~(uint32_t)(MOE_F_ADD_RESIDUAL | MOE_F_NOISE_INPUT | MOE_F_REROUTE)) return MOE_ERR_INVALID_ARG;
+    if (c->flags & MOE_F_REROUTE) {
+        if (!(c->capacity_factor > 0.0f) || c->gate == MOE_GATE_EXPERT_CHOICE) return MOE_ERR_INVALID_ARG;
+        if (c->gate == MOE_GATE_HIERARCHICAL) return MOE_ERR_UNSUPPORTED;
+    }
     if (c->top_k > 16 || c->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
     if (c->d_model % 64 || c->d_ff % 64) return MOE_ERR_UNSUPPORTED;
     if (c->n_shared == 1 && (c->d_ff_shared % 64 || c->act != MOE_ACT_SWIGLU)) return MOE_ERR_UNSUPPORTED;
@@ -281,10 +287,26 @@ moe_status moe_route(const moe_config* c, const void* x, const moe_weights* w, i
         return after_launch();
     }
     const float* noise = (noisy && (c->flags & MOE_F_NOISE_INPUT)) ? w->noise : nullptr;
+    const bool reroute = (c->flags & MOE_F_REROUTE) != 0;
+    float* keys = scores ? scores : (reroute ? at<float>(ws, L.keys) : nullptr);
     moe::launch_select(dots, NC, w->logit_bias, c->gate == MOE_GATE_SIGMOID_BIAS ? w->sel_bias : nullptr, noise,
                        hashed ? w->token_ids : nullptr, c->gate, T, E, c->top_k, c->seed, c->noise_offset, topk_idx,
-                       topk_gate, scores,
+                       topk_gate, keys,
                        at<float>(ws, L.P_part), status, h);
+    if (reroute && T > 0) {
+        // the capacity cut of dispatch, on scratch buffers, then the moves
+        const int64_t na = n_assign(c);
+        const int nb = (int)((na + moe::kAssignBlock - 1) / moe::kAssignBlock);
+        int32_t* hist = at<int32_t>(ws, L.hist);
+        int32_t* bbase = at<int32_t>(ws, L.blockbase);
+        int32_t* offs = at<int32_t>(ws, L.offsets);
+        const int64_t cap = capacity_of(c);
+        moe::launch_histogram(topk_idx, na, E, hist, h);
+        moe::launch_scan(hist, nb, E, cap, bbase, offs, nullptr, nullptr, h);
+        moe::launch_scatter(topk_idx, na, E, bbase, offs, cap, at<int32_t>(ws, L.perm_src),
+                            at<int32_t>(ws, L.slot_pos), h);
+        moe::launch_reroute(topk_idx, keys, at<int32_t>(ws, L.slot_pos), offs, T, E, c->top_k, cap, h);
+    }
     moe::launch_reduce_P(at<float>(ws, L.P_part), T > 0 ? moe::select_blocks(T, E) : 0, E, T, at<float>(ws, L.P_ws),
                          st ? st->P : nullptr, status, st ? st->device_status : nullptr, h);
     if (balance)

@@ -20,6 +20,7 @@
 //                   k_column_sums, k_seq_aux, k_balance_final reduce them
 //   k_update_bias   the auxiliary-loss-free bias step
 //   k_select_hier   hierarchical gate: groups, then experts inside each group
+//   k_reroute       capacity reroute of the overflowing assignments (one block)
 //   k_ec_scores, k_ec_select   expert choice: router probabilities, and each
 //                   expert's top-C tokens by radix select
 #include "device_common.h"
@@ -515,6 +516,173 @@ void launch_select_hier(const float* dots, int NC, const float* logit_bias, int 
     if (T <= 0) return;
     hipLaunchKernelGGL(k_select_hier, dim3(hier_select_blocks(T)), dim3(256), 0, s, dots, NC, logit_bias, T, E, A, KP,
                        KS, topk_idx, topk_gate, scores, P_part, status);
+}
+
+// Capacity reroute, one block.  The assignments past their expert's
+// capacity (slot_pos < 0 after the capacity cut) are compacted chunk by
+// chunk in (t, j) order.  All 16 waves then rank, for each of them, the
+// experts its token does not hold: all of them when E <= 64 (lane e counts
+// the keys above its own, read back from LDS), else the 16 best (wave
+// arg-max passes), and copy
+// the token's experts into LDS.  Wave 0 finally takes the entries one at a
+// time in order: lane q tests ranked expert q, and the first one that still
+// has room and is not held by then wins; when a truncated list is exhausted
+// a scan of all the token's experts decides.  Only moves of the same token
+// change what it holds, and its slots are consecutive, so the held set is
+// carried in registers from one slot to the next (also across chunks); the
+// next entry's lists are read ahead; moves are device-scope stores, waited
+// for at the end of each chunk.
+constexpr int kRerouteCand = 64;
+constexpr int kRerouteChunk = 256;
+constexpr int kRerouteWaves = 8;
+
+__global__ __launch_bounds__(kRerouteWaves * 64) void k_reroute(int32_t* __restrict__ idx, const float* __restrict__ keys,
+                                                  const int32_t* __restrict__ slot_pos,
+                                                  const int32_t* __restrict__ offsets, int T, int E, int k,
+                                                  int32_t C) {
+    __shared__ int32_t room[1024];
+    __shared__ int32_t list[kRerouteChunk];
+    __shared__ int32_t cand[kRerouteChunk][kRerouteCand];
+    __shared__ int32_t hold[kRerouteChunk][16];
+    __shared__ int32_t trunc_[kRerouteChunk];
+    __shared__ int32_t tokl[kRerouteChunk];      // token of each entry
+    __shared__ int32_t wcount[kRerouteWaves];
+    __shared__ uint64_t rk[kRerouteWaves][64];   // per wave: the 64 packed keys being ranked
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int e = tid; e < E; e += kRerouteWaves * 64) room[e] = C - (offsets[e + 1] - offsets[e]);
+    __syncthreads();
+    auto held = [&](const int32_t (&cur)[16], int e) {
+        bool h = false;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) h = h || cur[j] == e;
+        return h;
+    };
+    int64_t t_prev = -1;
+    int32_t cur[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) cur[j] = -1;
+    const int64_t na = (int64_t)T * k;
+    for (int64_t a0 = 0; a0 < na; a0 += kRerouteChunk) {
+        // 1. ordered list of the chunk's overflowing assignments
+        const int64_t a = a0 + tid;
+        bool ov = false;
+        if (tid < kRerouteChunk && a < na) {
+            const int32_t e = idx[a];
+            ov = slot_pos[a] < 0 && e >= 0 && e < E;
+        }
+        const uint64_t m = __ballot(ov);
+        if (lane == 0) wcount[w] = __popcll(m);
+        __syncthreads();
+        int base = 0, tot = 0;
+        for (int q = 0; q < kRerouteWaves; ++q) {
+            if (q < w) base += wcount[q];
+            tot += wcount[q];
+        }
+        if (ov) list[base + __popcll(m & ((1ull << lane) - 1ull))] = tid;
+        __syncthreads();
+        // 2. per entry: the token's experts, and the experts it does not hold, ranked
+        for (int i = w; i < tot; i += kRerouteWaves) {
+            const int t = (int)(a0 + list[i]) / k;     // T k < 2^31
+            if (lane == 0) tokl[i] = t;
+            int32_t ids[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                ids[j] = j < k ? __hip_atomic_load(&idx[(int64_t)t * k + j], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                               : -1;
+            if (lane < 16) hold[i][lane] = ids[lane < 16 ? lane : 0];
+            if (E <= 64) {
+                const uint64_t mine = (lane < E && !held(ids, lane)) ? pack_cand(keys[(int64_t)t * E + lane], lane) : 0ull;
+                rk[w][lane] = mine;
+                int rank = 0;
+#pragma unroll 16
+                for (int j = 0; j < 64; ++j) rank += rk[w][j] > mine ? 1 : 0;   // broadcast LDS reads
+                const int n_elig = __popcll(__ballot(mine != 0ull));
+                if (lane >= n_elig) cand[i][lane] = -1;
+                if (mine) cand[i][rank] = lane;
+                if (lane == 0) trunc_[i] = 0;
+            } else {
+                uint64_t kc[16];    // (key, index) of experts lane + 64 v, 0 when held or absent
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int e = lane + 64 * v;
+                    kc[v] = (e < E && !held(ids, e)) ? pack_cand(keys[(int64_t)t * E + e], e) : 0ull;
+                }
+                int last = -1;
+                for (int q = 0; q < 16; ++q) {
+                    uint64_t best = 0;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) best = kc[v] > best ? kc[v] : best;
+                    best = seg_max_u64<64>(best);
+                    const int e = best ? (int)(0xffffffffu - (uint32_t)best) : -1;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (e >= 0 && e == lane + 64 * v) kc[v] = 0ull;
+                    if (lane == 0) cand[i][q] = e;
+                    last = e;
+                }
+                if (lane >= 16) cand[i][lane] = -1;
+                if (lane == 0) trunc_[i] = last >= 0 ? 1 : 0;   // more experts may lie beyond the 16
+            }
+        }
+        __syncthreads();
+        // 3. the moves, in order
+        if (w == 0 && tot > 0) {
+            int32_t n_list = list[0], n_cand = cand[0][lane], n_trunc = trunc_[0], n_tok = tokl[0];
+            for (int i = 0; i < tot; ++i) {
+                const int64_t a1 = a0 + n_list;
+                const int t = n_tok;
+                const int32_t e_l = n_cand, tr = n_trunc;
+                if (t != t_prev) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) cur[j] = hold[i][j];
+                    t_prev = t;
+                }
+                if (i + 1 < tot) {          // read the next entry ahead
+                    n_list = list[i + 1];
+                    n_cand = cand[i + 1][lane];
+                    n_trunc = trunc_[i + 1];
+                    n_tok = tokl[i + 1];
+                }
+                const bool ok = e_l >= 0 && room[e_l] > 0 && !held(cur, e_l);
+                const uint64_t okm = __ballot(ok);
+                int chosen = -1;
+                if (okm) {
+                    chosen = __shfl(e_l, __ffsll((unsigned long long)okm) - 1, 64);
+                } else if (tr) {
+                    // every ranked expert is taken: scan all of them
+                    uint64_t best = 0;
+                    for (int e = lane; e < E; e += 64) {
+                        if (room[e] <= 0 || held(cur, e)) continue;
+                        const uint64_t c = pack_cand(keys[(int64_t)t * E + e], e);
+                        best = c > best ? c : best;
+                    }
+                    best = seg_max_u64<64>(best);
+                    if (best) chosen = (int)(0xffffffffu - (uint32_t)best);
+                }
+                if (chosen >= 0) {
+                    if (lane == 0) {
+                        __hip_atomic_store(&idx[a1], chosen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        room[chosen] -= 1;
+                    }
+                    const int js = (int)(a1 - (int64_t)t * k);
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        if (j == js) cur[j] = chosen;
+                }
+            }
+            // the moves are visible before the next chunk reads token ids
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        __syncthreads();
+    }
+}
+
+void launch_reroute(int32_t* idx, const float* keys, const int32_t* slot_pos, const int32_t* offsets, int T, int E,
+                    int k, int64_t C, hipStream_t s) {
+    if (T <= 0 || C < 0) return;
+    hipLaunchKernelGGL(k_reroute, dim3(1), dim3(kRerouteWaves * 64), 0, s, idx, keys, slot_pos, offsets, T, E, k,
+                       (int32_t)C);
 }
 
 // ---------------------------------------------------------------------------

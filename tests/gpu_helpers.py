@@ -38,7 +38,8 @@ def bind_config(cfg, *, T=None, noise_input=True, noise_offset=0):
                       act_dtype=cfg.act_dtype, act=cfg.act, gate=cfg.gate, capacity_factor=cfg.capacity_factor,
                       residual=cfg.residual, n_shared=cfg.n_shared, d_ff_shared=cfg.F_shared,
                       noise_input=noise_input and cfg.gate == "noisy_topk", seed=cfg.seed,
-                      noise_offset=noise_offset, n_groups=cfg.n_groups, group_top_k=cfg.group_top_k)
+                      noise_offset=noise_offset, n_groups=cfg.n_groups, group_top_k=cfg.group_top_k,
+                      reroute=cfg.reroute)
 
 
 def to_device(inp: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:

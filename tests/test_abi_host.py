@@ -189,3 +189,15 @@ def test_hash_gate_checks_token_ids_and_refuses_balance_statistics():
     assert L.moe_route(ctypes.byref(c), fake, ctypes.byref(w), fake, fake, None, ctypes.byref(st), fake, big,
                        None) == UNSUPPORTED
     assert moe.route_slots(c) == c.top_k
+
+
+def test_reroute_flag_validation():
+    base = dict(T=64, d_model=128, d_ff=128, n_experts=8, top_k=2)
+    assert moe.validate_config(moe.config(**base, capacity_factor=1.0, reroute=True)) == OK
+    assert moe.validate_config(moe.config(**base, reroute=True)) == INVALID                 # dropless
+    assert moe.validate_config(moe.config(**base, capacity_factor=1.0, gate="expert_choice",
+                                          reroute=True)) == INVALID
+    assert moe.validate_config(moe.config(**base, capacity_factor=1.0, gate="hierarchical", n_groups=2,
+                                          group_top_k=1, reroute=True)) == UNSUPPORTED
+    assert moe.workspace_size(moe.config(**base, capacity_factor=1.0, reroute=True)) > \
+        moe.workspace_size(moe.config(**base, capacity_factor=1.0))

@@ -67,6 +67,19 @@ MID = {
                                    logit_bias="zipf", capacity_factor=1.5, residual=True, seed=32),
     "hier_wide": Config("hier_wide", T=300, d=64, F=64, E=1024, k=16, act_dtype="bf16", act="relu",
                         gate="hierarchical", n_groups=32, group_top_k=4, seed=33),
+    # capacity reroute: overflowing assignments move to the token's next expert with room
+    "reroute_top2_zipf": Config("reroute_top2_zipf", T=1000, d=256, F=256, E=8, k=2, act_dtype="bf16",
+                                act="swiglu", gate="softmax_topk", capacity_factor=1.0, logit_bias="zipf",
+                                residual=True, reroute=True, seed=34),
+    "reroute_sigmoid_k4": Config("reroute_sigmoid_k4", T=700, d=128, F=128, E=32, k=4, act_dtype="bf16",
+                                 act="swiglu", gate="sigmoid_bias", sel_bias=True, capacity_factor=1.0,
+                                 residual=True, reroute=True, seed=35),
+    "reroute_hash_f32": Config("reroute_hash_f32", T=512, d=64, F=128, E=16, k=3, act_dtype="f32", act="relu",
+                               gate="hash", capacity_factor=0.9, residual=True, reroute=True, seed=36),
+    # more than 64 experts: ranked lists of 16, then the full scan once they are used up
+    "reroute_many_experts": Config("reroute_many_experts", T=900, d=64, F=64, E=200, k=2, act_dtype="bf16",
+                                   act="relu", gate="softmax_full", capacity_factor=1.0, logit_bias="zipf",
+                                   residual=True, reroute=True, seed=37),
 }
 
 
@@ -231,6 +244,8 @@ def _sampled_full_size(name, n_tokens=12, rows_per_expert=2, max_experts=24, noi
                      noise=dinp["noise"].cpu() if (noise_input and "noise" in dinp) else None,
                      token_ids=dinp["token_ids"].cpu() if "token_ids" in dinp else None,
                      w_group_router=dinp["w_group_router"].cpu() if "w_group_router" in dinp else None)
+    if cfg.reroute:
+        o["idx"] = oracle.reroute(cfg, o["keys"], o["idx"])
     o.update(oracle.dispatch(cfg, o["idx"]))
     o.update(oracle.stats(cfg, o["counts"], o["kept"], o["P"], cfg.T))
     o["status"] = 0
@@ -238,7 +253,7 @@ def _sampled_full_size(name, n_tokens=12, rows_per_expert=2, max_experts=24, noi
     H.compare_dispatch(cfg, g, o)
     R = o["R"]
     xp = oracle.gather_rows(cfg, x, o["perm_src"])
-    np.testing.assert_array_equal(H.bytes_of(g["x_perm"][:R]), xp.view(np.int16))
+    np.testing.assert_array_equal(H.bytes_of(g["x_perm"][:R]), xp.view(np.int16 if cfg.act_dtype == "bf16" else np.int32))
     H.log(f"[full] {name}: routing and dispatch bit-exact; sampling expert rows")
     rng = np.random.default_rng(0)
     off = o["offsets"]
@@ -301,6 +316,10 @@ def test_full_size_mixtral_hash_sampled():
 
 def test_full_size_hierarchical_sampled():
     _sampled_full_size("hier", n_tokens=24, max_experts=32, rows_per_expert=2)
+
+
+def test_full_size_switch_reroute():
+    _sampled_full_size("switch_reroute", n_tokens=32, max_experts=16, rows_per_expert=2)
 
 
 def test_full_size_noisy_philox_routing():

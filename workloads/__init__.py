@@ -1,6 +1,6 @@
 """Seeded synthetic workloads for the sparse token-choice MoE FFN layer.
 
-This module holds the eight layer shapes and a deterministic input generator.
+This module holds the nine layer shapes and a deterministic input generator.
 It contains none of the layer's arithmetic: it only draws tensors.  Both the
 HIP path and the CPU oracle take their inputs from here, and nothing here
 imports either of them.
@@ -34,6 +34,9 @@ Shapes and distributions follow the layer configurations studied on the pages:
                groups then 2 experts each, k = 4 ("Outrageously Large Neural
                Networks" reading notes, appendix B hierarchical MoE and the
                2 x 2 remark).
+* ``switch_reroute`` the Switch workload with capacity overflow rerouted to
+               each token's next expert with room instead of dropped
+               (Lecture29, "Inference load balance": drop, reroute or delay).
 
 Distributions: x ~ N(0,1); every weight ~ N(0, 1/fan_in); the DeepSeek-style
 selection bias ~ N(0, 0.1) read as a variance; the Switch logit bias is
@@ -78,6 +81,7 @@ class Config:
     seed: int = 0
     n_groups: int = 0           # hierarchical gate: groups of E / n_groups experts
     group_top_k: int = 0        # hierarchical gate: groups picked per token
+    reroute: bool = False       # capacity overflow moves to the token's next expert instead of dropping
 
     def replace(self, **kw) -> "Config":
         return dataclasses.replace(self, **kw)
@@ -106,6 +110,9 @@ CONFIGS: Dict[str, Config] = {
                            act="swiglu", gate="hash", seed=1007),
     "hier": Config("hier", T=8192, d=512, F=1024, E=256, k=4, act_dtype="bf16", act="relu",
                    gate="hierarchical", n_groups=16, group_top_k=2, seed=1008),
+    "switch_reroute": Config("switch_reroute", T=2048, d=512, F=1024, E=64, k=1, act_dtype="f32",
+                             act="relu", gate="softmax_full", capacity_factor=1.25, residual=True,
+                             logit_bias="zipf", reroute=True, seed=1002),
 }
 
 
