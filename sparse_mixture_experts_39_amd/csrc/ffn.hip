@@ -16,10 +16,13 @@
 //   * MFMA operand order: the weights are source 0 and the activations
 //     source 1, so the accumulator lanes hold 4 consecutive output columns of
 //     one row and the epilogue stores 8 (bf16) or 16 (fp32) bytes per lane.
-//   * bf16 uses v_mfma_f32_32x32x16_bf16 (one 16-byte fragment per lane = 8 k
-//     values); fp32 uses four v_mfma_f32_16x16x4_f32 per 16-byte fragment.
-//     The k positions inside a fragment are the same for both operands, so
-//     the product is exact whatever order the unit visits them in.
+//   * 16x16 MFMA blocks for both dtypes: bf16 uses v_mfma_f32_16x16x32_bf16
+//     (one 16-byte fragment per lane = 8 k values, a half slice is one
+//     k-step), fp32 four v_mfma_f32_16x16x4_f32 per 16-byte fragment.  With
+//     twice as many, half as long MFMAs as the 32x32x16 form the same fenced
+//     schedule (below) keeps the matrix unit busier (4-5 % on the Mixtral
+//     GEMMs).  The k positions inside a fragment are the same for both
+//     operands, so the product is exact whatever order the unit visits them.
 //   * K is staged through LDS in slices of 128-byte rows (64 bf16 / 32 fp32
 //     values): one direct-to-LDS buffer load (buffer_load_dwordx4 ... lds)
 //     of a wave moves 8 rows x 128 bytes, i.e. whole 128-byte lines, with no
@@ -146,10 +149,10 @@ __device__ __forceinline__ void lds_barrier() {
 template <bool BF16, int BM, int BN, int EPI>
 struct GemmEpilogue {
     static constexpr int WM = BM / 2, WN = BN / 2;
-    static constexpr int MB = BF16 ? 32 : 16;
+    static constexpr int MB = 16;              // 16x16 MFMA blocks
     static constexpr int FM = WM / MB, FN = WN / MB;
-    static constexpr int RA = BF16 ? 16 : 4;   // accumulator registers per MFMA block
-    typedef typename std::conditional<BF16, floatx16_t, floatx4_t>::type acc_t;
+    static constexpr int RA = 4;               // accumulator registers per MFMA block
+    typedef floatx4_t acc_t;
 
     // float4 index of partial element (i, j, 4*r4 .. 4*r4+3) of wave w, unit u
     __device__ static int64_t partial_index(int u, int w, int i, int j, int r4, int lane) {
@@ -168,16 +171,14 @@ struct GemmEpilogue {
                         make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
     }
 
-    // Column groups of the epilogue: the 32- (bf16) or 16-row (fp32) blocks i
-    // of the wave's B tile are independent, except that fp32 SwiGLU pairs
-    // block 2p (gate) with block 2p+1 (up).
-    static constexpr int IG = (!BF16 && EPI == EPI_SWIGLU) ? 2 : 1;
+    // Column groups of the epilogue: the 16-row blocks i of the wave's B tile
+    // are independent, except that SwiGLU pairs block 2p (gate) with block
+    // 2p+1 (up).
+    static constexpr int IG = EPI == EPI_SWIGLU ? 2 : 1;
 
-    // Output of blocks i0 .. i0+IG-1 (acc[0 .. IG-1]).  bf16 blocks (32x32):
-    // lane l, element r = 4q + t holds D[n = 8q + 4(l/32) + t][m = l % 32].
-    // fp32 blocks (16x16): element t holds D[n = 4(l/16) + t][m = l % 16].
-    // Either way a lane owns 4 consecutive output columns of one row per q
-    // and stores them at once.
+    // Output of blocks i0 .. i0+IG-1 (acc[0 .. IG-1]).  In a 16x16 block,
+    // lane l, element t holds D[n = 4(l/16) + t][m = l % 16]: a lane owns 4
+    // consecutive output columns of one row and stores them at once.
     __device__ static void store_cols(const GemmParams& p, const acc_t (*acc)[FM], int i0, int row0, int rows, int nt,
                                       int wm, int wn, int lane) {
         auto store4 = [&](int m, int64_t col, const float* v) {
@@ -192,38 +193,7 @@ struct GemmEpilogue {
             }
         };
         auto silu_mul = [](float gt, float up) { return gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up; };
-        if constexpr (BF16) {
-            const int h = lane >> 5;
-            const int blk = wn * (WN / 32) + i0;                 // 32-row block of the B tile
-#pragma unroll
-            for (int j = 0; j < FM; ++j) {
-                const int m = wm * WM + j * 32 + (lane & 31);
-                if (m >= rows) continue;
-                if constexpr (EPI == EPI_SWIGLU) {
-                    // rows 0-15 of the block are gate units, rows 16-31 the
-                    // up units of the same 16 hidden units: q and q+2 pair up
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        float v[4];
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) v[t] = silu_mul(acc[0][j][4 * q + t], acc[0][j][4 * (q + 2) + t]);
-                        store4(m, (int64_t)nt * (BN / 2) + blk * 16 + 8 * q + 4 * h, v);
-                    }
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float v[4];
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            float x = acc[0][j][4 * q + t];
-                            if constexpr (EPI == EPI_RELU) x = fmaxf(x, 0.0f);
-                            v[t] = x;
-                        }
-                        store4(m, (int64_t)nt * BN + blk * 32 + 8 * q + 4 * h, v);
-                    }
-                }
-            }
-        } else {
+        {
             const int lg = lane >> 4;
 #pragma unroll
             for (int j = 0; j < FM; ++j) {
@@ -260,10 +230,10 @@ template <bool BF16, int BM, int BN, int EPI, bool SPLIT>
 __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     constexpr int WM = BM / 2, WN = BN / 2;
-    constexpr int MB = BF16 ? 32 : 16;        // MFMA block edge (32x32x16 bf16, 16x16x4 fp32)
+    constexpr int MB = 16;                    // MFMA block edge (16x16x32 bf16, 16x16x4 fp32)
     constexpr int FM = WM / MB, FN = WN / MB;
     constexpr int ES = BF16 ? 2 : 4;
-    constexpr int KS = BF16 ? 2 : 1;          // fragments per 32-row block per half slice
+    constexpr int KS = 1;                     // k-steps per half slice
     constexpr int SA = BM * 128, SB = BN * 128;
     constexpr RingDepth RD = ring_depth(BM, BN);
     constexpr int NA = RD.na, NB = RD.nb;
@@ -272,7 +242,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     typedef GemmEpilogue<BF16, BM, BN, EPI> Epi;
     typedef typename Epi::acc_t acc_t;
     static_assert(FM >= 1 && FN >= 1, "tile smaller than one MFMA block");
-    static_assert(BF16 || EPI != EPI_SWIGLU || (FN % 2) == 0, "SwiGLU pairs 16-row blocks");
+    static_assert(EPI != EPI_SWIGLU || (FN % 2) == 0, "SwiGLU pairs 16-row blocks");
     static_assert(RD.wait0 < 64 && RD.bytes <= 160 * 1024, "ring exceeds vmcnt or LDS");
     __shared__ __align__(16) uint8_t lds[RD.bytes];
 
@@ -375,12 +345,11 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < FM; ++j)
 #pragma unroll
-            for (int r = 0; r < (BF16 ? 16 : 4); ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
 
-    // Fragment reads, per half slice h (64 bytes of K).  bf16 (32x32x16):
-    // lane l takes row l % 32 of a 32-row block at logical chunk
-    // 4h + 2s + l/32 for k-step s (8 k values per lane).  fp32 (16x16x4):
-    // lane l takes row l % 16 at chunk 4h + l/16 (4 k values, four MFMAs).
+    // Fragment reads, per half slice h (64 bytes of K): lane l takes row
+    // l % 16 of a 16-row block at logical chunk 4h + l/16 (8 bf16 k values,
+    // one 16x16x32 MFMA; or 4 fp32 k values, four 16x16x4 MFMAs).
     // Weights are MFMA source 0 (rows = output columns n), activations
     // source 1 (columns = token rows m).  The swizzle depends on the row mod
     // 16 only, so blocks i of one operand differ by the constant i*MB*128.
@@ -391,7 +360,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2) {
             const int lr = lane & (MB - 1);
-            const int ch = BF16 ? (4 * h + 2 * s2 + (lane >> 5)) : (4 * h + (lane >> 4));
+            const int ch = 4 * h + (lane >> 4);
             fo[h][s2][0] = (wm * WM + lr) * 128 + ((ch ^ swz(lr)) << 4);
             fo[h][s2][1] = NA * SA + (wn * WN + lr) * 128 + ((ch ^ swz(lr)) << 4);
         }
@@ -415,7 +384,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
                 for (int j = 0; j < FM; ++j) {
                     const u32x4_t fa = f[s2 * (FM + FN) + j], fb = f[s2 * (FM + FN) + FM + i];
                     if constexpr (BF16) {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             __builtin_bit_cast(bf16x8_t, fb), __builtin_bit_cast(bf16x8_t, fa), acc[i][j], 0, 0, 0);
                     } else {
                         const floatx4_t b4 = __builtin_bit_cast(floatx4_t, fb);
@@ -432,7 +401,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     auto mma1 = [&](const u32x4_t* f, int m) {
         if constexpr (BF16) {
             const int s2 = m / (FN * FM), i = (m / FM) % FN, j = m % FM;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f[s2 * (FM + FN) + FM + i]),
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f[s2 * (FM + FN) + FM + i]),
                                                                 __builtin_bit_cast(bf16x8_t, f[s2 * (FM + FN) + j]),
                                                                 acc[i][j], 0, 0, 0);
         }
