@@ -57,7 +57,7 @@ from typing import Dict, Optional
 
 import torch
 
-__all__ = ["Config", "CONFIGS", "get", "make_inputs", "expert_tensor_names"]
+__all__ = ["Config", "CONFIGS", "get", "make_inputs", "make_output_grad", "expert_tensor_names"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -198,3 +198,13 @@ def make_inputs(cfg: Config, device="cpu", with_noise: Optional[bool] = None) ->
         w = ranks.pow(-1.1)
         inp["token_ids"] = torch.multinomial(w / w.sum(), T, replacement=True, generator=gen).to(torch.int32)
     return inp
+
+
+def make_output_grad(cfg: Config, device="cpu") -> torch.Tensor:
+    """The gradient dL/dout [T][d] of one backward call: standard normal in
+    the activation dtype, from its own stream (seed + 7919) so the forward
+    inputs do not change."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(cfg.seed + 7919)
+    return _normal((cfg.T, cfg.d), 1.0, gen, device, cfg.torch_dtype)
