@@ -326,6 +326,69 @@ moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float g
 moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x, void* out,
                              const moe_stats* stats, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- backward --------------------------------------------------------- */
+
+/* Tensors of the forward call that the backward reads (device pointers, as
+ * the stage calls wrote them: moe_route, moe_dispatch, moe_expert_ffn). */
+typedef struct {
+    const int32_t* topk_idx;        /* [T][slots] */
+    const float* topk_gate;         /* [T][slots] */
+    const int32_t* expert_offsets;  /* [E+1] */
+    const int32_t* perm_src;        /* [max_rows] */
+    const int32_t* slot_pos;        /* [T][slots] */
+    const void* x_perm;             /* [max_rows][d] act dtype */
+    const void* y_perm;             /* [max_rows][d] act dtype: expert outputs before the gate */
+} moe_saved;
+
+/* Gradient outputs (device pointers).  dx is required; every other member
+ * may be NULL to skip it, except that dw_gate / dw_up / dw_down go together
+ * (dw_up NULL for ReLU), as do dws_gate / dws_up / dws_down.  Each output is
+ * overwritten, not accumulated into.  Expert weight gradients have the
+ * layouts and the act dtype of the weights; router gradients are fp32. */
+typedef struct {
+    void* dx;            /* [T][d] act dtype */
+    float* dw_router;    /* [E][d] */
+    float* dlogit_bias;  /* [E] */
+    void* dw_gate;       /* [E][d_ff][d]  (W1) */
+    void* dw_up;         /* [E][d_ff][d]  (W3, SwiGLU) */
+    void* dw_down;       /* [E][d][d_ff]  (W2) */
+    void* dws_gate;      /* [d_ff_shared][d] */
+    void* dws_up;        /* [d_ff_shared][d] */
+    void* dws_down;      /* [d][d_ff_shared] */
+} moe_grads;
+
+/* Bytes of workspace moe_layer_backward needs. */
+moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Backward of the whole layer for the output gradient dy [T][d] (act
+ * dtype): ordinary backpropagation through the experts each token was sent
+ * to, the selection held constant (Shazeer et al. reading notes, section 2.1
+ * key points: a masked expert has probability and gradient exactly zero, the
+ * kept ones pass a nonzero gradient to the router matrix; CS25 "Lecture29"
+ * notes, Q&A "Gradient flow and training cost"; Switch Transformers lesson:
+ * a single expert still trains the router through the gate probability).
+ * With h, a = W1 x, u = W3 x as in moe_expert_up:
+ *   dy_r  = g_tj dY_t for the row r of a kept slot (t, j);
+ *   dg_tj = <dY_t, y_r> (0 for a dropped slot);
+ *   dh = dy_r W2; da = dh u s (1 + a (1 - s)), s = sigmoid(a), du = dh SiLU(a)
+ *   (ReLU: da = dh [a > 0]); dx_r = da W1 + du W3;
+ *   dW2_e = sum_r dy_r^T h_r, dW1_e = sum_r da_r^T x_r, dW3_e = sum_r du_r^T x_r;
+ *   dz from dg by the gate family: softmax over the selected logits
+ *   dz_i = g_i (dg_i - sum_j g_j dg_j); full softmax and expert choice
+ *   dz = p (dp - <p, dp>); sigmoid with selection bias
+ *   dz_i = (dg_i - sum_j g_j dg_j) s_i (1 - s_i) / sum_sel s (the bias gets
+ *   nothing); hash routing: none;
+ *   dW_r = sum_t dz_t x_t^T, dlogit_bias = sum_t dz_t;
+ *   dx_t = [residual] dY_t + sum_j dx_{r(t,j)} + shared expert + dz_t W_r.
+ * Supported gates: SOFTMAX_TOPK, SOFTMAX_FULL, SIGMOID_BIAS, EXPERT_CHOICE,
+ * HASH; the others and MOE_F_REROUTE return MOE_ERR_UNSUPPORTED.  All sums
+ * are fp32 in fixed orders (bitwise reproducible); intermediates (dy_r, a,
+ * u, dh, da, du, h, dx_r) are stored in the act dtype.
+ *   x [T][d]: the forward input; w: the forward weights; sv: the saved
+ *   forward tensors; g: outputs; ws >= moe_backward_workspace_size bytes. */
+moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* w, const void* x, const void* dy,
+                              const moe_saved* sv, const moe_grads* g, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

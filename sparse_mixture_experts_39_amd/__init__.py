@@ -18,7 +18,8 @@ __all__ = [
     "MoeConfig", "MoeWeights", "MoeStats", "MoeError", "lib", "config", "weights_from", "alloc_stats",
     "workspace", "max_rows", "capacity", "validate_config", "workspace_size",
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_shared_expert",
-    "moe_combine", "moe_layer_forward",
+    "moe_combine", "moe_layer_forward", "MoeSaved", "MoeGrads", "backward_workspace_size", "backward_workspace",
+    "moe_layer_backward",
     "EXPORTED_SYMBOLS", "LIB_PATH",
 ]
 
@@ -36,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "moe_last_hip_error",
     "moe_status_string", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
     "moe_shared_expert", "moe_combine", "moe_layer_forward", "moe_update_bias",
+    "moe_backward_workspace_size", "moe_layer_backward",
 )
 
 
@@ -70,6 +72,16 @@ class MoeStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "counts", "kept", "f", "P", "n_dropped", "imbalance", "aux", "device_status",
         "z_loss", "importance", "importance_cv2", "load", "load_cv2", "seq_aux")]
+
+
+class MoeSaved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "topk_idx", "topk_gate", "expert_offsets", "perm_src", "slot_pos", "x_perm", "y_perm")]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "dx", "dw_router", "dlogit_bias", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up", "dws_down")]
 
 
 _lib = None
@@ -117,6 +129,10 @@ def lib():
         L.moe_layer_forward.argtypes = [C, W, P, P, S, P, sz, P]
         L.moe_update_bias.restype = ctypes.c_int
         L.moe_update_bias.argtypes = [C, P, ctypes.c_float, P, P]
+        L.moe_backward_workspace_size.restype = ctypes.c_int
+        L.moe_backward_workspace_size.argtypes = [C, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_layer_backward.restype = ctypes.c_int
+        L.moe_layer_backward.argtypes = [C, W, P, P, ctypes.POINTER(MoeSaved), ctypes.POINTER(MoeGrads), P, sz, P]
         _lib = L
     return _lib
 
@@ -346,3 +362,50 @@ def moe_update_bias(c: MoeConfig, counts, gamma: float, sel_bias, stream=None):
     rc = lib().moe_update_bias(ctypes.byref(c), _ptr(counts, torch.int32, (E,), "counts"), ctypes.c_float(gamma),
                                _ptr(sel_bias, torch.float32, (E,), "sel_bias"), _stream(stream))
     _check("moe_update_bias", rc)
+
+
+# ---------------------------------------------------------------- backward
+
+def backward_workspace_size(c: MoeConfig) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_backward_workspace_size", lib().moe_backward_workspace_size(ctypes.byref(c), ctypes.byref(n)))
+    return int(n.value)
+
+
+def backward_workspace(c: MoeConfig, device="cuda") -> torch.Tensor:
+    return torch.empty(max(backward_workspace_size(c), 1), dtype=torch.uint8, device=device)
+
+
+def moe_layer_backward(c: MoeConfig, w: MoeWeights, x, dy, saved: Dict[str, torch.Tensor],
+                       grads: Dict[str, torch.Tensor], ws=None, stream=None):
+    """Backward of the layer.  ``saved`` holds the forward's stage outputs
+    (topk_idx, topk_gate, expert_offsets, perm_src, slot_pos, x_perm, y_perm);
+    ``grads`` the output tensors to write (dx required; dw_router,
+    dlogit_bias, dw_gate / dw_up / dw_down, dws_gate / dws_up / dws_down
+    optional)."""
+    T, d, E, F, dt = c.T, c.d_model, c.n_experts, c.d_ff, _dt(c)
+    k, R = route_slots(c), max_rows(c)
+    sv = MoeSaved()
+    sv.topk_idx = _ptr(saved.get("topk_idx"), torch.int32, (T, k), "topk_idx")
+    sv.topk_gate = _ptr(saved.get("topk_gate"), torch.float32, (T, k), "topk_gate")
+    sv.expert_offsets = _ptr(saved.get("expert_offsets"), torch.int32, (E + 1,), "expert_offsets")
+    sv.perm_src = _ptr(saved.get("perm_src"), torch.int32, (R,), "perm_src")
+    sv.slot_pos = _ptr(saved.get("slot_pos"), torch.int32, (T, k), "slot_pos")
+    sv.x_perm = _ptr(saved.get("x_perm"), dt, (R, d), "x_perm")
+    sv.y_perm = _ptr(saved.get("y_perm"), dt, (R, d), "y_perm")
+    g = MoeGrads()
+    g.dx = _ptr(grads.get("dx"), dt, (T, d), "dx")
+    g.dw_router = _ptr(grads.get("dw_router"), torch.float32, (E, d), "dw_router")
+    g.dlogit_bias = _ptr(grads.get("dlogit_bias"), torch.float32, (E,), "dlogit_bias")
+    g.dw_gate = _ptr(grads.get("dw_gate"), dt, (E, F, d), "dw_gate")
+    g.dw_up = _ptr(grads.get("dw_up"), dt, (E, F, d), "dw_up")
+    g.dw_down = _ptr(grads.get("dw_down"), dt, (E, d, F), "dw_down")
+    Fs = c.d_ff_shared
+    g.dws_gate = _ptr(grads.get("dws_gate"), dt, (Fs, d), "dws_gate")
+    g.dws_up = _ptr(grads.get("dws_up"), dt, (Fs, d), "dws_up")
+    g.dws_down = _ptr(grads.get("dws_down"), dt, (d, Fs), "dws_down")
+    rc = lib().moe_layer_backward(ctypes.byref(c), ctypes.byref(w), _ptr(x, dt, (T, d), "x"),
+                                  _ptr(dy, dt, (T, d), "dy"), ctypes.byref(sv), ctypes.byref(g),
+                                  _ptr(ws, torch.uint8, name="ws"), ws.numel() if ws is not None else 0,
+                                  _stream(stream))
+    _check("moe_layer_backward", rc)

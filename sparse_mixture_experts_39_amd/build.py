@@ -1,8 +1,9 @@
 """Build libmoe.so (the gfx950 kernels and the C ABI of include/moe.h) in-tree.
 
 Every HIP source is compiled with hipcc for gfx950 only, with packed-fp32
-instructions disabled; route.hip is compiled without fp contraction because
-the router's integer decisions rest on a fixed sequence of fp32 operations.
+instructions disabled; route.hip and backward.hip are compiled without fp
+contraction because the router's integer decisions (and the backward's
+recomputed logits) rest on a fixed sequence of fp32 operations.
 """
 from __future__ import annotations
 
@@ -23,6 +24,7 @@ SOURCES = {
     "dispatch.hip": [],
     "combine.hip": [],
     "ffn.hip": [],
+    "backward.hip": ["-ffp-contract=off"],
 }
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -1,0 +1,576 @@
+// Backward pass of the MoE FFN layer on gfx950: the kernels that are not the
+// two input-gradient products (those run on the forward's grouped GEMM in
+// ffn.hip, against transposed weight copies made here).
+//
+// The layer trains by ordinary backpropagation through the experts each
+// token went to, with the top-k choice held constant; masked experts get
+// exactly zero gradient and the selected logits a nonzero one (Shazeer et al.
+// reading notes, section 2.1 key points; CS25 "Lecture29" notes, Q&A
+// "Gradient flow and training cost").
+//
+//   k_transpose      weight copies with the other dimension contiguous
+//   k_bwd_rows       per kept row r of assignment a = (t, j): dy_perm[r] =
+//                    g_a dY[t] and the gate gradient dg_a = <dY[t], y_perm[r]>
+//   k_bwd_act        SwiGLU / ReLU derivative: (dh, a, u) -> da | du and h
+//   k_gemm_tn        ragged-K grouped GEMM C_e = A_e^T B_e over the rows of
+//                    each expert: the expert weight gradients (MFMA)
+//   k_bwd_router     logit gradient dz of every token from dg and the gates
+//   k_bwd_dx         token gradient: residual + routed rows in slot order +
+//                    shared expert + dz W_r
+//   k_bwd_wr_part /
+//   k_bwd_wr_sum     router gradients dW_r = dz^T x and db = sum_t dz, in a
+//                    fixed order over token chunks
+//
+// Every reduction has one fixed order, so results are bitwise reproducible.
+// This file is compiled with -ffp-contract=off so the router recomputation
+// matches the forward's logits bit for bit.
+#include <hip/hip_runtime.h>
+
+#include "canon_math.h"
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+template <bool BF16>
+__device__ __forceinline__ void store_act(void* p, int64_t i, float v) {
+    if constexpr (BF16) ((uint16_t*)p)[i] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
+    else ((float*)p)[i] = v;
+}
+
+// Fixed-order sum over the 256 threads of a block (wave shuffles, then the
+// four wave totals in order).  Every thread gets the total.
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+}  // namespace
+
+// dst[b][c][coff + r] = src[b][r][c] for r < R, c < C (both multiples of
+// 64), through a 64 x 65 LDS tile.
+template <typename Tv>
+__global__ __launch_bounds__(256) void k_transpose(const Tv* __restrict__ src, int R, int C, int64_t sbatch,
+                                                   Tv* __restrict__ dst, int64_t ldd, int64_t dbatch, int coff) {
+    __shared__ Tv tile[64][65];
+    const int b = blockIdx.z;
+    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    const Tv* s = src + (int64_t)b * sbatch;
+    Tv* d = dst + (int64_t)b * dbatch;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int i = ty; i < 64; i += 4) tile[i][tx] = s[(int64_t)(r0 + i) * C + c0 + tx];
+    __syncthreads();
+    for (int i = ty; i < 64; i += 4) d[(int64_t)(c0 + i) * ldd + coff + r0 + tx] = tile[tx][i];
+}
+
+void launch_transpose(const void* src, int B, int R, int C, int64_t sbatch, void* dst, int64_t ldd, int64_t dbatch,
+                      int coff, int elem_bytes, hipStream_t s) {
+    if (B <= 0 || R <= 0 || C <= 0) return;
+    dim3 grid(C / 64, R / 64, B);
+    if (elem_bytes == 2)
+        hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)src, R, C, sbatch,
+                           (uint16_t*)dst, ldd, dbatch, coff);
+    else
+        hipLaunchKernelGGL(k_transpose<float>, grid, dim3(256), 0, s, (const float*)src, R, C, sbatch, (float*)dst,
+                           ldd, dbatch, coff);
+}
+
+// One block per permuted row r < offsets[E]; a = perm_src[r], t = a / slots.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_bwd_rows(const void* __restrict__ dy, const void* __restrict__ y_perm,
+                                                  const int32_t* __restrict__ perm_src,
+                                                  const int32_t* __restrict__ offsets, int E,
+                                                  const float* __restrict__ gates, int slots, int d,
+                                                  void* __restrict__ dy_perm, float* __restrict__ dg) {
+    __shared__ float red[4];
+    const int r = blockIdx.x;
+    if (r >= offsets[E]) return;
+    const int a = perm_src[r];
+    const int t = a / slots;
+    const float g = gates[a];
+    float acc = 0.0f;
+    for (int c = threadIdx.x; c < d; c += 256) {
+        const float v = load_act<BF16>(dy, (int64_t)t * d + c);
+        acc += v * load_act<BF16>(y_perm, (int64_t)r * d + c);
+        store_act<BF16>(dy_perm, (int64_t)r * d + c, g * v);
+    }
+    const float tot = block_sum256(acc, red);
+    if (threadIdx.x == 0) dg[a] = tot;
+}
+
+__global__ void k_zero_f32(float* p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+void launch_zero_f32(float* p, int64_t n, hipStream_t s) {
+    if (n <= 0) return;
+    hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+}
+
+void launch_bwd_rows(bool bf16, const void* dy, const void* y_perm, const int32_t* perm_src, const int32_t* offsets,
+                     int E, const float* gates, int slots, int d, int64_t max_rows, void* dy_perm, float* dg,
+                     hipStream_t s) {
+    if (max_rows <= 0) return;
+    if (bf16)
+        hipLaunchKernelGGL(k_bwd_rows<true>, dim3((unsigned)max_rows), dim3(256), 0, s, dy, y_perm, perm_src, offsets,
+                           E, gates, slots, d, dy_perm, dg);
+    else
+        hipLaunchKernelGGL(k_bwd_rows<false>, dim3((unsigned)max_rows), dim3(256), 0, s, dy, y_perm, perm_src,
+                           offsets, E, gates, slots, d, dy_perm, dg);
+}
+
+// Activation derivative on rows < rows_end (= offsets[E], or n_rows when
+// offsets is NULL), 4 columns per thread.  SwiGLU: h = SiLU(a) u,
+// da = dh u s (1 + a (1 - s)) with s = sigmoid(a), du = dh SiLU(a); ReLU:
+// h = relu(a), da = dh [a > 0].  da goes to dadu[r][0..F), du to
+// dadu[r][F..2F).
+template <bool BF16, bool SWIGLU>
+__global__ __launch_bounds__(256) void k_bwd_act(const void* __restrict__ dh, const void* __restrict__ a_in,
+                                                 const void* __restrict__ u_in, const int32_t* __restrict__ offsets,
+                                                 int E, int n_rows, int F, void* __restrict__ dadu,
+                                                 void* __restrict__ h_out) {
+    const int64_t rows_end = offsets ? offsets[E] : n_rows;
+    const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    const int64_t r = i4 / F;
+    if (r >= rows_end) return;
+    const int c = (int)(i4 - r * F);
+    const int ldo = SWIGLU ? 2 * F : F;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t i = i4 + q;
+        const float g = load_act<BF16>(dh, i);
+        const float av = load_act<BF16>(a_in, i);
+        if constexpr (SWIGLU) {
+            const float uv = load_act<BF16>(u_in, i);
+            const float sg = 1.0f / (1.0f + __expf(-av));
+            const float silu = av * sg;
+            store_act<BF16>(dadu, r * ldo + c + q, g * uv * sg * (1.0f + av * (1.0f - sg)));
+            store_act<BF16>(dadu, r * ldo + F + c + q, g * silu);
+            store_act<BF16>(h_out, i, silu * uv);
+        } else {
+            store_act<BF16>(dadu, r * ldo + c + q, av > 0.0f ? g : 0.0f);
+            store_act<BF16>(h_out, i, av > 0.0f ? av : 0.0f);
+        }
+    }
+}
+
+void launch_bwd_act(bool bf16, bool swiglu, const void* dh, const void* a, const void* u, const int32_t* offsets,
+                    int E, int64_t max_rows, int F, void* dadu, void* h, hipStream_t s) {
+    const int64_t n4 = max_rows * F / 4;
+    if (n4 <= 0) return;
+    const dim3 grid((unsigned)((n4 + 255) / 256));
+    const int nr = (int)max_rows;
+#define MOE_ACT_ARGS dh, a, u, offsets, E, nr, F, dadu, h
+    if (bf16) {
+        if (swiglu) hipLaunchKernelGGL((k_bwd_act<true, true>), grid, dim3(256), 0, s, MOE_ACT_ARGS);
+        else hipLaunchKernelGGL((k_bwd_act<true, false>), grid, dim3(256), 0, s, MOE_ACT_ARGS);
+    } else {
+        if (swiglu) hipLaunchKernelGGL((k_bwd_act<false, true>), grid, dim3(256), 0, s, MOE_ACT_ARGS);
+        else hipLaunchKernelGGL((k_bwd_act<false, false>), grid, dim3(256), 0, s, MOE_ACT_ARGS);
+    }
+#undef MOE_ACT_ARGS
+}
+
+// ---------------------------------------------------------------------------
+// Ragged-K grouped GEMM for the weight gradients:
+//   C_e[m][n] = sum over rows r in [off[e], off[e+1]) of A[r][m] B[r][n]
+// A [rows][lda], B [rows][ldb] (m, n contiguous), C_e [M][N] at C + e M N,
+// fp32 accumulation, one rounding to the act dtype at the end.  An expert
+// with no rows gets zeros.  128 x 128 tiles, 256 threads as 2 x 2 waves of
+// 64 x 64, K (= rows) in chunks staged through two LDS buffers from
+// registers, so the next chunk's loads are in flight during the MFMAs.
+//
+// bf16: the 16x16x32 MFMA wants 8 consecutive k of one row m per lane, so a
+// chunk of 64 rows is written to LDS transposed, as [m][64 k] with 16-byte
+// k-groups at physical slot g ^ (m & 7) ^ ((m >> 3) & 7): the fragment reads
+// (16 consecutive m, one group) and the transposed writes (m = 8 i + j over
+// lanes i) both spread over all banks.  A thread loads an 8 x 8 block (8
+// rows, 8 columns) and transposes it in registers.
+// fp32: the 16x16x4 MFMA takes one k per lane, so chunks of 32 rows stay
+// [k][m] in LDS (rows padded to 144 floats).
+// ---------------------------------------------------------------------------
+struct TnParams {
+    const void* A;
+    int64_t lda;
+    const void* B;
+    int64_t ldb;
+    void* C;
+    int M, N, E;
+    int tiles_m, tiles_n;
+    const int32_t* offsets;
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_gemm_tn(TnParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int BM = 128, BN = 128;
+    constexpr int KC = BF16 ? 64 : 32;                     // rows per chunk
+    constexpr int OPB = BF16 ? BM * KC * 2 : KC * 144 * 4; // bytes per operand per buffer
+    __shared__ __align__(16) uint8_t lds[2 * 2 * OPB];
+    const int tile = blockIdx.x;
+    const int per_e = p.tiles_m * p.tiles_n;
+    const int e = tile / per_e;
+    const int tm = (tile - e * per_e) / p.tiles_n, tn = tile - e * per_e - tm * p.tiles_n;
+    const int m_base = tm * BM, n_base = tn * BN;
+    const int lo = p.offsets[e], hi = p.offsets[e + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    floatx4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const int nchunks = (hi - lo + KC - 1) / KC;
+
+    if constexpr (BF16) {
+        // load unit: operand (tid < 128: A, else B), 8 columns from col0, 8 rows from k0
+        const bool isA = tid < 128;
+        const int u = tid & 127;
+        const int cg = u & 15, kq = u >> 4;
+        const int col0 = cg * 8;
+        const int gcol = (isA ? m_base : n_base) + col0;
+        const bool col_ok = gcol < (isA ? p.M : p.N);
+        const uint16_t* base = (const uint16_t*)(isA ? p.A : p.B);
+        const int64_t ld = isA ? p.lda : p.ldb;
+        u32x4_t st[8];
+        auto load = [&](int ch) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = lo + ch * KC + kq * 8 + i;
+                if (col_ok && r < hi) st[i] = *(const u32x4_t*)(base + (int64_t)r * ld + gcol);
+                else st[i] = u32x4_t{0u, 0u, 0u, 0u};
+            }
+        };
+        auto put = [&](int buf) {
+            uint8_t* dst = lds + (size_t)(buf * 2 + (isA ? 0 : 1)) * OPB;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int m = col0 + j;
+                u32x4_t v;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t x0 = st[2 * q][j >> 1], x1 = st[2 * q + 1][j >> 1];
+                    v[q] = (j & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+                }
+                const int slot = kq ^ (m & 7) ^ ((m >> 3) & 7);
+                *(u32x4_t*)(dst + m * 128 + slot * 16) = v;
+            }
+        };
+        if (nchunks > 0) {
+            load(0);
+            put(0);
+        }
+        __syncthreads();
+        for (int ch = 0; ch < nchunks; ++ch) {
+            const int buf = ch & 1;
+            if (ch + 1 < nchunks) load(ch + 1);
+            const uint8_t* sa = lds + (size_t)(buf * 2) * OPB;
+            const uint8_t* sb = lds + (size_t)(buf * 2 + 1) * OPB;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int g = ks * 4 + (lane >> 4);
+                u32x4_t fa[4], fb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = wm * 64 + i * 16 + (lane & 15);
+                    fa[i] = *(const u32x4_t*)(sa + m * 128 + ((g ^ (m & 7) ^ ((m >> 3) & 7)) * 16));
+                    const int n = wn * 64 + i * 16 + (lane & 15);
+                    fb[i] = *(const u32x4_t*)(sb + n * 128 + ((g ^ (n & 7) ^ ((n >> 3) & 7)) * 16));
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fb[i]),
+                                                                            __builtin_bit_cast(bf16x8_t, fa[j]),
+                                                                            acc[i][j], 0, 0, 0);
+            }
+            if (ch + 1 < nchunks) put(buf ^ 1);
+            __syncthreads();
+        }
+    } else {
+        // fp32: 32 rows x 128 columns per operand and chunk, 4 float4 loads
+        // per thread per operand (row tid/32 + 8 i, columns 4 (tid % 32))
+        const int c4 = (tid & 31) * 4, r0 = tid >> 5;
+        floatx4_t sta[4], stb[4];
+        const bool a_ok = m_base + c4 < p.M, b_ok = n_base + c4 < p.N;
+        auto load = [&](int ch) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = lo + ch * KC + r0 + 8 * i;
+                const bool rok = r < hi;
+                sta[i] = (rok && a_ok) ? *(const floatx4_t*)((const float*)p.A + (int64_t)r * p.lda + m_base + c4)
+                                       : floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                stb[i] = (rok && b_ok) ? *(const floatx4_t*)((const float*)p.B + (int64_t)r * p.ldb + n_base + c4)
+                                       : floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        };
+        auto put = [&](int buf) {
+            float* da = (float*)(lds + (size_t)(buf * 2) * OPB);
+            float* db = (float*)(lds + (size_t)(buf * 2 + 1) * OPB);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                *(floatx4_t*)(da + (r0 + 8 * i) * 144 + c4) = sta[i];
+                *(floatx4_t*)(db + (r0 + 8 * i) * 144 + c4) = stb[i];
+            }
+        };
+        if (nchunks > 0) {
+            load(0);
+            put(0);
+        }
+        __syncthreads();
+        for (int ch = 0; ch < nchunks; ++ch) {
+            const int buf = ch & 1;
+            if (ch + 1 < nchunks) load(ch + 1);
+            const float* sa = (const float*)(lds + (size_t)(buf * 2) * OPB);
+            const float* sb = (const float*)(lds + (size_t)(buf * 2 + 1) * OPB);
+#pragma unroll
+            for (int ks = 0; ks < KC / 4; ++ks) {
+                const int k = ks * 4 + (lane >> 4);
+                float fa[4], fb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    fa[i] = sa[k * 144 + wm * 64 + i * 16 + (lane & 15)];
+                    fb[i] = sb[k * 144 + wn * 64 + i * 16 + (lane & 15)];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb[i], fa[j], acc[i][j], 0, 0, 0);
+            }
+            if (ch + 1 < nchunks) put(buf ^ 1);
+            __syncthreads();
+        }
+    }
+    // lane holds C[m = .. + (lane & 15)][n = .. + 4 (lane >> 4) + t] of block (i = n block, j = m block)
+    void* Ce = (uint8_t*)p.C + (size_t)e * p.M * p.N * (BF16 ? 2 : 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int m = m_base + wm * 64 + j * 16 + (lane & 15);
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = n_base + wn * 64 + i * 16 + 4 * (lane >> 4);
+            if (n >= p.N) continue;
+            const int64_t o = (int64_t)m * p.N + n;
+            if constexpr (BF16) {
+                uint2 w;
+                w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+                w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+                *(uint2*)((uint16_t*)Ce + o) = w;
+            } else {
+                *(floatx4_t*)((float*)Ce + o) = acc[i][j];
+            }
+        }
+    }
+#endif
+}
+
+hipError_t launch_gemm_tn(bool bf16, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int M, int N,
+                          int E, const int32_t* offsets, hipStream_t s) {
+    TnParams p;
+    p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.C = C;
+    p.M = M; p.N = N; p.E = E;
+    p.tiles_m = (M + 127) / 128;
+    p.tiles_n = (N + 127) / 128;
+    p.offsets = offsets;
+    const int64_t grid = (int64_t)E * p.tiles_m * p.tiles_n;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    if (bf16) hipLaunchKernelGGL(k_gemm_tn<true>, dim3((unsigned)grid), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(k_gemm_tn<false>, dim3((unsigned)grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Router.  One wave per token: z_e = dots[t][e] (+ logit_bias[e]) exactly as
+// the forward forms it, then dz by the gate family (see moe.h):
+//   softmax over the selected:    dz_e = g_j (dg_j - sum_i g_i dg_i)  (e = idx_j)
+//   full softmax / expert choice: dz = p (dp - <p, dp>), p = softmax(z)
+//   sigmoid with selection bias:  dz_e = (dg_j - sum_i g_i dg_i) / S s_e (1 - s_e),
+//                                 S = sum of s over the selected
+// Slots of one token hold distinct experts, so dp_e is one dg; each dz
+// element is written once.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bwd_router(const float* __restrict__ dots, int NC,
+                                                    const float* __restrict__ logit_bias,
+                                                    const int32_t* __restrict__ idx, const float* __restrict__ gates,
+                                                    const float* __restrict__ dg, int gate, int T, int E, int slots,
+                                                    float* __restrict__ dz) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + w;
+    if (t >= T) return;
+    const int32_t* it = idx + (int64_t)t * slots;
+    const float* gt = gates + (int64_t)t * slots;
+    const float* dgt = dg + (int64_t)t * slots;
+    float* dzt = dz + (int64_t)t * E;
+    auto zv = [&](int e) { return logit_bias ? dots[(int64_t)t * NC + e] + logit_bias[e] : dots[(int64_t)t * NC + e]; };
+    auto wsum = [&](float v) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+        return v;
+    };
+    // slot of expert e in this token's selection, or -1 (expert choice keeps
+    // slot e for expert e)
+    auto slot_of = [&](int e) {
+        if (gate == MOE_GATE_EXPERT_CHOICE) return it[e] >= 0 ? e : -1;
+        for (int j = 0; j < slots; ++j)
+            if (it[j] == e) return j;
+        return -1;
+    };
+    if (gate == MOE_GATE_SOFTMAX_FULL || gate == MOE_GATE_EXPERT_CHOICE) {
+        float m = -INFINITY;
+        for (int e = lane; e < E; e += 64) m = fmaxf(m, zv(e));
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        float sum = 0.0f;
+        for (int e = lane; e < E; e += 64) sum += canon::expc(zv(e) - m);
+        sum = wsum(sum);
+        float c = 0.0f;
+        for (int e = lane; e < E; e += 64) {
+            const int j = slot_of(e);
+            if (j >= 0) c += canon::expc(zv(e) - m) / sum * dgt[j];
+        }
+        c = wsum(c);
+        for (int e = lane; e < E; e += 64) {
+            const int j = slot_of(e);
+            const float pe = canon::expc(zv(e) - m) / sum;
+            dzt[e] = pe * ((j >= 0 ? dgt[j] : 0.0f) - c);
+        }
+        return;
+    }
+    // selected-slot families: c = sum_j g_j dg_j over the token's slots
+    float c = 0.0f, S = 0.0f;
+    for (int j = lane; j < slots; j += 64) {
+        if (it[j] >= 0) {
+            c += gt[j] * dgt[j];
+            if (gate == MOE_GATE_SIGMOID_BIAS) S += canon::sigmoidc(zv(it[j]));
+        }
+    }
+    c = wsum(c);
+    S = wsum(S);
+    for (int e = lane; e < E; e += 64) {
+        const int j = slot_of(e);
+        float v = 0.0f;
+        if (j >= 0) {
+            if (gate == MOE_GATE_SIGMOID_BIAS) {
+                const float s = canon::sigmoidc(zv(e));
+                v = (dgt[j] - c) / S * (s * (1.0f - s));
+            } else {
+                v = gt[j] * (dgt[j] - c);
+            }
+        }
+        dzt[e] = v;
+    }
+}
+
+void launch_bwd_router(const float* dots, int NC, const float* logit_bias, const int32_t* idx, const float* gates,
+                       const float* dg, int gate, int T, int E, int slots, float* dz, hipStream_t s) {
+    if (T <= 0) return;
+    hipLaunchKernelGGL(k_bwd_router, dim3((T + 3) / 4), dim3(256), 0, s, dots, NC, logit_bias, idx, gates, dg, gate,
+                       T, E, slots, dz);
+}
+
+// Token gradient, one block per token, fp32 in this order: residual dY,
+// routed rows in slot order, shared expert, then dz_e W_r[e] for e ascending
+// (zero dz skipped).
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_bwd_dx(const void* __restrict__ dy, const void* __restrict__ dx_perm,
+                                                const int32_t* __restrict__ slot_pos, int slots,
+                                                const void* __restrict__ dx_shared, const float* __restrict__ dz,
+                                                const float* __restrict__ w_router, int E, int d, bool residual,
+                                                void* __restrict__ dx) {
+    const int t = blockIdx.x;
+    const int32_t* sp = slot_pos + (int64_t)t * slots;
+    const float* dzt = dz ? dz + (int64_t)t * E : nullptr;
+    for (int c = threadIdx.x; c < d; c += 256) {
+        float v = residual ? load_act<BF16>(dy, (int64_t)t * d + c) : 0.0f;
+        for (int j = 0; j < slots; ++j) {
+            const int r = sp[j];
+            if (r >= 0) v += load_act<BF16>(dx_perm, (int64_t)r * d + c);
+        }
+        if (dx_shared) v += load_act<BF16>(dx_shared, (int64_t)t * d + c);
+        if (dzt) {
+            for (int e = 0; e < E; ++e) {
+                const float g = dzt[e];
+                if (g != 0.0f) v += g * w_router[(int64_t)e * d + c];
+            }
+        }
+        store_act<BF16>(dx, (int64_t)t * d + c, v);
+    }
+}
+
+void launch_bwd_dx(bool bf16, const void* dy, const void* dx_perm, const int32_t* slot_pos, int slots,
+                   const void* dx_shared, const float* dz, const float* w_router, int T, int E, int d, bool residual,
+                   void* dx, hipStream_t s) {
+    if (T <= 0) return;
+    if (bf16)
+        hipLaunchKernelGGL(k_bwd_dx<true>, dim3(T), dim3(256), 0, s, dy, dx_perm, slot_pos, slots, dx_shared, dz,
+                           w_router, E, d, residual, dx);
+    else
+        hipLaunchKernelGGL(k_bwd_dx<false>, dim3(T), dim3(256), 0, s, dy, dx_perm, slot_pos, slots, dx_shared, dz,
+                           w_router, E, d, residual, dx);
+}
+
+// Router gradients in two fixed-order passes: block (e, column chunk, token
+// chunk q) sums tokens [q 256, q 256 + 256) in order into part[q][e][c]
+// (column d is the bias: the sum of dz); then k_bwd_wr_sum adds the chunks
+// in order.
+constexpr int kWrTokens = 256;
+
+int bwd_wr_chunks(int T) { return (T + kWrTokens - 1) / kWrTokens; }
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_bwd_wr_part(const float* __restrict__ dz, const void* __restrict__ x, int T,
+                                                     int E, int d, float* __restrict__ part) {
+    const int e = blockIdx.y, q = blockIdx.z;
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    const int t0 = q * kWrTokens, t1 = min(T, t0 + kWrTokens);
+    float acc = 0.0f, accb = 0.0f;
+    for (int t = t0; t < t1; ++t) {
+        const float g = dz[(int64_t)t * E + e];
+        accb += g;
+        if (c < d) acc += g * load_act<BF16>(x, (int64_t)t * d + c);
+    }
+    float* pe = part + ((int64_t)q * E + e) * (d + 1);
+    if (c < d) pe[c] = acc;
+    if (c == d) pe[d] = accb;
+}
+
+__global__ __launch_bounds__(256) void k_bwd_wr_sum(const float* __restrict__ part, int nq, int E, int d,
+                                                    float* __restrict__ dw, float* __restrict__ db) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t n = (int64_t)E * (d + 1);
+    if (i >= n) return;
+    float v = 0.0f;
+    for (int q = 0; q < nq; ++q) v += part[(int64_t)q * n + i];
+    const int e = (int)(i / (d + 1)), c = (int)(i - (int64_t)e * (d + 1));
+    if (c < d) {
+        if (dw) dw[(int64_t)e * d + c] = v;
+    } else if (db) {
+        db[e] = v;
+    }
+}
+
+void launch_bwd_wr(bool bf16, const float* dz, const void* x, int T, int E, int d, float* part, float* dw, float* db,
+                   hipStream_t s) {
+    const int nq = bwd_wr_chunks(T);
+    if (nq > 0) {
+        const dim3 grid((d + 1 + 255) / 256, E, nq);
+        if (bf16) hipLaunchKernelGGL(k_bwd_wr_part<true>, grid, dim3(256), 0, s, dz, x, T, E, d, part);
+        else hipLaunchKernelGGL(k_bwd_wr_part<false>, grid, dim3(256), 0, s, dz, x, T, E, d, part);
+    }
+    const int64_t n = (int64_t)E * (d + 1);
+    hipLaunchKernelGGL(k_bwd_wr_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, nq, E, d, dw, db);
+}
+
+}  // namespace moe

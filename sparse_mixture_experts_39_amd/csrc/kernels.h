@@ -76,4 +76,31 @@ hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, c
                                float* partial, int BM, int BN, hipStream_t s);
 GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N);
 
+// backward.hip
+// dst[b][c][coff + r] = src[b][r][c]; R and C multiples of 64.
+void launch_transpose(const void* src, int B, int R, int C, int64_t sbatch, void* dst, int64_t ldd, int64_t dbatch,
+                      int coff, int elem_bytes, hipStream_t s);
+void launch_zero_f32(float* p, int64_t n, hipStream_t s);
+// dy_perm[r] = gates[a] dy[a / slots] and dg[a] = <dy[a / slots], y_perm[r]>
+// for every kept row r (a = perm_src[r]).
+void launch_bwd_rows(bool bf16, const void* dy, const void* y_perm, const int32_t* perm_src, const int32_t* offsets,
+                     int E, const float* gates, int slots, int d, int64_t max_rows, void* dy_perm, float* dg,
+                     hipStream_t s);
+// da | du (row stride 2F; F for ReLU) and h from dh, a, u on the kept rows
+// (offsets == NULL: the first max_rows rows).
+void launch_bwd_act(bool bf16, bool swiglu, const void* dh, const void* a, const void* u, const int32_t* offsets,
+                    int E, int64_t max_rows, int F, void* dadu, void* h, hipStream_t s);
+// C_e[M][N] = sum over the rows r of expert e of A[r][m] B[r][n].
+hipError_t launch_gemm_tn(bool bf16, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int M, int N,
+                          int E, const int32_t* offsets, hipStream_t s);
+void launch_bwd_router(const float* dots, int NC, const float* logit_bias, const int32_t* idx, const float* gates,
+                       const float* dg, int gate, int T, int E, int slots, float* dz, hipStream_t s);
+void launch_bwd_dx(bool bf16, const void* dy, const void* dx_perm, const int32_t* slot_pos, int slots,
+                   const void* dx_shared, const float* dz, const float* w_router, int T, int E, int d, bool residual,
+                   void* dx, hipStream_t s);
+int bwd_wr_chunks(int T);
+// dW_r = dz^T x and db = sum_t dz; part holds bwd_wr_chunks(T) * E * (d + 1) floats.
+void launch_bwd_wr(bool bf16, const float* dz, const void* x, int T, int E, int d, float* part, float* dw, float* db,
+                   hipStream_t s);
+
 }  // namespace moe

@@ -163,6 +163,80 @@ moe_status check_ws(const moe_config* c, void* ws, size_t ws_bytes) {
     return MOE_OK;
 }
 
+// ---- backward workspace ----------------------------------------------------
+struct BwdLayout {
+    size_t dots, dg, dz, wr_part;                                  // router
+    size_t dyp, a, u, dh, dadu, hh, dxp, w2t, w13t;                // routed experts
+    size_t sa, su, sdh, sdadu, shh, sdx, sw2t, sw13t;              // shared expert
+    size_t plan, plan_copy, plan_s_copy, partial;
+    size_t total;
+};
+
+bool bwd_gate_supported(const moe_config* c) {
+    return c->gate == MOE_GATE_SOFTMAX_TOPK || c->gate == MOE_GATE_SOFTMAX_FULL ||
+           c->gate == MOE_GATE_SIGMOID_BIAS || c->gate == MOE_GATE_EXPERT_CHOICE || c->gate == MOE_GATE_HASH;
+}
+
+// Split-K workspace of the backward's grouped GEMMs (all plain stores).
+size_t bwd_partial_bytes_of(const moe_config* c) {
+    const bool bf = is_bf16(c);
+    size_t b = 0;
+    auto need = [&](int64_t rows, int E, int N) {
+        const moe::GemmShape g = moe::pick_gemm_shape(bf, 0, rows, E, N);
+        const size_t n = moe::gemm_partial_bytes(g.BM, g.BN);
+        if (n > b) b = n;
+    };
+    const int64_t R = max_rows_of(c);
+    if (R > 0) {
+        need(R, c->n_experts, c->d_ff);
+        need(R, c->n_experts, c->d_model);
+    }
+    if (c->n_shared > 0 && c->T > 0) {
+        need(c->T, 1, c->d_ff_shared);
+        need(c->T, 1, c->d_model);
+    }
+    return b;
+}
+
+BwdLayout compute_bwd_layout(const moe_config* c) {
+    BwdLayout L;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
+    const int E = c->n_experts, T = c->T, d = c->d_model, F = c->d_ff;
+    const size_t es = (size_t)elem_bytes(c);
+    const int ig = c->act == MOE_ACT_SWIGLU ? 2 : 1;
+    const int64_t R = max_rows_of(c);
+    L.dots = take((size_t)T * E * sizeof(float));
+    L.dg = take((size_t)n_assign(c) * sizeof(float));
+    L.dz = take((size_t)T * E * sizeof(float));
+    L.wr_part = take((size_t)moe::bwd_wr_chunks(T) * E * (d + 1) * sizeof(float));
+    L.dyp = take((size_t)R * d * es);
+    L.a = take((size_t)R * F * es);
+    L.u = take(ig == 2 ? (size_t)R * F * es : 0);
+    L.dh = take((size_t)R * F * es);
+    L.dadu = take((size_t)R * ig * F * es);
+    L.hh = take((size_t)R * F * es);
+    L.dxp = take((size_t)R * d * es);
+    L.w2t = take((size_t)E * F * d * es);
+    L.w13t = take((size_t)E * d * ig * F * es);
+    const bool sh = c->n_shared > 0;
+    const size_t Fs = sh ? (size_t)c->d_ff_shared : 0;
+    L.sa = take((size_t)T * Fs * es);
+    L.su = take((size_t)T * Fs * es);
+    L.sdh = take((size_t)T * Fs * es);
+    L.sdadu = take((size_t)T * 2 * Fs * es);
+    L.shh = take((size_t)T * Fs * es);
+    L.sdx = take(sh ? (size_t)T * d * es : 0);
+    L.sw2t = take(Fs * d * es);
+    L.sw13t = take((size_t)d * 2 * Fs * es);
+    L.plan = take(moe::ffn_tile_plan_ints(E) * sizeof(int32_t));
+    L.plan_copy = take(2 * sizeof(int32_t));
+    L.plan_s_copy = take(2 * sizeof(int32_t));
+    L.partial = take(bwd_partial_bytes_of(c));
+    L.total = o;
+    return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -483,6 +557,168 @@ moe_status moe_layer_forward(const moe_config* c, const moe_weights* w, const vo
     if (shared_out && (s = moe_shared_expert(c, x, w, shared_out, ws, ws_bytes, stream)) != MOE_OK) return s;
     const void* resid = (c->flags & MOE_F_ADD_RESIDUAL) ? x : nullptr;
     return moe_combine(c, y_perm, slot_pos, gates, resid, shared_out, out, stream);
+}
+
+moe_status moe_backward_workspace_size(const moe_config* c, size_t* bytes) {
+    const moe_status st = moe_validate_config(c);
+    if (st != MOE_OK) return st;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    *bytes = compute_bwd_layout(c).total;
+    return MOE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// C[rows][N] = A[rows][K] . B_e[N][K]^T per expert group (plain store).
+moe_status bwd_gemm(bool bf, const void* A, int64_t lda, const void* B, int64_t bstride, void* C, int64_t ldc, int N,
+                    int K, int E, int64_t rows, const int32_t* offsets, const BwdLayout& L, void* ws,
+                    int32_t* plan_copy, hipStream_t h) {
+    const moe::GemmShape g = moe::pick_gemm_shape(bf, 0, rows, E, N);
+    const hipError_t e = moe::launch_grouped_gemm(bf, 0, A, lda, B, nullptr, bstride, C, ldc, N, K, E, rows, offsets,
+                                                  at<int32_t>(ws, L.plan), plan_copy, at<float>(ws, L.partial), g.BM,
+                                                  g.BN, h);
+    return e == hipSuccess ? after_launch() : hip_status(e);
+}
+
+// Backward of one expert stack over ragged row groups (offsets, or one group
+// of `rows` rows when offsets is NULL; its offsets then go to plan_copy):
+// X [rows][d] inputs, DY [rows][d] output gradients, W1/W3 [E][F][d],
+// W2 [E][d][F].  Writes DX [rows][d] and, when dW1 is not NULL, the weight
+// gradients.  Buffers: A, U, DH, HH [rows][F], DADU [rows][ig F], W2T
+// [E][F][d], W13T [E][d][ig F].
+struct ExpertBufs {
+    void *a, *u, *dh, *dadu, *hh, *w2t, *w13t;
+};
+
+moe_status expert_backward(const moe_config* c, const void* X, const void* DY, int64_t rows, int E,
+                           const int32_t* offsets, const void* W1, const void* W3, const void* W2, int F,
+                           const ExpertBufs& b, void* DX, void* dW1, void* dW3, void* dW2, const BwdLayout& L,
+                           void* ws, int32_t* plan_copy, hipStream_t h) {
+    const bool bf = is_bf16(c);
+    const bool swiglu = c->act == MOE_ACT_SWIGLU;
+    const int ig = swiglu ? 2 : 1;
+    const int d = c->d_model;
+    const int es = elem_bytes(c);
+    moe_status s;
+    // weight copies with the other dimension contiguous: W2^T [E][F][d] and
+    // [W1^T | W3^T] [E][d][ig F]
+    moe::launch_transpose(W2, E, d, F, (int64_t)d * F, b.w2t, d, (int64_t)F * d, 0, es, h);
+    moe::launch_transpose(W1, E, F, d, (int64_t)F * d, b.w13t, (int64_t)ig * F, (int64_t)d * ig * F, 0, es, h);
+    if (swiglu)
+        moe::launch_transpose(W3, E, F, d, (int64_t)F * d, b.w13t, (int64_t)ig * F, (int64_t)d * ig * F, F, es, h);
+    // recompute a = X W1^T and u = X W3^T (the first call also builds the
+    // offsets of a single group)
+    if ((s = bwd_gemm(bf, X, d, W1, (int64_t)F * d, b.a, F, F, d, E, rows, offsets, L, ws, plan_copy, h)) != MOE_OK)
+        return s;
+    const int32_t* offs = offsets ? offsets : plan_copy;
+    if (swiglu &&
+        (s = bwd_gemm(bf, X, d, W3, (int64_t)F * d, b.u, F, F, d, E, rows, offsets, L, ws, plan_copy, h)) != MOE_OK)
+        return s;
+    // dh = DY W2
+    if ((s = bwd_gemm(bf, DY, d, b.w2t, (int64_t)F * d, b.dh, F, F, d, E, rows, offsets, L, ws, plan_copy, h)) !=
+        MOE_OK)
+        return s;
+    moe::launch_bwd_act(bf, swiglu, b.dh, b.a, b.u, offs, offsets ? E : 1, rows, F, b.dadu, b.hh, h);
+    // DX = da W1 + du W3 as one product over the concatenated reduction
+    if ((s = bwd_gemm(bf, b.dadu, (int64_t)ig * F, b.w13t, (int64_t)d * ig * F, DX, d, d, ig * F, E, rows, offsets, L,
+                      ws, plan_copy, h)) != MOE_OK)
+        return s;
+    if (!dW1) return MOE_OK;
+    hipError_t e;
+    const int Eg = offsets ? E : 1;
+    if ((e = moe::launch_gemm_tn(bf, DY, d, b.hh, F, dW2, d, F, Eg, offs, h)) != hipSuccess) return hip_status(e);
+    if ((e = moe::launch_gemm_tn(bf, b.dadu, (int64_t)ig * F, X, d, dW1, F, d, Eg, offs, h)) != hipSuccess)
+        return hip_status(e);
+    if (swiglu && (e = moe::launch_gemm_tn(bf, (const uint8_t*)b.dadu + (size_t)F * es, (int64_t)ig * F, X, d, dW3, F,
+                                           d, Eg, offs, h)) != hipSuccess)
+        return hip_status(e);
+    return after_launch();
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_backward(const moe_config* c, const moe_weights* w, const void* x, const void* dy,
+                              const moe_saved* sv, const moe_grads* g, void* ws, size_t ws_bytes, void* stream) {
+    moe_status s = moe_validate_config(c);
+    if (s != MOE_OK) return s;
+    if (!bwd_gate_supported(c) || (c->flags & MOE_F_REROUTE)) return MOE_ERR_UNSUPPORTED;
+    if (!w || !sv || !g) return MOE_ERR_INVALID_ARG;
+    const bool hashed = c->gate == MOE_GATE_HASH;
+    const bool swiglu = c->act == MOE_ACT_SWIGLU;
+    const int T = c->T, E = c->n_experts, d = c->d_model;
+    const int64_t R = max_rows_of(c);
+    if (!hashed && !w->w_router) return MOE_ERR_INVALID_ARG;
+    if (!sv->expert_offsets) return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (!x || !dy || !g->dx || !sv->topk_idx || !sv->topk_gate || !sv->slot_pos)) return MOE_ERR_INVALID_ARG;
+    if (R > 0 && (!sv->perm_src || !sv->x_perm || !sv->y_perm)) return MOE_ERR_INVALID_ARG;
+    if (!w->w_gate || !w->w_down || (swiglu && !w->w_up)) return MOE_ERR_INVALID_ARG;
+    const bool want_w = g->dw_gate || g->dw_up || g->dw_down;
+    if (want_w && (!g->dw_gate || !g->dw_down || (swiglu != (g->dw_up != nullptr)))) return MOE_ERR_INVALID_ARG;
+    const bool want_ws = g->dws_gate || g->dws_up || g->dws_down;
+    if (want_ws && (c->n_shared != 1 || !g->dws_gate || !g->dws_up || !g->dws_down)) return MOE_ERR_INVALID_ARG;
+    if (c->n_shared == 1 && T > 0 && (!w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_INVALID_ARG;
+    if (!ws) return MOE_ERR_WORKSPACE;
+    const BwdLayout L = compute_bwd_layout(c);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    hipStream_t h = (hipStream_t)stream;
+    const bool bf = is_bf16(c);
+    const int ns = slots_of(c);
+    float* dg = at<float>(ws, L.dg);
+    float* dz = hashed ? nullptr : at<float>(ws, L.dz);
+
+    // output-side rows: dy_r = g dY_t and the gate gradients
+    moe::launch_zero_f32(dg, n_assign(c), h);
+    moe::launch_bwd_rows(bf, dy, sv->y_perm, sv->perm_src, sv->expert_offsets, E, sv->topk_gate, ns, d, R,
+                         at<void>(ws, L.dyp), dg, h);
+    // routed experts
+    if (R > 0) {
+        const ExpertBufs b{at<void>(ws, L.a), at<void>(ws, L.u), at<void>(ws, L.dh), at<void>(ws, L.dadu),
+                           at<void>(ws, L.hh), at<void>(ws, L.w2t), at<void>(ws, L.w13t)};
+        if ((s = expert_backward(c, sv->x_perm, at<void>(ws, L.dyp), R, E, sv->expert_offsets, w->w_gate, w->w_up,
+                                 w->w_down, c->d_ff, b, at<void>(ws, L.dxp), want_w ? g->dw_gate : nullptr,
+                                 g->dw_up, g->dw_down, L, ws, at<int32_t>(ws, L.plan_copy), h)) != MOE_OK)
+            return s;
+    } else if (want_w) {
+        hipError_t e;
+        if ((e = moe::launch_gemm_tn(bf, nullptr, d, nullptr, c->d_ff, g->dw_down, d, c->d_ff, E,
+                                     sv->expert_offsets, h)) != hipSuccess ||
+            (e = moe::launch_gemm_tn(bf, nullptr, c->d_ff, nullptr, d, g->dw_gate, c->d_ff, d, E,
+                                     sv->expert_offsets, h)) != hipSuccess ||
+            (swiglu && (e = moe::launch_gemm_tn(bf, nullptr, c->d_ff, nullptr, d, g->dw_up, c->d_ff, d, E,
+                                                sv->expert_offsets, h)) != hipSuccess))
+            return hip_status(e);
+    }
+    // shared expert: every token, gate 1
+    const bool sh = c->n_shared == 1 && T > 0;
+    if (sh) {
+        const ExpertBufs b{at<void>(ws, L.sa), at<void>(ws, L.su), at<void>(ws, L.sdh), at<void>(ws, L.sdadu),
+                           at<void>(ws, L.shh), at<void>(ws, L.sw2t), at<void>(ws, L.sw13t)};
+        if ((s = expert_backward(c, x, dy, T, 1, nullptr, w->ws_gate, w->ws_up, w->ws_down, c->d_ff_shared, b,
+                                 at<void>(ws, L.sdx), want_ws ? g->dws_gate : nullptr, g->dws_up, g->dws_down, L, ws,
+                                 at<int32_t>(ws, L.plan_s_copy), h)) != MOE_OK)
+            return s;
+    }
+    // router: logits as the forward forms them, then dz and its products
+    if (!hashed && T > 0) {
+        float* dots = at<float>(ws, L.dots);
+        moe::launch_router_dots(bf, x, w->w_router, nullptr, T, d, E, E, dots, h);
+        moe::launch_bwd_router(dots, E, w->logit_bias, sv->topk_idx, sv->topk_gate, dg, c->gate, T, E, ns, dz, h);
+    }
+    if (g->dw_router || g->dlogit_bias) {
+        if (hashed || T == 0) {
+            if (g->dw_router) moe::launch_zero_f32(g->dw_router, (int64_t)E * d, h);
+            if (g->dlogit_bias) moe::launch_zero_f32(g->dlogit_bias, E, h);
+        } else {
+            moe::launch_bwd_wr(bf, dz, x, T, E, d, at<float>(ws, L.wr_part), g->dw_router, g->dlogit_bias, h);
+        }
+    }
+    moe::launch_bwd_dx(bf, dy, at<void>(ws, L.dxp), sv->slot_pos, ns, sh ? at<void>(ws, L.sdx) : nullptr, dz,
+                       hashed ? nullptr : w->w_router, T, E, d, (c->flags & MOE_F_ADD_RESIDUAL) != 0, g->dx, h);
+    return after_launch();
 }
 
 }  // extern "C"

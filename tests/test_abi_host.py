@@ -201,3 +201,33 @@ def test_reroute_flag_validation():
                                           group_top_k=1, reroute=True)) == UNSUPPORTED
     assert moe.workspace_size(moe.config(**base, capacity_factor=1.0, reroute=True)) > \
         moe.workspace_size(moe.config(**base, capacity_factor=1.0))
+
+
+def test_backward_validation_on_the_host():
+    """moe_layer_backward: unsupported gates and flags, missing outputs,
+    partial weight-gradient sets and a short workspace are all caught before
+    any launch (no pointer below is dereferenced)."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(0x1000)
+    big = 1 << 40
+
+    def call(c, w=None, sv=None, g=None, ws=fake, nbytes=big):
+        w = w or moe.MoeWeights(w_router=fake, w_gate=fake, w_up=fake, w_down=fake)
+        if sv is None:
+            sv = moe.MoeSaved(*([fake] * 7))
+        if g is None:
+            g = moe.MoeGrads(dx=fake)
+        return L.moe_layer_backward(ctypes.byref(c), ctypes.byref(w), fake, fake, ctypes.byref(sv), ctypes.byref(g),
+                                    ws, nbytes, None)
+
+    assert call(_cfg(gate="noisy_topk")) == UNSUPPORTED
+    assert call(_cfg(gate="hierarchical", n_groups=2, group_top_k=1)) == UNSUPPORTED
+    assert call(_cfg(capacity_factor=1.0, reroute=True)) == UNSUPPORTED
+    assert call(_cfg(), g=moe.MoeGrads()) == INVALID                              # no dx
+    assert call(_cfg(), g=moe.MoeGrads(dx=fake, dw_gate=fake)) == INVALID         # partial weight set
+    assert call(_cfg(act="relu", d_ff=256), g=moe.MoeGrads(dx=fake, dw_gate=fake, dw_up=fake, dw_down=fake)) == INVALID
+    assert call(_cfg(), g=moe.MoeGrads(dx=fake, dws_gate=fake, dws_up=fake, dws_down=fake)) == INVALID  # no shared
+    assert call(_cfg(), ws=None) == WORKSPACE
+    assert call(_cfg(), nbytes=16) == WORKSPACE
+    assert call(_cfg(), w=moe.MoeWeights(w_gate=fake, w_up=fake, w_down=fake)) == INVALID          # no router
+    assert moe.backward_workspace_size(_cfg(T=4096)) > moe.backward_workspace_size(_cfg(T=64)) > 0
