@@ -123,6 +123,9 @@ def main():
                     help="also request the balance statistics (z-loss, importance, load, seq_aux) from the route stage")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "mixtral_expert_up_hbm_traffic.md"),
                     help="rocprofv3 counter summary giving the dominant kernel's HBM bytes per launch")
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
+                    help="forward (default): the layer forward, stage by stage; backward: moe_layer_backward on the "
+                         "saved tensors of one forward (a separate JSON line with its own metric)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (counter calibration)")
     args = ap.parse_args()
@@ -174,6 +177,8 @@ def main():
     shared = torch.empty((T, d), dtype=dt, device=dev) if cfg.n_shared else None
     out = torch.empty((T, d), dtype=dt, device=dev)
     x = dinp["x"]
+    if args.which == "backward":
+        return bench_backward(args, cfg, c, dinp, w, ws, st, moe, torch)
     stages = ["route", "dispatch", "expert_up", "expert_down"] + (["shared_expert"] if shared is not None else []) + ["combine"]
 
     def step(ev):
@@ -286,6 +291,91 @@ def main():
         res["cpu_baseline"] = cpu_baseline(cfg, dinp, args.cpu_seconds)
     else:
         res["cpu_baseline"] = None
+    print(json.dumps(res))
+
+
+BACKWARD_METRIC = "MoE layer backward tokens/s (all gradients), Mixtral-shaped layer, 1 GPU"
+
+
+def bench_backward(args, cfg, c, dinp, w, ws, st, moe, torch):
+    """Time moe_layer_backward: one forward (untimed) makes the saved
+    tensors, then W warmup and K timed backward calls, each computing dx,
+    the router gradients and every expert weight gradient."""
+    import workloads
+    T, E, k, d, F = c.T, c.n_experts, moe.route_slots(c), c.d_model, c.d_ff
+    R = moe.max_rows(c)
+    dev = dinp["x"].device
+    dt = dinp["x"].dtype
+    i32 = dict(dtype=torch.int32, device=dev)
+    sv = dict(topk_idx=torch.empty((T, k), **i32), topk_gate=torch.empty((T, k), dtype=torch.float32, device=dev),
+              expert_offsets=torch.empty((E + 1,), **i32), perm_src=torch.empty((R,), **i32),
+              slot_pos=torch.empty((T, k), **i32), x_perm=torch.empty((R, d), dtype=dt, device=dev),
+              y_perm=torch.empty((R, d), dtype=dt, device=dev))
+    x = dinp["x"]
+    moe.moe_route(c, x, w, sv["topk_idx"], sv["topk_gate"], None, st, ws)
+    moe.moe_dispatch(c, x, sv["topk_idx"], sv["x_perm"], sv["expert_offsets"], sv["perm_src"], sv["slot_pos"], st,
+                     ws)
+    moe.moe_expert_ffn(c, sv["x_perm"], sv["expert_offsets"], w, sv["y_perm"], ws)
+    dy = workloads.make_output_grad(cfg, device=dev)
+    g = dict(dx=torch.empty((T, d), dtype=dt, device=dev),
+             dw_router=torch.empty((E, d), dtype=torch.float32, device=dev),
+             dlogit_bias=torch.empty((E,), dtype=torch.float32, device=dev),
+             dw_gate=torch.empty((E, F, d), dtype=dt, device=dev),
+             dw_down=torch.empty((E, d, F), dtype=dt, device=dev))
+    if cfg.act == "swiglu":
+        g["dw_up"] = torch.empty((E, F, d), dtype=dt, device=dev)
+    if cfg.n_shared:
+        fs = cfg.F_shared
+        g.update(dws_gate=torch.empty((fs, d), dtype=dt, device=dev), dws_up=torch.empty((fs, d), dtype=dt, device=dev),
+                 dws_down=torch.empty((d, fs), dtype=dt, device=dev))
+    bws = moe.backward_workspace(c)
+    for _ in range(args.warmup):
+        moe.moe_layer_backward(c, w, x, dy, sv, g, bws)
+    torch.cuda.synchronize()
+    log(f"bench: {args.warmup} warmup backward calls done, timing {args.steps}")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        moe.moe_layer_backward(c, w, x, dy, sv, g, bws)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    kept = int(sv["expert_offsets"][E].item())
+    mult = 2 if cfg.act == "swiglu" else 1
+    # matrix products of the backward: dh (1), dx (mult), dW2 (1), dW1 / dW3
+    # (mult) -- twice the forward's -- plus the recomputed a / u (mult)
+    useful = 2.0 * kept * d * F * (2 + 2 * mult)
+    recompute = 2.0 * kept * d * F * mult
+    if cfg.n_shared:
+        useful += 2.0 * T * d * cfg.F_shared * 6
+        recompute += 2.0 * T * d * cfg.F_shared * 2
+    peak_f = PEAK_MFMA_TFLOPS[cfg.act_dtype]
+    achieved = (useful + recompute) / (ms * 1e-3) / 1e12
+    res = {
+        "metric": BACKWARD_METRIC,
+        "value": T * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.act_dtype,
+        "data": "synthetic (seeded N(0,1) activations and output gradient, N(0,1/fan_in) weights)",
+        "config": {"workload": workload_desc(cfg) + " backward", "T": T, "d_model": d, "d_ff": F, "n_experts": E,
+                   "top_k": c.top_k, "parallelism": "single GPU, all experts resident"},
+        "event_ms_per_call": ms,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak_f, "unit": "TFLOP/s",
+                     "frac": achieved / peak_f, "traffic": None,
+                     "kernel": "whole backward call (all matrix products, including the recomputed a / u)",
+                     "per_launch": {"flops": useful + recompute, "useful_flops": useful, "avg_ms": ms}},
+        "rows_kept": kept,
+        "cpu_baseline": None,
+    }
     print(json.dumps(res))
 
 

@@ -52,34 +52,85 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
     return ((red[0] + red[1]) + red[2]) + red[3];
 }
 
+// Wait until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+// Workgroup barrier after this wave's LDS operations have completed; global
+// loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace
 
 // dst[b][c][coff + r] = src[b][r][c] for r < R, c < C (both multiples of
-// 64), through a 64 x 65 LDS tile.
-template <typename Tv>
-__global__ __launch_bounds__(256) void k_transpose(const Tv* __restrict__ src, int R, int C, int64_t sbatch,
-                                                   Tv* __restrict__ dst, int64_t ldd, int64_t dbatch, int coff) {
-    __shared__ Tv tile[64][65];
+// 64).  4-byte elements: one element per access through a 64 x 65 LDS tile.
+__global__ __launch_bounds__(256) void k_transpose(const float* __restrict__ src, int R, int C, int64_t sbatch,
+                                                   float* __restrict__ dst, int64_t ldd, int64_t dbatch, int coff) {
+    __shared__ float tile[64][65];
     const int b = blockIdx.z;
-    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-    const Tv* s = src + (int64_t)b * sbatch;
-    Tv* d = dst + (int64_t)b * dbatch;
+    const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+    const float* s = src + (int64_t)b * sbatch;
+    float* d = dst + (int64_t)b * dbatch;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     for (int i = ty; i < 64; i += 4) tile[i][tx] = s[(int64_t)(r0 + i) * C + c0 + tx];
     __syncthreads();
     for (int i = ty; i < 64; i += 4) d[(int64_t)(c0 + i) * ldd + coff + r0 + tx] = tile[tx][i];
 }
 
+// 2-byte elements, 16 bytes per access: a 64 x 64 tile goes through LDS
+// with its 16-byte column groups at slot g ^ ((r >> 3) & 7) in row r, so
+// the row-wise stores and the column-wise gathers both spread over banks.
+__global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict__ src, int R, int C, int64_t sbatch,
+                                                     uint16_t* __restrict__ dst, int64_t ldd, int64_t dbatch,
+                                                     int coff) {
+    __shared__ __align__(16) uint16_t tile[64 * 64];
+    const int b = blockIdx.z;
+    const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+    const uint16_t* s = src + (int64_t)b * sbatch;
+    uint16_t* d = dst + (int64_t)b * dbatch;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = (t >> 3) + 32 * h, g = t & 7;
+        const u32x4_t v = *(const u32x4_t*)(s + (int64_t)(r0 + r) * C + c0 + g * 8);
+        *(u32x4_t*)(tile + r * 64 + ((g ^ ((r >> 3) & 7)) << 3)) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int oc = (t >> 3) + 32 * h, rg = t & 7;     // output row oc, source rows rg*8 .. +7
+        u32x4_t v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ra = rg * 8 + 2 * q, rb = ra + 1;
+            const uint32_t lo = tile[ra * 64 + ((((oc >> 3) ^ ((ra >> 3) & 7)) << 3) | (oc & 7))];
+            const uint32_t hi = tile[rb * 64 + ((((oc >> 3) ^ ((rb >> 3) & 7)) << 3) | (oc & 7))];
+            v[q] = lo | (hi << 16);
+        }
+        *(u32x4_t*)(d + (int64_t)(c0 + oc) * ldd + coff + r0 + rg * 8) = v;
+    }
+}
+
 void launch_transpose(const void* src, int B, int R, int C, int64_t sbatch, void* dst, int64_t ldd, int64_t dbatch,
                       int coff, int elem_bytes, hipStream_t s) {
     if (B <= 0 || R <= 0 || C <= 0) return;
-    dim3 grid(C / 64, R / 64, B);
+    // consecutive blocks take consecutive source row blocks, so the blocks
+    // in flight write one stretch of each destination row (a power-of-two
+    // destination stride would otherwise land them all on one channel)
+    dim3 grid(R / 64, C / 64, B);
     if (elem_bytes == 2)
-        hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)src, R, C, sbatch,
-                           (uint16_t*)dst, ldd, dbatch, coff);
-    else
-        hipLaunchKernelGGL(k_transpose<float>, grid, dim3(256), 0, s, (const float*)src, R, C, sbatch, (float*)dst,
+        hipLaunchKernelGGL(k_transpose16, grid, dim3(256), 0, s, (const uint16_t*)src, R, C, sbatch, (uint16_t*)dst,
                            ldd, dbatch, coff);
+    else
+        hipLaunchKernelGGL(k_transpose, grid, dim3(256), 0, s, (const float*)src, R, C, sbatch, (float*)dst, ldd,
+                           dbatch, coff);
 }
 
 // One block per permuted row r < offsets[E]; a = perm_src[r], t = a / slots.
@@ -375,8 +426,213 @@ __global__ __launch_bounds__(256) void k_gemm_tn(TnParams p) {
 #endif
 }
 
+// bf16, 256 x 256 tiles, 512 threads: 8 waves of 64 (m) x 128 (n), so a
+// wave holds 128 accumulator registers and two waves share each SIMD;
+// chunks of 64 rows through two LDS buffers of 64 KB.  Threads 0-255 stage
+// an 8 x 8 block of A per chunk, threads 256-511 one of B, and write it
+// transposed into LDS (the schedule is given at the main loop).  Chunks past
+// the expert's rows read zeros (outside the buffer descriptor's range), so
+// the loop body has no branches.  Blocks map to tiles XCD by XCD, so the
+// tiles of one XCD share an expert's rows in L2.
+__global__ __launch_bounds__(512) void k_gemm_tn256(TnParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int BM = 256, KC = 64;
+    constexpr int OPB = BM * KC * 2;
+    __shared__ __align__(16) uint8_t lds[2 * 2 * OPB];
+    const int ntiles = p.E * p.tiles_m * p.tiles_n;
+    const int per_xcd = (ntiles + 7) / 8;
+    const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (tile >= ntiles) return;
+    const int per_e = p.tiles_m * p.tiles_n;
+    const int e = tile / per_e;
+    // inside an expert, groups of GM row tiles: the 32 CUs of an XCD run
+    // 4 row tiles x 8 column tiles at a time, so each staged chunk of A is
+    // fetched once per 8 tiles and each chunk of B once per 4
+    constexpr int GM = 4;
+    const int L = tile - e * per_e;
+    const int grp = L / (GM * p.tiles_n);
+    const int tm0 = grp * GM;
+    const int gm = min(p.tiles_m - tm0, GM);
+    const int in = L - grp * GM * p.tiles_n;
+    const int tm = tm0 + in % gm, tn = in / gm;
+    const int m_base = tm * BM, n_base = tn * BM;
+    const int lo = p.offsets[e], hi = p.offsets[e + 1];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nch = (hi - lo + KC - 1) / KC;
+
+    // staging: operand op (0: A, 1: B) of this thread, rows kq*8 .. +7 of
+    // the chunk, columns cg*8 .. +7 of the tile
+    const int op = wave >> 2;
+    const int cg = tid & 31, kq = (tid >> 5) & 7;
+    constexpr int kRsrcWord3 = 0x00020000;
+    const void* src = op == 0 ? p.A : p.B;
+    const int64_t ld = op == 0 ? p.lda : p.ldb;
+    const int col = (op == 0 ? m_base : n_base) + cg * 8;
+    const int lim = op == 0 ? p.M : p.N;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint16_t*)src + (int64_t)lo * ld), (short)0, (int)((int64_t)(hi - lo) * ld * 2), kRsrcWord3);
+    const uint32_t vo = col < lim ? (uint32_t)((kq * 8 * ld + col) * 2) : 0x80000000u;
+    const int row_bytes = (int)(ld * 2);
+    u32x4_t st[8];
+    auto load_row = [&](int ch, int i) __attribute__((always_inline)) {
+        st[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, (ch * KC + i) * row_bytes, 0));
+    };
+    // LDS layout of one operand in one buffer: row m (0..255) holds the 64
+    // k of the chunk as 8 groups of 8 (16 bytes), group g at slot
+    // g ^ (m & 7) ^ ((m >> 3) & 7).  (The swizzle g ^ ((m >> 1) & 7) makes
+    // the fragment reads conflict-free but not these transposed writes;
+    // measured on MI355X this one is the faster of the two.)
+    //
+    // Staged writes: column j of the thread's 8 x 8 block goes to row
+    // m = 8 cg + jj, jj = j ^ p with p = (cg >> 3) & 1, so each 16 lanes of a
+    // store cover rows of both parities; the slot is kq ^ jj ^ (cg & 7).
+    const int pbit = (cg >> 3) & 1;
+    const uint32_t w_lane = (uint32_t)(cg * 1024);
+    const int w_x = (kq ^ (cg & 7)) & 7;           // slot = w_x ^ jj
+    // v_perm selectors: column jj takes the low (jj even) or high halves of
+    // rows 2q and 2q + 1
+    const uint32_t sel_lo = 0x05040100u, sel_hi = 0x07060302u;
+    const uint32_t sel_j_even = pbit ? sel_hi : sel_lo, sel_j_odd = pbit ? sel_lo : sel_hi;
+    auto put_col = [&](int buf, int j) __attribute__((always_inline)) {
+        const uint32_t sel = (j & 1) ? sel_j_odd : sel_j_even;
+        u32x4_t v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = __builtin_amdgcn_perm(st[2 * q + 1][j >> 1], st[2 * q][j >> 1], sel);
+        const int jj = j ^ pbit;
+        const uint32_t off = w_lane + (uint32_t)(jj << 7) + (uint32_t)((w_x ^ jj) << 4);
+        *(u32x4_t*)(lds + (size_t)(buf * 2 + op) * OPB + off) = v;
+    };
+    // Fragment reads: row = R0 + (lane & 15) with R0 a multiple of 16, group
+    // g = 4 ks + (lane >> 4), so the slot is L ^ K with the lane part
+    // L = (lane >> 4) ^ (lane & 7) ^ ((lane >> 3) & 1) and the compile-time
+    // K = 4 ks ^ ((R0 >> 3) & 7) = 4 ks ^ ((2 blk) & 7).  The eight lane
+    // offsets (lane & 15) 128 + ((L ^ K) << 4) are formed once per chunk
+    // with the buffer base folded in; R0 128 and the operand base are
+    // immediates.
+    const int Lx = ((lane >> 4) ^ (lane & 7) ^ ((lane >> 3) & 1)) & 7;
+    const uint32_t r_lane = (uint32_t)((lane & 15) * 128);
+    uint32_t rb[8];
+    auto set_read_base = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int K = 0; K < 8; ++K) rb[K] = (uint32_t)(buf * 2 * OPB) + r_lane + (uint32_t)((Lx ^ K) << 4);
+    };
+    // buffer b: rb holds b's base; the other buffer is rb ^ (2 OPB)
+    auto frag = [&](int other, int opf, int ks, int blk) __attribute__((always_inline)) {
+        const int K = (4 * ks) ^ ((2 * blk) & 7);
+        const int R0 = (opf == 0 ? wm * 64 : wn * 128) + blk * 16;
+        const uint32_t a = (other ? (rb[K] ^ (uint32_t)(2 * OPB)) : rb[K]) + (uint32_t)(opf * OPB + R0 * 128);
+        return *(const u32x4_t*)(lds + a);
+    };
+    floatx4_t acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // B fragment of group q of the current chunk: k-step q >> 3, n-block
+    // q & 7; groups 16.. are the next chunk's (the other buffer)
+    auto bfrag = [&](int q) __attribute__((always_inline)) {
+        return q < 16 ? frag(0, 1, q >> 3, q & 7) : frag(1, 1, 0, q - 16);
+    };
+    // prologue: chunk 0 into buffer 0, chunk 1 staged, chunk 0's first
+    // A fragments and first two B fragments in registers
+#pragma unroll
+    for (int i = 0; i < 8; ++i) load_row(0, i);
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) put_col(0, j);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) load_row(1, i);
+    lds_barrier();
+    set_read_base(0);
+    u32x4_t fa0[4], fa1[4], fb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fa0[j] = frag(0, 0, 0, j);
+    fb[0] = bfrag(0);
+    fb[1] = bfrag(1);
+    // chunk ch (buffer b): 16 groups q of 4 MFMAs (k-step q >> 3, n-block
+    // q & 7, against the wave's 4 m-blocks); the B fragment of group q + 2
+    // is read during group q into slot (q + 2) % 4 (16 groups per chunk keep
+    // the slots aligned from one chunk to the next).  Groups 0-1 write the
+    // staged chunk ch+1 into buffer b^1, groups 2-5 issue the loads of chunk
+    // ch+2, groups 4-7 read the second k-step's A fragments.  One barrier,
+    // after group 13, when every read of buffer b has been issued: chunk
+    // ch+1 is then visible, so groups 14-15 read its first fragments and the
+    // next chunk starts without waiting; and buffer b is free for the writes
+    // of the next chunk.
+    for (int ch = 0; ch < nch; ++ch) {
+        const int b = ch & 1;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int ks = q >> 3, i = q & 7;
+            if (ks == 0) {
+                if (i == 0) wait_vmcnt<0>();
+                if (i < 2) {
+#pragma unroll
+                    for (int j = 4 * i; j < 4 * i + 4; ++j) put_col(b ^ 1, j);
+                } else if (i < 6) {
+                    load_row(ch + 2, 2 * (i - 2));
+                    load_row(ch + 2, 2 * (i - 2) + 1);
+                }
+                if (i >= 4) fa1[i - 4] = frag(0, 0, 1, i - 4);
+            } else if (i >= 6) {
+                fa0[2 * (i - 6)] = frag(1, 0, 0, 2 * (i - 6));
+                fa0[2 * (i - 6) + 1] = frag(1, 0, 0, 2 * (i - 6) + 1);
+            }
+            fb[(q + 2) % 4] = bfrag(q + 2);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fb[q % 4]),
+                                                                    __builtin_bit_cast(bf16x8_t, ks ? fa1[j] : fa0[j]),
+                                                                    acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q == 13) {
+                lds_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        set_read_base(b ^ 1);
+    }
+    // lane holds C[m][n .. n+3] of block (n-block i, m-block j)
+    uint16_t* Ce = (uint16_t*)p.C + (size_t)e * p.M * p.N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int m = m_base + wm * 64 + j * 16 + (lane & 15);
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int n = n_base + wn * 128 + i * 16 + 4 * (lane >> 4);
+            if (n >= p.N) continue;
+            uint2 w;
+            w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+            w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+            *(uint2*)(Ce + (int64_t)m * p.N + n) = w;
+        }
+    }
+#endif
+}
+
 hipError_t launch_gemm_tn(bool bf16, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int M, int N,
-                          int E, const int32_t* offsets, hipStream_t s) {
+                          int E, const int32_t* offsets, int64_t max_rows, hipStream_t s) {
+    // the 256 x 256 kernel addresses an expert's rows (plus two chunks of
+    // read-ahead) with 32-bit buffer offsets
+    const int64_t ldmax = lda > ldb ? lda : ldb;
+    if (bf16 && M >= 256 && N >= 256 && (max_rows + 128) * ldmax * 2 < ((int64_t)1 << 31)) {
+        TnParams p;
+        p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.C = C;
+        p.M = M; p.N = N; p.E = E;
+        p.tiles_m = (M + 255) / 256;
+        p.tiles_n = (N + 255) / 256;
+        p.offsets = offsets;
+        const int64_t nt = (int64_t)E * p.tiles_m * p.tiles_n;
+        if (nt <= 0) return hipSuccess;
+        if (nt > 0x7fffffff - 8) return hipErrorInvalidValue;
+        const int64_t grid = (nt + 7) / 8 * 8;
+        hipLaunchKernelGGL(k_gemm_tn256, dim3((unsigned)grid), dim3(512), 0, s, p);
+        return hipGetLastError();
+    }
     TnParams p;
     p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.C = C;
     p.M = M; p.N = N; p.E = E;

@@ -90,9 +90,10 @@ void launch_bwd_rows(bool bf16, const void* dy, const void* y_perm, const int32_
 // (offsets == NULL: the first max_rows rows).
 void launch_bwd_act(bool bf16, bool swiglu, const void* dh, const void* a, const void* u, const int32_t* offsets,
                     int E, int64_t max_rows, int F, void* dadu, void* h, hipStream_t s);
-// C_e[M][N] = sum over the rows r of expert e of A[r][m] B[r][n].
+// C_e[M][N] = sum over the rows r of expert e of A[r][m] B[r][n]; max_rows
+// bounds every expert's row count.
 hipError_t launch_gemm_tn(bool bf16, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int M, int N,
-                          int E, const int32_t* offsets, hipStream_t s);
+                          int E, const int32_t* offsets, int64_t max_rows, hipStream_t s);
 void launch_bwd_router(const float* dots, int NC, const float* logit_bias, const int32_t* idx, const float* gates,
                        const float* dg, int gate, int T, int E, int slots, float* dz, hipStream_t s);
 void launch_bwd_dx(bool bf16, const void* dy, const void* dx_perm, const int32_t* slot_pos, int slots,

@@ -628,11 +628,12 @@ moe_status expert_backward(const moe_config* c, const void* X, const void* DY, i
     if (!dW1) return MOE_OK;
     hipError_t e;
     const int Eg = offsets ? E : 1;
-    if ((e = moe::launch_gemm_tn(bf, DY, d, b.hh, F, dW2, d, F, Eg, offs, h)) != hipSuccess) return hip_status(e);
-    if ((e = moe::launch_gemm_tn(bf, b.dadu, (int64_t)ig * F, X, d, dW1, F, d, Eg, offs, h)) != hipSuccess)
+    if ((e = moe::launch_gemm_tn(bf, DY, d, b.hh, F, dW2, d, F, Eg, offs, rows, h)) != hipSuccess)
+        return hip_status(e);
+    if ((e = moe::launch_gemm_tn(bf, b.dadu, (int64_t)ig * F, X, d, dW1, F, d, Eg, offs, rows, h)) != hipSuccess)
         return hip_status(e);
     if (swiglu && (e = moe::launch_gemm_tn(bf, (const uint8_t*)b.dadu + (size_t)F * es, (int64_t)ig * F, X, d, dW3, F,
-                                           d, Eg, offs, h)) != hipSuccess)
+                                           d, Eg, offs, rows, h)) != hipSuccess)
         return hip_status(e);
     return after_launch();
 }
@@ -685,11 +686,11 @@ moe_status moe_layer_backward(const moe_config* c, const moe_weights* w, const v
     } else if (want_w) {
         hipError_t e;
         if ((e = moe::launch_gemm_tn(bf, nullptr, d, nullptr, c->d_ff, g->dw_down, d, c->d_ff, E,
-                                     sv->expert_offsets, h)) != hipSuccess ||
+                                     sv->expert_offsets, 0, h)) != hipSuccess ||
             (e = moe::launch_gemm_tn(bf, nullptr, c->d_ff, nullptr, d, g->dw_gate, c->d_ff, d, E,
-                                     sv->expert_offsets, h)) != hipSuccess ||
+                                     sv->expert_offsets, 0, h)) != hipSuccess ||
             (swiglu && (e = moe::launch_gemm_tn(bf, nullptr, c->d_ff, nullptr, d, g->dw_up, c->d_ff, d, E,
-                                                sv->expert_offsets, h)) != hipSuccess))
+                                                sv->expert_offsets, 0, h)) != hipSuccess))
             return hip_status(e);
     }
     // shared expert: every token, gate 1
