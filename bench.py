@@ -298,9 +298,10 @@ BACKWARD_METRIC = "MoE layer backward tokens/s (all gradients), Mixtral-shaped l
 
 
 def bench_backward(args, cfg, c, dinp, w, ws, st, moe, torch):
-    """Time moe_layer_backward: one forward (untimed) makes the saved
-    tensors, then W warmup and K timed backward calls, each computing dx,
-    the router gradients and every expert weight gradient."""
+    """Time moe_layer_backward: one training forward (untimed; its up
+    projection keeps the pre-activations) makes the saved tensors, then W
+    warmup and K timed backward calls, each computing dx, the router
+    gradients and every expert weight gradient."""
     import workloads
     T, E, k, d, F = c.T, c.n_experts, moe.route_slots(c), c.d_model, c.d_ff
     R = moe.max_rows(c)
@@ -315,7 +316,11 @@ def bench_backward(args, cfg, c, dinp, w, ws, st, moe, torch):
     moe.moe_route(c, x, w, sv["topk_idx"], sv["topk_gate"], None, st, ws)
     moe.moe_dispatch(c, x, sv["topk_idx"], sv["x_perm"], sv["expert_offsets"], sv["perm_src"], sv["slot_pos"], st,
                      ws)
-    moe.moe_expert_ffn(c, sv["x_perm"], sv["expert_offsets"], w, sv["y_perm"], ws)
+    H = torch.empty((R, F), dtype=dt, device=dev)
+    sv["pre_act"] = torch.empty((R, (2 if cfg.act == "swiglu" else 1) * F), dtype=dt, device=dev)
+    moe.moe_expert_up_train(c, sv["x_perm"], sv["expert_offsets"], w, H, sv["pre_act"], ws)
+    moe.moe_expert_down(c, H, sv["expert_offsets"], w, sv["y_perm"], ws)
+    del H
     dy = workloads.make_output_grad(cfg, device=dev)
     g = dict(dx=torch.empty((T, d), dtype=dt, device=dev),
              dw_router=torch.empty((E, d), dtype=torch.float32, device=dev),
@@ -345,9 +350,10 @@ def bench_backward(args, cfg, c, dinp, w, ws, st, moe, torch):
     kept = int(sv["expert_offsets"][E].item())
     mult = 2 if cfg.act == "swiglu" else 1
     # matrix products of the backward: dh (1), dx (mult), dW2 (1), dW1 / dW3
-    # (mult) -- twice the forward's -- plus the recomputed a / u (mult)
+    # (mult) -- twice the forward's; the routed a / u come saved from the
+    # forward, the shared expert's are recomputed
     useful = 2.0 * kept * d * F * (2 + 2 * mult)
-    recompute = 2.0 * kept * d * F * mult
+    recompute = 0.0
     if cfg.n_shared:
         useful += 2.0 * T * d * cfg.F_shared * 6
         recompute += 2.0 * T * d * cfg.F_shared * 2
@@ -371,7 +377,7 @@ def bench_backward(args, cfg, c, dinp, w, ws, st, moe, torch):
         "event_ms_per_call": ms,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak_f, "unit": "TFLOP/s",
                      "frac": achieved / peak_f, "traffic": None,
-                     "kernel": "whole backward call (all matrix products, including the recomputed a / u)",
+                     "kernel": "whole backward call (all matrix products; pre-activations saved by the forward)",
                      "per_launch": {"flops": useful + recompute, "useful_flops": useful, "avg_ms": ms}},
         "rows_kept": kept,
         "cpu_baseline": None,

@@ -290,6 +290,14 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32
  * Same layouts and ownership as moe_expert_ffn; h is caller-owned here. */
 moe_status moe_expert_up(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
                          const moe_weights* w, void* h, void* ws, size_t ws_bytes, void* stream);
+/* moe_expert_up for training: also stores the pre-activations
+ * pre_act[r] = [a | u] (SwiGLU, a = x_perm[r] W1_e^T, u = x_perm[r] W3_e^T,
+ * row stride 2 d_ff) or a (ReLU, row stride d_ff), in the act dtype, from
+ * the same fp32 accumulators as h.  moe_layer_backward reads them (through
+ * moe_saved.pre_act) instead of recomputing the two products. */
+moe_status moe_expert_up_train(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                               const moe_weights* w, void* h, void* pre_act, void* ws, size_t ws_bytes,
+                               void* stream);
 moe_status moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
                            const moe_weights* w, void* y_perm, void* ws, size_t ws_bytes, void* stream);
 
@@ -338,6 +346,8 @@ typedef struct {
     const int32_t* slot_pos;        /* [T][slots] */
     const void* x_perm;             /* [max_rows][d] act dtype */
     const void* y_perm;             /* [max_rows][d] act dtype: expert outputs before the gate */
+    const void* pre_act;            /* [max_rows][2 d_ff] (a | u; ReLU: [max_rows][d_ff], a) act dtype from
+                                       moe_expert_up_train, or NULL: the backward then recomputes a and u */
 } moe_saved;
 
 /* Gradient outputs (device pointers).  dx is required; every other member

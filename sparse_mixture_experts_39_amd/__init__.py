@@ -19,7 +19,7 @@ __all__ = [
     "workspace", "max_rows", "capacity", "validate_config", "workspace_size",
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_shared_expert",
     "moe_combine", "moe_layer_forward", "MoeSaved", "MoeGrads", "backward_workspace_size", "backward_workspace",
-    "moe_layer_backward",
+    "moe_layer_backward", "moe_expert_up_train",
     "EXPORTED_SYMBOLS", "LIB_PATH",
 ]
 
@@ -37,7 +37,7 @@ EXPORTED_SYMBOLS = (
     "moe_last_hip_error",
     "moe_status_string", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
     "moe_shared_expert", "moe_combine", "moe_layer_forward", "moe_update_bias",
-    "moe_backward_workspace_size", "moe_layer_backward",
+    "moe_backward_workspace_size", "moe_layer_backward", "moe_expert_up_train",
 )
 
 
@@ -76,7 +76,7 @@ class MoeStats(ctypes.Structure):
 
 class MoeSaved(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "topk_idx", "topk_gate", "expert_offsets", "perm_src", "slot_pos", "x_perm", "y_perm")]
+        "topk_idx", "topk_gate", "expert_offsets", "perm_src", "slot_pos", "x_perm", "y_perm", "pre_act")]
 
 
 class MoeGrads(ctypes.Structure):
@@ -129,6 +129,8 @@ def lib():
         L.moe_layer_forward.argtypes = [C, W, P, P, S, P, sz, P]
         L.moe_update_bias.restype = ctypes.c_int
         L.moe_update_bias.argtypes = [C, P, ctypes.c_float, P, P]
+        L.moe_expert_up_train.restype = ctypes.c_int
+        L.moe_expert_up_train.argtypes = [C, P, P, W, P, P, P, sz, P]
         L.moe_backward_workspace_size.restype = ctypes.c_int
         L.moe_backward_workspace_size.argtypes = [C, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_layer_backward.restype = ctypes.c_int
@@ -315,6 +317,19 @@ def moe_expert_up(c: MoeConfig, x_perm, expert_offsets, w: MoeWeights, h, ws=Non
     _check("moe_expert_up", rc)
 
 
+def moe_expert_up_train(c: MoeConfig, x_perm, expert_offsets, w: MoeWeights, h, pre_act, ws=None, stream=None):
+    """moe_expert_up that also stores the pre-activations [a | u] (SwiGLU) or a
+    (ReLU) for the backward."""
+    R, d, E, F = max_rows(c), c.d_model, c.n_experts, c.d_ff
+    ig = 2 if c.act == ACTS["swiglu"] else 1
+    rc = lib().moe_expert_up_train(ctypes.byref(c), _ptr(x_perm, _dt(c), (R, d), "x_perm"),
+                                   _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"), ctypes.byref(w),
+                                   _ptr(h, _dt(c), (R, F), "h"), _ptr(pre_act, _dt(c), (R, ig * F), "pre_act"),
+                                   _ptr(ws, torch.uint8, name="ws"), ws.numel() if ws is not None else 0,
+                                   _stream(stream))
+    _check("moe_expert_up_train", rc)
+
+
 def moe_expert_down(c: MoeConfig, h, expert_offsets, w: MoeWeights, y_perm, ws=None, stream=None):
     R, d, E, F = max_rows(c), c.d_model, c.n_experts, c.d_ff
     rc = lib().moe_expert_down(ctypes.byref(c), _ptr(h, _dt(c), (R, F), "h"),
@@ -393,6 +408,8 @@ def moe_layer_backward(c: MoeConfig, w: MoeWeights, x, dy, saved: Dict[str, torc
     sv.slot_pos = _ptr(saved.get("slot_pos"), torch.int32, (T, k), "slot_pos")
     sv.x_perm = _ptr(saved.get("x_perm"), dt, (R, d), "x_perm")
     sv.y_perm = _ptr(saved.get("y_perm"), dt, (R, d), "y_perm")
+    ig = 2 if c.act == ACTS["swiglu"] else 1
+    sv.pre_act = _ptr(saved.get("pre_act"), dt, (R, ig * F), "pre_act")
     g = MoeGrads()
     g.dx = _ptr(grads.get("dx"), dt, (T, d), "dx")
     g.dw_router = _ptr(grads.get("dw_router"), torch.float32, (E, d), "dw_router")

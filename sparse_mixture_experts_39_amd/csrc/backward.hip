@@ -179,15 +179,16 @@ void launch_bwd_rows(bool bf16, const void* dy, const void* y_perm, const int32_
 }
 
 // Activation derivative on rows < rows_end (= offsets[E], or n_rows when
-// offsets is NULL), 4 columns per thread.  SwiGLU: h = SiLU(a) u,
+// offsets is NULL), 4 columns per thread; a and u have row stride ld_au.
+// SwiGLU: h = SiLU(a) u,
 // da = dh u s (1 + a (1 - s)) with s = sigmoid(a), du = dh SiLU(a); ReLU:
 // h = relu(a), da = dh [a > 0].  da goes to dadu[r][0..F), du to
 // dadu[r][F..2F).
 template <bool BF16, bool SWIGLU>
 __global__ __launch_bounds__(256) void k_bwd_act(const void* __restrict__ dh, const void* __restrict__ a_in,
-                                                 const void* __restrict__ u_in, const int32_t* __restrict__ offsets,
-                                                 int E, int n_rows, int F, void* __restrict__ dadu,
-                                                 void* __restrict__ h_out) {
+                                                 const void* __restrict__ u_in, int64_t ld_au,
+                                                 const int32_t* __restrict__ offsets, int E, int n_rows, int F,
+                                                 void* __restrict__ dadu, void* __restrict__ h_out) {
     const int64_t rows_end = offsets ? offsets[E] : n_rows;
     const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     const int64_t r = i4 / F;
@@ -197,10 +198,11 @@ __global__ __launch_bounds__(256) void k_bwd_act(const void* __restrict__ dh, co
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int64_t i = i4 + q;
+        const int64_t ia = r * ld_au + c + q;
         const float g = load_act<BF16>(dh, i);
-        const float av = load_act<BF16>(a_in, i);
+        const float av = load_act<BF16>(a_in, ia);
         if constexpr (SWIGLU) {
-            const float uv = load_act<BF16>(u_in, i);
+            const float uv = load_act<BF16>(u_in, ia);
             const float sg = 1.0f / (1.0f + __expf(-av));
             const float silu = av * sg;
             store_act<BF16>(dadu, r * ldo + c + q, g * uv * sg * (1.0f + av * (1.0f - sg)));
@@ -213,13 +215,13 @@ __global__ __launch_bounds__(256) void k_bwd_act(const void* __restrict__ dh, co
     }
 }
 
-void launch_bwd_act(bool bf16, bool swiglu, const void* dh, const void* a, const void* u, const int32_t* offsets,
-                    int E, int64_t max_rows, int F, void* dadu, void* h, hipStream_t s) {
+void launch_bwd_act(bool bf16, bool swiglu, const void* dh, const void* a, const void* u, int64_t ld_au,
+                    const int32_t* offsets, int E, int64_t max_rows, int F, void* dadu, void* h, hipStream_t s) {
     const int64_t n4 = max_rows * F / 4;
     if (n4 <= 0) return;
     const dim3 grid((unsigned)((n4 + 255) / 256));
     const int nr = (int)max_rows;
-#define MOE_ACT_ARGS dh, a, u, offsets, E, nr, F, dadu, h
+#define MOE_ACT_ARGS dh, a, u, ld_au, offsets, E, nr, F, dadu, h
     if (bf16) {
         if (swiglu) hipLaunchKernelGGL((k_bwd_act<true, true>), grid, dim3(256), 0, s, MOE_ACT_ARGS);
         else hipLaunchKernelGGL((k_bwd_act<true, false>), grid, dim3(256), 0, s, MOE_ACT_ARGS);

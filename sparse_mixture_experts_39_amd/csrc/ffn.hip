@@ -52,7 +52,14 @@
 
 namespace moe {
 
-enum { EPI_STORE = 0, EPI_RELU = 1, EPI_SWIGLU = 2 };
+// Epilogues.  The _SAVE forms also store the pre-activations (a, and u for
+// SwiGLU) to C2 (row stride ldc2; u at column offset N), which a training
+// forward keeps for the backward.
+enum { EPI_STORE = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_SWIGLU_SAVE = 3, EPI_RELU_SAVE = 4 };
+
+constexpr bool epi_swiglu(int e) { return e == EPI_SWIGLU || e == EPI_SWIGLU_SAVE; }
+constexpr bool epi_relu(int e) { return e == EPI_RELU || e == EPI_RELU_SAVE; }
+constexpr bool epi_save(int e) { return e == EPI_SWIGLU_SAVE || e == EPI_RELU_SAVE; }
 
 struct GemmParams {
     const void* A;
@@ -70,6 +77,8 @@ struct GemmParams {
     const int32_t* offsets; // [E+1]
     const int32_t* plan;    // [E+1] tile prefix over experts, then full, split, tail
     float* partial;         // split-K partial accumulators
+    void* C2;               // pre-activations (_SAVE epilogues)
+    int64_t ldc2;
 };
 
 // Work decomposition.  The plan lists ceil(M_e / BM) row tiles per expert,
@@ -174,24 +183,25 @@ struct GemmEpilogue {
     // Column groups of the epilogue: the 16-row blocks i of the wave's B tile
     // are independent, except that SwiGLU pairs block 2p (gate) with block
     // 2p+1 (up).
-    static constexpr int IG = EPI == EPI_SWIGLU ? 2 : 1;
+    static constexpr int IG = epi_swiglu(EPI) ? 2 : 1;
 
     // Output of blocks i0 .. i0+IG-1 (acc[0 .. IG-1]).  In a 16x16 block,
     // lane l, element t holds D[n = 4(l/16) + t][m = l % 16]: a lane owns 4
     // consecutive output columns of one row and stores them at once.
     __device__ static void store_cols(const GemmParams& p, const acc_t (*acc)[FM], int i0, int row0, int rows, int nt,
                                       int wm, int wn, int lane) {
-        auto store4 = [&](int m, int64_t col, const float* v) {
-            const int64_t o = (int64_t)(row0 + m) * p.ldc + col;
+        auto store4_to = [&](void* dst, int64_t ld, int m, int64_t col, const float* v) {
+            const int64_t o = (int64_t)(row0 + m) * ld + col;
             if constexpr (BF16) {
                 uint2 w;
                 w.x = pack_bf16x2(v[0], v[1]);
                 w.y = pack_bf16x2(v[2], v[3]);
-                *(uint2*)((uint16_t*)p.C + o) = w;
+                *(uint2*)((uint16_t*)dst + o) = w;
             } else {
-                *(float4*)((float*)p.C + o) = make_float4(v[0], v[1], v[2], v[3]);
+                *(float4*)((float*)dst + o) = make_float4(v[0], v[1], v[2], v[3]);
             }
         };
+        auto store4 = [&](int m, int64_t col, const float* v) { store4_to(p.C, p.ldc, m, col, v); };
         auto silu_mul = [](float gt, float up) { return gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up; };
         {
             const int lg = lane >> 4;
@@ -199,21 +209,39 @@ struct GemmEpilogue {
             for (int j = 0; j < FM; ++j) {
                 const int m = wm * WM + j * 16 + (lane & 15);
                 if (m >= rows) continue;
-                if constexpr (EPI == EPI_SWIGLU) {
+                if constexpr (epi_swiglu(EPI)) {
                     const int fblock = (wn * FN + i0) >> 1;        // 16-row blocks alternate gate / up
                     float v[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) v[t] = silu_mul(acc[0][j][t], acc[1][j][t]);
-                    store4(m, (int64_t)nt * (BN / 2) + fblock * 16 + 4 * lg, v);
+                    const int64_t col = (int64_t)nt * (BN / 2) + fblock * 16 + 4 * lg;
+                    store4(m, col, v);
+                    if constexpr (epi_save(EPI)) {
+                        float a[4], u[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            a[t] = acc[0][j][t];
+                            u[t] = acc[1][j][t];
+                        }
+                        store4_to(p.C2, p.ldc2, m, col, a);
+                        store4_to(p.C2, p.ldc2, m, p.N + col, u);
+                    }
                 } else {
                     float v[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         float x = acc[0][j][t];
-                        if constexpr (EPI == EPI_RELU) x = fmaxf(x, 0.0f);
+                        if constexpr (epi_relu(EPI)) x = fmaxf(x, 0.0f);
                         v[t] = x;
                     }
-                    store4(m, (int64_t)nt * BN + wn * WN + i0 * 16 + 4 * lg, v);
+                    const int64_t col = (int64_t)nt * BN + wn * WN + i0 * 16 + 4 * lg;
+                    store4(m, col, v);
+                    if constexpr (epi_save(EPI)) {
+                        float a[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) a[t] = acc[0][j][t];
+                        store4_to(p.C2, p.ldc2, m, col, a);
+                    }
                 }
             }
         }
@@ -242,7 +270,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     typedef GemmEpilogue<BF16, BM, BN, EPI> Epi;
     typedef typename Epi::acc_t acc_t;
     static_assert(FM >= 1 && FN >= 1, "tile smaller than one MFMA block");
-    static_assert(EPI != EPI_SWIGLU || (FN % 2) == 0, "SwiGLU pairs 16-row blocks");
+    static_assert(!epi_swiglu(EPI) || (FN % 2) == 0, "SwiGLU pairs 16-row blocks");
     static_assert(RD.wait0 < 64 && RD.bytes <= 160 * 1024, "ring exceeds vmcnt or LDS");
     __shared__ __align__(16) uint8_t lds[RD.bytes];
 
@@ -287,8 +315,8 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     // (SGPRs) holding the tile's base and extent, a 32-bit lane offset, and
     // the K offset in an SGPR.
     constexpr int kRsrcWord3 = 0x00020000;
-    const int64_t brow_base = EPI == EPI_SWIGLU ? (int64_t)nt * (BN / 2) : (int64_t)nt * BN;
-    const int b_rows = EPI == EPI_SWIGLU ? BN / 2 : BN;
+    const int64_t brow_base = epi_swiglu(EPI) ? (int64_t)nt * (BN / 2) : (int64_t)nt * BN;
+    const int b_rows = epi_swiglu(EPI) ? BN / 2 : BN;
     const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const uint8_t*)p.A + (int64_t)row0 * p.lda * ES), (short)0,
         (int)(((int64_t)(rows - 1) * p.lda + p.K) * ES), kRsrcWord3);
@@ -296,7 +324,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const uint8_t*)p.B0 + boff), (short)0, (int)((int64_t)b_rows * p.K * ES), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint8_t*)(EPI == EPI_SWIGLU ? p.B1 : p.B0) + boff), (short)0,
+        (void*)((const uint8_t*)(epi_swiglu(EPI) ? p.B1 : p.B0) + boff), (short)0,
         (int)((int64_t)b_rows * p.K * ES), kRsrcWord3);
     uint32_t voffA[ga], voffB[gb];
 #pragma unroll
@@ -310,7 +338,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
         const int r = 8 * g + (lane >> 3);
         // SwiGLU: 16-row block j of the tile is rows (j/2)*16 .. +15 of W1 (j
         // even) or W3 (j odd)
-        const int rr = EPI == EPI_SWIGLU ? ((g >> 2) * 16 + (r & 15)) : r;
+        const int rr = epi_swiglu(EPI) ? ((g >> 2) * 16 + (r & 15)) : r;
         voffB[q] = (uint32_t)(rr * p.K * ES + (((lane & 7) ^ swz(r)) << 4));
     }
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -326,7 +354,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     auto issueB1 = [&](int v, int q) {
         uint8_t* dst = &lds[NA * SA + (v % NB) * SB + wave * gb * 1024];
         const int koff = (k0 + min(v, nk - 1)) * 128;
-        const bool up = EPI == EPI_SWIGLU && (((wave * gb + q) >> 1) & 1);
+        const bool up = epi_swiglu(EPI) && (((wave * gb + q) >> 1) & 1);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? rsB1 : rsB0, (lds_ptr_t)(dst + q * 1024), 16, voffB[q], koff,
                                                  0, 0);
     };
@@ -618,7 +646,7 @@ GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N) {
     if (!bf16 && g.BM > 128) g.BM = 128;
     // output columns per tile for BN = 256 / 128 / 64 (SwiGLU tiles hold gate
     // and up rows, so they produce half as many columns)
-    const int div = epi == EPI_SWIGLU ? 2 : 1;
+    const int div = epi_swiglu(epi) ? 2 : 1;
     g.BN = (N % (256 / div) == 0) ? 256 : (N % (128 / div) == 0 ? 128 : 64);
     return g;
 }
@@ -637,6 +665,8 @@ static void launch_bmbn(int epi, const GemmParams& p, int grid, hipStream_t s) {
     switch (epi) {
         case EPI_STORE: launch_pair<BF16, BM, BN, EPI_STORE>(p, grid, s); break;
         case EPI_RELU: launch_pair<BF16, BM, BN, EPI_RELU>(p, grid, s); break;
+        case EPI_RELU_SAVE: launch_pair<BF16, BM, BN, EPI_RELU_SAVE>(p, grid, s); break;
+        case EPI_SWIGLU_SAVE: launch_pair<BF16, BM, BN, EPI_SWIGLU_SAVE>(p, grid, s); break;
         default: launch_pair<BF16, BM, BN, EPI_SWIGLU>(p, grid, s); break;
     }
 }
@@ -665,16 +695,18 @@ static void launch_t(int epi, const GemmParams& p, int BM, int BN, int grid, hip
 hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B0, const void* B1,
                                int64_t b_expert_stride, void* C, int64_t ldc, int N, int K, int E, int64_t max_rows,
                                const int32_t* offsets, int32_t* plan, int32_t* plan_copy, float* partial, int BM,
-                               int BN, hipStream_t s) {
+                               int BN, hipStream_t s, void* C2, int64_t ldc2) {
     if (max_rows <= 0) return hipSuccess;
     GemmParams p;
     p.A = A; p.lda = lda; p.B0 = B0; p.B1 = B1; p.bstride = b_expert_stride;
     p.C = C; p.ldc = ldc; p.N = N; p.K = K; p.E = offsets ? E : 1;
-    p.NT = epi == EPI_SWIGLU ? N / (BN / 2) : N / BN;
+    p.NT = epi_swiglu(epi) ? N / (BN / 2) : N / BN;
     p.nk = K * (bf16 ? 2 : 4) / 128;
     p.offsets = offsets ? offsets : plan_copy;
     p.plan = plan;
     p.partial = partial;
+    p.C2 = C2;
+    p.ldc2 = ldc2;
     hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, offsets, E, (int)max_rows, BM, p.NT, p.nk, plan,
                        plan_copy);
     const int64_t m_tiles_ub = (max_rows + BM - 1) / BM + (p.E > 1 ? p.E : 0);

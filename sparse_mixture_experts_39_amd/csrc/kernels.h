@@ -66,14 +66,17 @@ size_t ffn_tile_plan_ints(int E);
 // Split-K partial accumulator workspace needed by a BM x BN launch.
 size_t gemm_partial_bytes(int BM, int BN);
 // Grouped GEMM C[rows][N] = act(A[rows][K] . B_e[N][K]^T) per expert group.
-// epi: 0 store, 1 relu, 2 swiglu (B0 = gate, B1 = up, N = d_ff, output width N).
+// epi: 0 store, 1 relu, 2 swiglu (B0 = gate, B1 = up, N = d_ff, output width N),
+// 3 swiglu that also stores a | u to C2 [rows][ldc2 >= 2N], 4 relu that also
+// stores a to C2.
 // Builds the tile plan on the device (offsets == NULL: one group of max_rows
 // rows, whose offsets go to plan_copy), then runs the GEMM and its split-K
 // fixup.
 hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B0, const void* B1,
                                int64_t b_expert_stride, void* C, int64_t ldc, int N, int K, int E,
                                int64_t max_rows, const int32_t* offsets, int32_t* plan, int32_t* plan_copy,
-                               float* partial, int BM, int BN, hipStream_t s);
+                               float* partial, int BM, int BN, hipStream_t s, void* C2 = nullptr,
+                               int64_t ldc2 = 0);
 GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N);
 
 // backward.hip
@@ -86,10 +89,10 @@ void launch_zero_f32(float* p, int64_t n, hipStream_t s);
 void launch_bwd_rows(bool bf16, const void* dy, const void* y_perm, const int32_t* perm_src, const int32_t* offsets,
                      int E, const float* gates, int slots, int d, int64_t max_rows, void* dy_perm, float* dg,
                      hipStream_t s);
-// da | du (row stride 2F; F for ReLU) and h from dh, a, u on the kept rows
-// (offsets == NULL: the first max_rows rows).
-void launch_bwd_act(bool bf16, bool swiglu, const void* dh, const void* a, const void* u, const int32_t* offsets,
-                    int E, int64_t max_rows, int F, void* dadu, void* h, hipStream_t s);
+// da | du (row stride 2F; F for ReLU) and h from dh, a, u (row stride ld_au)
+// on the kept rows (offsets == NULL: the first max_rows rows).
+void launch_bwd_act(bool bf16, bool swiglu, const void* dh, const void* a, const void* u, int64_t ld_au,
+                    const int32_t* offsets, int E, int64_t max_rows, int F, void* dadu, void* h, hipStream_t s);
 // C_e[M][N] = sum over the rows r of expert e of A[r][m] B[r][n]; max_rows
 // bounds every expert's row count.
 hipError_t launch_gemm_tn(bool bf16, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int M, int N,

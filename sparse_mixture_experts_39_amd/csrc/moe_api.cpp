@@ -432,14 +432,17 @@ moe_status moe_dispatch(const moe_config* c, const void* x, const int32_t* topk_
 // shared expert) and the plan writes its offsets to plan_copy.
 static moe_status run_gemm(const moe_config* c, bool up, const void* a, int64_t rows, int E, const int32_t* offsets,
                            const void* w1, const void* w3, const void* w2, int F, void* dst, int32_t* plan,
-                           int32_t* plan_copy, float* partial, hipStream_t h) {
+                           int32_t* plan_copy, float* partial, hipStream_t h, void* pre = nullptr) {
     const bool bf = is_bf16(c);
     const int d = c->d_model;
-    const int epi = up ? (c->act == MOE_ACT_SWIGLU ? 2 : 1) : 0;
+    const bool swiglu = c->act == MOE_ACT_SWIGLU;
+    // up with pre != NULL: the epilogue also stores the pre-activations
+    const int epi = up ? (swiglu ? (pre ? 3 : 2) : (pre ? 4 : 1)) : 0;
     const int N = up ? F : d;
     const moe::GemmShape g = moe::pick_gemm_shape(bf, epi, rows, E, N);
     const hipError_t e = up ? moe::launch_grouped_gemm(bf, epi, a, d, w1, w3, (int64_t)F * d, dst, F, F, d, E, rows,
-                                                       offsets, plan, plan_copy, partial, g.BM, g.BN, h)
+                                                       offsets, plan, plan_copy, partial, g.BM, g.BN, h, pre,
+                                                       (int64_t)(swiglu ? 2 : 1) * F)
                             : moe::launch_grouped_gemm(bf, 0, a, F, w2, nullptr, (int64_t)d * F, dst, d, d, F, E,
                                                        rows, offsets, plan, plan_copy, partial, g.BM, g.BN, h);
     if (e != hipSuccess) return hip_status(e);
@@ -467,6 +470,22 @@ moe_status moe_expert_up(const moe_config* c, const void* x_perm, const int32_t*
     return run_gemm(c, true, x_perm, R, c->n_experts, expert_offsets, w->w_gate, w->w_up, nullptr, c->d_ff, hbuf,
                     at<int32_t>(ws, L.plan_up), at<int32_t>(ws, L.plan_copy), at<float>(ws, L.partial),
                     (hipStream_t)stream);
+}
+
+moe_status moe_expert_up_train(const moe_config* c, const void* x_perm, const int32_t* expert_offsets,
+                               const moe_weights* w, void* hbuf, void* pre_act, void* ws, size_t ws_bytes,
+                               void* stream) {
+    moe_status s = moe_validate_config(c);
+    if (s != MOE_OK) return s;
+    if ((s = check_ffn_args(c, x_perm, expert_offsets, w, hbuf, true, false)) != MOE_OK) return s;
+    if (c->T > 0 && !pre_act) return MOE_ERR_INVALID_ARG;
+    if ((s = check_ws(c, ws, ws_bytes)) != MOE_OK) return s;
+    const int64_t R = max_rows_of(c);
+    if (R == 0) return MOE_OK;
+    const Layout L = compute_layout(c);
+    return run_gemm(c, true, x_perm, R, c->n_experts, expert_offsets, w->w_gate, w->w_up, nullptr, c->d_ff, hbuf,
+                    at<int32_t>(ws, L.plan_up), at<int32_t>(ws, L.plan_copy), at<float>(ws, L.partial),
+                    (hipStream_t)stream, pre_act);
 }
 
 moe_status moe_expert_down(const moe_config* c, const void* hbuf, const int32_t* expert_offsets, const moe_weights* w,
@@ -595,7 +614,7 @@ struct ExpertBufs {
 moe_status expert_backward(const moe_config* c, const void* X, const void* DY, int64_t rows, int E,
                            const int32_t* offsets, const void* W1, const void* W3, const void* W2, int F,
                            const ExpertBufs& b, void* DX, void* dW1, void* dW3, void* dW2, const BwdLayout& L,
-                           void* ws, int32_t* plan_copy, hipStream_t h) {
+                           void* ws, int32_t* plan_copy, hipStream_t h, const void* pre = nullptr) {
     const bool bf = is_bf16(c);
     const bool swiglu = c->act == MOE_ACT_SWIGLU;
     const int ig = swiglu ? 2 : 1;
@@ -608,19 +627,29 @@ moe_status expert_backward(const moe_config* c, const void* X, const void* DY, i
     moe::launch_transpose(W1, E, F, d, (int64_t)F * d, b.w13t, (int64_t)ig * F, (int64_t)d * ig * F, 0, es, h);
     if (swiglu)
         moe::launch_transpose(W3, E, F, d, (int64_t)F * d, b.w13t, (int64_t)ig * F, (int64_t)d * ig * F, F, es, h);
-    // recompute a = X W1^T and u = X W3^T (the first call also builds the
-    // offsets of a single group)
-    if ((s = bwd_gemm(bf, X, d, W1, (int64_t)F * d, b.a, F, F, d, E, rows, offsets, L, ws, plan_copy, h)) != MOE_OK)
-        return s;
+    // a = X W1^T and u = X W3^T: saved by the forward (pre = [a | u], row
+    // stride ig F; routed experts only), else recomputed.  dh = DY W2.  The
+    // first GEMM also builds the offsets of a single group.
+    const void* A_ = b.a;
+    const void* U_ = b.u;
+    int64_t ld_au = F;
+    if (pre) {
+        A_ = pre;
+        U_ = (const uint8_t*)pre + (size_t)F * es;
+        ld_au = (int64_t)ig * F;
+    } else {
+        if ((s = bwd_gemm(bf, X, d, W1, (int64_t)F * d, b.a, F, F, d, E, rows, offsets, L, ws, plan_copy, h)) !=
+            MOE_OK)
+            return s;
+        if (swiglu && (s = bwd_gemm(bf, X, d, W3, (int64_t)F * d, b.u, F, F, d, E, rows, offsets, L, ws, plan_copy,
+                                    h)) != MOE_OK)
+            return s;
+    }
     const int32_t* offs = offsets ? offsets : plan_copy;
-    if (swiglu &&
-        (s = bwd_gemm(bf, X, d, W3, (int64_t)F * d, b.u, F, F, d, E, rows, offsets, L, ws, plan_copy, h)) != MOE_OK)
-        return s;
-    // dh = DY W2
     if ((s = bwd_gemm(bf, DY, d, b.w2t, (int64_t)F * d, b.dh, F, F, d, E, rows, offsets, L, ws, plan_copy, h)) !=
         MOE_OK)
         return s;
-    moe::launch_bwd_act(bf, swiglu, b.dh, b.a, b.u, offs, offsets ? E : 1, rows, F, b.dadu, b.hh, h);
+    moe::launch_bwd_act(bf, swiglu, b.dh, A_, U_, ld_au, offs, offsets ? E : 1, rows, F, b.dadu, b.hh, h);
     // DX = da W1 + du W3 as one product over the concatenated reduction
     if ((s = bwd_gemm(bf, b.dadu, (int64_t)ig * F, b.w13t, (int64_t)d * ig * F, DX, d, d, ig * F, E, rows, offsets, L,
                       ws, plan_copy, h)) != MOE_OK)
@@ -681,7 +710,8 @@ moe_status moe_layer_backward(const moe_config* c, const moe_weights* w, const v
                            at<void>(ws, L.hh), at<void>(ws, L.w2t), at<void>(ws, L.w13t)};
         if ((s = expert_backward(c, sv->x_perm, at<void>(ws, L.dyp), R, E, sv->expert_offsets, w->w_gate, w->w_up,
                                  w->w_down, c->d_ff, b, at<void>(ws, L.dxp), want_w ? g->dw_gate : nullptr,
-                                 g->dw_up, g->dw_down, L, ws, at<int32_t>(ws, L.plan_copy), h)) != MOE_OK)
+                                 g->dw_up, g->dw_down, L, ws, at<int32_t>(ws, L.plan_copy), h, sv->pre_act)) !=
+            MOE_OK)
             return s;
     } else if (want_w) {
         hipError_t e;

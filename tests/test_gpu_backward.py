@@ -43,8 +43,10 @@ CASES = {
 }
 
 
-def run_forward_backward(cfg, dinp, dy):
-    """Forward stage by stage, then the backward; device tensors."""
+def run_forward_backward(cfg, dinp, dy, save=False):
+    """Forward stage by stage, then the backward; device tensors.  save=True
+    runs the up projection through moe_expert_up_train and hands its
+    pre-activations to the backward."""
     c = bind_config(cfg, T=dinp["x"].shape[0])
     T, E, k, d, F = c.T, c.n_experts, moe.route_slots(c), c.d_model, c.d_ff
     dt = dinp["x"].dtype
@@ -60,7 +62,18 @@ def run_forward_backward(cfg, dinp, dy):
     moe.moe_route(c, x, w, sv["topk_idx"], sv["topk_gate"], None, None, ws)
     moe.moe_dispatch(c, x, sv["topk_idx"], sv["x_perm"], sv["expert_offsets"], sv["perm_src"], sv["slot_pos"], None,
                      ws)
-    moe.moe_expert_ffn(c, sv["x_perm"], sv["expert_offsets"], w, sv["y_perm"], ws)
+    if save:
+        H = torch.empty((R, F), dtype=dt, device="cuda")
+        pre = torch.empty((R, (2 if cfg.act == "swiglu" else 1) * F), dtype=dt, device="cuda")
+        moe.moe_expert_up_train(c, sv["x_perm"], sv["expert_offsets"], w, H, pre, ws)
+        H2 = torch.empty_like(H)
+        moe.moe_expert_up(c, sv["x_perm"], sv["expert_offsets"], w, H2, ws)
+        kept = int(sv["expert_offsets"][E].item())
+        assert torch.equal(H[:kept].view(torch.uint8), H2[:kept].view(torch.uint8)), "h differs from moe_expert_up"
+        moe.moe_expert_down(c, H, sv["expert_offsets"], w, sv["y_perm"], ws)
+        sv["pre_act"] = pre
+    else:
+        moe.moe_expert_ffn(c, sv["x_perm"], sv["expert_offsets"], w, sv["y_perm"], ws)
     g = dict(dx=torch.full((T, d), float("nan"), dtype=dt, device="cuda"),
              dw_router=torch.full((E, d), float("nan"), dtype=torch.float32, device="cuda"),
              dlogit_bias=torch.full((E,), float("nan"), dtype=torch.float32, device="cuda"),
@@ -85,13 +98,16 @@ def _grad_names(cfg):
     return [("dw_gate", "dw1"), ("dw_down", "dw2")]
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_backward_matches_oracle(name):
+SAVED = ["f32_swiglu_topk_resid", "bf16_swiglu_topk_drops", "f32_relu_full_switch", "bf16_expert_choice"]
+
+
+@pytest.mark.parametrize("name,save", [(n, False) for n in CASES] + [(n, True) for n in SAVED])
+def test_backward_matches_oracle(name, save):
     cfg = workloads.Config(name, **CASES[name])
-    log(f"[backward parity] {name}")
+    log(f"[backward parity] {name} saved pre-activations={save}")
     inp = workloads.make_inputs(cfg)
     dy = workloads.make_output_grad(cfg)
-    sv, g = run_forward_backward(cfg, to_device(inp), dy.to("cuda"))
+    sv, g = run_forward_backward(cfg, to_device(inp), dy.to("cuda"), save=save)
     fwd = oracle.forward(cfg, inp)
     np.testing.assert_array_equal(sv["topk_idx"].numpy(), fwd["idx"], err_msg="routing")
     np.testing.assert_array_equal(sv["slot_pos"].numpy(), fwd["slot_pos"], err_msg="slot positions")
