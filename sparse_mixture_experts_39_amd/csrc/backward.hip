@@ -428,6 +428,29 @@ __global__ __launch_bounds__(256) void k_gemm_tn(TnParams p) {
 #endif
 }
 
+// Parameters of the two 256 x 256 bf16 products below.
+//   TN (weight gradients): C_e[M][N] = sum over the expert's rows r of
+//       A[r][m] B[r][n] (A, B row-major, m / n contiguous), C_e at e M N.
+//   NN (input gradients without weight transposes): C[r][n] = sum_k
+//       A[r][k] B_e[k][n] for the rows r of expert e (ragged), A row-major
+//       with k contiguous, B_e = B0 + e bstride for k < K1 and
+//       B1 + e bstride (row k - K1) beyond, both [rows][N] with n contiguous;
+//       prefix[E+1] holds the experts' 256-row tile counts, summed.
+struct XnParams {
+    const void* A;
+    int64_t lda;
+    const void* B0;
+    const void* B1;
+    int64_t ldb;
+    int64_t bstride;
+    void* C;
+    int64_t ldc;
+    int M, N, K, K1, E;
+    int tiles_m, tiles_n;
+    const int32_t* offsets;
+    const int32_t* prefix;
+};
+
 // bf16, 256 x 256 tiles, 512 threads: 8 waves of 64 (m) x 128 (n), so a
 // wave holds 128 accumulator registers and two waves share each SIMD;
 // chunks of 64 rows through two LDS buffers of 64 KB.  Threads 0-255 stage
@@ -436,50 +459,110 @@ __global__ __launch_bounds__(256) void k_gemm_tn(TnParams p) {
 // the expert's rows read zeros (outside the buffer descriptor's range), so
 // the loop body has no branches.  Blocks map to tiles XCD by XCD, so the
 // tiles of one XCD share an expert's rows in L2.
-__global__ __launch_bounds__(512) void k_gemm_tn256(TnParams p) {
+template <bool NN>
+__global__ __launch_bounds__(512) void k_gemm_x256(XnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int BM = 256, KC = 64;
     constexpr int OPB = BM * KC * 2;
     __shared__ __align__(16) uint8_t lds[2 * 2 * OPB];
-    const int ntiles = p.E * p.tiles_m * p.tiles_n;
+    // tiles: TN, E x tiles_m x tiles_n; NN, (sum of the experts' row tiles)
+    // x tiles_n.  Groups of GM row tiles: the 32 CUs of an XCD run 4 row
+    // tiles x 8 column tiles at a time, so each staged chunk of A is fetched
+    // once per 8 tiles and each chunk of B once per 4.
+    constexpr int GM = 4;
+    const int mt_all = NN ? p.prefix[p.E] : p.E * p.tiles_m;
+    const int ntiles = mt_all * p.tiles_n;
     const int per_xcd = (ntiles + 7) / 8;
     const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (tile >= ntiles) return;
-    const int per_e = p.tiles_m * p.tiles_n;
-    const int e = tile / per_e;
-    // inside an expert, groups of GM row tiles: the 32 CUs of an XCD run
-    // 4 row tiles x 8 column tiles at a time, so each staged chunk of A is
-    // fetched once per 8 tiles and each chunk of B once per 4
-    constexpr int GM = 4;
-    const int L = tile - e * per_e;
-    const int grp = L / (GM * p.tiles_n);
-    const int tm0 = grp * GM;
-    const int gm = min(p.tiles_m - tm0, GM);
-    const int in = L - grp * GM * p.tiles_n;
-    const int tm = tm0 + in % gm, tn = in / gm;
-    const int m_base = tm * BM, n_base = tn * BM;
+    int e, tm, tn;
+    if constexpr (NN) {
+        const int grp = tile / (GM * p.tiles_n);
+        const int gm = min(mt_all - grp * GM, GM);
+        const int in = tile - grp * GM * p.tiles_n;
+        const int mt = grp * GM + in % gm;
+        tn = in / gm;
+        int lo_e = 0, hi_e = p.E;                 // expert: prefix[e] <= mt < prefix[e+1]
+        while (hi_e - lo_e > 1) {
+            const int mid = (lo_e + hi_e) >> 1;
+            if (p.prefix[mid] <= mt) lo_e = mid; else hi_e = mid;
+        }
+        e = lo_e;
+        tm = mt - p.prefix[e];
+    } else {
+        const int per_e = p.tiles_m * p.tiles_n;
+        e = tile / per_e;
+        const int L = tile - e * per_e;
+        const int grp = L / (GM * p.tiles_n);
+        const int gm = min(p.tiles_m - grp * GM, GM);
+        const int in = L - grp * GM * p.tiles_n;
+        tm = grp * GM + in % gm;
+        tn = in / gm;
+    }
+    e = __builtin_amdgcn_readfirstlane(e);
+    tm = __builtin_amdgcn_readfirstlane(tm);
+    tn = __builtin_amdgcn_readfirstlane(tn);
     const int lo = p.offsets[e], hi = p.offsets[e + 1];
+    // TN: m_base is a column of A; NN: the first row of the tile
+    const int m_base = NN ? lo + tm * BM : tm * BM, n_base = tn * BM;
+    const int rows_tile = NN ? min(BM, hi - m_base) : BM;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int nch = (hi - lo + KC - 1) / KC;
+    const int nch = NN ? p.K / KC : (hi - lo + KC - 1) / KC;
 
-    // staging: operand op (0: A, 1: B) of this thread, rows kq*8 .. +7 of
-    // the chunk, columns cg*8 .. +7 of the tile
+    // staging: operand op (0: A, 1: B) of this thread.  Transposed staging
+    // (TN both operands, NN the weights): rows kq*8 .. +7 of the chunk,
+    // columns cg*8 .. +7 of the tile.  Direct staging (NN activations): row
+    // m0 + 32 i (i = 0..7) of the tile, k-group g of the chunk.
     const int op = wave >> 2;
+    const bool direct = NN && op == 0;
     const int cg = tid & 31, kq = (tid >> 5) & 7;
+    const int g_d = tid & 7, m0_d = (tid >> 3) & 31;
     constexpr int kRsrcWord3 = 0x00020000;
-    const void* src = op == 0 ? p.A : p.B;
-    const int64_t ld = op == 0 ? p.lda : p.ldb;
-    const int col = (op == 0 ? m_base : n_base) + cg * 8;
-    const int lim = op == 0 ? p.M : p.N;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint16_t*)src + (int64_t)lo * ld), (short)0, (int)((int64_t)(hi - lo) * ld * 2), kRsrcWord3);
-    const uint32_t vo = col < lim ? (uint32_t)((kq * 8 * ld + col) * 2) : 0x80000000u;
-    const int row_bytes = (int)(ld * 2);
+    __amdgpu_buffer_rsrc_t rs, rs1;
+    uint32_t vo;
+    int row_bytes;
+    if constexpr (NN) {
+        if (op == 0) {
+            rs = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.A + (int64_t)m_base * p.lda), (short)0,
+                                                   (int)((int64_t)rows_tile * p.lda * 2), kRsrcWord3);
+            rs1 = rs;
+            vo = (uint32_t)((m0_d * p.lda + g_d * 8) * 2);
+            row_bytes = (int)(p.lda * 2);
+        } else {
+            const int col = n_base + cg * 8;
+            const int64_t eoff = (int64_t)e * p.bstride;
+            rs = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.B0 + eoff), (short)0,
+                                                   (int)((int64_t)p.K1 * p.ldb * 2), kRsrcWord3);
+            rs1 = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)(p.B1 ? p.B1 : p.B0) + eoff), (short)0,
+                                                    p.B1 ? (int)((int64_t)(p.K - p.K1) * p.ldb * 2) : 0, kRsrcWord3);
+            vo = col < p.N ? (uint32_t)((kq * 8 * p.ldb + col) * 2) : 0x80000000u;
+            row_bytes = (int)(p.ldb * 2);
+        }
+    } else {
+        const void* src = op == 0 ? p.A : p.B0;
+        const int64_t ld = op == 0 ? p.lda : p.ldb;
+        const int col = (op == 0 ? m_base : n_base) + cg * 8;
+        const int lim = op == 0 ? p.M : p.N;
+        rs = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)src + (int64_t)lo * ld), (short)0,
+                                               (int)((int64_t)(hi - lo) * ld * 2), kRsrcWord3);
+        rs1 = rs;
+        vo = col < lim ? (uint32_t)((kq * 8 * ld + col) * 2) : 0x80000000u;
+        row_bytes = (int)(ld * 2);
+    }
     u32x4_t st[8];
     auto load_row = [&](int ch, int i) __attribute__((always_inline)) {
-        st[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, (ch * KC + i) * row_bytes, 0));
+        if (direct) {
+            st[i] = __builtin_bit_cast(u32x4_t,
+                                       __builtin_amdgcn_raw_buffer_load_b128(rs, vo, i * 32 * row_bytes + ch * KC * 2, 0));
+        } else if (NN && ch * KC >= p.K1) {
+            st[i] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs1, vo, (ch * KC - p.K1 + i) * row_bytes, 0));
+        } else {
+            st[i] = __builtin_bit_cast(u32x4_t,
+                                       __builtin_amdgcn_raw_buffer_load_b128(rs, vo, (ch * KC + i) * row_bytes, 0));
+        }
     };
     // LDS layout of one operand in one buffer: row m (0..255) holds the 64
     // k of the chunk as 8 groups of 8 (16 bytes), group g at slot
@@ -497,7 +580,16 @@ __global__ __launch_bounds__(512) void k_gemm_tn256(TnParams p) {
     // rows 2q and 2q + 1
     const uint32_t sel_lo = 0x05040100u, sel_hi = 0x07060302u;
     const uint32_t sel_j_even = pbit ? sel_hi : sel_lo, sel_j_odd = pbit ? sel_lo : sel_hi;
+    // Direct staging writes row m = m0 + 32 j, group g, at slot
+    // g ^ (m0 & 7) ^ (((m0 >> 3) + 4 j) & 7): the 8 lanes of a row cover its
+    // 8 slots.
+    const int d_x = g_d ^ (m0_d & 7);
     auto put_col = [&](int buf, int j) __attribute__((always_inline)) {
+        if (direct) {
+            const int slot = d_x ^ (((m0_d >> 3) + 4 * j) & 7);
+            *(u32x4_t*)(lds + (size_t)(buf * 2) * OPB + (m0_d + 32 * j) * 128 + slot * 16) = st[j];
+            return;
+        }
         const uint32_t sel = (j & 1) ? sel_j_odd : sel_j_even;
         u32x4_t v;
 #pragma unroll
@@ -598,11 +690,13 @@ __global__ __launch_bounds__(512) void k_gemm_tn256(TnParams p) {
         set_read_base(b ^ 1);
     }
     // lane holds C[m][n .. n+3] of block (n-block i, m-block j)
-    uint16_t* Ce = (uint16_t*)p.C + (size_t)e * p.M * p.N;
+    uint16_t* Ce = NN ? (uint16_t*)p.C + (int64_t)m_base * p.ldc : (uint16_t*)p.C + (size_t)e * p.M * p.N;
+    const int64_t ldc = NN ? p.ldc : p.N;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int m = m_base + wm * 64 + j * 16 + (lane & 15);
-        if (m >= p.M) continue;
+        const int ml = wm * 64 + j * 16 + (lane & 15);
+        if (NN ? ml >= rows_tile : m_base + ml >= p.M) continue;
+        const int m = NN ? ml : m_base + ml;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int n = n_base + wn * 128 + i * 16 + 4 * (lane >> 4);
@@ -610,7 +704,7 @@ __global__ __launch_bounds__(512) void k_gemm_tn256(TnParams p) {
             uint2 w;
             w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
             w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-            *(uint2*)(Ce + (int64_t)m * p.N + n) = w;
+            *(uint2*)(Ce + (int64_t)m * ldc + n) = w;
         }
     }
 #endif
@@ -622,8 +716,8 @@ hipError_t launch_gemm_tn(bool bf16, const void* A, int64_t lda, const void* B, 
     // read-ahead) with 32-bit buffer offsets
     const int64_t ldmax = lda > ldb ? lda : ldb;
     if (bf16 && M >= 256 && N >= 256 && (max_rows + 128) * ldmax * 2 < ((int64_t)1 << 31)) {
-        TnParams p;
-        p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.C = C;
+        XnParams p = {};
+        p.A = A; p.lda = lda; p.B0 = B; p.ldb = ldb; p.C = C;
         p.M = M; p.N = N; p.E = E;
         p.tiles_m = (M + 255) / 256;
         p.tiles_n = (N + 255) / 256;
@@ -632,7 +726,7 @@ hipError_t launch_gemm_tn(bool bf16, const void* A, int64_t lda, const void* B, 
         if (nt <= 0) return hipSuccess;
         if (nt > 0x7fffffff - 8) return hipErrorInvalidValue;
         const int64_t grid = (nt + 7) / 8 * 8;
-        hipLaunchKernelGGL(k_gemm_tn256, dim3((unsigned)grid), dim3(512), 0, s, p);
+        hipLaunchKernelGGL(k_gemm_x256<false>, dim3((unsigned)grid), dim3(512), 0, s, p);
         return hipGetLastError();
     }
     TnParams p;
@@ -646,6 +740,60 @@ hipError_t launch_gemm_tn(bool bf16, const void* A, int64_t lda, const void* B, 
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     if (bf16) hipLaunchKernelGGL(k_gemm_tn<true>, dim3((unsigned)grid), dim3(256), 0, s, p);
     else hipLaunchKernelGGL(k_gemm_tn<false>, dim3((unsigned)grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+__global__ void k_single_group(int32_t* offsets, int rows) {
+    if (threadIdx.x == 0) {
+        offsets[0] = 0;
+        offsets[1] = rows;
+    }
+}
+
+void launch_single_group_offsets(int32_t* offsets, int64_t rows, hipStream_t s) {
+    hipLaunchKernelGGL(k_single_group, dim3(1), dim3(64), 0, s, offsets, (int)rows);
+}
+
+// Row-tile prefix of the NN product: prefix[e+1] = prefix[e] + ceil(rows_e / 256).
+__global__ __launch_bounds__(1024) void k_nn_plan(const int32_t* __restrict__ offsets, int E,
+                                                  int32_t* __restrict__ prefix) {
+    __shared__ int32_t scan[1024];
+    const int e = threadIdx.x;
+    scan[e] = e < E ? (offsets[e + 1] - offsets[e] + 255) / 256 : 0;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int32_t v = e >= off ? scan[e - off] : 0;
+        __syncthreads();
+        scan[e] += v;
+        __syncthreads();
+    }
+    if (e == 0) prefix[0] = 0;
+    if (e < E) prefix[e + 1] = scan[e];
+}
+
+bool gemm_nn_supported(int64_t max_rows, int64_t lda, int K, int K1, int64_t ldb, int N) {
+    // 32-bit buffer offsets: a 256-row tile of A, and K1 / K - K1 rows of B
+    // (plus two chunks of read-ahead)
+    return N >= 256 && K % 64 == 0 && K1 % 64 == 0 && max_rows > 0 && 256 * lda * 2 < ((int64_t)1 << 31) &&
+           ((int64_t)K + 128) * ldb * 2 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_gemm_nn(const void* A, int64_t lda, const void* B0, const void* B1, int K1, int64_t ldb,
+                          int64_t bstride, void* C, int64_t ldc, int N, int K, int E, const int32_t* offsets,
+                          int64_t max_rows, int32_t* prefix, hipStream_t s) {
+    if (max_rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_nn_plan, dim3(1), dim3(1024), 0, s, offsets, E, prefix);
+    XnParams p = {};
+    p.A = A; p.lda = lda; p.B0 = B0; p.B1 = B1; p.ldb = ldb; p.bstride = bstride;
+    p.C = C; p.ldc = ldc; p.N = N; p.K = K; p.K1 = B1 ? K1 : K; p.E = E;
+    p.tiles_n = (N + 255) / 256;
+    p.offsets = offsets;
+    p.prefix = prefix;
+    const int64_t mt_ub = (max_rows + 255) / 256 + E;
+    const int64_t nt = mt_ub * p.tiles_n;
+    if (nt > 0x7fffffff - 8) return hipErrorInvalidValue;
+    const int64_t grid = (nt + 7) / 8 * 8;
+    hipLaunchKernelGGL(k_gemm_x256<true>, dim3((unsigned)grid), dim3(512), 0, s, p);
     return hipGetLastError();
 }
 
@@ -739,16 +887,19 @@ void launch_bwd_router(const float* dots, int NC, const float* logit_bias, const
 }
 
 // Token gradient, one block per token, fp32 in this order: residual dY,
-// routed rows in slot order, shared expert, then dz_e W_r[e] for e ascending
-// (zero dz skipped).
+// routed rows in slot order, shared expert, then the router term dz_t W_r:
+// over the token's selected experts in slot order when dz is zero elsewhere
+// (idx != NULL: softmax over the selected, sigmoid), else over all experts
+// in ascending order.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_bwd_dx(const void* __restrict__ dy, const void* __restrict__ dx_perm,
                                                 const int32_t* __restrict__ slot_pos, int slots,
                                                 const void* __restrict__ dx_shared, const float* __restrict__ dz,
-                                                const float* __restrict__ w_router, int E, int d, bool residual,
-                                                void* __restrict__ dx) {
+                                                const int32_t* __restrict__ idx, const float* __restrict__ w_router,
+                                                int E, int d, bool residual, void* __restrict__ dx) {
     const int t = blockIdx.x;
     const int32_t* sp = slot_pos + (int64_t)t * slots;
+    const int32_t* it = idx ? idx + (int64_t)t * slots : nullptr;
     const float* dzt = dz ? dz + (int64_t)t * E : nullptr;
     for (int c = threadIdx.x; c < d; c += 256) {
         float v = residual ? load_act<BF16>(dy, (int64_t)t * d + c) : 0.0f;
@@ -757,51 +908,68 @@ __global__ __launch_bounds__(256) void k_bwd_dx(const void* __restrict__ dy, con
             if (r >= 0) v += load_act<BF16>(dx_perm, (int64_t)r * d + c);
         }
         if (dx_shared) v += load_act<BF16>(dx_shared, (int64_t)t * d + c);
-        if (dzt) {
-            for (int e = 0; e < E; ++e) {
-                const float g = dzt[e];
-                if (g != 0.0f) v += g * w_router[(int64_t)e * d + c];
+        if (dzt && it) {
+            for (int j = 0; j < slots; ++j) {
+                const int e = it[j];
+                if (e >= 0) v += dzt[e] * w_router[(int64_t)e * d + c];
             }
+        } else if (dzt) {
+            for (int e = 0; e < E; ++e) v += dzt[e] * w_router[(int64_t)e * d + c];
         }
         store_act<BF16>(dx, (int64_t)t * d + c, v);
     }
 }
 
 void launch_bwd_dx(bool bf16, const void* dy, const void* dx_perm, const int32_t* slot_pos, int slots,
-                   const void* dx_shared, const float* dz, const float* w_router, int T, int E, int d, bool residual,
-                   void* dx, hipStream_t s) {
+                   const void* dx_shared, const float* dz, const int32_t* idx, const float* w_router, int T, int E,
+                   int d, bool residual, void* dx, hipStream_t s) {
     if (T <= 0) return;
     if (bf16)
         hipLaunchKernelGGL(k_bwd_dx<true>, dim3(T), dim3(256), 0, s, dy, dx_perm, slot_pos, slots, dx_shared, dz,
-                           w_router, E, d, residual, dx);
+                           idx, w_router, E, d, residual, dx);
     else
         hipLaunchKernelGGL(k_bwd_dx<false>, dim3(T), dim3(256), 0, s, dy, dx_perm, slot_pos, slots, dx_shared, dz,
-                           w_router, E, d, residual, dx);
+                           idx, w_router, E, d, residual, dx);
 }
 
-// Router gradients in two fixed-order passes: block (e, column chunk, token
-// chunk q) sums tokens [q 256, q 256 + 256) in order into part[q][e][c]
-// (column d is the bias: the sum of dz); then k_bwd_wr_sum adds the chunks
-// in order.
+// Router gradients dW_r = dz^T x and db = sum_t dz, as a tiled product in
+// two fixed-order passes.  Block (expert group of 64, column chunk of 256,
+// token chunk q of 256 tokens): the chunk's dz columns go to LDS, each
+// thread owns one column c and the 64 experts of the group, and adds
+// dz[t][e] x[t][c] over the chunk's tokens in order (x is read once per
+// expert group, not once per expert); column d (thread c == d) sums dz for
+// the bias.  k_bwd_wr_sum then adds the chunks in order.
 constexpr int kWrTokens = 256;
+constexpr int kWrExperts = 64;
 
 int bwd_wr_chunks(int T) { return (T + kWrTokens - 1) / kWrTokens; }
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_bwd_wr_part(const float* __restrict__ dz, const void* __restrict__ x, int T,
                                                      int E, int d, float* __restrict__ part) {
-    const int e = blockIdx.y, q = blockIdx.z;
+    __shared__ float zs[kWrTokens][kWrExperts];
+    const int e0 = blockIdx.y * kWrExperts, q = blockIdx.z;
     const int c = blockIdx.x * 256 + threadIdx.x;
-    const int t0 = q * kWrTokens, t1 = min(T, t0 + kWrTokens);
-    float acc = 0.0f, accb = 0.0f;
-    for (int t = t0; t < t1; ++t) {
-        const float g = dz[(int64_t)t * E + e];
-        accb += g;
-        if (c < d) acc += g * load_act<BF16>(x, (int64_t)t * d + c);
+    const int t0 = q * kWrTokens, nt = min(T - t0, kWrTokens);
+    const int ne = min(E - e0, kWrExperts);
+    for (int i = threadIdx.x; i < kWrTokens * kWrExperts; i += 256) {
+        const int tt = i / kWrExperts, ee = i - tt * kWrExperts;
+        zs[tt][ee] = (tt < nt && ee < ne) ? dz[(int64_t)(t0 + tt) * E + e0 + ee] : 0.0f;
     }
-    float* pe = part + ((int64_t)q * E + e) * (d + 1);
-    if (c < d) pe[c] = acc;
-    if (c == d) pe[d] = accb;
+    __syncthreads();
+    float acc[kWrExperts];
+#pragma unroll
+    for (int ee = 0; ee < kWrExperts; ++ee) acc[ee] = 0.0f;
+    for (int tt = 0; tt < nt; ++tt) {
+        const float xv = c < d ? load_act<BF16>(x, (int64_t)(t0 + tt) * d + c) : 1.0f;
+#pragma unroll
+        for (int ee = 0; ee < kWrExperts; ++ee) acc[ee] += zs[tt][ee] * xv;
+    }
+    if (c <= d) {
+#pragma unroll
+        for (int ee = 0; ee < kWrExperts; ++ee)
+            if (ee < ne) part[((int64_t)q * E + e0 + ee) * (d + 1) + c] = acc[ee];
+    }
 }
 
 __global__ __launch_bounds__(256) void k_bwd_wr_sum(const float* __restrict__ part, int nq, int E, int d,
@@ -823,7 +991,7 @@ void launch_bwd_wr(bool bf16, const float* dz, const void* x, int T, int E, int 
                    hipStream_t s) {
     const int nq = bwd_wr_chunks(T);
     if (nq > 0) {
-        const dim3 grid((d + 1 + 255) / 256, E, nq);
+        const dim3 grid((d + 1 + 255) / 256, (E + kWrExperts - 1) / kWrExperts, nq);
         if (bf16) hipLaunchKernelGGL(k_bwd_wr_part<true>, grid, dim3(256), 0, s, dz, x, T, E, d, part);
         else hipLaunchKernelGGL(k_bwd_wr_part<false>, grid, dim3(256), 0, s, dz, x, T, E, d, part);
     }

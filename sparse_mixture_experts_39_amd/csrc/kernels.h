@@ -97,11 +97,23 @@ void launch_bwd_act(bool bf16, bool swiglu, const void* dh, const void* a, const
 // bounds every expert's row count.
 hipError_t launch_gemm_tn(bool bf16, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int M, int N,
                           int E, const int32_t* offsets, int64_t max_rows, hipStream_t s);
+// C[r][n] = sum_k A[r][k] B_e[k][n] over the rows r of expert e (bf16),
+// with B_e = B0 + e bstride for k < K1 and B1 + e bstride (row k - K1)
+// beyond (B1 NULL: all of B0); prefix holds E + 1 ints of scratch.  Use
+// only where gemm_nn_supported() holds.
+// offsets = {0, rows}: one group of rows.
+void launch_single_group_offsets(int32_t* offsets, int64_t rows, hipStream_t s);
+bool gemm_nn_supported(int64_t max_rows, int64_t lda, int K, int K1, int64_t ldb, int N);
+hipError_t launch_gemm_nn(const void* A, int64_t lda, const void* B0, const void* B1, int K1, int64_t ldb,
+                          int64_t bstride, void* C, int64_t ldc, int N, int K, int E, const int32_t* offsets,
+                          int64_t max_rows, int32_t* prefix, hipStream_t s);
 void launch_bwd_router(const float* dots, int NC, const float* logit_bias, const int32_t* idx, const float* gates,
                        const float* dg, int gate, int T, int E, int slots, float* dz, hipStream_t s);
+// idx != NULL: dz is zero outside the token's selected experts (sum over
+// its slots); NULL: sum over every expert.
 void launch_bwd_dx(bool bf16, const void* dy, const void* dx_perm, const int32_t* slot_pos, int slots,
-                   const void* dx_shared, const float* dz, const float* w_router, int T, int E, int d, bool residual,
-                   void* dx, hipStream_t s);
+                   const void* dx_shared, const float* dz, const int32_t* idx, const float* w_router, int T, int E,
+                   int d, bool residual, void* dx, hipStream_t s);
 int bwd_wr_chunks(int T);
 // dW_r = dz^T x and db = sum_t dz; part holds bwd_wr_chunks(T) * E * (d + 1) floats.
 void launch_bwd_wr(bool bf16, const float* dz, const void* x, int T, int E, int d, float* part, float* dw, float* db,

@@ -168,9 +168,23 @@ struct BwdLayout {
     size_t dots, dg, dz, wr_part;                                  // router
     size_t dyp, a, u, dh, dadu, hh, dxp, w2t, w13t;                // routed experts
     size_t sa, su, sdh, sdadu, shh, sdx, sw2t, sw13t;              // shared expert
-    size_t plan, plan_copy, plan_s_copy, partial;
+    size_t plan, plan_copy, plan_s_copy, partial, nn_prefix;
     size_t total;
 };
+
+// The input-gradient products dh = dy W2 and dx = [da|du] [W1; W3] either
+// run on the forward's grouped GEMM against transposed weight copies, or
+// read the weights as stored (the NN product).  The copies cost a pass over
+// every weight, which only pays off when each expert has many rows: the NN
+// product is used below kNnRowsPerExpert rows per expert (bf16).
+constexpr int64_t kNnRowsPerExpert = 512;
+
+bool use_nn_product(const moe_config* c, int64_t rows, int E, int F) {
+    if (!is_bf16(c) || rows <= 0 || rows >= kNnRowsPerExpert * E) return false;
+    const int ig = c->act == MOE_ACT_SWIGLU ? 2 : 1;
+    const int d = c->d_model;
+    return moe::gemm_nn_supported(rows, d, d, d, F, F) && moe::gemm_nn_supported(rows, (int64_t)ig * F, ig * F, F, d, d);
+}
 
 bool bwd_gate_supported(const moe_config* c) {
     return c->gate == MOE_GATE_SOFTMAX_TOPK || c->gate == MOE_GATE_SOFTMAX_FULL ||
@@ -217,8 +231,9 @@ BwdLayout compute_bwd_layout(const moe_config* c) {
     L.dadu = take((size_t)R * ig * F * es);
     L.hh = take((size_t)R * F * es);
     L.dxp = take((size_t)R * d * es);
-    L.w2t = take((size_t)E * F * d * es);
-    L.w13t = take((size_t)E * d * ig * F * es);
+    const bool nn = use_nn_product(c, R, E, F);
+    L.w2t = take(nn ? 0 : (size_t)E * F * d * es);
+    L.w13t = take(nn ? 0 : (size_t)E * d * ig * F * es);
     const bool sh = c->n_shared > 0;
     const size_t Fs = sh ? (size_t)c->d_ff_shared : 0;
     L.sa = take((size_t)T * Fs * es);
@@ -227,12 +242,14 @@ BwdLayout compute_bwd_layout(const moe_config* c) {
     L.sdadu = take((size_t)T * 2 * Fs * es);
     L.shh = take((size_t)T * Fs * es);
     L.sdx = take(sh ? (size_t)T * d * es : 0);
-    L.sw2t = take(Fs * d * es);
-    L.sw13t = take((size_t)d * 2 * Fs * es);
+    const bool snn = sh && use_nn_product(c, T, 1, (int)Fs);
+    L.sw2t = take(snn ? 0 : Fs * d * es);
+    L.sw13t = take(snn ? 0 : (size_t)d * 2 * Fs * es);
     L.plan = take(moe::ffn_tile_plan_ints(E) * sizeof(int32_t));
     L.plan_copy = take(2 * sizeof(int32_t));
     L.plan_s_copy = take(2 * sizeof(int32_t));
     L.partial = take(bwd_partial_bytes_of(c));
+    L.nn_prefix = take((size_t)(E + 1) * sizeof(int32_t));
     L.total = o;
     return L;
 }
@@ -621,12 +638,17 @@ moe_status expert_backward(const moe_config* c, const void* X, const void* DY, i
     const int d = c->d_model;
     const int es = elem_bytes(c);
     moe_status s;
-    // weight copies with the other dimension contiguous: W2^T [E][F][d] and
-    // [W1^T | W3^T] [E][d][ig F]
-    moe::launch_transpose(W2, E, d, F, (int64_t)d * F, b.w2t, d, (int64_t)F * d, 0, es, h);
-    moe::launch_transpose(W1, E, F, d, (int64_t)F * d, b.w13t, (int64_t)ig * F, (int64_t)d * ig * F, 0, es, h);
-    if (swiglu)
-        moe::launch_transpose(W3, E, F, d, (int64_t)F * d, b.w13t, (int64_t)ig * F, (int64_t)d * ig * F, F, es, h);
+    const bool nn = use_nn_product(c, rows, E, F);
+    int32_t* nn_prefix = at<int32_t>(ws, L.nn_prefix);
+    // weight copies with the other dimension contiguous (only for the
+    // grouped-GEMM route): W2^T [E][F][d] and [W1^T | W3^T] [E][d][ig F]
+    if (!nn) {
+        moe::launch_transpose(W2, E, d, F, (int64_t)d * F, b.w2t, d, (int64_t)F * d, 0, es, h);
+        moe::launch_transpose(W1, E, F, d, (int64_t)F * d, b.w13t, (int64_t)ig * F, (int64_t)d * ig * F, 0, es, h);
+        if (swiglu)
+            moe::launch_transpose(W3, E, F, d, (int64_t)F * d, b.w13t, (int64_t)ig * F, (int64_t)d * ig * F, F, es,
+                                  h);
+    }
     // a = X W1^T and u = X W3^T: saved by the forward (pre = [a | u], row
     // stride ig F; routed experts only), else recomputed.  dh = DY W2.  The
     // first GEMM also builds the offsets of a single group.
@@ -646,14 +668,26 @@ moe_status expert_backward(const moe_config* c, const void* X, const void* DY, i
             return s;
     }
     const int32_t* offs = offsets ? offsets : plan_copy;
-    if ((s = bwd_gemm(bf, DY, d, b.w2t, (int64_t)F * d, b.dh, F, F, d, E, rows, offsets, L, ws, plan_copy, h)) !=
-        MOE_OK)
+    if (nn) {
+        // a single group needs its offsets before the NN product reads them
+        if (!offsets) moe::launch_single_group_offsets(plan_copy, rows, h);
+        const hipError_t e2 = moe::launch_gemm_nn(DY, d, W2, nullptr, d, F, (int64_t)d * F, b.dh, F, F, d, E, offs,
+                                                  rows, nn_prefix, h);
+        if (e2 != hipSuccess) return hip_status(e2);
+    } else if ((s = bwd_gemm(bf, DY, d, b.w2t, (int64_t)F * d, b.dh, F, F, d, E, rows, offsets, L, ws, plan_copy,
+                             h)) != MOE_OK) {
         return s;
+    }
     moe::launch_bwd_act(bf, swiglu, b.dh, A_, U_, ld_au, offs, offsets ? E : 1, rows, F, b.dadu, b.hh, h);
     // DX = da W1 + du W3 as one product over the concatenated reduction
-    if ((s = bwd_gemm(bf, b.dadu, (int64_t)ig * F, b.w13t, (int64_t)d * ig * F, DX, d, d, ig * F, E, rows, offsets, L,
-                      ws, plan_copy, h)) != MOE_OK)
+    if (nn) {
+        const hipError_t e2 = moe::launch_gemm_nn(b.dadu, (int64_t)ig * F, W1, swiglu ? W3 : nullptr, F, d,
+                                                  (int64_t)F * d, DX, d, d, ig * F, E, offs, rows, nn_prefix, h);
+        if (e2 != hipSuccess) return hip_status(e2);
+    } else if ((s = bwd_gemm(bf, b.dadu, (int64_t)ig * F, b.w13t, (int64_t)d * ig * F, DX, d, d, ig * F, E, rows,
+                             offsets, L, ws, plan_copy, h)) != MOE_OK) {
         return s;
+    }
     if (!dW1) return MOE_OK;
     hipError_t e;
     const int Eg = offsets ? E : 1;
@@ -747,8 +781,12 @@ moe_status moe_layer_backward(const moe_config* c, const moe_weights* w, const v
             moe::launch_bwd_wr(bf, dz, x, T, E, d, at<float>(ws, L.wr_part), g->dw_router, g->dlogit_bias, h);
         }
     }
+    // dz vanishes off the selected experts for the softmax-over-selected and
+    // sigmoid gates (not for the full softmax and expert choice)
+    const bool sparse_dz = c->gate == MOE_GATE_SOFTMAX_TOPK || c->gate == MOE_GATE_SIGMOID_BIAS;
     moe::launch_bwd_dx(bf, dy, at<void>(ws, L.dxp), sv->slot_pos, ns, sh ? at<void>(ws, L.sdx) : nullptr, dz,
-                       hashed ? nullptr : w->w_router, T, E, d, (c->flags & MOE_F_ADD_RESIDUAL) != 0, g->dx, h);
+                       sparse_dz ? sv->topk_idx : nullptr, hashed ? nullptr : w->w_router, T, E, d,
+                       (c->flags & MOE_F_ADD_RESIDUAL) != 0, g->dx, h);
     return after_launch();
 }
 

@@ -205,3 +205,67 @@ def test_backward_full_size_mixtral_sampled():
             err = rel_inf(got, want)
             log(f"  {key}[{e}] column/row {f}: rel err {err:.2e}")
             assert err <= TOL_OUT[dt]
+
+
+def test_backward_full_size_dsv3_sampled():
+    """DeepSeek-V3 shape (T 4096, d 7168, d_ff 2048, 256 experts, top-8,
+    sigmoid gate with selection bias, one shared expert, bf16): sampled
+    token gradients (routed rows, shared expert and router term) and one
+    expert's weight-gradient rows against the oracle's chain rule."""
+    cfg = workloads.get("dsv3")
+    log("[backward parity] dsv3 full size, sampled")
+    inp = workloads.make_inputs(cfg)
+    dy = workloads.make_output_grad(cfg)
+    dinp = to_device(inp)
+    sv, g = run_forward_backward(cfg, dinp, dy.to("cuda"), save=True)
+    del dinp
+    torch.cuda.empty_cache()
+    dt = "bf16"
+    x = oracle.act_to_f64(inp["x"], dt)
+    dY = oracle.act_to_f64(dy, dt)
+    idx, gates = sv["topk_idx"].numpy(), sv["topk_gate"].numpy().astype(np.float64)
+    slot_pos = sv["slot_pos"].numpy()
+    off = sv["expert_offsets"].numpy()
+    perm_src = sv["perm_src"].numpy()
+    y_perm = as_f64(sv["y_perm"])
+    Wr = inp["w_router"].double().numpy()
+    sb = inp["sel_bias"].double().numpy()
+    s1, s3, s2 = inp["ws_gate"][0], inp["ws_up"][0], inp["ws_down"][0]
+    rng = np.random.default_rng(13)
+    z_all = x @ Wr.T                           # fp64 logits (the device uses fp32: within tolerance)
+    for t in rng.choice(cfg.T, 2, replace=False):
+        want = np.zeros(cfg.d)
+        dgt = np.zeros(cfg.k)
+        for j in range(cfg.k):
+            r, e = int(slot_pos[t, j]), int(idx[t, j])
+            dgt[j] = float(np.dot(dY[t], y_perm[r]))
+            b = ob.expert_backward(cfg, x[t:t + 1], gates[t, j] * dY[t:t + 1], inp["w_gate"][e], inp["w_up"][e],
+                                   inp["w_down"][e])
+            want += b["dx"][0]
+        want += ob.expert_backward(cfg, x[t:t + 1], dY[t:t + 1], s1, s3, s2)["dx"][0]
+        sel = idx[t]
+        s = 1.0 / (1.0 + np.exp(-z_all[t, sel]))
+        c = float(np.dot(gates[t], dgt))
+        want += ((dgt - c) / s.sum() * s * (1.0 - s)) @ Wr[sel]
+        err = rel_inf(as_f64(g["dx"][t]), want)
+        log(f"  dx[{t}]: rel err {err:.2e}")
+        assert err <= TOL_OUT[dt]
+        assert np.isfinite(sb).all()
+    e = int(np.argmax(np.diff(off)))           # the busiest expert
+    lo, hi = int(off[e]), int(off[e + 1])
+    rows_t, rows_j = perm_src[lo:hi] // cfg.k, perm_src[lo:hi] % cfg.k
+    Xe = x[rows_t]
+    DYe = gates[rows_t, rows_j][:, None] * dY[rows_t]
+    W1e = oracle.act_to_f64(inp["w_gate"][e], dt)
+    W3e = oracle.act_to_f64(inp["w_up"][e], dt)
+    W2e = oracle.act_to_f64(inp["w_down"][e], dt)
+    for f in rng.choice(cfg.F, 3, replace=False):
+        a, u = Xe @ W1e[f], Xe @ W3e[f]
+        s = 1.0 / (1.0 + np.exp(-a))
+        dh = DYe @ W2e[:, f]
+        for key, want in (("dw_down", DYe.T @ (a * s * u)), ("dw_gate", (dh * u * s * (1.0 + a * (1.0 - s))) @ Xe),
+                          ("dw_up", (dh * a * s) @ Xe)):
+            got = as_f64(g[key][e][:, f]) if key == "dw_down" else as_f64(g[key][e][f])
+            err = rel_inf(got, want)
+            log(f"  {key}[{e}] ({hi - lo} rows) column/row {f}: rel err {err:.2e}")
+            assert err <= TOL_OUT[dt]
