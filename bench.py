@@ -96,16 +96,22 @@ def cpu_baseline(cfg, dinp, target_s):
 
     # two probes give the per-token slope and the fixed per-call cost (the
     # oracle converts every weight to fp64 on each call), then one run sized
-    # for target_s
-    t1 = run(min(8, cfg.T))
-    if cfg.T <= 8 or t1 >= target_s:
-        ts, t = min(8, cfg.T), t1
+    # for target_s; the second probe is large enough (128 tokens) that the
+    # slope holds at the sized run, where small per-expert row counts no
+    # longer hide the per-row cost
+    n1, n2 = min(16, cfg.T), min(128, cfg.T)
+    t1 = run(n1)
+    if cfg.T <= n1 or t1 >= target_s:
+        ts, t = n1, t1
     else:
-        t2 = run(min(32, cfg.T))
-        slope = max((t2 - t1) / (min(32, cfg.T) - 8), 1e-6)
-        fixed = max(t1 - 8 * slope, 0.0)
-        ts = int(min(cfg.T, max(32, (target_s - fixed) / slope)))
-        t = run(ts) if ts > 32 else t2
+        t2 = run(n2)
+        if n2 == cfg.T or t2 >= target_s:
+            ts, t = n2, t2
+        else:
+            slope = max((t2 - t1) / (n2 - n1), 1e-6)
+            fixed = max(t1 - n1 * slope, 0.0)
+            ts = int(min(cfg.T, max(n2, (target_s - fixed) / slope)))
+            t = run(ts) if ts > n2 else t2
     return {"value": ts / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {ts} of the {cfg.T} tokens, whole layer (route, dispatch, experts, combine) "
                       f"with all weights, {t:.1f} s of oracle time"}
