@@ -45,6 +45,9 @@
 //     accumulators of the same (row, unit) in one lane and writes h directly.
 //   * Split-K tail: a mostly empty last round of tiles is cut into K ranges
 //     (second launch, fp32 partials) and reduced in order by k_split_fixup.
+//   * Remainder tiles: with 256-row tiles, an expert's last <= 128 rows go to
+//     a further launch of 64-row tiles (kRemBM), so a row count just past a
+//     multiple of 256 does not pay for a whole padded tile.
 #include <type_traits>
 
 #include "device_common.h"
@@ -79,7 +82,17 @@ struct GemmParams {
     float* partial;         // split-K partial accumulators
     void* C2;               // pre-activations (_SAVE epilogues)
     int64_t ldc2;
+    int rem_bm;             // > 0: row tiles start after the expert's first
+                            // floor(M_e / rem_bm) * rem_bm rows (remainder launch)
 };
+
+// First row of row tile mt of expert e.  The remainder launch covers the rows
+// left after the expert's whole tiles of the main launch (rem_bm rows each).
+__device__ __forceinline__ int tile_row0(const GemmParams& p, int e, int mt, int BM) {
+    int base = p.offsets[e];
+    if (p.rem_bm > 0) base += (p.offsets[e + 1] - base) / p.rem_bm * p.rem_bm;
+    return base + mt * BM;
+}
 
 // Work decomposition.  The plan lists ceil(M_e / BM) row tiles per expert,
 // each with NT column tiles, T tiles in all.  When the last round of tiles
@@ -90,6 +103,18 @@ struct GemmParams {
 // do not depend on timing.  kSplitUnits is the CU count of the target chip.
 constexpr int kSplitUnits = 256;
 constexpr int kMaxSplit = 16;
+
+// Remainder tiles.  With 256-row tiles an expert whose row count lies just
+// past a multiple of 256 pays a whole tile of padding rows for a few real
+// ones.  When at most kRemThr rows are left after an expert's whole tiles,
+// they go to a second launch of kRemBM-row tiles (ceil(r / kRemBM) of them,
+// a quarter of the MFMA work of a 256-row tile each) instead.  Each launch
+// has its own plan, and its own split-K tail.
+#ifndef MOE_GEMM_REM
+#define MOE_GEMM_REM 1
+#endif
+constexpr int kRemBM = 64;
+constexpr int kRemThr = 128;
 
 // Tile L of the natural order: experts in order; inside an expert, groups of
 // NG column tiles, row tiles fastest inside a group.
@@ -299,7 +324,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     }
     int e, mt, nt;
     decode_tile(p, L, e, mt, nt);
-    const int row0 = p.offsets[e] + mt * BM;
+    const int row0 = tile_row0(p, e, mt, BM);
     const int rows = min(BM, p.offsets[e + 1] - row0);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -577,63 +602,81 @@ __global__ __launch_bounds__(64) void k_split_fixup(GemmParams p) {
     }
     int e, mt, nt;
     decode_tile(p, full + t, e, mt, nt);
-    const int row0 = p.offsets[e] + mt * BM;
+    const int row0 = tile_row0(p, e, mt, BM);
     const int rows = min(BM, p.offsets[e + 1] - row0);
     Epi::store_cols(p, acc, i0, row0, rows, nt, w >> 1, w & 1, lane);
 #endif
 }
 
-// Tile plan: prefix[e+1] = sum_{e' <= e} ceil(M_e' / BM), then the split-K
-// decision {full, split, tail} (see kSplitUnits).  With offsets == NULL the
-// plan describes one group of uniform_rows rows and offsets_copy receives
-// {0, uniform_rows}.  One block of 1024 threads (E <= 1024).
+// Tile plan: prefix[e+1] = sum_{e' <= e} (row tiles of expert e'), then the
+// split-K decision {full, split, tail} (see kSplitUnits).  Expert e has
+// ceil(M_e / BM) row tiles, or, with rem_bm > 0 and a remainder
+// r = M_e mod BM in 1 .. kRemThr, floor(M_e / BM) tiles here and
+// ceil(r / rem_bm) tiles in the remainder plan, which follows at
+// prefix[E + 4] in the same layout.  With offsets == NULL the plan describes
+// one group of uniform_rows rows and offsets_copy receives {0, uniform_rows}.
+// One block of 1024 threads (E <= 1024).
 __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ offsets, int E, int uniform_rows,
-                                                    int BM, int NT, int nk, int32_t* __restrict__ prefix,
-                                                    int32_t* __restrict__ offsets_copy) {
-    __shared__ int32_t scan[1024];
+                                                    int BM, int rem_bm, int NT, int nk,
+                                                    int32_t* __restrict__ prefix, int32_t* __restrict__ offsets_copy) {
+    __shared__ int32_t scan[2][1024];
     const int e = threadIdx.x;
-    int32_t n = 0;
+    int32_t M = 0;
     if (offsets == nullptr) {
         if (e == 0) {
             offsets_copy[0] = 0;
             offsets_copy[1] = uniform_rows;
-            n = (uniform_rows + BM - 1) / BM;
+            M = uniform_rows;
         }
         E = 1;
     } else if (e < E) {
-        const int32_t M = offsets[e + 1] - offsets[e];
-        n = (M + BM - 1) / BM;
+        M = offsets[e + 1] - offsets[e];
     }
-    scan[e] = n;
+    int32_t n = (M + BM - 1) / BM, n2 = 0;
+    if (rem_bm > 0) {
+        const int32_t r = M % BM;
+        if (r > 0 && r <= kRemThr) {
+            n = M / BM;
+            n2 = (r + rem_bm - 1) / rem_bm;
+        }
+    }
+    scan[0][e] = n;
+    scan[1][e] = n2;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
-        const int32_t v = e >= off ? scan[e - off] : 0;
+        const int32_t v0 = e >= off ? scan[0][e - off] : 0;
+        const int32_t v1 = e >= off ? scan[1][e - off] : 0;
         __syncthreads();
-        scan[e] += v;
+        scan[0][e] += v0;
+        scan[1][e] += v1;
         __syncthreads();
     }
-    if (e == 0) prefix[0] = 0;
-    if (e < E) prefix[e + 1] = scan[e];
-    if (e == 0) {
-        const int total = scan[E - 1] * NT;
-        const int rem = total % kSplitUnits;
-        int split = 1, tail = 0;
-        if (rem > 0 && rem <= kSplitUnits / 2) {
-            int sp = kSplitUnits / rem;
-            sp = min(sp, kMaxSplit);
-            sp = min(sp, nk / 4);                  // at least 4 slices per range
-            if (sp >= 2) {
-                split = sp;
-                tail = rem;
+    const int plans = rem_bm > 0 ? 2 : 1;
+    for (int h = 0; h < plans; ++h) {
+        int32_t* pr = prefix + h * (E + 4);
+        if (e == 0) pr[0] = 0;
+        if (e < E) pr[e + 1] = scan[h][e];
+        if (e == 0) {
+            const int total = scan[h][E - 1] * NT;
+            const int rem = total % kSplitUnits;
+            int split = 1, tail = 0;
+            if (rem > 0 && rem <= kSplitUnits / 2) {
+                int sp = kSplitUnits / rem;
+                sp = min(sp, kMaxSplit);
+                sp = min(sp, nk / 4);                  // at least 4 slices per range
+                if (sp >= 2) {
+                    split = sp;
+                    tail = rem;
+                }
             }
+            pr[E + 1] = total - tail;
+            pr[E + 2] = split;
+            pr[E + 3] = tail;
         }
-        prefix[E + 1] = total - tail;
-        prefix[E + 2] = split;
-        prefix[E + 3] = tail;
     }
 }
 
-size_t ffn_tile_plan_ints(int E) { return (size_t)(E + 1) + 3; }
+size_t ffn_tile_plan_ints(int E) { return 2 * ((size_t)E + 4); }
 
 size_t gemm_partial_bytes(int BM, int BN) { return (size_t)kSplitUnits * BM * BN * sizeof(float); }
 
@@ -707,14 +750,24 @@ hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, c
     p.partial = partial;
     p.C2 = C2;
     p.ldc2 = ldc2;
-    hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, offsets, E, (int)max_rows, BM, p.NT, p.nk, plan,
-                       plan_copy);
+    p.rem_bm = 0;
+    const bool rem = MOE_GEMM_REM && bf16 && BM == 256;
+    hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, offsets, E, (int)max_rows, BM, rem ? kRemBM : 0, p.NT,
+                       p.nk, plan, plan_copy);
     const int64_t m_tiles_ub = (max_rows + BM - 1) / BM + (p.E > 1 ? p.E : 0);
     int64_t grid = (m_tiles_ub * p.NT + 7) / 8 * 8;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     if (!bf16 && BM > 128) return hipErrorInvalidValue;
     if (bf16) launch_t<true>(epi, p, BM, BN, (int)grid, s);
     else launch_t<false>(epi, p, BM, BN, (int)grid, s);
+    if (rem) {
+        GemmParams q = p;
+        q.plan = plan + (p.E + 4);
+        q.rem_bm = BM;
+        const int64_t grid2 = ((int64_t)p.E * ((kRemThr + kRemBM - 1) / kRemBM) * p.NT + 7) / 8 * 8;
+        if (grid2 > 0x7fffffff) return hipErrorInvalidValue;
+        launch_t<true>(epi, q, kRemBM, BN, (int)grid2, s);
+    }
     return hipGetLastError();
 }
 

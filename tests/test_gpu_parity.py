@@ -15,6 +15,7 @@ import torch
 import oracle
 import workloads
 from workloads import Config
+import sparse_mixture_experts_39_amd as moe
 import tests.gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
@@ -215,6 +216,40 @@ def test_empty_batch():
     assert (g["offsets"].numpy() == 0).all()
     assert (g["stats"]["counts"].numpy() == 0).all()
     assert int(g["stats"]["n_dropped"][0]) == 0
+
+
+# Expert row counts that put every kind of remainder after 256-row tiles:
+# none, 1, 64, 65, 128 (these go to the 64-row remainder launch), 129 and 255
+# (a whole 256-row tile), and experts smaller than one tile.  The caller hands
+# the offsets straight to moe_expert_ffn; every row is checked.
+REM_COUNTS = [256, 257, 320, 321, 384, 385, 511, 0, 1, 64, 100, 128, 129, 577]
+
+
+@pytest.mark.parametrize("act", ["swiglu", "relu"])
+def test_expert_ffn_remainder_tiles(act):
+    E = len(REM_COUNTS)
+    cfg = Config("rem_" + act, T=2700, d=512, F=512, E=E, k=2, act_dtype="bf16", act=act,
+                 gate="softmax_topk", seed=31)
+    c = H.bind_config(cfg)
+    R = moe.max_rows(c)
+    assert sum(REM_COUNTS) <= R and R // E >= 384     # 256-row tiles are chosen for this average
+    inp = workloads.make_inputs(cfg)
+    d = H.to_device(inp)
+    x_perm = torch.cat([d["x"], d["x"]])[:R].contiguous()
+    off = np.concatenate([[0], np.cumsum(REM_COUNTS)]).astype(np.int32)
+    offsets = torch.from_numpy(off).to("cuda")
+    y_perm = torch.zeros((R, cfg.d), dtype=torch.bfloat16, device="cuda")
+    H.log(f"[rem] {act}: expert_ffn with counts {REM_COUNTS}")
+    moe.moe_expert_ffn(c, x_perm, offsets, moe.weights_from(c, d), y_perm, moe.workspace(c))
+    torch.cuda.synchronize()
+    xp = x_perm.cpu()
+    y = y_perm.cpu()
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        ref = oracle.expert_ffn(cfg, xp[lo:hi], *oracle.expert_weights(cfg, inp, e))
+        H.assert_close_rel(H.as_f64(y[lo:hi]), ref, "bf16", f"expert {e} ({hi - lo} rows)")
 
 
 def test_nonfinite_input_sets_device_status():
