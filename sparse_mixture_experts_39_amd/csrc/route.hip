@@ -156,6 +156,151 @@ __global__ __launch_bounds__(NT) void k_router_dots(const void* __restrict__ x, 
     }
 }
 
+// Few score columns (NC < 64), d a multiple of 128: one wave per block, one
+// output per lane (BE columns x 64/BE tokens).  There are only T*NC/64 waves,
+// at most a couple per CU, so nothing else runs while a wave waits for
+// memory: K chunks of 128 are fetched S chunks ahead straight into a ring of
+// LDS slots (direct-to-LDS loads, no staging registers, waits with fixed
+// counts), and every output still walks i = 0..d-1 in order with one fma per
+// step.  The rows of a slot are XOR swizzled in 16-byte chunks so that the
+// lanes reading different rows at one k hit distinct banks.  Each slot is an
+// LDS array of its own and the chunk loop is unrolled over the slots, so the
+// compiler sees which loads fill the slot being read and waits for those
+// only (with one array it would wait for every load in flight).
+template <int BE, bool BF16>
+struct RingDots {
+    static constexpr int KC = 128, BT = 64 / BE, XS = BF16 ? 2 : 4;
+    static constexpr int XROW = KC * XS, WROW = KC * 4;      // bytes per row of a slot
+    static constexpr int XB = BT * XROW, WB = BE * WROW;     // x and w bytes per slot
+    static constexpr int XI = XB / 1024, WI = WB / 1024, NI = XI + WI;   // 1 KB loads per chunk
+    static constexpr int SB = XB + WB;
+    static constexpr int S_VM = 63 / NI + 1;                 // slots the vmcnt range allows
+    static constexpr int S_LDS = 64 * 1024 / SB;             // slots within 64 KB of LDS
+    static constexpr int S = S_VM < S_LDS ? (S_VM < 8 ? S_VM : 8) : (S_LDS < 8 ? S_LDS : 8);
+    static constexpr bool ok = XB % 1024 == 0 && WB % 1024 == 0 && S >= 2;
+};
+
+template <int N>
+__device__ __forceinline__ void dots_wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+template <int BE, bool BF16>
+__global__ __launch_bounds__(64) void k_router_dots_ring(const void* __restrict__ x, const float* __restrict__ w0,
+                                                         const float* __restrict__ w1, int T, int d, int E, int NC,
+                                                         float* __restrict__ dots) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    (void)w1;
+    typedef RingDots<BE, BF16> P;
+    constexpr int KC = P::KC, BT = P::BT, XS = P::XS, XROW = P::XROW, WROW = P::WROW, XB = P::XB;
+    constexpr int XI = P::XI, WI = P::WI, NI = P::NI, SB = P::SB, S = P::S;
+    constexpr int XCH = XROW / 16, WCH = WROW / 16;          // 16-byte chunks per row
+    static_assert(P::ok, "shape does not tile into whole 1 KB loads");
+    typedef __attribute__((address_space(3))) void* lds_ptr_t;
+    static_assert(S <= 8, "at most 8 slots");
+    __shared__ __align__(16) uint8_t sl0[SB], sl1[SB], sl2[SB], sl3[SB], sl4[SB], sl5[SB], sl6[SB], sl7[SB];
+    auto slot = [&](int j) -> uint8_t* {
+        return j == 0 ? sl0 : j == 1 ? sl1 : j == 2 ? sl2 : j == 3 ? sl3 : j == 4 ? sl4 : j == 5 ? sl5 : j == 6 ? sl6 : sl7;
+    };
+
+    const int lane = threadIdx.x;
+    const int cg = lane % BE, tg = lane / BE;
+    const int t0 = blockIdx.x * BT;
+    const int nch = d / KC;
+
+    // per-lane byte offset of each 1 KB load: x rows (tokens clamped to
+    // T - 1), then w rows (columns clamped to NC - 1, NC == E here); LDS
+    // chunk p of row r holds logical chunk p ^ (r mod chunks per row).
+    // Buffer descriptors hold the bases, the chunk's K offset goes in the
+    // scalar offset.
+    constexpr int kRsrcWord3 = 0x00020000;
+    const __amdgpu_buffer_rsrc_t rsx =
+        __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)((int64_t)T * d * XS), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rsw =
+        __builtin_amdgcn_make_buffer_rsrc((void*)w0, (short)0, (int)((int64_t)E * d * 4), kRsrcWord3);
+    uint32_t offx[XI], offw[WI];
+#pragma unroll
+    for (int q = 0; q < XI; ++q) {
+        const int o = q * 1024 + 16 * lane;
+        const int r = o / XROW, pc = (o % XROW) / 16;
+        offx[q] = (uint32_t)(min(t0 + r, T - 1) * d * XS + ((pc ^ (r % XCH)) * 16));
+    }
+#pragma unroll
+    for (int q = 0; q < WI; ++q) {
+        const int o = q * 1024 + 16 * lane;
+        const int r = o / WROW, pc = (o % WROW) / 16;
+        offw[q] = (uint32_t)(min(r, NC - 1) * d * 4 + ((pc ^ (r % WCH)) * 16));
+    }
+    // chunk v goes to slot j = v % S (j is a compile-time constant at every
+    // call); past the last chunk the last one is fetched again, so every
+    // iteration issues NI loads
+    auto issue = [&](int j, int v) {
+        uint8_t* sl = slot(j);
+        const int kc = min(v, nch - 1) * KC;
+#pragma unroll
+        for (int q = 0; q < XI; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (lds_ptr_t)(sl + q * 1024), 16, offx[q], kc * XS, 0, 0);
+#pragma unroll
+        for (int q = 0; q < WI; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)(sl + XB + q * 1024), 16, offw[q], kc * 4, 0, 0);
+    };
+
+#pragma unroll
+    for (int v = 0; v < S - 1; ++v) issue(v, v);
+    float acc = 0.0f;
+    for (int c0 = 0; c0 < nch; c0 += S) {
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+        const int c = c0 + j;
+        if (c >= nch) break;
+        // the slot of chunk c - 1 is rewritten below: its reads are done
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue((j + S - 1) % S, c + S - 1);
+        dots_wait_vmcnt<(S - 1) * NI>();     // chunk c has landed
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const uint8_t* xrow = slot(j) + tg * XROW;
+        const uint8_t* wrow = slot(j) + XB + cg * WROW;
+        // 16-byte chunk j of this lane's x and w rows
+        auto X = [&](int j) { return *(const u32x4_t*)(xrow + ((j ^ (tg % XCH)) * 16)); };
+        auto W = [&](int j) { return *(const float4*)(wrow + ((j ^ (cg % WCH)) * 16)); };
+#pragma unroll
+        for (int g = 0; g < KC / 8; ++g) {          // 8 steps: k = 8g .. 8g + 7
+            const float4 wa = W(2 * g), wb = W(2 * g + 1);
+            float xv[8];
+            if constexpr (BF16) {
+                const u32x4_t v = X(g);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    xv[2 * h] = __uint_as_float(v[h] << 16);
+                    xv[2 * h + 1] = __uint_as_float(v[h] & 0xffff0000u);
+                }
+            } else {
+                const u32x4_t v0 = X(2 * g), v1 = X(2 * g + 1);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    xv[h] = __uint_as_float(v0[h]);
+                    xv[4 + h] = __uint_as_float(v1[h]);
+                }
+            }
+            acc = __builtin_fmaf(xv[0], wa.x, acc);
+            acc = __builtin_fmaf(xv[1], wa.y, acc);
+            acc = __builtin_fmaf(xv[2], wa.z, acc);
+            acc = __builtin_fmaf(xv[3], wa.w, acc);
+            acc = __builtin_fmaf(xv[4], wb.x, acc);
+            acc = __builtin_fmaf(xv[5], wb.y, acc);
+            acc = __builtin_fmaf(xv[6], wb.z, acc);
+            acc = __builtin_fmaf(xv[7], wb.w, acc);
+        }
+    }
+    }
+    dots_wait_vmcnt<0>();   // refetches of the last chunk may still be landing
+    const int t = t0 + tg;
+    if (t < T && cg < NC) dots[(int64_t)t * NC + cg] = acc;
+#endif
+}
+
 // ---------------------------------------------------------------------------
 // selection, gates, probabilities
 // ---------------------------------------------------------------------------
@@ -1031,6 +1176,16 @@ static void launch_dots_t(const void* x, const float* w0, const float* w1, int T
         return;
     }
     const int BE = pow2_at_least(NC);
+    if (d % 128 == 0 && BE >= 2 && BE <= 16 && NC == E && (int64_t)T * d * (BF16 ? 2 : 4) < (1ll << 31)) {
+        dim3 grid((T + 64 / BE - 1) / (64 / BE), 1);
+        switch (BE) {
+            case 2: hipLaunchKernelGGL((k_router_dots_ring<2, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, NC, dots); break;
+            case 4: hipLaunchKernelGGL((k_router_dots_ring<4, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, NC, dots); break;
+            case 8: hipLaunchKernelGGL((k_router_dots_ring<8, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, NC, dots); break;
+            default: hipLaunchKernelGGL((k_router_dots_ring<16, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, NC, dots); break;
+        }
+        return;
+    }
     const int BT = 64 / BE;
     dim3 grid((T + BT - 1) / BT, 1);
     // K chunks of 128 when d allows it, else 64 (d is a multiple of 64)

@@ -218,6 +218,27 @@ def test_empty_batch():
     assert int(g["stats"]["n_dropped"][0]) == 0
 
 
+# Router products at few columns (one wave per block, K chunks of 128 through
+# a ring of LDS slots when d is a multiple of 128): every column count class,
+# both dtypes, fewer chunks than ring slots and more (with a ragged last
+# round), a ragged last block of tokens.  The scores must be bit-identical.
+ROUTER_SHAPES = [(2, "bf16", 384), (3, "f32", 1152), (4, "bf16", 1152), (5, "f32", 384), (8, "bf16", 1152),
+                 (8, "f32", 384), (12, "bf16", 384), (16, "bf16", 1152), (16, "f32", 1152), (32, "bf16", 384),
+                 (8, "bf16", 320)]
+
+
+@pytest.mark.parametrize("E,dt,d", ROUTER_SHAPES)
+def test_router_dots_shapes(E, dt, d):
+    cfg = Config(f"dots_{E}_{dt}_{d}", T=777, d=d, F=64, E=E, k=min(2, E), act_dtype=dt, act="relu",
+                 gate="softmax_topk", seed=40 + E)
+    H.log(f"[dots] E={E} {dt} d={d}")
+    inp = workloads.make_inputs(cfg)
+    g = H.run_stages(cfg, H.to_device(inp))
+    o = oracle.route(cfg, inp["x"], inp["w_router"])
+    o["status"] = 0
+    H.compare_route(cfg, g, o, cfg.T)
+
+
 # Expert row counts that put every kind of remainder after 256-row tiles:
 # none, 1, 64, 65, 128 (these go to the 64-row remainder launch), 129 and 255
 # (a whole 256-row tile), and experts smaller than one tile.  The caller hands
