@@ -21,7 +21,9 @@
 //                 experts -> offsets, and the load statistics
 //   k_scatter     same ranking as k_histogram, plus the wave prefix inside the
 //                 block -> slot_pos / perm_src
-//   k_permute     x_perm[row] = x[perm_src[row] / k], 16-byte vector copies
+//   k_permute_tokens  token-major: each token row of x is read once and
+//                 written to the rows its kept slots point at (slot_pos),
+//                 16-byte vector copies
 #include "device_common.h"
 #include "kernels.h"
 
@@ -167,32 +169,36 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ top
     }
 }
 
-// Grid-stride over (row, 16-byte chunk); rows >= offsets[E] are not copied.
-__global__ __launch_bounds__(256) void k_permute(const uint4* __restrict__ x, int k, int cpr,
-                                                 const int32_t* __restrict__ perm_src,
-                                                 const int32_t* __restrict__ offsets, int E, int64_t max_rows,
-                                                 uint4* __restrict__ x_perm) {
-    const int64_t R = offsets[E];
-    const int64_t total = (R < max_rows ? R : max_rows) * cpr;
+// Grid-stride over (token, 16-byte chunk): the chunk is read once and stored
+// to every kept slot's row.  A wave covers consecutive chunks of one row, so
+// its slot_pos reads hit one address.
+__global__ __launch_bounds__(256) void k_permute_tokens(const uint4* __restrict__ x, int k, int cpr,
+                                                        const int32_t* __restrict__ slot_pos, int64_t T,
+                                                        uint4* __restrict__ x_perm) {
+    const int64_t total = T * cpr;
     const int64_t stride = (int64_t)gridDim.x * 256 * 4;
     for (int64_t base = (int64_t)blockIdx.x * 256 * 4 + threadIdx.x; base < total; base += stride) {
         uint4 v[4];
-        int64_t dst[4];
+        int64_t t[4];
+        int c[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int64_t i = base + (int64_t)u * 256;
-            dst[u] = -1;
+            t[u] = -1;
             if (i < total) {
-                const int64_t row = i / cpr;
-                const int c = (int)(i - row * cpr);
-                const int64_t t = perm_src[row] / k;
-                v[u] = x[t * cpr + c];
-                dst[u] = i;
+                t[u] = i / cpr;
+                c[u] = (int)(i - t[u] * cpr);
+                v[u] = x[i];
             }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (dst[u] >= 0) x_perm[dst[u]] = v[u];
+        for (int u = 0; u < 4; ++u) {
+            if (t[u] < 0) continue;
+            for (int j = 0; j < k; ++j) {
+                const int32_t r = slot_pos[t[u] * k + j];
+                if (r >= 0) x_perm[(int64_t)r * cpr + c[u]] = v[u];
+            }
+        }
     }
 }
 
@@ -218,15 +224,15 @@ void launch_scatter(const int32_t* topk_idx, int64_t n_assign, int E, const int3
                        blockbase, offsets, capacity, perm_src, slot_pos);
 }
 
-void launch_permute_rows(const void* x, int k, int d, int elem_bytes, const int32_t* perm_src, const int32_t* offsets,
-                         int E, int64_t max_rows, void* x_perm, hipStream_t s) {
+void launch_permute_tokens(const void* x, int k, int d, int elem_bytes, const int32_t* slot_pos, int64_t T,
+                           void* x_perm, hipStream_t s) {
     const int cpr = d * elem_bytes / 16;
-    const int64_t total = max_rows * cpr;
+    const int64_t total = T * cpr;
     if (total == 0) return;
     int64_t nb = (total + 1023) / 1024;
     if (nb > 16384) nb = 16384;
-    hipLaunchKernelGGL(k_permute, dim3((unsigned)nb), dim3(256), 0, s, (const uint4*)x, k, cpr, perm_src, offsets, E,
-                       max_rows, (uint4*)x_perm);
+    hipLaunchKernelGGL(k_permute_tokens, dim3((unsigned)nb), dim3(256), 0, s, (const uint4*)x, k, cpr, slot_pos, T,
+                       (uint4*)x_perm);
 }
 
 }  // namespace moe

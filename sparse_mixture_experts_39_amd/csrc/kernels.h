@@ -51,8 +51,9 @@ void launch_scan(const int32_t* hist, int nblocks, int E, int64_t capacity,
                  int32_t* blockbase, int32_t* offsets, const float* P, const moe_stats* st, hipStream_t s);
 void launch_scatter(const int32_t* topk_idx, int64_t n_assign, int E, const int32_t* blockbase,
                     const int32_t* offsets, int64_t capacity, int32_t* perm_src, int32_t* slot_pos, hipStream_t s);
-void launch_permute_rows(const void* x, int k, int d, int elem_bytes, const int32_t* perm_src, const int32_t* offsets,
-                         int E, int64_t max_rows, void* x_perm, hipStream_t s);
+// Token-major copy: x[t] to row slot_pos[t][j] for every kept slot j.
+void launch_permute_tokens(const void* x, int k, int d, int elem_bytes, const int32_t* slot_pos, int64_t T,
+                           void* x_perm, hipStream_t s);
 
 // combine.hip
 void launch_combine(const void* y_perm, const int32_t* slot_pos, const float* gates, const void* residual,

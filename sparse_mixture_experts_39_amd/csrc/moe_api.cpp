@@ -438,8 +438,7 @@ moe_status moe_dispatch(const moe_config* c, const void* x, const int32_t* topk_
     moe::launch_histogram(topk_idx, na, E, hist, h);
     moe::launch_scan(hist, nb, E, cap, bbase, expert_offsets, P, st, h);
     moe::launch_scatter(topk_idx, na, E, bbase, expert_offsets, cap, perm_src, slot_pos, h);
-    moe::launch_permute_rows(x, slots_of(c), c->d_model, elem_bytes(c), perm_src, expert_offsets, E, max_rows_of(c),
-                             x_perm, h);
+    moe::launch_permute_tokens(x, slots_of(c), c->d_model, elem_bytes(c), slot_pos, c->T, x_perm, h);
     return after_launch();
 }
 

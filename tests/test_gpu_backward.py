@@ -40,6 +40,10 @@ CASES = {
                               seed=207),
     "bf16_no_tokens": dict(T=0, d=128, F=128, E=8, k=2, act_dtype="bf16", act="swiglu", gate="softmax_topk",
                            seed=208),
+    # about 800 rows per expert: 256-row tiles, and every expert's last 14..47
+    # rows go to the 64-row remainder launch (forward up/down, dh, dx)
+    "bf16_swiglu_256_tiles": dict(T=1600, d=256, F=256, E=4, k=2, act_dtype="bf16", act="swiglu",
+                                  gate="softmax_topk", seed=209),
 }
 
 
@@ -98,7 +102,8 @@ def _grad_names(cfg):
     return [("dw_gate", "dw1"), ("dw_down", "dw2")]
 
 
-SAVED = ["f32_swiglu_topk_resid", "bf16_swiglu_topk_drops", "f32_relu_full_switch", "bf16_expert_choice"]
+SAVED = ["f32_swiglu_topk_resid", "bf16_swiglu_topk_drops", "f32_relu_full_switch", "bf16_expert_choice",
+         "bf16_swiglu_256_tiles"]
 
 
 @pytest.mark.parametrize("name,save", [(n, False) for n in CASES] + [(n, True) for n in SAVED])
