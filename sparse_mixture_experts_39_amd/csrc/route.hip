@@ -1170,9 +1170,22 @@ template <bool BF16>
 static void launch_dots_t(const void* x, const float* w0, const float* w1, int T, int d, int E, int NC, float* dots,
                           hipStream_t s) {
     if (NC >= 64) {
-        dim3 grid((T + 63) / 64, (NC + 63) / 64);
-        hipLaunchKernelGGL((k_router_dots<4, 4, 64, 256, 64, BF16>), grid, dim3(256), 0, s, x, w0, w1, T, d, E, NC,
-                           dots);
+        // 16 x TT tokens x 64 columns per block of 256 threads; TT is the
+        // largest of 4, 2, 1 that still gives at least 512 blocks (two per CU),
+        // so that a CU has a second block to run while one waits on memory
+        const int cb = (NC + 63) / 64;
+        int TT = 4;
+        while (TT > 1 && (int64_t)((T + 16 * TT - 1) / (16 * TT)) * cb < 512) TT /= 2;
+        dim3 grid((T + 16 * TT - 1) / (16 * TT), cb);
+        if (TT == 4)
+            hipLaunchKernelGGL((k_router_dots<4, 4, 64, 256, 64, BF16>), grid, dim3(256), 0, s, x, w0, w1, T, d, E, NC,
+                               dots);
+        else if (TT == 2)
+            hipLaunchKernelGGL((k_router_dots<2, 4, 64, 256, 64, BF16>), grid, dim3(256), 0, s, x, w0, w1, T, d, E, NC,
+                               dots);
+        else
+            hipLaunchKernelGGL((k_router_dots<1, 4, 64, 256, 64, BF16>), grid, dim3(256), 0, s, x, w0, w1, T, d, E, NC,
+                               dots);
         return;
     }
     const int BE = pow2_at_least(NC);

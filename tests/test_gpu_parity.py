@@ -221,10 +221,11 @@ def test_empty_batch():
 # Router products at few columns (one wave per block, K chunks of 128 through
 # a ring of LDS slots when d is a multiple of 128): every column count class,
 # both dtypes, fewer chunks than ring slots and more (with a ragged last
-# round), a ragged last block of tokens.  The scores must be bit-identical.
+# round), a ragged last block of tokens; and two shapes of the many-column
+# kernel.  The scores must be bit-identical.
 ROUTER_SHAPES = [(2, "bf16", 384), (3, "f32", 1152), (4, "bf16", 1152), (5, "f32", 384), (8, "bf16", 1152),
                  (8, "f32", 384), (12, "bf16", 384), (16, "bf16", 1152), (16, "f32", 1152), (32, "bf16", 384),
-                 (8, "bf16", 320)]
+                 (8, "bf16", 320), (64, "bf16", 384), (96, "f32", 384)]
 
 
 @pytest.mark.parametrize("E,dt,d", ROUTER_SHAPES)
