@@ -240,6 +240,35 @@ def test_router_dots_shapes(E, dt, d):
     H.compare_route(cfg, g, o, cfg.T)
 
 
+# Dispatch against the oracle's stable counting sort at larger sizes: 16384
+# assignments and one more, one expert, capacity drops under a skewed router
+# (most assignments of the busiest experts dropped), four slots per token.
+DISPATCH_CASES = {
+    "disp_e8_k2": dict(T=4096, E=8, k=2),
+    "disp_e16_full": dict(T=16384, E=16, k=1),
+    "disp_e16_over": dict(T=16385, E=16, k=1),
+    "disp_e16_cap_zipf": dict(T=16384, E=16, k=1, capacity_factor=1.25, logit_bias="zipf"),
+    "disp_e12_k4_cap_zipf": dict(T=4096, E=12, k=4, capacity_factor=1.1, logit_bias="zipf"),
+    "disp_e5_k3_cap": dict(T=1000, E=5, k=3, capacity_factor=1.0),
+    "disp_e1": dict(T=700, E=1, k=1),
+}
+
+
+@pytest.mark.parametrize("name", list(DISPATCH_CASES))
+def test_dispatch_sizes_and_drops(name):
+    kw = DISPATCH_CASES[name]
+    cfg = Config(name, d=64, F=64, act_dtype="bf16", act="relu", gate="softmax_topk", residual=True, seed=50, **kw)
+    H.log(f"[dispatch] {name}")
+    inp = workloads.make_inputs(cfg)
+    g = H.run_stages(cfg, H.to_device(inp))
+    o = oracle.route(cfg, inp["x"], inp["w_router"], logit_bias=inp.get("logit_bias"))
+    o.update(oracle.dispatch(cfg, o["idx"]))
+    o.update(oracle.stats(cfg, o["counts"], o["kept"], o["P"], cfg.T))
+    o["status"] = 0
+    H.compare_route(cfg, g, o, cfg.T)
+    H.compare_dispatch(cfg, g, o)
+
+
 # Expert row counts that put every kind of remainder after 256-row tiles:
 # none, 1, 64, 65, 128 (these go to the 64-row remainder launch), 129 and 255
 # (a whole 256-row tile), and experts smaller than one tile.  The caller hands
