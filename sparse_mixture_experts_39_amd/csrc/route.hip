@@ -164,9 +164,11 @@ __global__ __launch_bounds__(NT) void k_router_dots(const void* __restrict__ x, 
 // counts), and every output still walks i = 0..d-1 in order with one fma per
 // step.  The rows of a slot are XOR swizzled in 16-byte chunks so that the
 // lanes reading different rows at one k hit distinct banks.  Each slot is an
-// LDS array of its own and the chunk loop is unrolled over the slots, so the
-// compiler sees which loads fill the slot being read and waits for those
-// only (with one array it would wait for every load in flight).
+// LDS array of its own and the chunk loop is unrolled over the slots: with
+// one array the compiler, unable to tell which bytes the loads in flight
+// write, waited for all of them before some of the reads; this way most of
+// its waits coincide with the fixed-count ones (it still drains part of the
+// ring at a few slots).
 template <int BE, bool BF16>
 struct RingDots {
     static constexpr int KC = 128, BT = 64 / BE, XS = BF16 ? 2 : 4;
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(64) void k_router_dots_ring(const void* __restrict_
     float acc = 0.0f;
     for (int c0 = 0; c0 < nch; c0 += S) {
 #pragma unroll
-    for (int j = 0; j < S; ++j) {
+      for (int j = 0; j < S; ++j) {
         const int c = c0 + j;
         if (c >= nch) break;
         // the slot of chunk c - 1 is rewritten below: its reads are done
@@ -262,9 +264,9 @@ __global__ __launch_bounds__(64) void k_router_dots_ring(const void* __restrict_
         asm volatile("" ::: "memory");
         const uint8_t* xrow = slot(j) + tg * XROW;
         const uint8_t* wrow = slot(j) + XB + cg * WROW;
-        // 16-byte chunk j of this lane's x and w rows
-        auto X = [&](int j) { return *(const u32x4_t*)(xrow + ((j ^ (tg % XCH)) * 16)); };
-        auto W = [&](int j) { return *(const float4*)(wrow + ((j ^ (cg % WCH)) * 16)); };
+        // 16-byte chunk q of this lane's x and w rows
+        auto X = [&](int q) { return *(const u32x4_t*)(xrow + ((q ^ (tg % XCH)) * 16)); };
+        auto W = [&](int q) { return *(const float4*)(wrow + ((q ^ (cg % WCH)) * 16)); };
 #pragma unroll
         for (int g = 0; g < KC / 8; ++g) {          // 8 steps: k = 8g .. 8g + 7
             const float4 wa = W(2 * g), wb = W(2 * g + 1);
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(64) void k_router_dots_ring(const void* __restrict_
             acc = __builtin_fmaf(xv[6], wb.z, acc);
             acc = __builtin_fmaf(xv[7], wb.w, acc);
         }
-    }
+      }
     }
     dots_wait_vmcnt<0>();   // refetches of the last chunk may still be landing
     const int t = t0 + tg;
