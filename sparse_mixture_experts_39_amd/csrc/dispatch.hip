@@ -18,7 +18,8 @@
 //                 in LDS; per-block histogram hist[b][e]
 //   k_scan        one block: column scan over blocks (rank base of each block
 //                 inside each expert), capacity cut, exclusive scan over
-//                 experts -> offsets, and the load statistics
+//                 experts -> offsets, and the load statistics; k_scan_wave
+//                 is the same for at most 64 experts in one wave
 //   k_scatter     same ranking as k_histogram, plus the wave prefix inside the
 //                 block -> slot_pos / perm_src
 //   k_permute_tokens  token-major: each token row of x is read once and
@@ -138,6 +139,75 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ hist,
     }
 }
 
+// k_scan for at most 64 experts: one wave, lane e = expert e, shuffles
+// instead of LDS and barriers.  The sums are the same: the integer scans are
+// exact, and the fixed halving tree of the aux sum differs from the wide
+// kernel's only in levels that add zeros.
+__global__ __launch_bounds__(64) void k_scan_wave(const int32_t* __restrict__ hist, int nblocks, int E,
+                                                  int64_t capacity, int32_t* __restrict__ blockbase,
+                                                  int32_t* __restrict__ offsets, const float* __restrict__ P,
+                                                  int32_t* counts_out, int32_t* kept_out, float* f_out,
+                                                  int32_t* dropped_out, float* imbalance_out, float* aux_out) {
+    const int e = threadIdx.x;
+    int32_t c = 0, kp = 0;
+    if (e < E) {
+        int32_t run = 0;
+        int b = 0;
+        for (; b + 16 <= nblocks; b += 16) {
+            int32_t h[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) h[u] = hist[(int64_t)(b + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                blockbase[(int64_t)(b + u) * E + e] = run;
+                run += h[u];
+            }
+        }
+        for (; b < nblocks; ++b) {
+            blockbase[(int64_t)b * E + e] = run;
+            run += hist[(int64_t)b * E + e];
+        }
+        c = run;
+        kp = (capacity >= 0 && (int64_t)c > capacity) ? (int32_t)capacity : c;
+    }
+    int32_t sc = kp;   // inclusive scan of kept over experts
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t v = __shfl_up(sc, off, 64);
+        if (e >= off) sc += v;
+    }
+    int64_t kt = kp, ct = c;
+    int32_t mx = c;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        kt += __shfl_down(kt, off, 64);
+        ct += __shfl_down(ct, off, 64);
+        mx = max(mx, __shfl_down(mx, off, 64));
+    }
+    kt = __shfl(kt, 0, 64);
+    ct = __shfl(ct, 0, 64);
+    mx = __shfl(mx, 0, 64);
+    if (e < E) {
+        offsets[e] = sc - kp;
+        if (e == E - 1) offsets[E] = sc;
+        if (counts_out) counts_out[e] = c;
+        if (kept_out) kept_out[e] = kp;
+    }
+    const double fe = (e < E && ct > 0) ? (double)c / (double)ct : 0.0;
+    if (e < E && f_out) f_out[e] = (float)fe;
+    double ax = (e < E && P) ? fe * (double)P[e] : 0.0;
+#pragma unroll
+    for (int half = 32; half >= 1; half >>= 1) {
+        const double o = __shfl_down(ax, half, 64);
+        if (e < half) ax += o;
+    }
+    if (e == 0) {
+        if (dropped_out) dropped_out[0] = (int32_t)(ct - kt);
+        if (imbalance_out) imbalance_out[0] = ct > 0 ? (float)((double)mx * (double)E / (double)ct) : 0.0f;
+        if (aux_out && P) aux_out[0] = (float)((double)E * ax);
+    }
+}
+
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ topk_idx, int64_t n_assign, int E,
                                                  int ebits, const int32_t* __restrict__ blockbase,
                                                  const int32_t* __restrict__ offsets, int64_t capacity,
@@ -211,9 +281,14 @@ void launch_histogram(const int32_t* topk_idx, int64_t n_assign, int E, int32_t*
 
 void launch_scan(const int32_t* hist, int nblocks, int E, int64_t capacity, int32_t* blockbase,
                  int32_t* offsets, const float* P, const moe_stats* st, hipStream_t s) {
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, nblocks, E, capacity, blockbase, offsets, P,
-                       st ? st->counts : nullptr, st ? st->kept : nullptr, st ? st->f : nullptr,
-                       st ? st->n_dropped : nullptr, st ? st->imbalance : nullptr, st ? st->aux : nullptr);
+    if (E <= 64)
+        hipLaunchKernelGGL(k_scan_wave, dim3(1), dim3(64), 0, s, hist, nblocks, E, capacity, blockbase, offsets, P,
+                           st ? st->counts : nullptr, st ? st->kept : nullptr, st ? st->f : nullptr,
+                           st ? st->n_dropped : nullptr, st ? st->imbalance : nullptr, st ? st->aux : nullptr);
+    else
+        hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, nblocks, E, capacity, blockbase, offsets, P,
+                           st ? st->counts : nullptr, st ? st->kept : nullptr, st ? st->f : nullptr,
+                           st ? st->n_dropped : nullptr, st ? st->imbalance : nullptr, st ? st->aux : nullptr);
 }
 
 void launch_scatter(const int32_t* topk_idx, int64_t n_assign, int E, const int32_t* blockbase,
