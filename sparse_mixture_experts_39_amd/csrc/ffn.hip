@@ -48,6 +48,7 @@
 //   * Remainder tiles: with 256-row tiles, an expert's last <= 128 rows go to
 //     a further launch of 64-row tiles (kRemBM), so a row count just past a
 //     multiple of 256 does not pay for a whole padded tile.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -694,45 +695,58 @@ GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N) {
     return g;
 }
 
-// Whole tiles, split units (exit at once when the plan has no split), fixup.
+// Whole tiles, split units (exit at once when the plan has no split), fixup;
+// the last two only when the plan may have a split.
 template <bool BF16, int BM, int BN, int EPI>
-static void launch_pair(const GemmParams& p, int grid, hipStream_t s) {
+static void launch_pair(const GemmParams& p, int grid, bool may_split, hipStream_t s) {
     hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, false>), dim3(grid), dim3(256), 0, s, p);
+    if (!may_split) return;
     hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, true>), dim3(kSplitUnits), dim3(256), 0, s, p);
     constexpr int groups = GemmEpilogue<BF16, BM, BN, EPI>::FN / GemmEpilogue<BF16, BM, BN, EPI>::IG;
     hipLaunchKernelGGL((k_split_fixup<BF16, BM, BN, EPI>), dim3(kSplitUnits / 2 * 4 * groups), dim3(64), 0, s, p);
 }
 
 template <bool BF16, int BM, int BN>
-static void launch_bmbn(int epi, const GemmParams& p, int grid, hipStream_t s) {
+static void launch_bmbn(int epi, const GemmParams& p, int grid, bool ms, hipStream_t s) {
     switch (epi) {
-        case EPI_STORE: launch_pair<BF16, BM, BN, EPI_STORE>(p, grid, s); break;
-        case EPI_RELU: launch_pair<BF16, BM, BN, EPI_RELU>(p, grid, s); break;
-        case EPI_RELU_SAVE: launch_pair<BF16, BM, BN, EPI_RELU_SAVE>(p, grid, s); break;
-        case EPI_SWIGLU_SAVE: launch_pair<BF16, BM, BN, EPI_SWIGLU_SAVE>(p, grid, s); break;
-        default: launch_pair<BF16, BM, BN, EPI_SWIGLU>(p, grid, s); break;
+        case EPI_STORE: launch_pair<BF16, BM, BN, EPI_STORE>(p, grid, ms, s); break;
+        case EPI_RELU: launch_pair<BF16, BM, BN, EPI_RELU>(p, grid, ms, s); break;
+        case EPI_RELU_SAVE: launch_pair<BF16, BM, BN, EPI_RELU_SAVE>(p, grid, ms, s); break;
+        case EPI_SWIGLU_SAVE: launch_pair<BF16, BM, BN, EPI_SWIGLU_SAVE>(p, grid, ms, s); break;
+        default: launch_pair<BF16, BM, BN, EPI_SWIGLU>(p, grid, ms, s); break;
     }
 }
 
 template <bool BF16>
-static void launch_t(int epi, const GemmParams& p, int BM, int BN, int grid, hipStream_t s) {
+static void launch_t(int epi, const GemmParams& p, int BM, int BN, int grid, bool ms, hipStream_t s) {
     if constexpr (BF16) {
         if (BM == 256) {
-            if (BN == 256) return launch_bmbn<BF16, 256, 256>(epi, p, grid, s);
-            if (BN == 128) return launch_bmbn<BF16, 256, 128>(epi, p, grid, s);
-            return launch_bmbn<BF16, 256, 64>(epi, p, grid, s);
+            if (BN == 256) return launch_bmbn<BF16, 256, 256>(epi, p, grid, ms, s);
+            if (BN == 128) return launch_bmbn<BF16, 256, 128>(epi, p, grid, ms, s);
+            return launch_bmbn<BF16, 256, 64>(epi, p, grid, ms, s);
         }
     }
     if (BN == 256) {
-        if (BM == 128) return launch_bmbn<BF16, 128, 256>(epi, p, grid, s);
-        return launch_bmbn<BF16, 64, 256>(epi, p, grid, s);
+        if (BM == 128) return launch_bmbn<BF16, 128, 256>(epi, p, grid, ms, s);
+        return launch_bmbn<BF16, 64, 256>(epi, p, grid, ms, s);
     }
     if (BN == 128) {
-        if (BM == 128) return launch_bmbn<BF16, 128, 128>(epi, p, grid, s);
-        return launch_bmbn<BF16, 64, 128>(epi, p, grid, s);
+        if (BM == 128) return launch_bmbn<BF16, 128, 128>(epi, p, grid, ms, s);
+        return launch_bmbn<BF16, 64, 128>(epi, p, grid, ms, s);
     }
-    if (BM == 128) return launch_bmbn<BF16, 128, 64>(epi, p, grid, s);
-    return launch_bmbn<BF16, 64, 64>(epi, p, grid, s);
+    if (BM == 128) return launch_bmbn<BF16, 128, 64>(epi, p, grid, ms, s);
+    return launch_bmbn<BF16, 64, 64>(epi, p, grid, ms, s);
+}
+
+// Whether a plan of `total` tiles takes the split-K tail (the rule of
+// k_tile_plan, for launches whose row counts the host knows).
+static bool plan_may_split(int64_t total, int nk) {
+    const int64_t rem = total % kSplitUnits;
+    if (rem <= 0 || rem > kSplitUnits / 2) return false;
+    int64_t sp = kSplitUnits / rem;
+    sp = std::min<int64_t>(sp, kMaxSplit);
+    sp = std::min<int64_t>(sp, nk / 4);
+    return sp >= 2;
 }
 
 hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B0, const void* B1,
@@ -758,15 +772,26 @@ hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, c
     int64_t grid = (m_tiles_ub * p.NT + 7) / 8 * 8;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     if (!bf16 && BM > 128) return hipErrorInvalidValue;
-    if (bf16) launch_t<true>(epi, p, BM, BN, (int)grid, s);
-    else launch_t<false>(epi, p, BM, BN, (int)grid, s);
-    if (rem) {
+    // With offsets == NULL the host knows the row count and launches only
+    // the parts of the plan that have work; routed counts live on the device.
+    bool main_split = true, rem_launch = rem, rem_split = true;
+    if (offsets == nullptr) {
+        const int64_t r = max_rows % BM;
+        const bool rem_active = rem && r > 0 && r <= kRemThr;
+        const int64_t n_main = rem_active ? max_rows / BM : (max_rows + BM - 1) / BM;
+        main_split = plan_may_split(n_main * p.NT, p.nk);
+        rem_launch = rem_active;
+        rem_split = rem_active && plan_may_split((r + kRemBM - 1) / kRemBM * p.NT, p.nk);
+    }
+    if (bf16) launch_t<true>(epi, p, BM, BN, (int)grid, main_split, s);
+    else launch_t<false>(epi, p, BM, BN, (int)grid, main_split, s);
+    if (rem_launch) {
         GemmParams q = p;
         q.plan = plan + (p.E + 4);
         q.rem_bm = BM;
         const int64_t grid2 = ((int64_t)p.E * ((kRemThr + kRemBM - 1) / kRemBM) * p.NT + 7) / 8 * 8;
         if (grid2 > 0x7fffffff) return hipErrorInvalidValue;
-        launch_t<true>(epi, q, kRemBM, BN, (int)grid2, s);
+        launch_t<true>(epi, q, kRemBM, BN, (int)grid2, rem_split, s);
     }
     return hipGetLastError();
 }
