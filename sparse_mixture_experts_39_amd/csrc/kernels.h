@@ -12,8 +12,10 @@
 namespace moe {
 
 // route.hip
+// zero_word (optional) is set to 0 by this launch, visible to later launches on the stream.
 void launch_router_dots(bool bf16, const void* x, const float* w0, const float* w1, int T, int d, int E, int NC,
-                        float* dots, hipStream_t s);
+                        float* dots, hipStream_t s,
+                        int32_t* zero_word = nullptr);
 int select_blocks(int T, int E);
 // Hierarchical gate: A groups of E / A experts, KP groups then KS experts per
 // group per token; P partials of hier_select_blocks(T) blocks.

@@ -352,11 +352,14 @@ moe_status moe_route(const moe_config* c, const void* x, const moe_weights* w, i
     const bool balance = st && (st->z_loss || st->importance || st->importance_cv2 || st->load || st->load_cv2 ||
                                 st->seq_aux);
     if ((hashed || hierarchical(c)) && balance) return MOE_ERR_UNSUPPORTED;
-    moe::launch_zero_i32(status, 1, h);
-    if (!hashed)
+    // the device status word is cleared by the router product (or on its own
+    // without one); the selection sets it after
+    if (hashed)
+        moe::launch_zero_i32(status, 1, h);
+    else
         moe::launch_router_dots(is_bf16(c), x, w->w_router,
                                 noisy ? w->w_noise : (hierarchical(c) ? w->w_group_router : nullptr), T, c->d_model,
-                                E, NC, dots, h);
+                                E, NC, dots, h, status);
     if (hierarchical(c)) {
         moe::launch_select_hier(dots, NC, w->logit_bias, T, E, c->n_groups, c->group_top_k,
                                 c->top_k / c->group_top_k, topk_idx, topk_gate, scores, at<float>(ws, L.P_part),

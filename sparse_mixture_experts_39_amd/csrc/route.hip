@@ -42,7 +42,8 @@ namespace moe {
 template <int TT, int EE, int BE, int NT, int KC, bool BF16>
 __global__ __launch_bounds__(NT) void k_router_dots(const void* __restrict__ x, const float* __restrict__ w0,
                                                     const float* __restrict__ w1, int T, int d, int E, int NC,
-                                                    float* __restrict__ dots) {
+                                                    float* __restrict__ dots, int32_t* __restrict__ zero_word) {
+    if (zero_word && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) zero_word[0] = 0;
     constexpr int LD = KC + 4;
     constexpr int NCG = BE / EE;          // column groups
     constexpr int NTG = NT / NCG;         // token groups
@@ -191,9 +192,10 @@ __device__ __forceinline__ void dots_wait_vmcnt() {
 template <int BE, bool BF16>
 __global__ __launch_bounds__(64) void k_router_dots_ring(const void* __restrict__ x, const float* __restrict__ w0,
                                                          const float* __restrict__ w1, int T, int d, int E, int NC,
-                                                         float* __restrict__ dots) {
+                                                         float* __restrict__ dots, int32_t* __restrict__ zero_word) {
 #if defined(__HIP_DEVICE_COMPILE__)
     (void)w1;
+    if (zero_word && blockIdx.x == 0 && threadIdx.x == 0) zero_word[0] = 0;
     typedef RingDots<BE, BF16> P;
     constexpr int KC = P::KC, BT = P::BT, XS = P::XS, XROW = P::XROW, WROW = P::WROW, XB = P::XB;
     constexpr int XI = P::XI, WI = P::WI, NI = P::NI, SB = P::SB, S = P::S;
@@ -1170,7 +1172,7 @@ static int pow2_at_least(int v) { int p = 1; while (p < v) p <<= 1; return p; }
 
 template <bool BF16>
 static void launch_dots_t(const void* x, const float* w0, const float* w1, int T, int d, int E, int NC, float* dots,
-                          hipStream_t s) {
+                          int32_t* zero_word, hipStream_t s) {
     if (NC >= 64) {
         // 16 x TT tokens x 64 columns per block of 256 threads; TT is the
         // largest of 4, 2, 1 that still gives at least 512 blocks (two per CU),
@@ -1181,23 +1183,23 @@ static void launch_dots_t(const void* x, const float* w0, const float* w1, int T
         dim3 grid((T + 16 * TT - 1) / (16 * TT), cb);
         if (TT == 4)
             hipLaunchKernelGGL((k_router_dots<4, 4, 64, 256, 64, BF16>), grid, dim3(256), 0, s, x, w0, w1, T, d, E, NC,
-                               dots);
+                               dots, zero_word);
         else if (TT == 2)
             hipLaunchKernelGGL((k_router_dots<2, 4, 64, 256, 64, BF16>), grid, dim3(256), 0, s, x, w0, w1, T, d, E, NC,
-                               dots);
+                               dots, zero_word);
         else
             hipLaunchKernelGGL((k_router_dots<1, 4, 64, 256, 64, BF16>), grid, dim3(256), 0, s, x, w0, w1, T, d, E, NC,
-                               dots);
+                               dots, zero_word);
         return;
     }
     const int BE = pow2_at_least(NC);
     if (d % 128 == 0 && BE >= 2 && BE <= 16 && NC == E && (int64_t)T * d * (BF16 ? 2 : 4) < (1ll << 31)) {
         dim3 grid((T + 64 / BE - 1) / (64 / BE), 1);
         switch (BE) {
-            case 2: hipLaunchKernelGGL((k_router_dots_ring<2, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, NC, dots); break;
-            case 4: hipLaunchKernelGGL((k_router_dots_ring<4, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, NC, dots); break;
-            case 8: hipLaunchKernelGGL((k_router_dots_ring<8, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, NC, dots); break;
-            default: hipLaunchKernelGGL((k_router_dots_ring<16, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, NC, dots); break;
+            case 2: hipLaunchKernelGGL((k_router_dots_ring<2, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, NC, dots, zero_word); break;
+            case 4: hipLaunchKernelGGL((k_router_dots_ring<4, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, NC, dots, zero_word); break;
+            case 8: hipLaunchKernelGGL((k_router_dots_ring<8, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, NC, dots, zero_word); break;
+            default: hipLaunchKernelGGL((k_router_dots_ring<16, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, NC, dots, zero_word); break;
         }
         return;
     }
@@ -1210,10 +1212,10 @@ static void launch_dots_t(const void* x, const float* w0, const float* w1, int T
     case B:                                                                                                     \
         if (k128)                                                                                               \
             hipLaunchKernelGGL((k_router_dots<1, 1, B, 64, 128, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E, \
-                               NC, dots);                                                                       \
+                               NC, dots, zero_word);                                                                     \
         else                                                                                                    \
             hipLaunchKernelGGL((k_router_dots<1, 1, B, 64, 64, BF16>), grid, dim3(64), 0, s, x, w0, w1, T, d, E,  \
-                               NC, dots);                                                                       \
+                               NC, dots, zero_word);                                                                     \
         break;
         MOE_DOTS_CASE(1) MOE_DOTS_CASE(2) MOE_DOTS_CASE(4) MOE_DOTS_CASE(8) MOE_DOTS_CASE(16) MOE_DOTS_CASE(32)
 #undef MOE_DOTS_CASE
@@ -1221,10 +1223,13 @@ static void launch_dots_t(const void* x, const float* w0, const float* w1, int T
 }
 
 void launch_router_dots(bool bf16, const void* x, const float* w0, const float* w1, int T, int d, int E, int NC,
-                        float* dots, hipStream_t s) {
-    if (T <= 0) return;
-    if (bf16) launch_dots_t<true>(x, w0, w1, T, d, E, NC, dots, s);
-    else launch_dots_t<false>(x, w0, w1, T, d, E, NC, dots, s);
+                        float* dots, hipStream_t s, int32_t* zero_word) {
+    if (T <= 0) {
+        if (zero_word) launch_zero_i32(zero_word, 1, s);
+        return;
+    }
+    if (bf16) launch_dots_t<true>(x, w0, w1, T, d, E, NC, dots, zero_word, s);
+    else launch_dots_t<false>(x, w0, w1, T, d, E, NC, dots, zero_word, s);
 }
 
 int select_blocks(int T, int E) {
