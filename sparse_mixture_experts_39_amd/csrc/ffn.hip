@@ -617,9 +617,13 @@ __global__ __launch_bounds__(64) void k_split_fixup(GemmParams p) {
 // prefix[E + 4] in the same layout.  With offsets == NULL the plan describes
 // one group of uniform_rows rows and offsets_copy receives {0, uniform_rows}.
 // One block of 1024 threads (E <= 1024).
+// With prefix2 != NULL the same block also writes the plan of a second GEMM
+// over the same groups (BM2, rem_bm2, NT2, nk2), so two GEMMs share a launch.
 __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ offsets, int E, int uniform_rows,
                                                     int BM, int rem_bm, int NT, int nk,
-                                                    int32_t* __restrict__ prefix, int32_t* __restrict__ offsets_copy) {
+                                                    int32_t* __restrict__ prefix, int32_t* __restrict__ offsets_copy,
+                                                    int BM2, int rem_bm2, int NT2, int nk2,
+                                                    int32_t* __restrict__ prefix2) {
     __shared__ int32_t scan[2][1024];
     const int e = threadIdx.x;
     int32_t M = 0;
@@ -633,51 +637,76 @@ __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ 
     } else if (e < E) {
         M = offsets[e + 1] - offsets[e];
     }
-    int32_t n = (M + BM - 1) / BM, n2 = 0;
-    if (rem_bm > 0) {
-        const int32_t r = M % BM;
-        if (r > 0 && r <= kRemThr) {
-            n = M / BM;
-            n2 = (r + rem_bm - 1) / rem_bm;
-        }
-    }
-    scan[0][e] = n;
-    scan[1][e] = n2;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int32_t v0 = e >= off ? scan[0][e - off] : 0;
-        const int32_t v1 = e >= off ? scan[1][e - off] : 0;
-        __syncthreads();
-        scan[0][e] += v0;
-        scan[1][e] += v1;
-        __syncthreads();
-    }
-    const int plans = rem_bm > 0 ? 2 : 1;
-    for (int h = 0; h < plans; ++h) {
-        int32_t* pr = prefix + h * (E + 4);
-        if (e == 0) pr[0] = 0;
-        if (e < E) pr[e + 1] = scan[h][e];
-        if (e == 0) {
-            const int total = scan[h][E - 1] * NT;
-            const int rem = total % kSplitUnits;
-            int split = 1, tail = 0;
-            if (rem > 0 && rem <= kSplitUnits / 2) {
-                int sp = kSplitUnits / rem;
-                sp = min(sp, kMaxSplit);
-                sp = min(sp, nk / 4);                  // at least 4 slices per range
-                if (sp >= 2) {
-                    split = sp;
-                    tail = rem;
-                }
+    auto plan = [&](int bm, int rbm, int nt, int nkk, int32_t* pre) {
+        int32_t n = (M + bm - 1) / bm, n2 = 0;
+        if (rbm > 0) {
+            const int32_t r = M % bm;
+            if (r > 0 && r <= kRemThr) {
+                n = M / bm;
+                n2 = (r + rbm - 1) / rbm;
             }
-            pr[E + 1] = total - tail;
-            pr[E + 2] = split;
-            pr[E + 3] = tail;
         }
-    }
+        __syncthreads();   // a previous plan's reads of scan are done
+        scan[0][e] = n;
+        scan[1][e] = n2;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int32_t v0 = e >= off ? scan[0][e - off] : 0;
+            const int32_t v1 = e >= off ? scan[1][e - off] : 0;
+            __syncthreads();
+            scan[0][e] += v0;
+            scan[1][e] += v1;
+            __syncthreads();
+        }
+        const int plans = rbm > 0 ? 2 : 1;
+        for (int h = 0; h < plans; ++h) {
+            int32_t* pr = pre + h * (E + 4);
+            if (e == 0) pr[0] = 0;
+            if (e < E) pr[e + 1] = scan[h][e];
+            if (e == 0) {
+                const int total = scan[h][E - 1] * nt;
+                const int rem = total % kSplitUnits;
+                int split = 1, tail = 0;
+                if (rem > 0 && rem <= kSplitUnits / 2) {
+                    int sp = kSplitUnits / rem;
+                    sp = min(sp, kMaxSplit);
+                    sp = min(sp, nkk / 4);                 // at least 4 slices per range
+                    if (sp >= 2) {
+                        split = sp;
+                        tail = rem;
+                    }
+                }
+                pr[E + 1] = total - tail;
+                pr[E + 2] = split;
+                pr[E + 3] = tail;
+            }
+        }
+    };
+    plan(BM, rem_bm, NT, nk, prefix);
+    if (prefix2) plan(BM2, rem_bm2, NT2, nk2, prefix2);
 }
 
 size_t ffn_tile_plan_ints(int E) { return 2 * ((size_t)E + 4); }
+
+// Tile counts and K slices of a grouped GEMM as launch_grouped_gemm sets them.
+static void gemm_geometry(bool bf16, int epi, int N, int K, int BM, int BN, int& NT, int& nk, int& rem_bm) {
+    NT = epi_swiglu(epi) ? N / (BN / 2) : N / BN;
+    nk = K * (bf16 ? 2 : 4) / 128;
+    rem_bm = (MOE_GEMM_REM && bf16 && BM == 256) ? kRemBM : 0;
+}
+
+hipError_t launch_tile_plans(bool bf16, const int32_t* offsets, int E, int64_t max_rows, int epi1, int N1, int K1,
+                             int BM1, int BN1, int32_t* plan1, int epi2, int N2, int K2, int BM2, int BN2,
+                             int32_t* plan2, hipStream_t s) {
+    if (max_rows <= 0) return hipSuccess;
+    if (!offsets) return hipErrorInvalidValue;
+    int nt1, nk1, r1, nt2, nk2, r2;
+    gemm_geometry(bf16, epi1, N1, K1, BM1, BN1, nt1, nk1, r1);
+    gemm_geometry(bf16, epi2, N2, K2, BM2, BN2, nt2, nk2, r2);
+    hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, offsets, E, (int)max_rows, BM1, r1, nt1, nk1, plan1,
+                       (int32_t*)nullptr, BM2, r2, nt2, nk2, plan2);
+    return hipGetLastError();
+}
 
 size_t gemm_partial_bytes(int BM, int BN) { return (size_t)kSplitUnits * BM * BN * sizeof(float); }
 
@@ -752,7 +781,7 @@ static bool plan_may_split(int64_t total, int nk) {
 hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B0, const void* B1,
                                int64_t b_expert_stride, void* C, int64_t ldc, int N, int K, int E, int64_t max_rows,
                                const int32_t* offsets, int32_t* plan, int32_t* plan_copy, float* partial, int BM,
-                               int BN, hipStream_t s, void* C2, int64_t ldc2) {
+                               int BN, hipStream_t s, void* C2, int64_t ldc2, bool plan_ready) {
     if (max_rows <= 0) return hipSuccess;
     GemmParams p;
     p.A = A; p.lda = lda; p.B0 = B0; p.B1 = B1; p.bstride = b_expert_stride;
@@ -766,8 +795,9 @@ hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, c
     p.ldc2 = ldc2;
     p.rem_bm = 0;
     const bool rem = MOE_GEMM_REM && bf16 && BM == 256;
-    hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, offsets, E, (int)max_rows, BM, rem ? kRemBM : 0, p.NT,
-                       p.nk, plan, plan_copy);
+    if (!plan_ready)
+        hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, offsets, E, (int)max_rows, BM, rem ? kRemBM : 0,
+                           p.NT, p.nk, plan, plan_copy, 0, 0, 0, 0, (int32_t*)nullptr);
     const int64_t m_tiles_ub = (max_rows + BM - 1) / BM + (p.E > 1 ? p.E : 0);
     int64_t grid = (m_tiles_ub * p.NT + 7) / 8 * 8;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;

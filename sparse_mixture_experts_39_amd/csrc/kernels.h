@@ -80,7 +80,12 @@ hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, c
                                int64_t b_expert_stride, void* C, int64_t ldc, int N, int K, int E,
                                int64_t max_rows, const int32_t* offsets, int32_t* plan, int32_t* plan_copy,
                                float* partial, int BM, int BN, hipStream_t s, void* C2 = nullptr,
-                               int64_t ldc2 = 0);
+                               int64_t ldc2 = 0, bool plan_ready = false);
+// The tile plans of two grouped GEMMs over the same expert groups in one
+// launch; the GEMMs are then launched with plan_ready = true.
+hipError_t launch_tile_plans(bool bf16, const int32_t* offsets, int E, int64_t max_rows, int epi1, int N1, int K1,
+                             int BM1, int BN1, int32_t* plan1, int epi2, int N2, int K2, int BM2, int BN2,
+                             int32_t* plan2, hipStream_t s);
 GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N);
 
 // backward.hip

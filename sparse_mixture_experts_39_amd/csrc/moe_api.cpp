@@ -451,7 +451,8 @@ moe_status moe_dispatch(const moe_config* c, const void* x, const int32_t* topk_
 // shared expert) and the plan writes its offsets to plan_copy.
 static moe_status run_gemm(const moe_config* c, bool up, const void* a, int64_t rows, int E, const int32_t* offsets,
                            const void* w1, const void* w3, const void* w2, int F, void* dst, int32_t* plan,
-                           int32_t* plan_copy, float* partial, hipStream_t h, void* pre = nullptr) {
+                           int32_t* plan_copy, float* partial, hipStream_t h, void* pre = nullptr,
+                           bool plan_ready = false) {
     const bool bf = is_bf16(c);
     const int d = c->d_model;
     const bool swiglu = c->act == MOE_ACT_SWIGLU;
@@ -461,9 +462,10 @@ static moe_status run_gemm(const moe_config* c, bool up, const void* a, int64_t 
     const moe::GemmShape g = moe::pick_gemm_shape(bf, epi, rows, E, N);
     const hipError_t e = up ? moe::launch_grouped_gemm(bf, epi, a, d, w1, w3, (int64_t)F * d, dst, F, F, d, E, rows,
                                                        offsets, plan, plan_copy, partial, g.BM, g.BN, h, pre,
-                                                       (int64_t)(swiglu ? 2 : 1) * F)
+                                                       (int64_t)(swiglu ? 2 : 1) * F, plan_ready)
                             : moe::launch_grouped_gemm(bf, 0, a, F, w2, nullptr, (int64_t)d * F, dst, d, d, F, E,
-                                                       rows, offsets, plan, plan_copy, partial, g.BM, g.BN, h);
+                                                       rows, offsets, plan, plan_copy, partial, g.BM, g.BN, h,
+                                                       nullptr, 0, plan_ready);
     if (e != hipSuccess) return hip_status(e);
     return after_launch();
 }
@@ -531,8 +533,25 @@ moe_status moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t
     if (R == 0) return MOE_OK;
     const Layout L = compute_layout(c);
     void* H = at<void>(ws, L.H);
-    if ((s = moe_expert_up(c, x_perm, expert_offsets, w, H, ws, ws_bytes, stream)) != MOE_OK) return s;
-    return moe_expert_down(c, H, expert_offsets, w, y_perm, ws, ws_bytes, stream);
+    // both tile plans in one launch, then the two products
+    const bool bf = is_bf16(c);
+    const int E = c->n_experts, d = c->d_model, F = c->d_ff;
+    const int epi_up = c->act == MOE_ACT_SWIGLU ? 2 : 1;
+    const moe::GemmShape gu = moe::pick_gemm_shape(bf, epi_up, R, E, F);
+    const moe::GemmShape gd = moe::pick_gemm_shape(bf, 0, R, E, d);
+    hipStream_t h = (hipStream_t)stream;
+    int32_t* pu = at<int32_t>(ws, L.plan_up);
+    int32_t* pd = at<int32_t>(ws, L.plan_down);
+    int32_t* pc = at<int32_t>(ws, L.plan_copy);
+    float* part = at<float>(ws, L.partial);
+    const hipError_t e = moe::launch_tile_plans(bf, expert_offsets, E, R, epi_up, F, d, gu.BM, gu.BN, pu, 0, d, F,
+                                                gd.BM, gd.BN, pd, h);
+    if (e != hipSuccess) return hip_status(e);
+    if ((s = run_gemm(c, true, x_perm, R, E, expert_offsets, w->w_gate, w->w_up, nullptr, F, H, pu, pc, part, h,
+                      nullptr, true)) != MOE_OK)
+        return s;
+    return run_gemm(c, false, H, R, E, expert_offsets, nullptr, nullptr, w->w_down, F, y_perm, pd, pc, part, h,
+                    nullptr, true);
 }
 
 moe_status moe_shared_expert(const moe_config* c, const void* x, const moe_weights* w, void* shared_out, void* ws,
