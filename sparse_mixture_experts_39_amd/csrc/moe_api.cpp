@@ -449,6 +449,16 @@ moe_status moe_dispatch(const moe_config* c, const void* x, const int32_t* topk_
 // on the device).  up = true: a -> H (ReLU / SwiGLU epilogue); up = false:
 // H -> y.  With offsets == NULL the call covers one group of `rows` rows (the
 // shared expert) and the plan writes its offsets to plan_copy.
+// Epilogue and tile shape of one of the two products (the same for its tile
+// plan and its launch).
+static int gemm_epi(const moe_config* c, bool up, bool pre) {
+    const bool swiglu = c->act == MOE_ACT_SWIGLU;
+    return up ? (swiglu ? (pre ? 3 : 2) : (pre ? 4 : 1)) : 0;
+}
+static moe::GemmShape gemm_shape(const moe_config* c, bool up, bool pre, int64_t rows, int E, int F) {
+    return moe::pick_gemm_shape(is_bf16(c), gemm_epi(c, up, pre), rows, E, up ? F : c->d_model);
+}
+
 static moe_status run_gemm(const moe_config* c, bool up, const void* a, int64_t rows, int E, const int32_t* offsets,
                            const void* w1, const void* w3, const void* w2, int F, void* dst, int32_t* plan,
                            int32_t* plan_copy, float* partial, hipStream_t h, void* pre = nullptr,
@@ -457,9 +467,8 @@ static moe_status run_gemm(const moe_config* c, bool up, const void* a, int64_t 
     const int d = c->d_model;
     const bool swiglu = c->act == MOE_ACT_SWIGLU;
     // up with pre != NULL: the epilogue also stores the pre-activations
-    const int epi = up ? (swiglu ? (pre ? 3 : 2) : (pre ? 4 : 1)) : 0;
-    const int N = up ? F : d;
-    const moe::GemmShape g = moe::pick_gemm_shape(bf, epi, rows, E, N);
+    const int epi = gemm_epi(c, up, pre != nullptr);
+    const moe::GemmShape g = gemm_shape(c, up, pre != nullptr, rows, E, F);
     const hipError_t e = up ? moe::launch_grouped_gemm(bf, epi, a, d, w1, w3, (int64_t)F * d, dst, F, F, d, E, rows,
                                                        offsets, plan, plan_copy, partial, g.BM, g.BN, h, pre,
                                                        (int64_t)(swiglu ? 2 : 1) * F, plan_ready)
@@ -536,9 +545,9 @@ moe_status moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t
     // both tile plans in one launch, then the two products
     const bool bf = is_bf16(c);
     const int E = c->n_experts, d = c->d_model, F = c->d_ff;
-    const int epi_up = c->act == MOE_ACT_SWIGLU ? 2 : 1;
-    const moe::GemmShape gu = moe::pick_gemm_shape(bf, epi_up, R, E, F);
-    const moe::GemmShape gd = moe::pick_gemm_shape(bf, 0, R, E, d);
+    const int epi_up = gemm_epi(c, true, false);
+    const moe::GemmShape gu = gemm_shape(c, true, false, R, E, F);
+    const moe::GemmShape gd = gemm_shape(c, false, false, R, E, F);
     hipStream_t h = (hipStream_t)stream;
     int32_t* pu = at<int32_t>(ws, L.plan_up);
     int32_t* pd = at<int32_t>(ws, L.plan_down);
