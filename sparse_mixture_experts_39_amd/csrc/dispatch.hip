@@ -60,6 +60,29 @@ __global__ __launch_bounds__(256) void k_histogram(const int32_t* __restrict__ t
         hist[(int64_t)blockIdx.x * E + i] = ((cnt[i] + cnt[E + i]) + cnt[2 * E + i]) + cnt[3 * E + i];
 }
 
+// Column e of the per-block histogram: blockbase[b][e] = exclusive prefix over
+// the blocks (16 loads in flight at a time); returns the column total.
+__device__ __forceinline__ int32_t column_scan(const int32_t* __restrict__ hist, int nblocks, int E, int e,
+                                               int32_t* __restrict__ blockbase) {
+    int32_t run = 0;
+    int b = 0;
+    for (; b + 16 <= nblocks; b += 16) {
+        int32_t h[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) h[u] = hist[(int64_t)(b + u) * E + e];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            blockbase[(int64_t)(b + u) * E + e] = run;
+            run += h[u];
+        }
+    }
+    for (; b < nblocks; ++b) {
+        blockbase[(int64_t)b * E + e] = run;
+        run += hist[(int64_t)b * E + e];
+    }
+    return run;
+}
+
 __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ hist, int nblocks, int E,
                                                int64_t capacity, int32_t* __restrict__ blockbase,
                                                int32_t* __restrict__ offsets, const float* __restrict__ P,
@@ -73,24 +96,7 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ hist,
     const int e = threadIdx.x;
     int32_t c = 0, kp = 0;
     if (e < E) {
-        // column scan over the blocks, 16 loads in flight at a time
-        int32_t run = 0;
-        int b = 0;
-        for (; b + 16 <= nblocks; b += 16) {
-            int32_t h[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) h[u] = hist[(int64_t)(b + u) * E + e];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                blockbase[(int64_t)(b + u) * E + e] = run;
-                run += h[u];
-            }
-        }
-        for (; b < nblocks; ++b) {
-            blockbase[(int64_t)b * E + e] = run;
-            run += hist[(int64_t)b * E + e];
-        }
-        c = run;
+        c = column_scan(hist, nblocks, E, e, blockbase);
         kp = (capacity >= 0 && (int64_t)c > capacity) ? (int32_t)capacity : c;
     }
     // inclusive scan of kept over experts (Hillis-Steele, integers)
@@ -151,23 +157,7 @@ __global__ __launch_bounds__(64) void k_scan_wave(const int32_t* __restrict__ hi
     const int e = threadIdx.x;
     int32_t c = 0, kp = 0;
     if (e < E) {
-        int32_t run = 0;
-        int b = 0;
-        for (; b + 16 <= nblocks; b += 16) {
-            int32_t h[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) h[u] = hist[(int64_t)(b + u) * E + e];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                blockbase[(int64_t)(b + u) * E + e] = run;
-                run += h[u];
-            }
-        }
-        for (; b < nblocks; ++b) {
-            blockbase[(int64_t)b * E + e] = run;
-            run += hist[(int64_t)b * E + e];
-        }
-        c = run;
+        c = column_scan(hist, nblocks, E, e, blockbase);
         kp = (capacity >= 0 && (int64_t)c > capacity) ? (int32_t)capacity : c;
     }
     int32_t sc = kp;   // inclusive scan of kept over experts
