@@ -144,7 +144,9 @@ typedef struct {
     int32_t act_dtype;      /* moe_dtype of x, out, expert weights and intermediates */
     int32_t act;            /* moe_act */
     int32_t gate;           /* moe_gate */
-    float capacity_factor;  /* > 0: C = ceil(cf * T * k / E); <= 0: dropless */
+    double capacity_factor; /* > 0: C = ceil(cf * T * k / E) with cf read as a decimal of six
+                               places (q / 10^6, q = cf * 10^6 rounded, halves up) and the ceiling
+                               taken exactly, at most T * k; <= 0: dropless; must be finite */
     uint32_t flags;         /* MOE_F_* */
     uint64_t seed;          /* Philox key of the noisy gate */
     uint64_t noise_offset;  /* Philox counter offset (words 2,3) of the noisy gate */
@@ -226,9 +228,13 @@ moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
  * min(T*k, E*C); E*C under expert choice.  -1 for an invalid configuration. */
 int64_t moe_max_rows(const moe_config* cfg);
 
-/* Expert capacity C = ceil(capacity_factor * T * k / E) computed in fp64
- * (Lecture29, "Inference load balance"), or -1 when dropless or invalid;
- * under expert choice the tokens each expert takes. */
+/* Expert capacity C = ceil(capacity_factor * T * k / E) (Lecture29,
+ * "Inference load balance"; awesome-ai-roadmap 19.6.1 "Expert capacity"),
+ * with the factor read as the six-place decimal q / 10^6 (q = factor * 10^6
+ * rounded to the nearest integer, halves up) and the ceiling taken in exact
+ * integer arithmetic, so 1.1 * 2560 / 64 gives 44, not 45.  Clamped to T * k
+ * (to T under expert choice, where it is the tokens each expert takes).
+ * -1 when dropless or invalid. */
 int64_t moe_capacity(const moe_config* cfg);
 
 /* Selection slots per token in topk_idx / topk_gate / slot_pos: top_k, or
@@ -243,7 +249,11 @@ const char* moe_status_string(moe_status s);
 
 /* ---- stages ------------------------------------------------------------- */
 
-/* Route.  For every token: fp32 logits z = W_r x (+ logit_bias) with the
+/* Route (CS25 "Lecture29" notes, "Top-two routing": logits z = W_r x, the
+ * top-k experts, gates from the selected logits; awesome-ai-roadmap 19.3.2:
+ * the selected softmax equals the full softmax restricted to the top-k and
+ * renormalised; CS336 lecture 4 notes, section 11: the router runs in fp32).
+ * For every token: fp32 logits z = W_r x (+ logit_bias) with the
  * fixed sequential-fma order, the selection score, the k best experts
  * (score descending, ties to the lower index), the gates, and the router
  * probabilities, whose batch mean is written to stats->P.
@@ -273,7 +283,11 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* top
                         int32_t* slot_pos, const moe_stats* stats,
                         void* ws, size_t ws_bytes, void* stream);
 
-/* Expert FFNs as two grouped GEMMs over ragged per-expert row ranges:
+/* Expert FFNs (Lecture29, "Top-two routing": run each selected expert on
+ * the tokens dispatched to it; "Dense baseline": the SwiGLU MLP; Shazeer
+ * notes 2.2: the one-hidden-layer ReLU expert; CS336 lecture 4 notes,
+ * section 10: the tokens of all experts on one device become large matrix
+ * products) as two grouped GEMMs over ragged per-expert row ranges:
  * rows [off[e], off[e+1]) of x_perm go through expert e, the hidden tensor
  * is stored in the act dtype inside ws, and y_perm receives the expert
  * outputs in the same row order (fp32 accumulation).
@@ -328,8 +342,11 @@ moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t*
  * pointers or a non-finite gamma. */
 moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float gamma, float* sel_bias, void* stream);
 
-/* The whole layer: route, dispatch, experts (+ shared expert), combine, with
- * every intermediate carved from ws.  x [T][d], out [T][d].  The residual is
+/* The whole layer (Lecture29, "Top-two routing" minimal pseudocode: route,
+ * dispatch by expert, run the experts, combine and restore the token order;
+ * y = sum over the selected experts of g_i Expert_i(x); awesome-ai-roadmap
+ * 19.3.2 and 19.5 for the shared expert): route, dispatch, experts (+ shared
+ * expert), combine, with every intermediate carved from ws.  x [T][d], out [T][d].  The residual is
  * added when cfg->flags has MOE_F_ADD_RESIDUAL. */
 moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x, void* out,
                              const moe_stats* stats, void* ws, size_t ws_bytes, void* stream);

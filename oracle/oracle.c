@@ -29,9 +29,9 @@
  * SC'11) followed by the Box-Muller transform, with a fixed counter mapping.
  *
  * Parity pins are documented with the tests that apply them.  The Philox
- * stream's agreement with the published generator is parity unpinned (no
- * known-answer vectors are available here); its distribution is pinned
- * statistically.
+ * generator is pinned to the published known-answer vectors of Philox4x32-10
+ * (stored with their citation among the test fixtures); the Gaussian draws
+ * made from it are pinned statistically.
  */
 #include <math.h>
 #include <stdint.h>
@@ -542,12 +542,29 @@ OC_EXPORT int oc_route(const oc_config* cfg, const void* x, const float* w_route
 /* dispatch                                                                 */
 /* ------------------------------------------------------------------------ */
 
-/* Expert capacity C = ceil(capacity_factor * T * k / E) (Lecture29, section
- * "Inference load balance"; Switch lesson: capacity = capacity factor x
- * average tokens per expert).  Returns -1 when dropless. */
+/* Expert capacity C = ceil(alpha * T * k / E) (Lecture29, section "Inference
+ * load balance"; Switch lesson: capacity = capacity factor x average tokens
+ * per expert).  The capacity factor alpha is a decimal quantity (1.0, 1.25,
+ * 1.1, ...), so it is read as the rational q / 10^6 with q the nearest
+ * integer to alpha * 10^6 (halves up), and the ceiling is taken in exact
+ * integer arithmetic: for every factor written with at most six decimals
+ * this is the printed formula with the factor as written, with no binary
+ * rounding of the factor.  The result is clamped to `cap` (a larger
+ * capacity has no effect). */
+static int64_t decimal_capacity(double cf, int64_t T, int64_t k, int64_t E, int64_t cap) {
+    const double qd = floor(cf * 1e6 + 0.5);
+    if (!(qd < 9.0e18)) return cap;               /* beyond any integer C: nothing is cut */
+    const unsigned __int128 num = (unsigned __int128)(uint64_t)qd * (uint64_t)T * (uint64_t)k;
+    const unsigned __int128 den = (unsigned __int128)1000000u * (uint64_t)E;
+    const unsigned __int128 C = (num + den - 1) / den;
+    return C < (unsigned __int128)cap ? (int64_t)C : cap;
+}
+
+/* Token choice: -1 when dropless (factor <= 0); else the capacity above,
+ * at most T * k. */
 OC_EXPORT int64_t oc_capacity(const oc_config* cfg) {
     if (!(cfg->capacity_factor > 0.0)) return -1;
-    return (int64_t)ceil(cfg->capacity_factor * (double)cfg->T * (double)cfg->k / (double)cfg->E);
+    return decimal_capacity(cfg->capacity_factor, cfg->T, cfg->k, cfg->E, (int64_t)cfg->T * cfg->k);
 }
 
 /*
@@ -902,12 +919,11 @@ OC_EXPORT void oc_update_bias(int32_t E, const int32_t* counts, float gamma, flo
 /* ------------------------------------------------------------------------ */
 
 /* Tokens per expert under expert choice: C = ceil(cf * T * k / E) with the
- * capacity factor cf (1 when not set) and k the mean number of experts per
- * token, at most T. */
+ * capacity factor cf (1 when not set) read as a six-place decimal as for
+ * token choice, and k the mean number of experts per token, at most T. */
 OC_EXPORT int64_t oc_ec_capacity(const oc_config* cfg) {
     const double cf = cfg->capacity_factor > 0.0 ? cfg->capacity_factor : 1.0;
-    int64_t C = (int64_t)ceil(cf * (double)cfg->T * (double)cfg->k / (double)cfg->E);
-    return C < cfg->T ? C : cfg->T;
+    return decimal_capacity(cf, cfg->T, cfg->k, cfg->E, cfg->T);
 }
 
 /*

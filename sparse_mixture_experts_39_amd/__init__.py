@@ -55,7 +55,7 @@ class MoeConfig(ctypes.Structure):
         ("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
         ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32),
         ("d_ff_shared", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("act", ctypes.c_int32),
-        ("gate", ctypes.c_int32), ("capacity_factor", ctypes.c_float), ("flags", ctypes.c_uint32),
+        ("gate", ctypes.c_int32), ("capacity_factor", ctypes.c_double), ("flags", ctypes.c_uint32),
         ("seed", ctypes.c_uint64), ("noise_offset", ctypes.c_uint64),
         ("seq_len", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("n_groups", ctypes.c_int32), ("group_top_k", ctypes.c_int32),

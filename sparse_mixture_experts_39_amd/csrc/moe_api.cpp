@@ -35,19 +35,33 @@ int route_blocks(const moe_config* c) {
 int slots_of(const moe_config* c) { return expert_choice(c) ? c->n_experts : c->top_k; }
 int64_t n_assign(const moe_config* c) { return (int64_t)c->T * slots_of(c); }
 
-// tokens each expert takes under expert choice
-int64_t ec_capacity_of(const moe_config* c) {
-    const double cf = c->capacity_factor > 0.0f ? (double)c->capacity_factor : 1.0;
-    const int64_t v = (int64_t)ceil(cf * (double)c->T * (double)c->top_k / (double)c->n_experts);
-    return v < c->T ? v : c->T;
+// C = ceil(cf * T * k / E) with the capacity factor taken as the decimal it
+// is written as: cf is read as q / 10^6, q = cf * 10^6 rounded to the nearest
+// integer (halves up), and the ceiling is taken on integers, so factors such
+// as 1.1 or 0.1 give the capacity of the printed formula instead of that of
+// their nearest binary fraction.  At most `limit`.
+int64_t decimal_capacity(double cf, int64_t T, int64_t k, int64_t E, int64_t limit) {
+    const double scaled = cf * 1e6;      // own statement: never fused with the + 0.5
+    const double q = floor(scaled + 0.5);
+    if (!(q < 9.0e18)) return limit;
+    const unsigned __int128 num = (unsigned __int128)(uint64_t)q * (uint64_t)(T * k);
+    const uint64_t den = 1000000ull * (uint64_t)E;
+    const unsigned __int128 C = num / den + (num % den != 0 ? 1 : 0);
+    return C < (unsigned __int128)limit ? (int64_t)C : limit;
 }
 
-// capacity cut applied by the dispatch stage (-1: none)
+// tokens each expert takes under expert choice (cf <= 0 reads as 1; at most T)
+int64_t ec_capacity_of(const moe_config* c) {
+    const double cf = c->capacity_factor > 0.0 ? c->capacity_factor : 1.0;
+    return decimal_capacity(cf, c->T, c->top_k, c->n_experts, c->T);
+}
+
+// capacity cut applied by the dispatch stage (-1: none); at most T * k, so
+// it always fits in 32 bits
 int64_t capacity_of(const moe_config* c) {
     if (expert_choice(c)) return -1;
-    if (!(c->capacity_factor > 0.0f)) return -1;
-    const double v = ceil((double)c->capacity_factor * (double)c->T * (double)c->top_k / (double)c->n_experts);
-    return (int64_t)v;
+    if (!(c->capacity_factor > 0.0)) return -1;
+    return decimal_capacity(c->capacity_factor, c->T, c->top_k, c->n_experts, (int64_t)c->T * c->top_k);
 }
 
 int64_t max_rows_of(const moe_config* c) {
@@ -267,10 +281,10 @@ moe_status moe_validate_config(const moe_config* c) {
     if (c->top_k > c->n_experts) return MOE_ERR_INVALID_ARG;
     if (c->n_shared < 0 || c->n_shared > 1) return MOE_ERR_INVALID_ARG;
     if (c->n_shared == 1 && c->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
-    if (c->capacity_factor != c->capacity_factor) return MOE_ERR_INVALID_ARG;
+    if (!isfinite(c->capacity_factor)) return MOE_ERR_INVALID_ARG;
     if (c->flags & ~(uint32_t)(MOE_F_ADD_RESIDUAL | MOE_F_NOISE_INPUT | MOE_F_REROUTE)) return MOE_ERR_INVALID_ARG;
     if (c->flags & MOE_F_REROUTE) {
-        if (!(c->capacity_factor > 0.0f) || c->gate == MOE_GATE_EXPERT_CHOICE) return MOE_ERR_INVALID_ARG;
+        if (!(c->capacity_factor > 0.0) || c->gate == MOE_GATE_EXPERT_CHOICE) return MOE_ERR_INVALID_ARG;
         if (c->gate == MOE_GATE_HIERARCHICAL) return MOE_ERR_UNSUPPORTED;
     }
     if (c->top_k > 16 || c->n_experts > 1024) return MOE_ERR_UNSUPPORTED;

@@ -8,7 +8,9 @@
 import ctypes
 import math
 import os
+import random
 import re
+from fractions import Fraction
 
 import pytest
 
@@ -57,6 +59,9 @@ def _cfg(**kw):
     (dict(n_shared=1, d_ff_shared=0), INVALID),
     (dict(n_shared=1, d_ff_shared=64, act="relu"), UNSUPPORTED),
     (dict(capacity_factor=float("nan")), INVALID),
+    (dict(capacity_factor=float("inf")), INVALID),
+    (dict(capacity_factor=float("-inf")), INVALID),
+    (dict(capacity_factor=1e300), OK),
 ])
 def test_validate_config(kw, status):
     assert moe.validate_config(_cfg(**kw)) == status
@@ -92,6 +97,80 @@ def test_switch_capacity_is_forty():
     cfg = workloads.get("switch")
     c = moe.config(T=cfg.T, d_model=cfg.d, d_ff=cfg.F, n_experts=cfg.E, top_k=cfg.k, capacity_factor=1.25)
     assert moe.capacity(c) == 40 == math.ceil(1.25 * 2048 / 64)
+
+
+# Capacity factors as they are written (decimal strings); the pages quote
+# factors such as 1.0, 1.25 and 2.0, and the formula C = ceil(cf T k / E)
+# (Lecture29, "Inference load balance"; awesome-ai-roadmap 19.6.1).
+_CF_STRINGS = ["0.1", "0.25", "0.5", "0.9", "1.0", "1.05", "1.1", "1.2", "1.25", "1.3", "1.5", "1.7", "2.0",
+               "2.5", "3.3", "0.333333", "1.000001", "4.75"]
+
+
+def _exact_capacity(cf: str, T: int, E: int, k: int, limit: int) -> int:
+    """The printed formula on the factor as written, in exact rationals."""
+    v = Fraction(cf) * T * k / E
+    return min(limit, -(-v.numerator // v.denominator))
+
+
+def _capacity_cases():
+    rng = random.Random(20261203)
+    cases = []
+    # boundary shapes named in the review of the float32 factor: 1.1*2560/64,
+    # 1.2*4000*2/16, 0.1*160/8 land exactly on integers
+    cases += [("1.1", 2560, 64, 1), ("1.2", 4000, 16, 2), ("0.1", 160, 8, 1), ("1.25", 2048, 64, 1)]
+    while len(cases) < 640:
+        cf = rng.choice(_CF_STRINGS)
+        E = rng.choice([1, 2, 3, 6, 8, 16, 60, 64, 100, 256, 1000, 1024])
+        k = rng.randint(1, min(E, 16))
+        # half the cases on exact-integer boundaries (T a multiple of E * 10^6 / gcd), half random
+        if rng.random() < 0.5:
+            f = Fraction(cf)
+            step = (E * f.denominator) // math.gcd(E * f.denominator, f.numerator * k)
+            T = step * rng.randint(1, max(1, 60000 // max(step, 1)))
+            if T * k >= 2 ** 31 or T > 200000:
+                T = rng.randint(0, 50000)
+        else:
+            T = rng.randint(0, 50000)
+        cases.append((cf, T, E, k))
+    return cases
+
+
+def test_capacity_sweep_matches_the_oracle_and_the_printed_formula():
+    """moe_capacity (library) and oracle.capacity (CPU oracle) give the same
+    C for 640 (cf, T, E, k) combinations, token choice and expert choice,
+    and both equal the exact ceiling of the printed formula with the factor
+    as written (Fraction of the decimal string): no off-by-one from a binary
+    capacity factor on integer boundaries."""
+    n_boundary = 0
+    for cf, T, E, k in _capacity_cases():
+        for gate in ("softmax_topk", "expert_choice"):
+            c = moe.config(T=T, d_model=64, d_ff=64, n_experts=E, top_k=k, gate=gate, capacity_factor=float(cf))
+            assert moe.validate_config(c) == OK
+            ocfg = workloads.Config(name="sweep", T=T, d=64, F=64, E=E, k=k, act_dtype="f32", act="relu",
+                                    gate=gate, capacity_factor=float(cf), seed=0)
+            limit = T if gate == "expert_choice" else T * k
+            want = _exact_capacity(cf, T, E, k, limit)
+            got_lib, got_or = moe.capacity(c), oracle.capacity(ocfg)
+            assert got_lib == got_or == want, (cf, T, E, k, gate, got_lib, got_or, want)
+            if gate == "softmax_topk":
+                assert moe.max_rows(c) == min(T * k, E * want)
+                v = Fraction(cf) * T * k / E
+                n_boundary += v.denominator == 1
+    assert n_boundary >= 100      # the sweep really visits integer boundaries
+
+
+def test_capacity_edge_factors():
+    """Tiny factors give C = 0 (every assignment dropped), huge ones clamp to
+    T k (token choice) or T (expert choice); both sides agree."""
+    for cf, want_tc, want_ec in [(1e-9, 0, 0), (4e-7, 0, 0), (1e300, 64 * 2, 64), (1e7, 64 * 2, 64)]:
+        c = _cfg(capacity_factor=cf)
+        assert moe.capacity(c) == want_tc
+        ce = _cfg(capacity_factor=cf, gate="expert_choice")
+        assert moe.capacity(ce) == want_ec
+        ocfg = workloads.Config(name="edge", T=64, d=128, F=256, E=8, k=2, act_dtype="f32", act="relu",
+                                gate="softmax_topk", capacity_factor=cf, seed=0)
+        assert oracle.capacity(ocfg) == want_tc
+        assert oracle.capacity(ocfg.replace(gate="expert_choice")) == want_ec
 
 
 def test_workspace_grows_with_tokens():

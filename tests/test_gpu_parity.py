@@ -269,6 +269,32 @@ def test_dispatch_sizes_and_drops(name):
     H.compare_dispatch(cfg, g, o)
 
 
+# Capacity factors whose product with T k / E is an integer (C = 44, 600 and
+# 2 exactly by the printed formula) and which a binary float32 factor would
+# round up by one; a Zipf logit bias makes the busiest experts overflow, so
+# the drop masks decide at exactly C.
+CAPACITY_BOUNDARY = {
+    "cap_1p1_T2560_E64_k1": (dict(T=2560, E=64, k=1, capacity_factor=1.1), 44),
+    "cap_1p2_T4000_E16_k2": (dict(T=4000, E=16, k=2, capacity_factor=1.2), 600),
+    "cap_0p1_T160_E8_k1": (dict(T=160, E=8, k=1, capacity_factor=0.1), 2),
+}
+
+
+@pytest.mark.parametrize("name", list(CAPACITY_BOUNDARY))
+def test_capacity_on_integer_boundaries_drops_bit_exact(name):
+    kw, C_formula = CAPACITY_BOUNDARY[name]
+    cfg = Config(name, d=64, F=64, act_dtype="bf16", act="relu", gate="softmax_topk", residual=True,
+                 logit_bias="zipf", seed=51, **kw)
+    H.log(f"[capacity] {name}")
+    assert oracle.capacity(cfg) == C_formula == moe.capacity(H.bind_config(cfg))
+    inp = workloads.make_inputs(cfg)
+    g = H.run_stages(cfg, H.to_device(inp))
+    o = full_oracle(cfg, inp)
+    check_all(cfg, g, o)
+    kept = g["stats"]["kept"].numpy()
+    assert kept.max() == C_formula and int(g["stats"]["n_dropped"][0]) > 0
+
+
 # Expert row counts that put every kind of remainder after 256-row tiles:
 # none, 1, 64, 65, 128 (these go to the 64-row remainder launch), 129 and 255
 # (a whole 256-row tile), and experts smaller than one tile.  The caller hands

@@ -5,8 +5,9 @@ stands for (numpy's fp64 libm, i.e. the exact value to ~1e-16) within a few
 fp32 ulps, plus exact special values.  A wrong series coefficient, a
 dropped reduction term or a wrong quadrant rotation fails these bounds.
 The Gaussian stream is checked against N(0,1) (mean, variance, KS distance,
-lag correlation).  Its agreement with the published Philox generator itself
-is parity unpinned.
+lag correlation).  The Philox4x32-10 generator underneath it is pinned to the
+generator's published known-answer vectors in tests/test_oracle_hash.py
+(fixture tests/golden/philox4x32_10_kat.json, with its citation).
 """
 import math
 
