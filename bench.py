@@ -132,9 +132,19 @@ def main():
     ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
                     help="forward (default): the layer forward, stage by stage; backward: moe_layer_backward on the "
                          "saved tensors of one forward (a separate JSON line with its own metric)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure the achievable ceilings (register-only bf16 MFMA rate for both MFMA shapes, "
+                         "device copy rate) and print them as one JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (counter calibration)")
     args = ap.parse_args()
+
+    if args.peaks:
+        from sparse_mixture_experts_39_amd import peaks
+        res = peaks.measure_all()
+        res["device"] = __import__("torch").cuda.get_device_name(0)
+        print(json.dumps(res))
+        return
 
     if args.calibrate_copy:
         import torch

@@ -16,6 +16,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 LIB_PATH = os.path.join(HERE, "libmoe.so")
+# measurement aid (peak probes, cache flush): its own library, not the ABI
+PEAK_SOURCE = "peak.hip"
+PEAK_LIB_PATH = os.path.join(HERE, "libmoe_peak.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = {
@@ -44,17 +47,23 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    """Compile every source and link libmoe.so; always rebuilds."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda kv: _compile(*kv), SOURCES.items()))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path):
+    tmp = path + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950"] + objs + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(jobs: int = 8) -> str:
+    """Compile every source, link libmoe.so and libmoe_peak.so; always rebuilds."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    todo = list(SOURCES.items()) + [(PEAK_SOURCE, [])]
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda kv: _compile(*kv), todo))
+    _link(objs[:-1], LIB_PATH)
+    _link(objs[-1:], PEAK_LIB_PATH)
     return LIB_PATH
 
 

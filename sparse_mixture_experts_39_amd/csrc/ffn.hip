@@ -46,8 +46,9 @@
 //   * Split-K tail: a mostly empty last round of tiles is cut into K ranges
 //     (second launch, fp32 partials) and reduced in order by k_split_fixup.
 //   * Remainder tiles: with 256-row tiles, an expert's last <= 128 rows go to
-//     a further launch of 64-row tiles (kRemBM), so a row count just past a
-//     multiple of 256 does not pay for a whole padded tile.
+//     64-row tiles (kRemBM) in the same launch, after all whole tiles (so a
+//     split-K tail cuts the small remainder tiles first), and a row count
+//     just past a multiple of 256 does not pay for a whole padded tile.
 #include <algorithm>
 #include <type_traits>
 
@@ -83,17 +84,9 @@ struct GemmParams {
     float* partial;         // split-K partial accumulators
     void* C2;               // pre-activations (_SAVE epilogues)
     int64_t ldc2;
-    int rem_bm;             // > 0: row tiles start after the expert's first
-                            // floor(M_e / rem_bm) * rem_bm rows (remainder launch)
+    int rem;                // 1: an expert's last <= kRemThr rows go to kRemBM-row tiles
+    int64_t unit_f4;        // float4s of partial accumulators per split unit (main tile)
 };
-
-// First row of row tile mt of expert e.  The remainder launch covers the rows
-// left after the expert's whole tiles of the main launch (rem_bm rows each).
-__device__ __forceinline__ int tile_row0(const GemmParams& p, int e, int mt, int BM) {
-    int base = p.offsets[e];
-    if (p.rem_bm > 0) base += (p.offsets[e + 1] - base) / p.rem_bm * p.rem_bm;
-    return base + mt * BM;
-}
 
 // Work decomposition.  The plan lists ceil(M_e / BM) row tiles per expert,
 // each with NT column tiles, T tiles in all.  When the last round of tiles
@@ -108,33 +101,74 @@ constexpr int kMaxSplit = 16;
 // Remainder tiles.  With 256-row tiles an expert whose row count lies just
 // past a multiple of 256 pays a whole tile of padding rows for a few real
 // ones.  When at most kRemThr rows are left after an expert's whole tiles,
-// they go to a second launch of kRemBM-row tiles (ceil(r / kRemBM) of them,
-// a quarter of the MFMA work of a 256-row tile each) instead.  Each launch
-// has its own plan, and its own split-K tail.
+// they go to ceil(r / kRemBM) tiles of kRemBM rows instead (a quarter of the
+// MFMA work of a 256-row tile each), in the same launch, after every whole
+// tile.  (Placing them right after their expert's whole tiles of each column
+// group, to share the weight panel in L2, measured no faster for the up
+// projection and slower for the down projection, whose split-K tail then
+// cuts whole tiles instead of remainder tiles.)
 #ifndef MOE_GEMM_REM
 #define MOE_GEMM_REM 1
+#endif
+// Waves along N of a 256 x 256 bf16 tile: 2 (4 waves, one per SIMD; the
+// default) or 4 (8 waves, two per SIMD, no remainder tiles).  Other tiles
+// always use 4 waves.
+#ifndef MOE_GEMM_WGN256
+#define MOE_GEMM_WGN256 2
 #endif
 constexpr int kRemBM = 64;
 constexpr int kRemThr = 128;
 
-// Tile L of the natural order: experts in order; inside an expert, groups of
-// NG column tiles, row tiles fastest inside a group.
-__device__ __forceinline__ void decode_tile(const GemmParams& p, int L, int& e, int& mt, int& nt) {
+// Whole BM-row tiles of an expert with M rows: ceil(M / BM), or floor(M / BM)
+// when its last r = M mod BM rows (0 < r <= kRemThr) go to remainder tiles.
+__host__ __device__ __forceinline__ int whole_tiles(int M, int BM, bool rem) {
+    const int r = M % BM;
+    return (rem && r > 0 && r <= kRemThr) ? M / BM : (M + BM - 1) / BM;
+}
+
+// Tile L of the natural order: first every whole tile, then every remainder
+// tile (so that a split-K tail takes remainder tiles first); within each
+// kind, experts in order, and inside an expert groups of NG column tiles
+// with row tiles fastest inside a group.  The plan holds the whole-tile
+// prefix over the experts at [0, E], the remainder-tile prefix at
+// [E + 4, 2E + 4].  Returns the expert, the column tile, the first row and
+// the row count, and whether it is a remainder tile.
+struct TileDesc {
+    int e, nt, row0, rows;
+    bool rem;
+};
+__device__ __forceinline__ TileDesc decode_tile(const GemmParams& p, int L, int BM) {
     const int NT = p.NT;
+    const int whole_total = p.plan[p.E] * NT;
+    TileDesc t;
+    t.rem = L >= whole_total;
+    const int32_t* pre = t.rem ? p.plan + p.E + 4 : p.plan;
+    if (t.rem) L -= whole_total;
     int lo = 0, hi = p.E;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (p.plan[mid] * NT <= L) lo = mid; else hi = mid;
+        if (pre[mid] * NT <= L) lo = mid; else hi = mid;
     }
-    e = lo;
-    const int tiles_e = p.plan[e + 1] - p.plan[e];
-    const int local = L - p.plan[e] * NT;
+    t.e = lo;
+    const int tiles_e = pre[t.e + 1] - pre[t.e];
+    const int local = L - pre[t.e] * NT;
     constexpr int NG = 8;
     const int grp = local / (tiles_e * NG);
     const int inside = local - grp * tiles_e * NG;
-    mt = inside % tiles_e;
-    nt = grp * NG + inside / tiles_e;
+    const int mt = inside % tiles_e;
+    t.nt = grp * NG + inside / tiles_e;
+    const int off = p.offsets[t.e], M = p.offsets[t.e + 1] - off;
+    if (t.rem) {
+        t.row0 = off + whole_tiles(M, BM, true) * BM + mt * kRemBM;
+        t.rows = min(kRemBM, off + M - t.row0);
+    } else {
+        t.row0 = off + mt * BM;
+        t.rows = min(BM, off + M - t.row0);
+    }
+    return t;
 }
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 // XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row.  LDS serves
 // 16 lanes of a 16-byte read per pass: rows r .. r+15 at one logical chunk
@@ -150,8 +184,8 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 struct RingDepth {
     int na, nb, wait, wait0, bytes;
 };
-constexpr RingDepth ring_depth(int BM, int BN) {
-    const int SA = BM * 128, SB = BN * 128, ga = BM / 32, gb = BN / 32;
+constexpr RingDepth ring_depth(int BM, int BN, int NW) {
+    const int SA = BM * 128, SB = BN * 128, ga = BM / 8 / NW, gb = BN / 8 / NW;
     RingDepth best{2, 2, 0, ga + gb, 2 * (SA + SB)};
     for (int na = 2; na <= 16; ++na)
         for (int nb = na; nb <= na + 1; ++nb) {
@@ -181,17 +215,33 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Epilogue of one wave's accumulators (shared by the GEMM and the split-K
 // fixup).
-template <bool BF16, int BM, int BN, int EPI>
-struct GemmEpilogue {
-    static constexpr int WM = BM / 2, WN = BN / 2;
-    static constexpr int MB = 16;              // 16x16 MFMA blocks
-    static constexpr int FM = WM / MB, FN = WN / MB;
-    static constexpr int RA = 4;               // accumulator registers per MFMA block
-    typedef floatx4_t acc_t;
+// MFMA block edge of the bf16 products: 32 (v_mfma_f32_32x32x16_bf16) or
+// 16 (v_mfma_f32_16x16x32_bf16); fp32 always uses 16x16x4 blocks.
+#ifndef MOE_GEMM_MB_BF16
+#define MOE_GEMM_MB_BF16 16
+#endif
+template <bool BF16>
+constexpr int mfma_block() { return BF16 ? MOE_GEMM_MB_BF16 : 16; }
 
-    // float4 index of partial element (i, j, 4*r4 .. 4*r4+3) of wave w, unit u
-    __device__ static int64_t partial_index(int u, int w, int i, int j, int r4, int lane) {
-        return (((((int64_t)u * 4 + w) * FN + i) * FM + j) * (RA / 4) + r4) * 64 + lane;
+template <bool BF16, int BM, int BN, int EPI, int WGM, int WGN>
+struct GemmEpilogue {
+    static constexpr int NW = WGM * WGN;       // waves: WGM along M, WGN along N
+    static constexpr int WM = BM / WGM, WN = BN / WGN;
+    static constexpr int MB = mfma_block<BF16>();
+    static constexpr int FM = WM / MB, FN = WN / MB;
+    static constexpr int RA = MB == 32 ? 16 : 4;   // accumulator registers per MFMA block
+    typedef typename std::conditional<MB == 32, floatx16_t, floatx4_t>::type acc_t;
+
+    // A lane's accumulators are RA / 4 groups of 4 consecutive output columns
+    // of one token row.  16x16 block: lane l, element t holds D[n = 4(l/16) +
+    // t][m = l % 16]; 32x32 block: element 4g + t holds D[n = 8g + 4(l/32) +
+    // t][m = l % 32].  Column offset of group g inside the block:
+    __device__ static int group_col(int g, int lane) { return MB == 32 ? 8 * g + 4 * (lane >> 5) : 4 * (lane >> 4); }
+
+    // float4 index of partial element (i, j, 4*r4 .. 4*r4+3) of wave w, unit
+    // u (units are p.unit_f4 float4s apart whatever the tile's row count)
+    __device__ static int64_t partial_index(const GemmParams& p, int u, int w, int i, int j, int r4, int lane) {
+        return (int64_t)u * p.unit_f4 + ((((int64_t)w * FN + i) * FM + j) * (RA / 4) + r4) * 64 + lane;
     }
 
     __device__ static void store_partial(const GemmParams& p, const acc_t (&acc)[FN][FM], int u, int w, int lane) {
@@ -202,18 +252,17 @@ struct GemmEpilogue {
             for (int j = 0; j < FM; ++j)
 #pragma unroll
                 for (int r4 = 0; r4 < RA / 4; ++r4)
-                    dst[partial_index(u, w, i, j, r4, lane)] =
+                    dst[partial_index(p, u, w, i, j, r4, lane)] =
                         make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
     }
 
-    // Column groups of the epilogue: the 16-row blocks i of the wave's B tile
+    // Column groups of the epilogue: the MB-row blocks i of the wave's B tile
     // are independent, except that SwiGLU pairs block 2p (gate) with block
     // 2p+1 (up).
     static constexpr int IG = epi_swiglu(EPI) ? 2 : 1;
 
-    // Output of blocks i0 .. i0+IG-1 (acc[0 .. IG-1]).  In a 16x16 block,
-    // lane l, element t holds D[n = 4(l/16) + t][m = l % 16]: a lane owns 4
-    // consecutive output columns of one row and stores them at once.
+    // Output of blocks i0 .. i0+IG-1 (acc[0 .. IG-1]): a lane stores each of
+    // its groups of 4 consecutive output columns at once.
     __device__ static void store_cols(const GemmParams& p, const acc_t (*acc)[FM], int i0, int row0, int rows, int nt,
                                       int wm, int wn, int lane) {
         auto store4_to = [&](void* dst, int64_t ld, int m, int64_t col, const float* v) {
@@ -229,25 +278,25 @@ struct GemmEpilogue {
         };
         auto store4 = [&](int m, int64_t col, const float* v) { store4_to(p.C, p.ldc, m, col, v); };
         auto silu_mul = [](float gt, float up) { return gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up; };
-        {
-            const int lg = lane >> 4;
 #pragma unroll
-            for (int j = 0; j < FM; ++j) {
-                const int m = wm * WM + j * 16 + (lane & 15);
-                if (m >= rows) continue;
+        for (int j = 0; j < FM; ++j) {
+            const int m = wm * WM + j * MB + (lane & (MB - 1));
+            if (m >= rows) continue;
+#pragma unroll
+            for (int g = 0; g < RA / 4; ++g) {
                 if constexpr (epi_swiglu(EPI)) {
-                    const int fblock = (wn * FN + i0) >> 1;        // 16-row blocks alternate gate / up
+                    const int fblock = (wn * FN + i0) >> 1;        // MB-row blocks alternate gate / up
                     float v[4];
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = silu_mul(acc[0][j][t], acc[1][j][t]);
-                    const int64_t col = (int64_t)nt * (BN / 2) + fblock * 16 + 4 * lg;
+                    for (int t = 0; t < 4; ++t) v[t] = silu_mul(acc[0][j][4 * g + t], acc[1][j][4 * g + t]);
+                    const int64_t col = (int64_t)nt * (BN / 2) + fblock * MB + group_col(g, lane);
                     store4(m, col, v);
                     if constexpr (epi_save(EPI)) {
                         float a[4], u[4];
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
-                            a[t] = acc[0][j][t];
-                            u[t] = acc[1][j][t];
+                            a[t] = acc[0][j][4 * g + t];
+                            u[t] = acc[1][j][4 * g + t];
                         }
                         store4_to(p.C2, p.ldc2, m, col, a);
                         store4_to(p.C2, p.ldc2, m, p.N + col, u);
@@ -256,16 +305,16 @@ struct GemmEpilogue {
                     float v[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        float x = acc[0][j][t];
+                        float x = acc[0][j][4 * g + t];
                         if constexpr (epi_relu(EPI)) x = fmaxf(x, 0.0f);
                         v[t] = x;
                     }
-                    const int64_t col = (int64_t)nt * BN + wn * WN + i0 * 16 + 4 * lg;
+                    const int64_t col = (int64_t)nt * BN + wn * WN + i0 * MB + group_col(g, lane);
                     store4(m, col, v);
                     if constexpr (epi_save(EPI)) {
                         float a[4];
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) a[t] = acc[0][j][t];
+                        for (int t = 0; t < 4; ++t) a[t] = acc[0][j][4 * g + t];
                         store4_to(p.C2, p.ldc2, m, col, a);
                     }
                 }
@@ -280,57 +329,34 @@ struct GemmEpilogue {
     }
 };
 
-template <bool BF16, int BM, int BN, int EPI, bool SPLIT>
-__global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-    constexpr int WM = BM / 2, WN = BN / 2;
-    constexpr int MB = 16;                    // MFMA block edge (16x16x32 bf16, 16x16x4 fp32)
+// One tile of the grouped GEMM (rows [t.row0, t.row0 + t.rows) of expert
+// t.e, column tile t.nt, K slices [k0, k1)); `lds` is the kernel's LDS.
+template <bool BF16, int BM, int BN, int EPI, bool SPLIT, int WGN>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, lds_u8* lds, const TileDesc& t, int k0, int k1,
+                                          int unit) {
+    constexpr int NW = 2 * WGN;               // waves: 2 along M, WGN along N
+    constexpr int WM = BM / 2, WN = BN / WGN;
+    constexpr int MB = mfma_block<BF16>();    // MFMA block edge (32x32x16 or 16x16x32 bf16, 16x16x4 fp32)
     constexpr int FM = WM / MB, FN = WN / MB;
     constexpr int ES = BF16 ? 2 : 4;
-    constexpr int KS = 1;                     // k-steps per half slice
+    constexpr int KS = MB == 32 ? 2 : 1;      // k-steps per half slice (64 bytes of K)
     constexpr int SA = BM * 128, SB = BN * 128;
-    constexpr RingDepth RD = ring_depth(BM, BN);
+    constexpr RingDepth RD = ring_depth(BM, BN, NW);
     constexpr int NA = RD.na, NB = RD.nb;
     constexpr int GA = BM / 8, GB = BN / 8;   // 1 KB load groups: 8 rows x 128 bytes
-    constexpr int ga = GA / 4, gb = GB / 4;   // groups per wave
-    typedef GemmEpilogue<BF16, BM, BN, EPI> Epi;
+    constexpr int ga = GA / NW, gb = GB / NW; // groups per wave
+    static_assert(GA % NW == 0 && GB % NW == 0, "load groups split evenly over the waves");
+    typedef GemmEpilogue<BF16, BM, BN, EPI, 2, WGN> Epi;
     typedef typename Epi::acc_t acc_t;
     static_assert(FM >= 1 && FN >= 1, "tile smaller than one MFMA block");
-    static_assert(!epi_swiglu(EPI) || (FN % 2) == 0, "SwiGLU pairs 16-row blocks");
+    static_assert(!epi_swiglu(EPI) || (FN % 2) == 0, "SwiGLU pairs MB-row blocks");
     static_assert(RD.wait0 < 64 && RD.bytes <= 160 * 1024, "ring exceeds vmcnt or LDS");
-    __shared__ __align__(16) uint8_t lds[RD.bytes];
-
-    // ---- work unit.  Whole tiles (SPLIT = false): block ids are dealt
-    // round-robin to the 8 XCDs, so tiles are remapped to give each XCD a
-    // contiguous range (its blocks share weight and activation panels in its
-    // L2).  Split units (SPLIT = true, a launch of its own): block u is unit
-    // u, range u % split of tail tile u / split.
-    const int total = p.plan[p.E] * p.NT;
-    const int full = p.plan[p.E + 1], split = p.plan[p.E + 2], tail = p.plan[p.E + 3];
-    int L, k0 = 0, k1 = p.nk, unit = -1;
-    if constexpr (!SPLIT) {
-        const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-        const int per_xcd = split > 1 ? full / 8 : (total + 7) / 8;
-        if (slot >= per_xcd) return;
-        L = xcd * per_xcd + slot;
-        if (L >= total) return;
-    } else {
-        if (split <= 1) return;
-        unit = blockIdx.x;
-        if (unit >= tail * split) return;
-        L = full + unit / split;
-        const int c = unit % split;
-        k0 = c * p.nk / split;
-        k1 = (c + 1) * p.nk / split;
-    }
-    int e, mt, nt;
-    decode_tile(p, L, e, mt, nt);
-    const int row0 = tile_row0(p, e, mt, BM);
-    const int rows = min(BM, p.offsets[e + 1] - row0);
+    typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
+    const int e = t.e, nt = t.nt, row0 = t.row0, rows = t.rows;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
 
     // ---- direct-to-LDS loads.  Slot layout: NA A slots of BM rows, then NB B
     // slots of BN rows, 128 bytes per row.  One buffer_load_dwordx4 ... lds of
@@ -362,9 +388,9 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     for (int q = 0; q < gb; ++q) {
         const int g = wave * gb + q;
         const int r = 8 * g + (lane >> 3);
-        // SwiGLU: 16-row block j of the tile is rows (j/2)*16 .. +15 of W1 (j
-        // even) or W3 (j odd)
-        const int rr = epi_swiglu(EPI) ? ((g >> 2) * 16 + (r & 15)) : r;
+        // SwiGLU: MB-row block j of the tile is rows (j/2)*MB .. +MB-1 of W1
+        // (j even) or W3 (j odd); a group is 8 rows, so block j = g / (MB/8)
+        const int rr = epi_swiglu(EPI) ? ((g / (MB / 4)) * MB + (r & (MB - 1))) : r;
         voffB[q] = (uint32_t)(rr * p.K * ES + (((lane & 7) ^ swz(r)) << 4));
     }
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -373,14 +399,14 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     // one into a free slot (nobody reads it), which keeps the per-wave load
     // count of every batch the same
     auto issueA1 = [&](int v, int q) {      // group q of this wave's part of A slice v
-        uint8_t* dst = &lds[(v % NA) * SA + wave * ga * 1024];
+        lds_u8* dst = &lds[(v % NA) * SA + wave * ga * 1024];
         const int koff = (k0 + min(v, nk - 1)) * 128;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)(dst + q * 1024), 16, voffA[q], koff, 0, 0);
     };
     auto issueB1 = [&](int v, int q) {
-        uint8_t* dst = &lds[NA * SA + (v % NB) * SB + wave * gb * 1024];
+        lds_u8* dst = &lds[NA * SA + (v % NB) * SB + wave * gb * 1024];
         const int koff = (k0 + min(v, nk - 1)) * 128;
-        const bool up = epi_swiglu(EPI) && (((wave * gb + q) >> 1) & 1);
+        const bool up = epi_swiglu(EPI) && (((wave * gb + q) / (MB / 8)) & 1);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? rsB1 : rsB0, (lds_ptr_t)(dst + q * 1024), 16, voffB[q], koff,
                                                  0, 0);
     };
@@ -399,14 +425,17 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < FM; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < Epi::RA; ++r) acc[i][j][r] = 0.0f;
 
-    // Fragment reads, per half slice h (64 bytes of K): lane l takes row
-    // l % 16 of a 16-row block at logical chunk 4h + l/16 (8 bf16 k values,
-    // one 16x16x32 MFMA; or 4 fp32 k values, four 16x16x4 MFMAs).
-    // Weights are MFMA source 0 (rows = output columns n), activations
-    // source 1 (columns = token rows m).  The swizzle depends on the row mod
-    // 16 only, so blocks i of one operand differ by the constant i*MB*128.
+    // Fragment reads, per half slice h (64 bytes of K, 4 chunks of 16
+    // bytes): 16x16 blocks: lane l takes row l % 16 at logical chunk
+    // 4h + l/16 (8 bf16 k values, one 16x16x32 MFMA; or 4 fp32 k values,
+    // four 16x16x4 MFMAs); 32x32 blocks: k-step s2 (2 chunks) of the half,
+    // lane l takes row l % 32 at chunk 4h + 2 s2 + l/32 (8 bf16 k values of
+    // one 32x32x16 MFMA).  Weights are MFMA source 0 (rows = output columns
+    // n), activations source 1 (columns = token rows m).  The swizzle depends
+    // on the row mod 16 only, so blocks i of one operand differ by the
+    // constant i*MB*128.
     constexpr int NF = KS * (FM + FN);       // fragments per half slice
     int fo[2][KS][2];
 #pragma unroll
@@ -414,7 +443,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2) {
             const int lr = lane & (MB - 1);
-            const int ch = 4 * h + (lane >> 4);
+            const int ch = MB == 32 ? 4 * h + 2 * s2 + (lane >> 5) : 4 * h + (lane >> 4);
             fo[h][s2][0] = (wm * WM + lr) * 128 + ((ch ^ swz(lr)) << 4);
             fo[h][s2][1] = NA * SA + (wn * WN + lr) * 128 + ((ch ^ swz(lr)) << 4);
         }
@@ -422,8 +451,17 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     // FN B blocks
     auto read1 = [&](int ks, int h, u32x4_t* f, int r) {
         const int s2 = r / (FM + FN), q = r % (FM + FN);
-        if (q < FM) f[r] = *(const u32x4_t*)(&lds[(ks % NA) * SA] + fo[h][s2][0] + q * MB * 128);
-        else f[r] = *(const u32x4_t*)(&lds[(ks % NB) * SB] + fo[h][s2][1] + (q - FM) * MB * 128);
+        if (q < FM) f[r] = *(lds_u32x4*)(&lds[(ks % NA) * SA] + fo[h][s2][0] + q * MB * 128);
+        else f[r] = *(lds_u32x4*)(&lds[(ks % NB) * SB] + fo[h][s2][1] + (q - FM) * MB * 128);
+    };
+    // one bf16 MFMA of the block shape: acc += W-fragment x activation-fragment
+    auto mfma_bf16 = [](const u32x4_t& fw, const u32x4_t& fx, acc_t& a) {
+        if constexpr (MB == 32)
+            a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fw),
+                                                        __builtin_bit_cast(bf16x8_t, fx), a, 0, 0, 0);
+        else
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fw),
+                                                        __builtin_bit_cast(bf16x8_t, fx), a, 0, 0, 0);
     };
     auto read_frags = [&](int ks, int h, u32x4_t* f) {
 #pragma unroll
@@ -438,8 +476,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
                 for (int j = 0; j < FM; ++j) {
                     const u32x4_t fa = f[s2 * (FM + FN) + j], fb = f[s2 * (FM + FN) + FM + i];
                     if constexpr (BF16) {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, fb), __builtin_bit_cast(bf16x8_t, fa), acc[i][j], 0, 0, 0);
+                        mfma_bf16(fb, fa, acc[i][j]);
                     } else {
                         const floatx4_t b4 = __builtin_bit_cast(floatx4_t, fb);
                         const floatx4_t a4 = __builtin_bit_cast(floatx4_t, fa);
@@ -455,9 +492,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
     auto mma1 = [&](const u32x4_t* f, int m) {
         if constexpr (BF16) {
             const int s2 = m / (FN * FM), i = (m / FM) % FN, j = m % FM;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f[s2 * (FM + FN) + FM + i]),
-                                                                __builtin_bit_cast(bf16x8_t, f[s2 * (FM + FN) + j]),
-                                                                acc[i][j], 0, 0, 0);
+            mfma_bf16(f[s2 * (FM + FN) + FM + i], f[s2 * (FM + FN) + j], acc[i][j]);
         }
     };
     // Pipeline over slices ks = 0 .. nk-1 (two half slices each).  Between
@@ -563,21 +598,69 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmParams p) {
 
     if constexpr (SPLIT) Epi::store_partial(p, acc, unit, wave, lane);
     else Epi::store(p, acc, row0, rows, nt, wm, wn, lane);
+}
+
+// LDS bytes of a launch: its tile's ring, or the larger of that and the
+// remainder tile's ring when remainder tiles can occur (256-row bf16 tiles).
+template <bool BF16, int BM, int BN, int WGN>
+constexpr int gemm_lds_bytes() {
+    constexpr int main_bytes = ring_depth(BM, BN, 2 * WGN).bytes;
+    if constexpr (BF16 && BM == 256) {
+        constexpr int rem_bytes = ring_depth(kRemBM, BN, 4).bytes;
+        return main_bytes > rem_bytes ? main_bytes : rem_bytes;
+    }
+    return main_bytes;
+}
+
+// The grouped GEMM kernel: finds its work unit and runs its tile.  Whole
+// tiles (SPLIT = false): block ids are dealt round-robin to the 8 XCDs, so
+// tiles are remapped to give each XCD a contiguous range (its blocks share
+// weight and activation panels in its L2).  Split units (SPLIT = true, a
+// launch of its own): block u is unit u, range u % split of tail tile
+// u / split.  Remainder tiles (256-row bf16 launches) run with 64-row tiles
+// (launches of 4 waves only).
+template <bool BF16, int BM, int BN, int EPI, bool SPLIT, int WGN>
+__global__ __launch_bounds__(128 * WGN) void k_grouped_gemm(GemmParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+    __shared__ __align__(16) uint8_t lds_mem[gemm_lds_bytes<BF16, BM, BN, WGN>()];
+    lds_u8* lds = (lds_u8*)lds_mem;
+    const int total = (p.plan[p.E] + p.plan[2 * p.E + 4]) * p.NT;
+    const int full = p.plan[p.E + 1], split = p.plan[p.E + 2], tail = p.plan[p.E + 3];
+    int L, k0 = 0, k1 = p.nk, unit = -1;
+    if constexpr (!SPLIT) {
+        const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+        const int per_xcd = split > 1 ? full / 8 : (total + 7) / 8;
+        if (slot >= per_xcd) return;
+        L = xcd * per_xcd + slot;
+        if (L >= total) return;
+    } else {
+        if (split <= 1) return;
+        unit = blockIdx.x;
+        if (unit >= tail * split) return;
+        L = full + unit / split;
+        const int c = unit % split;
+        k0 = c * p.nk / split;
+        k1 = (c + 1) * p.nk / split;
+    }
+    const TileDesc t = decode_tile(p, L, BM);
+    if constexpr (BF16 && BM == 256 && WGN == 2) {
+        if (t.rem) {
+            gemm_tile<BF16, kRemBM, BN, EPI, SPLIT, 2>(p, lds, t, k0, k1, unit);
+            return;
+        }
+    }
+    gemm_tile<BF16, BM, BN, EPI, SPLIT, WGN>(p, lds, t, k0, k1, unit);
 #endif
 }
 
 // Split-K fixup: block (t, w, g) adds, in range order, the `split` partial
 // accumulators of column group g of wave w of tail tile t, and applies the
 // epilogue to them.
-template <bool BF16, int BM, int BN, int EPI>
-__global__ __launch_bounds__(64) void k_split_fixup(GemmParams p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    typedef GemmEpilogue<BF16, BM, BN, EPI> Epi;
-    constexpr int FM = Epi::FM, FN = Epi::FN, RA = Epi::RA, IG = Epi::IG, NGRP = FN / IG;
-    const int full = p.plan[p.E + 1], split = p.plan[p.E + 2], tail = p.plan[p.E + 3];
-    const int t = blockIdx.x / (4 * NGRP), w = (blockIdx.x / NGRP) % 4, i0 = (blockIdx.x % NGRP) * IG;
+template <bool BF16, int BM, int BN, int EPI, int WGM, int WGN>
+__device__ __forceinline__ void fixup_tile(const GemmParams& p, const TileDesc& t, int w, int i0, int split) {
+    typedef GemmEpilogue<BF16, BM, BN, EPI, WGM, WGN> Epi;
+    constexpr int FM = Epi::FM, RA = Epi::RA, IG = Epi::IG;
     const int lane = threadIdx.x;
-    if (split <= 1 || t >= tail) return;
     typename Epi::acc_t acc[IG][FM];
     const float4* src = (const float4*)p.partial;
 #pragma unroll
@@ -586,43 +669,61 @@ __global__ __launch_bounds__(64) void k_split_fixup(GemmParams p) {
         for (int j = 0; j < FM; ++j)
 #pragma unroll
             for (int r = 0; r < RA; ++r) acc[i][j][r] = 0.0f;
+    const int tt = blockIdx.x / (Epi::NW * (Epi::FN / IG));
     for (int c = 0; c < split; ++c) {
-        const int u = t * split + c;
+        const int u = tt * split + c;
 #pragma unroll
         for (int i = 0; i < IG; ++i)
 #pragma unroll
             for (int j = 0; j < FM; ++j)
 #pragma unroll
                 for (int r4 = 0; r4 < RA / 4; ++r4) {
-                    const float4 v = src[Epi::partial_index(u, w, i0 + i, j, r4, lane)];
+                    const float4 v = src[Epi::partial_index(p, u, w, i0 + i, j, r4, lane)];
                     acc[i][j][4 * r4] += v.x;
                     acc[i][j][4 * r4 + 1] += v.y;
                     acc[i][j][4 * r4 + 2] += v.z;
                     acc[i][j][4 * r4 + 3] += v.w;
                 }
     }
-    int e, mt, nt;
-    decode_tile(p, full + t, e, mt, nt);
-    const int row0 = tile_row0(p, e, mt, BM);
-    const int rows = min(BM, p.offsets[e + 1] - row0);
-    Epi::store_cols(p, acc, i0, row0, rows, nt, w >> 1, w & 1, lane);
+    Epi::store_cols(p, acc, i0, t.row0, t.rows, t.nt, w / WGN, w % WGN, lane);
+}
+
+// Split-K fixup: block (t, w, g) adds, in range order, the `split` partial
+// accumulators of column group g of wave w of tail tile t, and applies the
+// epilogue to them (with the remainder-tile layout for remainder tiles).
+template <bool BF16, int BM, int BN, int EPI, int WGM, int WGN>
+__global__ __launch_bounds__(64) void k_split_fixup(GemmParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef GemmEpilogue<BF16, BM, BN, EPI, WGM, WGN> Epi;
+    constexpr int IG = Epi::IG, NGRP = Epi::FN / IG, NW = Epi::NW;
+    const int full = p.plan[p.E + 1], split = p.plan[p.E + 2], tail = p.plan[p.E + 3];
+    const int t = blockIdx.x / (NW * NGRP), w = (blockIdx.x / NGRP) % NW, i0 = (blockIdx.x % NGRP) * IG;
+    if (split <= 1 || t >= tail) return;
+    const TileDesc td = decode_tile(p, full + t, BM);
+    if constexpr (BF16 && BM == 256 && WGM == 2 && WGN == 2) {
+        if (td.rem) {
+            fixup_tile<BF16, kRemBM, BN, EPI, 2, 2>(p, td, w, i0, split);
+            return;
+        }
+    }
+    fixup_tile<BF16, BM, BN, EPI, WGM, WGN>(p, td, w, i0, split);
 #endif
 }
 
-// Tile plan: prefix[e+1] = sum_{e' <= e} (row tiles of expert e'), then the
-// split-K decision {full, split, tail} (see kSplitUnits).  Expert e has
-// ceil(M_e / BM) row tiles, or, with rem_bm > 0 and a remainder
-// r = M_e mod BM in 1 .. kRemThr, floor(M_e / BM) tiles here and
-// ceil(r / rem_bm) tiles in the remainder plan, which follows at
-// prefix[E + 4] in the same layout.  With offsets == NULL the plan describes
+// Tile plan: prefix[e+1] = sum_{e' <= e} (whole row tiles of expert e'),
+// then the split-K decision {full, split, tail} (see kSplitUnits), then at
+// [E + 4, 2E + 4] the same prefix of remainder tiles.  Expert e has
+// ceil(M_e / BM) whole tiles, or, with rem set and a remainder
+// r = M_e mod BM in 1 .. kRemThr, floor(M_e / BM) whole tiles and
+// ceil(r / kRemBM) remainder tiles.  With offsets == NULL the plan describes
 // one group of uniform_rows rows and offsets_copy receives {0, uniform_rows}.
 // One block of 1024 threads (E <= 1024).
 // With prefix2 != NULL the same block also writes the plan of a second GEMM
-// over the same groups (BM2, rem_bm2, NT2, nk2), so two GEMMs share a launch.
+// over the same groups (BM2, rem2, NT2, nk2), so two GEMMs share a launch.
 __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ offsets, int E, int uniform_rows,
-                                                    int BM, int rem_bm, int NT, int nk,
+                                                    int BM, int rem, int NT, int nk,
                                                     int32_t* __restrict__ prefix, int32_t* __restrict__ offsets_copy,
-                                                    int BM2, int rem_bm2, int NT2, int nk2,
+                                                    int BM2, int rem2, int NT2, int nk2,
                                                     int32_t* __restrict__ prefix2) {
     __shared__ int32_t scan[2][1024];
     const int e = threadIdx.x;
@@ -637,18 +738,13 @@ __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ 
     } else if (e < E) {
         M = offsets[e + 1] - offsets[e];
     }
-    auto plan = [&](int bm, int rbm, int nt, int nkk, int32_t* pre) {
-        int32_t n = (M + bm - 1) / bm, n2 = 0;
-        if (rbm > 0) {
-            const int32_t r = M % bm;
-            if (r > 0 && r <= kRemThr) {
-                n = M / bm;
-                n2 = (r + rbm - 1) / rbm;
-            }
-        }
+    auto plan = [&](int bm, int rm, int nt, int nkk, int32_t* pre) {
+        const int32_t whole = whole_tiles(M, bm, rm != 0);
+        const int32_t r = M - whole * bm;            // rows left for remainder tiles (0 unless rm)
+        const int32_t nr = r > 0 ? (r + kRemBM - 1) / kRemBM : 0;
         __syncthreads();   // a previous plan's reads of scan are done
-        scan[0][e] = n;
-        scan[1][e] = n2;
+        scan[0][e] = whole;
+        scan[1][e] = nr;
         __syncthreads();
         for (int off = 1; off < 1024; off <<= 1) {
             const int32_t v0 = e >= off ? scan[0][e - off] : 0;
@@ -658,41 +754,45 @@ __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ 
             scan[1][e] += v1;
             __syncthreads();
         }
-        const int plans = rbm > 0 ? 2 : 1;
-        for (int h = 0; h < plans; ++h) {
-            int32_t* pr = pre + h * (E + 4);
-            if (e == 0) pr[0] = 0;
-            if (e < E) pr[e + 1] = scan[h][e];
-            if (e == 0) {
-                const int total = scan[h][E - 1] * nt;
-                const int rem = total % kSplitUnits;
-                int split = 1, tail = 0;
-                if (rem > 0 && rem <= kSplitUnits / 2) {
-                    int sp = kSplitUnits / rem;
-                    sp = min(sp, kMaxSplit);
-                    sp = min(sp, nkk / 4);                 // at least 4 slices per range
-                    if (sp >= 2) {
-                        split = sp;
-                        tail = rem;
-                    }
+        if (e == 0) {
+            pre[0] = 0;
+            pre[E + 4] = 0;
+        }
+        if (e < E) {
+            pre[e + 1] = scan[0][e];
+            pre[E + 4 + e + 1] = scan[1][e];
+        }
+        if (e == 0) {
+            const int total = (scan[0][E - 1] + scan[1][E - 1]) * nt;
+            const int left = total % kSplitUnits;
+            int split = 1, tail = 0;
+            if (left > 0 && left <= kSplitUnits / 2) {
+                int sp = kSplitUnits / left;
+                sp = min(sp, kMaxSplit);
+                sp = min(sp, nkk / 4);                 // at least 4 slices per range
+                if (sp >= 2) {
+                    split = sp;
+                    tail = left;
                 }
-                pr[E + 1] = total - tail;
-                pr[E + 2] = split;
-                pr[E + 3] = tail;
             }
+            pre[E + 1] = total - tail;
+            pre[E + 2] = split;
+            pre[E + 3] = tail;
         }
     };
-    plan(BM, rem_bm, NT, nk, prefix);
-    if (prefix2) plan(BM2, rem_bm2, NT2, nk2, prefix2);
+    plan(BM, rem, NT, nk, prefix);
+    if (prefix2) plan(BM2, rem2, NT2, nk2, prefix2);
 }
 
-size_t ffn_tile_plan_ints(int E) { return 2 * ((size_t)E + 4); }
+size_t ffn_tile_plan_ints(int E) { return 2 * (size_t)E + 5; }
 
 // Tile counts and K slices of a grouped GEMM as launch_grouped_gemm sets them.
-static void gemm_geometry(bool bf16, int epi, int N, int K, int BM, int BN, int& NT, int& nk, int& rem_bm) {
+static bool uses_rem(bool bf16, int BM) { return MOE_GEMM_REM && MOE_GEMM_WGN256 == 2 && bf16 && BM == 256; }
+
+static void gemm_geometry(bool bf16, int epi, int N, int K, int BM, int BN, int& NT, int& nk, int& rem) {
     NT = epi_swiglu(epi) ? N / (BN / 2) : N / BN;
     nk = K * (bf16 ? 2 : 4) / 128;
-    rem_bm = (MOE_GEMM_REM && bf16 && BM == 256) ? kRemBM : 0;
+    rem = uses_rem(bf16, BM) ? 1 : 0;
 }
 
 hipError_t launch_tile_plans(bool bf16, const int32_t* offsets, int E, int64_t max_rows, int epi1, int N1, int K1,
@@ -726,24 +826,46 @@ GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N) {
 
 // Whole tiles, split units (exit at once when the plan has no split), fixup;
 // the last two only when the plan may have a split.
+template <bool BF16, int BM, int BN>
+constexpr int waves_n() { return (BF16 && BM == 256 && BN == 256) ? MOE_GEMM_WGN256 : 2; }
+
 template <bool BF16, int BM, int BN, int EPI>
 static void launch_pair(const GemmParams& p, int grid, bool may_split, hipStream_t s) {
-    hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, false>), dim3(grid), dim3(256), 0, s, p);
+    constexpr int WGN = waves_n<BF16, BM, BN>();
+    typedef GemmEpilogue<BF16, BM, BN, EPI, 2, WGN> Epi;
+    hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, false, WGN>), dim3(grid), dim3(128 * WGN), 0, s, p);
     if (!may_split) return;
-    hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, true>), dim3(kSplitUnits), dim3(256), 0, s, p);
-    constexpr int groups = GemmEpilogue<BF16, BM, BN, EPI>::FN / GemmEpilogue<BF16, BM, BN, EPI>::IG;
-    hipLaunchKernelGGL((k_split_fixup<BF16, BM, BN, EPI>), dim3(kSplitUnits / 2 * 4 * groups), dim3(64), 0, s, p);
+    hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, true, WGN>), dim3(kSplitUnits), dim3(128 * WGN), 0, s, p);
+    constexpr int groups = Epi::FN / Epi::IG;
+    hipLaunchKernelGGL((k_split_fixup<BF16, BM, BN, EPI, 2, WGN>), dim3(kSplitUnits / 2 * Epi::NW * groups), dim3(64),
+                       0, s, p);
 }
 
 template <bool BF16, int BM, int BN>
 static void launch_bmbn(int epi, const GemmParams& p, int grid, bool ms, hipStream_t s) {
+    // SwiGLU tiles need an even number of MFMA blocks per wave along N (gate
+    // and up blocks in pairs); gemm_shape_supported() keeps other shapes away
+    constexpr bool swiglu_ok = (BN / waves_n<BF16, BM, BN>() / mfma_block<BF16>()) % 2 == 0;
     switch (epi) {
         case EPI_STORE: launch_pair<BF16, BM, BN, EPI_STORE>(p, grid, ms, s); break;
         case EPI_RELU: launch_pair<BF16, BM, BN, EPI_RELU>(p, grid, ms, s); break;
         case EPI_RELU_SAVE: launch_pair<BF16, BM, BN, EPI_RELU_SAVE>(p, grid, ms, s); break;
-        case EPI_SWIGLU_SAVE: launch_pair<BF16, BM, BN, EPI_SWIGLU_SAVE>(p, grid, ms, s); break;
-        default: launch_pair<BF16, BM, BN, EPI_SWIGLU>(p, grid, ms, s); break;
+        case EPI_SWIGLU_SAVE:
+            if constexpr (swiglu_ok) launch_pair<BF16, BM, BN, EPI_SWIGLU_SAVE>(p, grid, ms, s);
+            break;
+        default:
+            if constexpr (swiglu_ok) launch_pair<BF16, BM, BN, EPI_SWIGLU>(p, grid, ms, s);
+            break;
     }
+}
+
+// Whether launch_t has a kernel for this tile shape and epilogue.
+static bool gemm_shape_supported(bool bf16, int epi, int BM, int BN) {
+    if (!bf16 && BM > 128) return false;
+    if (!epi_swiglu(epi)) return true;
+    const int mb = bf16 ? mfma_block<true>() : mfma_block<false>();
+    const int wgn = (bf16 && BM == 256 && BN == 256) ? MOE_GEMM_WGN256 : 2;
+    return (BN / wgn / mb) % 2 == 0;
 }
 
 template <bool BF16>
@@ -786,43 +908,38 @@ hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, c
     GemmParams p;
     p.A = A; p.lda = lda; p.B0 = B0; p.B1 = B1; p.bstride = b_expert_stride;
     p.C = C; p.ldc = ldc; p.N = N; p.K = K; p.E = offsets ? E : 1;
-    p.NT = epi_swiglu(epi) ? N / (BN / 2) : N / BN;
-    p.nk = K * (bf16 ? 2 : 4) / 128;
+    int rem = 0;
+    gemm_geometry(bf16, epi, N, K, BM, BN, p.NT, p.nk, rem);
     p.offsets = offsets ? offsets : plan_copy;
     p.plan = plan;
     p.partial = partial;
     p.C2 = C2;
     p.ldc2 = ldc2;
-    p.rem_bm = 0;
-    const bool rem = MOE_GEMM_REM && bf16 && BM == 256;
+    p.rem = rem;
+    p.unit_f4 = (int64_t)BM * BN / 4;
+    if (!gemm_shape_supported(bf16, epi, BM, BN) || (rem && !gemm_shape_supported(bf16, epi, kRemBM, BN)))
+        return hipErrorInvalidValue;
     if (!plan_ready)
-        hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, offsets, E, (int)max_rows, BM, rem ? kRemBM : 0,
-                           p.NT, p.nk, plan, plan_copy, 0, 0, 0, 0, (int32_t*)nullptr);
-    const int64_t m_tiles_ub = (max_rows + BM - 1) / BM + (p.E > 1 ? p.E : 0);
-    int64_t grid = (m_tiles_ub * p.NT + 7) / 8 * 8;
+        hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, offsets, E, (int)max_rows, BM, rem, p.NT, p.nk,
+                           plan, plan_copy, 0, 0, 0, 0, (int32_t*)nullptr);
+    // row tiles: at most ceil(rows / BM) plus, per expert, one partial tile or
+    // up to ceil(kRemThr / kRemBM) remainder tiles
+    const int64_t per_expert = rem ? (kRemThr + kRemBM - 1) / kRemBM : 1;
+    const int64_t m_tiles_ub = (max_rows + BM - 1) / BM + (p.E > 1 ? p.E * per_expert : per_expert);
+    const int64_t grid = (m_tiles_ub * p.NT + 7) / 8 * 8;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    if (!bf16 && BM > 128) return hipErrorInvalidValue;
-    // With offsets == NULL the host knows the row count and launches only
-    // the parts of the plan that have work; routed counts live on the device.
-    bool main_split = true, rem_launch = rem, rem_split = true;
+    // With offsets == NULL the host knows the row count and launches the
+    // split-K parts only when the plan has a tail; routed counts live on the
+    // device.
+    bool may_split = true;
     if (offsets == nullptr) {
-        const int64_t r = max_rows % BM;
-        const bool rem_active = rem && r > 0 && r <= kRemThr;
-        const int64_t n_main = rem_active ? max_rows / BM : (max_rows + BM - 1) / BM;
-        main_split = plan_may_split(n_main * p.NT, p.nk);
-        rem_launch = rem_active;
-        rem_split = rem_active && plan_may_split((r + kRemBM - 1) / kRemBM * p.NT, p.nk);
+        const int64_t whole = whole_tiles((int)max_rows, BM, rem != 0);
+        const int64_t r = max_rows - whole * BM;
+        const int64_t tiles = whole + (r > 0 ? (r + kRemBM - 1) / kRemBM : 0);
+        may_split = plan_may_split(tiles * p.NT, p.nk);
     }
-    if (bf16) launch_t<true>(epi, p, BM, BN, (int)grid, main_split, s);
-    else launch_t<false>(epi, p, BM, BN, (int)grid, main_split, s);
-    if (rem_launch) {
-        GemmParams q = p;
-        q.plan = plan + (p.E + 4);
-        q.rem_bm = BM;
-        const int64_t grid2 = ((int64_t)p.E * ((kRemThr + kRemBM - 1) / kRemBM) * p.NT + 7) / 8 * 8;
-        if (grid2 > 0x7fffffff) return hipErrorInvalidValue;
-        launch_t<true>(epi, q, kRemBM, BN, (int)grid2, rem_split, s);
-    }
+    if (bf16) launch_t<true>(epi, p, BM, BN, (int)grid, may_split, s);
+    else launch_t<false>(epi, p, BM, BN, (int)grid, may_split, s);
     return hipGetLastError();
 }
 

@@ -74,7 +74,7 @@ size_t gemm_partial_bytes(int BM, int BN);
 // stores a to C2.
 // Builds the tile plan on the device (offsets == NULL: one group of max_rows
 // rows, whose offsets go to plan_copy), then runs the GEMM and its split-K
-// fixup; with 256-row bf16 tiles a second launch of 64-row tiles covers the
+// fixup; with 256-row bf16 tiles, 64-row tiles of the same launch cover the
 // rows an expert has left past its whole tiles when there are at most 128.
 hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B0, const void* B1,
                                int64_t b_expert_stride, void* C, int64_t ldc, int N, int K, int E,

@@ -1,0 +1,152 @@
+// Achievable-peak microbenchmarks of one MI355X (gfx950), used by the
+// benchmark to quote measured ceilings beside the published ones:
+//   * matrix-core rate: waves issuing independent bf16 MFMAs back to back
+//     from registers (no memory traffic), for the two bf16 shapes the
+//     grouped GEMMs could use (16x16x32 and 32x32x16);
+//   * device-memory copy rate: 16-byte loads and stores over buffers far
+//     larger than the 256 MB last-level cache;
+//   * a cache flush: a pass of plain stores over a large buffer, so that a
+//     timed stage does not find its inputs in the last-level cache.
+// These entry points are a measurement aid and not part of the layer's ABI
+// (include/moe.h); they are built into their own library.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace {
+
+using moe::bf16x8_t;
+using moe::floatx16_t;
+using moe::floatx4_t;
+
+// Each wave computes a 128 x 128 tile of accumulators in the grouped GEMM's
+// register pattern: NB weight fragments times NB activation fragments per
+// k-step, weight fragment outer (64 16x16x32 blocks, or 16 32x32x16 blocks,
+// 256 accumulator registers either way), iters k-steps of 128 x 128 x K
+// (K = 32 or 16), i.e. iters * 1048576 (shape 16) or iters * 524288 (shape
+// 32) flops per wave.  Operands are fixed per lane but differ between
+// fragments and lanes (bit patterns of ordinary bf16 numbers), so the
+// multipliers toggle as they do on real data.  The accumulator sum is stored
+// so that nothing is optimised away.
+template <int SHAPE>
+__global__ __launch_bounds__(256) void k_peak_mfma(int iters, float* __restrict__ out) {
+    constexpr int NB = SHAPE == 16 ? 8 : 4;
+    const uint32_t seed = (blockIdx.x * 256u + threadIdx.x) * 2654435761u;
+    bf16x8_t a[NB], b[NB];
+#pragma unroll
+    for (int v = 0; v < NB; ++v) {
+        moe::u32x4_t wa, wb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // bf16 pairs with exponents near 1.0 and random mantissas and signs
+            const uint32_t r1 = (seed ^ (0x9e3779b9u * (4 * v + i + 1))) * 0x85ebca6bu;
+            const uint32_t r2 = (seed ^ (0xc2b2ae35u * (4 * v + i + 7))) * 0x27d4eb2fu;
+            wa[i] = (0x3f003f00u | (r1 & 0x807f807fu));
+            wb[i] = (0x3f003f00u | (r2 & 0x807f807fu));
+        }
+        a[v] = __builtin_bit_cast(bf16x8_t, wa);
+        b[v] = __builtin_bit_cast(bf16x8_t, wb);
+    }
+    float s = 0.0f;
+    if constexpr (SHAPE == 16) {
+        floatx4_t acc[NB][NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[i], a[j], acc[i][j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) s += acc[i][j][0] + acc[i][j][1] + acc[i][j][2] + acc[i][j][3];
+    } else {
+        floatx16_t acc[NB][NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[i], a[j], acc[i][j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s += acc[i][j][r];
+    }
+    out[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+// dst[i] = src[i] for n16 16-byte chunks; each thread moves 4 chunks per
+// round, a grid stride apart, with the 4 loads in flight together.
+__global__ __launch_bounds__(256) void k_peak_copy(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                   int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+        dst[i] = v0;
+        dst[i + stride] = v1;
+        dst[i + 2 * stride] = v2;
+        dst[i + 3 * stride] = v3;
+    }
+    for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+// buf[i] = value for n16 16-byte chunks (plain stores).
+__global__ __launch_bounds__(256) void k_fill16(uint4* __restrict__ buf, int64_t n16, uint32_t value) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const uint4 v = make_uint4(value, value ^ 1u, value ^ 2u, value ^ 3u);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) buf[i] = v;
+}
+
+}  // namespace
+
+extern "C" {
+
+// MFMA rate probe: `blocks` blocks of 256 threads (4 waves), each wave
+// issuing iters * 64 v_mfma_f32_16x16x32_bf16 (shape 16: iters * 1048576
+// flops) or iters * 16 v_mfma_f32_32x32x16_bf16 (shape 32: iters * 524288
+// flops).  out: blocks * 256 floats (device).  0 on success, -1 for
+// bad arguments, else the HIP error.
+int moe_peak_mfma(int shape, int iters, int blocks, float* out, void* stream) {
+    if ((shape != 16 && shape != 32) || iters <= 0 || blocks <= 0 || !out) return -1;
+    hipStream_t s = (hipStream_t)stream;
+    if (shape == 16)
+        hipLaunchKernelGGL(k_peak_mfma<16>, dim3(blocks), dim3(256), 0, s, iters, out);
+    else
+        hipLaunchKernelGGL(k_peak_mfma<32>, dim3(blocks), dim3(256), 0, s, iters, out);
+    return (int)hipGetLastError();
+}
+
+// Copy probe: bytes (a multiple of 16) from src to dst, both device buffers
+// of at least that size.
+int moe_peak_copy(const void* src, void* dst, int64_t bytes, int blocks, void* stream) {
+    if (!src || !dst || bytes <= 0 || (bytes & 15) || blocks <= 0) return -1;
+    hipLaunchKernelGGL(k_peak_copy, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)src, (uint4*)dst,
+                       bytes / 16);
+    return (int)hipGetLastError();
+}
+
+// Cache flush: plain stores of `bytes` (a multiple of 16) into buf.
+int moe_cache_flush(void* buf, int64_t bytes, uint32_t value, void* stream) {
+    if (!buf || bytes <= 0 || (bytes & 15)) return -1;
+    hipLaunchKernelGGL(k_fill16, dim3(4096), dim3(256), 0, (hipStream_t)stream, (uint4*)buf, bytes / 16, value);
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"
