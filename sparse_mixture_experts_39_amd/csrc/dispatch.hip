@@ -20,11 +20,16 @@
 //                 inside each expert), capacity cut, exclusive scan over
 //                 experts -> offsets, and the load statistics; k_scan_wave
 //                 is the same for at most 64 experts in one wave
-//   k_scatter     same ranking as k_histogram, plus the wave prefix inside the
-//                 block -> slot_pos / perm_src
-//   k_permute_tokens  token-major: each token row of x is read once and
-//                 written to the rows its kept slots point at (slot_pos),
-//                 16-byte vector copies
+//   k_scatter_permute  block-owned tokens: their assignments' ranks (the
+//                 scan's base for the histogram block plus the earlier ids of
+//                 that block) -> slot_pos / perm_src, and each owned token
+//                 row of x read once into registers and written to the rows
+//                 its kept slots point at, 16-byte vector copies
+//   k_scatter, k_permute_tokens  the same in two passes, for rows too wide
+//                 for one block's registers (and k_scatter alone for the
+//                 capacity reroute)
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -230,34 +235,85 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ top
 }
 
 // Grid-stride over (token, 16-byte chunk): the chunk is read once and stored
-// to every kept slot's row.  A wave covers consecutive chunks of one row, so
-// its slot_pos reads hit one address.
+// to every kept slot's row (rows too wide for k_scatter_permute's registers).
 __global__ __launch_bounds__(256) void k_permute_tokens(const uint4* __restrict__ x, int k, int cpr,
                                                         const int32_t* __restrict__ slot_pos, int64_t T,
                                                         uint4* __restrict__ x_perm) {
     const int64_t total = T * cpr;
-    const int64_t stride = (int64_t)gridDim.x * 256 * 4;
-    for (int64_t base = (int64_t)blockIdx.x * 256 * 4 + threadIdx.x; base < total; base += stride) {
-        uint4 v[4];
-        int64_t t[4];
-        int c[4];
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
+        const int64_t t = i / cpr;
+        const int c = (int)(i - t * cpr);
+        const uint4 v = x[i];
+        for (int j = 0; j < k; ++j) {
+            const int32_t r = slot_pos[t * k + j];
+            if (r >= 0) x_perm[(int64_t)r * cpr + c] = v;
+        }
+    }
+}
+
+// Scatter and row copy in one pass.  Block b owns tokens [b TPB, b TPB + TPB)
+// and their assignments a = t k + j.  The rank of a inside its expert is the
+// scan's base for a's histogram block plus the number of earlier assignments
+// of that block to the same expert (counted from the block's ids, staged in
+// LDS), so slot_pos / perm_src match k_scatter exactly.  The owned token rows
+// of x are read into registers before the ranks are known and stored to every
+// kept slot's row afterwards: each x row is read once, and the rank work
+// overlaps the loads.
+constexpr int kSpMaxChunks = 16;   // 16-byte chunks per thread (registers)
+constexpr int kSpMaxAssign = 256;  // assignments per block
+
+__global__ __launch_bounds__(256) void k_scatter_permute(const int32_t* __restrict__ topk_idx, int64_t T, int k,
+                                                         int E, int tpb, const int32_t* __restrict__ blockbase,
+                                                         const int32_t* __restrict__ offsets, int64_t capacity,
+                                                         const uint4* __restrict__ x, int cpr,
+                                                         int32_t* __restrict__ perm_src,
+                                                         int32_t* __restrict__ slot_pos, uint4* __restrict__ x_perm) {
+    __shared__ int32_t sidx[kAssignBlock + kSpMaxAssign];
+    __shared__ int32_t srow[kSpMaxAssign];
+    const int tid = threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.x * tpb;
+    const int nt = (int)min((int64_t)tpb, T - t0);
+    if (nt <= 0) return;
+    const int64_t a0 = t0 * k, a1 = (t0 + nt) * k;
+    const int64_t h0 = a0 / kAssignBlock * kAssignBlock;   // first histogram block touched
+    const int nidx = (int)(a1 - h0);
+    for (int i = tid; i < nidx; i += 256) sidx[i] = topk_idx[h0 + i];
+    // the owned rows of x, chunk q = tid + 256 i of the block's nt * cpr chunks
+    const int nch = nt * cpr;
+    uint4 v[kSpMaxChunks];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t i = base + (int64_t)u * 256;
-            t[u] = -1;
-            if (i < total) {
-                t[u] = i / cpr;
-                c[u] = (int)(i - t[u] * cpr);
-                v[u] = x[i];
+    for (int i = 0; i < kSpMaxChunks; ++i) {
+        const int q = tid + 256 * i;
+        if (q < nch) v[i] = x[t0 * cpr + q];
+    }
+    __syncthreads();
+    const int na = (int)(a1 - a0);
+    if (tid < na) {
+        const int64_t a = a0 + tid;
+        const int ev = sidx[a - h0];
+        int32_t row = -1;
+        if (ev >= 0 && ev < E) {       // an id outside [0, E) is dropped (never indexes memory)
+            const int64_t hb = a / kAssignBlock;
+            int32_t r = blockbase[hb * E + ev];
+            for (int64_t q = hb * kAssignBlock; q < a; ++q) r += sidx[q - h0] == ev;
+            if (capacity < 0 || (int64_t)r < capacity) {
+                row = offsets[ev] + r;
+                perm_src[row] = (int32_t)a;
             }
         }
+        slot_pos[a] = row;
+        srow[tid] = row;
+    }
+    __syncthreads();
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (t[u] < 0) continue;
-            for (int j = 0; j < k; ++j) {
-                const int32_t r = slot_pos[t[u] * k + j];
-                if (r >= 0) x_perm[(int64_t)r * cpr + c[u]] = v[u];
-            }
+    for (int i = 0; i < kSpMaxChunks; ++i) {
+        const int q = tid + 256 * i;
+        if (q >= nch) break;
+        const int u = q / cpr, c = q - u * cpr;
+        for (int j = 0; j < k; ++j) {
+            const int32_t r = srow[u * k + j];
+            if (r >= 0) x_perm[(int64_t)r * cpr + c] = v[i];
         }
     }
 }
@@ -289,15 +345,28 @@ void launch_scatter(const int32_t* topk_idx, int64_t n_assign, int E, const int3
                        blockbase, offsets, capacity, perm_src, slot_pos);
 }
 
-void launch_permute_tokens(const void* x, int k, int d, int elem_bytes, const int32_t* slot_pos, int64_t T,
-                           void* x_perm, hipStream_t s) {
+void launch_scatter_permute(const int32_t* topk_idx, int64_t T, int k, int E, const int32_t* blockbase,
+                            const int32_t* offsets, int64_t capacity, const void* x, int d, int elem_bytes,
+                            int32_t* perm_src, int32_t* slot_pos, void* x_perm, hipStream_t s) {
+    if (T <= 0) return;
     const int cpr = d * elem_bytes / 16;
-    const int64_t total = T * cpr;
-    if (total == 0) return;
-    int64_t nb = (total + 1023) / 1024;
-    if (nb > 16384) nb = 16384;
-    hipLaunchKernelGGL(k_permute_tokens, dim3((unsigned)nb), dim3(256), 0, s, (const uint4*)x, k, cpr, slot_pos, T,
-                       (uint4*)x_perm);
+    if (cpr > 256 * kSpMaxChunks || k > kSpMaxAssign) {
+        // a row does not fit the registers of one block, or a token has more
+        // slots than one block ranks: scatter, then copy
+        launch_scatter(topk_idx, T * k, E, blockbase, offsets, capacity, perm_src, slot_pos, s);
+        const int64_t nb = std::min<int64_t>((T * cpr + 255) / 256, 16384);
+        hipLaunchKernelGGL(k_permute_tokens, dim3((unsigned)nb), dim3(256), 0, s, (const uint4*)x, k, cpr, slot_pos,
+                           T, (uint4*)x_perm);
+        return;
+    }
+    // tokens per block: as many as fit kSpMaxChunks chunks per thread and
+    // kSpMaxAssign assignments
+    int tpb = 256 * kSpMaxChunks / cpr;
+    if (tpb > kSpMaxAssign / k) tpb = kSpMaxAssign / k;
+    if (tpb < 1) tpb = 1;
+    const int64_t nb = (T + tpb - 1) / tpb;
+    hipLaunchKernelGGL(k_scatter_permute, dim3((unsigned)nb), dim3(256), 0, s, topk_idx, T, k, E, tpb, blockbase,
+                       offsets, capacity, (const uint4*)x, cpr, perm_src, slot_pos, (uint4*)x_perm);
 }
 
 }  // namespace moe

@@ -91,18 +91,23 @@ __global__ __launch_bounds__(256) void k_peak_mfma(int iters, float* __restrict_
     out[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
-// dst[i] = src[i] for n16 16-byte chunks; each thread moves 4 chunks per
-// round, a grid stride apart, with the 4 loads in flight together.
-__global__ __launch_bounds__(256) void k_peak_copy(const uint4* __restrict__ src, uint4* __restrict__ dst,
+// dst[i] = src[i] for n16 16-byte chunks; each thread moves U chunks per
+// round, a grid stride apart, with the U loads in flight together (NT:
+// non-temporal loads and stores, which do not keep the lines in the caches).
+template <int U, bool NT>
+__global__ __launch_bounds__(256) void k_peak_copy(const moe::u32x4_t* __restrict__ src, moe::u32x4_t* __restrict__ dst,
                                                    int64_t n16) {
     const int64_t stride = (int64_t)gridDim.x * 256;
     int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
-        dst[i] = v0;
-        dst[i + stride] = v1;
-        dst[i + 2 * stride] = v2;
-        dst[i + 3 * stride] = v3;
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        moe::u32x4_t v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = NT ? __builtin_nontemporal_load(&src[i + u * stride]) : src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (NT) __builtin_nontemporal_store(v[u], &dst[i + u * stride]);
+            else dst[i + u * stride] = v[u];
+        }
     }
     for (; i < n16; i += stride) dst[i] = src[i];
 }
@@ -134,11 +139,21 @@ int moe_peak_mfma(int shape, int iters, int blocks, float* out, void* stream) {
 }
 
 // Copy probe: bytes (a multiple of 16) from src to dst, both device buffers
-// of at least that size.
-int moe_peak_copy(const void* src, void* dst, int64_t bytes, int blocks, void* stream) {
-    if (!src || !dst || bytes <= 0 || (bytes & 15) || blocks <= 0) return -1;
-    hipLaunchKernelGGL(k_peak_copy, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)src, (uint4*)dst,
-                       bytes / 16);
+// of at least that size; `blocks` blocks of 256 threads, `unroll` (4 or 8)
+// 16-byte chunks in flight per thread, non-temporal accesses when nt != 0.
+int moe_peak_copy(const void* src, void* dst, int64_t bytes, int blocks, int unroll, int nt, void* stream) {
+    if (!src || !dst || bytes <= 0 || (bytes & 15) || blocks <= 0 || (unroll != 4 && unroll != 8)) return -1;
+    hipStream_t s = (hipStream_t)stream;
+    const moe::u32x4_t* a = (const moe::u32x4_t*)src;
+    moe::u32x4_t* b = (moe::u32x4_t*)dst;
+    const int64_t n = bytes / 16;
+    if (unroll == 4) {
+        if (nt) hipLaunchKernelGGL((k_peak_copy<4, true>), dim3(blocks), dim3(256), 0, s, a, b, n);
+        else hipLaunchKernelGGL((k_peak_copy<4, false>), dim3(blocks), dim3(256), 0, s, a, b, n);
+    } else {
+        if (nt) hipLaunchKernelGGL((k_peak_copy<8, true>), dim3(blocks), dim3(256), 0, s, a, b, n);
+        else hipLaunchKernelGGL((k_peak_copy<8, false>), dim3(blocks), dim3(256), 0, s, a, b, n);
+    }
     return (int)hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ def lib():
         L.moe_peak_mfma.restype = ctypes.c_int
         L.moe_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
         L.moe_peak_copy.restype = ctypes.c_int
-        L.moe_peak_copy.argtypes = [P, P, ctypes.c_int64, ctypes.c_int, P]
+        L.moe_peak_copy.argtypes = [P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P]
         L.moe_cache_flush.restype = ctypes.c_int
         L.moe_cache_flush.argtypes = [P, ctypes.c_int64, ctypes.c_uint32, P]
         _lib = L
@@ -75,9 +75,9 @@ def mfma_tflops(shape: int, blocks_per_cu: int = 1, iters: int = 10000, reps: in
     return flops / t / 1e12
 
 
-def copy_gbs(mib: int = 2048, reps: int = 5) -> float:
+def copy_gbs(mib: int = 2048, reps: int = 5, blocks_per_cu: int = 8, unroll: int = 8, nt: bool = False) -> float:
     """Device copy rate (GB/s counting bytes read + bytes written) over two
-    buffers of mib MiB each."""
+    buffers of mib MiB each (far beyond the 256 MB last-level cache)."""
     n = mib << 20
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -85,8 +85,8 @@ def copy_gbs(mib: int = 2048, reps: int = 5) -> float:
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
 
     def run():
-        rc = lib().moe_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n, n_cu * 8,
-                                 _stream())
+        rc = lib().moe_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n,
+                                 n_cu * blocks_per_cu, unroll, int(nt), _stream())
         if rc != 0:
             raise RuntimeError(f"moe_peak_copy failed ({rc})")
 
@@ -94,6 +94,18 @@ def copy_gbs(mib: int = 2048, reps: int = 5) -> float:
     torch.cuda.synchronize()
     t = _timed(run, reps)
     return 2.0 * n / t / 1e9
+
+
+def best_copy_gbs() -> Dict[str, float]:
+    """The copy probe over a small sweep of launch shapes; the best is the
+    measured copy ceiling."""
+    res = {}
+    for bpc in (4, 8, 16):
+        for unroll in (4, 8):
+            for nt in (False, True):
+                res[f"copy_b{bpc}_u{unroll}{'_nt' if nt else ''}"] = copy_gbs(blocks_per_cu=bpc, unroll=unroll, nt=nt,
+                                                                             reps=3)
+    return res
 
 
 def flush(buf: torch.Tensor, value: int = 0):
@@ -105,8 +117,10 @@ def flush(buf: torch.Tensor, value: int = 0):
 
 
 def measure_all() -> Dict[str, float]:
-    return {
+    res = {
         "mfma_bf16_16x16x32_tflops": mfma_tflops(16),
         "mfma_bf16_32x32x16_tflops": mfma_tflops(32),
-        "copy_gbs": copy_gbs(),
+        **best_copy_gbs(),
     }
+    res["copy_gbs"] = max(v for k, v in res.items() if k.startswith("copy_"))
+    return res

@@ -77,6 +77,14 @@ MID = {
                                  residual=True, reroute=True, seed=35),
     "reroute_hash_f32": Config("reroute_hash_f32", T=512, d=64, F=128, E=16, k=3, act_dtype="f32", act="relu",
                                gate="hash", capacity_factor=0.9, residual=True, reroute=True, seed=36),
+    # rows wider than one block's registers (4160 16-byte chunks): dispatch
+    # falls back to scatter + copy, combine runs in column passes
+    "wide_rows": Config("wide_rows", T=70, d=33280, F=64, E=4, k=2, act_dtype="bf16", act="relu",
+                        gate="softmax_topk", residual=True, seed=38),
+    # expert choice with more than 256 (and 512) slots per token: dispatch
+    # ranks in two passes, combine reads the slot rows unstaged
+    "ec_wide_slots": Config("ec_wide_slots", T=150, d=64, F=64, E=600, k=2, act_dtype="bf16", act="relu",
+                            gate="expert_choice", capacity_factor=1.0, residual=True, seed=39),
     # more than 64 experts: ranked lists of 16, then the full scan once they are used up
     "reroute_many_experts": Config("reroute_many_experts", T=900, d=64, F=64, E=200, k=2, act_dtype="bf16",
                                    act="relu", gate="softmax_full", capacity_factor=1.0, logit_bias="zipf",
