@@ -255,13 +255,14 @@ __global__ __launch_bounds__(256) void k_permute_tokens(const uint4* __restrict_
 // Scatter and row copy in one pass.  Block b owns tokens [b TPB, b TPB + TPB)
 // and their assignments a = t k + j.  The rank of a inside its expert is the
 // scan's base for a's histogram block plus the number of earlier assignments
-// of that block to the same expert (counted from the block's ids, staged in
-// LDS), so slot_pos / perm_src match k_scatter exactly.  The owned token rows
-// of x are read into registers before the ranks are known and stored to every
-// kept slot's row afterwards: each x row is read once, and the rank work
-// overlaps the loads.
-constexpr int kSpMaxChunks = 16;   // 16-byte chunks per thread (registers)
-constexpr int kSpMaxAssign = 256;  // assignments per block
+// of that block to the same expert (counted with wave ballots over the
+// block's ids, staged in LDS), so slot_pos / perm_src match k_scatter
+// exactly.  The owned token rows of x are read into registers before the
+// ranks are known and stored to every kept slot's row afterwards: each x row
+// is read once, and the rank work overlaps the loads.  Blocks are small
+// (a few tokens), so many of them are in flight on every CU.
+constexpr int kSpMaxChunks = 4;    // 16-byte chunks per thread (registers)
+constexpr int kSpMaxAssign = 64;   // assignments per block
 
 __global__ __launch_bounds__(256) void k_scatter_permute(const int32_t* __restrict__ topk_idx, int64_t T, int k,
                                                          int E, int tpb, const int32_t* __restrict__ blockbase,
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(256) void k_scatter_permute(const int32_t* __restri
                                                          int32_t* __restrict__ slot_pos, uint4* __restrict__ x_perm) {
     __shared__ int32_t sidx[kAssignBlock + kSpMaxAssign];
     __shared__ int32_t srow[kSpMaxAssign];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t t0 = (int64_t)blockIdx.x * tpb;
     const int nt = (int)min((int64_t)tpb, T - t0);
     if (nt <= 0) return;
@@ -288,22 +289,31 @@ __global__ __launch_bounds__(256) void k_scatter_permute(const int32_t* __restri
         if (q < nch) v[i] = x[t0 * cpr + q];
     }
     __syncthreads();
+    // wave w ranks the owned assignments i = w, w + 4, ...: the count of
+    // earlier ids equal to its expert in its histogram block, 64 at a time
     const int na = (int)(a1 - a0);
-    if (tid < na) {
-        const int64_t a = a0 + tid;
+    for (int i = wave; i < na; i += 4) {
+        const int64_t a = a0 + i;
         const int ev = sidx[a - h0];
-        int32_t row = -1;
-        if (ev >= 0 && ev < E) {       // an id outside [0, E) is dropped (never indexes memory)
-            const int64_t hb = a / kAssignBlock;
-            int32_t r = blockbase[hb * E + ev];
-            for (int64_t q = hb * kAssignBlock; q < a; ++q) r += sidx[q - h0] == ev;
-            if (capacity < 0 || (int64_t)r < capacity) {
-                row = offsets[ev] + r;
-                perm_src[row] = (int32_t)a;
-            }
+        const bool valid = ev >= 0 && ev < E;   // an id outside [0, E) is dropped (never indexes memory)
+        const int64_t hs = a / kAssignBlock * kAssignBlock;
+        int32_t cnt = 0;
+        for (int64_t q0 = hs; q0 < a; q0 += 64) {
+            const int64_t q = q0 + lane;
+            cnt += __popcll(__ballot(q < a && sidx[q - h0] == ev));
         }
-        slot_pos[a] = row;
-        srow[tid] = row;
+        if (lane == 0) {
+            int32_t row = -1;
+            if (valid) {
+                const int32_t r = blockbase[(a / kAssignBlock) * E + ev] + cnt;
+                if (capacity < 0 || (int64_t)r < capacity) {
+                    row = offsets[ev] + r;
+                    perm_src[row] = (int32_t)a;
+                }
+            }
+            slot_pos[a] = row;
+            srow[i] = row;
+        }
     }
     __syncthreads();
 #pragma unroll

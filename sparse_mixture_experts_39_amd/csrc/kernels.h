@@ -55,7 +55,7 @@ void launch_scatter(const int32_t* topk_idx, int64_t n_assign, int E, const int3
                     const int32_t* offsets, int64_t capacity, int32_t* perm_src, int32_t* slot_pos, hipStream_t s);
 // Scatter (slot_pos / perm_src, as launch_scatter) and the row copy x[t] ->
 // x_perm[slot_pos[t][j]] for every kept slot, in one launch (two when a row
-// has more than 4096 16-byte chunks or a token more than 256 slots);
+// has more than 1024 16-byte chunks or a token more than 64 slots);
 // d * elem_bytes a multiple of 16.
 void launch_scatter_permute(const int32_t* topk_idx, int64_t T, int k, int E, const int32_t* blockbase,
                             const int32_t* offsets, int64_t capacity, const void* x, int d, int elem_bytes,
