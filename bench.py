@@ -76,45 +76,97 @@ def measured_traffic(path, workload, stage):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_stages(cfg, inputs):
+    """The oracle's layer forward (the same calls, in the same order, as
+    oracle.forward), with the wall time of each stage."""
+    import numpy as np
+    import oracle
+    t = {}
+    x = oracle._np(inputs["x"])
+    T = x.shape[0]
+    c0 = time.perf_counter()
+    r = oracle.route(cfg, x, inputs["w_router"], logit_bias=inputs.get("logit_bias"),
+                     sel_bias=inputs.get("sel_bias"), w_noise=inputs.get("w_noise"), noise=None,
+                     want_probs=True, token_ids=inputs.get("token_ids"),
+                     w_group_router=inputs.get("w_group_router"))
+    if getattr(cfg, "reroute", False):
+        r["idx"] = oracle.reroute(cfg, r["keys"], r["idx"])
+    c1 = time.perf_counter()
+    dp = oracle.dispatch(cfg, r["idx"], T=T)
+    x_perm = oracle.gather_rows(cfg, x, dp["perm_src"])
+    c2 = time.perf_counter()
+    y = np.zeros((dp["R"], cfg.d), dtype=np.float64)
+    off = dp["offsets"]
+    for e in range(cfg.E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            y[lo:hi] = oracle.expert_ffn(cfg, x_perm[lo:hi], *oracle.expert_weights(cfg, inputs, e))
+    shared = None
+    if cfg.n_shared:
+        shared = oracle.expert_ffn(cfg, x, *oracle.shared_weights(inputs), F=cfg.F_shared)
+    c3 = time.perf_counter()
+    oracle.combine(cfg, dp["slot_pos"], r["gates"], y, x, shared=shared)
+    oracle.stats(cfg, dp["counts"], dp["kept"], r["P"], T)
+    c4 = time.perf_counter()
+    t.update(route=c1 - c0, dispatch=c2 - c1, experts=c3 - c2, combine=c4 - c3)
+    return t
+
+
 def cpu_baseline(cfg, dinp, target_s):
     """The oracle as it stands, on the host cores, on the first Ts tokens of
     the same workload (whole layer, every weight); Ts is sized so the run
-    takes about target_s seconds."""
+    takes about target_s seconds.  The sized run is timed stage by stage."""
     import oracle
     host = {k: v.cpu() for k, v in dinp.items()}
     cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
 
-    def run(ts):
+    def sub_inputs(ts):
         sub = dict(host)
         sub["x"] = host["x"][:ts].contiguous()
         if "noise" in sub:
             sub["noise"] = host["noise"][:ts].contiguous()
-        c = cfg.replace(T=ts)
+        if "token_ids" in sub:
+            sub["token_ids"] = host["token_ids"][:ts].contiguous()
+        return sub
+
+    def run(ts):
+        sub = sub_inputs(ts)
         t0 = time.perf_counter()
-        oracle.forward(c, sub, noise="philox")
+        oracle.forward(cfg.replace(T=ts), sub, noise="philox")
         return time.perf_counter() - t0
 
     # two probes give the per-token slope and the fixed per-call cost (the
-    # oracle converts every weight to fp64 on each call), then one run sized
-    # for target_s; the second probe is large enough (128 tokens) that the
-    # slope holds at the sized run, where small per-expert row counts no
-    # longer hide the per-row cost
+    # oracle converts every weight to fp64 on each call), then one staged
+    # run sized for target_s; the second probe is large enough (128 tokens)
+    # that the slope holds at the sized run
     n1, n2 = min(16, cfg.T), min(128, cfg.T)
     t1 = run(n1)
-    if cfg.T <= n1 or t1 >= target_s:
-        ts, t = n1, t1
-    else:
+    ts = n1
+    if cfg.T > n1 and t1 < target_s:
         t2 = run(n2)
-        if n2 == cfg.T or t2 >= target_s:
-            ts, t = n2, t2
-        else:
+        ts = n2
+        if n2 < cfg.T and t2 < target_s:
             slope = max((t2 - t1) / (n2 - n1), 1e-6)
             fixed = max(t1 - n1 * slope, 0.0)
             ts = int(min(cfg.T, max(n2, (target_s - fixed) / slope)))
-            t = run(ts) if ts > n2 else t2
+    stages = oracle_stages(cfg.replace(T=ts), sub_inputs(ts))
+    t = sum(stages.values())
     return {"value": ts / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {ts} of the {cfg.T} tokens, whole layer (route, dispatch, experts, combine) "
-                      f"with all weights, {t:.1f} s of oracle time"}
+                      f"with all weights, {t:.1f} s of oracle time",
+            "cpu_model": cpu_model(),
+            "stages_s": stages,
+            "stages_tokens_per_s": {k: (ts / v if v > 0 else None) for k, v in stages.items()}}
 
 
 def main():
@@ -132,6 +184,11 @@ def main():
     ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
                     help="forward (default): the layer forward, stage by stage; backward: moe_layer_backward on the "
                          "saved tensors of one forward (a separate JSON line with its own metric)")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="MiB read before each stage of the cache-flushed stage pass (0: no such pass)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the copy-rate probe of the forward line")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time K replays of one HIP-graph capture of moe_layer_forward (graph_tokens_per_s)")
     ap.add_argument("--peaks", action="store_true",
                     help="only measure the achievable ceilings (register-only bf16 MFMA rate for both MFMA shapes, "
                          "device copy rate) and print them as one JSON line")
@@ -196,42 +253,89 @@ def main():
     if args.which == "backward":
         return bench_backward(args, cfg, c, dinp, w, ws, st, moe, torch)
     stages = ["route", "dispatch", "expert_up", "expert_down"] + (["shared_expert"] if shared is not None else []) + ["combine"]
+    from sparse_mixture_experts_39_amd import peaks
+    flush_buf = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib > 0 else None
 
-    def step(ev):
-        ev[0].record()
-        moe.moe_route(c, x, w, idx, gates, None, st, ws)
-        ev[1].record()
-        moe.moe_dispatch(c, x, idx, x_perm, offsets, perm_src, slot_pos, st, ws)
-        ev[2].record()
-        moe.moe_expert_up(c, x_perm, offsets, w, H, ws)
-        ev[3].record()
-        moe.moe_expert_down(c, H, offsets, w, y_perm, ws)
-        ev[4].record()
-        i = 5
+    def stage_calls():
+        yield lambda: moe.moe_route(c, x, w, idx, gates, None, st, ws)
+        yield lambda: moe.moe_dispatch(c, x, idx, x_perm, offsets, perm_src, slot_pos, st, ws)
+        yield lambda: moe.moe_expert_up(c, x_perm, offsets, w, H, ws)
+        yield lambda: moe.moe_expert_down(c, H, offsets, w, y_perm, ws)
         if shared is not None:
-            moe.moe_shared_expert(c, x, w, shared, ws)
-            ev[i].record()
-            i += 1
-        moe.moe_combine(c, y_perm, slot_pos, gates, x if cfg.residual else None, shared, out)
-        ev[i].record()
+            yield lambda: moe.moe_shared_expert(c, x, w, shared, ws)
+        yield lambda: moe.moe_combine(c, y_perm, slot_pos, gates, x if cfg.residual else None, shared, out)
 
-    nev = len(stages) + 1
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps + args.warmup)]
-    for i in range(args.warmup):
-        step(events[i])
+    def staged_step(ev, flush):
+        # with flush: a read pass over a buffer four times the last-level
+        # cache before each stage, outside its event pair
+        for j, call in enumerate(stage_calls()):
+            if flush:
+                peaks.flush(flush_buf, j)
+            ev[2 * j].record()
+            call()
+            ev[2 * j + 1].record()
+
+    layer_out = torch.empty_like(x)
+
+    def layer_step():
+        moe.moe_layer_forward(c, w, x, layer_out, st, ws)
+
+    # 1) the metric: K timed calls of moe_layer_forward, the whole layer
+    for _ in range(args.warmup):
+        layer_step()
     torch.cuda.synchronize()
-    log(f"bench: {args.warmup} warmup steps done, timing {args.steps}")
+    log(f"bench: {args.warmup} warmup layer calls done, timing {args.steps}")
+    le0, le1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[args.warmup + i])
+    le0.record()
+    for _ in range(args.steps):
+        layer_step()
+    le1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    layer_event_ms = le0.elapsed_time(le1) / args.steps
 
-    stage_ms = {s: 0.0 for s in stages}
-    for i in range(args.steps):
-        ev = events[args.warmup + i]
-        for j, s in enumerate(stages):
-            stage_ms[s] += ev[j].elapsed_time(ev[j + 1]) / args.steps
+    # 1b) optional: the same call captured once in a HIP graph and replayed
+    graph_ms = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            layer_step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            layer_step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        ge0, ge1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ge0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        ge1.record()
+        torch.cuda.synchronize()
+        graph_ms = ge0.elapsed_time(ge1) / args.steps
+
+    # 2) stage breakdown: the same work as separate ABI calls, events between
+    def timed_stages(n, flush):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(stages))] for _ in range(n)]
+        for i in range(n):
+            staged_step(evs[i], flush)
+        torch.cuda.synchronize()
+        ms = {s: 0.0 for s in stages}
+        for ev in evs:
+            for j, s_ in enumerate(stages):
+                ms[s_] += ev[2 * j].elapsed_time(ev[2 * j + 1]) / n
+        return ms
+
+    for _ in range(min(args.warmup, 5)):
+        staged_step([torch.cuda.Event(enable_timing=True) for _ in range(2 * len(stages))], False)
+    stage_ms = timed_stages(args.steps, False)
+    stage_ms_flushed = timed_stages(min(args.steps, 10), True) if flush_buf is not None else None
+    log("bench: stage passes done")
+    copy_gbs = peaks.copy_gbs(mib=1024, reps=3, blocks_per_cu=8, unroll=8, nt=True) if not args.no_peaks else None
 
     kept = int(st["kept"].sum().item())
     es = 2 if cfg.act_dtype == "bf16" else 4
@@ -273,6 +377,18 @@ def main():
     gemm_ms = stage_ms["expert_up"] + stage_ms["expert_down"]
     disp_bytes = T * d * es + kept * d * es                            # read x once, write k copies
     comb_bytes = kept * d * es + T * d * es + (T * d * es if cfg.residual else 0) + (T * d * es if shared is not None else 0)
+    # route: the algorithmic bytes (x read once, router matrices, indices and
+    # gates written) and the fp32 dot-product flops of the router product
+    router_cols = E * (2 if cfg.gate == "noisy_topk" else 1) + (cfg.n_groups if cfg.gate == "hierarchical" else 0)
+    route_bytes = (T * d * es + router_cols * d * 4 + T * k * 8) if cfg.gate != "hash" else T * k * 8 + T * 4
+    route_flops = 2.0 * T * router_cols * d if cfg.gate != "hash" else 0.0
+
+    def hbm_pct(nbytes, ms):
+        return 100.0 * nbytes / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9)
+
+    def copy_pct(nbytes, ms):
+        return None if not copy_gbs else 100.0 * nbytes / (ms * 1e-3) / (copy_gbs * 1e9)
+
     value = T * args.steps / wall
     res = {
         "metric": METRIC,
@@ -289,10 +405,20 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
         "config": {"workload": workload_desc(cfg), "T": T, "d_model": d, "d_ff": F, "n_experts": E, "top_k": c.top_k,
                    "parallelism": "single GPU, all experts resident"},
+        "timed_call": "moe_layer_forward",
+        "layer_event_ms": layer_event_ms,
         "grouped_gemm_pct_mfma_peak": 100.0 * (flops_up + flops_down) / (gemm_ms * 1e-3) / (peak_f * 1e12),
-        "dispatch_pct_hbm_peak": 100.0 * disp_bytes / (stage_ms["dispatch"] * 1e-3) / (PEAK_HBM_GBS * 1e9),
-        "combine_pct_hbm_peak": 100.0 * comb_bytes / (stage_ms["combine"] * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "dispatch_pct_hbm_peak": hbm_pct(disp_bytes, stage_ms["dispatch"]),
+        "combine_pct_hbm_peak": hbm_pct(comb_bytes, stage_ms["combine"]),
+        "route_gbs": route_bytes / (stage_ms["route"] * 1e-3) / 1e9,
+        "route_pct_hbm_peak": hbm_pct(route_bytes, stage_ms["route"]),
+        "route_valu_tflops": route_flops / (stage_ms["route"] * 1e-3) / 1e12,
+        "route_pct_fp32_peak": 100.0 * route_flops / (stage_ms["route"] * 1e-3) / (PEAK_MFMA_TFLOPS["f32"] * 1e12),
+        "stage_bytes": {"route": route_bytes, "dispatch": disp_bytes, "combine": comb_bytes},
         "stages_ms": stage_ms,
+        "measured_copy_gbs": copy_gbs,
+        "dispatch_pct_measured_copy": copy_pct(disp_bytes, stage_ms["dispatch"]),
+        "combine_pct_measured_copy": copy_pct(comb_bytes, stage_ms["combine"]),
         "expert_up_roofline": r_up,
         "expert_down_roofline": r_down,
         "roofline": roofline,
@@ -300,6 +426,17 @@ def main():
         "gemm_source_sha256": kernel_source_hash(),
         "experts_with_rows": active,
     }
+    if graph_ms is not None:
+        res["graph_ms_per_step"] = graph_ms
+        res["graph_tokens_per_s"] = T / (graph_ms * 1e-3)
+    if stage_ms_flushed is not None:
+        res["stages_ms_cache_flushed"] = stage_ms_flushed
+        res["flush_mib"] = args.flush_mib
+        res["dispatch_pct_hbm_peak_flushed"] = hbm_pct(disp_bytes, stage_ms_flushed["dispatch"])
+        res["combine_pct_hbm_peak_flushed"] = hbm_pct(comb_bytes, stage_ms_flushed["combine"])
+        res["route_pct_hbm_peak_flushed"] = hbm_pct(route_bytes, stage_ms_flushed["route"])
+        res["dispatch_pct_measured_copy_flushed"] = copy_pct(disp_bytes, stage_ms_flushed["dispatch"])
+        res["combine_pct_measured_copy_flushed"] = copy_pct(comb_bytes, stage_ms_flushed["combine"])
     if shared is not None:
         res["shared_expert_roofline"] = roof("shared_expert", flops_sh, sh_bytes)
     if not args.no_cpu_baseline:

@@ -86,6 +86,7 @@ struct GemmParams {
     int64_t ldc2;
     int rem;                // 1: an expert's last <= kRemThr rows go to kRemBM-row tiles
     int64_t unit_f4;        // float4s of partial accumulators per split unit (main tile)
+    int main_blocks;        // blocks [0, main_blocks) take whole tiles, the rest split units
 };
 
 // Work decomposition.  The plan lists ceil(M_e / BM) row tiles per expert,
@@ -331,7 +332,8 @@ struct GemmEpilogue {
 
 // One tile of the grouped GEMM (rows [t.row0, t.row0 + t.rows) of expert
 // t.e, column tile t.nt, K slices [k0, k1)); `lds` is the kernel's LDS.
-template <bool BF16, int BM, int BN, int EPI, bool SPLIT, int WGN>
+// unit >= 0: a split unit, which stores its fp32 partial accumulators.
+template <bool BF16, int BM, int BN, int EPI, int WGN>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, lds_u8* lds, const TileDesc& t, int k0, int k1,
                                           int unit) {
     constexpr int NW = 2 * WGN;               // waves: 2 along M, WGN along N
@@ -596,7 +598,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, lds_u8* lds, cons
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();   // reloads of the last slice may still be landing
 
-    if constexpr (SPLIT) Epi::store_partial(p, acc, unit, wave, lane);
+    if (unit >= 0) Epi::store_partial(p, acc, unit, wave, lane);
     else Epi::store(p, acc, row0, rows, nt, wm, wn, lane);
 }
 
@@ -612,14 +614,15 @@ constexpr int gemm_lds_bytes() {
     return main_bytes;
 }
 
-// The grouped GEMM kernel: finds its work unit and runs its tile.  Whole
-// tiles (SPLIT = false): block ids are dealt round-robin to the 8 XCDs, so
-// tiles are remapped to give each XCD a contiguous range (its blocks share
-// weight and activation panels in its L2).  Split units (SPLIT = true, a
-// launch of its own): block u is unit u, range u % split of tail tile
-// u / split.  Remainder tiles (256-row bf16 launches) run with 64-row tiles
-// (launches of 4 waves only).
-template <bool BF16, int BM, int BN, int EPI, bool SPLIT, int WGN>
+// The grouped GEMM kernel: finds its work unit and runs its tile.  Blocks
+// [0, p.main_blocks) take whole tiles: block ids are dealt round-robin to the
+// 8 XCDs, so tiles are remapped to give each XCD a contiguous range (its
+// blocks share weight and activation panels in its L2).  Later blocks are the
+// split-K units of the tail: block p.main_blocks + u is unit u, range
+// u % split of tail tile u / split; being dispatched last, they fill the CUs
+// that the last round of whole tiles leaves idle.  Remainder tiles
+// (256-row bf16 launches of 4 waves) run with 64-row tiles.
+template <bool BF16, int BM, int BN, int EPI, int WGN>
 __global__ __launch_bounds__(128 * WGN) void k_grouped_gemm(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     __shared__ __align__(16) uint8_t lds_mem[gemm_lds_bytes<BF16, BM, BN, WGN>()];
@@ -627,7 +630,7 @@ __global__ __launch_bounds__(128 * WGN) void k_grouped_gemm(GemmParams p) {
     const int total = (p.plan[p.E] + p.plan[2 * p.E + 4]) * p.NT;
     const int full = p.plan[p.E + 1], split = p.plan[p.E + 2], tail = p.plan[p.E + 3];
     int L, k0 = 0, k1 = p.nk, unit = -1;
-    if constexpr (!SPLIT) {
+    if ((int)blockIdx.x < p.main_blocks) {
         const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
         const int per_xcd = split > 1 ? full / 8 : (total + 7) / 8;
         if (slot >= per_xcd) return;
@@ -635,7 +638,7 @@ __global__ __launch_bounds__(128 * WGN) void k_grouped_gemm(GemmParams p) {
         if (L >= total) return;
     } else {
         if (split <= 1) return;
-        unit = blockIdx.x;
+        unit = blockIdx.x - p.main_blocks;
         if (unit >= tail * split) return;
         L = full + unit / split;
         const int c = unit % split;
@@ -645,17 +648,14 @@ __global__ __launch_bounds__(128 * WGN) void k_grouped_gemm(GemmParams p) {
     const TileDesc t = decode_tile(p, L, BM);
     if constexpr (BF16 && BM == 256 && WGN == 2) {
         if (t.rem) {
-            gemm_tile<BF16, kRemBM, BN, EPI, SPLIT, 2>(p, lds, t, k0, k1, unit);
+            gemm_tile<BF16, kRemBM, BN, EPI, 2>(p, lds, t, k0, k1, unit);
             return;
         }
     }
-    gemm_tile<BF16, BM, BN, EPI, SPLIT, WGN>(p, lds, t, k0, k1, unit);
+    gemm_tile<BF16, BM, BN, EPI, WGN>(p, lds, t, k0, k1, unit);
 #endif
 }
 
-// Split-K fixup: block (t, w, g) adds, in range order, the `split` partial
-// accumulators of column group g of wave w of tail tile t, and applies the
-// epilogue to them.
 template <bool BF16, int BM, int BN, int EPI, int WGM, int WGN>
 __device__ __forceinline__ void fixup_tile(const GemmParams& p, const TileDesc& t, int w, int i0, int split) {
     typedef GemmEpilogue<BF16, BM, BN, EPI, WGM, WGN> Epi;
@@ -829,13 +829,17 @@ GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N) {
 template <bool BF16, int BM, int BN>
 constexpr int waves_n() { return (BF16 && BM == 256 && BN == 256) ? MOE_GEMM_WGN256 : 2; }
 
+// Whole tiles and split units in one launch, then the fixup when the plan
+// may have a split.
 template <bool BF16, int BM, int BN, int EPI>
-static void launch_pair(const GemmParams& p, int grid, bool may_split, hipStream_t s) {
+static void launch_pair(const GemmParams& p0, int grid, bool may_split, hipStream_t s) {
     constexpr int WGN = waves_n<BF16, BM, BN>();
     typedef GemmEpilogue<BF16, BM, BN, EPI, 2, WGN> Epi;
-    hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, false, WGN>), dim3(grid), dim3(128 * WGN), 0, s, p);
+    GemmParams p = p0;
+    p.main_blocks = grid;
+    hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, WGN>), dim3(grid + (may_split ? kSplitUnits : 0)),
+                       dim3(128 * WGN), 0, s, p);
     if (!may_split) return;
-    hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, true, WGN>), dim3(kSplitUnits), dim3(128 * WGN), 0, s, p);
     constexpr int groups = Epi::FN / Epi::IG;
     hipLaunchKernelGGL((k_split_fixup<BF16, BM, BN, EPI, 2, WGN>), dim3(kSplitUnits / 2 * Epi::NW * groups), dim3(64),
                        0, s, p);
@@ -927,7 +931,7 @@ hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, c
     const int64_t per_expert = rem ? (kRemThr + kRemBM - 1) / kRemBM : 1;
     const int64_t m_tiles_ub = (max_rows + BM - 1) / BM + (p.E > 1 ? p.E * per_expert : per_expert);
     const int64_t grid = (m_tiles_ub * p.NT + 7) / 8 * 8;
-    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    if (grid > 0x7fffffff - kSplitUnits) return hipErrorInvalidValue;
     // With offsets == NULL the host knows the row count and launches the
     // split-K parts only when the plan has a tail; routed counts live on the
     // device.

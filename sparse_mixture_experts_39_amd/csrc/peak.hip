@@ -5,8 +5,9 @@
 //     grouped GEMMs could use (16x16x32 and 32x32x16);
 //   * device-memory copy rate: 16-byte loads and stores over buffers far
 //     larger than the 256 MB last-level cache;
-//   * a cache flush: a pass of plain stores over a large buffer, so that a
-//     timed stage does not find its inputs in the last-level cache.
+//   * a cache flush: a read pass over a buffer larger than the 256 MB
+//     last-level cache, so that a timed stage finds neither its inputs nor
+//     dirty lines of the previous stage in it.
 // These entry points are a measurement aid and not part of the layer's ABI
 // (include/moe.h); they are built into their own library.
 #include <hip/hip_runtime.h>
@@ -112,11 +113,20 @@ __global__ __launch_bounds__(256) void k_peak_copy(const moe::u32x4_t* __restric
     for (; i < n16; i += stride) dst[i] = src[i];
 }
 
-// buf[i] = value for n16 16-byte chunks (plain stores).
-__global__ __launch_bounds__(256) void k_fill16(uint4* __restrict__ buf, int64_t n16, uint32_t value) {
+// A read pass over n16 16-byte chunks of buf: the lines it brings in evict
+// whatever the caches held (a dirty line of an earlier kernel is written back
+// here, not during the next timed kernel).  The chunks are folded into one
+// word per thread that is stored only if it equals `never`, which keeps the
+// loads from being optimised away.
+__global__ __launch_bounds__(256) void k_touch16(const moe::u32x4_t* __restrict__ buf, int64_t n16, uint32_t never,
+                                                 uint32_t* __restrict__ sink) {
     const int64_t stride = (int64_t)gridDim.x * 256;
-    const uint4 v = make_uint4(value, value ^ 1u, value ^ 2u, value ^ 3u);
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) buf[i] = v;
+    uint32_t acc = 0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) {
+        const moe::u32x4_t v = buf[i];
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    if (acc == never) sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
 }  // namespace
@@ -157,10 +167,14 @@ int moe_peak_copy(const void* src, void* dst, int64_t bytes, int blocks, int unr
     return (int)hipGetLastError();
 }
 
-// Cache flush: plain stores of `bytes` (a multiple of 16) into buf.
-int moe_cache_flush(void* buf, int64_t bytes, uint32_t value, void* stream) {
-    if (!buf || bytes <= 0 || (bytes & 15)) return -1;
-    hipLaunchKernelGGL(k_fill16, dim3(4096), dim3(256), 0, (hipStream_t)stream, (uint4*)buf, bytes / 16, value);
+// Cache flush: a read pass over `bytes` (a multiple of 16) of buf, a device
+// buffer larger than the last-level cache; sink: 4096 * 256 uint32 of device
+// memory that is written only in the (practically impossible) case that a
+// thread's fold of its chunks equals `never`.
+int moe_cache_flush(const void* buf, int64_t bytes, uint32_t never, uint32_t* sink, void* stream) {
+    if (!buf || !sink || bytes <= 0 || (bytes & 15)) return -1;
+    hipLaunchKernelGGL(k_touch16, dim3(4096), dim3(256), 0, (hipStream_t)stream, (const moe::u32x4_t*)buf, bytes / 16,
+                       never, sink);
     return (int)hipGetLastError();
 }
 

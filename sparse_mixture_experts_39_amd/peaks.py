@@ -2,7 +2,7 @@
 
 Binding of libmoe_peak.so (csrc/peak.hip), a measurement aid that is not part
 of the layer's ABI: a register-only bf16 MFMA rate probe for the two MFMA
-shapes, a device copy probe, and a cache flush (plain stores over a buffer
+shapes, a device copy probe, and a cache flush (a read pass over a buffer
 larger than the 256 MB last-level cache) for stage timings that must not find
 their inputs in the cache.
 """
@@ -31,7 +31,7 @@ def lib():
         L.moe_peak_copy.restype = ctypes.c_int
         L.moe_peak_copy.argtypes = [P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P]
         L.moe_cache_flush.restype = ctypes.c_int
-        L.moe_cache_flush.argtypes = [P, ctypes.c_int64, ctypes.c_uint32, P]
+        L.moe_cache_flush.argtypes = [P, ctypes.c_int64, ctypes.c_uint32, P, P]
         _lib = L
     return _lib
 
@@ -108,10 +108,20 @@ def best_copy_gbs() -> Dict[str, float]:
     return res
 
 
-def flush(buf: torch.Tensor, value: int = 0):
-    """Plain stores over the whole (contiguous, device) buffer."""
+_sink = None
+
+
+def flush(buf: torch.Tensor, salt: int = 0):
+    """A read pass over the whole (contiguous, device) buffer, which should be
+    larger than the last-level cache (256 MB): afterwards the caches hold
+    clean lines of `buf` only."""
+    global _sink
+    if _sink is None or _sink.device != buf.device:
+        _sink = torch.empty(4096 * 256, dtype=torch.int32, device=buf.device)
     nbytes = buf.numel() * buf.element_size() // 16 * 16
-    rc = lib().moe_cache_flush(ctypes.c_void_p(buf.data_ptr()), nbytes, value & 0xFFFFFFFF, _stream())
+    never = (0x9E3779B9 * (salt + 1)) & 0xFFFFFFFF
+    rc = lib().moe_cache_flush(ctypes.c_void_p(buf.data_ptr()), nbytes, never, ctypes.c_void_p(_sink.data_ptr()),
+                               _stream())
     if rc != 0:
         raise RuntimeError(f"moe_cache_flush failed ({rc})")
 
