@@ -1173,7 +1173,8 @@ static int pow2_at_least(int v) { int p = 1; while (p < v) p <<= 1; return p; }
 template <bool BF16>
 static void launch_dots_t(const void* x, const float* w0, const float* w1, int T, int d, int E, int NC, float* dots,
                           int32_t* zero_word, hipStream_t s) {
-    if (NC >= 64) {
+    if (NC > 32) {
+        // (also 33 .. 63 columns: the few-column kernels below stop at 32)
         // 16 x TT tokens x 64 columns per block of 256 threads; TT is the
         // largest of 4, 2, 1 that still gives at least 512 blocks (two per CU),
         // so that a CU has a second block to run while one waits on memory

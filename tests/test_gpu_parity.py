@@ -30,6 +30,9 @@ MID = {
                              gate="sigmoid_bias", n_shared=1, F_shared=192, sel_bias=True, seed=13),
     "noisy_small": Config("noisy_small", T=500, d=64, F=128, E=40, k=4, act_dtype="bf16", act="relu",
                           gate="noisy_topk", seed=14),
+    # noisy gate with 2 E = 40 router columns (33 .. 63 columns)
+    "noisy_40_cols": Config("noisy_40_cols", T=300, d=128, F=64, E=20, k=3, act_dtype="f32", act="relu",
+                            gate="noisy_topk", seed=41),
     "f32_swiglu_mid": Config("f32_swiglu_mid", T=600, d=320, F=448, E=12, k=2, act_dtype="f32", act="swiglu",
                              gate="softmax_topk", seed=15),
     "many_experts": Config("many_experts", T=2000, d=64, F=64, E=1024, k=16, act_dtype="bf16", act="relu",
@@ -233,7 +236,9 @@ def test_empty_batch():
 # kernel.  The scores must be bit-identical.
 ROUTER_SHAPES = [(2, "bf16", 384), (3, "f32", 1152), (4, "bf16", 1152), (5, "f32", 384), (8, "bf16", 1152),
                  (8, "f32", 384), (12, "bf16", 384), (16, "bf16", 1152), (16, "f32", 1152), (32, "bf16", 384),
-                 (8, "bf16", 320), (64, "bf16", 384), (96, "f32", 384)]
+                 (8, "bf16", 320), (64, "bf16", 384), (96, "f32", 384),
+                 # 33 .. 63 columns (a gap of the few-column kernels, found by the random-shape sweep)
+                 (33, "f32", 128), (40, "bf16", 1152), (63, "bf16", 320)]
 
 
 @pytest.mark.parametrize("E,dt,d", ROUTER_SHAPES)
