@@ -283,6 +283,23 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* top
                         int32_t* slot_pos, const moe_stats* stats,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* moe_dispatch for callers that cannot allocate device memory (code under
+ * HIP-graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and the same outputs as moe_dispatch, but the per-block
+ * histograms and rank bases live in a static device array of the library
+ * (4 MiB per GPU, held until the process ends) instead of a caller
+ * workspace, and nothing is allocated.  Needs twice ceil(T slots / 256) * E * 4
+ * bytes (each rounded up to 256) of that array, i.e. ceil(T slots / 256) * E
+ * up to about 524288;
+ * a larger call returns MOE_ERR_UNSUPPORTED before anything is enqueued.  The
+ * aux statistic reads stats->P (NULL: aux is not written).  Every call on a
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (several
+ * streams or threads) race and must be serialised by the caller.  A failure
+ * to resolve the array's device address returns MOE_ERR_HIP. */
+moe_status moe_dispatch_noalloc(const moe_config* cfg, const void* x, const int32_t* topk_idx, void* x_perm,
+                                int32_t* expert_offsets, int32_t* perm_src, int32_t* slot_pos,
+                                const moe_stats* stats, void* stream);
+
 /* Expert FFNs (Lecture29, "Top-two routing": run each selected expert on
  * the tokens dispatched to it; "Dense baseline": the SwiGLU MLP; Shazeer
  * notes 2.2: the one-hidden-layer ReLU expert; CS336 lecture 4 notes,

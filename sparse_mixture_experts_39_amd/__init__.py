@@ -19,7 +19,7 @@ __all__ = [
     "workspace", "max_rows", "capacity", "validate_config", "workspace_size",
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_shared_expert",
     "moe_combine", "moe_layer_forward", "MoeSaved", "MoeGrads", "backward_workspace_size", "backward_workspace",
-    "moe_layer_backward", "moe_expert_up_train",
+    "moe_layer_backward", "moe_expert_up_train", "moe_dispatch_noalloc",
     "EXPORTED_SYMBOLS", "LIB_PATH",
 ]
 
@@ -37,7 +37,7 @@ EXPORTED_SYMBOLS = (
     "moe_last_hip_error",
     "moe_status_string", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
     "moe_shared_expert", "moe_combine", "moe_layer_forward", "moe_update_bias",
-    "moe_backward_workspace_size", "moe_layer_backward", "moe_expert_up_train",
+    "moe_backward_workspace_size", "moe_layer_backward", "moe_expert_up_train", "moe_dispatch_noalloc",
 )
 
 
@@ -115,6 +115,8 @@ def lib():
         L.moe_route.argtypes = [C, P, W, P, P, P, S, P, sz, P]
         L.moe_dispatch.restype = ctypes.c_int
         L.moe_dispatch.argtypes = [C, P, P, P, P, P, P, S, P, sz, P]
+        L.moe_dispatch_noalloc.restype = ctypes.c_int
+        L.moe_dispatch_noalloc.argtypes = [C, P, P, P, P, P, P, S, P]
         L.moe_expert_ffn.restype = ctypes.c_int
         L.moe_expert_ffn.argtypes = [C, P, P, W, P, P, sz, P]
         L.moe_expert_up.restype = ctypes.c_int
@@ -297,6 +299,22 @@ def moe_dispatch(c: MoeConfig, x, topk_idx, x_perm, expert_offsets, perm_src, sl
                             _ptr(slot_pos, torch.int32, (T, k), "slot_pos"), _sref(st),
                             _ptr(ws, torch.uint8, name="ws"), ws.numel() if ws is not None else 0, _stream(stream))
     _check("moe_dispatch", rc)
+
+
+def moe_dispatch_noalloc(c: MoeConfig, x, topk_idx, x_perm, expert_offsets, perm_src, slot_pos, stats=None,
+                         stream=None):
+    """moe_dispatch with the library's static device scratch instead of a
+    workspace (nothing is allocated; calls on one GPU must not overlap)."""
+    T, E, k, d = c.T, c.n_experts, route_slots(c), c.d_model
+    R = max_rows(c)
+    st = _stats_struct(stats)
+    rc = lib().moe_dispatch_noalloc(ctypes.byref(c), _ptr(x, _dt(c), (T, d), "x"),
+                                    _ptr(topk_idx, torch.int32, (T, k), "topk_idx"),
+                                    _ptr(x_perm, _dt(c), (R, d), "x_perm"),
+                                    _ptr(expert_offsets, torch.int32, (E + 1,), "expert_offsets"),
+                                    _ptr(perm_src, torch.int32, (R,), "perm_src"),
+                                    _ptr(slot_pos, torch.int32, (T, k), "slot_pos"), _sref(st), _stream(stream))
+    _check("moe_dispatch_noalloc", rc)
 
 
 def moe_expert_ffn(c: MoeConfig, x_perm, expert_offsets, w: MoeWeights, y_perm, ws=None, stream=None):

@@ -29,6 +29,7 @@
 //                 for one block's registers (and k_scatter alone for the
 //                 capacity reroute)
 #include <algorithm>
+#include <mutex>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -326,6 +327,32 @@ __global__ __launch_bounds__(256) void k_scatter_permute(const int32_t* __restri
             if (r >= 0) x_perm[(int64_t)r * cpr + c] = v[i];
         }
     }
+}
+
+// Scratch of moe_dispatch_noalloc (callers that cannot allocate): the
+// per-block histograms and rank bases of one call.  Every GPU the library
+// runs on holds its own copy until the process ends; the host side keeps each
+// device's address, resolved once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[kDispatchScratchBytes];
+
+hipError_t dispatch_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 void launch_histogram(const int32_t* topk_idx, int64_t n_assign, int E, int32_t* hist, hipStream_t s) {

@@ -53,6 +53,10 @@ void launch_scan(const int32_t* hist, int nblocks, int E, int64_t capacity,
                  int32_t* blockbase, int32_t* offsets, const float* P, const moe_stats* st, hipStream_t s);
 void launch_scatter(const int32_t* topk_idx, int64_t n_assign, int E, const int32_t* blockbase,
                     const int32_t* offsets, int64_t capacity, int32_t* perm_src, int32_t* slot_pos, hipStream_t s);
+// Static device scratch of moe_dispatch_noalloc: its size, and its device
+// address on the current device (never the symbol itself in host code).
+constexpr size_t kDispatchScratchBytes = (size_t)4 << 20;
+hipError_t dispatch_scratch(void** ptr);
 // Scatter (slot_pos / perm_src, as launch_scatter) and the row copy x[t] ->
 // x_perm[slot_pos[t][j]] for every kept slot, in one launch (two when a row
 // has more than 1024 16-byte chunks or a token more than 64 slots);

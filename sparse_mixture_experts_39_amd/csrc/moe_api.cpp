@@ -459,6 +459,32 @@ moe_status moe_dispatch(const moe_config* c, const void* x, const int32_t* topk_
     return after_launch();
 }
 
+moe_status moe_dispatch_noalloc(const moe_config* c, const void* x, const int32_t* topk_idx, void* x_perm,
+                                int32_t* expert_offsets, int32_t* perm_src, int32_t* slot_pos, const moe_stats* st,
+                                void* stream) {
+    moe_status s = moe_validate_config(c);
+    if (s != MOE_OK) return s;
+    if (!expert_offsets) return MOE_ERR_INVALID_ARG;
+    if (c->T > 0 && (!x || !topk_idx || !x_perm || !perm_src || !slot_pos)) return MOE_ERR_INVALID_ARG;
+    const int E = c->n_experts;
+    const int64_t na = n_assign(c);
+    const int nb = (int)((na + moe::kAssignBlock - 1) / moe::kAssignBlock);
+    const size_t hist_bytes = align_up((size_t)nb * E * sizeof(int32_t));
+    if (2 * hist_bytes > moe::kDispatchScratchBytes) return MOE_ERR_UNSUPPORTED;
+    void* base = nullptr;
+    if ((s = hip_status(moe::dispatch_scratch(&base))) != MOE_OK) return s;
+    hipStream_t h = (hipStream_t)stream;
+    int32_t* hist = (int32_t*)base;
+    int32_t* bbase = (int32_t*)((char*)base + hist_bytes);
+    const int64_t cap = capacity_of(c);
+    const float* P = (st && st->P) ? st->P : nullptr;   // aux needs the caller's P
+    moe::launch_histogram(topk_idx, na, E, hist, h);
+    moe::launch_scan(hist, nb, E, cap, bbase, expert_offsets, P, st, h);
+    moe::launch_scatter_permute(topk_idx, c->T, slots_of(c), E, bbase, expert_offsets, cap, x, c->d_model,
+                                elem_bytes(c), perm_src, slot_pos, x_perm, h);
+    return after_launch();
+}
+
 // One grouped GEMM of an expert stack (tile plan, GEMM and split-K fixup, all
 // on the device).  up = true: a -> H (ReLU / SwiGLU epilogue); up = false:
 // H -> y.  With offsets == NULL the call covers one group of `rows` rows (the
