@@ -257,13 +257,13 @@ __global__ __launch_bounds__(64) void k_router_dots_ring(const void* __restrict_
 #pragma unroll
       for (int j = 0; j < S; ++j) {
         const int c = c0 + j;
-        if (c >= nch) break;
         // the slot of chunk c - 1 is rewritten below: its reads are done
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         issue((j + S - 1) % S, c + S - 1);
         dots_wait_vmcnt<(S - 1) * NI>();     // chunk c has landed
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+        if (c >= nch) continue;              // past the end: loads only (uniform), no exit from the body
         const uint8_t* xrow = slot(j) + tg * XROW;
         const uint8_t* wrow = slot(j) + XB + cg * WROW;
         // 16-byte chunk q of this lane's x and w rows
