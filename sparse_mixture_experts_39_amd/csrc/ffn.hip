@@ -87,6 +87,10 @@ struct GemmParams {
     int rem;                // 1: an expert's last <= kRemThr rows go to kRemBM-row tiles
     int64_t unit_f4;        // float4s of partial accumulators per split unit (main tile)
     int main_blocks;        // blocks [0, main_blocks) take whole tiles, the rest split units
+    // k-major B ([K][N] per expert, KM_B launches): row stride of B and the
+    // k rows that come from B0 (the rest from B1, row k - K1)
+    int64_t ldb;
+    int K1;
 };
 
 // Work decomposition.  The plan lists ceil(M_e / BM) row tiles per expert,
@@ -176,6 +180,39 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 // then cover every (row parity, physical chunk) pair, i.e. 16 distinct
 // 16-byte bank groups.  Depends on r mod 16 only.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+// Operand layouts of gemm_tile: both k-contiguous (the forward products), or
+// B k-major (B_e stored [K][N]: the backward's products through a weight as
+// stored, dh = dy W2 and dx = [da | du] [W1; W3]).
+enum { KM_NONE = 0, KM_B = 1 };
+
+// A k-major B slice is 64 k rows of the tile's BN columns (2 BN bytes per
+// row, the same 32 KB as 256 rows of 128 bytes at BN = 256).  Fragments come
+// from ds_read_b64_tr_b16: within 16 lanes, lane L reads 8 bytes (4 columns)
+// of k row L / 4 and receives column L of 4 k rows, so two reads give a lane
+// the 8 consecutive k of one column that an MFMA operand holds.  The 16-byte
+// chunks of a row are XOR swizzled by swzk(k row) in bits 1..3: the 8 k rows
+// that 32 lanes read in one pass (4 rows of each of two lane groups) then
+// fall in 8 distinct 32-byte bank groups.  Needs BN >= 128 (16 chunks per
+// row).
+__device__ __forceinline__ int swzk(int kr) { return ((kr & 3) | (((kr >> 3) & 1) << 2)) << 1; }
+
+// Direct-to-LDS 16-byte buffer load issued as an instruction the compiler does
+// not model.  Launches that read LDS with ds_read_b64_tr_b16 use it for every
+// slice load: for a load it issues itself the compiler cannot tell which LDS
+// bytes it writes and waits for all of them before every transposing read,
+// which would drain the ring.  Ordering comes from the explicit vmcnt waits
+// and barriers of the pipeline; the instruction writes no register.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, const lds_u8* dst) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)dst;
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(m0), "s"(soff)
+                 : "memory");
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
 
 // Ring depths of the A and B slices.  Batch j (issued after the barrier of
 // slice j) loads A slice j + NA and B slice j + NB, in that order; before that
@@ -333,7 +370,8 @@ struct GemmEpilogue {
 // One tile of the grouped GEMM (rows [t.row0, t.row0 + t.rows) of expert
 // t.e, column tile t.nt, K slices [k0, k1)); `lds` is the kernel's LDS.
 // unit >= 0: a split unit, which stores its fp32 partial accumulators.
-template <bool BF16, int BM, int BN, int EPI, int WGN>
+// KM: operand layout (KM_NONE or KM_B; see swzk).
+template <bool BF16, int BM, int BN, int EPI, int WGN, int KM = KM_NONE>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, lds_u8* lds, const TileDesc& t, int k0, int k1,
                                           int unit) {
     constexpr int NW = 2 * WGN;               // waves: 2 along M, WGN along N
@@ -355,6 +393,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, lds_u8* lds, cons
     static_assert(RD.wait0 < 64 && RD.bytes <= 160 * 1024, "ring exceeds vmcnt or LDS");
     typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
     const int e = t.e, nt = t.nt, row0 = t.row0, rows = t.rows;
+    constexpr bool BKM = KM == KM_B;
+    static_assert(KM == KM_NONE || (BF16 && EPI == EPI_STORE && MB == 16 && BN >= 128),
+                  "k-major B: bf16, plain store, 16x16 blocks, k rows of at least 256 bytes");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
@@ -369,31 +410,48 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, lds_u8* lds, cons
     // (SGPRs) holding the tile's base and extent, a 32-bit lane offset, and
     // the K offset in an SGPR.
     constexpr int kRsrcWord3 = 0x00020000;
-    const int64_t brow_base = epi_swiglu(EPI) ? (int64_t)nt * (BN / 2) : (int64_t)nt * BN;
-    const int b_rows = epi_swiglu(EPI) ? BN / 2 : BN;
-    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint8_t*)p.A + (int64_t)row0 * p.lda * ES), (short)0,
-        (int)(((int64_t)(rows - 1) * p.lda + p.K) * ES), kRsrcWord3);
-    const int64_t boff = ((int64_t)e * p.bstride + brow_base * p.K) * ES;
-    const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint8_t*)p.B0 + boff), (short)0, (int)((int64_t)b_rows * p.K * ES), kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint8_t*)(epi_swiglu(EPI) ? p.B1 : p.B0) + boff), (short)0,
-        (int)((int64_t)b_rows * p.K * ES), kRsrcWord3);
+    __amdgpu_buffer_rsrc_t rsA, rsB0, rsB1;
     uint32_t voffA[ga], voffB[gb];
+    rsA = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.A + (int64_t)row0 * p.lda * ES), (short)0,
+                                            (int)(((int64_t)(rows - 1) * p.lda + p.K) * ES), kRsrcWord3);
 #pragma unroll
     for (int q = 0; q < ga; ++q) {
         const int r = 8 * (wave * ga + q) + (lane >> 3);
         voffA[q] = (uint32_t)(min(r, rows - 1) * (int)p.lda * ES + (((lane & 7) ^ swz(r)) << 4));
     }
+    if constexpr (BKM) {
+        // B_e stored [K][N]: k rows below K1 from B0, the rest from B1.  A
+        // 1 KB load group is 512 / BN k rows of the tile's BN columns: lane l
+        // takes k row g (512 / BN) + l / (BN / 8), physical chunk l % (BN / 8),
+        // and fetches logical chunk (l % (BN / 8)) ^ swzk(k row)
+        const int64_t boff = (int64_t)e * p.bstride * ES;
+        rsB0 = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.B0 + boff), (short)0,
+                                                 (int)((int64_t)p.K1 * p.ldb * ES), kRsrcWord3);
+        rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)(p.B1 ? p.B1 : p.B0) + boff), (short)0,
+                                                 (int)((int64_t)(p.K - p.K1) * p.ldb * ES), kRsrcWord3);
 #pragma unroll
-    for (int q = 0; q < gb; ++q) {
-        const int g = wave * gb + q;
-        const int r = 8 * g + (lane >> 3);
-        // SwiGLU: MB-row block j of the tile is rows (j/2)*MB .. +MB-1 of W1
-        // (j even) or W3 (j odd); a group is 8 rows, so block j = g / (MB/8)
-        const int rr = epi_swiglu(EPI) ? ((g / (MB / 4)) * MB + (r & (MB - 1))) : r;
-        voffB[q] = (uint32_t)(rr * p.K * ES + (((lane & 7) ^ swz(r)) << 4));
+        for (int q = 0; q < gb; ++q) {
+            const int kr = (wave * gb + q) * (512 / BN) + lane / (BN / 8);
+            const int c = (lane % (BN / 8)) ^ swzk(kr);
+            voffB[q] = (uint32_t)(((int64_t)kr * p.ldb + nt * BN + 8 * c) * ES);
+        }
+    } else {
+        const int64_t brow_base = epi_swiglu(EPI) ? (int64_t)nt * (BN / 2) : (int64_t)nt * BN;
+        const int b_rows = epi_swiglu(EPI) ? BN / 2 : BN;
+        const int64_t boff = ((int64_t)e * p.bstride + brow_base * p.K) * ES;
+        rsB0 = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.B0 + boff), (short)0,
+                                                 (int)((int64_t)b_rows * p.K * ES), kRsrcWord3);
+        rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)(epi_swiglu(EPI) ? p.B1 : p.B0) + boff),
+                                                 (short)0, (int)((int64_t)b_rows * p.K * ES), kRsrcWord3);
+#pragma unroll
+        for (int q = 0; q < gb; ++q) {
+            const int g = wave * gb + q;
+            const int r = 8 * g + (lane >> 3);
+            // SwiGLU: MB-row block j of the tile is rows (j/2)*MB .. +MB-1 of W1
+            // (j even) or W3 (j odd); a group is 8 rows, so block j = g / (MB/8)
+            const int rr = epi_swiglu(EPI) ? ((g / (MB / 4)) * MB + (r & (MB - 1))) : r;
+            voffB[q] = (uint32_t)(rr * p.K * ES + (((lane & 7) ^ swz(r)) << 4));
+        }
     }
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
     const int nk = k1 - k0;
@@ -402,15 +460,26 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, lds_u8* lds, cons
     // count of every batch the same
     auto issueA1 = [&](int v, int q) {      // group q of this wave's part of A slice v
         lds_u8* dst = &lds[(v % NA) * SA + wave * ga * 1024];
-        const int koff = (k0 + min(v, nk - 1)) * 128;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)(dst + q * 1024), 16, voffA[q], koff, 0, 0);
+        const int kk = k0 + min(v, nk - 1);
+        if constexpr (KM == KM_NONE) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)(dst + q * 1024), 16, voffA[q], kk * 128, 0, 0);
+        } else {
+            dma16(rsA, voffA[q], (uint32_t)(kk * 128), dst + q * 1024);
+        }
     };
     auto issueB1 = [&](int v, int q) {
         lds_u8* dst = &lds[NA * SA + (v % NB) * SB + wave * gb * 1024];
-        const int koff = (k0 + min(v, nk - 1)) * 128;
-        const bool up = epi_swiglu(EPI) && (((wave * gb + q) / (MB / 8)) & 1);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? rsB1 : rsB0, (lds_ptr_t)(dst + q * 1024), 16, voffB[q], koff,
-                                                 0, 0);
+        const int kk = k0 + min(v, nk - 1);
+        if constexpr (KM == KM_NONE) {
+            const bool up = epi_swiglu(EPI) && (((wave * gb + q) / (MB / 8)) & 1);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? rsB1 : rsB0, (lds_ptr_t)(dst + q * 1024), 16, voffB[q],
+                                                     kk * 128, 0, 0);
+        } else {
+            const int kr = kk * 64;
+            const bool hi = kr >= p.K1;
+            dma16(hi ? rsB1 : rsB0, voffB[q], (uint32_t)((int64_t)(hi ? kr - p.K1 : kr) * p.ldb * ES),
+                  dst + q * 1024);
+        }
     };
     auto issueA = [&](int v) {
 #pragma unroll
@@ -451,10 +520,37 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, lds_u8* lds, cons
         }
     // fragment r of half slice h: k-step r / (FM + FN), then FM A blocks and
     // FN B blocks
+    // k-major B: lane base address of each MFMA block of the wave (k rows
+    // 8 (l/16) + (l%16)/4 of the slice, 4 columns at (l%4) * 4 of the block);
+    // half h adds 32 k rows, the second read of a fragment 4 more.  Within a
+    // slice the swizzle of these rows is the lane constant sw.
+    constexpr int RBB = BN * 2;
+    int kbb[BKM ? FN : 1];
+    if constexpr (BKM) {
+        const int g4 = lane >> 4, L = lane & 15;
+        const int sw = ((L >> 2) | ((g4 & 1) << 2)) << 1;
+        const int kr = 8 * g4 + (L >> 2);
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int col = wn * WN + i * 16 + 4 * (L & 3);
+            kbb[i] = NA * SA + kr * RBB + (((col >> 3) ^ sw) << 4) + ((col & 7) << 1);
+        }
+    }
+    auto trfrag = [&](int off, int rowbytes) {
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds + off));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds + off + 4 * rowbytes));
+        typedef short v8i16_t __attribute__((ext_vector_type(8)));
+        const v8i16_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(u32x4_t, both);
+    };
     auto read1 = [&](int ks, int h, u32x4_t* f, int r) {
         const int s2 = r / (FM + FN), q = r % (FM + FN);
-        if (q < FM) f[r] = *(lds_u32x4*)(&lds[(ks % NA) * SA] + fo[h][s2][0] + q * MB * 128);
-        else f[r] = *(lds_u32x4*)(&lds[(ks % NB) * SB] + fo[h][s2][1] + (q - FM) * MB * 128);
+        if (q < FM) {
+            f[r] = *(lds_u32x4*)(&lds[(ks % NA) * SA] + fo[h][s2][0] + q * MB * 128);
+        } else {
+            if constexpr (BKM) f[r] = trfrag((ks % NB) * SB + kbb[q - FM] + 32 * h * RBB, RBB);
+            else f[r] = *(lds_u32x4*)(&lds[(ks % NB) * SB] + fo[h][s2][1] + (q - FM) * MB * 128);
+        }
     };
     // one bf16 MFMA of the block shape: acc += W-fragment x activation-fragment
     auto mfma_bf16 = [](const u32x4_t& fw, const u32x4_t& fx, acc_t& a) {
@@ -622,7 +718,7 @@ constexpr int gemm_lds_bytes() {
 // u % split of tail tile u / split; being dispatched last, they fill the CUs
 // that the last round of whole tiles leaves idle.  Remainder tiles
 // (256-row bf16 launches of 4 waves) run with 64-row tiles.
-template <bool BF16, int BM, int BN, int EPI, int WGN>
+template <bool BF16, int BM, int BN, int EPI, int WGN, int KM = KM_NONE>
 __global__ __launch_bounds__(128 * WGN) void k_grouped_gemm(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     __shared__ __align__(16) uint8_t lds_mem[gemm_lds_bytes<BF16, BM, BN, WGN>()];
@@ -648,11 +744,11 @@ __global__ __launch_bounds__(128 * WGN) void k_grouped_gemm(GemmParams p) {
     const TileDesc t = decode_tile(p, L, BM);
     if constexpr (BF16 && BM == 256 && WGN == 2) {
         if (t.rem) {
-            gemm_tile<BF16, kRemBM, BN, EPI, 2>(p, lds, t, k0, k1, unit);
+            gemm_tile<BF16, kRemBM, BN, EPI, 2, KM>(p, lds, t, k0, k1, unit);
             return;
         }
     }
-    gemm_tile<BF16, BM, BN, EPI, WGN>(p, lds, t, k0, k1, unit);
+    gemm_tile<BF16, BM, BN, EPI, WGN, KM>(p, lds, t, k0, k1, unit);
 #endif
 }
 
@@ -831,13 +927,13 @@ constexpr int waves_n() { return (BF16 && BM == 256 && BN == 256) ? MOE_GEMM_WGN
 
 // Whole tiles and split units in one launch, then the fixup when the plan
 // may have a split.
-template <bool BF16, int BM, int BN, int EPI>
+template <bool BF16, int BM, int BN, int EPI, int KM = KM_NONE>
 static void launch_pair(const GemmParams& p0, int grid, bool may_split, hipStream_t s) {
     constexpr int WGN = waves_n<BF16, BM, BN>();
     typedef GemmEpilogue<BF16, BM, BN, EPI, 2, WGN> Epi;
     GemmParams p = p0;
     p.main_blocks = grid;
-    hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, WGN>), dim3(grid + (may_split ? kSplitUnits : 0)),
+    hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, WGN, KM>), dim3(grid + (may_split ? kSplitUnits : 0)),
                        dim3(128 * WGN), 0, s, p);
     if (!may_split) return;
     constexpr int groups = Epi::FN / Epi::IG;
@@ -921,6 +1017,8 @@ hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, c
     p.ldc2 = ldc2;
     p.rem = rem;
     p.unit_f4 = (int64_t)BM * BN / 4;
+    p.ldb = 0;
+    p.K1 = 0;
     if (!gemm_shape_supported(bf16, epi, BM, BN) || (rem && !gemm_shape_supported(bf16, epi, kRemBM, BN)))
         return hipErrorInvalidValue;
     if (!plan_ready)
@@ -946,5 +1044,66 @@ hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, c
     else launch_t<false>(epi, p, BM, BN, (int)grid, may_split, s);
     return hipGetLastError();
 }
+
+
+// ---- products with k-major operands (the backward's products through the
+// weights as stored and its weight gradients)
+
+bool grouped_gemm_nn_supported(int64_t lda, int K, int K1, int64_t ldb, int N, bool has_b1) {
+    if (K <= 0 || K % 64 || K1 <= 0 || K1 > K || K1 % 64) return false;
+    if ((K1 < K) != has_b1) return false;
+    if (N <= 0 || N % 128 || lda % 8 || ldb % 8 || ldb < N) return false;
+    if ((int64_t)K1 * ldb * 2 >= ((int64_t)1 << 31) || (int64_t)(K - K1) * ldb * 2 >= ((int64_t)1 << 31)) return false;
+    if ((255 * lda + K) * 2 >= ((int64_t)1 << 31)) return false;
+    return true;
+}
+
+template <int BM>
+static void launch_nn_bm(const GemmParams& p, int BN, int grid, bool ms, hipStream_t s) {
+    if (BN == 256) launch_pair<true, BM, 256, EPI_STORE, KM_B>(p, grid, ms, s);
+    else launch_pair<true, BM, 128, EPI_STORE, KM_B>(p, grid, ms, s);
+}
+
+hipError_t launch_grouped_gemm_nn(const void* A, int64_t lda, const void* B0, const void* B1, int K1, int64_t ldb,
+                                  int64_t bstride, void* C, int64_t ldc, int N, int K, int E, int64_t max_rows,
+                                  const int32_t* offsets, int32_t* plan, int32_t* plan_copy, float* partial,
+                                  hipStream_t s) {
+    if (max_rows <= 0) return hipSuccess;
+    if (!grouped_gemm_nn_supported(lda, K, K1, ldb, N, B1 != nullptr)) return hipErrorInvalidValue;
+    const GemmShape g = pick_gemm_shape(true, EPI_STORE, max_rows, offsets ? E : 1, N);
+    const int BM = g.BM, BN = (N % 256 == 0) ? 256 : 128;
+    GemmParams p;
+    p.A = A; p.lda = lda; p.B0 = B0; p.B1 = B1; p.bstride = bstride;
+    p.C = C; p.ldc = ldc; p.N = N; p.K = K; p.E = offsets ? E : 1;
+    int rem = 0;
+    gemm_geometry(true, EPI_STORE, N, K, BM, BN, p.NT, p.nk, rem);
+    p.offsets = offsets ? offsets : plan_copy;
+    p.plan = plan;
+    p.partial = partial;
+    p.C2 = nullptr;
+    p.ldc2 = 0;
+    p.rem = rem;
+    p.unit_f4 = (int64_t)BM * BN / 4;
+    p.ldb = ldb;
+    p.K1 = K1;
+    hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, offsets, E, (int)max_rows, BM, rem, p.NT, p.nk, plan,
+                       plan_copy, 0, 0, 0, 0, (int32_t*)nullptr);
+    const int64_t per_expert = rem ? (kRemThr + kRemBM - 1) / kRemBM : 1;
+    const int64_t m_tiles_ub = (max_rows + BM - 1) / BM + (p.E > 1 ? p.E * per_expert : per_expert);
+    const int64_t grid = (m_tiles_ub * p.NT + 7) / 8 * 8;
+    if (grid > 0x7fffffff - kSplitUnits) return hipErrorInvalidValue;
+    bool may_split = true;
+    if (offsets == nullptr) {
+        const int64_t whole = whole_tiles((int)max_rows, BM, rem != 0);
+        const int64_t r = max_rows - whole * BM;
+        const int64_t tiles = whole + (r > 0 ? (r + kRemBM - 1) / kRemBM : 0);
+        may_split = plan_may_split(tiles * p.NT, p.nk);
+    }
+    if (BM == 256) launch_nn_bm<256>(p, BN, (int)grid, may_split, s);
+    else if (BM == 128) launch_nn_bm<128>(p, BN, (int)grid, may_split, s);
+    else launch_nn_bm<64>(p, BN, (int)grid, may_split, s);
+    return hipGetLastError();
+}
+
 
 }  // namespace moe

@@ -95,6 +95,17 @@ hipError_t launch_tile_plans(bool bf16, const int32_t* offsets, int E, int64_t m
                              int BM1, int BN1, int32_t* plan1, int epi2, int N2, int K2, int BM2, int BN2,
                              int32_t* plan2, hipStream_t s);
 GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N);
+// C[r][n] = sum_k A[r][k] B_e[k][n] over the rows r of expert e (bf16), with
+// B_e read as stored ([K][N], row stride ldb): rows k < K1 from B0 + e
+// bstride, the rest from B1 + e bstride (row k - K1).  The forward's grouped
+// GEMM with the weight tile read by transposing LDS reads; its tile plan,
+// remainder tiles and split-K tail (plan, plan_copy, partial as for
+// launch_grouped_gemm).
+bool grouped_gemm_nn_supported(int64_t lda, int K, int K1, int64_t ldb, int N, bool has_b1);
+hipError_t launch_grouped_gemm_nn(const void* A, int64_t lda, const void* B0, const void* B1, int K1, int64_t ldb,
+                                  int64_t bstride, void* C, int64_t ldc, int N, int K, int E, int64_t max_rows,
+                                  const int32_t* offsets, int32_t* plan, int32_t* plan_copy, float* partial,
+                                  hipStream_t s);
 
 // backward.hip
 // dst[b][c][coff + r] = src[b][r][c]; R and C multiples of 64.

@@ -193,7 +193,19 @@ struct BwdLayout {
 // product is used below kNnRowsPerExpert rows per expert (bf16).
 constexpr int64_t kNnRowsPerExpert = 512;
 
+// bf16 backward products through the weights as stored: the grouped GEMM
+// reading its weight tiles k-major (transposing LDS reads) takes dh = dy W2
+// and dx = [da | du] [W1; W3] without weight copies, whatever the rows.
+bool use_km_products(const moe_config* c, int F) {
+    if (!is_bf16(c)) return false;
+    const bool swiglu = c->act == MOE_ACT_SWIGLU;
+    const int ig = swiglu ? 2 : 1, d = c->d_model;
+    return moe::grouped_gemm_nn_supported(d, d, d, F, F, false) &&
+           moe::grouped_gemm_nn_supported((int64_t)ig * F, ig * F, F, d, d, swiglu);
+}
+
 bool use_nn_product(const moe_config* c, int64_t rows, int E, int F) {
+    if (use_km_products(c, F)) return false;
     if (!is_bf16(c) || rows <= 0 || rows >= kNnRowsPerExpert * E) return false;
     const int ig = c->act == MOE_ACT_SWIGLU ? 2 : 1;
     const int d = c->d_model;
@@ -245,7 +257,7 @@ BwdLayout compute_bwd_layout(const moe_config* c) {
     L.dadu = take((size_t)R * ig * F * es);
     L.hh = take((size_t)R * F * es);
     L.dxp = take((size_t)R * d * es);
-    const bool nn = use_nn_product(c, R, E, F);
+    const bool nn = use_nn_product(c, R, E, F) || use_km_products(c, F);
     L.w2t = take(nn ? 0 : (size_t)E * F * d * es);
     L.w13t = take(nn ? 0 : (size_t)E * d * ig * F * es);
     const bool sh = c->n_shared > 0;
@@ -256,7 +268,7 @@ BwdLayout compute_bwd_layout(const moe_config* c) {
     L.sdadu = take((size_t)T * 2 * Fs * es);
     L.shh = take((size_t)T * Fs * es);
     L.sdx = take(sh ? (size_t)T * d * es : 0);
-    const bool snn = sh && use_nn_product(c, T, 1, (int)Fs);
+    const bool snn = sh && (use_nn_product(c, T, 1, (int)Fs) || use_km_products(c, (int)Fs));
     L.sw2t = take(snn ? 0 : Fs * d * es);
     L.sw13t = take(snn ? 0 : (size_t)d * 2 * Fs * es);
     L.plan = take(moe::ffn_tile_plan_ints(E) * sizeof(int32_t));
@@ -708,11 +720,12 @@ moe_status expert_backward(const moe_config* c, const void* X, const void* DY, i
     const int d = c->d_model;
     const int es = elem_bytes(c);
     moe_status s;
-    const bool nn = use_nn_product(c, rows, E, F);
+    const bool km = use_km_products(c, F);
+    const bool nn = !km && use_nn_product(c, rows, E, F);
     int32_t* nn_prefix = at<int32_t>(ws, L.nn_prefix);
     // weight copies with the other dimension contiguous (only for the
-    // grouped-GEMM route): W2^T [E][F][d] and [W1^T | W3^T] [E][d][ig F]
-    if (!nn) {
+    // grouped-GEMM route on copies): W2^T [E][F][d] and [W1^T | W3^T] [E][d][ig F]
+    if (!nn && !km) {
         moe::launch_transpose(W2, E, d, F, (int64_t)d * F, b.w2t, d, (int64_t)F * d, 0, es, h);
         moe::launch_transpose(W1, E, F, d, (int64_t)F * d, b.w13t, (int64_t)ig * F, (int64_t)d * ig * F, 0, es, h);
         if (swiglu)
@@ -738,7 +751,14 @@ moe_status expert_backward(const moe_config* c, const void* X, const void* DY, i
             return s;
     }
     const int32_t* offs = offsets ? offsets : plan_copy;
-    if (nn) {
+    int32_t* plan = at<int32_t>(ws, L.plan);
+    float* partial = at<float>(ws, L.partial);
+    if (km) {
+        // with offsets == NULL the plan launch also writes the group's offsets
+        const hipError_t e2 = moe::launch_grouped_gemm_nn(DY, d, W2, nullptr, d, F, (int64_t)d * F, b.dh, F, F, d, E,
+                                                          rows, offsets, plan, plan_copy, partial, h);
+        if (e2 != hipSuccess) return hip_status(e2);
+    } else if (nn) {
         // a single group needs its offsets before the NN product reads them
         if (!offsets) moe::launch_single_group_offsets(plan_copy, rows, h);
         const hipError_t e2 = moe::launch_gemm_nn(DY, d, W2, nullptr, d, F, (int64_t)d * F, b.dh, F, F, d, E, offs,
@@ -750,7 +770,12 @@ moe_status expert_backward(const moe_config* c, const void* X, const void* DY, i
     }
     moe::launch_bwd_act(bf, swiglu, b.dh, A_, U_, ld_au, offs, offsets ? E : 1, rows, F, b.dadu, b.hh, h);
     // DX = da W1 + du W3 as one product over the concatenated reduction
-    if (nn) {
+    if (km) {
+        const hipError_t e2 = moe::launch_grouped_gemm_nn(b.dadu, (int64_t)ig * F, W1, swiglu ? W3 : nullptr, F, d,
+                                                          (int64_t)F * d, DX, d, d, ig * F, E, rows, offsets, plan,
+                                                          plan_copy, partial, h);
+        if (e2 != hipSuccess) return hip_status(e2);
+    } else if (nn) {
         const hipError_t e2 = moe::launch_gemm_nn(b.dadu, (int64_t)ig * F, W1, swiglu ? W3 : nullptr, F, d,
                                                   (int64_t)F * d, DX, d, d, ig * F, E, offs, rows, nn_prefix, h);
         if (e2 != hipSuccess) return hip_status(e2);

@@ -44,6 +44,19 @@ CASES = {
     # rows go to the 64-row remainder launch (forward up/down, dh, dx)
     "bf16_swiglu_256_tiles": dict(T=1600, d=256, F=256, E=4, k=2, act_dtype="bf16", act="swiglu",
                                   gate="softmax_topk", seed=209),
+    # bf16 shapes whose products through the weights read them as stored
+    # (k-major weight tiles) and whose weight gradients read both operands
+    # as stored: many experts with a few rows or none (zero gradients, k
+    # slices cut inside 64 rows), ReLU (one weight in the dx reduction)
+    "bf16_km_relu_zipf_sparse": dict(T=512, d=256, F=512, E=32, k=1, act_dtype="bf16", act="relu",
+                                     gate="softmax_full", logit_bias="zipf", seed=210),
+    # 128-column weight tiles for dh (d_ff 384), 256 for dx; weight gradients
+    # on the staged product (d_ff not a multiple of 256)
+    "bf16_km_bn128": dict(T=1200, d=512, F=384, E=6, k=2, act_dtype="bf16", act="swiglu", gate="softmax_topk",
+                          seed=211),
+    # the shared expert: one group of T rows (offsets built by the plan launch)
+    "bf16_km_shared": dict(T=640, d=256, F=256, E=8, k=2, act_dtype="bf16", act="swiglu", gate="sigmoid_bias",
+                           sel_bias=True, n_shared=1, F_shared=512, seed=212),
 }
 
 
