@@ -269,23 +269,44 @@ __global__ __launch_bounds__(64) void k_router_dots_ring(const void* __restrict_
         // 16-byte chunk q of this lane's x and w rows
         auto X = [&](int q) { return *(const u32x4_t*)(xrow + ((q ^ (tg % XCH)) * 16)); };
         auto W = [&](int q) { return *(const float4*)(wrow + ((q ^ (cg % WCH)) * 16)); };
+        // the operands of 8 steps (k = 8g .. 8g + 7) are read PD groups
+        // ahead into a ring of register sets, so a read's latency is covered
+        // by the dependent fmas of the groups before (scheduling fences keep
+        // the compiler from sinking the reads to their use)
+        constexpr int NG = KC / 8, PD = 2;
+        u32x4_t xf[PD + 1][BF16 ? 1 : 2];
+        float4 wf[PD + 1][2];
+        auto fetch = [&](int g, int b) {
+            if constexpr (BF16) {
+                xf[b][0] = X(g);
+            } else {
+                xf[b][0] = X(2 * g);
+                xf[b][1] = X(2 * g + 1);
+            }
+            wf[b][0] = W(2 * g);
+            wf[b][1] = W(2 * g + 1);
+        };
 #pragma unroll
-        for (int g = 0; g < KC / 8; ++g) {          // 8 steps: k = 8g .. 8g + 7
-            const float4 wa = W(2 * g), wb = W(2 * g + 1);
+        for (int g = 0; g < PD; ++g) fetch(g, g);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {          // 8 steps: k = 8g .. 8g + 7
+            const int b = g % (PD + 1);
+            if (g + PD < NG) fetch(g + PD, (g + PD) % (PD + 1));
+            __builtin_amdgcn_sched_barrier(0);      // the reads stay ahead of this group's fmas
+            const float4 wa = wf[b][0], wb = wf[b][1];
             float xv[8];
             if constexpr (BF16) {
-                const u32x4_t v = X(g);
+                const u32x4_t v = xf[b][0];
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
                     xv[2 * h] = __uint_as_float(v[h] << 16);
                     xv[2 * h + 1] = __uint_as_float(v[h] & 0xffff0000u);
                 }
             } else {
-                const u32x4_t v0 = X(2 * g), v1 = X(2 * g + 1);
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
-                    xv[h] = __uint_as_float(v0[h]);
-                    xv[4 + h] = __uint_as_float(v1[h]);
+                    xv[h] = __uint_as_float(xf[b][0][h]);
+                    xv[4 + h] = __uint_as_float(xf[b][1][h]);
                 }
             }
             acc = __builtin_fmaf(xv[0], wa.x, acc);
@@ -296,6 +317,7 @@ __global__ __launch_bounds__(64) void k_router_dots_ring(const void* __restrict_
             acc = __builtin_fmaf(xv[5], wb.y, acc);
             acc = __builtin_fmaf(xv[6], wb.z, acc);
             acc = __builtin_fmaf(xv[7], wb.w, acc);
+            __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
