@@ -464,7 +464,9 @@ __global__ __launch_bounds__(512) void k_gemm_x256(XnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int BM = 256, KC = 64;
     constexpr int OPB = BM * KC * 2;
-    __shared__ __align__(16) uint8_t lds[2 * 2 * OPB];
+    // staged output: 8 waves x 64 rows of 256 bytes, rows padded by 16 bytes
+    constexpr int SPITCH = 128 * 2 + 16, SBYTES = 8 * 64 * SPITCH;
+    __shared__ __align__(16) uint8_t lds[2 * 2 * OPB > SBYTES ? 2 * 2 * OPB : SBYTES];
     // tiles: TN, E x tiles_m x tiles_n; NN, (sum of the experts' row tiles)
     // x tiles_n.  Groups of GM row tiles: the 32 CUs of an XCD run 4 row
     // tiles x 8 column tiles at a time, so each staged chunk of A is fetched
@@ -692,6 +694,40 @@ __global__ __launch_bounds__(512) void k_gemm_x256(XnParams p) {
     // lane holds C[m][n .. n+3] of block (n-block i, m-block j)
     uint16_t* Ce = NN ? (uint16_t*)p.C + (int64_t)m_base * p.ldc : (uint16_t*)p.C + (size_t)e * p.M * p.N;
     const int64_t ldc = NN ? p.ldc : p.N;
+    if (ldc % 8 == 0 && p.N % 8 == 0 && (((uintptr_t)Ce) & 15) == 0) {
+        // through LDS, so every global store covers whole 128-byte lines (a
+        // lane's direct 8-byte stores leave each instruction 32 bytes of 16
+        // rows): each wave stages its 64 x 128 outputs in its own region
+        // (padded rows: the 16 rows x 2 column groups of a half wave hit 32
+        // distinct bank pairs) and stores 4 rows of 256 bytes per instruction
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();   // every wave is past its last fragment read
+        asm volatile("" ::: "memory");
+        uint8_t* reg = lds + wave * 64 * SPITCH;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ml = j * 16 + (lane & 15);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                u32x2_t w;
+                w[0] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+                w[1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+                *(u32x2_t*)(reg + ml * SPITCH + (i * 16 + 4 * (lane >> 4)) * 2) = w;
+            }
+        }
+        const int lr = lane >> 4, lc = lane & 15;
+        const int n = n_base + wn * 128 + lc * 8;
+#pragma unroll
+        for (int r = 0; r < 64; r += 4) {
+            const int mr = r + lr;
+            const u32x4_t v = *(const u32x4_t*)(reg + mr * SPITCH + lc * 16);
+            const int ml = wm * 64 + mr;
+            if ((NN ? ml < rows_tile : m_base + ml < p.M) && n < p.N)
+                *(u32x4_t*)(Ce + (int64_t)(NN ? ml : m_base + ml) * ldc + n) = v;
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int ml = wm * 64 + j * 16 + (lane & 15);
