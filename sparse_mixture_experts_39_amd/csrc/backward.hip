@@ -977,8 +977,96 @@ void launch_bwd_dx(bool bf16, const void* dy, const void* dx_perm, const int32_t
 // the bias.  k_bwd_wr_sum then adds the chunks in order.
 constexpr int kWrTokens = 256;
 constexpr int kWrExperts = 64;
+// Up to 16 experts (k_bwd_wr_few): 32-token chunks, each thread 8 columns
+// (one 16-byte load of bf16 x per token, or two of fp32) and every expert of
+// the call, so no multiply-add is spent on absent experts and x is read once.
+constexpr int kWrFewTokens = 32;
+constexpr int kWrFewExperts = 16;
 
-int bwd_wr_chunks(int T) { return (T + kWrTokens - 1) / kWrTokens; }
+int bwd_wr_chunks(int T, int E) {
+    const int tok = E <= kWrFewExperts ? kWrFewTokens : kWrTokens;
+    return (T + tok - 1) / tok;
+}
+
+template <int EX, bool BF16>
+__global__ __launch_bounds__(256) void k_bwd_wr_few(const float* __restrict__ dz, const void* __restrict__ x, int T,
+                                                    int E, int d, float* __restrict__ part) {
+    constexpr int CPT = 8;    // columns per thread
+    __shared__ float zs[kWrFewTokens][EX];
+    const int q = blockIdx.z;
+    const int c0 = (blockIdx.x * 256 + threadIdx.x) * CPT;
+    const int t0 = q * kWrFewTokens, nt = min(T - t0, kWrFewTokens);
+    for (int i = threadIdx.x; i < kWrFewTokens * EX; i += 256) {
+        const int tt = i / EX, ee = i - tt * EX;
+        zs[tt][ee] = (tt < nt && ee < E) ? dz[(int64_t)(t0 + tt) * E + ee] : 0.0f;
+    }
+    __syncthreads();
+    if (c0 > d) return;
+    float acc[EX][CPT];
+#pragma unroll
+    for (int ee = 0; ee < EX; ++ee)
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) acc[ee][u] = 0.0f;
+    // whole vector loads where all 8 columns are below d (x rows 16-byte
+    // aligned), else per column; column d itself is the bias (x = 1)
+    const bool vec = c0 + CPT <= d && (d % CPT) == 0;
+    auto row = [&](int tt, float* xv) {
+        const int64_t base = (int64_t)(t0 + tt) * d + c0;
+        if (vec) {
+            if constexpr (BF16) {
+                const u32x4_t v = *(const u32x4_t*)((const uint16_t*)x + base);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    xv[2 * h] = __uint_as_float(v[h] << 16);
+                    xv[2 * h + 1] = __uint_as_float(v[h] & 0xffff0000u);
+                }
+            } else {
+                const float4 a = *(const float4*)((const float*)x + base), b = *(const float4*)((const float*)x + base + 4);
+                xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
+                xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < CPT; ++u) {
+                const int c = c0 + u;
+                xv[u] = c < d ? load_act<BF16>(x, base + u) : (c == d ? 1.0f : 0.0f);
+            }
+        }
+    };
+    constexpr int UT = 8;     // tokens whose rows are loaded before their multiply-adds
+    for (int tb = 0; tb < nt; tb += UT) {
+        float xv[UT][CPT];
+#pragma unroll
+        for (int j = 0; j < UT; ++j) {
+            if (tb + j < nt) row(tb + j, xv[j]);
+            else {
+#pragma unroll
+                for (int u = 0; u < CPT; ++u) xv[j][u] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < UT; ++j) {
+            // past the chunk's tokens the rows are zero and zs reads 0: the
+            // multiply-adds add +0 and change nothing, so they are not skipped
+            const int tj = min(tb + j, kWrFewTokens - 1);
+#pragma unroll
+            for (int ee = 0; ee < EX; ++ee) {
+                const float z = tb + j < nt ? zs[tj][ee] : 0.0f;
+#pragma unroll
+                for (int u = 0; u < CPT; ++u) acc[ee][u] += z * xv[j][u];
+            }
+        }
+    }
+#pragma unroll
+    for (int ee = 0; ee < EX; ++ee) {
+        if (ee < E) {
+            float* dst = part + ((int64_t)q * E + ee) * (d + 1);
+#pragma unroll
+            for (int u = 0; u < CPT; ++u)
+                if (c0 + u <= d) dst[c0 + u] = acc[ee][u];
+        }
+    }
+}
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_bwd_wr_part(const float* __restrict__ dz, const void* __restrict__ x, int T,
@@ -1013,8 +1101,17 @@ __global__ __launch_bounds__(256) void k_bwd_wr_sum(const float* __restrict__ pa
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t n = (int64_t)E * (d + 1);
     if (i >= n) return;
+    // chunks in order; 8 loads in flight ahead of the ordered adds
     float v = 0.0f;
-    for (int q = 0; q < nq; ++q) v += part[(int64_t)q * n + i];
+    int q = 0;
+    for (; q + 8 <= nq; q += 8) {
+        float h[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) h[u] = part[(int64_t)(q + u) * n + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v += h[u];
+    }
+    for (; q < nq; ++q) v += part[(int64_t)q * n + i];
     const int e = (int)(i / (d + 1)), c = (int)(i - (int64_t)e * (d + 1));
     if (c < d) {
         if (dw) dw[(int64_t)e * d + c] = v;
@@ -1025,8 +1122,17 @@ __global__ __launch_bounds__(256) void k_bwd_wr_sum(const float* __restrict__ pa
 
 void launch_bwd_wr(bool bf16, const float* dz, const void* x, int T, int E, int d, float* part, float* dw, float* db,
                    hipStream_t s) {
-    const int nq = bwd_wr_chunks(T);
-    if (nq > 0) {
+    const int nq = bwd_wr_chunks(T, E);
+    if (nq > 0 && E <= kWrFewExperts) {
+        const dim3 grid((d + 1 + 256 * 8 - 1) / (256 * 8), 1, nq);
+        if (E <= 8) {
+            if (bf16) hipLaunchKernelGGL((k_bwd_wr_few<8, true>), grid, dim3(256), 0, s, dz, x, T, E, d, part);
+            else hipLaunchKernelGGL((k_bwd_wr_few<8, false>), grid, dim3(256), 0, s, dz, x, T, E, d, part);
+        } else {
+            if (bf16) hipLaunchKernelGGL((k_bwd_wr_few<16, true>), grid, dim3(256), 0, s, dz, x, T, E, d, part);
+            else hipLaunchKernelGGL((k_bwd_wr_few<16, false>), grid, dim3(256), 0, s, dz, x, T, E, d, part);
+        }
+    } else if (nq > 0) {
         const dim3 grid((d + 1 + 255) / 256, (E + kWrExperts - 1) / kWrExperts, nq);
         if (bf16) hipLaunchKernelGGL(k_bwd_wr_part<true>, grid, dim3(256), 0, s, dz, x, T, E, d, part);
         else hipLaunchKernelGGL(k_bwd_wr_part<false>, grid, dim3(256), 0, s, dz, x, T, E, d, part);

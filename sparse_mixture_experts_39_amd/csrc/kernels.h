@@ -142,8 +142,8 @@ void launch_bwd_router(const float* dots, int NC, const float* logit_bias, const
 void launch_bwd_dx(bool bf16, const void* dy, const void* dx_perm, const int32_t* slot_pos, int slots,
                    const void* dx_shared, const float* dz, const int32_t* idx, const float* w_router, int T, int E,
                    int d, bool residual, void* dx, hipStream_t s);
-int bwd_wr_chunks(int T);
-// dW_r = dz^T x and db = sum_t dz; part holds bwd_wr_chunks(T) * E * (d + 1) floats.
+int bwd_wr_chunks(int T, int E);
+// dW_r = dz^T x and db = sum_t dz; part holds bwd_wr_chunks(T, E) * E * (d + 1) floats.
 void launch_bwd_wr(bool bf16, const float* dz, const void* x, int T, int E, int d, float* part, float* dw, float* db,
                    hipStream_t s);
 

@@ -249,7 +249,7 @@ BwdLayout compute_bwd_layout(const moe_config* c) {
     L.dots = take((size_t)T * E * sizeof(float));
     L.dg = take((size_t)n_assign(c) * sizeof(float));
     L.dz = take((size_t)T * E * sizeof(float));
-    L.wr_part = take((size_t)moe::bwd_wr_chunks(T) * E * (d + 1) * sizeof(float));
+    L.wr_part = take((size_t)moe::bwd_wr_chunks(T, E) * E * (d + 1) * sizeof(float));
     L.dyp = take((size_t)R * d * es);
     L.a = take((size_t)R * F * es);
     L.u = take(ig == 2 ? (size_t)R * F * es : 0);
