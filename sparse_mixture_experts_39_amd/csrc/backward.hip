@@ -40,6 +40,36 @@ __device__ __forceinline__ void store_act(void* p, int64_t i, float v) {
     else ((float*)p)[i] = v;
 }
 
+// 8 consecutive activations from element i (i and the row stride multiples
+// of 8: one 16-byte access for bf16, two for fp32), exact in fp32.
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* p, int64_t i, float* v) {
+    if constexpr (BF16) {
+        const u32x4_t w = *(const u32x4_t*)((const uint16_t*)p + i);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            v[2 * h] = __uint_as_float(w[h] << 16);
+            v[2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
+        }
+    } else {
+        const float4 a = *(const float4*)((const float*)p + i), b = *(const float4*)((const float*)p + i + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+}
+template <bool BF16>
+__device__ __forceinline__ void store8(void* p, int64_t i, const float* v) {
+    if constexpr (BF16) {
+        u32x4_t w;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) w[h] = pack_bf16x2(v[2 * h], v[2 * h + 1]);
+        *(u32x4_t*)((uint16_t*)p + i) = w;
+    } else {
+        *(float4*)((float*)p + i) = make_float4(v[0], v[1], v[2], v[3]);
+        *(float4*)((float*)p + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+}
+
 // Fixed-order sum over the 256 threads of a block (wave shuffles, then the
 // four wave totals in order).  Every thread gets the total.
 __device__ __forceinline__ float block_sum256(float v, float* red) {
@@ -147,10 +177,25 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const void* __restrict__ dy, c
     const int t = a / slots;
     const float g = gates[a];
     float acc = 0.0f;
-    for (int c = threadIdx.x; c < d; c += 256) {
-        const float v = load_act<BF16>(dy, (int64_t)t * d + c);
-        acc += v * load_act<BF16>(y_perm, (int64_t)r * d + c);
-        store_act<BF16>(dy_perm, (int64_t)r * d + c, g * v);
+    if (d % 8 == 0 && ((((uintptr_t)dy) | ((uintptr_t)y_perm) | ((uintptr_t)dy_perm)) & 15) == 0) {
+        // 8 consecutive columns per thread and step (16-byte accesses)
+        for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+            float v[8], y[8], o[8];
+            load8<BF16>(dy, (int64_t)t * d + c, v);
+            load8<BF16>(y_perm, (int64_t)r * d + c, y);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                acc += v[u] * y[u];
+                o[u] = g * v[u];
+            }
+            store8<BF16>(dy_perm, (int64_t)r * d + c, o);
+        }
+    } else {
+        for (int c = threadIdx.x; c < d; c += 256) {
+            const float v = load_act<BF16>(dy, (int64_t)t * d + c);
+            acc += v * load_act<BF16>(y_perm, (int64_t)r * d + c);
+            store_act<BF16>(dy_perm, (int64_t)r * d + c, g * v);
+        }
     }
     const float tot = block_sum256(acc, red);
     if (threadIdx.x == 0) dg[a] = tot;
@@ -937,6 +982,48 @@ __global__ __launch_bounds__(256) void k_bwd_dx(const void* __restrict__ dy, con
     const int32_t* sp = slot_pos + (int64_t)t * slots;
     const int32_t* it = idx ? idx + (int64_t)t * slots : nullptr;
     const float* dzt = dz ? dz + (int64_t)t * E : nullptr;
+    if (d % 8 == 0 && ((((uintptr_t)dy) | ((uintptr_t)dx_perm) | ((uintptr_t)dx_shared) | ((uintptr_t)w_router) |
+                        ((uintptr_t)dx)) & 15) == 0) {
+        // 8 consecutive columns per thread and step (16-byte accesses); the
+        // same operations per element in the same order as below
+        for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+            float v[8], q[8];
+            if (residual) load8<BF16>(dy, (int64_t)t * d + c, v);
+            else {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = 0.0f;
+            }
+            for (int j = 0; j < slots; ++j) {
+                const int r = sp[j];
+                if (r >= 0) {
+                    load8<BF16>(dx_perm, (int64_t)r * d + c, q);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) v[u] += q[u];
+                }
+            }
+            if (dx_shared) {
+                load8<BF16>(dx_shared, (int64_t)t * d + c, q);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] += q[u];
+            }
+            auto add_router = [&](int e) {
+                load8<false>(w_router, (int64_t)e * d + c, q);
+                const float z = dzt[e];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] += z * q[u];
+            };
+            if (dzt && it) {
+                for (int j = 0; j < slots; ++j) {
+                    const int e = it[j];
+                    if (e >= 0) add_router(e);
+                }
+            } else if (dzt) {
+                for (int e = 0; e < E; ++e) add_router(e);
+            }
+            store8<BF16>(dx, (int64_t)t * d + c, v);
+        }
+        return;
+    }
     for (int c = threadIdx.x; c < d; c += 256) {
         float v = residual ? load_act<BF16>(dy, (int64_t)t * d + c) : 0.0f;
         for (int j = 0; j < slots; ++j) {
