@@ -52,8 +52,8 @@ def workload_desc(cfg):
 
 def kernel_source_hash() -> str:
     import hashlib
-    h = hashlib.sha256()
-    for f in ("ffn.hip", "device_common.h"):
+    h = hashlib.sha256()   # the grouped GEMM's sources: kernels, helpers, work decomposition
+    for f in ("ffn.hip", "device_common.h", "tile_plan.h"):
         with open(os.path.join(ROOT, "sparse_mixture_experts_39_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -33,6 +33,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "tile_plan.h"
 
 namespace moe {
 
@@ -89,11 +90,74 @@ __device__ __forceinline__ int32_t column_scan(const int32_t* __restrict__ hist,
     return run;
 }
 
+// Tile plans of the expert GEMMs that follow the dispatch (tile_plan.h),
+// from the kept counts: a block of 1024 threads, thread e = expert e.
+__device__ void block_plan(const PlanGeom& g, int32_t M, int E, int e, int32_t (*pl)[1024]) {
+    const int32_t whole = e < E ? whole_tiles(M, g.BM, g.rem != 0) : 0;
+    const int32_t nr = e < E ? remainder_tiles(M, g.BM, g.rem != 0) : 0;
+    __syncthreads();   // earlier reads of pl are done
+    pl[0][e] = whole;
+    pl[1][e] = nr;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int32_t v0 = e >= off ? pl[0][e - off] : 0;
+        const int32_t v1 = e >= off ? pl[1][e - off] : 0;
+        __syncthreads();
+        pl[0][e] += v0;
+        pl[1][e] += v1;
+        __syncthreads();
+    }
+    if (e == 0) {
+        g.pre[0] = 0;
+        g.pre[E + 4] = 0;
+        const int total = (pl[0][E - 1] + pl[1][E - 1]) * g.NT;
+        int split, tail;
+        split_rule(total, g.nk, split, tail);
+        g.pre[E + 1] = total - tail;
+        g.pre[E + 2] = split;
+        g.pre[E + 3] = tail;
+    }
+    if (e < E) {
+        g.pre[e + 1] = pl[0][e];
+        g.pre[E + 4 + e + 1] = pl[1][e];
+    }
+}
+
+// The same for at most 64 experts: one wave, lane e = expert e.
+__device__ void wave_plan(const PlanGeom& g, int32_t M, int E, int e) {
+    int32_t sw = e < E ? whole_tiles(M, g.BM, g.rem != 0) : 0;
+    int32_t sr = e < E ? remainder_tiles(M, g.BM, g.rem != 0) : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t a = __shfl_up(sw, off, 64), b = __shfl_up(sr, off, 64);
+        if (e >= off) {
+            sw += a;
+            sr += b;
+        }
+    }
+    const int32_t tw = __shfl(sw, E - 1, 64), tr = __shfl(sr, E - 1, 64);
+    if (e == 0) {
+        g.pre[0] = 0;
+        g.pre[E + 4] = 0;
+        const int total = (tw + tr) * g.NT;
+        int split, tail;
+        split_rule(total, g.nk, split, tail);
+        g.pre[E + 1] = total - tail;
+        g.pre[E + 2] = split;
+        g.pre[E + 3] = tail;
+    }
+    if (e < E) {
+        g.pre[e + 1] = sw;
+        g.pre[E + 4 + e + 1] = sr;
+    }
+}
+
 __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ hist, int nblocks, int E,
                                                int64_t capacity, int32_t* __restrict__ blockbase,
                                                int32_t* __restrict__ offsets, const float* __restrict__ P,
                                                int32_t* counts_out, int32_t* kept_out, float* f_out,
-                                               int32_t* dropped_out, float* imbalance_out, float* aux_out) {
+                                               int32_t* dropped_out, float* imbalance_out, float* aux_out,
+                                               PlanGeom g1, PlanGeom g2) {
     __shared__ int32_t scan[1024];
     __shared__ int64_t kept_red[1024];
     __shared__ int64_t cnt_red[1024];
@@ -149,6 +213,11 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ hist,
         if (imbalance_out) imbalance_out[0] = total > 0 ? (float)((double)max_red[0] * (double)E / (double)total) : 0.0f;
         if (aux_out && P) aux_out[0] = (float)((double)E * aux_red[0]);
     }
+    if (g1.pre || g2.pre) {
+        __shared__ int32_t pl[2][1024];
+        if (g1.pre) block_plan(g1, kp, E, e, pl);
+        if (g2.pre) block_plan(g2, kp, E, e, pl);
+    }
 }
 
 // k_scan for at most 64 experts: one wave, lane e = expert e, shuffles
@@ -159,7 +228,8 @@ __global__ __launch_bounds__(64) void k_scan_wave(const int32_t* __restrict__ hi
                                                   int64_t capacity, int32_t* __restrict__ blockbase,
                                                   int32_t* __restrict__ offsets, const float* __restrict__ P,
                                                   int32_t* counts_out, int32_t* kept_out, float* f_out,
-                                                  int32_t* dropped_out, float* imbalance_out, float* aux_out) {
+                                                  int32_t* dropped_out, float* imbalance_out, float* aux_out,
+                                                  PlanGeom g1, PlanGeom g2) {
     const int e = threadIdx.x;
     int32_t c = 0, kp = 0;
     if (e < E) {
@@ -202,6 +272,8 @@ __global__ __launch_bounds__(64) void k_scan_wave(const int32_t* __restrict__ hi
         if (imbalance_out) imbalance_out[0] = ct > 0 ? (float)((double)mx * (double)E / (double)ct) : 0.0f;
         if (aux_out && P) aux_out[0] = (float)((double)E * ax);
     }
+    if (g1.pre) wave_plan(g1, kp, E, e);
+    if (g2.pre) wave_plan(g2, kp, E, e);
 }
 
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ topk_idx, int64_t n_assign, int E,
@@ -363,15 +435,18 @@ void launch_histogram(const int32_t* topk_idx, int64_t n_assign, int E, int32_t*
 }
 
 void launch_scan(const int32_t* hist, int nblocks, int E, int64_t capacity, int32_t* blockbase,
-                 int32_t* offsets, const float* P, const moe_stats* st, hipStream_t s) {
+                 int32_t* offsets, const float* P, const moe_stats* st, hipStream_t s, const PlanGeom* g1,
+                 const PlanGeom* g2) {
+    const PlanGeom none = {0, 0, 0, 0, nullptr};
+    const PlanGeom a = g1 ? *g1 : none, b = g2 ? *g2 : none;
     if (E <= 64)
         hipLaunchKernelGGL(k_scan_wave, dim3(1), dim3(64), 0, s, hist, nblocks, E, capacity, blockbase, offsets, P,
                            st ? st->counts : nullptr, st ? st->kept : nullptr, st ? st->f : nullptr,
-                           st ? st->n_dropped : nullptr, st ? st->imbalance : nullptr, st ? st->aux : nullptr);
+                           st ? st->n_dropped : nullptr, st ? st->imbalance : nullptr, st ? st->aux : nullptr, a, b);
     else
         hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, nblocks, E, capacity, blockbase, offsets, P,
                            st ? st->counts : nullptr, st ? st->kept : nullptr, st ? st->f : nullptr,
-                           st ? st->n_dropped : nullptr, st ? st->imbalance : nullptr, st ? st->aux : nullptr);
+                           st ? st->n_dropped : nullptr, st ? st->imbalance : nullptr, st ? st->aux : nullptr, a, b);
 }
 
 void launch_scatter(const int32_t* topk_idx, int64_t n_assign, int E, const int32_t* blockbase,

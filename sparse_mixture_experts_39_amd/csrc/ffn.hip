@@ -54,6 +54,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "tile_plan.h"
 
 namespace moe {
 
@@ -99,9 +100,8 @@ struct GemmParams {
 // those `tail` tiles are cut into `split` K ranges each, one block per range:
 // every block writes its fp32 partial accumulators, and k_split_fixup adds
 // the ranges of a tile in a fixed order and applies the epilogue, so results
-// do not depend on timing.  kSplitUnits is the CU count of the target chip.
-constexpr int kSplitUnits = 256;
-constexpr int kMaxSplit = 16;
+// do not depend on timing.  kSplitUnits (tile_plan.h) is the CU count of
+// the target chip.
 
 // Remainder tiles.  With 256-row tiles an expert whose row count lies just
 // past a multiple of 256 pays a whole tile of padding rows for a few real
@@ -121,15 +121,7 @@ constexpr int kMaxSplit = 16;
 #ifndef MOE_GEMM_WGN256
 #define MOE_GEMM_WGN256 2
 #endif
-constexpr int kRemBM = 64;
-constexpr int kRemThr = 128;
-
-// Whole BM-row tiles of an expert with M rows: ceil(M / BM), or floor(M / BM)
-// when its last r = M mod BM rows (0 < r <= kRemThr) go to remainder tiles.
-__host__ __device__ __forceinline__ int whole_tiles(int M, int BM, bool rem) {
-    const int r = M % BM;
-    return (rem && r > 0 && r <= kRemThr) ? M / BM : (M + BM - 1) / BM;
-}
+// (kRemBM, kRemThr and whole_tiles: tile_plan.h)
 
 // Tile L of the natural order: first every whole tile, then every remainder
 // tile (so that a split-K tail takes remainder tiles first); within each
@@ -909,8 +901,7 @@ __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ 
     }
     auto plan = [&](int bm, int rm, int nt, int nkk, int32_t* pre) {
         const int32_t whole = whole_tiles(M, bm, rm != 0);
-        const int32_t r = M - whole * bm;            // rows left for remainder tiles (0 unless rm)
-        const int32_t nr = r > 0 ? (r + kRemBM - 1) / kRemBM : 0;
+        const int32_t nr = remainder_tiles(M, bm, rm != 0);
         __syncthreads();   // a previous plan's reads of scan are done
         scan[0][e] = whole;
         scan[1][e] = nr;
@@ -933,17 +924,8 @@ __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ 
         }
         if (e == 0) {
             const int total = (scan[0][E - 1] + scan[1][E - 1]) * nt;
-            const int left = total % kSplitUnits;
-            int split = 1, tail = 0;
-            if (left > 0 && left <= kSplitUnits / 2) {
-                int sp = kSplitUnits / left;
-                sp = min(sp, kMaxSplit);
-                sp = min(sp, nkk / 4);                 // at least 4 slices per range
-                if (sp >= 2) {
-                    split = sp;
-                    tail = left;
-                }
-            }
+            int split, tail;
+            split_rule(total, nkk, split, tail);
             pre[E + 1] = total - tail;
             pre[E + 2] = split;
             pre[E + 3] = tail;
@@ -962,6 +944,14 @@ static void gemm_geometry(bool bf16, int epi, int N, int K, int BM, int BN, int&
     NT = epi_swiglu(epi) ? N / (BN / 2) : N / BN;
     nk = K * (bf16 ? 2 : 4) / 128;
     rem = uses_rem(bf16, BM) ? 1 : 0;
+}
+
+PlanGeom plan_geom(bool bf16, int epi, int N, int K, int BM, int BN, int32_t* pre) {
+    PlanGeom g;
+    gemm_geometry(bf16, epi, N, K, BM, BN, g.NT, g.nk, g.rem);
+    g.BM = BM;
+    g.pre = pre;
+    return g;
 }
 
 hipError_t launch_tile_plans(bool bf16, const int32_t* offsets, int E, int64_t max_rows, int epi1, int N1, int K1,
@@ -1065,12 +1055,9 @@ static void launch_t(int epi, const GemmParams& p, int BM, int BN, int grid, boo
 // Whether a plan of `total` tiles takes the split-K tail (the rule of
 // k_tile_plan, for launches whose row counts the host knows).
 static bool plan_may_split(int64_t total, int nk) {
-    const int64_t rem = total % kSplitUnits;
-    if (rem <= 0 || rem > kSplitUnits / 2) return false;
-    int64_t sp = kSplitUnits / rem;
-    sp = std::min<int64_t>(sp, kMaxSplit);
-    sp = std::min<int64_t>(sp, nk / 4);
-    return sp >= 2;
+    int split, tail;
+    split_rule((int)(total % kSplitUnits), nk, split, tail);
+    return split >= 2;
 }
 
 hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B0, const void* B1,

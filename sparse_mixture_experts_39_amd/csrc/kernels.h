@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "../../include/moe.h"
+#include "tile_plan.h"
 
 namespace moe {
 
@@ -49,8 +50,11 @@ void launch_ec_route(const float* dots, const float* logit_bias, int T, int E, i
 // dispatch.hip
 constexpr int kAssignBlock = 256;  // assignments per histogram / scatter block
 void launch_histogram(const int32_t* topk_idx, int64_t n_assign, int E, int32_t* hist, hipStream_t s);
+// g1 / g2 (optional): the scan also writes the tile plans of the two expert
+// GEMMs that follow, from the kept counts (tile_plan.h).
 void launch_scan(const int32_t* hist, int nblocks, int E, int64_t capacity,
-                 int32_t* blockbase, int32_t* offsets, const float* P, const moe_stats* st, hipStream_t s);
+                 int32_t* blockbase, int32_t* offsets, const float* P, const moe_stats* st, hipStream_t s,
+                 const PlanGeom* g1 = nullptr, const PlanGeom* g2 = nullptr);
 void launch_scatter(const int32_t* topk_idx, int64_t n_assign, int E, const int32_t* blockbase,
                     const int32_t* offsets, int64_t capacity, int32_t* perm_src, int32_t* slot_pos, hipStream_t s);
 // Static device scratch of moe_dispatch_noalloc: its size, and its device
@@ -95,6 +99,9 @@ hipError_t launch_tile_plans(bool bf16, const int32_t* offsets, int E, int64_t m
                              int BM1, int BN1, int32_t* plan1, int epi2, int N2, int K2, int BM2, int BN2,
                              int32_t* plan2, hipStream_t s);
 GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N);
+// Plan geometry of a grouped GEMM launch (as launch_grouped_gemm sets it),
+// for a plan written ahead of the launch (plan_ready).
+PlanGeom plan_geom(bool bf16, int epi, int N, int K, int BM, int BN, int32_t* pre);
 // C[r][n] = sum_k A[r][k] B_e[k][n] over the rows r of expert e (bf16), with
 // B_e read as stored ([K][N], row stride ldb): rows k < K1 from B0 + e
 // bstride, the rest from B1 + e bstride (row k - K1).  The forward's grouped

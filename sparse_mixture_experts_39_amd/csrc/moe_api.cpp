@@ -447,15 +447,11 @@ moe_status moe_update_bias(const moe_config* c, const int32_t* counts, float gam
     return after_launch();
 }
 
-moe_status moe_dispatch(const moe_config* c, const void* x, const int32_t* topk_idx, void* x_perm,
-                        int32_t* expert_offsets, int32_t* perm_src, int32_t* slot_pos, const moe_stats* st, void* ws,
-                        size_t ws_bytes, void* stream) {
-    moe_status s = moe_validate_config(c);
-    if (s != MOE_OK) return s;
-    if (!expert_offsets) return MOE_ERR_INVALID_ARG;
-    if (c->T > 0 && (!x || !topk_idx || !x_perm || !perm_src || !slot_pos)) return MOE_ERR_INVALID_ARG;
-    if ((s = check_ws(c, ws, ws_bytes)) != MOE_OK) return s;
-    hipStream_t h = (hipStream_t)stream;
+// The dispatch kernels on validated arguments; gu / gd (optional): the scan
+// also writes the tile plans of the two expert GEMMs that follow.
+static moe_status dispatch_stages(const moe_config* c, const void* x, const int32_t* topk_idx, void* x_perm,
+                                  int32_t* expert_offsets, int32_t* perm_src, int32_t* slot_pos, const moe_stats* st,
+                                  void* ws, hipStream_t h, const moe::PlanGeom* gu, const moe::PlanGeom* gd) {
     const Layout L = compute_layout(c);
     const int E = c->n_experts;
     const int64_t na = n_assign(c);
@@ -465,10 +461,22 @@ moe_status moe_dispatch(const moe_config* c, const void* x, const int32_t* topk_
     int32_t* bbase = at<int32_t>(ws, L.blockbase);
     const float* P = (st && st->P) ? st->P : at<float>(ws, L.P_ws);
     moe::launch_histogram(topk_idx, na, E, hist, h);
-    moe::launch_scan(hist, nb, E, cap, bbase, expert_offsets, P, st, h);
+    moe::launch_scan(hist, nb, E, cap, bbase, expert_offsets, P, st, h, gu, gd);
     moe::launch_scatter_permute(topk_idx, c->T, slots_of(c), E, bbase, expert_offsets, cap, x, c->d_model,
                                 elem_bytes(c), perm_src, slot_pos, x_perm, h);
     return after_launch();
+}
+
+moe_status moe_dispatch(const moe_config* c, const void* x, const int32_t* topk_idx, void* x_perm,
+                        int32_t* expert_offsets, int32_t* perm_src, int32_t* slot_pos, const moe_stats* st, void* ws,
+                        size_t ws_bytes, void* stream) {
+    moe_status s = moe_validate_config(c);
+    if (s != MOE_OK) return s;
+    if (!expert_offsets) return MOE_ERR_INVALID_ARG;
+    if (c->T > 0 && (!x || !topk_idx || !x_perm || !perm_src || !slot_pos)) return MOE_ERR_INVALID_ARG;
+    if ((s = check_ws(c, ws, ws_bytes)) != MOE_OK) return s;
+    return dispatch_stages(c, x, topk_idx, x_perm, expert_offsets, perm_src, slot_pos, st, ws, (hipStream_t)stream,
+                           nullptr, nullptr);
 }
 
 moe_status moe_dispatch_noalloc(const moe_config* c, const void* x, const int32_t* topk_idx, void* x_perm,
@@ -584,35 +592,56 @@ moe_status moe_expert_down(const moe_config* c, const void* hbuf, const int32_t*
                     (hipStream_t)stream);
 }
 
+// Tile plan geometry of the two expert GEMMs (up, down) of the layer, the
+// plans going to the workspace's plan_up / plan_down.
+static void ffn_plan_geoms(const moe_config* c, void* ws, moe::PlanGeom* gu, moe::PlanGeom* gd) {
+    const Layout L = compute_layout(c);
+    const int64_t R = max_rows_of(c);
+    const bool bf = is_bf16(c);
+    const int E = c->n_experts, d = c->d_model, F = c->d_ff;
+    const moe::GemmShape su = gemm_shape(c, true, false, R, E, F);
+    const moe::GemmShape sd = gemm_shape(c, false, false, R, E, F);
+    *gu = moe::plan_geom(bf, gemm_epi(c, true, false), F, d, su.BM, su.BN, at<int32_t>(ws, L.plan_up));
+    *gd = moe::plan_geom(bf, 0, d, F, sd.BM, sd.BN, at<int32_t>(ws, L.plan_down));
+}
+
+// The expert FFN on validated arguments; plans_ready: the dispatch scan has
+// already written both tile plans.
+static moe_status ffn_stages(const moe_config* c, const void* x_perm, const int32_t* expert_offsets,
+                             const moe_weights* w, void* y_perm, void* ws, hipStream_t h, bool plans_ready) {
+    const int64_t R = max_rows_of(c);
+    if (R == 0) return MOE_OK;
+    const Layout L = compute_layout(c);
+    void* H = at<void>(ws, L.H);
+    const bool bf = is_bf16(c);
+    const int E = c->n_experts, d = c->d_model, F = c->d_ff;
+    int32_t* pu = at<int32_t>(ws, L.plan_up);
+    int32_t* pd = at<int32_t>(ws, L.plan_down);
+    int32_t* pc = at<int32_t>(ws, L.plan_copy);
+    float* part = at<float>(ws, L.partial);
+    moe_status s;
+    if (!plans_ready) {
+        // both tile plans in one launch, then the two products
+        const moe::GemmShape gu = gemm_shape(c, true, false, R, E, F);
+        const moe::GemmShape gd = gemm_shape(c, false, false, R, E, F);
+        const hipError_t e = moe::launch_tile_plans(bf, expert_offsets, E, R, gemm_epi(c, true, false), F, d, gu.BM,
+                                                    gu.BN, pu, 0, d, F, gd.BM, gd.BN, pd, h);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    if ((s = run_gemm(c, true, x_perm, R, E, expert_offsets, w->w_gate, w->w_up, nullptr, F, H, pu, pc, part, h,
+                      nullptr, true)) != MOE_OK)
+        return s;
+    return run_gemm(c, false, H, R, E, expert_offsets, nullptr, nullptr, w->w_down, F, y_perm, pd, pc, part, h,
+                    nullptr, true);
+}
+
 moe_status moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* expert_offsets,
                           const moe_weights* w, void* y_perm, void* ws, size_t ws_bytes, void* stream) {
     moe_status s = moe_validate_config(c);
     if (s != MOE_OK) return s;
     if ((s = check_ffn_args(c, x_perm, expert_offsets, w, y_perm, true, true)) != MOE_OK) return s;
     if ((s = check_ws(c, ws, ws_bytes)) != MOE_OK) return s;
-    const int64_t R = max_rows_of(c);
-    if (R == 0) return MOE_OK;
-    const Layout L = compute_layout(c);
-    void* H = at<void>(ws, L.H);
-    // both tile plans in one launch, then the two products
-    const bool bf = is_bf16(c);
-    const int E = c->n_experts, d = c->d_model, F = c->d_ff;
-    const int epi_up = gemm_epi(c, true, false);
-    const moe::GemmShape gu = gemm_shape(c, true, false, R, E, F);
-    const moe::GemmShape gd = gemm_shape(c, false, false, R, E, F);
-    hipStream_t h = (hipStream_t)stream;
-    int32_t* pu = at<int32_t>(ws, L.plan_up);
-    int32_t* pd = at<int32_t>(ws, L.plan_down);
-    int32_t* pc = at<int32_t>(ws, L.plan_copy);
-    float* part = at<float>(ws, L.partial);
-    const hipError_t e = moe::launch_tile_plans(bf, expert_offsets, E, R, epi_up, F, d, gu.BM, gu.BN, pu, 0, d, F,
-                                                gd.BM, gd.BN, pd, h);
-    if (e != hipSuccess) return hip_status(e);
-    if ((s = run_gemm(c, true, x_perm, R, E, expert_offsets, w->w_gate, w->w_up, nullptr, F, H, pu, pc, part, h,
-                      nullptr, true)) != MOE_OK)
-        return s;
-    return run_gemm(c, false, H, R, E, expert_offsets, nullptr, nullptr, w->w_down, F, y_perm, pd, pc, part, h,
-                    nullptr, true);
+    return ffn_stages(c, x_perm, expert_offsets, w, y_perm, ws, (hipStream_t)stream, false);
 }
 
 moe_status moe_shared_expert(const moe_config* c, const void* x, const moe_weights* w, void* shared_out, void* ws,
@@ -669,9 +698,13 @@ moe_status moe_layer_forward(const moe_config* c, const moe_weights* w, const vo
     void* y_perm = at<void>(ws, L.y_perm);
     void* shared_out = c->n_shared ? at<void>(ws, L.shared_out) : nullptr;
     if ((s = moe_route(c, x, w, idx, gates, nullptr, st, ws, ws_bytes, stream)) != MOE_OK) return s;
-    if ((s = moe_dispatch(c, x, idx, x_perm, offsets, perm_src, slot_pos, st, ws, ws_bytes, stream)) != MOE_OK)
+    // the dispatch scan also writes the expert GEMMs' tile plans (one launch fewer)
+    moe::PlanGeom gu, gd;
+    ffn_plan_geoms(c, ws, &gu, &gd);
+    if ((s = dispatch_stages(c, x, idx, x_perm, offsets, perm_src, slot_pos, st, ws, (hipStream_t)stream, &gu,
+                             &gd)) != MOE_OK)
         return s;
-    if ((s = moe_expert_ffn(c, x_perm, offsets, w, y_perm, ws, ws_bytes, stream)) != MOE_OK) return s;
+    if ((s = ffn_stages(c, x_perm, offsets, w, y_perm, ws, (hipStream_t)stream, true)) != MOE_OK) return s;
     if (shared_out && (s = moe_shared_expert(c, x, w, shared_out, ws, ws_bytes, stream)) != MOE_OK) return s;
     const void* resid = (c->flags & MOE_F_ADD_RESIDUAL) ? x : nullptr;
     return moe_combine(c, y_perm, slot_pos, gates, resid, shared_out, out, stream);
