@@ -565,7 +565,8 @@ __global__ __launch_bounds__(512) void k_gemm_x256(XnParams p) {
     const int op = wave >> 2;
     const bool direct = NN && op == 0;
     const int cg = tid & 31, kq = (tid >> 5) & 7;
-    const int g_d = tid & 7, m0_d = (tid >> 3) & 31;
+    // (direct: 8 consecutive lanes take 8 consecutive rows m0 of one k-group)
+    const int m0_d = (tid & 7) | (((tid >> 6) & 3) << 3), g_d = (tid >> 3) & 7;
     constexpr int kRsrcWord3 = 0x00020000;
     __amdgpu_buffer_rsrc_t rs, rs1;
     uint32_t vo;
@@ -611,59 +612,60 @@ __global__ __launch_bounds__(512) void k_gemm_x256(XnParams p) {
                                        __builtin_amdgcn_raw_buffer_load_b128(rs, vo, (ch * KC + i) * row_bytes, 0));
         }
     };
-    // LDS layout of one operand in one buffer: row m (0..255) holds the 64
-    // k of the chunk as 8 groups of 8 (16 bytes), group g at slot
-    // g ^ (m & 7) ^ ((m >> 3) & 7).  (The swizzle g ^ ((m >> 1) & 7) makes
-    // the fragment reads conflict-free but not these transposed writes;
-    // measured on MI355X this one is the faster of the two.)
+    // LDS layout of one operand in one buffer (32 KB), in MFMA fragment
+    // order: the 16 bytes of tile row m, k-group g (k = 8 g .. 8 g + 7 of the
+    // chunk) sit in the 1 KB block 2 (m >> 4) + (g >> 2) at 16-byte position
+    //   16 (g & 3) + (m & 8) + ((m & 7) ^ ((m >> 3) & 7)).
+    // A fragment read (16 rows from R0, one k-step) is then one block, and
+    // each aligned group of 8 lanes reads one aligned 128 bytes; measured on
+    // MI355X with SQ_LDS_BANK_CONFLICT this read has no bank conflict, nor
+    // have the writes below, which put 8 consecutive lanes into 8 distinct
+    // 16-byte slots of 128-byte lines.  (The earlier row-major swizzle
+    // g ^ (m & 7) ^ ((m >> 3) & 7) cost 4 conflict cycles per fragment read.)
     //
-    // Staged writes: column j of the thread's 8 x 8 block goes to row
-    // m = 8 cg + jj, jj = j ^ p with p = (cg >> 3) & 1, so each 16 lanes of a
-    // store cover rows of both parities; the slot is kq ^ jj ^ (cg & 7).
-    const int pbit = (cg >> 3) & 1;
-    const uint32_t w_lane = (uint32_t)(cg * 1024);
-    const int w_x = (kq ^ (cg & 7)) & 7;           // slot = w_x ^ jj
-    // v_perm selectors: column jj takes the low (jj even) or high halves of
+    // Transposed writes: column j of the thread's 8 x 8 block is row
+    // m = 8 cg + j, group kq: block 2 (cg >> 1) + (kq >> 2), position
+    // 16 (kq & 3) + 8 (cg & 1) + (j ^ (cg & 7)).
+    const uint32_t w_lane = (uint32_t)((2 * (cg >> 1) + (kq >> 2)) * 1024 + 256 * (kq & 3) + 128 * (cg & 1));
+    const int w_x = cg & 7;
+    // v_perm selectors: column j takes the low (j even) or high halves of
     // rows 2q and 2q + 1
     const uint32_t sel_lo = 0x05040100u, sel_hi = 0x07060302u;
-    const uint32_t sel_j_even = pbit ? sel_hi : sel_lo, sel_j_odd = pbit ? sel_lo : sel_hi;
-    // Direct staging writes row m = m0 + 32 j, group g, at slot
-    // g ^ (m0 & 7) ^ (((m0 >> 3) + 4 j) & 7): the 8 lanes of a row cover its
-    // 8 slots.
-    const int d_x = g_d ^ (m0_d & 7);
+    // Direct writes: row m = m0 + 32 j, group g: block 2 (m0 >> 4) + 4 j +
+    // (g >> 2), position 16 (g & 3) + (m0 & 8) + ((m0 & 7) ^ x_j) with
+    // x_j = ((m0 >> 3) & 3) | ((j & 1) << 2).
+    const uint32_t d_lane = (uint32_t)((2 * (m0_d >> 4) + (g_d >> 2)) * 1024 + 256 * (g_d & 3) + 16 * (m0_d & 8));
+    const int d_x = (m0_d & 7) ^ ((m0_d >> 3) & 3);
     auto put_col = [&](int buf, int j) __attribute__((always_inline)) {
         if (direct) {
-            const int slot = d_x ^ (((m0_d >> 3) + 4 * j) & 7);
-            *(u32x4_t*)(lds + (size_t)(buf * 2) * OPB + (m0_d + 32 * j) * 128 + slot * 16) = st[j];
+            const uint32_t off = d_lane + (uint32_t)(j * 4096) + (uint32_t)((d_x ^ ((j & 1) << 2)) << 4);
+            *(u32x4_t*)(lds + (size_t)(buf * 2) * OPB + off) = st[j];
             return;
         }
-        const uint32_t sel = (j & 1) ? sel_j_odd : sel_j_even;
+        const uint32_t sel = (j & 1) ? sel_hi : sel_lo;
         u32x4_t v;
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = __builtin_amdgcn_perm(st[2 * q + 1][j >> 1], st[2 * q][j >> 1], sel);
-        const int jj = j ^ pbit;
-        const uint32_t off = w_lane + (uint32_t)(jj << 7) + (uint32_t)((w_x ^ jj) << 4);
+        const uint32_t off = w_lane + (uint32_t)((j ^ w_x) << 4);
         *(u32x4_t*)(lds + (size_t)(buf * 2 + op) * OPB + off) = v;
     };
-    // Fragment reads: row = R0 + (lane & 15) with R0 a multiple of 16, group
-    // g = 4 ks + (lane >> 4), so the slot is L ^ K with the lane part
-    // L = (lane >> 4) ^ (lane & 7) ^ ((lane >> 3) & 1) and the compile-time
-    // K = 4 ks ^ ((R0 >> 3) & 7) = 4 ks ^ ((2 blk) & 7).  The eight lane
-    // offsets (lane & 15) 128 + ((L ^ K) << 4) are formed once per chunk
-    // with the buffer base folded in; R0 128 and the operand base are
-    // immediates.
-    const int Lx = ((lane >> 4) ^ (lane & 7) ^ ((lane >> 3) & 1)) & 7;
-    const uint32_t r_lane = (uint32_t)((lane & 15) * 128);
-    uint32_t rb[8];
+    // Fragment reads: lane l takes row R0 + (l & 15), group 4 ks + (l >> 4),
+    // i.e. position 16 (l >> 4) + (l & 8) + ((l & 7) ^ (2 b | ((l >> 3) & 1)))
+    // of block 2 (R0 >> 4) + ks, with b = (R0 >> 4) & 3 known at compile time
+    // (the wave's row offsets are multiples of 64).  The four lane offsets are
+    // formed once per chunk with the buffer base folded in.
+    uint32_t rb[4];
     auto set_read_base = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int K = 0; K < 8; ++K) rb[K] = (uint32_t)(buf * 2 * OPB) + r_lane + (uint32_t)((Lx ^ K) << 4);
+        for (int bb = 0; bb < 4; ++bb)
+            rb[bb] = (uint32_t)(buf * 2 * OPB) +
+                     (uint32_t)(16 * (16 * (lane >> 4) + (lane & 8) + ((lane & 7) ^ ((2 * bb) | ((lane >> 3) & 1)))));
     };
     // buffer b: rb holds b's base; the other buffer is rb ^ (2 OPB)
     auto frag = [&](int other, int opf, int ks, int blk) __attribute__((always_inline)) {
-        const int K = (4 * ks) ^ ((2 * blk) & 7);
-        const int R0 = (opf == 0 ? wm * 64 : wn * 128) + blk * 16;
-        const uint32_t a = (other ? (rb[K] ^ (uint32_t)(2 * OPB)) : rb[K]) + (uint32_t)(opf * OPB + R0 * 128);
+        const int B = (opf == 0 ? wm * 4 : wn * 8) + blk;
+        const uint32_t r = rb[blk & 3];
+        const uint32_t a = (other ? (r ^ (uint32_t)(2 * OPB)) : r) + (uint32_t)(opf * OPB + (2 * B + ks) * 1024);
         return *(const u32x4_t*)(lds + a);
     };
     floatx4_t acc[8][4];
