@@ -13,11 +13,13 @@
 //                    g_a dY[t] and the gate gradient dg_a = <dY[t], y_perm[r]>
 //   k_bwd_act        SwiGLU / ReLU derivative: (dh, a, u) -> da | du and h
 //   k_gemm_tn        ragged-K grouped GEMM C_e = A_e^T B_e over the rows of
-//                    each expert: the expert weight gradients (MFMA)
+//                    each expert: the expert weight gradients (MFMA; bf16
+//                    256 x 256 tiles in k_gemm_wgrad, persistent)
 //   k_bwd_router     logit gradient dz of every token from dg and the gates
 //   k_bwd_dx         token gradient: residual + routed rows in slot order +
 //                    shared expert + dz W_r
-//   k_bwd_wr_part /
+//   k_bwd_wr_few /
+//   k_bwd_wr_mma /
 //   k_bwd_wr_sum     router gradients dW_r = dz^T x and db = sum_t dz, in a
 //                    fixed order over token chunks
 //
@@ -793,6 +795,267 @@ __global__ __launch_bounds__(512) void k_gemm_x256(XnParams p) {
 #endif
 }
 
+// Weight gradients, bf16, persistent: C_e = A_e^T B_e over the expert's
+// rows, 256 x 256 tiles as in k_gemm_x256 (same LDS layout, transposed
+// staging and per-chunk schedule), but one block per CU walks its tiles as
+// a single stream of 64-row chunks.  The loads two chunks ahead cross into
+// the next tile, so a tile's first chunks arrive while the previous tile is
+// still multiplying; at a tile's last chunk the block stages its outputs
+// through the LDS buffer that chunk has just released (each wave its own
+// 8 KB, 32 rows at a time), issues the stores and goes on with the next
+// tile, whose first chunk is already in the other buffer.  The stores drain
+// during the next tile's first chunk: the wait that ends that chunk's loads
+// is taken before they are issued.  Experts with fewer rows than a tile
+// need (or none) take one chunk that reads zeros.  Block b serves XCD b % 8;
+// the 32 blocks of an XCD take consecutive tiles of that XCD's range, so
+// concurrent tiles share an expert's rows in L2 as in the per-tile launch.
+__global__ __launch_bounds__(512) void k_gemm_wgrad(XnParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int BM = 256, KC = 64, GM = 4;
+    constexpr int OPB = BM * KC * 2;
+    __shared__ __align__(16) uint8_t lds[4 * OPB];
+    const int per_e = p.tiles_m * p.tiles_n;
+    const int ntiles = p.E * per_e;
+    const int per_xcd = (ntiles + 7) / 8;
+    const int xcd = blockIdx.x % 8, nslot = gridDim.x / 8;
+    const int t_end = min((xcd + 1) * per_xcd, ntiles);
+    const int t_first = xcd * per_xcd + (int)(blockIdx.x / 8);
+    if (t_first >= t_end) return;
+
+    // tile -> expert and 256 x 256 block of C_e, in groups of GM row tiles
+    // (the 32 CUs of an XCD run 4 row tiles x 8 column tiles at a time)
+    int te, tmb, tnb, tlo, trows;
+    auto decode = [&](int tile) __attribute__((always_inline)) {
+        const int e = tile / per_e;
+        const int L = tile - e * per_e;
+        const int grp = L / (GM * p.tiles_n);
+        const int gm = min(p.tiles_m - grp * GM, GM);
+        const int in = L - grp * GM * p.tiles_n;
+        te = __builtin_amdgcn_readfirstlane(e);
+        tmb = __builtin_amdgcn_readfirstlane((grp * GM + in % gm) * BM);
+        tnb = __builtin_amdgcn_readfirstlane((in / gm) * BM);
+        tlo = __builtin_amdgcn_readfirstlane(p.offsets[te]);
+        trows = __builtin_amdgcn_readfirstlane(p.offsets[te + 1]) - tlo;
+    };
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // load cursor: operand op (0: A, 1: B) of this thread, rows kq*8 .. +7
+    // of the chunk, columns cg*8 .. +7 of the tile
+    const int op = wave >> 2;
+    const int cg = tid & 31, kq = (tid >> 5) & 7;
+    const uint16_t* src = (const uint16_t*)(op == 0 ? p.A : p.B0);
+    const int64_t ld = op == 0 ? p.lda : p.ldb;
+    const int lim = op == 0 ? p.M : p.N;
+    const int row_bytes = (int)(ld * 2);
+    constexpr int kRsrcWord3 = 0x00020000;
+    int lt = t_first, lch = 0, lnch = 1;
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t vo;
+    auto load_setup = [&]() __attribute__((always_inline)) {
+        decode(lt);
+        lnch = max(1, (trows + KC - 1) / KC);
+        rs = __builtin_amdgcn_make_buffer_rsrc((void*)(src + (int64_t)tlo * ld), (short)0,
+                                               (int)((int64_t)trows * ld * 2), kRsrcWord3);
+        const int col = (op == 0 ? tmb : tnb) + cg * 8;
+        vo = col < lim ? (uint32_t)((kq * 8 * ld + col) * 2) : 0x80000000u;
+    };
+    auto advance_load = [&]() __attribute__((always_inline)) {
+        if (++lch == lnch) {
+            lch = 0;
+            lt += nslot;
+            if (lt < t_end) load_setup();
+        }
+    };
+    u32x4_t st[8];
+    auto load_row = [&](int i) __attribute__((always_inline)) {
+        st[i] = __builtin_bit_cast(u32x4_t,
+                                   __builtin_amdgcn_raw_buffer_load_b128(rs, vo, (lch * KC + i) * row_bytes, 0));
+    };
+    // LDS layout and transposed writes as in k_gemm_x256: the chunk of tile
+    // row m, k-group g in block 2 (m >> 4) + (g >> 2) at 16-byte position
+    // 16 (g & 3) + (m & 8) + ((m & 7) ^ ((m >> 3) & 7)).
+    const uint32_t w_lane = (uint32_t)((2 * (cg >> 1) + (kq >> 2)) * 1024 + 256 * (kq & 3) + 128 * (cg & 1));
+    const int w_x = cg & 7;
+    const uint32_t sel_lo = 0x05040100u, sel_hi = 0x07060302u;
+    auto put_col = [&](int buf, int j) __attribute__((always_inline)) {
+        const uint32_t sel = (j & 1) ? sel_hi : sel_lo;
+        u32x4_t v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = __builtin_amdgcn_perm(st[2 * q + 1][j >> 1], st[2 * q][j >> 1], sel);
+        *(u32x4_t*)(lds + (size_t)(buf * 2 + op) * OPB + w_lane + (uint32_t)((j ^ w_x) << 4)) = v;
+    };
+    uint32_t rb[4];
+    auto set_read_base = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+            rb[bb] = (uint32_t)(buf * 2 * OPB) +
+                     (uint32_t)(16 * (16 * (lane >> 4) + (lane & 8) + ((lane & 7) ^ ((2 * bb) | ((lane >> 3) & 1)))));
+    };
+    auto frag = [&](int other, int opf, int ks, int blk) __attribute__((always_inline)) {
+        const int B = (opf == 0 ? wm * 4 : wn * 8) + blk;
+        const uint32_t r = rb[blk & 3];
+        const uint32_t a = (other ? (r ^ (uint32_t)(2 * OPB)) : r) + (uint32_t)(opf * OPB + (2 * B + ks) * 1024);
+        return *(const u32x4_t*)(lds + a);
+    };
+    floatx4_t acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    auto bfrag = [&](int q) __attribute__((always_inline)) {
+        return q < 16 ? frag(0, 1, q >> 3, q & 7) : frag(1, 1, 0, q - 16);
+    };
+
+    // compute cursor: the tile whose chunks are being multiplied
+    int ct = t_first, cch = 0;
+    decode(ct);
+    int ce = te, cmb = tmb, cnb = tnb, cnch = max(1, (trows + KC - 1) / KC);
+    const bool staged = p.N % 8 == 0 && (((uintptr_t)p.C) & 15) == 0;
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    // outputs of the compute tile; buffer b is free (its last reads ended at
+    // the chunk's barrier) and holds 8 KB per wave: 32 rows of 256 bytes
+    // with 16-byte column group c of row r at slot c ^ (r & 15)
+    auto epilogue = [&](int b) __attribute__((always_inline)) {
+        uint16_t* Ce = (uint16_t*)p.C + (size_t)ce * p.M * p.N;
+        wait_vmcnt<0>();   // the loads of the chunk after next have landed before the stores join the count
+        if (staged) {
+            uint8_t* reg = lds + b * 2 * OPB + wave * 8192;
+            const int lr = lane >> 4, lc = lane & 15;
+            const int n = cnb + wn * 128 + lc * 8;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int ml = jj * 16 + lc;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int c = 2 * i + (lr >> 1);
+                        u32x2_t w;
+                        w[0] = pack_bf16x2(acc[i][2 * h + jj][0], acc[i][2 * h + jj][1]);
+                        w[1] = pack_bf16x2(acc[i][2 * h + jj][2], acc[i][2 * h + jj][3]);
+                        *(u32x2_t*)(reg + ml * 256 + ((c ^ lc) << 4) + (lr & 1) * 8) = w;
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int mr = 4 * r + lr;
+                    const u32x4_t v = *(const u32x4_t*)(reg + mr * 256 + ((lc ^ (mr & 15)) << 4));
+                    const int m = cmb + wm * 64 + h * 32 + mr;
+                    if (m < p.M && n < p.N) *(u32x4_t*)(Ce + (int64_t)m * p.N + n) = v;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = cmb + wm * 64 + j * 16 + (lane & 15);
+                if (m >= p.M) continue;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int n = cnb + wn * 128 + i * 16 + 4 * (lane >> 4);
+                    if (n >= p.N) continue;
+                    uint2 w;
+                    w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+                    w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+                    *(uint2*)(Ce + (int64_t)m * p.N + n) = w;
+                }
+            }
+        }
+        lds_barrier();   // every wave is done with buffer b before it is refilled
+    };
+
+    // prologue: stream chunk 0 into buffer 0, chunk 1 staged in registers
+    load_setup();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) load_row(i);
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) put_col(0, j);
+    advance_load();
+    if (lt < t_end) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) load_row(i);
+    }
+    advance_load();
+    lds_barrier();
+    set_read_base(0);
+    u32x4_t fa0[4], fa1[4], fb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fa0[j] = frag(0, 0, 0, j);
+    fb[0] = bfrag(0);
+    fb[1] = bfrag(1);
+    // stream chunk s (buffer b = s & 1): the schedule of k_gemm_x256, with
+    // the loads of stream chunk s + 2 in groups 2-5; the load cursor moves on
+    // at the end of the chunk
+    bool fresh = false;   // the chunk before ended a tile and waited for the loads
+    for (int s = 0;; ++s) {
+        const int b = s & 1;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int ks = q >> 3, i = q & 7;
+            if (ks == 0) {
+                if (i == 0 && !fresh) wait_vmcnt<0>();
+                if (i < 2) {
+#pragma unroll
+                    for (int j = 4 * i; j < 4 * i + 4; ++j) put_col(b ^ 1, j);
+                } else if (i < 6) {
+                    if (lt < t_end) {
+                        load_row(2 * (i - 2));
+                        load_row(2 * (i - 2) + 1);
+                    }
+                }
+                if (i >= 4) fa1[i - 4] = frag(0, 0, 1, i - 4);
+            } else if (i >= 6) {
+                fa0[2 * (i - 6)] = frag(1, 0, 0, 2 * (i - 6));
+                fa0[2 * (i - 6) + 1] = frag(1, 0, 0, 2 * (i - 6) + 1);
+            }
+            fb[(q + 2) % 4] = bfrag(q + 2);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fb[q % 4]),
+                                                                    __builtin_bit_cast(bf16x8_t, ks ? fa1[j] : fa0[j]),
+                                                                    acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q == 13) {
+                lds_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        fresh = false;
+        set_read_base(b ^ 1);
+        advance_load();
+        if (++cch == cnch) {
+            epilogue(b);
+            ct += nslot;
+            if (ct >= t_end) break;
+            decode(ct);
+            ce = te; cmb = tmb; cnb = tnb; cnch = max(1, (trows + KC - 1) / KC);
+            cch = 0;
+            fresh = true;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    }
+#endif
+}
+
+// Blocks of the persistent weight-gradient launch: the current device's CU
+// count, rounded down to a multiple of 8 (at least 8), read once per device.
+static int wgrad_blocks() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
+        cached[dev] = cus / 8 * 8;
+    }
+    return cached[dev];
+}
+
 hipError_t launch_gemm_tn(bool bf16, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int M, int N,
                           int E, const int32_t* offsets, int64_t max_rows, hipStream_t s) {
     // the 256 x 256 kernel addresses an expert's rows (plus two chunks of
@@ -808,8 +1071,9 @@ hipError_t launch_gemm_tn(bool bf16, const void* A, int64_t lda, const void* B, 
         const int64_t nt = (int64_t)E * p.tiles_m * p.tiles_n;
         if (nt <= 0) return hipSuccess;
         if (nt > 0x7fffffff - 8) return hipErrorInvalidValue;
-        const int64_t grid = (nt + 7) / 8 * 8;
-        hipLaunchKernelGGL(k_gemm_x256<false>, dim3((unsigned)grid), dim3(512), 0, s, p);
+        // one block per CU (128 KB of LDS each), a multiple of 8 blocks
+        const int64_t grid = (nt + 7) / 8 * 8 < wgrad_blocks() ? (nt + 7) / 8 * 8 : wgrad_blocks();
+        hipLaunchKernelGGL(k_gemm_wgrad, dim3((unsigned)grid), dim3(512), 0, s, p);
         return hipGetLastError();
     }
     TnParams p;
@@ -1057,15 +1321,12 @@ void launch_bwd_dx(bool bf16, const void* dy, const void* dx_perm, const int32_t
                            idx, w_router, E, d, residual, dx);
 }
 
-// Router gradients dW_r = dz^T x and db = sum_t dz, as a tiled product in
-// two fixed-order passes.  Block (expert group of 64, column chunk of 256,
-// token chunk q of 256 tokens): the chunk's dz columns go to LDS, each
-// thread owns one column c and the 64 experts of the group, and adds
-// dz[t][e] x[t][c] over the chunk's tokens in order (x is read once per
-// expert group, not once per expert); column d (thread c == d) sums dz for
-// the bias.  k_bwd_wr_sum then adds the chunks in order.
-constexpr int kWrTokens = 256;
-constexpr int kWrExperts = 64;
+// Router gradients dW_r = dz^T x and db = sum_t dz, in two fixed-order
+// passes: partial sums per token chunk, then k_bwd_wr_sum adds the chunks in
+// order.  Column d of a partial row is the bias (x read as 1 there).
+// More than 16 experts (k_bwd_wr_mma): chunks of 512 tokens on the fp32
+// matrix cores, blocks of 64 experts x 256 columns.
+constexpr int kWrTokens = 512;
 // Up to 16 experts (k_bwd_wr_few): 32-token chunks, each thread 8 columns
 // (one 16-byte load of bf16 x per token, or two of fp32) and every expert of
 // the call, so no multiply-add is spent on absent experts and x is read once.
@@ -1157,32 +1418,98 @@ __global__ __launch_bounds__(256) void k_bwd_wr_few(const float* __restrict__ dz
     }
 }
 
+// part[q][e][c] = sum over the tokens t of chunk q of dz[t][e] x[t][c], c <= d
+// (x[t][d] = 1), with v_mfma_f32_16x16x4_f32: at k-step s a lane supplies
+// token t0 + 4 s + (lane >> 4), expert e0 + 16 eb + (lane & 15) for block row
+// eb and column c0 + 16 cb + (lane & 15) for block column cb; the wave's
+// 4 x 4 blocks cover 64 experts x 64 columns, the block's 4 waves 256
+// columns.  Each output lands on a lane as C[4 (lane >> 4) + i][lane & 15],
+// so a store covers 4 rows of 64 contiguous bytes.  Tokens are added in
+// k-step order, four per MFMA, so the partials do not depend on the launch.
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_bwd_wr_part(const float* __restrict__ dz, const void* __restrict__ x, int T,
-                                                     int E, int d, float* __restrict__ part) {
-    __shared__ float zs[kWrTokens][kWrExperts];
-    const int e0 = blockIdx.y * kWrExperts, q = blockIdx.z;
-    const int c = blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(256) void k_bwd_wr_mma(const float* __restrict__ dz, const void* __restrict__ x, int T,
+                                                    int E, int d, float* __restrict__ part) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int KG = 4;   // k-steps per loop turn (16 tokens)
+    const int e0 = blockIdx.x * 64, q = blockIdx.z;
+    const int lane = threadIdx.x & 63, r = lane & 15, kk = lane >> 4;
+    const int c0 = blockIdx.y * 256 + (threadIdx.x >> 6) * 64;
     const int t0 = q * kWrTokens, nt = min(T - t0, kWrTokens);
-    const int ne = min(E - e0, kWrExperts);
-    for (int i = threadIdx.x; i < kWrTokens * kWrExperts; i += 256) {
-        const int tt = i / kWrExperts, ee = i - tt * kWrExperts;
-        zs[tt][ee] = (tt < nt && ee < ne) ? dz[(int64_t)(t0 + tt) * E + e0 + ee] : 0.0f;
-    }
-    __syncthreads();
-    float acc[kWrExperts];
+    // loads through buffer descriptors over the chunk's rows: experts past E,
+    // columns past d - 1 and tokens past the chunk read zeros; the bias
+    // column d adds 1 for each token of the chunk
+    constexpr int kRsrcWord3 = 0x00020000;
+    constexpr int XB = BF16 ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(dz + (int64_t)t0 * E), (short)0, nt * E * 4, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)x + (int64_t)t0 * d * XB), (short)0, nt * d * XB, kRsrcWord3);
+    uint32_t zo[4], xo[4];
+    float c1[4];
 #pragma unroll
-    for (int ee = 0; ee < kWrExperts; ++ee) acc[ee] = 0.0f;
-    for (int tt = 0; tt < nt; ++tt) {
-        const float xv = c < d ? load_act<BF16>(x, (int64_t)(t0 + tt) * d + c) : 1.0f;
-#pragma unroll
-        for (int ee = 0; ee < kWrExperts; ++ee) acc[ee] += zs[tt][ee] * xv;
+    for (int u = 0; u < 4; ++u) {
+        const int e = e0 + 16 * u + r, c = c0 + 16 * u + r;
+        zo[u] = e < E ? (uint32_t)((kk * E + e) * 4) : 0x80000000u;
+        xo[u] = c < d ? (uint32_t)((kk * d + c) * XB) : 0x80000000u;
+        c1[u] = c == d ? 1.0f : 0.0f;
     }
-    if (c <= d) {
+    floatx4_t acc[4][4];
 #pragma unroll
-        for (int ee = 0; ee < kWrExperts; ++ee)
-            if (ee < ne) part[((int64_t)q * E + e0 + ee) * (d + 1) + c] = acc[ee];
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float fa0[KG][4], fb0[KG][4], fa1[KG][4], fb1[KG][4];
+    auto load = [&](float (&fa)[KG][4], float (&fb)[KG][4], int s0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < KG; ++g) {
+            const int tk = 4 * (s0 + g);   // first token of the k-step in the chunk
+            const bool tv = tk + kk < nt;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                fa[g][u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, zo[u], tk * E * 4, 0));
+                float xv;
+                if constexpr (BF16)
+                    xv = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rx, xo[u], tk * d * 2, 0)
+                                         << 16);
+                else
+                    xv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, xo[u], tk * d * 4, 0));
+                fb[g][u] = xv + (tv ? c1[u] : 0.0f);
+            }
+        }
+    };
+    auto mma = [&](const float (&fa)[KG][4], const float (&fb)[KG][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < KG; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[g][i], fb[g][j], acc[i][j], 0, 0, 0);
+    };
+    // k-steps past the chunk hold zeros; the next KG k-steps load during the
+    // current ones
+    const int nsteps = (nt + 3) / 4;
+    load(fa0, fb0, 0);
+    for (int s0 = 0; s0 < nsteps; s0 += 2 * KG) {
+        if (s0 + KG < nsteps) load(fa1, fb1, s0 + KG);
+        mma(fa0, fb0);
+        if (s0 + KG >= nsteps) break;
+        if (s0 + 2 * KG < nsteps) load(fa0, fb0, s0 + 2 * KG);
+        mma(fa1, fb1);
     }
+    float* pq = part + (int64_t)q * E * (d + 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int e = e0 + 16 * i + 4 * kk + v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = c0 + 16 * j + r;
+                if (e < E && c <= d) pq[(int64_t)e * (d + 1) + c] = acc[i][j][v];
+            }
+        }
+#endif
 }
 
 __global__ __launch_bounds__(256) void k_bwd_wr_sum(const float* __restrict__ part, int nq, int E, int d,
@@ -1222,9 +1549,9 @@ void launch_bwd_wr(bool bf16, const float* dz, const void* x, int T, int E, int 
             else hipLaunchKernelGGL((k_bwd_wr_few<16, false>), grid, dim3(256), 0, s, dz, x, T, E, d, part);
         }
     } else if (nq > 0) {
-        const dim3 grid((d + 1 + 255) / 256, (E + kWrExperts - 1) / kWrExperts, nq);
-        if (bf16) hipLaunchKernelGGL(k_bwd_wr_part<true>, grid, dim3(256), 0, s, dz, x, T, E, d, part);
-        else hipLaunchKernelGGL(k_bwd_wr_part<false>, grid, dim3(256), 0, s, dz, x, T, E, d, part);
+        const dim3 grid((E + 63) / 64, (d + 1 + 255) / 256, nq);
+        if (bf16) hipLaunchKernelGGL(k_bwd_wr_mma<true>, grid, dim3(256), 0, s, dz, x, T, E, d, part);
+        else hipLaunchKernelGGL(k_bwd_wr_mma<false>, grid, dim3(256), 0, s, dz, x, T, E, d, part);
     }
     const int64_t n = (int64_t)E * (d + 1);
     hipLaunchKernelGGL(k_bwd_wr_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, nq, E, d, dw, db);

@@ -844,6 +844,8 @@ moe_status moe_layer_backward(const moe_config* c, const moe_weights* w, const v
     const int T = c->T, E = c->n_experts, d = c->d_model;
     const int64_t R = max_rows_of(c);
     if (!hashed && !w->w_router) return MOE_ERR_INVALID_ARG;
+    // the router gradient reads 512-token chunks of x with 32-bit byte offsets
+    if (!hashed && (int64_t)512 * d * 4 >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     if (!sv->expert_offsets) return MOE_ERR_INVALID_ARG;
     if (T > 0 && (!x || !dy || !g->dx || !sv->topk_idx || !sv->topk_gate || !sv->slot_pos)) return MOE_ERR_INVALID_ARG;
     if (R > 0 && (!sv->perm_src || !sv->x_perm || !sv->y_perm)) return MOE_ERR_INVALID_ARG;
