@@ -476,9 +476,9 @@ __global__ __launch_bounds__(256) void k_gemm_tn(TnParams p) {
 }
 
 // Parameters of the two 256 x 256 bf16 products below.
-//   TN (weight gradients): C_e[M][N] = sum over the expert's rows r of
+//   TN (weight gradients, k_gemm_wgrad): C_e[M][N] = sum over the expert's rows r of
 //       A[r][m] B[r][n] (A, B row-major, m / n contiguous), C_e at e M N.
-//   NN (input gradients without weight transposes): C[r][n] = sum_k
+//   NN (input gradients without weight transposes, k_gemm_nn256): C[r][n] = sum_k
 //       A[r][k] B_e[k][n] for the rows r of expert e (ragged), A row-major
 //       with k contiguous, B_e = B0 + e bstride for k < K1 and
 //       B1 + e bstride (row k - K1) beyond, both [rows][N] with n contiguous;
@@ -498,34 +498,31 @@ struct XnParams {
     const int32_t* prefix;
 };
 
-// bf16, 256 x 256 tiles, 512 threads: 8 waves of 64 (m) x 128 (n), so a
-// wave holds 128 accumulator registers and two waves share each SIMD;
-// chunks of 64 rows through two LDS buffers of 64 KB.  Threads 0-255 stage
-// an 8 x 8 block of A per chunk, threads 256-511 one of B, and write it
-// transposed into LDS (the schedule is given at the main loop).  Chunks past
-// the expert's rows read zeros (outside the buffer descriptor's range), so
-// the loop body has no branches.  Blocks map to tiles XCD by XCD, so the
-// tiles of one XCD share an expert's rows in L2.
-template <bool NN>
-__global__ __launch_bounds__(512) void k_gemm_x256(XnParams p) {
+// NN product, bf16, 256 x 256 tiles, 512 threads: 8 waves of 64 (m) x 128
+// (n), so a wave holds 128 accumulator registers and two waves share each
+// SIMD; chunks of 64 k through two LDS buffers of 64 KB.  Threads 0-255
+// stage 8 rows x one k-group of A per chunk as they are, threads 256-511 an
+// 8 x 8 block of B, written transposed into LDS (the schedule is given at
+// the main loop).  Weight rows past K1 come from B1.  Blocks map to tiles
+// XCD by XCD, so the tiles of one XCD share an expert's weights in L2.
+__global__ __launch_bounds__(512) void k_gemm_nn256(XnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int BM = 256, KC = 64;
     constexpr int OPB = BM * KC * 2;
     // staged output: 8 waves x 64 rows of 256 bytes, rows padded by 16 bytes
     constexpr int SPITCH = 128 * 2 + 16, SBYTES = 8 * 64 * SPITCH;
     __shared__ __align__(16) uint8_t lds[2 * 2 * OPB > SBYTES ? 2 * 2 * OPB : SBYTES];
-    // tiles: TN, E x tiles_m x tiles_n; NN, (sum of the experts' row tiles)
-    // x tiles_n.  Groups of GM row tiles: the 32 CUs of an XCD run 4 row
+    // tiles: (sum of the experts' row tiles) x tiles_n.  Groups of GM row tiles: the 32 CUs of an XCD run 4 row
     // tiles x 8 column tiles at a time, so each staged chunk of A is fetched
     // once per 8 tiles and each chunk of B once per 4.
     constexpr int GM = 4;
-    const int mt_all = NN ? p.prefix[p.E] : p.E * p.tiles_m;
+    const int mt_all = p.prefix[p.E];
     const int ntiles = mt_all * p.tiles_n;
     const int per_xcd = (ntiles + 7) / 8;
     const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (tile >= ntiles) return;
     int e, tm, tn;
-    if constexpr (NN) {
+    {
         const int grp = tile / (GM * p.tiles_n);
         const int gm = min(mt_all - grp * GM, GM);
         const int in = tile - grp * GM * p.tiles_n;
@@ -538,34 +535,25 @@ __global__ __launch_bounds__(512) void k_gemm_x256(XnParams p) {
         }
         e = lo_e;
         tm = mt - p.prefix[e];
-    } else {
-        const int per_e = p.tiles_m * p.tiles_n;
-        e = tile / per_e;
-        const int L = tile - e * per_e;
-        const int grp = L / (GM * p.tiles_n);
-        const int gm = min(p.tiles_m - grp * GM, GM);
-        const int in = L - grp * GM * p.tiles_n;
-        tm = grp * GM + in % gm;
-        tn = in / gm;
     }
     e = __builtin_amdgcn_readfirstlane(e);
     tm = __builtin_amdgcn_readfirstlane(tm);
     tn = __builtin_amdgcn_readfirstlane(tn);
     const int lo = p.offsets[e], hi = p.offsets[e + 1];
-    // TN: m_base is a column of A; NN: the first row of the tile
-    const int m_base = NN ? lo + tm * BM : tm * BM, n_base = tn * BM;
-    const int rows_tile = NN ? min(BM, hi - m_base) : BM;
+    // first row of the tile
+    const int m_base = lo + tm * BM, n_base = tn * BM;
+    const int rows_tile = min(BM, hi - m_base);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int nch = NN ? p.K / KC : (hi - lo + KC - 1) / KC;
+    const int nch = p.K / KC;
 
     // staging: operand op (0: A, 1: B) of this thread.  Transposed staging
-    // (TN both operands, NN the weights): rows kq*8 .. +7 of the chunk,
-    // columns cg*8 .. +7 of the tile.  Direct staging (NN activations): row
-    // m0 + 32 i (i = 0..7) of the tile, k-group g of the chunk.
+    // (the weights): rows kq*8 .. +7 of the chunk, columns cg*8 .. +7 of the
+    // tile.  Direct staging (the activations): row m0 + 32 i (i = 0..7) of
+    // the tile, k-group g of the chunk.
     const int op = wave >> 2;
-    const bool direct = NN && op == 0;
+    const bool direct = op == 0;
     const int cg = tid & 31, kq = (tid >> 5) & 7;
     // (direct: 8 consecutive lanes take 8 consecutive rows m0 of one k-group)
     const int m0_d = (tid & 7) | (((tid >> 6) & 3) << 3), g_d = (tid >> 3) & 7;
@@ -573,7 +561,6 @@ __global__ __launch_bounds__(512) void k_gemm_x256(XnParams p) {
     __amdgpu_buffer_rsrc_t rs, rs1;
     uint32_t vo;
     int row_bytes;
-    if constexpr (NN) {
         if (op == 0) {
             rs = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.A + (int64_t)m_base * p.lda), (short)0,
                                                    (int)((int64_t)rows_tile * p.lda * 2), kRsrcWord3);
@@ -590,23 +577,12 @@ __global__ __launch_bounds__(512) void k_gemm_x256(XnParams p) {
             vo = col < p.N ? (uint32_t)((kq * 8 * p.ldb + col) * 2) : 0x80000000u;
             row_bytes = (int)(p.ldb * 2);
         }
-    } else {
-        const void* src = op == 0 ? p.A : p.B0;
-        const int64_t ld = op == 0 ? p.lda : p.ldb;
-        const int col = (op == 0 ? m_base : n_base) + cg * 8;
-        const int lim = op == 0 ? p.M : p.N;
-        rs = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)src + (int64_t)lo * ld), (short)0,
-                                               (int)((int64_t)(hi - lo) * ld * 2), kRsrcWord3);
-        rs1 = rs;
-        vo = col < lim ? (uint32_t)((kq * 8 * ld + col) * 2) : 0x80000000u;
-        row_bytes = (int)(ld * 2);
-    }
     u32x4_t st[8];
     auto load_row = [&](int ch, int i) __attribute__((always_inline)) {
         if (direct) {
             st[i] = __builtin_bit_cast(u32x4_t,
                                        __builtin_amdgcn_raw_buffer_load_b128(rs, vo, i * 32 * row_bytes + ch * KC * 2, 0));
-        } else if (NN && ch * KC >= p.K1) {
+        } else if (ch * KC >= p.K1) {
             st[i] = __builtin_bit_cast(
                 u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs1, vo, (ch * KC - p.K1 + i) * row_bytes, 0));
         } else {
@@ -741,8 +717,8 @@ __global__ __launch_bounds__(512) void k_gemm_x256(XnParams p) {
         set_read_base(b ^ 1);
     }
     // lane holds C[m][n .. n+3] of block (n-block i, m-block j)
-    uint16_t* Ce = NN ? (uint16_t*)p.C + (int64_t)m_base * p.ldc : (uint16_t*)p.C + (size_t)e * p.M * p.N;
-    const int64_t ldc = NN ? p.ldc : p.N;
+    uint16_t* Ce = (uint16_t*)p.C + (int64_t)m_base * p.ldc;
+    const int64_t ldc = p.ldc;
     if (ldc % 8 == 0 && p.N % 8 == 0 && (((uintptr_t)Ce) & 15) == 0) {
         // through LDS, so every global store covers whole 128-byte lines (a
         // lane's direct 8-byte stores leave each instruction 32 bytes of 16
@@ -772,16 +748,15 @@ __global__ __launch_bounds__(512) void k_gemm_x256(XnParams p) {
             const int mr = r + lr;
             const u32x4_t v = *(const u32x4_t*)(reg + mr * SPITCH + lc * 16);
             const int ml = wm * 64 + mr;
-            if ((NN ? ml < rows_tile : m_base + ml < p.M) && n < p.N)
-                *(u32x4_t*)(Ce + (int64_t)(NN ? ml : m_base + ml) * ldc + n) = v;
+            if (ml < rows_tile && n < p.N) *(u32x4_t*)(Ce + (int64_t)ml * ldc + n) = v;
         }
         return;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int ml = wm * 64 + j * 16 + (lane & 15);
-        if (NN ? ml >= rows_tile : m_base + ml >= p.M) continue;
-        const int m = NN ? ml : m_base + ml;
+        if (ml >= rows_tile) continue;
+        const int m = ml;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int n = n_base + wn * 128 + i * 16 + 4 * (lane >> 4);
@@ -796,7 +771,7 @@ __global__ __launch_bounds__(512) void k_gemm_x256(XnParams p) {
 }
 
 // Weight gradients, bf16, persistent: C_e = A_e^T B_e over the expert's
-// rows, 256 x 256 tiles as in k_gemm_x256 (same LDS layout, transposed
+// rows, 256 x 256 tiles as in k_gemm_nn256 (same LDS layout, transposed
 // staging and per-chunk schedule), but one block per CU walks its tiles as
 // a single stream of 64-row chunks.  The loads two chunks ahead cross into
 // the next tile, so a tile's first chunks arrive while the previous tile is
@@ -873,7 +848,7 @@ __global__ __launch_bounds__(512) void k_gemm_wgrad(XnParams p) {
         st[i] = __builtin_bit_cast(u32x4_t,
                                    __builtin_amdgcn_raw_buffer_load_b128(rs, vo, (lch * KC + i) * row_bytes, 0));
     };
-    // LDS layout and transposed writes as in k_gemm_x256: the chunk of tile
+    // LDS layout and transposed writes as in k_gemm_nn256: the chunk of tile
     // row m, k-group g in block 2 (m >> 4) + (g >> 2) at 16-byte position
     // 16 (g & 3) + (m & 8) + ((m & 7) ^ ((m >> 3) & 7)).
     const uint32_t w_lane = (uint32_t)((2 * (cg >> 1) + (kq >> 2)) * 1024 + 256 * (kq & 3) + 128 * (cg & 1));
@@ -985,7 +960,7 @@ __global__ __launch_bounds__(512) void k_gemm_wgrad(XnParams p) {
     for (int j = 0; j < 4; ++j) fa0[j] = frag(0, 0, 0, j);
     fb[0] = bfrag(0);
     fb[1] = bfrag(1);
-    // stream chunk s (buffer b = s & 1): the schedule of k_gemm_x256, with
+    // stream chunk s (buffer b = s & 1): the schedule of k_gemm_nn256, with
     // the loads of stream chunk s + 2 in groups 2-5; the load cursor moves on
     // at the end of the chunk
     bool fresh = false;   // the chunk before ended a tile and waited for the loads
@@ -1140,7 +1115,7 @@ hipError_t launch_gemm_nn(const void* A, int64_t lda, const void* B0, const void
     const int64_t nt = mt_ub * p.tiles_n;
     if (nt > 0x7fffffff - 8) return hipErrorInvalidValue;
     const int64_t grid = (nt + 7) / 8 * 8;
-    hipLaunchKernelGGL(k_gemm_x256<true>, dim3((unsigned)grid), dim3(512), 0, s, p);
+    hipLaunchKernelGGL(k_gemm_nn256, dim3((unsigned)grid), dim3(512), 0, s, p);
     return hipGetLastError();
 }
 
