@@ -57,6 +57,13 @@ CASES = {
     # the shared expert: one group of T rows (offsets built by the plan launch)
     "bf16_km_shared": dict(T=640, d=256, F=256, E=8, k=2, act_dtype="bf16", act="swiglu", gate="sigmoid_bias",
                            sel_bias=True, n_shared=1, F_shared=512, seed=212),
+    # more than 16 experts: the router weight gradient on the matrix cores with
+    # a partial block of experts (100 = 64 + 36), of columns (d + 1 = 321 =
+    # 256 + 65, the bias column in the tail) and of tokens (1000 = 512 + 488)
+    "f32_router_grad_e100": dict(T=1000, d=320, F=128, E=100, k=2, act_dtype="f32", act="swiglu",
+                                 gate="softmax_full", seed=213),
+    "bf16_router_grad_e100": dict(T=1000, d=320, F=128, E=100, k=2, act_dtype="bf16", act="relu",
+                                  gate="softmax_topk", logit_bias="zipf", seed=214),
 }
 
 
