@@ -425,7 +425,9 @@ moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
  *   dW_r = sum_t dz_t x_t^T, dlogit_bias = sum_t dz_t;
  *   dx_t = [residual] dY_t + sum_j dx_{r(t,j)} + shared expert + dz_t W_r.
  * Supported gates: SOFTMAX_TOPK, SOFTMAX_FULL, SIGMOID_BIAS, EXPERT_CHOICE,
- * HASH; the others and MOE_F_REROUTE return MOE_ERR_UNSUPPORTED.  All sums
+ * HASH; the others and MOE_F_REROUTE return MOE_ERR_UNSUPPORTED, as does a
+ * router gradient with d_model >= 2^20 (its 512-token chunks of x are
+ * addressed with 32-bit byte offsets).  All sums
  * are fp32 in fixed orders (bitwise reproducible); intermediates (dy_r, a,
  * u, dh, da, du, h, dx_r) are stored in the act dtype.
  *   x [T][d]: the forward input; w: the forward weights; sv: the saved
