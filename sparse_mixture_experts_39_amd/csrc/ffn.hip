@@ -363,9 +363,6 @@ struct GemmEpilogue {
     static constexpr int PITCH = OC * 2 + 16;                  // LDS bytes per staged row
     static constexpr int STAGE_BYTES = NW * WM * PITCH;
     static constexpr bool can_stage = BF16 && MB == 16 && !epi_save(EPI) && (OC * 2) % 16 == 0 && 64 % (OC * 2 / 16) == 0;
-    __device__ static bool stage_ok(const GemmParams& p) {
-        return (p.ldc % 8) == 0 && (((uintptr_t)p.C) & 15) == 0;
-    }
     __device__ static void store_staged(const GemmParams& p, const acc_t (&acc)[FN][FM], int row0, int rows, int nt,
                                         int wm, int wn, int lane, int wave, lds_u8* lds) {
         typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -419,8 +416,12 @@ struct GemmEpilogue {
 // One tile of the grouped GEMM (rows [t.row0, t.row0 + t.rows) of expert
 // t.e, column tile t.nt, K slices [k0, k1)); `lds` is the kernel's LDS.
 // unit >= 0: a split unit, which stores its fp32 partial accumulators.
-// KM: operand layout (KM_NONE or KM_B; see swzk).
-template <bool BF16, int BM, int BN, int EPI, int WGN, int KM = KM_NONE>
+// KM: operand layout (KM_NONE or KM_B; see swzk).  STG: the output goes
+// through LDS (epilogues that can stage, and C / ldc aligned for it, checked
+// by the host); the direct-store form is a separate instantiation because
+// compiled into the same kernel it raises the register demand past the file
+// and the compiler spills accumulators around the epilogue.
+template <bool BF16, int BM, int BN, int EPI, int WGN, int KM = KM_NONE, bool STG = false>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, lds_u8* lds, const TileDesc& t, int k0, int k1,
                                           int unit) {
     constexpr int NW = 2 * WGN;               // waves: 2 along M, WGN along N
@@ -748,16 +749,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, lds_u8* lds, cons
 
     if (unit >= 0) {
         Epi::store_partial(p, acc, unit, wave, lane);
-    } else if constexpr (Epi::can_stage) {
+    } else if constexpr (Epi::can_stage && STG) {
         static_assert(Epi::STAGE_BYTES <= RD.bytes, "staged output fits in the ring's LDS");
-        if (Epi::stage_ok(p)) {
-            // every wave is past its last fragment read and its slice loads
-            // have landed: the ring's LDS is free for the staged output
-            lds_barrier();
-            Epi::store_staged(p, acc, row0, rows, nt, wm, wn, lane, wave, lds);
-        } else {
-            Epi::store(p, acc, row0, rows, nt, wm, wn, lane);
-        }
+        // every wave is past its last fragment read and its slice loads have
+        // landed: the ring's LDS is free for the staged output
+        lds_barrier();
+        Epi::store_staged(p, acc, row0, rows, nt, wm, wn, lane, wave, lds);
     } else {
         Epi::store(p, acc, row0, rows, nt, wm, wn, lane);
     }
@@ -783,7 +780,7 @@ constexpr int gemm_lds_bytes() {
 // u % split of tail tile u / split; being dispatched last, they fill the CUs
 // that the last round of whole tiles leaves idle.  Remainder tiles
 // (256-row bf16 launches of 4 waves) run with 64-row tiles.
-template <bool BF16, int BM, int BN, int EPI, int WGN, int KM = KM_NONE>
+template <bool BF16, int BM, int BN, int EPI, int WGN, int KM = KM_NONE, bool STG = false>
 __global__ __launch_bounds__(128 * WGN) void k_grouped_gemm(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     __shared__ __align__(16) uint8_t lds_mem[gemm_lds_bytes<BF16, BM, BN, WGN>()];
@@ -809,11 +806,11 @@ __global__ __launch_bounds__(128 * WGN) void k_grouped_gemm(GemmParams p) {
     const TileDesc t = decode_tile(p, L, BM);
     if constexpr (BF16 && BM == 256 && WGN == 2) {
         if (t.rem) {
-            gemm_tile<BF16, kRemBM, BN, EPI, 2, KM>(p, lds, t, k0, k1, unit);
+            gemm_tile<BF16, kRemBM, BN, EPI, 2, KM, STG>(p, lds, t, k0, k1, unit);
             return;
         }
     }
-    gemm_tile<BF16, BM, BN, EPI, WGN, KM>(p, lds, t, k0, k1, unit);
+    gemm_tile<BF16, BM, BN, EPI, WGN, KM, STG>(p, lds, t, k0, k1, unit);
 #endif
 }
 
@@ -996,8 +993,16 @@ static void launch_pair(const GemmParams& p0, int grid, bool may_split, hipStrea
     typedef GemmEpilogue<BF16, BM, BN, EPI, 2, WGN> Epi;
     GemmParams p = p0;
     p.main_blocks = grid;
-    hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, WGN, KM>), dim3(grid + (may_split ? kSplitUnits : 0)),
-                       dim3(128 * WGN), 0, s, p);
+    const dim3 g(grid + (may_split ? kSplitUnits : 0)), b(128 * WGN);
+    // the staged-output instantiation where the epilogue can stage and C
+    // and ldc allow 16-byte row stores
+    bool staged = false;
+    if constexpr (Epi::can_stage) staged = p.ldc % 8 == 0 && ((uintptr_t)p.C & 15) == 0;
+    if (staged) {
+        if constexpr (Epi::can_stage) hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, WGN, KM, true>), g, b, 0, s, p);
+    } else {
+        hipLaunchKernelGGL((k_grouped_gemm<BF16, BM, BN, EPI, WGN, KM, false>), g, b, 0, s, p);
+    }
     if (!may_split) return;
     constexpr int groups = Epi::FN / Epi::IG;
     hipLaunchKernelGGL((k_split_fixup<BF16, BM, BN, EPI, 2, WGN>), dim3(kSplitUnits / 2 * Epi::NW * groups), dim3(64),

@@ -342,6 +342,44 @@ def test_expert_ffn_remainder_tiles(act):
         H.assert_close_rel(H.as_f64(y[lo:hi]), ref, "bf16", f"expert {e} ({hi - lo} rows)")
 
 
+@pytest.mark.parametrize("act", ["swiglu", "relu"])
+def test_expert_gemms_unaligned_outputs_bitwise(act):
+    """Outputs whose rows cannot be stored 16 bytes at a time (the buffer
+    starts 2 bytes past a 16-byte boundary) go through the direct-store
+    instantiation of the grouped GEMM instead of the LDS-staged one; both
+    must write the same bits."""
+    E = len(REM_COUNTS)
+    cfg = Config("unal_" + act, T=2700, d=512, F=512, E=E, k=2, act_dtype="bf16", act=act,
+                 gate="softmax_topk", seed=32)
+    c = H.bind_config(cfg)
+    R = moe.max_rows(c)
+    inp = workloads.make_inputs(cfg)
+    d = H.to_device(inp)
+    w = moe.weights_from(c, d)
+    ws = moe.workspace(c)
+    x_perm = torch.cat([d["x"], d["x"]])[:R].contiguous()
+    off = np.concatenate([[0], np.cumsum(REM_COUNTS)]).astype(np.int32)
+    offsets = torch.from_numpy(off).to("cuda")
+    kept = int(off[-1])
+
+    def unaligned(rows, cols):
+        t = torch.full((rows * cols + 1,), float("nan"), dtype=torch.bfloat16, device="cuda")[1:].view(rows, cols)
+        assert t.data_ptr() % 16 == 2
+        return t
+
+    H.log(f"[unaligned] {act}: expert_up / expert_down, aligned and 2-byte-offset outputs")
+    h_a = torch.zeros((R, cfg.F), dtype=torch.bfloat16, device="cuda")
+    y_a = torch.zeros((R, cfg.d), dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_up(c, x_perm, offsets, w, h_a, ws)
+    moe.moe_expert_down(c, h_a, offsets, w, y_a, ws)
+    h_u, y_u = unaligned(R, cfg.F), unaligned(R, cfg.d)
+    moe.moe_expert_up(c, x_perm, offsets, w, h_u, ws)
+    moe.moe_expert_down(c, h_a, offsets, w, y_u, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(h_a[:kept].view(torch.int16), h_u[:kept].view(torch.int16)), "h differs"
+    assert torch.equal(y_a[:kept].view(torch.int16), y_u[:kept].view(torch.int16)), "y differs"
+
+
 def test_nonfinite_input_sets_device_status():
     cfg = Config("nan", T=64, d=64, F=64, E=8, k=2, act_dtype="f32", act="relu", gate="softmax_topk", seed=2)
     inp = workloads.make_inputs(cfg)
