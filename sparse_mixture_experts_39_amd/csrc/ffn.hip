@@ -12,7 +12,10 @@
 //
 // Kernel design (one kernel template, k_grouped_gemm):
 //   * 256 threads = 4 waves in a 2x2 grid; a block computes a BM x BN tile,
-//     each wave a (BM/2) x (BN/2) tile of MFMA blocks.
+//     each wave a (BM/2) x (BN/2) tile of MFMA blocks.  The 256 x 256 bf16
+//     tiles of the forward products use 8 waves instead (gemm_tile_pp): two
+//     per SIMD in two groups that alternate between reading a slice and
+//     multiplying it, so one wave's MFMAs cover the other's waits.
 //   * MFMA operand order: the weights are source 0 and the activations
 //     source 1, so the accumulator lanes hold 4 consecutive output columns of
 //     one row and the epilogue stores 8 (bf16) or 16 (fp32) bytes per lane.
@@ -115,11 +118,12 @@ struct GemmParams {
 #ifndef MOE_GEMM_REM
 #define MOE_GEMM_REM 1
 #endif
-// Waves along N of a 256 x 256 bf16 tile: 2 (4 waves, one per SIMD; the
-// default) or 4 (8 waves, two per SIMD, no remainder tiles).  Other tiles
-// always use 4 waves.
-#ifndef MOE_GEMM_WGN256
-#define MOE_GEMM_WGN256 2
+// Schedule of the 256 x 256 bf16 tiles of products with k-contiguous
+// operands (the forward's up and down projections): 1 = gemm_tile_pp, eight
+// waves in two groups that alternate between loading and multiplying; 0 =
+// gemm_tile with four waves.  Other tiles always use gemm_tile.
+#ifndef MOE_GEMM_PP
+#define MOE_GEMM_PP 1
 #endif
 // (kRemBM, kRemThr and whole_tiles: tile_plan.h)
 
@@ -760,13 +764,206 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, lds_u8* lds, cons
     }
 }
 
+// Ping-pong schedule of the 256 x 256 bf16 tile with k-contiguous operands.
+// Eight waves, two per SIMD (waves w and w + 4 share one).  Group G = wave / 4
+// computes rows [128 G, 128 G + 128) of the tile and wave q = wave % 4 of the
+// group the columns [64 q, 64 q + 64) (wm = G, wn = q of the 2 x 4 epilogue
+// layout).  Each group alternates between a memory phase (read the current
+// slice's 24 fragments into registers) and a compute phase (the slice's 64
+// MFMAs on registers only), with a block barrier between phases and group 1
+// one phase behind group 0: on every SIMD one wave multiplies while the other
+// waits on LDS, memory or the barrier, so the matrix unit does not idle
+// while a wave stalls.
+//   barriers 2k .. 2k+1:   group 0 memory phase of slice k, group 1 compute k-1
+//   barriers 2k+1 .. 2k+2: group 0 compute k, group 1 memory phase of slice k
+// Slice s must be in LDS at barrier 2s.  Group 0 loads all of A into a ring
+// of 2 slots, group 1 all of B into a ring of 3 (5 slots of 32 KB in all).
+// The slot of slice s is free once group 1's memory phase of s has ended
+// (barrier 2s + 2).  Each group issues its slice k - 1 + N (N its ring's
+// slots) in its memory phase of slice k, into the slot of slice k - 1: A
+// slice k + 1 then has 2 phases to land, B slice k + 2 has 3, and every
+// phase carries the loads of one operand (issuing group 1's loads a phase
+// earlier puts both operands' loads into one phase, and that burst stalls
+// the address unit: measured 16 % slower).  Before barrier 2k + 2 a wave
+// waits for its own loads of slice k + 1.  Both groups pass 2 nk + 1
+// barriers and no load goes past the last slice; after the last barrier
+// every LDS read and load is complete, so the epilogue stages through the
+// ring's LDS without a further barrier.
+template <int EPI, bool STG>
+__device__ __forceinline__ void gemm_tile_pp(const GemmParams& p, lds_u8* lds, const TileDesc& t, int k0, int k1,
+                                             int unit) {
+    constexpr int BM = 256, BN = 256, WGN = 4, MB = 16;
+    constexpr int WM = BM / 2, WN = BN / WGN, FM = WM / MB, FN = WN / MB;   // 128 x 64 per wave: 8 x 4 blocks
+    constexpr int SL = 256 * 128;                                          // bytes of an A or a B slice
+    constexpr int NA = 2, NB = 3;
+    constexpr int GL = 8;            // 1 KB load groups per wave and slice (32 per operand, 4 waves)
+    constexpr int NF = FM + FN;      // fragments per half slice
+    constexpr int ES = 2;
+    typedef GemmEpilogue<true, BM, BN, EPI, 2, WGN> Epi;
+    typedef typename Epi::acc_t acc_t;
+    static_assert((NA + NB) * SL <= 160 * 1024, "rings fit in LDS");
+    static_assert(!epi_swiglu(EPI) || (FN % 2) == 0, "SwiGLU pairs MB-row blocks");
+    typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
+    typedef __attribute__((address_space(3))) void* lds_ptr_t;
+    const int e = t.e, nt = t.nt, row0 = t.row0, rows = t.rows;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = wave >> 2, q = wave & 3;
+    const int nk = k1 - k0;
+    constexpr int kRsrcWord3 = 0x00020000;
+
+    // Slice loads (as in gemm_tile): group 0 wave q fills A rows
+    // [64 q, 64 q + 64) of a slot, group 1 wave q B rows [64 q, 64 q + 64);
+    // load group g of the wave is slot rows 8 (8 q + g) .. + 7.
+    __amdgpu_buffer_rsrc_t rs0, rs1;
+    uint32_t voff[GL];
+    if (G == 0) {
+        rs0 = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.A + (int64_t)row0 * p.lda * ES), (short)0,
+                                                (int)(((int64_t)(rows - 1) * p.lda + p.K) * ES), kRsrcWord3);
+        rs1 = rs0;
+#pragma unroll
+        for (int g = 0; g < GL; ++g) {
+            const int r = 8 * (8 * q + g) + (lane >> 3);
+            voff[g] = (uint32_t)(min(r, rows - 1) * (int)p.lda * ES + (((lane & 7) ^ swz(r)) << 4));
+        }
+    } else {
+        const int64_t brow_base = epi_swiglu(EPI) ? (int64_t)nt * (BN / 2) : (int64_t)nt * BN;
+        const int b_rows = epi_swiglu(EPI) ? BN / 2 : BN;
+        const int64_t boff = ((int64_t)e * p.bstride + brow_base * p.K) * ES;
+        rs0 = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.B0 + boff), (short)0,
+                                                (int)((int64_t)b_rows * p.K * ES), kRsrcWord3);
+        rs1 = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)(epi_swiglu(EPI) ? p.B1 : p.B0) + boff),
+                                                (short)0, (int)((int64_t)b_rows * p.K * ES), kRsrcWord3);
+#pragma unroll
+        for (int g = 0; g < GL; ++g) {
+            const int gg = 8 * q + g;
+            const int r = 8 * gg + (lane >> 3);
+            // SwiGLU: 16-row block j = gg / 2 of the tile is rows (j / 2) 16 ..
+            // + 15 of W1 (j even) or W3 (j odd)
+            const int rr = epi_swiglu(EPI) ? ((gg / 4) * MB + (r & (MB - 1))) : r;
+            voff[g] = (uint32_t)(rr * p.K * ES + (((lane & 7) ^ swz(r)) << 4));
+        }
+    }
+    const int N = G == 0 ? NA : NB;                  // slots of this wave's ring
+    lds_u8* const ring = &lds[G == 0 ? 0 : NA * SL];
+    // this wave's share of slice v of its operand, if v is a slice of the range
+    auto issue = [&](int v) {
+        if (v >= nk) return;
+        const int kk = k0 + v;
+        lds_u8* dst = ring + (v % N) * SL + q * GL * 1024;
+#pragma unroll
+        for (int g = 0; g < GL; ++g) {
+            // SwiGLU B: gate rows for (g / 2) even, up rows for odd (8 q is even)
+            const bool up = G != 0 && epi_swiglu(EPI) && ((g >> 1) & 1);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? rs1 : rs0, (lds_ptr_t)(dst + g * 1024), 16, voff[g],
+                                                     kk * 128, 0, 0);
+        }
+    };
+    // before barrier 2k + 2: this wave's loads of slice k + 1 have landed
+    // (with a ring of 3 the next slice's loads may stay in flight)
+    auto wait_next = [&](int k) {
+        if (N == 3 && k + 2 < nk) wait_vmcnt<GL>();
+        else wait_vmcnt<0>();
+    };
+
+    // Fragments of slice s (both halves): lane l reads row l % 16 of each
+    // 16-row block at logical chunk 4 h + l / 16.
+    int foA[2], foB[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int lr = lane & (MB - 1), ch = 4 * h + (lane >> 4);
+        foA[h] = (G * WM + lr) * 128 + ((ch ^ swz(lr)) << 4);
+        foB[h] = NA * SL + (q * WN + lr) * 128 + ((ch ^ swz(lr)) << 4);
+    }
+    u32x4_t f[2 * NF];
+    auto read_slice = [&](int s) {
+        const lds_u8* a = &lds[(s % NA) * SL];
+        const lds_u8* b = &lds[(s % NB) * SL];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int j = 0; j < FM; ++j) f[h * NF + j] = *(lds_u32x4*)(a + foA[h] + j * MB * 128);
+#pragma unroll
+            for (int i = 0; i < FN; ++i) f[h * NF + FM + i] = *(lds_u32x4*)(b + foB[h] + i * MB * 128);
+        }
+    };
+    acc_t acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // the slice's MFMAs at raised issue priority, so the SIMD's other wave
+    // (in its memory phase) takes only the issue slots they leave
+    auto compute = [&]() {
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f[h * NF + FM + i]),
+                                                                        __builtin_bit_cast(bf16x8_t, f[h * NF + j]),
+                                                                        acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // phase boundary: nothing moves across it
+    auto phase_barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // memory phase of slice k: this wave's loads of slice k - 1 + N (into the
+    // slot of slice k - 1), then the fragments of slice k (dealing the loads
+    // out between the fragment reads measured level)
+    auto memory = [&](int k) {
+        issue(k - 1 + N);
+        read_slice(k);
+    };
+
+    // prologue: slices 0 .. N - 2 of the ring, slice 0 landed
+    issue(0);
+    if (N == 3) issue(1);
+    wait_next(-1);
+    phase_barrier();                             // barrier 0
+    if (G == 0) {
+        for (int k = 0; k < nk; ++k) {
+            memory(k);
+            phase_barrier();                     // barrier 2k + 1
+            compute();
+            wait_next(k);
+            phase_barrier();                     // barrier 2k + 2
+        }
+    } else {
+        phase_barrier();                         // barrier 1
+        for (int k = 0; k < nk; ++k) {
+            memory(k);
+            wait_next(k);
+            phase_barrier();                     // barrier 2k + 2
+            compute();
+            if (k + 1 < nk) phase_barrier();     // barrier 2k + 3
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (unit >= 0) {
+        Epi::store_partial(p, acc, unit, wave, lane);
+    } else if constexpr (Epi::can_stage && STG) {
+        static_assert(Epi::STAGE_BYTES <= (NA + NB) * SL, "staged output fits in the ring's LDS");
+        Epi::store_staged(p, acc, row0, rows, nt, G, q, lane, wave, lds);
+    } else {
+        Epi::store(p, acc, row0, rows, nt, G, q, lane);
+    }
+}
+
 // LDS bytes of a launch: its tile's ring, or the larger of that and the
 // remainder tile's ring when remainder tiles can occur (256-row bf16 tiles).
 template <bool BF16, int BM, int BN, int WGN>
 constexpr int gemm_lds_bytes() {
     constexpr int main_bytes = ring_depth(BM, BN, 2 * WGN).bytes;
     if constexpr (BF16 && BM == 256) {
-        constexpr int rem_bytes = ring_depth(kRemBM, BN, 4).bytes;
+        constexpr int rem_bytes = ring_depth(kRemBM, BN, 2 * WGN).bytes;
         return main_bytes > rem_bytes ? main_bytes : rem_bytes;
     }
     return main_bytes;
@@ -779,7 +976,8 @@ constexpr int gemm_lds_bytes() {
 // split-K units of the tail: block p.main_blocks + u is unit u, range
 // u % split of tail tile u / split; being dispatched last, they fill the CUs
 // that the last round of whole tiles leaves idle.  Remainder tiles
-// (256-row bf16 launches of 4 waves) run with 64-row tiles.
+// (256-row bf16 launches) run with 64-row tiles; whole 256 x 256 tiles of
+// k-contiguous products with the ping-pong schedule.
 template <bool BF16, int BM, int BN, int EPI, int WGN, int KM = KM_NONE, bool STG = false>
 __global__ __launch_bounds__(128 * WGN) void k_grouped_gemm(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -804,13 +1002,16 @@ __global__ __launch_bounds__(128 * WGN) void k_grouped_gemm(GemmParams p) {
         k1 = (c + 1) * p.nk / split;
     }
     const TileDesc t = decode_tile(p, L, BM);
-    if constexpr (BF16 && BM == 256 && WGN == 2) {
+    if constexpr (BF16 && BM == 256) {
         if (t.rem) {
-            gemm_tile<BF16, kRemBM, BN, EPI, 2, KM, STG>(p, lds, t, k0, k1, unit);
+            gemm_tile<BF16, kRemBM, BN, EPI, WGN, KM, STG>(p, lds, t, k0, k1, unit);
             return;
         }
     }
-    gemm_tile<BF16, BM, BN, EPI, WGN, KM, STG>(p, lds, t, k0, k1, unit);
+    if constexpr (BF16 && BM == 256 && BN == 256 && WGN == 4 && KM == KM_NONE)
+        gemm_tile_pp<EPI, STG>(p, lds, t, k0, k1, unit);
+    else
+        gemm_tile<BF16, BM, BN, EPI, WGN, KM, STG>(p, lds, t, k0, k1, unit);
 #endif
 }
 
@@ -858,9 +1059,9 @@ __global__ __launch_bounds__(64) void k_split_fixup(GemmParams p) {
     const int t = blockIdx.x / (NW * NGRP), w = (blockIdx.x / NGRP) % NW, i0 = (blockIdx.x % NGRP) * IG;
     if (split <= 1 || t >= tail) return;
     const TileDesc td = decode_tile(p, full + t, BM);
-    if constexpr (BF16 && BM == 256 && WGM == 2 && WGN == 2) {
+    if constexpr (BF16 && BM == 256 && WGM == 2) {
         if (td.rem) {
-            fixup_tile<BF16, kRemBM, BN, EPI, 2, 2>(p, td, w, i0, split);
+            fixup_tile<BF16, kRemBM, BN, EPI, 2, WGN>(p, td, w, i0, split);
             return;
         }
     }
@@ -935,7 +1136,7 @@ __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ 
 size_t ffn_tile_plan_ints(int E) { return 2 * (size_t)E + 5; }
 
 // Tile counts and K slices of a grouped GEMM as launch_grouped_gemm sets them.
-static bool uses_rem(bool bf16, int BM) { return MOE_GEMM_REM && MOE_GEMM_WGN256 == 2 && bf16 && BM == 256; }
+static bool uses_rem(bool bf16, int BM) { return MOE_GEMM_REM && bf16 && BM == 256; }
 
 static void gemm_geometry(bool bf16, int epi, int N, int K, int BM, int BN, int& NT, int& nk, int& rem) {
     NT = epi_swiglu(epi) ? N / (BN / 2) : N / BN;
@@ -982,14 +1183,15 @@ GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N) {
 
 // Whole tiles, split units (exit at once when the plan has no split), fixup;
 // the last two only when the plan may have a split.
-template <bool BF16, int BM, int BN>
-constexpr int waves_n() { return (BF16 && BM == 256 && BN == 256) ? MOE_GEMM_WGN256 : 2; }
+// Waves along N of a tile: 4 for the ping-pong tiles (8 waves), else 2.
+template <bool BF16, int BM, int BN, int KM = KM_NONE>
+constexpr int waves_n() { return (BF16 && BM == 256 && BN == 256 && KM == KM_NONE && MOE_GEMM_PP) ? 4 : 2; }
 
 // Whole tiles and split units in one launch, then the fixup when the plan
 // may have a split.
 template <bool BF16, int BM, int BN, int EPI, int KM = KM_NONE>
 static void launch_pair(const GemmParams& p0, int grid, bool may_split, hipStream_t s) {
-    constexpr int WGN = waves_n<BF16, BM, BN>();
+    constexpr int WGN = waves_n<BF16, BM, BN, KM>();
     typedef GemmEpilogue<BF16, BM, BN, EPI, 2, WGN> Epi;
     GemmParams p = p0;
     p.main_blocks = grid;
@@ -1032,7 +1234,7 @@ static bool gemm_shape_supported(bool bf16, int epi, int BM, int BN) {
     if (!bf16 && BM > 128) return false;
     if (!epi_swiglu(epi)) return true;
     const int mb = bf16 ? mfma_block<true>() : mfma_block<false>();
-    const int wgn = (bf16 && BM == 256 && BN == 256) ? MOE_GEMM_WGN256 : 2;
+    const int wgn = (bf16 && BM == 256 && BN == 256 && MOE_GEMM_PP) ? 4 : 2;
     return (BN / wgn / mb) % 2 == 0;
 }
 
