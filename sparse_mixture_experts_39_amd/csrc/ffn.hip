@@ -118,10 +118,11 @@ struct GemmParams {
 #ifndef MOE_GEMM_REM
 #define MOE_GEMM_REM 1
 #endif
-// Schedule of the 256 x 256 bf16 tiles of products with k-contiguous
-// operands (the forward's up and down projections): 1 = gemm_tile_pp, eight
-// waves in two groups that alternate between loading and multiplying; 0 =
-// gemm_tile with four waves.  Other tiles always use gemm_tile.
+// Schedule of the 256 x 256 bf16 tiles (the forward's up and down
+// projections, the backward's products through the weights as stored): 1 =
+// gemm_tile_pp, eight waves in two groups that alternate between loading and
+// multiplying; 0 = gemm_tile with four waves.  Other tiles always use
+// gemm_tile.
 #ifndef MOE_GEMM_PP
 #define MOE_GEMM_PP 1
 #endif
@@ -789,7 +790,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, lds_u8* lds, cons
 // barriers and no load goes past the last slice; after the last barrier
 // every LDS read and load is complete, so the epilogue stages through the
 // ring's LDS without a further barrier.
-template <int EPI, bool STG>
+// With KM == KM_B (B_e stored [K][N], see swzk) the B slices are 64 k rows of
+// the tile's 256 columns, their fragments come from transposing reads, and
+// every slice load is a dma16 (see there).
+template <int EPI, bool STG, int KM = KM_NONE>
 __device__ __forceinline__ void gemm_tile_pp(const GemmParams& p, lds_u8* lds, const TileDesc& t, int k0, int k1,
                                              int unit) {
     constexpr int BM = 256, BN = 256, WGN = 4, MB = 16;
@@ -803,6 +807,8 @@ __device__ __forceinline__ void gemm_tile_pp(const GemmParams& p, lds_u8* lds, c
     typedef typename Epi::acc_t acc_t;
     static_assert((NA + NB) * SL <= 160 * 1024, "rings fit in LDS");
     static_assert(!epi_swiglu(EPI) || (FN % 2) == 0, "SwiGLU pairs MB-row blocks");
+    constexpr bool BKM = KM == KM_B;
+    static_assert(!BKM || EPI == EPI_STORE, "k-major B: plain store");
     typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
     const int e = t.e, nt = t.nt, row0 = t.row0, rows = t.rows;
@@ -816,16 +822,37 @@ __device__ __forceinline__ void gemm_tile_pp(const GemmParams& p, lds_u8* lds, c
     // [64 q, 64 q + 64) of a slot, group 1 wave q B rows [64 q, 64 q + 64);
     // load group g of the wave is slot rows 8 (8 q + g) .. + 7.
     __amdgpu_buffer_rsrc_t rs0, rs1;
-    uint32_t voff[GL];
+    // lane offsets of the loads; the k-major launches keep three lane
+    // constants instead and form each offset when the load is issued (eight
+    // offsets in registers made the compiler spill them inside the loop)
+    uint32_t voff[BKM ? 1 : GL];
+    uint32_t lc0 = 0, lc1 = 0, lc2 = 0;
     if (G == 0) {
         rs0 = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.A + (int64_t)row0 * p.lda * ES), (short)0,
                                                 (int)(((int64_t)(rows - 1) * p.lda + p.K) * ES), kRsrcWord3);
         rs1 = rs0;
+        if constexpr (BKM) {
+            lc0 = (uint32_t)(64 * q + (lane >> 3));                      // A row of load group 0
+            lc1 = (uint32_t)(((lane & 7) ^ (lane >> 4)) << 4);            // chunk offset, even groups
+            lc2 = (uint32_t)(((lane & 7) ^ (4 + (lane >> 4))) << 4);      // chunk offset, odd groups
+        } else {
 #pragma unroll
-        for (int g = 0; g < GL; ++g) {
-            const int r = 8 * (8 * q + g) + (lane >> 3);
-            voff[g] = (uint32_t)(min(r, rows - 1) * (int)p.lda * ES + (((lane & 7) ^ swz(r)) << 4));
+            for (int g = 0; g < GL; ++g) {
+                const int r = 8 * (8 * q + g) + (lane >> 3);
+                voff[g] = (uint32_t)(min(r, rows - 1) * (int)p.lda * ES + (((lane & 7) ^ swz(r)) << 4));
+            }
         }
+    } else if constexpr (BKM) {
+        // k rows below K1 from B0, the rest from B1; load group gg = 8 q + g
+        // is k rows 2 gg, 2 gg + 1 of the slice: lane l takes k row
+        // 2 gg + l / 32, physical chunk l % 32, logical chunk (l % 32) ^ swzk
+        const int64_t boff = (int64_t)e * p.bstride * ES;
+        rs0 = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.B0 + boff), (short)0,
+                                                (int)((int64_t)p.K1 * p.ldb * ES), kRsrcWord3);
+        rs1 = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)(p.B1 ? p.B1 : p.B0) + boff), (short)0,
+                                                (int)((int64_t)(p.K - p.K1) * p.ldb * ES), kRsrcWord3);
+        lc0 = (uint32_t)(((int64_t)(16 * q + (lane >> 5)) * p.ldb + nt * BN) * ES);   // k row of load group 0
+        lc1 = (uint32_t)((lane & 31) ^ ((lane >> 5) << 1));                           // chunk before swzk's g bits
     } else {
         const int64_t brow_base = epi_swiglu(EPI) ? (int64_t)nt * (BN / 2) : (int64_t)nt * BN;
         const int b_rows = epi_swiglu(EPI) ? BN / 2 : BN;
@@ -851,12 +878,36 @@ __device__ __forceinline__ void gemm_tile_pp(const GemmParams& p, lds_u8* lds, c
         if (v >= nk) return;
         const int kk = k0 + v;
         lds_u8* dst = ring + (v % N) * SL + q * GL * 1024;
+        if constexpr (BKM) {
+            if (G == 0) {
+                // A row 64 q + 8 g + l / 8 (clamped to the tile's last row),
+                // chunk (l % 8) ^ swz(row) with swz(row) = 4 (g % 2) + l / 16
 #pragma unroll
-        for (int g = 0; g < GL; ++g) {
-            // SwiGLU B: gate rows for (g / 2) even, up rows for odd (8 q is even)
-            const bool up = G != 0 && epi_swiglu(EPI) && ((g >> 1) & 1);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? rs1 : rs0, (lds_ptr_t)(dst + g * 1024), 16, voff[g],
-                                                     kk * 128, 0, 0);
+                for (int g = 0; g < GL; ++g) {
+                    const uint32_t r = min(lc0 + 8 * g, (uint32_t)(rows - 1));
+                    dma16(rs0, r * (uint32_t)(p.lda * ES) + ((g & 1) ? lc2 : lc1), (uint32_t)(kk * 128), dst + g * 1024);
+                }
+            } else {
+                // k row 16 q + 2 g + l / 32 of the slice; its swzk is
+                // 2 (l / 32) + 4 (g % 2) + 8 (g / 4), whose g bits are a constant
+                const int kr = kk * 64;
+                const bool hi = kr >= p.K1;
+                const __amdgpu_buffer_rsrc_t rs = hi ? rs1 : rs0;
+                const uint32_t soff = (uint32_t)((int64_t)(hi ? kr - p.K1 : kr) * p.ldb * ES);
+#pragma unroll
+                for (int g = 0; g < GL; ++g) {
+                    const uint32_t c = lc1 ^ (uint32_t)((4 * (g & 1) + 8 * (g >> 2)));
+                    dma16(rs, lc0 + (uint32_t)(2 * g * p.ldb * ES) + c * 16, soff, dst + g * 1024);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < GL; ++g) {
+                // SwiGLU B: gate rows for (g / 2) even, up rows for odd (8 q is even)
+                const bool up = G != 0 && epi_swiglu(EPI) && ((g >> 1) & 1);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(up ? rs1 : rs0, (lds_ptr_t)(dst + g * 1024), 16, voff[g],
+                                                         kk * 128, 0, 0);
+            }
         }
     };
     // before barrier 2k + 2: this wave's loads of slice k + 1 have landed
@@ -875,6 +926,21 @@ __device__ __forceinline__ void gemm_tile_pp(const GemmParams& p, lds_u8* lds, c
         foA[h] = (G * WM + lr) * 128 + ((ch ^ swz(lr)) << 4);
         foB[h] = NA * SL + (q * WN + lr) * 128 + ((ch ^ swz(lr)) << 4);
     }
+    // k-major B: lane base of each 16-column block of the wave (k rows
+    // 8 (l / 16) + (l % 16) / 4 of the slice, 4 columns at 4 (l % 4)); half h
+    // adds 32 k rows, a fragment's second read 4 more (as in gemm_tile)
+    constexpr int RBB = BN * 2;
+    int kbb[BKM ? FN : 1];
+    if constexpr (BKM) {
+        const int g4 = lane >> 4, L = lane & 15;
+        const int sw = ((L >> 2) | ((g4 & 1) << 2)) << 1;
+        const int kr = 8 * g4 + (L >> 2);
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int col = q * WN + i * 16 + 4 * (L & 3);
+            kbb[i] = NA * SL + kr * RBB + (((col >> 3) ^ sw) << 4) + ((col & 7) << 1);
+        }
+    }
     u32x4_t f[2 * NF];
     auto read_slice = [&](int s) {
         const lds_u8* a = &lds[(s % NA) * SL];
@@ -884,7 +950,18 @@ __device__ __forceinline__ void gemm_tile_pp(const GemmParams& p, lds_u8* lds, c
 #pragma unroll
             for (int j = 0; j < FM; ++j) f[h * NF + j] = *(lds_u32x4*)(a + foA[h] + j * MB * 128);
 #pragma unroll
-            for (int i = 0; i < FN; ++i) f[h * NF + FM + i] = *(lds_u32x4*)(b + foB[h] + i * MB * 128);
+            for (int i = 0; i < FN; ++i) {
+                if constexpr (BKM) {
+                    const lds_u8* bp = b + kbb[i] + 32 * h * RBB;
+                    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)bp);
+                    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(bp + 4 * RBB));
+                    typedef short v8i16_t __attribute__((ext_vector_type(8)));
+                    const v8i16_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    f[h * NF + FM + i] = __builtin_bit_cast(u32x4_t, both);
+                } else {
+                    f[h * NF + FM + i] = *(lds_u32x4*)(b + foB[h] + i * MB * 128);
+                }
+            }
         }
     };
     acc_t acc[FN][FM];
@@ -976,8 +1053,8 @@ constexpr int gemm_lds_bytes() {
 // split-K units of the tail: block p.main_blocks + u is unit u, range
 // u % split of tail tile u / split; being dispatched last, they fill the CUs
 // that the last round of whole tiles leaves idle.  Remainder tiles
-// (256-row bf16 launches) run with 64-row tiles; whole 256 x 256 tiles of
-// k-contiguous products with the ping-pong schedule.
+// (256-row bf16 launches) run with 64-row tiles; whole 256 x 256 tiles with
+// the ping-pong schedule.
 template <bool BF16, int BM, int BN, int EPI, int WGN, int KM = KM_NONE, bool STG = false>
 __global__ __launch_bounds__(128 * WGN) void k_grouped_gemm(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -1008,8 +1085,8 @@ __global__ __launch_bounds__(128 * WGN) void k_grouped_gemm(GemmParams p) {
             return;
         }
     }
-    if constexpr (BF16 && BM == 256 && BN == 256 && WGN == 4 && KM == KM_NONE)
-        gemm_tile_pp<EPI, STG>(p, lds, t, k0, k1, unit);
+    if constexpr (BF16 && BM == 256 && BN == 256 && WGN == 4)
+        gemm_tile_pp<EPI, STG, KM>(p, lds, t, k0, k1, unit);
     else
         gemm_tile<BF16, BM, BN, EPI, WGN, KM, STG>(p, lds, t, k0, k1, unit);
 #endif
@@ -1185,7 +1262,7 @@ GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N) {
 // the last two only when the plan may have a split.
 // Waves along N of a tile: 4 for the ping-pong tiles (8 waves), else 2.
 template <bool BF16, int BM, int BN, int KM = KM_NONE>
-constexpr int waves_n() { return (BF16 && BM == 256 && BN == 256 && KM == KM_NONE && MOE_GEMM_PP) ? 4 : 2; }
+constexpr int waves_n() { return (BF16 && BM == 256 && BN == 256 && MOE_GEMM_PP) ? 4 : 2; }
 
 // Whole tiles and split units in one launch, then the fixup when the plan
 // may have a split.
