@@ -1064,11 +1064,22 @@ __global__ __launch_bounds__(128 * WGN) void k_grouped_gemm(GemmParams p) {
     const int full = p.plan[p.E + 1], split = p.plan[p.E + 2], tail = p.plan[p.E + 3];
     int L, k0 = 0, k1 = p.nk, unit = -1;
     if ((int)blockIdx.x < p.main_blocks) {
+        // The tiles run as whole units (all but a split tail) are nw whole and
+        // nr remainder tiles; XCD x takes an equal share of each, as
+        // contiguous ranges, and deals its remainder tiles evenly among its
+        // whole tiles: the remainder tiles reread their experts' weights from
+        // memory, so spread out they overlap the other CUs' products, and no
+        // XCD runs a round of whole tiles more than the others.
         const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-        const int per_xcd = split > 1 ? full / 8 : (total + 7) / 8;
-        if (slot >= per_xcd) return;
-        L = xcd * per_xcd + slot;
-        if (L >= total) return;
+        const int nfull = split > 1 ? full : total;
+        const int W = min(p.plan[p.E] * p.NT, nfull), R = nfull - W;
+        const int w0 = (int)((int64_t)xcd * W / 8), nw = (int)((int64_t)(xcd + 1) * W / 8) - w0;
+        const int r0 = (int)((int64_t)xcd * R / 8), nr = (int)((int64_t)(xcd + 1) * R / 8) - r0;
+        const int n = nw + nr;
+        if (slot >= n) return;
+        // remainder tiles among the XCD's slots [0, s): floor(s nr / n)
+        const int c0 = (int)((int64_t)slot * nr / n), c1 = (int)((int64_t)(slot + 1) * nr / n);
+        L = c1 > c0 ? W + r0 + c0 : w0 + slot - c0;
     } else {
         if (split <= 1) return;
         unit = blockIdx.x - p.main_blocks;
@@ -1271,8 +1282,10 @@ static void launch_pair(const GemmParams& p0, int grid, bool may_split, hipStrea
     constexpr int WGN = waves_n<BF16, BM, BN, KM>();
     typedef GemmEpilogue<BF16, BM, BN, EPI, 2, WGN> Epi;
     GemmParams p = p0;
-    p.main_blocks = grid;
-    const dim3 g(grid + (may_split ? kSplitUnits : 0)), b(128 * WGN);
+    // per XCD at most ceil(whole / 8) + ceil(remainder / 8) tiles: two block
+    // slots per XCD beyond the tile bound
+    p.main_blocks = grid + 16;
+    const dim3 g(p.main_blocks + (may_split ? kSplitUnits : 0)), b(128 * WGN);
     // the staged-output instantiation where the epilogue can stage and C
     // and ldc allow 16-byte row stores
     bool staged = false;
@@ -1373,7 +1386,7 @@ hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, c
     const int64_t per_expert = rem ? (kRemThr + kRemBM - 1) / kRemBM : 1;
     const int64_t m_tiles_ub = (max_rows + BM - 1) / BM + (p.E > 1 ? p.E * per_expert : per_expert);
     const int64_t grid = (m_tiles_ub * p.NT + 7) / 8 * 8;
-    if (grid > 0x7fffffff - kSplitUnits) return hipErrorInvalidValue;
+    if (grid > 0x7fffffff - kSplitUnits - 16) return hipErrorInvalidValue;
     // With offsets == NULL the host knows the row count and launches the
     // split-K parts only when the plan has a tail; routed counts live on the
     // device.
@@ -1435,7 +1448,7 @@ hipError_t launch_grouped_gemm_nn(const void* A, int64_t lda, const void* B0, co
     const int64_t per_expert = rem ? (kRemThr + kRemBM - 1) / kRemBM : 1;
     const int64_t m_tiles_ub = (max_rows + BM - 1) / BM + (p.E > 1 ? p.E * per_expert : per_expert);
     const int64_t grid = (m_tiles_ub * p.NT + 7) / 8 * 8;
-    if (grid > 0x7fffffff - kSplitUnits) return hipErrorInvalidValue;
+    if (grid > 0x7fffffff - kSplitUnits - 16) return hipErrorInvalidValue;
     bool may_split = true;
     if (offsets == nullptr) {
         const int64_t whole = whole_tiles((int)max_rows, BM, rem != 0);
