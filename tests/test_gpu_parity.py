@@ -342,6 +342,39 @@ def test_expert_ffn_remainder_tiles(act):
         H.assert_close_rel(H.as_f64(y[lo:hi]), ref, "bf16", f"expert {e} ({hi - lo} rows)")
 
 
+# Reductions of 1, 2 and 3 K slices (64 bf16 values each) through 256 x 256
+# tiles, whose two wave groups take turns loading and multiplying: the
+# shortest prologues and drains of that schedule.  (d, F) puts the short K
+# on the up projection (K = d, N = F) or on the down projection (K = F,
+# N = d = 256); the other product and every expert row are checked too.
+@pytest.mark.parametrize("d,F", [(64, 256), (128, 256), (192, 256), (256, 64), (256, 128), (256, 192)])
+@pytest.mark.parametrize("act", ["swiglu", "relu"])
+def test_expert_ffn_short_reductions(d, F, act):
+    E = len(REM_COUNTS)
+    cfg = Config(f"shortk_{act}_{d}_{F}", T=2700, d=d, F=F, E=E, k=2, act_dtype="bf16", act=act,
+                 gate="softmax_topk", seed=33)
+    c = H.bind_config(cfg)
+    R = moe.max_rows(c)
+    assert sum(REM_COUNTS) <= R and R // E >= 384     # 256-row tiles are chosen for this average
+    inp = workloads.make_inputs(cfg)
+    dv = H.to_device(inp)
+    x_perm = torch.cat([dv["x"], dv["x"]])[:R].contiguous()
+    off = np.concatenate([[0], np.cumsum(REM_COUNTS)]).astype(np.int32)
+    offsets = torch.from_numpy(off).to("cuda")
+    y_perm = torch.zeros((R, d), dtype=torch.bfloat16, device="cuda")
+    H.log(f"[short-k] {act} d={d} F={F}: expert_ffn with counts {REM_COUNTS}")
+    moe.moe_expert_ffn(c, x_perm, offsets, moe.weights_from(c, dv), y_perm, moe.workspace(c))
+    torch.cuda.synchronize()
+    xp = x_perm.cpu()
+    y = y_perm.cpu()
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        ref = oracle.expert_ffn(cfg, xp[lo:hi], *oracle.expert_weights(cfg, inp, e))
+        H.assert_close_rel(H.as_f64(y[lo:hi]), ref, "bf16", f"expert {e} ({hi - lo} rows)")
+
+
 @pytest.mark.parametrize("act", ["swiglu", "relu"])
 def test_expert_gemms_unaligned_outputs_bitwise(act):
     """Outputs whose rows cannot be stored 16 bytes at a time (the buffer
