@@ -364,7 +364,10 @@ moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float g
  * y = sum over the selected experts of g_i Expert_i(x); awesome-ai-roadmap
  * 19.3.2 and 19.5 for the shared expert): route, dispatch, experts (+ shared
  * expert), combine, with every intermediate carved from ws.  x [T][d], out [T][d].  The residual is
- * added when cfg->flags has MOE_F_ADD_RESIDUAL. */
+ * added when cfg->flags has MOE_F_ADD_RESIDUAL.  When x is under 2 GiB the
+ * dispatch writes only the permutation and the up projection reads each
+ * expert row straight from x (row perm_src[r] / k), so the workspace's x_perm
+ * is not written; the outputs are the same as those of the stage calls. */
 moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x, void* out,
                              const moe_stats* stats, void* ws, size_t ws_bytes, void* stream);
 

@@ -95,6 +95,13 @@ struct GemmParams {
     // k rows that come from B0 (the rest from B1, row k - K1)
     int64_t ldb;
     int K1;
+    // row gather of A (k-contiguous launches): when arows is set, row i of the
+    // grouped matrix is row arows[i] / arow_div of A, whose a_bytes bytes the
+    // loads may touch (the layer forward reads the activations through the
+    // dispatch's assignment ids t k + j in place of a permuted copy)
+    const int32_t* arows;
+    int64_t a_bytes;
+    int arow_div;
 };
 
 // Work decomposition.  The plan lists ceil(M_e / BM) row tiles per expert,
@@ -467,12 +474,22 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, lds_u8* lds, cons
     constexpr int kRsrcWord3 = 0x00020000;
     __amdgpu_buffer_rsrc_t rsA, rsB0, rsB1;
     uint32_t voffA[ga], voffB[gb];
-    rsA = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.A + (int64_t)row0 * p.lda * ES), (short)0,
-                                            (int)(((int64_t)(rows - 1) * p.lda + p.K) * ES), kRsrcWord3);
+    if (KM == KM_NONE && p.arows) {
+        rsA = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, (int)p.a_bytes, kRsrcWord3);
 #pragma unroll
-    for (int q = 0; q < ga; ++q) {
-        const int r = 8 * (wave * ga + q) + (lane >> 3);
-        voffA[q] = (uint32_t)(min(r, rows - 1) * (int)p.lda * ES + (((lane & 7) ^ swz(r)) << 4));
+        for (int q = 0; q < ga; ++q) {
+            const int r = 8 * (wave * ga + q) + (lane >> 3);
+            voffA[q] = (uint32_t)(p.arows[row0 + min(r, rows - 1)] / p.arow_div) * (uint32_t)(p.lda * ES) +
+                       (uint32_t)(((lane & 7) ^ swz(r)) << 4);
+        }
+    } else {
+        rsA = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.A + (int64_t)row0 * p.lda * ES), (short)0,
+                                                (int)(((int64_t)(rows - 1) * p.lda + p.K) * ES), kRsrcWord3);
+#pragma unroll
+        for (int q = 0; q < ga; ++q) {
+            const int r = 8 * (wave * ga + q) + (lane >> 3);
+            voffA[q] = (uint32_t)(min(r, rows - 1) * (int)p.lda * ES + (((lane & 7) ^ swz(r)) << 4));
+        }
     }
     if constexpr (BKM) {
         // B_e stored [K][N]: k rows below K1 from B0, the rest from B1.  A
@@ -827,7 +844,17 @@ __device__ __forceinline__ void gemm_tile_pp(const GemmParams& p, lds_u8* lds, c
     // offsets in registers made the compiler spill them inside the loop)
     uint32_t voff[BKM ? 1 : GL];
     uint32_t lc0 = 0, lc1 = 0, lc2 = 0;
-    if (G == 0) {
+    if (G == 0 && !BKM && p.arows) {
+        // gathered rows: the descriptor spans A, each lane its row's offset
+        rs0 = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, (int)p.a_bytes, kRsrcWord3);
+        rs1 = rs0;
+#pragma unroll
+        for (int g = 0; g < GL; ++g) {
+            const int r = 8 * (8 * q + g) + (lane >> 3);
+            voff[g] = (uint32_t)(p.arows[row0 + min(r, rows - 1)] / p.arow_div) * (uint32_t)(p.lda * ES) +
+                      (uint32_t)(((lane & 7) ^ swz(r)) << 4);
+        }
+    } else if (G == 0) {
         rs0 = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.A + (int64_t)row0 * p.lda * ES), (short)0,
                                                 (int)(((int64_t)(rows - 1) * p.lda + p.K) * ES), kRsrcWord3);
         rs1 = rs0;
@@ -1360,7 +1387,8 @@ static bool plan_may_split(int64_t total, int nk) {
 hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B0, const void* B1,
                                int64_t b_expert_stride, void* C, int64_t ldc, int N, int K, int E, int64_t max_rows,
                                const int32_t* offsets, int32_t* plan, int32_t* plan_copy, float* partial, int BM,
-                               int BN, hipStream_t s, void* C2, int64_t ldc2, bool plan_ready) {
+                               int BN, hipStream_t s, void* C2, int64_t ldc2, bool plan_ready,
+                               const int32_t* arows, int64_t a_rows, int arow_div) {
     if (max_rows <= 0) return hipSuccess;
     GemmParams p;
     p.A = A; p.lda = lda; p.B0 = B0; p.B1 = B1; p.bstride = b_expert_stride;
@@ -1376,8 +1404,13 @@ hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, c
     p.unit_f4 = (int64_t)BM * BN / 4;
     p.ldb = 0;
     p.K1 = 0;
+    p.arows = arows;
+    p.a_bytes = arows ? a_rows * lda * (bf16 ? 2 : 4) : 0;
+    p.arow_div = arow_div > 0 ? arow_div : 1;
     if (!gemm_shape_supported(bf16, epi, BM, BN) || (rem && !gemm_shape_supported(bf16, epi, kRemBM, BN)))
         return hipErrorInvalidValue;
+    // a gathered row's 32-bit byte offset must stay below 2^31
+    if (arows && (a_rows <= 0 || arow_div <= 0 || p.a_bytes >= ((int64_t)1 << 31))) return hipErrorInvalidValue;
     if (!plan_ready)
         hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, offsets, E, (int)max_rows, BM, rem, p.NT, p.nk,
                            plan, plan_copy, 0, 0, 0, 0, (int32_t*)nullptr);
@@ -1443,6 +1476,9 @@ hipError_t launch_grouped_gemm_nn(const void* A, int64_t lda, const void* B0, co
     p.unit_f4 = (int64_t)BM * BN / 4;
     p.ldb = ldb;
     p.K1 = K1;
+    p.arows = nullptr;
+    p.a_bytes = 0;
+    p.arow_div = 1;
     hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, offsets, E, (int)max_rows, BM, rem, p.NT, p.nk, plan,
                        plan_copy, 0, 0, 0, 0, (int32_t*)nullptr);
     const int64_t per_expert = rem ? (kRemThr + kRemBM - 1) / kRemBM : 1;

@@ -88,11 +88,14 @@ size_t gemm_partial_bytes(int BM, int BN);
 // rows, whose offsets go to plan_copy), then runs the GEMM and its split-K
 // fixup; with 256-row bf16 tiles, 64-row tiles of the same launch cover the
 // rows an expert has left past its whole tiles when there are at most 128.
+// With arows != NULL row i of the grouped A is row arows[i] / arow_div of A,
+// which has a_rows rows of lda elements (under 2^31 bytes).
 hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B0, const void* B1,
                                int64_t b_expert_stride, void* C, int64_t ldc, int N, int K, int E,
                                int64_t max_rows, const int32_t* offsets, int32_t* plan, int32_t* plan_copy,
                                float* partial, int BM, int BN, hipStream_t s, void* C2 = nullptr,
-                               int64_t ldc2 = 0, bool plan_ready = false);
+                               int64_t ldc2 = 0, bool plan_ready = false, const int32_t* arows = nullptr,
+                               int64_t a_rows = 0, int arow_div = 1);
 // The tile plans of two grouped GEMMs over the same expert groups in one
 // launch; the GEMMs are then launched with plan_ready = true.
 hipError_t launch_tile_plans(bool bf16, const int32_t* offsets, int E, int64_t max_rows, int epi1, int N1, int K1,

@@ -448,7 +448,9 @@ moe_status moe_update_bias(const moe_config* c, const int32_t* counts, float gam
 }
 
 // The dispatch kernels on validated arguments; gu / gd (optional): the scan
-// also writes the tile plans of the two expert GEMMs that follow.
+// also writes the tile plans of the two expert GEMMs that follow.  x_perm ==
+// NULL: only the permutation (perm_src, slot_pos) is written, no rows are
+// copied (the layer's up projection then gathers the rows of x itself).
 static moe_status dispatch_stages(const moe_config* c, const void* x, const int32_t* topk_idx, void* x_perm,
                                   int32_t* expert_offsets, int32_t* perm_src, int32_t* slot_pos, const moe_stats* st,
                                   void* ws, hipStream_t h, const moe::PlanGeom* gu, const moe::PlanGeom* gd) {
@@ -462,8 +464,11 @@ static moe_status dispatch_stages(const moe_config* c, const void* x, const int3
     const float* P = (st && st->P) ? st->P : at<float>(ws, L.P_ws);
     moe::launch_histogram(topk_idx, na, E, hist, h);
     moe::launch_scan(hist, nb, E, cap, bbase, expert_offsets, P, st, h, gu, gd);
-    moe::launch_scatter_permute(topk_idx, c->T, slots_of(c), E, bbase, expert_offsets, cap, x, c->d_model,
-                                elem_bytes(c), perm_src, slot_pos, x_perm, h);
+    if (x_perm)
+        moe::launch_scatter_permute(topk_idx, c->T, slots_of(c), E, bbase, expert_offsets, cap, x, c->d_model,
+                                    elem_bytes(c), perm_src, slot_pos, x_perm, h);
+    else
+        moe::launch_scatter(topk_idx, na, E, bbase, expert_offsets, cap, perm_src, slot_pos, h);
     return after_launch();
 }
 
@@ -519,10 +524,12 @@ static moe::GemmShape gemm_shape(const moe_config* c, bool up, bool pre, int64_t
     return moe::pick_gemm_shape(is_bf16(c), gemm_epi(c, up, pre), rows, E, up ? F : c->d_model);
 }
 
+// up with arows != NULL: row i of the up projection's input is row
+// arows[i] / slots of a (the T rows of x; arows holds assignment ids).
 static moe_status run_gemm(const moe_config* c, bool up, const void* a, int64_t rows, int E, const int32_t* offsets,
                            const void* w1, const void* w3, const void* w2, int F, void* dst, int32_t* plan,
                            int32_t* plan_copy, float* partial, hipStream_t h, void* pre = nullptr,
-                           bool plan_ready = false) {
+                           bool plan_ready = false, const int32_t* arows = nullptr) {
     const bool bf = is_bf16(c);
     const int d = c->d_model;
     const bool swiglu = c->act == MOE_ACT_SWIGLU;
@@ -531,7 +538,8 @@ static moe_status run_gemm(const moe_config* c, bool up, const void* a, int64_t 
     const moe::GemmShape g = gemm_shape(c, up, pre != nullptr, rows, E, F);
     const hipError_t e = up ? moe::launch_grouped_gemm(bf, epi, a, d, w1, w3, (int64_t)F * d, dst, F, F, d, E, rows,
                                                        offsets, plan, plan_copy, partial, g.BM, g.BN, h, pre,
-                                                       (int64_t)(swiglu ? 2 : 1) * F, plan_ready)
+                                                       (int64_t)(swiglu ? 2 : 1) * F, plan_ready, arows, c->T,
+                                                       slots_of(c))
                             : moe::launch_grouped_gemm(bf, 0, a, F, w2, nullptr, (int64_t)d * F, dst, d, d, F, E,
                                                        rows, offsets, plan, plan_copy, partial, g.BM, g.BN, h,
                                                        nullptr, 0, plan_ready);
@@ -606,9 +614,11 @@ static void ffn_plan_geoms(const moe_config* c, void* ws, moe::PlanGeom* gu, moe
 }
 
 // The expert FFN on validated arguments; plans_ready: the dispatch scan has
-// already written both tile plans.
+// already written both tile plans; arows != NULL: x_perm is x and row i of
+// the experts' input is its row arows[i] / slots (arows: perm_src).
 static moe_status ffn_stages(const moe_config* c, const void* x_perm, const int32_t* expert_offsets,
-                             const moe_weights* w, void* y_perm, void* ws, hipStream_t h, bool plans_ready) {
+                             const moe_weights* w, void* y_perm, void* ws, hipStream_t h, bool plans_ready,
+                             const int32_t* arows = nullptr) {
     const int64_t R = max_rows_of(c);
     if (R == 0) return MOE_OK;
     const Layout L = compute_layout(c);
@@ -629,7 +639,7 @@ static moe_status ffn_stages(const moe_config* c, const void* x_perm, const int3
         if (e != hipSuccess) return hip_status(e);
     }
     if ((s = run_gemm(c, true, x_perm, R, E, expert_offsets, w->w_gate, w->w_up, nullptr, F, H, pu, pc, part, h,
-                      nullptr, true)) != MOE_OK)
+                      nullptr, true, arows)) != MOE_OK)
         return s;
     return run_gemm(c, false, H, R, E, expert_offsets, nullptr, nullptr, w->w_down, F, y_perm, pd, pc, part, h,
                     nullptr, true);
@@ -698,13 +708,18 @@ moe_status moe_layer_forward(const moe_config* c, const moe_weights* w, const vo
     void* y_perm = at<void>(ws, L.y_perm);
     void* shared_out = c->n_shared ? at<void>(ws, L.shared_out) : nullptr;
     if ((s = moe_route(c, x, w, idx, gates, nullptr, st, ws, ws_bytes, stream)) != MOE_OK) return s;
-    // the dispatch scan also writes the expert GEMMs' tile plans (one launch fewer)
+    // the dispatch scan also writes the expert GEMMs' tile plans (one launch
+    // fewer), and when x is under 2 GiB the up projection gathers its rows of
+    // x through perm_src, so the dispatch copies no rows
     moe::PlanGeom gu, gd;
     ffn_plan_geoms(c, ws, &gu, &gd);
-    if ((s = dispatch_stages(c, x, idx, x_perm, offsets, perm_src, slot_pos, st, ws, (hipStream_t)stream, &gu,
-                             &gd)) != MOE_OK)
+    const bool gather = (int64_t)c->T * c->d_model * elem_bytes(c) < ((int64_t)1 << 31);
+    if ((s = dispatch_stages(c, x, idx, gather ? nullptr : x_perm, offsets, perm_src, slot_pos, st, ws,
+                             (hipStream_t)stream, &gu, &gd)) != MOE_OK)
         return s;
-    if ((s = ffn_stages(c, x_perm, offsets, w, y_perm, ws, (hipStream_t)stream, true)) != MOE_OK) return s;
+    if ((s = ffn_stages(c, gather ? x : x_perm, offsets, w, y_perm, ws, (hipStream_t)stream, true,
+                        gather ? perm_src : nullptr)) != MOE_OK)
+        return s;
     if (shared_out && (s = moe_shared_expert(c, x, w, shared_out, ws, ws_bytes, stream)) != MOE_OK) return s;
     const void* resid = (c->flags & MOE_F_ADD_RESIDUAL) ? x : nullptr;
     return moe_combine(c, y_perm, slot_pos, gates, resid, shared_out, out, stream);
