@@ -784,17 +784,68 @@ __global__ __launch_bounds__(512) void k_gemm_nn256(XnParams p) {
 // need (or none) take one chunk that reads zeros.  Block b serves XCD b % 8;
 // the 32 blocks of an XCD take consecutive tiles of that XCD's range, so
 // concurrent tiles share an expert's rows in L2 as in the per-tile launch.
+// The XCD ranges are contiguous and of equal cost, a tile costing its
+// expert's 64-row chunks (at least one) plus kTileEnd for its output stores:
+// a tile's time grows with its expert's rows, so ranges of equal tile counts
+// left the XCD with the most rows (DeepSeek-V3: rows on 80 of 256 experts)
+// finishing last.
 __global__ __launch_bounds__(512) void k_gemm_wgrad(XnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int BM = 256, KC = 64, GM = 4;
+    constexpr int kTileEnd = 3;   // a tile's output stores, in chunk times (about 9000 against 3300 cycles)
     constexpr int OPB = BM * KC * 2;
     __shared__ __align__(16) uint8_t lds[4 * OPB];
+    __shared__ int xcd_range[2];
     const int per_e = p.tiles_m * p.tiles_n;
     const int ntiles = p.E * per_e;
-    const int per_xcd = (ntiles + 7) / 8;
     const int xcd = blockIdx.x % 8, nslot = gridDim.x / 8;
-    const int t_end = min((xcd + 1) * per_xcd, ntiles);
-    const int t_first = xcd * per_xcd + (int)(blockIdx.x / 8);
+    if (threadIdx.x < 64) {
+        // wave 0: lane l sums the cost of experts [l s, l s + s), a wave scan
+        // gives the cost before each segment, and for bound x (this XCD's
+        // first tile and the next XCD's) the lane whose segment reaches
+        // x total / 8 walks its experts to the first tile t with
+        // 8 cost(tiles before t) >= x total
+        const int l = threadIdx.x, seg = (p.E + 63) / 64;
+        const int e0 = min(l * seg, p.E), e1 = min(e0 + seg, p.E);
+        auto cost = [&](int e) -> int64_t {
+            const int rows = p.offsets[e + 1] - p.offsets[e];
+            return (int64_t)per_e * (max(1, (rows + KC - 1) / KC) + kTileEnd);
+        };
+        int64_t own = 0;
+        for (int e = e0; e < e1; ++e) own += cost(e);
+        int64_t inc = own;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int64_t v = __shfl_up(inc, o);
+            if (l >= o) inc += v;
+        }
+        const int64_t total = __shfl(inc, 63);
+        for (int j = 0; j < 2; ++j) {
+            const int x = xcd + j;
+            int t = x == 0 ? 0 : ntiles;
+            if (x > 0 && x < 8) {
+                const int64_t target = (int64_t)x * total;
+                const uint64_t reach = __ballot(8 * inc >= target);
+                const int src = __ffsll((unsigned long long)reach) - 1;
+                int cand = e1 * per_e;
+                int64_t c = inc - own;
+                for (int e = e0; e < e1; ++e) {
+                    const int64_t ce = cost(e);
+                    if (8 * (c + ce) >= target) {
+                        const int64_t per_tile = ce / per_e;
+                        const int64_t need = target - 8 * c;
+                        cand = e * per_e + (int)(need > 0 ? (need + 8 * per_tile - 1) / (8 * per_tile) : 0);
+                        break;
+                    }
+                    c += ce;
+                }
+                t = __shfl(cand, src);
+            }
+            if (l == 0) xcd_range[j] = t;
+        }
+    }
+    __syncthreads();
+    const int t_end = xcd_range[1];
+    const int t_first = xcd_range[0] + (int)(blockIdx.x / 8);
     if (t_first >= t_end) return;
 
     // tile -> expert and 256 x 256 block of C_e, in groups of GM row tiles
