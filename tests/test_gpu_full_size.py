@@ -6,7 +6,8 @@ the oracle then runs the whole layer (about a minute of fp64 work on 16
 cores for each).  Routing and dispatch must match bit for bit over all
 tokens (top-k indices, selection scores, counts, offsets, permutation, drop
 masks, x_perm bytes); every row of y_perm, the shared expert and every
-output token within the bf16 tolerance of tests/gpu_helpers.py.  The sampled
+output token within the bf16 tolerance of tests/gpu_helpers.py; the
+whole-layer call's output equals the stage calls' byte for byte.  The sampled
 full-size tests in test_gpu_parity.py stay as fast pre-checks.
 """
 from __future__ import annotations
@@ -31,6 +32,10 @@ def test_full_size_layer_every_row(name):
     H.log(f"[full-size] {name}: drawing inputs on the GPU")
     dinp = workloads.make_inputs(cfg, device="cuda", with_noise=False)
     g = H.run_stages(cfg, dinp, noise_input=False)
+    # the whole-layer call (its up projection gathers the rows of x) writes
+    # the same bytes as the stage calls checked against the oracle below
+    out_layer, _ = H.run_layer(cfg, dinp, noise_input=False, stats=False)
+    assert torch.equal(out_layer.view(torch.int16), g["out"].view(torch.int16)), "layer differs from stages"
     H.log(f"[full-size] {name}: GPU layer done; copying inputs to the host")
     host = {k: v.cpu() for k, v in dinp.items()}
     del dinp

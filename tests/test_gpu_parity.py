@@ -145,8 +145,16 @@ def test_noisy_builtin_philox_stream_matches_oracle():
     check_all(cfg, g, o)
 
 
-def test_layer_forward_equals_stages_and_is_deterministic():
-    cfg = MID["sigmoid_shared"]
+# moe_layer_forward gathers the up projection's rows from x (the stage calls
+# read the dispatch's x_perm copy): small tiles, 256 x 256 ping-pong tiles with
+# split-K units, remainder tiles, expert choice, hash routing and fp32.
+LAYER_EQ = ["sigmoid_shared", "split_k_bf16", "tiles_256_bf16", "rag_bf16_swiglu", "ec_bf16_swiglu",
+            "hash_bf16_swiglu", "f32_swiglu_mid", "split_k_relu_cap"]
+
+
+@pytest.mark.parametrize("name", LAYER_EQ)
+def test_layer_forward_equals_stages_and_is_deterministic(name):
+    cfg = MID[name]
     inp = workloads.make_inputs(cfg)
     d = H.to_device(inp)
     g = H.run_stages(cfg, d)
