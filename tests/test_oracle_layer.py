@@ -243,6 +243,38 @@ def test_f_P_sum_to_one_and_stats():
     assert o["aux"] == pytest.approx(cfg.E * float((o["f"] * o["P"]).sum()))
 
 
+@pytest.mark.parametrize("case", ["k1", "k2"])
+def test_load_statistics_on_a_hand_worked_selection(case):
+    """Counts, capacity cut, f, drops, imbalance and the balance term worked
+    out by hand for a fixed selection (capacity C = ceil(cf T k / E) with the
+    first C assignments of an expert in (t, j) order kept, Lecture29
+    "Inference load balance"; f_i before drops with sum 1, CS336 notes
+    section 9; I = max_i n_i / mean_i n_i, Lecture29 "Myth 3"; the balance
+    term E sum f_i P_i, CS336 notes section 9).  The expected values tell
+    max/mean apart from max/min (an expert with no tokens), from kept counts
+    in place of routed ones, and from a T / E mean in place of T k / E."""
+    if case == "k1":
+        cfg = small(E=4, k=1, T=8, capacity_factor=1.0)
+        idx = np.array([[0], [0], [1], [0], [2], [0], [1], [0]], np.int32)
+        counts, kept, dropped, imb, aux = [5, 2, 1, 0], [2, 2, 1, 0], 3, 2.5, 1.4
+        f = [5 / 8, 2 / 8, 1 / 8, 0.0]
+    else:
+        cfg = small(E=4, k=2, T=4, capacity_factor=1.0)
+        idx = np.array([[0, 1], [0, 2], [0, 1], [3, 0]], np.int32)
+        counts, kept, dropped, imb, aux = [4, 2, 1, 1], [2, 2, 1, 1], 2, 2.0, 1.25
+        f = [4 / 8, 2 / 8, 1 / 8, 1 / 8]
+    P = np.array([0.4, 0.3, 0.2, 0.1])
+    dp = oracle.dispatch(cfg, idx)
+    assert dp["C"] == 2
+    np.testing.assert_array_equal(dp["counts"], counts)
+    np.testing.assert_array_equal(dp["kept"], kept)
+    st = oracle.stats(cfg, dp["counts"], dp["kept"], P, cfg.T)
+    np.testing.assert_allclose(st["f"], f, rtol=0, atol=1e-15)
+    assert st["n_dropped"] == dropped
+    assert st["imbalance"] == imb
+    assert st["aux"] == pytest.approx(aux, abs=1e-14)
+
+
 def test_uniform_routing_gives_unit_balance_terms():
     """Token t points at expert t mod E (one-hot logits), k = 1: every expert
     gets T/E tokens, so f_i = 1/E (Lecture29 routing analysis: the uniform
