@@ -101,7 +101,7 @@ hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, c
 hipError_t launch_tile_plans(bool bf16, const int32_t* offsets, int E, int64_t max_rows, int epi1, int N1, int K1,
                              int BM1, int BN1, int32_t* plan1, int epi2, int N2, int K2, int BM2, int BN2,
                              int32_t* plan2, hipStream_t s);
-GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N);
+GemmShape pick_gemm_shape(bool bf16, int epi, int64_t rows, int E, int N, int K = 0);
 // Plan geometry of a grouped GEMM launch (as launch_grouped_gemm sets it),
 // for a plan written ahead of the launch (plan_ready).
 PlanGeom plan_geom(bool bf16, int epi, int N, int K, int BM, int BN, int32_t* pre);

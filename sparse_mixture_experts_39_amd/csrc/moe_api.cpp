@@ -93,19 +93,19 @@ size_t partial_bytes_of(const moe_config* c) {
     const bool bf = c->act_dtype == MOE_BF16;
     const int epi_up = c->act == MOE_ACT_SWIGLU ? 2 : 1;
     size_t b = 0;
-    auto need = [&](int epi, int64_t rows, int E, int N) {
-        const moe::GemmShape g = moe::pick_gemm_shape(bf, epi, rows, E, N);
+    auto need = [&](int epi, int64_t rows, int E, int N, int K) {
+        const moe::GemmShape g = moe::pick_gemm_shape(bf, epi, rows, E, N, K);
         const size_t n = moe::gemm_partial_bytes(g.BM, g.BN);
         if (n > b) b = n;
     };
     const int64_t R = max_rows_of(c);
     if (R > 0) {
-        need(epi_up, R, c->n_experts, c->d_ff);
-        need(0, R, c->n_experts, c->d_model);
+        need(epi_up, R, c->n_experts, c->d_ff, c->d_model);
+        need(0, R, c->n_experts, c->d_model, c->d_ff);
     }
     if (c->n_shared > 0 && c->T > 0) {
-        need(2, c->T, 1, c->d_ff_shared);
-        need(0, c->T, 1, c->d_model);
+        need(2, c->T, 1, c->d_ff_shared, c->d_model);
+        need(0, c->T, 1, c->d_model, c->d_ff_shared);
     }
     return b;
 }
@@ -521,7 +521,7 @@ static int gemm_epi(const moe_config* c, bool up, bool pre) {
     return up ? (swiglu ? (pre ? 3 : 2) : (pre ? 4 : 1)) : 0;
 }
 static moe::GemmShape gemm_shape(const moe_config* c, bool up, bool pre, int64_t rows, int E, int F) {
-    return moe::pick_gemm_shape(is_bf16(c), gemm_epi(c, up, pre), rows, E, up ? F : c->d_model);
+    return moe::pick_gemm_shape(is_bf16(c), gemm_epi(c, up, pre), rows, E, up ? F : c->d_model, up ? c->d_model : F);
 }
 
 // up with arows != NULL: row i of the up projection's input is row

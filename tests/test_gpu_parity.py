@@ -45,6 +45,11 @@ MID = {
                           gate="softmax_topk", seed=18),
     "split_k_relu_cap": Config("split_k_relu_cap", T=900, d=768, F=640, E=5, k=2, act_dtype="bf16", act="relu",
                                gate="softmax_full", capacity_factor=1.0, seed=19),
+    # about 128 rows per expert with a long up reduction (K = d = 2048): the
+    # up projection takes 256-row tiles (remainder tiles included), the down
+    # projection (K = 256) 128-row tiles
+    "k2048_avg128": Config("k2048_avg128", T=512, d=2048, F=256, E=8, k=2, act_dtype="bf16", act="swiglu",
+                           gate="softmax_topk", seed=27),
     # 256 x 256 tiles without split: every accumulator goes through the
     # LDS-staged epilogue
     "tiles_256_bf16": Config("tiles_256_bf16", T=2048, d=256, F=256, E=2, k=1, act_dtype="bf16", act="swiglu",
@@ -148,7 +153,7 @@ def test_noisy_builtin_philox_stream_matches_oracle():
 # moe_layer_forward gathers the up projection's rows from x (the stage calls
 # read the dispatch's x_perm copy): small tiles, 256 x 256 ping-pong tiles with
 # split-K units, remainder tiles, expert choice, hash routing and fp32.
-LAYER_EQ = ["sigmoid_shared", "split_k_bf16", "tiles_256_bf16", "rag_bf16_swiglu", "ec_bf16_swiglu",
+LAYER_EQ = ["sigmoid_shared", "split_k_bf16", "k2048_avg128", "tiles_256_bf16", "rag_bf16_swiglu", "ec_bf16_swiglu",
             "hash_bf16_swiglu", "f32_swiglu_mid", "split_k_relu_cap"]
 
 
