@@ -48,8 +48,8 @@
 //     accumulators of the same (row, unit) in one lane and writes h directly.
 //   * Split-K tail: a mostly empty last round of tiles is cut into K ranges
 //     (second launch, fp32 partials) and reduced in order by k_split_fixup.
-//   * Remainder tiles: with 256-row tiles, an expert's last <= 128 rows go to
-//     64-row tiles (kRemBM) in the same launch, after all whole tiles (so a
+//   * Remainder tiles: with 256-row tiles, an expert's last <= 64 rows go to
+//     a 64-row tile (kRemBM) in the same launch, after all whole tiles (so a
 //     split-K tail cuts the small remainder tiles first), and a row count
 //     just past a multiple of 256 does not pay for a whole padded tile.
 #include <algorithm>

@@ -86,8 +86,8 @@ size_t gemm_partial_bytes(int BM, int BN);
 // stores a to C2.
 // Builds the tile plan on the device (offsets == NULL: one group of max_rows
 // rows, whose offsets go to plan_copy), then runs the GEMM and its split-K
-// fixup; with 256-row bf16 tiles, 64-row tiles of the same launch cover the
-// rows an expert has left past its whole tiles when there are at most 128.
+// fixup; with 256-row bf16 tiles, a 64-row tile of the same launch covers the
+// rows an expert has left past its whole tiles when there are at most 64.
 // With arows != NULL row i of the grouped A is row arows[i] / arow_div of A,
 // which has a_rows rows of lda elements (under 2^31 bytes).
 hipError_t launch_grouped_gemm(bool bf16, int epi, const void* A, int64_t lda, const void* B0, const void* B1,

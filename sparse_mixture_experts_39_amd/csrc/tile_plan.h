@@ -20,7 +20,7 @@ namespace moe {
 constexpr int kSplitUnits = 256;   // CUs of the target chip
 constexpr int kMaxSplit = 16;
 constexpr int kRemBM = 64;
-constexpr int kRemThr = 128;
+constexpr int kRemThr = 64;    // one remainder tile at most: each re-reads its weight panel
 
 __host__ __device__ __forceinline__ int whole_tiles(int M, int BM, bool rem) {
     const int r = M % BM;
