@@ -322,8 +322,9 @@ def test_capacity_on_integer_boundaries_drops_bit_exact(name):
 
 
 # Expert row counts that put every kind of remainder after 256-row tiles:
-# none, 1, 64, 65, 128 (these go to the 64-row remainder launch), 129 and 255
-# (a whole 256-row tile), and experts smaller than one tile.  The caller hands
+# none, 1 and 64 (these go to a 64-row remainder tile of the same launch), 65,
+# 128, 129 and 255 (a whole, padded 256-row tile), and experts smaller than one
+# tile, on either side of the 64-row threshold.  The caller hands
 # the offsets straight to moe_expert_ffn; every row is checked.
 REM_COUNTS = [256, 257, 320, 321, 384, 385, 511, 0, 1, 64, 100, 128, 129, 577]
 
